@@ -1,0 +1,429 @@
+"""Plain, slow, float64 CPU oracle for Persistent Block-Sparse Attention (PBSA).
+
+TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the benchmark's
+CPU-baseline leg import this module.  It shares no code, table or helper with the
+HIP library, and it imports nothing from that library's package.
+
+What it follows.  No page prints code, pseudo-code or a worked example for PBSA; the
+method is described in prose, and the oracle takes the plainest reading of it:
+
+  [SF]  "Sparse Forcing: Native Trainable Sparse Attention for Real-time Autoregressive
+        Diffusion Video Generation" (gist.science explainers, English/Chinese/Portuguese),
+        section 2 "Methodology": B "Core Mechanism: Structured Memory Decomposition"
+        (persistent memory P_t with sinks + local sliding window L_t), C "Persistent
+        Block-Sparse Attention" (dense access to P_t, top-K routing inside L_t from
+        compressed block representatives, Top-C update of P_t as the window slides),
+        and the Chinese page's 2.2 (blockified compression, coarse scoring, the hybrid
+        mask).
+  [LF]  "Light Forcing: Accelerating Autoregressive Video Diffusion via Sparse Attention"
+        (papernotes.org), "Key designs": chunk-aware growth (the per-chunk sparsity
+        s_i = s_base - alpha_i * beta and its FLOPs identity) and hierarchical sparse
+        attention (mean pooling at block and frame level, frame top-K united with forced
+        frames, block top-K inside the chosen frames, and the block mask).
+
+Readings taken where the pages leave a step open (each is restated at its function):
+  * blocks tile each latent frame on its own; the last block of a frame may be short;
+  * a representative is the arithmetic mean of its block's tokens (frame rep: mean of
+    the frame's tokens, not the mean of block reps);
+  * the coarse score is scale * <q_rep, k_rep>;
+  * ordering for every top-k is (score descending, id ascending); lists are returned
+    ascending;
+  * top-K chooses among the window blocks only; P_t is attended whole; the current
+    chunk's own blocks are always attended, with no causal mask inside the chunk;
+  * sink blocks are the first S blocks of frame 0, pinned in P_t from the first update;
+  * the memory score of a history block is the sum over the chunk's query blocks of its
+    coarse score (a column sum).  That operator is NOT fixed by the pages: parity
+    unpinned for the operator itself; the Top-C step applied to it is pinned.
+
+Everything floating point is float64.  Inputs given as float32/bf16-valued arrays are
+widened to float64 first.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+# --------------------------------------------------------------------------------------
+# Blockified compression.  [SF] 2.C / Chinese 2.2: the latent is tiled into blocks, each
+# summarised by one representative vector; [LF] HSA step (1): mean pooling at block and
+# frame level.
+# --------------------------------------------------------------------------------------
+
+
+def blocks_per_frame(n: int, B: int) -> int:
+    """Number of blocks a frame of n tokens splits into (last block may be short)."""
+    return -(-n // B)
+
+
+def frame_block_ranges(n: int, B: int):
+    """Token ranges [a, b) of the blocks of one frame: block j is [B*j, min(B*(j+1), n))."""
+    return [(B * j, min(B * (j + 1), n)) for j in range(blocks_per_frame(n, B))]
+
+
+def block_token_range(g: int, n: int, B: int):
+    """Token range [a, b) of global block g = f*nb + j inside a frame-major token array."""
+    nb = blocks_per_frame(n, B)
+    f, j = divmod(g, nb)
+    a, b = frame_block_ranges(n, B)[j]
+    return f * n + a, f * n + b
+
+
+def mean_pool(x, n: int, B: int):
+    """Block and frame representatives of a frame-major token array.
+
+    x: [frames * n, d].  Returns (block_rep [frames*nb, d], frame_rep [frames, d]) as the
+    plain arithmetic means of the tokens each covers ([LF] HSA (1), mean pooling).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    T, d = x.shape
+    if T % n:
+        raise ValueError("token count is not a whole number of frames")
+    frames = T // n
+    nb = blocks_per_frame(n, B)
+    block_rep = np.zeros((frames * nb, d))
+    frame_rep = np.zeros((frames, d))
+    for f in range(frames):
+        frame = x[f * n:(f + 1) * n]
+        frame_rep[f] = frame.sum(axis=0) / n
+        for j, (a, b) in enumerate(frame_block_ranges(n, B)):
+            block_rep[f * nb + j] = frame[a:b].sum(axis=0) / (b - a)
+    return block_rep, frame_rep
+
+
+# --------------------------------------------------------------------------------------
+# Coarse scoring and routing.  [SF] 2.C: block-level scores from the compressed
+# representatives; top-K blocks of the window kept per query block.
+# --------------------------------------------------------------------------------------
+
+
+def coarse_scores(q_rep, k_rep, scale: float):
+    """S[r, j] = scale * <q_rep[r], k_rep[j]> (block-level attention logits)."""
+    q_rep = np.asarray(q_rep, dtype=np.float64)
+    k_rep = np.asarray(k_rep, dtype=np.float64)
+    return scale * (q_rep @ k_rep.T)
+
+
+def top_ids(values, ids, k: int):
+    """The first k of `ids` ordered by (value descending, id ascending), returned ascending.
+
+    Ties go to the lower id.  If k >= len(ids) every id is kept.
+    """
+    values = np.asarray(values, dtype=np.float64)
+    ids = np.asarray(ids, dtype=np.int64)
+    if values.shape != ids.shape:
+        raise ValueError("values and ids differ in length")
+    if k <= 0 or ids.size == 0:
+        return []
+    # np.lexsort sorts by its last key first: primary = -value, secondary = id.
+    order = np.lexsort((ids, -values))
+    return sorted(int(g) for g in ids[order[:k]])
+
+
+# --------------------------------------------------------------------------------------
+# Attention.  [SF] 2.C / Chinese 2.2 "fine-grained attention" and "mask mechanism": each
+# query attends to every persistent block plus its selected window blocks; with a fixed
+# selection that is ordinary softmax attention restricted by a block mask.
+# --------------------------------------------------------------------------------------
+
+
+def masked_attention(q, k, v, mask, scale: float):
+    """Dense softmax attention with an explicit boolean mask [Tq, Tk].
+
+    O[t] = sum_s softmax_s(scale * q_t . k_s over allowed s) v_s, LSE[t] = log sum_s exp(.)
+    (natural log).  A row with no allowed key is an error.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    mask = np.asarray(mask, dtype=bool)
+    if not mask.any(axis=1).all():
+        raise ValueError("a query row has no allowed key")
+    s = np.where(mask, scale * (q @ k.T), -np.inf)
+    m = s.max(axis=1, keepdims=True)
+    e = np.where(mask, np.exp(s - m), 0.0)
+    l = e.sum(axis=1, keepdims=True)
+    o = (e / l) @ v
+    lse = (m + np.log(l))[:, 0]
+    return o, lse
+
+
+def masked_attention_grad(q, k, v, mask, scale: float, dout):
+    """Closed-form gradient of masked_attention's O with respect to q, k and v.
+
+    With P = softmax rows (zero where masked): dV = P^T dO; dP = dO V^T;
+    D = rowsum(dO * O); dS = P * (dP - D); dQ = scale dS K; dK = scale dS^T Q.
+    The mask (the block selection) is held constant: no gradient flows through routing.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    mask = np.asarray(mask, dtype=bool)
+    s = np.where(mask, scale * (q @ k.T), -np.inf)
+    m = s.max(axis=1, keepdims=True)
+    e = np.where(mask, np.exp(s - m), 0.0)
+    p = e / e.sum(axis=1, keepdims=True)
+    o = p @ v
+    dv = p.T @ dout
+    dp = dout @ v.T
+    D = (dout * o).sum(axis=1, keepdims=True)
+    ds = p * (dp - D)
+    dq = scale * (ds @ k)
+    dk = scale * (ds.T @ q)
+    return dq, dk, dv
+
+
+def block_mask(q_blocks, kv_blocks_per_query_block, n: int, B: int, q_tokens: int,
+               kv_tokens: int, q_block_ids=None):
+    """Expand per-query-block allowed KV block lists into a token mask [q_tokens, kv_tokens].
+
+    q_blocks: the query blocks, as global ids in the query token array's own tiling.
+    kv_blocks_per_query_block[i]: allowed KV global block ids for q_blocks[i].
+    """
+    mask = np.zeros((q_tokens, kv_tokens), dtype=bool)
+    for r, allowed in zip(q_blocks, kv_blocks_per_query_block):
+        a, b = block_token_range(r, n, B)
+        for g in allowed:
+            ka, kb = block_token_range(g, n, B)
+            mask[a:b, ka:kb] = True
+    return mask
+
+
+# --------------------------------------------------------------------------------------
+# Persistent memory and sliding window bookkeeping.  [SF] 2.B (P_t bounded, sinks always
+# kept, L_t = recent blocks) and 2.C "dynamic update" (window slides, leaving blocks are
+# scored, the best are promoted, the rest dropped).
+# --------------------------------------------------------------------------------------
+
+
+@dataclass(frozen=True)
+class Schedule:
+    """Shapes of one persistent-mode rollout (per head)."""
+    n: int          # tokens per latent frame
+    B: int          # tokens per block
+    F: int          # frames per generated chunk
+    W: int          # window length in history frames
+    C: int          # persistent capacity in blocks (sinks included)
+    S: int          # sink blocks: global ids 0..S-1 (frame 0)
+    K: int          # top-K window blocks per query block
+    scale: float
+
+    @property
+    def nb(self) -> int:
+        return blocks_per_frame(self.n, self.B)
+
+    def window_frames(self, c: int):
+        """History frames inside the window while chunk c (0-based) is generated."""
+        h = c * self.F
+        return list(range(max(0, h - self.W), h))
+
+    def window_blocks(self, c: int):
+        """L_t: blocks of the window frames, sinks excluded (they live in P_t)."""
+        return [f * self.nb + j for f in self.window_frames(c) for j in range(self.nb)
+                if f * self.nb + j >= self.S]
+
+    def evicted_blocks(self, c: int):
+        """Window blocks that leave the window when chunk c's frames are appended."""
+        h = c * self.F
+        lo, hi = max(0, h - self.W), max(0, h + self.F - self.W)
+        return [f * self.nb + j for f in range(lo, hi) for j in range(self.nb)
+                if f * self.nb + j >= self.S]
+
+    def chunk_blocks(self, c: int):
+        """Global ids of chunk c's own blocks."""
+        return list(range(c * self.F * self.nb, (c + 1) * self.F * self.nb))
+
+
+def route(scores_window, window_ids, K: int):
+    """Per query block, the top-K window blocks by (score desc, id asc), ascending."""
+    return [top_ids(row, window_ids, K) for row in np.asarray(scores_window)]
+
+
+def memory_update(P, sinks, scores_P, evicted_ids, scores_E, C: int):
+    """Top-C retention of the persistent memory.
+
+    P: current persistent ids (sinks included); scores_P[r, i]: coarse score of P[i] for
+    query block r; evicted_ids / scores_E likewise for the blocks leaving the window.
+    Candidates R = (P without sinks) + evicted; memory score m_j = sum_r S[r, j];
+    P' = sinks + the first (C - |sinks|) candidates by (m desc, id asc).  Unkept evicted
+    blocks are dropped.
+    """
+    sinks = sorted(set(sinks))
+    P = list(P)
+    scores_P = np.asarray(scores_P, dtype=np.float64)
+    scores_E = np.asarray(scores_E, dtype=np.float64)
+    if scores_P.shape[-1:] != (len(P),) or scores_E.shape[-1:] != (len(evicted_ids),):
+        raise ValueError("score columns do not match the candidate ids")
+    cand, msum = [], []
+    for i, g in enumerate(P):
+        if g not in sinks:
+            cand.append(g)
+            msum.append(scores_P[:, i].sum())
+    for i, g in enumerate(evicted_ids):
+        cand.append(g)
+        msum.append(scores_E[:, i].sum())
+    keep = top_ids(msum, cand, C - len(sinks))
+    return sorted(sinks + keep)
+
+
+@dataclass
+class PersistentRollout:
+    """Oracle state of one head's rollout: P_t and the frame-major history it indexes.
+
+    The history arrays hold every generated token (the dense KV cache); the oracle reads
+    from them only the blocks P_t and the window name.
+    """
+    sch: Schedule
+    d: int
+    chunk: int = 0
+    P: list = field(default_factory=list)
+    hist_k: list = field(default_factory=list)   # per appended chunk: [F*n, d] float64
+    hist_v: list = field(default_factory=list)
+    hist_krep: list = field(default_factory=list)  # per appended chunk: [F*nb, d]
+
+    def _history(self):
+        if not self.hist_k:
+            z = np.zeros((0, self.d))
+            return z, z, z
+        return (np.concatenate(self.hist_k), np.concatenate(self.hist_v),
+                np.concatenate(self.hist_krep))
+
+    def select(self, q_chunk):
+        """Pool the chunk's queries, score P_t and L_t, route.
+
+        Returns dict(q_rep, P, L, scores_P [Nq, |P|], scores_L [Nq, |L|], sel).
+        """
+        s = self.sch
+        q_rep, _ = mean_pool(q_chunk, s.n, s.B)
+        _, _, krep = self._history()
+        L = s.window_blocks(self.chunk)
+        P = list(self.P)
+        scores_P = coarse_scores(q_rep, krep[P], s.scale) if P else np.zeros((len(q_rep), 0))
+        scores_L = coarse_scores(q_rep, krep[L], s.scale) if L else np.zeros((len(q_rep), 0))
+        sel = route(scores_L, L, s.K)
+        return dict(q_rep=q_rep, P=P, L=L, scores_P=scores_P, scores_L=scores_L, sel=sel)
+
+    def attended_blocks(self, sel):
+        """A_r = P_t + sel[r] + the chunk's own blocks, as history/chunk global ids."""
+        own = self.sch.chunk_blocks(self.chunk)
+        return [sorted(set(self.P) | set(row) | set(own)) for row in sel]
+
+    def attend(self, q_chunk, k_chunk, v_chunk, sel, rows=None):
+        """Gathered form: per query block, softmax attention over the tokens of A_r.
+
+        rows: optional iterable of query-token indices (chunk-local) to compute; others
+        are left as NaN.  Returns (O [F*n, d], LSE [F*n]).
+        """
+        s = self.sch
+        hk, hv, _ = self._history()
+        K_all = np.concatenate([hk, np.asarray(k_chunk, np.float64)])
+        V_all = np.concatenate([hv, np.asarray(v_chunk, np.float64)])
+        q = np.asarray(q_chunk, np.float64)
+        Tq = q.shape[0]
+        o = np.full((Tq, self.d), np.nan)
+        lse = np.full(Tq, np.nan)
+        want = None if rows is None else set(int(t) for t in rows)
+        for r, allowed in enumerate(self.attended_blocks(sel)):
+            a, b = block_token_range(r, s.n, s.B)
+            idx = [t for t in range(a, b) if want is None or t in want]
+            if not idx:
+                continue
+            toks = np.concatenate([np.arange(*block_token_range(g, s.n, s.B))
+                                   for g in allowed])
+            mask = np.ones((len(idx), len(toks)), dtype=bool)
+            oo, ll = masked_attention(q[idx], K_all[toks], V_all[toks], mask, s.scale)
+            o[idx], lse[idx] = oo, ll
+        return o, lse
+
+    def attend_dense(self, q_chunk, k_chunk, v_chunk, sel):
+        """Parity form: dense attention over the whole history + chunk with the block mask."""
+        s = self.sch
+        hk, hv, _ = self._history()
+        K_all = np.concatenate([hk, np.asarray(k_chunk, np.float64)])
+        V_all = np.concatenate([hv, np.asarray(v_chunk, np.float64)])
+        q = np.asarray(q_chunk, np.float64)
+        base = self.chunk * s.F * s.nb
+        allowed = self.attended_blocks(sel)
+        # query block r of the chunk is global block base + r of the full token array
+        mask_full = block_mask([base + r for r in range(len(allowed))], allowed, s.n, s.B,
+                               K_all.shape[0], K_all.shape[0])
+        q0 = self.chunk * s.F * s.n
+        mask = mask_full[q0:q0 + q.shape[0]]
+        return masked_attention(q, K_all, V_all, mask, s.scale)
+
+    def update(self, routed, k_chunk, v_chunk):
+        """Top-C memory update, then append the chunk to the history (advances the chunk)."""
+        s = self.sch
+        E = s.evicted_blocks(self.chunk)
+        L = routed["L"]
+        col = {g: i for i, g in enumerate(L)}
+        scores_E = routed["scores_L"][:, [col[g] for g in E]] if E else \
+            np.zeros((routed["scores_L"].shape[0], 0))
+        sinks = list(range(s.S))
+        self.P = memory_update(routed["P"], sinks, routed["scores_P"], E, scores_E, s.C)
+        k_chunk = np.asarray(k_chunk, np.float64)
+        self.hist_k.append(k_chunk)
+        self.hist_v.append(np.asarray(v_chunk, np.float64))
+        self.hist_krep.append(mean_pool(k_chunk, s.n, s.B)[0])
+        self.chunk += 1
+
+
+# --------------------------------------------------------------------------------------
+# Trainable two-level path.  [LF] HSA: frame-level top-K of pooled frame representatives
+# united with forced frames, then block-level top-K among the blocks of those frames; the
+# block mask is 1 exactly on the chosen (frame, block) pairs.  [LF] CAG: per-chunk budget.
+# --------------------------------------------------------------------------------------
+
+
+def two_level_select(q_rep_row, k_block_rep, k_frame_rep, i: int, F: int, nb: int,
+                     top_frames: int, k_i: int, scale: float):
+    """Selected KV blocks (global ids, ascending) for one query block of chunk i (1-based).
+
+    Chunk 1 attends densely to its own frames.  For i >= 2 the history is frames
+    [0, F(i-1)); p(f) = scale <q_rep, k_frame_rep[f]> over history frames;
+    T = top_frames best history frames united with the forced frames {0, the latest
+    history frame, the chunk's own F frames}; the candidates are every block of the frames
+    in T; the result is their first k_i by (scale <q_rep, k_block_rep[g]> desc, g asc).
+    """
+    if i == 1:
+        return list(range(F * nb))
+    hist = list(range(F * (i - 1)))
+    p = coarse_scores(q_rep_row[None, :], k_frame_rep[hist], scale)[0]
+    T = set(top_ids(p, hist, top_frames))
+    T |= {0, F * (i - 1) - 1}
+    T |= {F * (i - 1) + t for t in range(F)}
+    cand = [f * nb + j for f in sorted(T) for j in range(nb)]
+    o = coarse_scores(q_rep_row[None, :], k_block_rep[cand], scale)[0]
+    return top_ids(o, cand, min(k_i, len(cand)))
+
+
+def cag_budgets(alphas, k_ref: int, i_ref: int):
+    """Per-chunk block budgets k_i for chunks i = 1..len(alphas) ([LF] CAG).
+
+    Each chunk i >= 2 keeps the fraction (1 - s_base + alpha_i * beta) of the N_i blocks it
+    can see, where N_i grows linearly with i.  Reading: 1 - s_base and beta are both the
+    fraction that makes chunk i_ref keep k_ref blocks at alpha = 0, so
+    k_i = floor(k_ref * i * (1 + alpha_i) / i_ref + 1/2), at least 1.  Chunk 1 is dense
+    (the identity's sum starts at i = 2) and is reported as 0 here.
+    """
+    out = []
+    for i, a in enumerate(alphas, start=1):
+        if i == 1:
+            out.append(0)
+            continue
+        out.append(max(1, int(math.floor(k_ref * i * (1.0 + float(a)) / i_ref + 0.5))))
+    return out
+
+
+def cag_target_sparsity(alphas, s_base: float, beta: float, lq, lk):
+    """s_target implied by the CAG FLOPs identity over chunks i = 2..n ([LF] CAG):
+
+    sum_i (1 - s_base + alpha_i beta) lq_i lk_i d = (1 - s_target) sum_i lq_i lk_i d.
+    (d cancels.)
+    """
+    num = sum((1.0 - s_base + a * beta) * q * k for a, q, k in
+              zip(alphas[1:], lq[1:], lk[1:]))
+    den = sum(q * k for q, k in zip(lq[1:], lk[1:]))
+    return 1.0 - num / den
