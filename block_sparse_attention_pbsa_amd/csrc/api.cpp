@@ -1,0 +1,289 @@
+// C ABI of libpbsa: argument validation, then launches on the caller's stream.
+// Every check runs on the host before anything is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/pbsa.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+pbsa_status fail(pbsa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+pbsa_status hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) {
+    g_err.clear();
+    return PBSA_OK;
+  }
+  return fail(PBSA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+constexpr int64_t kMaxSlots = 4096;
+constexpr int kMaxChunks = 256;
+
+pbsa_status check_dims(const pbsa_dims* d, int mode) {
+  if (!d) return fail(PBSA_ERR_NULL, "dims is NULL");
+  if (d->heads < 1) return fail(PBSA_ERR_SHAPE, "heads must be >= 1 (got %d)", d->heads);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(d->head_dim > 0 ? PBSA_ERR_UNSUPPORTED : PBSA_ERR_SHAPE,
+                "head_dim must be 64 or 128 (got %d)", d->head_dim);
+  if (d->block != 64)
+    return fail(d->block > 0 ? PBSA_ERR_UNSUPPORTED : PBSA_ERR_SHAPE,
+                "block must be 64 (got %d)", d->block);
+  if (d->frame_tokens < 1) return fail(PBSA_ERR_SHAPE, "frame_tokens must be >= 1");
+  if (d->chunk_frames < 1) return fail(PBSA_ERR_SHAPE, "chunk_frames must be >= 1");
+  if (!(d->scale > 0.f) || !std::isfinite(d->scale))
+    return fail(PBSA_ERR_SHAPE, "scale must be a positive finite number");
+  if (mode == 0) {
+    const int nb = pbsa::nb_of(*d);
+    if (d->window_frames < d->chunk_frames)
+      return fail(PBSA_ERR_SHAPE, "window_frames (%d) must be >= chunk_frames (%d)",
+                  d->window_frames, d->chunk_frames);
+    if (d->sinks < 0 || d->sinks > d->capacity || d->sinks > nb)
+      return fail(PBSA_ERR_SHAPE, "need 0 <= sinks <= min(capacity, blocks per frame)");
+    if (d->capacity < 0) return fail(PBSA_ERR_SHAPE, "capacity must be >= 0");
+    if (d->topk < 1) return fail(PBSA_ERR_SHAPE, "topk must be >= 1");
+    const int64_t slots = pbsa::slots_of(*d);
+    if (slots > kMaxSlots)
+      return fail(PBSA_ERR_UNSUPPORTED, "capacity + window blocks = %lld exceeds %lld",
+                  static_cast<long long>(slots), static_cast<long long>(kMaxSlots));
+    if (d->capacity - d->sinks > 1024)
+      return fail(PBSA_ERR_UNSUPPORTED, "capacity - sinks must be <= 1024");
+  } else if (mode != 1) {
+    return fail(PBSA_ERR_SHAPE, "mode must be 0 (persistent) or 1 (two-level)");
+  }
+  return PBSA_OK;
+}
+
+pbsa_status check_tok(const pbsa_tensor& t, const char* name, int head_dim) {
+  if (!t.data) return fail(PBSA_ERR_NULL, "%s is NULL", name);
+  if (reinterpret_cast<uintptr_t>(t.data) % 16)
+    return fail(PBSA_ERR_ALIGN, "%s must be 16-byte aligned", name);
+  if (t.token_stride % 8 || t.head_stride % 8)
+    return fail(PBSA_ERR_ALIGN, "%s strides must be multiples of 8 elements", name);
+  if (t.token_stride < head_dim || t.head_stride < 0)
+    return fail(PBSA_ERR_SHAPE, "%s strides out of range", name);
+  return PBSA_OK;
+}
+
+#define PBSA_TRY(x)                  \
+  do {                               \
+    pbsa_status st__ = (x);          \
+    if (st__ != PBSA_OK) return st__; \
+  } while (0)
+
+pbsa_status check_cache(const pbsa_cache* c) {
+  if (!c) return fail(PBSA_ERR_NULL, "cache is NULL");
+  if (!c->k || !c->v || !c->rep || !c->block_id || !c->len)
+    return fail(PBSA_ERR_NULL, "a cache buffer is NULL");
+  if (reinterpret_cast<uintptr_t>(c->k) % 16 || reinterpret_cast<uintptr_t>(c->v) % 16 ||
+      reinterpret_cast<uintptr_t>(c->rep) % 16)
+    return fail(PBSA_ERR_ALIGN, "cache k, v and rep must be 16-byte aligned");
+  if (c->chunk_index < 0) return fail(PBSA_ERR_STATE, "chunk_index is negative");
+  return PBSA_OK;
+}
+
+hipStream_t stream_of(void* s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+int pbsa_abi_version(void) { return PBSA_ABI_VERSION; }
+
+const char* pbsa_status_str(int status) {
+  switch (status) {
+    case PBSA_OK: return "ok";
+    case PBSA_ERR_NULL: return "null pointer";
+    case PBSA_ERR_SHAPE: return "bad shape";
+    case PBSA_ERR_UNSUPPORTED: return "unsupported";
+    case PBSA_ERR_ALIGN: return "misaligned";
+    case PBSA_ERR_WORKSPACE: return "workspace too small";
+    case PBSA_ERR_STATE: return "bad cache state";
+    case PBSA_ERR_HIP: return "hip error";
+    default: return "unknown status";
+  }
+}
+
+const char* pbsa_last_error(void) { return g_err.c_str(); }
+
+pbsa_status pbsa_check_dims(const pbsa_dims* dims, int32_t mode) {
+  PBSA_TRY(check_dims(dims, mode));
+  g_err.clear();
+  return PBSA_OK;
+}
+
+int64_t pbsa_cache_slots(const pbsa_dims* dims) {
+  if (check_dims(dims, 0) != PBSA_OK) return 0;
+  return pbsa::slots_of(*dims);
+}
+
+size_t pbsa_workspace_bytes(const pbsa_dims* dims, int32_t op, int32_t arg, int32_t arg2) {
+  if (op == PBSA_OP_MEMORY_UPDATE) {
+    if (check_dims(dims, 0) != PBSA_OK) return 0;
+    return pbsa::memory_update_workspace(*dims);
+  }
+  if (op == PBSA_OP_ATTN_BWD) {
+    if (check_dims(dims, 1) != PBSA_OK || arg < 1 || arg2 < 1) return 0;
+    return pbsa::attn_bwd_workspace(*dims, arg, arg2);
+  }
+  return 0;
+}
+
+pbsa_status pbsa_cache_reset(const pbsa_dims* dims, pbsa_cache* cache, void* stream) {
+  PBSA_TRY(check_dims(dims, 0));
+  PBSA_TRY(check_cache(cache));
+  cache->chunk_index = 0;
+  return hip_status(pbsa::launch_cache_reset(*dims, *cache, stream_of(stream)), "cache_reset");
+}
+
+pbsa_status pbsa_pool(const pbsa_dims* dims, pbsa_tensor x, int32_t frames, float* block_rep,
+                      float* frame_rep, void* stream) {
+  PBSA_TRY(check_dims(dims, 1));
+  PBSA_TRY(check_tok(x, "x", dims->head_dim));
+  if (frames < 0) return fail(PBSA_ERR_SHAPE, "frames must be >= 0");
+  if (!block_rep) return fail(PBSA_ERR_NULL, "block_rep is NULL");
+  if (reinterpret_cast<uintptr_t>(block_rep) % 16)
+    return fail(PBSA_ERR_ALIGN, "block_rep must be 16-byte aligned");
+  return hip_status(pbsa::launch_pool(*dims, pbsa::tok_in(x), frames, block_rep, frame_rep,
+                                      stream_of(stream)),
+                    "pool");
+}
+
+pbsa_status pbsa_score_topk(const pbsa_dims* dims, const float* q_rep, const pbsa_cache* cache,
+                            float* scores, int32_t* sel, void* stream) {
+  PBSA_TRY(check_dims(dims, 0));
+  PBSA_TRY(check_cache(cache));
+  if (!q_rep || !scores || !sel) return fail(PBSA_ERR_NULL, "q_rep, scores and sel are required");
+  if (reinterpret_cast<uintptr_t>(q_rep) % 16)
+    return fail(PBSA_ERR_ALIGN, "q_rep must be 16-byte aligned");
+  return hip_status(pbsa::launch_score_topk(*dims, q_rep, *cache, scores, sel, stream_of(stream)),
+                    "score_topk");
+}
+
+pbsa_status pbsa_attn_fwd(const pbsa_dims* dims, pbsa_tensor q, const pbsa_cache* cache,
+                          pbsa_tensor chunk_k, pbsa_tensor chunk_v, const int32_t* sel,
+                          pbsa_tensor o, float* lse, void* stream) {
+  PBSA_TRY(check_dims(dims, 0));
+  PBSA_TRY(check_cache(cache));
+  PBSA_TRY(check_tok(q, "q", dims->head_dim));
+  PBSA_TRY(check_tok(chunk_k, "chunk_k", dims->head_dim));
+  PBSA_TRY(check_tok(chunk_v, "chunk_v", dims->head_dim));
+  PBSA_TRY(check_tok(o, "o", dims->head_dim));
+  if (!sel || !lse) return fail(PBSA_ERR_NULL, "sel and lse are required");
+  return hip_status(pbsa::launch_attn_fwd_persistent(*dims, pbsa::tok_in(q), *cache,
+                                                     pbsa::tok_in(chunk_k),
+                                                     pbsa::tok_in(chunk_v), sel,
+                                                     pbsa::tok_out(o), lse, stream_of(stream)),
+                    "attn_fwd");
+}
+
+pbsa_status pbsa_memory_update(const pbsa_dims* dims, const float* scores, pbsa_cache* cache,
+                               pbsa_tensor chunk_k, pbsa_tensor chunk_v, const float* chunk_rep,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  PBSA_TRY(check_dims(dims, 0));
+  PBSA_TRY(check_cache(cache));
+  PBSA_TRY(check_tok(chunk_k, "chunk_k", dims->head_dim));
+  PBSA_TRY(check_tok(chunk_v, "chunk_v", dims->head_dim));
+  if (!scores || !chunk_rep) return fail(PBSA_ERR_NULL, "scores and chunk_rep are required");
+  const size_t need = pbsa::memory_update_workspace(*dims);
+  if (!workspace || workspace_bytes < need)
+    return fail(PBSA_ERR_WORKSPACE, "memory_update needs %zu workspace bytes (got %zu)", need,
+                workspace ? workspace_bytes : static_cast<size_t>(0));
+  if (cache->chunk_index > (int64_t{1} << 40) / (dims->chunk_frames * pbsa::nb_of(*dims)))
+    return fail(PBSA_ERR_STATE, "chunk_index out of range");
+  pbsa_status st = hip_status(
+      pbsa::launch_memory_update(*dims, scores, *cache, pbsa::tok_in(chunk_k),
+                                 pbsa::tok_in(chunk_v), chunk_rep, workspace, stream_of(stream)),
+      "memory_update");
+  if (st == PBSA_OK) cache->chunk_index += 1;
+  return st;
+}
+
+pbsa_status pbsa_score_topk_2lvl(const pbsa_dims* dims, int32_t chunks, int32_t top_frames,
+                                 const int32_t* k_per_chunk, const float* q_rep,
+                                 const float* block_rep, const float* frame_rep,
+                                 int32_t max_sel, int32_t* sel, int32_t* nsel, void* stream) {
+  PBSA_TRY(check_dims(dims, 1));
+  if (chunks < 1 || chunks > kMaxChunks)
+    return fail(PBSA_ERR_SHAPE, "chunks must be in [1, %d]", kMaxChunks);
+  if (top_frames < 0) return fail(PBSA_ERR_SHAPE, "top_frames must be >= 0");
+  if (!k_per_chunk || !q_rep || !block_rep || !frame_rep || !sel || !nsel)
+    return fail(PBSA_ERR_NULL, "a two-level selection buffer is NULL");
+  const int nb = pbsa::nb_of(*dims);
+  if (max_sel < dims->chunk_frames * nb)
+    return fail(PBSA_ERR_SHAPE, "max_sel must be >= chunk_frames * blocks per frame");
+  for (int i = 1; i < chunks; ++i)
+    if (k_per_chunk[i] < 1 || k_per_chunk[i] > max_sel)
+      return fail(PBSA_ERR_SHAPE, "k_per_chunk[%d] = %d outside [1, max_sel]", i, k_per_chunk[i]);
+  const int64_t cand = static_cast<int64_t>(chunks) * dims->chunk_frames * nb;
+  if (cand * 12 + static_cast<int64_t>(chunks) * dims->chunk_frames * 8 > 60 * 1024)
+    return fail(PBSA_ERR_UNSUPPORTED, "clip too long for the selection kernel's LDS");
+  return hip_status(pbsa::launch_score_topk_2lvl(*dims, chunks, top_frames, k_per_chunk, q_rep,
+                                                 block_rep, frame_rep, max_sel, sel, nsel,
+                                                 stream_of(stream)),
+                    "score_topk_2lvl");
+}
+
+pbsa_status pbsa_attn_fwd_2lvl(const pbsa_dims* dims, int32_t chunks, pbsa_tensor q,
+                               pbsa_tensor k, pbsa_tensor v, const int32_t* sel,
+                               const int32_t* nsel, int32_t max_sel, pbsa_tensor o, float* lse,
+                               void* stream) {
+  PBSA_TRY(check_dims(dims, 1));
+  if (chunks < 1) return fail(PBSA_ERR_SHAPE, "chunks must be >= 1");
+  PBSA_TRY(check_tok(q, "q", dims->head_dim));
+  PBSA_TRY(check_tok(k, "k", dims->head_dim));
+  PBSA_TRY(check_tok(v, "v", dims->head_dim));
+  PBSA_TRY(check_tok(o, "o", dims->head_dim));
+  if (!sel || !nsel || !lse) return fail(PBSA_ERR_NULL, "sel, nsel and lse are required");
+  if (max_sel < 1) return fail(PBSA_ERR_SHAPE, "max_sel must be >= 1");
+  return hip_status(pbsa::launch_attn_fwd_2lvl(*dims, chunks, pbsa::tok_in(q), pbsa::tok_in(k),
+                                               pbsa::tok_in(v), sel, nsel, max_sel,
+                                               pbsa::tok_out(o), lse, stream_of(stream)),
+                    "attn_fwd_2lvl");
+}
+
+pbsa_status pbsa_attn_bwd(const pbsa_dims* dims, int32_t chunks, pbsa_tensor q, pbsa_tensor k,
+                          pbsa_tensor v, pbsa_tensor o, const float* lse, pbsa_tensor dout,
+                          const int32_t* sel, const int32_t* nsel, int32_t max_sel,
+                          pbsa_tensor dq, pbsa_tensor dk, pbsa_tensor dv, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  PBSA_TRY(check_dims(dims, 1));
+  if (chunks < 1) return fail(PBSA_ERR_SHAPE, "chunks must be >= 1");
+  PBSA_TRY(check_tok(q, "q", dims->head_dim));
+  PBSA_TRY(check_tok(k, "k", dims->head_dim));
+  PBSA_TRY(check_tok(v, "v", dims->head_dim));
+  PBSA_TRY(check_tok(o, "o", dims->head_dim));
+  PBSA_TRY(check_tok(dout, "dout", dims->head_dim));
+  PBSA_TRY(check_tok(dq, "dq", dims->head_dim));
+  PBSA_TRY(check_tok(dk, "dk", dims->head_dim));
+  PBSA_TRY(check_tok(dv, "dv", dims->head_dim));
+  if (!lse || !sel || !nsel) return fail(PBSA_ERR_NULL, "lse, sel and nsel are required");
+  if (max_sel < 1) return fail(PBSA_ERR_SHAPE, "max_sel must be >= 1");
+  const size_t need = pbsa::attn_bwd_workspace(*dims, chunks, max_sel);
+  if (!workspace || workspace_bytes < need)
+    return fail(PBSA_ERR_WORKSPACE, "attn_bwd needs %zu workspace bytes (got %zu)", need,
+                workspace ? workspace_bytes : static_cast<size_t>(0));
+  return hip_status(pbsa::launch_attn_bwd(*dims, chunks, pbsa::tok_in(q), pbsa::tok_in(k),
+                                          pbsa::tok_in(v), pbsa::tok_in(o), lse,
+                                          pbsa::tok_in(dout), sel, nsel, max_sel,
+                                          pbsa::tok_out(dq), pbsa::tok_out(dk),
+                                          pbsa::tok_out(dv), workspace, stream_of(stream)),
+                    "attn_bwd");
+}
+
+}  // extern "C"

@@ -1,0 +1,66 @@
+// Internal launchers: argument checking happens in api.cpp, these only enqueue kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/pbsa.h"
+
+namespace pbsa {
+
+struct TokIn {
+  const uint16_t* p;
+  int64_t ts;  // token stride (elements)
+  int64_t hs;  // head stride (elements)
+};
+struct TokOut {
+  uint16_t* p;
+  int64_t ts;
+  int64_t hs;
+};
+
+inline TokIn tok_in(const pbsa_tensor& t) {
+  return TokIn{static_cast<const uint16_t*>(t.data), t.token_stride, t.head_stride};
+}
+inline TokOut tok_out(const pbsa_tensor& t) {
+  return TokOut{static_cast<uint16_t*>(t.data), t.token_stride, t.head_stride};
+}
+
+inline int nb_of(const pbsa_dims& d) { return (d.frame_tokens + d.block - 1) / d.block; }
+inline int64_t slots_of(const pbsa_dims& d) {
+  return static_cast<int64_t>(d.capacity) + static_cast<int64_t>(d.window_frames) * nb_of(d);
+}
+
+hipError_t launch_pool(const pbsa_dims& d, TokIn x, int frames, float* block_rep,
+                       float* frame_rep, hipStream_t s);
+
+hipError_t launch_cache_reset(const pbsa_dims& d, const pbsa_cache& c, hipStream_t s);
+
+hipError_t launch_score_topk(const pbsa_dims& d, const float* q_rep, const pbsa_cache& c,
+                             float* scores, int32_t* sel, hipStream_t s);
+
+hipError_t launch_score_topk_2lvl(const pbsa_dims& d, int chunks, int top_frames,
+                                  const int32_t* k_per_chunk, const float* q_rep,
+                                  const float* block_rep, const float* frame_rep, int max_sel,
+                                  int32_t* sel, int32_t* nsel, hipStream_t s);
+
+hipError_t launch_attn_fwd_persistent(const pbsa_dims& d, TokIn q, const pbsa_cache& c,
+                                      TokIn ck, TokIn cv, const int32_t* sel, TokOut o,
+                                      float* lse, hipStream_t s);
+
+hipError_t launch_attn_fwd_2lvl(const pbsa_dims& d, int chunks, TokIn q, TokIn k, TokIn v,
+                                const int32_t* sel, const int32_t* nsel, int max_sel, TokOut o,
+                                float* lse, hipStream_t s);
+
+size_t attn_bwd_workspace(const pbsa_dims& d, int chunks, int max_sel);
+hipError_t launch_attn_bwd(const pbsa_dims& d, int chunks, TokIn q, TokIn k, TokIn v, TokIn o,
+                           const float* lse, TokIn dout, const int32_t* sel,
+                           const int32_t* nsel, int max_sel, TokOut dq, TokOut dk, TokOut dv,
+                           void* ws, hipStream_t s);
+
+size_t memory_update_workspace(const pbsa_dims& d);
+hipError_t launch_memory_update(const pbsa_dims& d, const float* scores, const pbsa_cache& c,
+                                TokIn ck, TokIn cv, const float* chunk_rep, void* ws,
+                                hipStream_t s);
+
+}  // namespace pbsa

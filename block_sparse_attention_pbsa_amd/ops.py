@@ -1,0 +1,304 @@
+"""Python binding of libpbsa (ctypes): argument marshalling only.
+
+Every function here checks dtypes, devices and shapes of torch tensors, then calls the C
+entry point of the same name with raw device pointers and torch's current HIP stream.  All
+arithmetic runs in the library's gfx950 kernels.  If libpbsa.so is missing the first call
+raises; there is no fallback.
+
+Token tensors are bf16 torch tensors of shape (tokens, heads, head_dim) whose last
+dimension is contiguous; any other token/head strides are passed through (so an
+(H, T, d) tensor can be handed over as ``x.permute(1, 0, 2)``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpbsa.so")
+_lib = None
+
+PBSA_OK = 0
+PBSA_OP_MEMORY_UPDATE = 1
+PBSA_OP_ATTN_BWD = 2
+
+
+class PbsaError(RuntimeError):
+    def __init__(self, fn, status, text):
+        super().__init__(f"{fn} failed with status {status}: {text}")
+        self.status = status
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("block", ctypes.c_int32), ("frame_tokens", ctypes.c_int32),
+                ("chunk_frames", ctypes.c_int32), ("window_frames", ctypes.c_int32),
+                ("capacity", ctypes.c_int32), ("sinks", ctypes.c_int32),
+                ("topk", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+class Tensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("token_stride", ctypes.c_int64),
+                ("head_stride", ctypes.c_int64)]
+
+
+class CacheC(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("rep", ctypes.c_void_p),
+                ("block_id", ctypes.c_void_p), ("len", ctypes.c_void_p),
+                ("chunk_index", ctypes.c_int64)]
+
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_SIGS = {
+    "pbsa_abi_version": ([], ctypes.c_int),
+    "pbsa_status_str": ([ctypes.c_int], ctypes.c_char_p),
+    "pbsa_last_error": ([], ctypes.c_char_p),
+    "pbsa_check_dims": ([ctypes.POINTER(Dims), _I32], ctypes.c_int),
+    "pbsa_cache_slots": ([ctypes.POINTER(Dims)], ctypes.c_int64),
+    "pbsa_workspace_bytes": ([ctypes.POINTER(Dims), _I32, _I32, _I32], ctypes.c_size_t),
+    "pbsa_cache_reset": ([ctypes.POINTER(Dims), ctypes.POINTER(CacheC), _P], ctypes.c_int),
+    "pbsa_pool": ([ctypes.POINTER(Dims), Tensor, _I32, _P, _P, _P], ctypes.c_int),
+    "pbsa_score_topk": ([ctypes.POINTER(Dims), _P, ctypes.POINTER(CacheC), _P, _P, _P],
+                        ctypes.c_int),
+    "pbsa_attn_fwd": ([ctypes.POINTER(Dims), Tensor, ctypes.POINTER(CacheC), Tensor, Tensor, _P,
+                       Tensor, _P, _P], ctypes.c_int),
+    "pbsa_memory_update": ([ctypes.POINTER(Dims), _P, ctypes.POINTER(CacheC), Tensor, Tensor, _P,
+                            _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "pbsa_score_topk_2lvl": ([ctypes.POINTER(Dims), _I32, _I32, ctypes.POINTER(_I32), _P, _P, _P,
+                              _I32, _P, _P, _P], ctypes.c_int),
+    "pbsa_attn_fwd_2lvl": ([ctypes.POINTER(Dims), _I32, Tensor, Tensor, Tensor, _P, _P, _I32,
+                            Tensor, _P, _P], ctypes.c_int),
+    "pbsa_attn_bwd": ([ctypes.POINTER(Dims), _I32, Tensor, Tensor, Tensor, Tensor, _P, Tensor,
+                       _P, _P, _I32, Tensor, Tensor, Tensor, _P, ctypes.c_size_t, _P],
+                      ctypes.c_int),
+}
+
+
+def lib():
+    """Load libpbsa.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                               "`python -m block_sparse_attention_pbsa_amd.build`")
+        L = ctypes.CDLL(_LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def exported_symbols():
+    return list(_SIGS)
+
+
+def _check(fn, st):
+    if st != PBSA_OK:
+        raise PbsaError(fn, st, lib().pbsa_last_error().decode())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _dev(t, name, dtype):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+
+
+def _contig(t, name, dtype, shape):
+    _dev(t, name, dtype)
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _tok(t, name, tokens, heads, head_dim):
+    _dev(t, name, torch.bfloat16)
+    if t.dim() != 3 or tuple(t.shape) != (tokens, heads, head_dim):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected "
+                         f"{(tokens, heads, head_dim)} (tokens, heads, head_dim)")
+    if t.stride(2) != 1:
+        raise ValueError(f"{name}: the head_dim axis must be contiguous")
+    return Tensor(t.data_ptr(), t.stride(0), t.stride(1))
+
+
+@dataclass(frozen=True)
+class Shape:
+    """Shapes of one attention layer (mirrors pbsa_dims)."""
+    heads: int
+    head_dim: int
+    frame_tokens: int
+    chunk_frames: int
+    window_frames: int = 1
+    capacity: int = 0
+    sinks: int = 0
+    topk: int = 1
+    scale: float | None = None
+    block: int = 64
+
+    @property
+    def nb(self) -> int:
+        return -(-self.frame_tokens // self.block)
+
+    @property
+    def nq(self) -> int:
+        return self.chunk_frames * self.nb
+
+    @property
+    def chunk_tokens(self) -> int:
+        return self.chunk_frames * self.frame_tokens
+
+    @property
+    def slots(self) -> int:
+        return self.capacity + self.window_frames * self.nb
+
+    def c(self) -> Dims:
+        s = self.scale if self.scale is not None else self.head_dim ** -0.5
+        return Dims(self.heads, self.head_dim, self.block, self.frame_tokens, self.chunk_frames,
+                    self.window_frames, self.capacity, self.sinks, self.topk, s)
+
+
+class Cache:
+    """Device buffers of one layer's persistent-mode KV cache (see pbsa_cache in pbsa.h)."""
+
+    def __init__(self, shape: Shape, device="cuda"):
+        H, S, d = shape.heads, shape.slots, shape.head_dim
+        self.shape = shape
+        self.k = torch.zeros(H, S, shape.block, d, dtype=torch.bfloat16, device=device)
+        self.v = torch.zeros_like(self.k)
+        self.rep = torch.zeros(H, S, d, dtype=torch.float32, device=device)
+        self.block_id = torch.full((H, S), -1, dtype=torch.int32, device=device)
+        self.len = torch.zeros(H, S, dtype=torch.int32, device=device)
+        self.chunk_index = 0
+
+    def c(self) -> CacheC:
+        return CacheC(self.k.data_ptr(), self.v.data_ptr(), self.rep.data_ptr(),
+                      self.block_id.data_ptr(), self.len.data_ptr(), self.chunk_index)
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in
+                   (self.k, self.v, self.rep, self.block_id, self.len))
+
+
+# ------------------------------------------------------------------------------ calls
+def pbsa_cache_slots(shape: Shape) -> int:
+    return int(lib().pbsa_cache_slots(ctypes.byref(shape.c())))
+
+
+def pbsa_workspace_bytes(shape: Shape, op: int, arg: int = 0, arg2: int = 0) -> int:
+    return int(lib().pbsa_workspace_bytes(ctypes.byref(shape.c()), op, arg, arg2))
+
+
+def pbsa_cache_reset(shape: Shape, cache: Cache):
+    cc = cache.c()
+    _check("pbsa_cache_reset", lib().pbsa_cache_reset(ctypes.byref(shape.c()), ctypes.byref(cc),
+                                                      _stream()))
+    cache.chunk_index = cc.chunk_index
+
+
+def pbsa_pool(shape: Shape, x, frames: int, block_rep, frame_rep=None):
+    H, d, nb = shape.heads, shape.head_dim, shape.nb
+    xt = _tok(x, "x", frames * shape.frame_tokens, H, d)
+    _contig(block_rep, "block_rep", torch.float32, (H, frames * nb, d))
+    if frame_rep is not None:
+        _contig(frame_rep, "frame_rep", torch.float32, (H, frames, d))
+    _check("pbsa_pool", lib().pbsa_pool(ctypes.byref(shape.c()), xt, frames, _ptr(block_rep),
+                                        _ptr(frame_rep), _stream()))
+
+
+def pbsa_score_topk(shape: Shape, q_rep, cache: Cache, scores, sel):
+    H, d = shape.heads, shape.head_dim
+    _contig(q_rep, "q_rep", torch.float32, (H, shape.nq, d))
+    _contig(scores, "scores", torch.float32, (H, shape.nq, shape.slots))
+    _contig(sel, "sel", torch.int32, (H, shape.nq, shape.topk))
+    _check("pbsa_score_topk", lib().pbsa_score_topk(ctypes.byref(shape.c()), _ptr(q_rep),
+                                                    ctypes.byref(cache.c()), _ptr(scores),
+                                                    _ptr(sel), _stream()))
+
+
+def pbsa_attn_fwd(shape: Shape, q, cache: Cache, chunk_k, chunk_v, sel, o, lse):
+    H, d, T = shape.heads, shape.head_dim, shape.chunk_tokens
+    qt = _tok(q, "q", T, H, d)
+    kt = _tok(chunk_k, "chunk_k", T, H, d)
+    vt = _tok(chunk_v, "chunk_v", T, H, d)
+    ot = _tok(o, "o", T, H, d)
+    _contig(sel, "sel", torch.int32, (H, shape.nq, shape.topk))
+    _contig(lse, "lse", torch.float32, (H, T))
+    _check("pbsa_attn_fwd", lib().pbsa_attn_fwd(ctypes.byref(shape.c()), qt,
+                                                ctypes.byref(cache.c()), kt, vt, _ptr(sel), ot,
+                                                _ptr(lse), _stream()))
+
+
+def pbsa_memory_update(shape: Shape, scores, cache: Cache, chunk_k, chunk_v, chunk_rep,
+                       workspace):
+    H, d, T = shape.heads, shape.head_dim, shape.chunk_tokens
+    _contig(scores, "scores", torch.float32, (H, shape.nq, shape.slots))
+    kt = _tok(chunk_k, "chunk_k", T, H, d)
+    vt = _tok(chunk_v, "chunk_v", T, H, d)
+    _contig(chunk_rep, "chunk_rep", torch.float32, (H, shape.nq, d))
+    _dev(workspace, "workspace", torch.uint8)
+    cc = cache.c()
+    _check("pbsa_memory_update", lib().pbsa_memory_update(
+        ctypes.byref(shape.c()), _ptr(scores), ctypes.byref(cc), kt, vt, _ptr(chunk_rep),
+        _ptr(workspace), workspace.numel(), _stream()))
+    cache.chunk_index = cc.chunk_index
+
+
+def pbsa_score_topk_2lvl(shape: Shape, chunks: int, top_frames: int, k_per_chunk, q_rep,
+                         block_rep, frame_rep, sel, nsel):
+    H, d = shape.heads, shape.head_dim
+    nq = chunks * shape.nq
+    _contig(q_rep, "q_rep", torch.float32, (H, nq, d))
+    _contig(block_rep, "block_rep", torch.float32, (H, nq, d))
+    _contig(frame_rep, "frame_rep", torch.float32, (H, chunks * shape.chunk_frames, d))
+    _dev(sel, "sel", torch.int32)
+    if sel.dim() != 3 or tuple(sel.shape[:2]) != (H, nq) or not sel.is_contiguous():
+        raise ValueError("sel must be a contiguous (heads, Nq, max_sel) int32 tensor")
+    _contig(nsel, "nsel", torch.int32, (H, nq))
+    ks = (ctypes.c_int32 * chunks)(*[int(k) for k in k_per_chunk])
+    _check("pbsa_score_topk_2lvl", lib().pbsa_score_topk_2lvl(
+        ctypes.byref(shape.c()), chunks, top_frames, ks, _ptr(q_rep), _ptr(block_rep),
+        _ptr(frame_rep), sel.shape[2], _ptr(sel), _ptr(nsel), _stream()))
+
+
+def pbsa_attn_fwd_2lvl(shape: Shape, chunks: int, q, k, v, sel, nsel, o, lse):
+    H, d = shape.heads, shape.head_dim
+    T = chunks * shape.chunk_tokens
+    nq = chunks * shape.nq
+    qt, kt, vt, ot = (_tok(t, nm, T, H, d) for t, nm in ((q, "q"), (k, "k"), (v, "v"), (o, "o")))
+    _dev(sel, "sel", torch.int32)
+    _contig(nsel, "nsel", torch.int32, (H, nq))
+    _contig(lse, "lse", torch.float32, (H, T))
+    _check("pbsa_attn_fwd_2lvl", lib().pbsa_attn_fwd_2lvl(
+        ctypes.byref(shape.c()), chunks, qt, kt, vt, _ptr(sel), _ptr(nsel), sel.shape[2], ot,
+        _ptr(lse), _stream()))
+
+
+def pbsa_attn_bwd(shape: Shape, chunks: int, q, k, v, o, lse, dout, sel, nsel, dq, dk, dv,
+                  workspace):
+    H, d = shape.heads, shape.head_dim
+    T = chunks * shape.chunk_tokens
+    nq = chunks * shape.nq
+    ts = [_tok(t, nm, T, H, d) for t, nm in ((q, "q"), (k, "k"), (v, "v"), (o, "o"),
+                                              (dout, "dout"), (dq, "dq"), (dk, "dk"), (dv, "dv"))]
+    _contig(lse, "lse", torch.float32, (H, T))
+    _dev(sel, "sel", torch.int32)
+    _contig(nsel, "nsel", torch.int32, (H, nq))
+    _dev(workspace, "workspace", torch.uint8)
+    _check("pbsa_attn_bwd", lib().pbsa_attn_bwd(
+        ctypes.byref(shape.c()), chunks, ts[0], ts[1], ts[2], ts[3], _ptr(lse), ts[4],
+        _ptr(sel), _ptr(nsel), sel.shape[2], ts[5], ts[6], ts[7], _ptr(workspace),
+        workspace.numel(), _stream()))

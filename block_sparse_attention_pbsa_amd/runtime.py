@@ -1,0 +1,104 @@
+"""Host-side driver of one layer's PBSA rollout: the per-chunk step as a sequence of
+library calls on torch's current stream, with every buffer allocated once up front.
+
+Per chunk (Sparse Forcing, gist.science, 2.C):
+    pool(q) -> q_rep;  pool(k) -> k_rep;  score_topk(q_rep, cache) -> scores, sel;
+    attn_fwd(q, cache, k, v, sel) -> o, lse;  memory_update(scores, cache, k, v, k_rep).
+With several denoising passes per chunk the persistent memory is shared: only the last
+pass (the one whose K/V enter the cache) calls memory_update.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import ops
+
+
+class PersistentLayer:
+    def __init__(self, shape: ops.Shape, device="cuda"):
+        self.shape = shape
+        H, d, nq, T = shape.heads, shape.head_dim, shape.nq, shape.chunk_tokens
+        self.cache = ops.Cache(shape, device)
+        self.q_rep = torch.empty(H, nq, d, dtype=torch.float32, device=device)
+        self.k_rep = torch.empty(H, nq, d, dtype=torch.float32, device=device)
+        self.scores = torch.empty(H, nq, shape.slots, dtype=torch.float32, device=device)
+        self.sel = torch.empty(H, nq, shape.topk, dtype=torch.int32, device=device)
+        self.o = torch.empty(T, H, d, dtype=torch.bfloat16, device=device)
+        self.lse = torch.empty(H, T, dtype=torch.float32, device=device)
+        nbytes = ops.pbsa_workspace_bytes(shape, ops.PBSA_OP_MEMORY_UPDATE)
+        self.workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+
+    def reset(self):
+        ops.pbsa_cache_reset(self.shape, self.cache)
+
+    def route(self, q):
+        s = self.shape
+        ops.pbsa_pool(s, q, s.chunk_frames, self.q_rep)
+        ops.pbsa_score_topk(s, self.q_rep, self.cache, self.scores, self.sel)
+
+    def attend(self, q, k, v):
+        ops.pbsa_attn_fwd(self.shape, q, self.cache, k, v, self.sel, self.o, self.lse)
+
+    def update(self, k, v):
+        s = self.shape
+        ops.pbsa_pool(s, k, s.chunk_frames, self.k_rep)
+        ops.pbsa_memory_update(s, self.scores, self.cache, k, v, self.k_rep, self.workspace)
+
+    def step(self, q, k, v, attend=True):
+        """One chunk: route, attend (optional), update the memory and append the chunk."""
+        self.route(q)
+        if attend:
+            self.attend(q, k, v)
+        self.update(k, v)
+
+
+class TwoLevelClip:
+    """Buffers and calls of the trainable two-level path over one clip."""
+
+    def __init__(self, shape: ops.Shape, chunks: int, top_frames: int, max_sel: int,
+                 device="cuda"):
+        self.shape, self.chunks, self.top_frames, self.max_sel = shape, chunks, top_frames, max_sel
+        H, d = shape.heads, shape.head_dim
+        nq = chunks * shape.nq
+        T = chunks * shape.chunk_tokens
+        self.q_rep = torch.empty(H, nq, d, dtype=torch.float32, device=device)
+        self.k_rep = torch.empty(H, nq, d, dtype=torch.float32, device=device)
+        self.k_frame = torch.empty(H, chunks * shape.chunk_frames, d, dtype=torch.float32,
+                                   device=device)
+        self.sel = torch.full((H, nq, max_sel), -1, dtype=torch.int32, device=device)
+        self.nsel = torch.zeros(H, nq, dtype=torch.int32, device=device)
+        self.o = torch.empty(T, H, d, dtype=torch.bfloat16, device=device)
+        self.lse = torch.empty(H, T, dtype=torch.float32, device=device)
+        self.dq = torch.empty(T, H, d, dtype=torch.bfloat16, device=device)
+        self.dk = torch.empty_like(self.dq)
+        self.dv = torch.empty_like(self.dq)
+        nbytes = ops.pbsa_workspace_bytes(shape, ops.PBSA_OP_ATTN_BWD, chunks, max_sel)
+        self.workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+
+    def select(self, q, k, k_per_chunk):
+        s, F = self.shape, self.chunks * self.shape.chunk_frames
+        ops.pbsa_pool(s, q, F, self.q_rep)
+        ops.pbsa_pool(s, k, F, self.k_rep, self.k_frame)
+        ops.pbsa_score_topk_2lvl(s, self.chunks, self.top_frames, k_per_chunk, self.q_rep,
+                                 self.k_rep, self.k_frame, self.sel, self.nsel)
+
+    def forward(self, q, k, v):
+        ops.pbsa_attn_fwd_2lvl(self.shape, self.chunks, q, k, v, self.sel, self.nsel, self.o,
+                               self.lse)
+
+    def backward(self, q, k, v, dout):
+        ops.pbsa_attn_bwd(self.shape, self.chunks, q, k, v, self.o, self.lse, dout, self.sel,
+                          self.nsel, self.dq, self.dk, self.dv, self.workspace)
+
+
+def cag_budgets(alphas, k_ref: int, i_ref: int):
+    """Per-chunk block budgets of the trainable path (Light Forcing, chunk-aware growth):
+    chunk i >= 2 keeps a fraction of the blocks it sees that grows with its noise level
+    alpha_i; with the fraction chosen so chunk i_ref keeps k_ref blocks at alpha = 0,
+    k_i = floor(k_ref * i * (1 + alpha_i) / i_ref + 1/2) (at least 1).  Chunk 1 is dense
+    and gets 0 here (its entry is not read)."""
+    import math
+    out = [0]
+    for i in range(2, len(alphas) + 1):
+        out.append(max(1, int(math.floor(k_ref * i * (1.0 + float(alphas[i - 1])) / i_ref + 0.5))))
+    return out

@@ -1,0 +1,218 @@
+/*
+ * pbsa.h -- C ABI of libpbsa, Persistent Block-Sparse Attention (PBSA) for MI355X (gfx950).
+ *
+ * The method: "Sparse Forcing: Native Trainable Sparse Attention for Real-time
+ * Autoregressive Diffusion Video Generation" (gist.science explainer), section 2
+ * "Methodology": B (the KV cache split into a bounded persistent memory P_t, sinks
+ * included, plus a sliding local window L_t), C "Persistent Block-Sparse Attention" (block
+ * representatives, coarse block scores, top-K routing inside L_t, dense access to P_t, a
+ * Top-C update of P_t as the window slides), E (one kernel family for decoding and
+ * training).  The trainable two-level selection follows "Light Forcing: Accelerating
+ * Autoregressive Video Diffusion via Sparse Attention" (papernotes.org), "Key designs":
+ * hierarchical sparse attention (frame-level then block-level top-K) and chunk-aware growth
+ * (per-chunk budgets).
+ *
+ * Conventions for every call
+ *  - Tokens are bf16, passed as raw 16-bit patterns.  Representatives, scores and
+ *    log-sum-exp values are fp32.  Block lists are int32 global block ids.
+ *  - Frames are tiled into blocks on their own: block j of frame f holds tokens
+ *    f*frame_tokens + [block*j, min(block*(j+1), frame_tokens)); the last block of a frame
+ *    may be short.  Global block id g = f*nb + j with nb = ceil(frame_tokens / block).
+ *  - Pointers are DEVICE pointers unless a comment says "host".  The caller owns every
+ *    buffer; the library never allocates, frees or keeps device memory, and keeps no
+ *    state between calls except the thread-local error text.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Every call only enqueues work on
+ *    it and returns; no call synchronises or reads device memory back.  Buffers must stay
+ *    valid until that work has run.
+ *  - Arguments are validated before anything is enqueued; on error nothing is enqueued
+ *    and a status below is returned, with detail in pbsa_last_error().  A failed launch
+ *    returns PBSA_ERR_HIP.  Calls are reentrant.
+ *  - Supported: head_dim 64 or 128, block 64, 1 <= frame_tokens, token strides multiples
+ *    of 8 elements and token pointers 16-byte aligned.
+ */
+#ifndef PBSA_H_
+#define PBSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PBSA_ABI_VERSION 1
+
+typedef enum pbsa_status {
+  PBSA_OK = 0,
+  PBSA_ERR_NULL = 1,        /* a required pointer is NULL */
+  PBSA_ERR_SHAPE = 2,       /* sizes inconsistent or out of range */
+  PBSA_ERR_UNSUPPORTED = 3, /* valid but not built: head_dim other than 64/128, block != 64 */
+  PBSA_ERR_ALIGN = 4,       /* token pointer or stride not aligned for 16-byte loads */
+  PBSA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than pbsa_workspace_bytes */
+  PBSA_ERR_STATE = 6,       /* cache bookkeeping out of range (chunk_index) */
+  PBSA_ERR_HIP = 7          /* a HIP call failed; its text is in pbsa_last_error() */
+} pbsa_status;
+
+/* Shapes of one attention layer.  For the two-level (trainable) calls only heads,
+ * head_dim, block, frame_tokens, chunk_frames and scale are read. */
+typedef struct pbsa_dims {
+  int32_t heads;         /* H */
+  int32_t head_dim;      /* d: 64 or 128 */
+  int32_t block;         /* tokens per block: 64 */
+  int32_t frame_tokens;  /* tokens per latent frame, n */
+  int32_t chunk_frames;  /* frames generated per chunk, F */
+  int32_t window_frames; /* history frames in the local window, W (F <= W) */
+  int32_t capacity;      /* persistent memory capacity in blocks, C (sinks included) */
+  int32_t sinks;         /* sink blocks S: global ids 0..S-1, S <= min(C, nb) */
+  int32_t topk;          /* window blocks routed per query block, K >= 1 */
+  float scale;           /* softmax scale, usually 1/sqrt(d) */
+} pbsa_dims;
+
+/* A bf16 token tensor: element (head h, token t, channel c) lives at
+ * data[h*head_stride + t*token_stride + c] (strides in elements).  [T][H][d] has
+ * token_stride = H*d, head_stride = d; [H][T][d] has token_stride = d, head_stride = T*d. */
+typedef struct pbsa_tensor {
+  void* data;
+  int64_t token_stride;
+  int64_t head_stride;
+} pbsa_tensor;
+
+/* Persistent-mode KV cache of one layer.  slots = capacity + window_frames*nb per head.
+ * Slots [0, capacity) hold P_t (slots [0, sinks) the sinks); slot capacity + (f % W)*nb + j
+ * holds window block j of history frame f.  A slot keeps its block's tokens row-major,
+ * rows past len zero.  The struct itself is host memory; its pointers are device memory
+ * of these sizes:
+ *   k, v      bf16 [heads][slots][block][head_dim]
+ *   rep       fp32 [heads][slots][head_dim]   the block's mean key (its representative)
+ *   block_id  int32 [heads][slots]            global block id, -1 = empty
+ *   len       int32 [heads][slots]            valid tokens of the block
+ * chunk_index counts the chunks appended so far; pbsa_memory_update advances it. */
+typedef struct pbsa_cache {
+  void* k;
+  void* v;
+  float* rep;
+  int32_t* block_id;
+  int32_t* len;
+  int64_t chunk_index;
+} pbsa_cache;
+
+/* ---- helpers ---------------------------------------------------------------------- */
+
+int pbsa_abi_version(void);
+const char* pbsa_status_str(int status);
+/* Text of the last error on this thread ("" if none). */
+const char* pbsa_last_error(void);
+
+/* Checks dims alone (range and support).  mode 0: persistent calls; 1: two-level calls. */
+pbsa_status pbsa_check_dims(const pbsa_dims* dims, int32_t mode);
+
+/* Slots per head of the persistent cache: capacity + window_frames * nb (0 if invalid). */
+int64_t pbsa_cache_slots(const pbsa_dims* dims);
+
+enum { PBSA_OP_MEMORY_UPDATE = 1, PBSA_OP_ATTN_BWD = 2 };
+/* Workspace bytes a call needs.  MEMORY_UPDATE: `arg` unused.  ATTN_BWD: `arg` = clip
+ * chunks, `arg2` = max_sel. */
+size_t pbsa_workspace_bytes(const pbsa_dims* dims, int32_t op, int32_t arg, int32_t arg2);
+
+/* Empties the cache (block_id = -1, len = 0, chunk_index = 0).  K/V/rep are left as they
+ * are; slots are fully written before they are first read. */
+pbsa_status pbsa_cache_reset(const pbsa_dims* dims, pbsa_cache* cache, void* stream);
+
+/* ---- step 1: pooling -----------------------------------------------------------------
+ * Blockified compression (Sparse Forcing 2.C; Light Forcing, hierarchical sparse
+ * attention step 1, mean pooling).  For `frames` frames of x (frames*frame_tokens tokens
+ * per head) writes block_rep[h][g][c] = mean of block g's tokens and, if frame_rep is not
+ * NULL, frame_rep[h][f][c] = mean of frame f's frame_tokens tokens.
+ * block_rep: fp32 [heads][frames*nb][head_dim]; frame_rep: fp32 [heads][frames][head_dim].
+ */
+pbsa_status pbsa_pool(const pbsa_dims* dims, pbsa_tensor x, int32_t frames, float* block_rep,
+                      float* frame_rep, void* stream);
+
+/* ---- step 2: coarse scores and top-K routing (persistent mode) -----------------------
+ * Sparse Forcing 2.C: for the chunk's Nq = chunk_frames*nb query blocks, with q_rep fp32
+ * [heads][Nq][head_dim] (from pbsa_pool of the chunk's queries):
+ *   scores[h][r][s] = scale * <q_rep[h][r], cache.rep[h][s]> for every valid slot s
+ *                     (P_t and window), -inf for empty slots; fp32 [heads][Nq][slots].
+ *   sel[h][r][0..K) = the K window blocks (sinks excluded) with the highest score, ties to
+ *                     the lower global id, written as global ids in ascending order; -1
+ *                     fills the tail when the window holds fewer than K blocks.
+ *                     int32 [heads][Nq][topk].
+ */
+pbsa_status pbsa_score_topk(const pbsa_dims* dims, const float* q_rep, const pbsa_cache* cache,
+                            float* scores, int32_t* sel, void* stream);
+
+/* ---- step 3: attention over the selected blocks (persistent mode) --------------------
+ * Sparse Forcing 2.C and the Chinese page's 2.2 (fine-grained attention, hybrid mask):
+ * every query token t of query block r attends, with softmax scale dims.scale, to the
+ * valid tokens of: every occupied persistent slot, the window blocks sel[h][r][*], and all
+ * chunk_frames*nb blocks of the current chunk (chunk_k/chunk_v, no causal mask inside the
+ * chunk).  Writes o (bf16, same shape as q: chunk_frames*frame_tokens tokens per head)
+ * and lse[h][t] = natural-log sum of exp(scale * q.k) over the attended keys (fp32
+ * [heads][chunk tokens]).  q, chunk_k, chunk_v: chunk_frames*frame_tokens tokens each.
+ */
+pbsa_status pbsa_attn_fwd(const pbsa_dims* dims, pbsa_tensor q, const pbsa_cache* cache,
+                          pbsa_tensor chunk_k, pbsa_tensor chunk_v, const int32_t* sel,
+                          pbsa_tensor o, float* lse, void* stream);
+
+/* ---- step 4: persistent-memory update and window append ------------------------------
+ * Sparse Forcing 2.B/2.C (Top-C retention as the window slides, sinks always kept).  With
+ * c = cache.chunk_index and h = c*chunk_frames appended frames, appending the chunk pushes
+ * frames [max(0,h-W), max(0,h+F-W)) out of the window; their non-sink blocks E join the
+ * non-sink persistent blocks as candidates R; each candidate's memory score is the sum over
+ * the chunk's query blocks of its coarse score (column sums of `scores` from
+ * pbsa_score_topk of this chunk); the new P_t is the sinks plus the C - S best candidates
+ * by (memory score desc, id asc).  Kept blocks stay in their slots, promoted blocks are
+ * copied (K, V, rep, len) into the freed slots in ascending id order, and the chunk's K/V
+ * and chunk_rep (fp32 [heads][Nq][head_dim], pbsa_pool of chunk_k) are written into the
+ * window slots of the frames that left.  On chunk 0 the sink blocks go to slots [0, S).
+ * Finally cache->chunk_index is incremented (host).
+ * workspace: device, >= pbsa_workspace_bytes(dims, PBSA_OP_MEMORY_UPDATE, 0, 0) bytes.
+ */
+pbsa_status pbsa_memory_update(const pbsa_dims* dims, const float* scores, pbsa_cache* cache,
+                               pbsa_tensor chunk_k, pbsa_tensor chunk_v, const float* chunk_rep,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- trainable path: two-level selection ---------------------------------------------
+ * Light Forcing, hierarchical sparse attention (steps 2 and 3) with the chunk-aware
+ * budget.  A clip of `chunks` chunks (chunk_frames frames each) is processed as one
+ * forward.  For query block r of chunk i (1-based):
+ *   i = 1:  all blocks of chunk 1's own frames (dense).
+ *   i >= 2: frame scores scale*<q_rep, frame_rep[f]> over history frames f < F(i-1); the
+ *           top_frames best (ties to the lower frame) united with frame 0, frame F(i-1)-1
+ *           and the chunk's own frames; among all blocks of those frames, the
+ *           min(k_per_chunk[i-1], candidates) best by scale*<q_rep, block_rep[g]>, ties to
+ *           the lower id.
+ * Writes sel[h][r][0..nsel) ascending global ids (int32 [heads][Nq][max_sel], the tail
+ * left untouched) and nsel[h][r] (int32 [heads][Nq]), Nq = chunks*chunk_frames*nb.
+ * q_rep, block_rep: fp32 [heads][Nq][head_dim]; frame_rep fp32 [heads][chunks*F][head_dim].
+ * k_per_chunk: HOST int32 [chunks] (entry 0 unused), chunks <= 256.  max_sel must be at
+ * least chunk_frames*nb and every k_per_chunk entry.
+ */
+pbsa_status pbsa_score_topk_2lvl(const pbsa_dims* dims, int32_t chunks, int32_t top_frames,
+                                 const int32_t* k_per_chunk, const float* q_rep,
+                                 const float* block_rep, const float* frame_rep,
+                                 int32_t max_sel, int32_t* sel, int32_t* nsel, void* stream);
+
+/* Attention of the clip's queries over their selected blocks (sel/nsel from
+ * pbsa_score_topk_2lvl): o (bf16, like q) and lse (fp32 [heads][clip tokens]).
+ * q, k, v: chunks*chunk_frames*frame_tokens tokens per head. */
+pbsa_status pbsa_attn_fwd_2lvl(const pbsa_dims* dims, int32_t chunks, pbsa_tensor q,
+                               pbsa_tensor k, pbsa_tensor v, const int32_t* sel,
+                               const int32_t* nsel, int32_t max_sel, pbsa_tensor o, float* lse,
+                               void* stream);
+
+/* Gradient of pbsa_attn_fwd_2lvl's output with the selection held constant (no gradient
+ * through routing or pooling): given o, lse from the forward and the upstream gradient
+ * dout, writes dq, dk, dv (bf16, same shapes as q, k, v).  Deterministic: no atomics.
+ * workspace: device, >= pbsa_workspace_bytes(dims, PBSA_OP_ATTN_BWD, chunks, max_sel). */
+pbsa_status pbsa_attn_bwd(const pbsa_dims* dims, int32_t chunks, pbsa_tensor q, pbsa_tensor k,
+                          pbsa_tensor v, pbsa_tensor o, const float* lse, pbsa_tensor dout,
+                          const int32_t* sel, const int32_t* nsel, int32_t max_sel,
+                          pbsa_tensor dq, pbsa_tensor dk, pbsa_tensor dv, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PBSA_H_ */

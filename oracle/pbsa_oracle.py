@@ -241,16 +241,14 @@ def route(scores_window, window_ids, K: int):
     return [top_ids(row, window_ids, K) for row in np.asarray(scores_window)]
 
 
-def memory_update(P, sinks, scores_P, evicted_ids, scores_E, C: int):
-    """Top-C retention of the persistent memory.
+def memory_scores(P, sinks, scores_P, evicted_ids, scores_E):
+    """Candidates of the Top-C update and their memory scores.
 
-    P: current persistent ids (sinks included); scores_P[r, i]: coarse score of P[i] for
-    query block r; evicted_ids / scores_E likewise for the blocks leaving the window.
-    Candidates R = (P without sinks) + evicted; memory score m_j = sum_r S[r, j];
-    P' = sinks + the first (C - |sinks|) candidates by (m desc, id asc).  Unkept evicted
-    blocks are dropped.
+    Candidates R = (P without sinks) + evicted (in that order); the memory score of a
+    candidate is the sum over the chunk's query blocks of its coarse score (a column sum
+    of the block-score matrix).  Returns (ids, scores).
     """
-    sinks = sorted(set(sinks))
+    sinks = set(sinks)
     P = list(P)
     scores_P = np.asarray(scores_P, dtype=np.float64)
     scores_E = np.asarray(scores_E, dtype=np.float64)
@@ -264,31 +262,45 @@ def memory_update(P, sinks, scores_P, evicted_ids, scores_E, C: int):
     for i, g in enumerate(evicted_ids):
         cand.append(g)
         msum.append(scores_E[:, i].sum())
+    return cand, msum
+
+
+def memory_update(P, sinks, scores_P, evicted_ids, scores_E, C: int):
+    """Top-C retention of the persistent memory.
+
+    P: current persistent ids (sinks included); scores_P[r, i]: coarse score of P[i] for
+    query block r; evicted_ids / scores_E likewise for the blocks leaving the window.
+    P' = sinks + the first (C - |sinks|) candidates (see memory_scores) by (memory score
+    desc, id asc).  Unkept evicted blocks are dropped.
+    """
+    sinks = sorted(set(sinks))
+    cand, msum = memory_scores(P, sinks, scores_P, evicted_ids, scores_E)
     keep = top_ids(msum, cand, C - len(sinks))
     return sorted(sinks + keep)
 
 
 @dataclass
 class PersistentRollout:
-    """Oracle state of one head's rollout: P_t and the frame-major history it indexes.
+    """Oracle state of one head's rollout: P_t plus the tokens of the blocks it can still use.
 
-    The history arrays hold every generated token (the dense KV cache); the oracle reads
-    from them only the blocks P_t and the window name.
+    Tokens of a block are kept while the block is in the window or in P_t and discarded
+    once it is dropped (the pages' "discarded" history); with keep_history=True every
+    generated token is also kept, for the dense-mask parity form.  Stored tokens keep the
+    caller's dtype and are widened to float64 when used.
     """
     sch: Schedule
     d: int
+    keep_history: bool = False
     chunk: int = 0
     P: list = field(default_factory=list)
-    hist_k: list = field(default_factory=list)   # per appended chunk: [F*n, d] float64
+    tok_k: dict = field(default_factory=dict)   # global block id -> [len, d]
+    tok_v: dict = field(default_factory=dict)
+    krep: dict = field(default_factory=dict)    # global block id -> [d] float64
+    hist_k: list = field(default_factory=list)  # keep_history: per chunk [F*n, d]
     hist_v: list = field(default_factory=list)
-    hist_krep: list = field(default_factory=list)  # per appended chunk: [F*nb, d]
 
-    def _history(self):
-        if not self.hist_k:
-            z = np.zeros((0, self.d))
-            return z, z, z
-        return (np.concatenate(self.hist_k), np.concatenate(self.hist_v),
-                np.concatenate(self.hist_krep))
+    def _reps(self, ids):
+        return np.array([self.krep[g] for g in ids]).reshape(len(ids), self.d)
 
     def select(self, q_chunk):
         """Pool the chunk's queries, score P_t and L_t, route.
@@ -297,16 +309,15 @@ class PersistentRollout:
         """
         s = self.sch
         q_rep, _ = mean_pool(q_chunk, s.n, s.B)
-        _, _, krep = self._history()
         L = s.window_blocks(self.chunk)
         P = list(self.P)
-        scores_P = coarse_scores(q_rep, krep[P], s.scale) if P else np.zeros((len(q_rep), 0))
-        scores_L = coarse_scores(q_rep, krep[L], s.scale) if L else np.zeros((len(q_rep), 0))
+        scores_P = coarse_scores(q_rep, self._reps(P), s.scale) if P else np.zeros((len(q_rep), 0))
+        scores_L = coarse_scores(q_rep, self._reps(L), s.scale) if L else np.zeros((len(q_rep), 0))
         sel = route(scores_L, L, s.K)
         return dict(q_rep=q_rep, P=P, L=L, scores_P=scores_P, scores_L=scores_L, sel=sel)
 
     def attended_blocks(self, sel):
-        """A_r = P_t + sel[r] + the chunk's own blocks, as history/chunk global ids."""
+        """A_r = P_t + sel[r] + the chunk's own blocks, as global block ids."""
         own = self.sch.chunk_blocks(self.chunk)
         return [sorted(set(self.P) | set(row) | set(own)) for row in sel]
 
@@ -317,10 +328,12 @@ class PersistentRollout:
         are left as NaN.  Returns (O [F*n, d], LSE [F*n]).
         """
         s = self.sch
-        hk, hv, _ = self._history()
-        K_all = np.concatenate([hk, np.asarray(k_chunk, np.float64)])
-        V_all = np.concatenate([hv, np.asarray(v_chunk, np.float64)])
-        q = np.asarray(q_chunk, np.float64)
+        q = np.asarray(q_chunk)
+        base = self.chunk * s.F * s.nb
+        own_k, own_v = {}, {}
+        for b in range(s.F * s.nb):
+            a0, b0 = block_token_range(b, s.n, s.B)
+            own_k[base + b], own_v[base + b] = k_chunk[a0:b0], v_chunk[a0:b0]
         Tq = q.shape[0]
         o = np.full((Tq, self.d), np.nan)
         lse = np.full(Tq, np.nan)
@@ -330,19 +343,23 @@ class PersistentRollout:
             idx = [t for t in range(a, b) if want is None or t in want]
             if not idx:
                 continue
-            toks = np.concatenate([np.arange(*block_token_range(g, s.n, s.B))
-                                   for g in allowed])
-            mask = np.ones((len(idx), len(toks)), dtype=bool)
-            oo, ll = masked_attention(q[idx], K_all[toks], V_all[toks], mask, s.scale)
+            K = np.concatenate([np.asarray(own_k[g] if g in own_k else self.tok_k[g], np.float64)
+                                for g in allowed])
+            V = np.concatenate([np.asarray(own_v[g] if g in own_v else self.tok_v[g], np.float64)
+                                for g in allowed])
+            mask = np.ones((len(idx), K.shape[0]), dtype=bool)
+            oo, ll = masked_attention(np.asarray(q[idx], np.float64), K, V, mask, s.scale)
             o[idx], lse[idx] = oo, ll
         return o, lse
 
     def attend_dense(self, q_chunk, k_chunk, v_chunk, sel):
-        """Parity form: dense attention over the whole history + chunk with the block mask."""
+        """Parity form: dense attention over the whole history + chunk with the block mask
+        (needs keep_history=True)."""
+        if not self.keep_history:
+            raise ValueError("the dense form needs keep_history=True")
         s = self.sch
-        hk, hv, _ = self._history()
-        K_all = np.concatenate([hk, np.asarray(k_chunk, np.float64)])
-        V_all = np.concatenate([hv, np.asarray(v_chunk, np.float64)])
+        K_all = np.concatenate([np.asarray(x, np.float64) for x in self.hist_k + [k_chunk]])
+        V_all = np.concatenate([np.asarray(x, np.float64) for x in self.hist_v + [v_chunk]])
         q = np.asarray(q_chunk, np.float64)
         base = self.chunk * s.F * s.nb
         allowed = self.attended_blocks(sel)
@@ -353,21 +370,44 @@ class PersistentRollout:
         mask = mask_full[q0:q0 + q.shape[0]]
         return masked_attention(q, K_all, V_all, mask, s.scale)
 
-    def update(self, routed, k_chunk, v_chunk):
-        """Top-C memory update, then append the chunk to the history (advances the chunk)."""
+    def update_candidates(self, routed):
+        """(candidate ids, memory scores) the Top-C update of this chunk ranks."""
         s = self.sch
         E = s.evicted_blocks(self.chunk)
-        L = routed["L"]
-        col = {g: i for i, g in enumerate(L)}
+        col = {g: i for i, g in enumerate(routed["L"])}
         scores_E = routed["scores_L"][:, [col[g] for g in E]] if E else \
             np.zeros((routed["scores_L"].shape[0], 0))
+        return memory_scores(routed["P"], list(range(s.S)), routed["scores_P"], E, scores_E)
+
+    def update(self, routed, k_chunk, v_chunk, P_override=None):
+        """Top-C memory update, then append the chunk (advances the chunk index).
+
+        P_override: a persistent set chosen elsewhere among equally valid ones (when memory
+        scores tie within rounding); it must be the sinks plus candidates of this update.
+        """
+        s = self.sch
         sinks = list(range(s.S))
-        self.P = memory_update(routed["P"], sinks, routed["scores_P"], E, scores_E, s.C)
-        k_chunk = np.asarray(k_chunk, np.float64)
-        self.hist_k.append(k_chunk)
-        self.hist_v.append(np.asarray(v_chunk, np.float64))
-        self.hist_krep.append(mean_pool(k_chunk, s.n, s.B)[0])
+        cand, msum = self.update_candidates(routed)
+        if P_override is None:
+            self.P = sorted(sinks + top_ids(msum, cand, s.C - s.S))
+        else:
+            if not set(P_override) <= set(sinks) | set(cand) or len(P_override) > s.C:
+                raise ValueError("override is not sinks plus candidates")
+            self.P = sorted(int(g) for g in P_override)
+        base = self.chunk * s.F * s.nb
+        krep, _ = mean_pool(k_chunk, s.n, s.B)
+        for b in range(s.F * s.nb):
+            a0, b0 = block_token_range(b, s.n, s.B)
+            self.tok_k[base + b] = k_chunk[a0:b0]
+            self.tok_v[base + b] = v_chunk[a0:b0]
+            self.krep[base + b] = krep[b]
+        if self.keep_history:
+            self.hist_k.append(k_chunk)
+            self.hist_v.append(v_chunk)
         self.chunk += 1
+        live = set(self.P) | set(s.window_blocks(self.chunk))
+        for g in [g for g in self.tok_k if g not in live]:
+            del self.tok_k[g], self.tok_v[g], self.krep[g]
 
 
 # --------------------------------------------------------------------------------------
@@ -377,25 +417,38 @@ class PersistentRollout:
 # --------------------------------------------------------------------------------------
 
 
-def two_level_select(q_rep_row, k_block_rep, k_frame_rep, i: int, F: int, nb: int,
-                     top_frames: int, k_i: int, scale: float):
-    """Selected KV blocks (global ids, ascending) for one query block of chunk i (1-based).
-
-    Chunk 1 attends densely to its own frames.  For i >= 2 the history is frames
-    [0, F(i-1)); p(f) = scale <q_rep, k_frame_rep[f]> over history frames;
-    T = top_frames best history frames united with the forced frames {0, the latest
-    history frame, the chunk's own F frames}; the candidates are every block of the frames
-    in T; the result is their first k_i by (scale <q_rep, k_block_rep[g]> desc, g asc).
-    """
-    if i == 1:
-        return list(range(F * nb))
+def two_level_frames(q_rep_row, k_frame_rep, i: int, F: int, top_frames: int, scale: float):
+    """Frame stage for a query block of chunk i >= 2 (1-based): (history frames, their
+    scores, the chosen frame set T).  p(f) = scale <q_rep, k_frame_rep[f]> over history
+    frames f < F(i-1); T = the top_frames best (ties to the lower frame) united with the
+    forced frames {0, F(i-1)-1} and the chunk's own F frames."""
     hist = list(range(F * (i - 1)))
     p = coarse_scores(q_rep_row[None, :], k_frame_rep[hist], scale)[0]
     T = set(top_ids(p, hist, top_frames))
     T |= {0, F * (i - 1) - 1}
     T |= {F * (i - 1) + t for t in range(F)}
-    cand = [f * nb + j for f in sorted(T) for j in range(nb)]
+    return hist, p, sorted(T)
+
+
+def two_level_blocks(q_rep_row, k_block_rep, frames, nb: int, scale: float):
+    """Block stage: every block of the given frames and its score scale <q_rep, k_rep>."""
+    cand = [f * nb + j for f in sorted(frames) for j in range(nb)]
     o = coarse_scores(q_rep_row[None, :], k_block_rep[cand], scale)[0]
+    return cand, o
+
+
+def two_level_select(q_rep_row, k_block_rep, k_frame_rep, i: int, F: int, nb: int,
+                     top_frames: int, k_i: int, scale: float):
+    """Selected KV blocks (global ids, ascending) for one query block of chunk i (1-based).
+
+    Chunk 1 attends densely to its own frames.  For i >= 2: the frames of
+    two_level_frames, then the first min(k_i, candidates) of their blocks by (score desc,
+    id asc).
+    """
+    if i == 1:
+        return list(range(F * nb))
+    _, _, T = two_level_frames(q_rep_row, k_frame_rep, i, F, top_frames, scale)
+    cand, o = two_level_blocks(q_rep_row, k_block_rep, T, nb, scale)
     return top_ids(o, cand, min(k_i, len(cand)))
 
 

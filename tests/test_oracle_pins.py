@@ -251,7 +251,7 @@ def test_memory_update_brute_force_and_invariants(seed):
 def _rollout(wl, seed, heads=(0,), chunks=None):
     sch = orc.Schedule(wl.frame_tokens, wl.block, wl.chunk_frames, wl.window_frames,
                        wl.capacity, wl.sinks, wl.topk, wl.scale)
-    ros = {h: orc.PersistentRollout(sch, wl.head_dim) for h in heads}
+    ros = {h: orc.PersistentRollout(sch, wl.head_dim, keep_history=True) for h in heads}
     last = None
     for c in range(wl.measured_chunk + 1 if chunks is None else chunks):
         q, k, v = synth.chunk_qkv(wl, seed, c)
