@@ -1,0 +1,273 @@
+"""PBSA benchmark on one MI355X: ms per chunk of the persistent-mode hot path.
+
+One step = one chunk of one attention layer (one denoising pass) on the Wan2.1-1.3B-shaped
+5-second workload: 12 heads, head_dim 128, 1560-token frames, 3-frame chunks (4680
+queries), 21-frame history, 64-token blocks, capacity 64 (1 sink), window 6 frames,
+top-32:
+    pool(q) + pool(k) + score_topk + attn_fwd + memory_update
+on seeded synthetic bf16 inputs already resident in HBM.  The cache is bootstrapped by
+replaying the 7 history chunks; each timed step then feeds the measured chunk's tensors
+again, so the rollout keeps sliding with steady shapes.
+
+Prints one JSON line.  `roofline` is for the dominant kernel (attention forward, bf16 MFMA):
+achieved = algorithmic FLOP per launch (4 * head_dim per attended (query, key) pair)
+divided by that kernel's mean duration, measured with HIP events on the stream it runs on.
+`cpu_baseline` times the fp64 oracle's chunk step on this host for one head and scales it
+to the 12 heads of a chunk.
+
+  python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--train]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "PBSA ms/chunk + effective TFLOP/s & % MFMA/HBM roofline, 1 MI355X"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--train", action="store_true",
+                    help="also time the trainable two-level fwd+bwd clip (extra field)")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "attn_fwd_wan_5s_traffic.json"),
+                    help="HBM traffic per attention launch from rocprofv3 counters (if present)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import torch
+    from block_sparse_attention_pbsa_amd import ops, runtime, synth
+
+    wl = synth.WORKLOADS["wan_5s"]
+    seed = synth.SEEDS["wan_5s"]
+    shape = ops.Shape(wl.heads, wl.head_dim, wl.frame_tokens, wl.chunk_frames, wl.window_frames,
+                      wl.capacity, wl.sinks, wl.topk, wl.scale)
+    torch.cuda.set_device(0)
+
+    def dev(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).cuda().to(torch.bfloat16)
+
+    layer = runtime.PersistentLayer(shape)
+    layer.reset()
+    for c in range(wl.measured_chunk):
+        q, k, v = synth.chunk_qkv(wl, seed, c)
+        layer.step(dev(q), dev(k), dev(v), attend=False)
+    qn, kn, vn = synth.chunk_qkv(wl, seed, wl.measured_chunk)
+    q, k, v = dev(qn), dev(kn), dev(vn)
+    torch.cuda.synchronize()
+    print(f"bootstrapped {wl.measured_chunk} chunks", file=sys.stderr, flush=True)
+
+    def attended_flop():
+        """4*d * sum over (head, query token) of attended keys, from the current state."""
+        bid = layer.cache.block_id.cpu().numpy()
+        ln = layer.cache.len.cpu().numpy()
+        C, nb, n = wl.capacity, wl.nb, wl.frame_tokens
+        total = 0
+        layer.route(q)  # routing for the current state (outside any timed region)
+        sels = layer.sel.cpu().numpy()
+        for h in range(wl.heads):
+            p_keys = int(ln[h, :C][bid[h, :C] >= 0].sum())
+            ring = {int(g): int(l) for g, l in zip(bid[h, C:], ln[h, C:]) if g >= 0}
+            sel = sels[h]
+            for r in range(shape.nq):
+                keys = p_keys + wl.chunk_frames * n + sum(ring[int(g)] for g in sel[r] if g >= 0)
+                qlen = min(64, n - 64 * (r % nb))
+                total += qlen * keys
+        return 4 * wl.head_dim * total
+
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        layer.route(q)
+        if ev is not None:
+            ev[0].record(stream)
+        layer.attend(q, k, v)
+        if ev is not None:
+            ev[1].record(stream)
+        layer.update(k, v)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    flop_before = attended_flop()
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    ms_step = total_ms / args.steps
+    attn_ms = [a.elapsed_time(b) for a, b in evs]
+    attn_avg = float(np.mean(attn_ms))
+    flop_after = attended_flop()
+    flop = 0.5 * (flop_before + flop_after)
+    achieved = flop / (attn_avg * 1e-3) / 1e12
+
+    # per-op medians (separately timed, for the record)
+    def timed(fn, reps=20):
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts))
+
+    ops_ms = {
+        "pool_q": timed(lambda: ops.pbsa_pool(shape, q, wl.chunk_frames, layer.q_rep)),
+        "pool_k": timed(lambda: ops.pbsa_pool(shape, k, wl.chunk_frames, layer.k_rep)),
+        "score_topk": timed(lambda: ops.pbsa_score_topk(shape, layer.q_rep, layer.cache,
+                                                        layer.scores, layer.sel)),
+        "attn_fwd": timed(lambda: layer.attend(q, k, v)),
+    }
+    pool_bytes = shape.chunk_tokens * wl.heads * wl.head_dim * 2 + shape.nq * wl.heads * wl.head_dim * 4
+
+    traffic = None
+    if os.path.exists(args.traffic):
+        try:
+            traffic = json.load(open(args.traffic)).get("bytes_per_launch")
+        except (OSError, ValueError):
+            traffic = None
+
+    result = {
+        "metric": METRIC,
+        "value": round(ms_step, 4),
+        "unit": "ms/chunk",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "wan_5s: Wan2.1-1.3B-shaped 5 s rollout, one layer, one chunk",
+                   "heads": wl.heads, "head_dim": wl.head_dim, "frame_tokens": wl.frame_tokens,
+                   "chunk_frames": wl.chunk_frames, "query_tokens": shape.chunk_tokens,
+                   "history_frames": wl.history_frames, "block": wl.block,
+                   "capacity": wl.capacity, "sinks": wl.sinks,
+                   "window_frames": wl.window_frames, "topk": wl.topk},
+        "tflops_effective": round(flop / (ms_step * 1e-3) / 1e12, 2),
+        "attn_fwd_flop": int(flop),
+        "attn_fwd_ms": round(attn_avg, 4),
+        "ops_ms_median": {k_: round(v_, 4) for k_, v_ in ops_ms.items()},
+        "pool_q_gbs": round(pool_bytes / (ops_ms["pool_q"] * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "kernel": "attn_fwd_persistent_kernel<128>"},
+    }
+
+    if args.train:
+        result["train"] = bench_train(torch, ops, runtime, synth, dev, stream)
+
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(wl, seed)
+    print(json.dumps(result), flush=True)
+
+
+def bench_train(torch, ops, runtime, synth, dev, stream):
+    """Trainable two-level path on the 24-frame clip: fwd+bwd ms per clip (extra field)."""
+    wl = synth.WORKLOADS["wan_train"]
+    seed = synth.SEEDS["wan_train"]
+    shape = ops.Shape(wl.heads, wl.head_dim, wl.frame_tokens, wl.chunk_frames, scale=wl.scale)
+    qn, kn, vn = synth.clip_qkv(wl, seed)
+    q, k, v = dev(qn), dev(kn), dev(vn)
+    dout = dev(synth.clip_dout(wl, seed, qn.shape[0]))
+    ks = runtime.cag_budgets(synth.clip_alphas(wl, seed), wl.topk, wl.clip_chunks)
+    clip = runtime.TwoLevelClip(shape, wl.clip_chunks, wl.top_frames,
+                                max(max(ks), wl.chunk_frames * wl.nb))
+    clip.select(q, k, ks)
+    torch.cuda.synchronize()
+    sel, nsel = clip.sel.cpu().numpy(), clip.nsel.cpu().numpy()
+    n, nb = wl.frame_tokens, wl.nb
+    keys = 0
+    for h in range(wl.heads):
+        for r in range(nsel.shape[1]):
+            qlen = min(64, n - 64 * (r % nb))
+            keys += qlen * sum(min(64, n - 64 * (int(g) % nb)) for g in sel[h, r, :nsel[h, r]])
+    fwd_flop = 4 * wl.head_dim * keys
+    bwd_flop = 8 * wl.head_dim * keys
+
+    def run(fn, reps=10):
+        for _ in range(3):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    sel_ms = run(lambda: clip.select(q, k, ks))
+    fwd_ms = run(lambda: clip.forward(q, k, v))
+    bwd_ms = run(lambda: clip.backward(q, k, v, dout))
+    return {"workload": "wan_train: 24-frame clip, 8 chunks, two-level top-8 frames",
+            "select_ms": round(sel_ms, 4), "fwd_ms": round(fwd_ms, 4),
+            "bwd_ms": round(bwd_ms, 4),
+            "fwd_tflops": round(fwd_flop / (fwd_ms * 1e-3) / 1e12, 2),
+            "bwd_tflops": round(bwd_flop / (bwd_ms * 1e-3) / 1e12, 2),
+            "fwd_flop": int(fwd_flop), "bwd_flop": int(bwd_flop)}
+
+
+def cpu_baseline(wl, seed):
+    """The fp64 oracle's chunk step (select, gathered attention, update) for ONE head of the
+    measured chunk, on this host, scaled x12 heads to ms per chunk."""
+    import oracle as orc
+    from block_sparse_attention_pbsa_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - reporting only
+        threads = os.cpu_count() or 1
+    sch = orc.Schedule(wl.frame_tokens, wl.block, wl.chunk_frames, wl.window_frames,
+                       wl.capacity, wl.sinks, wl.topk, wl.scale)
+    ro = orc.PersistentRollout(sch, wl.head_dim)
+    h = 0
+    for c in range(wl.measured_chunk):
+        q, k, v = synth.chunk_qkv(wl, seed, c)
+        ro.update(ro.select(q[:, h]), k[:, h], v[:, h])
+    q, k, v = synth.chunk_qkv(wl, seed, wl.measured_chunk)
+    qh, kh, vh = q[:, h].copy(), k[:, h].copy(), v[:, h].copy()
+    t = time.perf_counter()
+    rt = ro.select(qh)
+    ro.attend(qh, kh, vh, rt["sel"])
+    ro.update(rt, kh, vh)
+    sec = time.perf_counter() - t
+    return {"value": round(sec * 1e3 * wl.heads, 1), "unit": "ms/chunk", "cores": threads,
+            "kind": "oracle",
+            "sample": "one head of the wan_5s measured chunk (pool, score, route, gathered "
+                      "fp64 attention over all 4680 queries, Top-C update), scaled x12 heads"}
+
+
+if __name__ == "__main__":
+    main()
