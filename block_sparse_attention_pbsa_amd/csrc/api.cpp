@@ -2,6 +2,7 @@
 // Every check runs on the host before anything is enqueued.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -63,6 +64,12 @@ pbsa_status check_dims(const pbsa_dims* d, int mode) {
                   static_cast<long long>(slots), static_cast<long long>(kMaxSlots));
     if (d->capacity - d->sinks > 1024)
       return fail(PBSA_ERR_UNSUPPORTED, "capacity - sinks must be <= 1024");
+    if (static_cast<int64_t>(d->window_frames) * nb > 1024)
+      return fail(PBSA_ERR_UNSUPPORTED, "window blocks must be <= 1024");
+    // LDS of the memory-update selection: block tables + candidate arrays
+    const int64_t ncand = static_cast<int64_t>(d->capacity - d->sinks) + int64_t{d->chunk_frames} * nb;
+    if (ncand * 16 + slots * 8 > 56 * 1024)
+      return fail(PBSA_ERR_UNSUPPORTED, "capacity/window too large for the memory update");
   } else if (mode != 1) {
     return fail(PBSA_ERR_SHAPE, "mode must be 0 (persistent) or 1 (two-level)");
   }
@@ -230,9 +237,13 @@ pbsa_status pbsa_score_topk_2lvl(const pbsa_dims* dims, int32_t chunks, int32_t 
   for (int i = 1; i < chunks; ++i)
     if (k_per_chunk[i] < 1 || k_per_chunk[i] > max_sel)
       return fail(PBSA_ERR_SHAPE, "k_per_chunk[%d] = %d outside [1, max_sel]", i, k_per_chunk[i]);
-  const int64_t cand = static_cast<int64_t>(chunks) * dims->chunk_frames * nb;
-  if (cand * 12 + static_cast<int64_t>(chunks) * dims->chunk_frames * 8 > 60 * 1024)
-    return fail(PBSA_ERR_UNSUPPORTED, "clip too long for the selection kernel's LDS");
+  {
+    const int64_t frames_total = static_cast<int64_t>(chunks) * dims->chunk_frames;
+    const int64_t fr_max = std::min<int64_t>(int64_t{top_frames} + 2 + dims->chunk_frames, frames_total);
+    if (fr_max * nb > 1024 || frames_total > 256)
+      return fail(PBSA_ERR_UNSUPPORTED,
+                  "two-level selection supports <= 256 clip frames and <= 1024 candidate blocks");
+  }
   return hip_status(pbsa::launch_score_topk_2lvl(*dims, chunks, top_frames, k_per_chunk, q_rep,
                                                  block_rep, frame_rep, max_sel, sel, nsel,
                                                  stream_of(stream)),

@@ -18,24 +18,28 @@ struct Lds {
   static constexpr int COLS = D * CS;
 };
 
-// A 64-row x D-channel bf16 tile staged through registers by a 128-thread workgroup.
-// Thread t owns channels [8*(t % CH), +8) of rows 4*KG*p + 4*(t / CH) + i (i < 4): each
-// load instruction reads whole 256-byte rows, and each thread holds 4 consecutive rows of
-// one channel chunk, which it can write row-major or transposed.
-template <int D>
+// An R-row x D-channel bf16 tile (R = 64 or 32) staged through registers by NT threads.
+// Thread t owns channels [8*(t % CH), +8) of RG consecutive rows RG*KG*q + RG*(t / CH) + i
+// (i < RG): each load instruction reads whole 2*D-byte rows, and each thread holds RG
+// consecutive rows of one channel chunk, which it can write row-major or transposed.
+template <int D, int NT = 128, int R = kBlock>
 struct Tile {
-  static constexpr int CH = D / 8;
-  static constexpr int KG = 128 / CH;
-  static constexpr int NP = kBlock / (4 * KG);
-  u32x4 r[NP][4];
+  static constexpr int CH = D / 8;                       // 16-byte chunks per row
+  static constexpr int CPT = R * CH / NT;                // chunks per thread
+  static constexpr int RG = CPT < 4 ? CPT : 4;           // consecutive rows per group
+  static constexpr int NP = CPT / RG;                    // row groups per thread
+  static constexpr int KG = NT / CH;                     // row groups per pass
+  static_assert(CPT >= 1 && RG * KG * NP == R, "unsupported tile split");
+  u32x4 r[NP][RG];
 
+  // rows [0, len) from p (row stride `stride` elements); rows past len read as zero
   __device__ __forceinline__ void load(const uint16_t* p, int64_t stride, int len, int t) {
     const int cc = t % CH, kg = t / CH;
 #pragma unroll
     for (int q = 0; q < NP; ++q)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 4 * KG * q + 4 * kg + i;
+      for (int i = 0; i < RG; ++i) {
+        const int row = RG * KG * q + RG * kg + i;
         r[q][i] = row < len ? *reinterpret_cast<const u32x4*>(p + row * stride + 8 * cc)
                             : u32x4{0, 0, 0, 0};
       }
@@ -46,29 +50,33 @@ struct Tile {
 #pragma unroll
     for (int q = 0; q < NP; ++q)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 4 * KG * q + 4 * kg + i;
+      for (int i = 0; i < RG; ++i) {
+        const int row = RG * KG * q + RG * kg + i;
         *reinterpret_cast<u32x4*>(lds + row * Lds<D>::RS + 8 * cc) = r[q][i];
       }
   }
 
+  __device__ __forceinline__ static uint32_t pair(uint32_t x, uint32_t y, int odd) {
+    return odd ? (x >> 16) | (y & 0xffff0000u) : (x & 0xffffu) | (y << 16);
+  }
+
+  // channel-major copy [D][R + 4] (used where a transposed operand must also be written)
   __device__ __forceinline__ void store_cols(uint16_t* lds, int t) const {
+    static_assert(R == kBlock, "column stores are laid out for 64-row tiles");
     const int cc = t % CH, kg = t / CH;
 #pragma unroll
     for (int q = 0; q < NP; ++q) {
-      const int row0 = 4 * KG * q + 4 * kg;
+      const int row0 = RG * KG * q + RG * kg;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int w = e >> 1;
-        uint32_t a, b;
-        if (e & 1) {
-          a = (r[q][0][w] >> 16) | (r[q][1][w] & 0xffff0000u);
-          b = (r[q][2][w] >> 16) | (r[q][3][w] & 0xffff0000u);
+        const int w = e >> 1, odd = e & 1;
+        uint16_t* dst = lds + (8 * cc + e) * Lds<D>::CS + row0;
+        if constexpr (RG == 4) {
+          *reinterpret_cast<u32x2*>(dst) =
+              u32x2{pair(r[q][0][w], r[q][1][w], odd), pair(r[q][2][w], r[q][3][w], odd)};
         } else {
-          a = (r[q][0][w] & 0xffffu) | (r[q][1][w] << 16);
-          b = (r[q][2][w] & 0xffffu) | (r[q][3][w] << 16);
+          *reinterpret_cast<uint32_t*>(dst) = pair(r[q][0][w], r[q][1][w], odd);
         }
-        *reinterpret_cast<u32x2*>(lds + (8 * cc + e) * Lds<D>::CS + row0) = u32x2{a, b};
       }
     }
   }
@@ -91,6 +99,28 @@ __device__ __forceinline__ u32x4 rd_cols(const uint16_t* lds, int dt, int t4, in
   const u32x2 hi = *reinterpret_cast<const u32x2*>(p + 8);
   return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
+// Channel-major view of a ROW-major tile through gfx950's transposing LDS read
+// (ds_read_b64_tr_b16).  Within each 16-lane group the instruction returns to lane i the
+// element (4e + i/4, i%4) of the 16 x 4 matrix formed by the lanes' 64-bit reads, e = 0..3.
+// Lane j = 4e + m of a group therefore addresses row K0 + e, channels D0 + 4m .. +3, and
+// lane i receives rows K0..K0+3 of channel D0 + i.  Same operand as rd_cols on a
+// channel-major copy: channel row 32*dt + c32, rows 16*t4 + 4*h2 + [0,4) then +8.
+typedef short s16x4_ __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_ lds_s16x4;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+template <int D>
+__device__ __forceinline__ u32x4 rd_rows_tr(const uint16_t* lds, int dt, int t4, int l) {
+  const int g = l >> 4, i = l & 15;
+  const int d0 = 32 * dt + 16 * (g & 1);
+  const int k0 = 16 * t4 + 4 * (g >> 1);
+  const int off = (k0 + (i >> 2)) * Lds<D>::RS + d0 + 4 * (i & 3);
+  lds_u16* p = (lds_u16*)(lds) + off;  // generic -> LDS address space
+  const s16x4_ lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+  const s16x4_ hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 8 * Lds<D>::RS));
+  const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+  return u32x4{a[0], a[1], b[0], b[1]};
+}
+
 // B/A operand from two 32-row accumulator tiles: k-step t4 (16 rows) packed to bf16 in the
 // order rd_cols expects.
 __device__ __forceinline__ u32x4 pack_step(const f32x16* acc, int t4) {

@@ -28,8 +28,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats to packed bf16 (round to nearest even) with gfx950's v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
 // 32x32x16 bf16 MFMA, fp32 accumulate.  Operand layout (wave64): lane l supplies row/col
@@ -45,6 +49,60 @@ __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
   return x;
+}
+
+// Sort key for "score descending, id ascending": order-preserving float bits in the high
+// word, ~id in the low word.  NaN scores order as -inf.  Key 0 sorts below every key.
+__device__ __forceinline__ uint64_t rank_key(float score, int id) {
+  if (score != score) score = -INFINITY;
+  const uint32_t b = __float_as_uint(score);
+  const uint32_t o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return (static_cast<uint64_t>(o) << 32) | static_cast<uint32_t>(~static_cast<uint32_t>(id));
+}
+__device__ __forceinline__ int rank_key_id(uint64_t k) {
+  return static_cast<int>(~static_cast<uint32_t>(k & 0xffffffffu));
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), m, 64);
+  const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), m, 64);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Bitonic sort, descending, of the 64*E keys held by one wave: element i = 64*e + lane is
+// v[e] of that lane.  Partners closer than 64 are exchanged across lanes, farther ones
+// inside a lane's registers.
+template <int E>
+__device__ __forceinline__ void wave_sort_desc(uint64_t (&v)[E], int lane) {
+  constexpr int N = 64 * E;
+#pragma unroll
+  for (int k = 2; k <= N; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j >= 64) {
+        const int je = j >> 6;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          if (e & je) continue;
+          const int ep = e | je;
+          const bool desc = ((64 * e + lane) & k) == 0;
+          const uint64_t a = v[e], b = v[ep];
+          const uint64_t hi = a > b ? a : b, lo = a > b ? b : a;
+          v[e] = desc ? hi : lo;
+          v[ep] = desc ? lo : hi;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const uint64_t o = shfl_xor_u64(v[e], j);
+          const bool lower = (lane & j) == 0;
+          const bool desc = ((64 * e + lane) & k) == 0;
+          const uint64_t hi = v[e] > o ? v[e] : o, lo = v[e] > o ? o : v[e];
+          v[e] = (lower == desc) ? hi : lo;
+        }
+      }
+    }
+  }
 }
 
 // Ceil division.

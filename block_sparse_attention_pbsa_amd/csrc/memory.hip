@@ -38,16 +38,20 @@ __device__ __forceinline__ bool ahead(float sa, int ia, float sb, int ib) {
 __device__ __forceinline__ float order_key(float x) { return x != x ? -INFINITY : x; }
 }  // namespace
 
-// grid H, 256 threads.  Dynamic LDS: 4 arrays of ncand_max = (C - S) + F*nb entries.
+// grid H, 256 threads.  Dynamic LDS: the head's block_id and len tables (2 * slots ints)
+// followed by 4 arrays of ncand_max = (C - S) + F*nb candidate entries.  Serial steps
+// (ordered enumeration, slot assignment) run on one thread over LDS only.
 __global__ void __launch_bounds__(256) memory_select_kernel(MemArgs a) {
   extern __shared__ int mem_smem[];
   const int h = blockIdx.x, t = threadIdx.x;
   const int ncand_max = (a.C - a.S) + a.F * a.nb;
-  int* cslot = mem_smem;                       // candidate's slot
+  int* sbid = mem_smem;                        // [slots]
+  int* slen = sbid + a.slots;                  // [slots]
+  int* cslot = slen + a.slots;                 // candidate's slot
   int* cid = cslot + ncand_max;                // candidate's block id
   float* cm = reinterpret_cast<float*>(cid + ncand_max);  // memory score
   int* ckeep = reinterpret_cast<int*>(cm + ncand_max);    // kept?
-  __shared__ int nP, nE, nfree, npromo;
+  __shared__ int nP, nE;
   __shared__ int free_slots[1024];
   int32_t* bid = a.bid + static_cast<int64_t>(h) * a.slots;
   int32_t* blen = a.blen + static_cast<int64_t>(h) * a.slots;
@@ -63,13 +67,18 @@ __global__ void __launch_bounds__(256) memory_select_kernel(MemArgs a) {
     }
     return;
   }
+  for (int s = t; s < a.slots; s += 256) {
+    sbid[s] = bid[s];
+    slen[s] = blen[s];
+  }
+  __syncthreads();
   if (t == 0) {
     // enumerate candidates in a fixed order: persistent non-sink slots, then leaving blocks
     int m = 0;
     for (int s = a.S; s < a.C; ++s)
-      if (bid[s] >= a.S) {
+      if (sbid[s] >= a.S) {
         cslot[m] = s;
-        cid[m] = bid[s];
+        cid[m] = sbid[s];
         ++m;
       }
     nP = m;
@@ -77,9 +86,9 @@ __global__ void __launch_bounds__(256) memory_select_kernel(MemArgs a) {
       const int64_t f_new = hF + b / a.nb;  // chunk frame landing in this window slot
       if (f_new < a.W) continue;           // slot was empty: nothing leaves
       const int s = a.C + static_cast<int>(f_new % a.W) * a.nb + b % a.nb;
-      if (bid[s] >= a.S) {
+      if (sbid[s] >= a.S) {
         cslot[m] = s;
-        cid[m] = bid[s];
+        cid[m] = sbid[s];
         ++m;
       }
     }
@@ -116,7 +125,6 @@ __global__ void __launch_bounds__(256) memory_select_kernel(MemArgs a) {
       }
       if (!occupied_kept) free_slots[nf++] = s;
     }
-    nfree = nf;
     // promoted leaving blocks in ascending id order take free slots in ascending order
     int np = 0;
     for (;;) {
@@ -131,14 +139,18 @@ __global__ void __launch_bounds__(256) memory_select_kernel(MemArgs a) {
       const int rf = b_rel / a.nb, j = b_rel % a.nb;
       const int fb = static_cast<int>(((rf - hF % a.W) % a.W + a.W) % a.W);
       dst[fb * a.nb + j] = s;
-      bid[s] = cid[best];
-      blen[s] = blen[cslot[best]];
+      sbid[s] = cid[best];
+      slen[s] = slen[cslot[best]];
     }
-    npromo = np;
     for (int k = np; k < nf; ++k) {
-      bid[free_slots[k]] = -1;
-      blen[free_slots[k]] = 0;
+      sbid[free_slots[k]] = -1;
+      slen[free_slots[k]] = 0;
     }
+  }
+  __syncthreads();
+  for (int s = a.S + t; s < a.C; s += 256) {
+    bid[s] = sbid[s];
+    blen[s] = slen[s];
   }
 }
 
@@ -229,7 +241,7 @@ hipError_t launch_memory_update(const pbsa_dims& d, const float* scores, const p
   a.nq = d.chunk_frames * nb;
   a.chunk = c.chunk_index;
   const int ncand_max = (d.capacity - d.sinks) + d.chunk_frames * nb;
-  const size_t lds = static_cast<size_t>(ncand_max) * 16;
+  const size_t lds = static_cast<size_t>(ncand_max) * 16 + static_cast<size_t>(a.slots) * 8;
   hipLaunchKernelGGL(memory_select_kernel, dim3(d.heads), dim3(256), lds, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

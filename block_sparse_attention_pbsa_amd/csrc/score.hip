@@ -10,8 +10,8 @@
 //
 // Latency-bound (~1e8 FLOP per chunk): scores are fp32 FMA dot products on the vector ALUs,
 // which keeps them within ~1e-7 of the exact value, so selections agree with an exact
-// reference wherever score gaps are larger.  Top-K is a rank count per candidate in LDS:
-// rank(j) = #{i : i ahead of j in (score desc, id asc)}; NaN scores order as -inf.
+// reference wherever score gaps are larger.  Top-K is an in-register bitonic sort of
+// 64-bit (score, ~id) keys across one wave; NaN scores order as -inf.
 #include "common.h"
 #include "launch.h"
 
@@ -43,79 +43,91 @@ __device__ __forceinline__ float dot_rep(const float* __restrict__ q_lds,
 
 }  // namespace
 
-// grid (Nq, H), 256 threads.  Dynamic LDS: slots floats + slots ints + slots ints.
-template <int D>
-__global__ void __launch_bounds__(256)
+// grid (Nq, H), one wave per query block.  Lane l scores persistent slots l, l + 64, ...
+// and window slots C + l + 64e (e < E), keeping the window candidates' sort keys in
+// registers; one bitonic sort picks the top K, a second orders them by id.
+template <int D, int E>
+__global__ void __launch_bounds__(64)
     score_topk_kernel(const float* __restrict__ q_rep, const float* __restrict__ rep,
                       const int32_t* __restrict__ block_id, int slots, int C, int S, int K,
-                      int nq, float scale, float* __restrict__ scores, int32_t* __restrict__ sel) {
-  extern __shared__ float smem[];
+                      int nq, float scale, float* __restrict__ scores,
+                      int32_t* __restrict__ sel) {
   __shared__ float q_lds[D];
-  __shared__ int n_win;
-  float* sc = smem;                                        // [slots]
-  int* ids = reinterpret_cast<int*>(sc + slots);           // [slots]
-  int* keep = ids + slots;                                 // [slots]
-  const int r = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+  const int r = blockIdx.x, h = blockIdx.y, l = threadIdx.x;
   const float* qr = q_rep + (static_cast<int64_t>(h) * nq + r) * D;
-  for (int c = t; c < D; c += 256) q_lds[c] = qr[c];
-  if (t == 0) n_win = 0;
+  for (int c = l; c < D; c += 64) q_lds[c] = qr[c];
   __syncthreads();
   const int32_t* bid = block_id + static_cast<int64_t>(h) * slots;
   const float* rp = rep + static_cast<int64_t>(h) * slots * D;
   float* srow = scores + (static_cast<int64_t>(h) * nq + r) * slots;
-  int my_win = 0;
-  for (int s = t; s < slots; s += 256) {
+  for (int s = l; s < C; s += 64) {
     const int id = bid[s];
-    float v = -INFINITY;
-    if (id >= 0) v = scale * dot_rep<D>(q_lds, rp + static_cast<int64_t>(s) * D);
-    srow[s] = v;
-    sc[s] = order_key(v);
-    // window candidates: occupied ring slots holding non-sink blocks
-    const bool cand = s >= C && id >= S;
-    ids[s] = cand ? id : -1;
-    my_win += cand;
+    srow[s] = id >= 0 ? scale * dot_rep<D>(q_lds, rp + static_cast<int64_t>(s) * D) : -INFINITY;
   }
-  atomicAdd(&n_win, my_win);
-  __syncthreads();
-  const int nsel = K < n_win ? K : n_win;
-  for (int s = C + t; s < slots; s += 256) {
-    int k = 0;
-    const int id = ids[s];
-    if (id >= 0) {
-      const float v = sc[s];
-      int rank = 0;
-      for (int u = C; u < slots; ++u) rank += (ids[u] >= 0) && ahead(sc[u], ids[u], v, id);
-      k = rank < nsel;
+  const int nwin = slots - C;
+  uint64_t key[E];
+  int nvalid = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int w = l + 64 * e;
+    key[e] = 0;
+    if (w < nwin) {
+      const int s = C + w;
+      const int id = bid[s];
+      float v = -INFINITY;
+      if (id >= 0) v = scale * dot_rep<D>(q_lds, rp + static_cast<int64_t>(s) * D);
+      srow[s] = v;
+      // window candidates: occupied ring slots holding non-sink blocks
+      if (id >= S) {
+        key[e] = rank_key(v, id);
+        ++nvalid;
+      }
     }
-    keep[s] = k;
   }
-  __syncthreads();
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) nvalid += __shfl_xor(nvalid, o, 64);
+  const int nsel = K < nvalid ? K : nvalid;
+  wave_sort_desc<E>(key, l);
+  // the first nsel keys are the selection; order them by id (ascending = ~id descending)
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = 64 * e + l;
+    key[e] = i < nsel ? static_cast<uint64_t>(~static_cast<uint32_t>(rank_key_id(key[e]))) : 0;
+  }
+  wave_sort_desc<E>(key, l);
   int32_t* out = sel + (static_cast<int64_t>(h) * nq + r) * K;
-  for (int s = C + t; s < slots; s += 256) {
-    if (keep[s]) {
-      const int id = ids[s];
-      int pos = 0;
-      for (int u = C; u < slots; ++u) pos += keep[u] && ids[u] < id;
-      out[pos] = id;
-    }
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = 64 * e + l;
+    if (i < nsel) out[i] = static_cast<int>(~static_cast<uint32_t>(key[e]));
   }
-  for (int p = nsel + t; p < K; p += 256) out[p] = -1;
+  for (int p = nsel + l; p < K; p += 64) out[p] = -1;
+}
+
+template <int D>
+static hipError_t launch_score_d(const pbsa_dims& d, const float* q_rep, const pbsa_cache& c,
+                                 float* scores, int32_t* sel, hipStream_t s) {
+  const int nb = nb_of(d);
+  const int nq = d.chunk_frames * nb;
+  const int slots = static_cast<int>(slots_of(d));
+  const int nwin = slots - d.capacity;
+  dim3 grid(nq, d.heads);
+#define PBSA_SCORE_E(EE)                                                                    \
+  hipLaunchKernelGGL((score_topk_kernel<D, EE>), grid, dim3(64), 0, s, q_rep, c.rep,         \
+                     c.block_id, slots, d.capacity, d.sinks, d.topk, nq, d.scale, scores, sel)
+  if (nwin <= 64) PBSA_SCORE_E(1);
+  else if (nwin <= 128) PBSA_SCORE_E(2);
+  else if (nwin <= 256) PBSA_SCORE_E(4);
+  else if (nwin <= 512) PBSA_SCORE_E(8);
+  else PBSA_SCORE_E(16);  // window blocks <= 1024 (checked at the boundary)
+#undef PBSA_SCORE_E
+  return hipGetLastError();
 }
 
 hipError_t launch_score_topk(const pbsa_dims& d, const float* q_rep, const pbsa_cache& c,
                              float* scores, int32_t* sel, hipStream_t s) {
-  const int nb = nb_of(d);
-  const int nq = d.chunk_frames * nb;
-  const int slots = static_cast<int>(slots_of(d));
-  const size_t lds = static_cast<size_t>(slots) * 12;
-  dim3 grid(nq, d.heads);
-  if (d.head_dim == 128)
-    hipLaunchKernelGGL(score_topk_kernel<128>, grid, dim3(256), lds, s, q_rep, c.rep, c.block_id,
-                       slots, d.capacity, d.sinks, d.topk, nq, d.scale, scores, sel);
-  else
-    hipLaunchKernelGGL(score_topk_kernel<64>, grid, dim3(256), lds, s, q_rep, c.rep, c.block_id,
-                       slots, d.capacity, d.sinks, d.topk, nq, d.scale, scores, sel);
-  return hipGetLastError();
+  return d.head_dim == 128 ? launch_score_d<128>(d, q_rep, c, scores, sel, s)
+                           : launch_score_d<64>(d, q_rep, c, scores, sel, s);
 }
 
 // ---------------------------------------------------------------- two-level selection
@@ -125,113 +137,145 @@ struct ChunkBudgets {
   int32_t k[kMaxChunks];
 };
 
-// grid (Nq_total, H), 256 threads.  Dynamic LDS sized for the largest candidate set:
-// frames floats + frames ints (frame stage), cand floats + cand ints + cand ints.
-template <int D>
-__global__ void __launch_bounds__(256)
+// grid (Nq_total, H), one wave per query block.  Frame stage: lane l scores history frames
+// l + 64e; a bitonic sort picks the top_frames; chosen and forced frames are flagged in LDS.
+// Block stage: candidates (every block of the flagged frames, ascending) are scored into
+// sort keys, sorted, the first k kept and re-sorted by id.
+template <int D, int EF, int E>
+__global__ void __launch_bounds__(64)
     score_topk_2lvl_kernel(const float* __restrict__ q_rep, const float* __restrict__ block_rep,
                            const float* __restrict__ frame_rep, int F, int nb, int chunks,
                            int top_frames, ChunkBudgets budgets, float scale, int max_sel,
                            int32_t* __restrict__ sel, int32_t* __restrict__ nsel_out) {
-  extern __shared__ float smem[];
+  extern __shared__ int fflag[];  // [chunks * F]: frame chosen?  then the chosen list
   __shared__ float q_lds[D];
-  __shared__ int n_frames_sel;
-  const int r = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+  const int r = blockIdx.x, h = blockIdx.y, l = threadIdx.x;
   const int nq = chunks * F * nb;
   const int frames_total = chunks * F;
   const int i = r / (F * nb) + 1;  // 1-based chunk of this query block
   int32_t* out = sel + (static_cast<int64_t>(h) * nq + r) * max_sel;
   if (i == 1) {
-    for (int g = t; g < F * nb; g += 256) out[g] = g;
-    if (t == 0) nsel_out[static_cast<int64_t>(h) * nq + r] = F * nb;
+    for (int g = l; g < F * nb; g += 64) out[g] = g;
+    if (l == 0) nsel_out[static_cast<int64_t>(h) * nq + r] = F * nb;
     return;
   }
   const float* qr = q_rep + (static_cast<int64_t>(h) * nq + r) * D;
-  for (int c = t; c < D; c += 256) q_lds[c] = qr[c];
+  for (int c = l; c < D; c += 64) q_lds[c] = qr[c];
   const int hist = F * (i - 1);
   const int vis = hist + F;  // frames this chunk can see
-  float* fsc = smem;                                   // [frames_total]
-  int* fsel = reinterpret_cast<int*>(fsc + frames_total);  // [frames_total]
-  float* csc = reinterpret_cast<float*>(fsel + frames_total);  // [frames_total*nb]
-  int* cid = reinterpret_cast<int*>(csc + frames_total * nb);   // [frames_total*nb]
-  int* ckeep = cid + frames_total * nb;                         // [frames_total*nb]
+  int* flist = fflag + frames_total;
+  // forced: sink frame, latest history frame, the chunk's own frames
+  for (int f = l; f < vis; f += 64) fflag[f] = (f == 0 || f >= hist - 1);
   __syncthreads();
   const float* fr = frame_rep + static_cast<int64_t>(h) * frames_total * D;
-  for (int f = t; f < hist; f += 256) fsc[f] = order_key(scale * dot_rep<D>(q_lds, fr + static_cast<int64_t>(f) * D));
-  __syncthreads();
-  for (int f = t; f < vis; f += 256) {
-    int chosen;
-    if (f >= hist - 1 || f == 0) {
-      chosen = 1;  // forced: sink frame, latest history frame, the chunk's own frames
-    } else {
-      int rank = 0;
-      const float v = fsc[f];
-      for (int u = 0; u < hist; ++u) rank += ahead(fsc[u], u, v, f);
-      chosen = rank < top_frames;
-    }
-    fsel[f] = chosen;
+  uint64_t fk[EF];
+#pragma unroll
+  for (int e = 0; e < EF; ++e) {
+    const int f = l + 64 * e;
+    fk[e] = f < hist ? rank_key(scale * dot_rep<D>(q_lds, fr + static_cast<int64_t>(f) * D), f) : 0;
   }
-  // frame 0 and the latest history frame may also have been chosen by score; a frame is in
-  // the set either way.
+  wave_sort_desc<EF>(fk, l);
+  const int ntop = top_frames < hist ? top_frames : hist;
+#pragma unroll
+  for (int e = 0; e < EF; ++e)
+    if (64 * e + l < ntop) fflag[rank_key_id(fk[e])] = 1;
   __syncthreads();
-  if (t == 0) {
-    // list the chosen frames in ascending order (at most a few hundred frames)
-    int m = 0;
-    for (int f = 0; f < vis; ++f)
-      if (fsel[f]) fsel[m++] = f;
-    n_frames_sel = m;
+  // chosen frames in ascending order (ballot compaction over the visible frames)
+  int nfr = 0;
+  for (int f0 = 0; f0 < vis; f0 += 64) {
+    const int f = f0 + l;
+    const bool on = f < vis && fflag[f];
+    const unsigned long long m = __ballot(on);
+    if (on) flist[nfr + __popcll(m & ((1ull << l) - 1ull))] = f;
+    nfr += __popcll(m);
   }
   __syncthreads();
-  const int ncand = n_frames_sel * nb;
+  const int ncand = nfr * nb;
   const float* br = block_rep + static_cast<int64_t>(h) * nq * D;
-  for (int c = t; c < ncand; c += 256) {
-    const int g = fsel[c / nb] * nb + (c % nb);
-    cid[c] = g;
-    csc[c] = order_key(scale * dot_rep<D>(q_lds, br + static_cast<int64_t>(g) * D));
+  uint64_t key[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int c = l + 64 * e;
+    key[e] = 0;
+    if (c < ncand) {
+      const int g = flist[c / nb] * nb + (c % nb);
+      key[e] = rank_key(scale * dot_rep<D>(q_lds, br + static_cast<int64_t>(g) * D), g);
+    }
   }
-  __syncthreads();
   int k = budgets.k[i - 1];
   if (k > ncand) k = ncand;
   if (k < 1) k = 1;
-  for (int c = t; c < ncand; c += 256) {
-    const float v = csc[c];
-    const int g = cid[c];
-    int rank = 0;
-    for (int u = 0; u < ncand; ++u) rank += ahead(csc[u], cid[u], v, g);
-    ckeep[c] = rank < k;
+  wave_sort_desc<E>(key, l);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int idx = 64 * e + l;
+    key[e] = idx < k ? static_cast<uint64_t>(~static_cast<uint32_t>(rank_key_id(key[e]))) : 0;
   }
-  __syncthreads();
-  // candidates are listed in ascending id order, so a prefix count gives the position
-  for (int c = t; c < ncand; c += 256) {
-    if (ckeep[c]) {
-      int pos = 0;
-      for (int u = 0; u < c; ++u) pos += ckeep[u];
-      out[pos] = cid[c];
-    }
+  wave_sort_desc<E>(key, l);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int idx = 64 * e + l;
+    if (idx < k) out[idx] = static_cast<int>(~static_cast<uint32_t>(key[e]));
   }
-  if (t == 0) nsel_out[static_cast<int64_t>(h) * nq + r] = k;
+  if (l == 0) nsel_out[static_cast<int64_t>(h) * nq + r] = k;
+}
+
+template <int D, int EF>
+static hipError_t launch_2lvl_e(int E, dim3 grid, size_t lds, hipStream_t s, const float* q_rep,
+                                const float* block_rep, const float* frame_rep, int F, int nb,
+                                int chunks, int top_frames, const ChunkBudgets& b, float scale,
+                                int max_sel, int32_t* sel, int32_t* nsel) {
+#define PBSA_2LVL_E(EE)                                                                      \
+  hipLaunchKernelGGL((score_topk_2lvl_kernel<D, EF, EE>), grid, dim3(64), lds, s, q_rep,       \
+                     block_rep, frame_rep, F, nb, chunks, top_frames, b, scale, max_sel, sel, \
+                     nsel)
+  if (E <= 1) PBSA_2LVL_E(1);
+  else if (E <= 2) PBSA_2LVL_E(2);
+  else if (E <= 4) PBSA_2LVL_E(4);
+  else if (E <= 8) PBSA_2LVL_E(8);
+  else PBSA_2LVL_E(16);
+#undef PBSA_2LVL_E
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_2lvl_d(const pbsa_dims& d, int chunks, int top_frames,
+                                const ChunkBudgets& b, const float* q_rep,
+                                const float* block_rep, const float* frame_rep, int max_sel,
+                                int32_t* sel, int32_t* nsel, hipStream_t s) {
+  const int nb = nb_of(d);
+  const int F = d.chunk_frames;
+  const int nq = chunks * F * nb;
+  const int frames_total = chunks * F;
+  // candidates: at most (top_frames + 2 + F) frames of nb blocks, and never more than
+  // the frames a chunk can see
+  const int fr_max = top_frames + 2 + F < frames_total ? top_frames + 2 + F : frames_total;
+  const int ncand = fr_max * nb;
+  const int E = (ncand + 63) / 64;
+  const int EF = (frames_total + 63) / 64;
+  const size_t lds = static_cast<size_t>(2 * frames_total) * sizeof(int);
+  dim3 grid(nq, d.heads);
+  if (EF <= 1)
+    return launch_2lvl_e<D, 1>(E, grid, lds, s, q_rep, block_rep, frame_rep, F, nb, chunks,
+                               top_frames, b, d.scale, max_sel, sel, nsel);
+  if (EF <= 2)
+    return launch_2lvl_e<D, 2>(E, grid, lds, s, q_rep, block_rep, frame_rep, F, nb, chunks,
+                               top_frames, b, d.scale, max_sel, sel, nsel);
+  return launch_2lvl_e<D, 4>(E, grid, lds, s, q_rep, block_rep, frame_rep, F, nb, chunks,
+                             top_frames, b, d.scale, max_sel, sel, nsel);
 }
 
 hipError_t launch_score_topk_2lvl(const pbsa_dims& d, int chunks, int top_frames,
                                   const int32_t* k_per_chunk, const float* q_rep,
                                   const float* block_rep, const float* frame_rep, int max_sel,
                                   int32_t* sel, int32_t* nsel, hipStream_t s) {
-  const int nb = nb_of(d);
-  const int nq = chunks * d.chunk_frames * nb;
-  const int frames_total = chunks * d.chunk_frames;
   ChunkBudgets b;
   for (int i = 0; i < kMaxChunks; ++i) b.k[i] = i < chunks ? k_per_chunk[i] : 0;
-  const size_t lds = static_cast<size_t>(frames_total) * 8 + static_cast<size_t>(frames_total) * nb * 12;
-  dim3 grid(nq, d.heads);
-  if (d.head_dim == 128)
-    hipLaunchKernelGGL(score_topk_2lvl_kernel<128>, grid, dim3(256), lds, s, q_rep, block_rep,
-                       frame_rep, d.chunk_frames, nb, chunks, top_frames, b, d.scale, max_sel,
-                       sel, nsel);
-  else
-    hipLaunchKernelGGL(score_topk_2lvl_kernel<64>, grid, dim3(256), lds, s, q_rep, block_rep,
-                       frame_rep, d.chunk_frames, nb, chunks, top_frames, b, d.scale, max_sel,
-                       sel, nsel);
-  return hipGetLastError();
+  return d.head_dim == 128
+             ? launch_2lvl_d<128>(d, chunks, top_frames, b, q_rep, block_rep, frame_rep, max_sel,
+                                  sel, nsel, s)
+             : launch_2lvl_d<64>(d, chunks, top_frames, b, q_rep, block_rep, frame_rep, max_sel,
+                                 sel, nsel, s);
 }
 
 }  // namespace pbsa
