@@ -45,6 +45,9 @@ def parse():
                     help="also time the trainable two-level fwd+bwd clip (extra field)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "attn_fwd_wan_5s_traffic.json"),
                     help="HBM traffic per attention launch from rocprofv3 counters (if present)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="after timing, copy a 512 MiB buffer 3 times (calibrates the "
+                         "FETCH_SIZE / WRITE_SIZE counters against known bytes)")
     return ap.parse_args()
 
 
@@ -187,6 +190,14 @@ def main():
 
     if args.train:
         result["train"] = bench_train(torch, ops, runtime, synth, dev, stream)
+
+    if args.copy_probe:
+        src = torch.ones(256 * 1024 * 1024, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_probe_bytes"] = src.numel() * 2
 
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(wl, seed)

@@ -8,14 +8,24 @@ namespace pbsa {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Row-major LDS tile [64][D + 8] and channel-major tile [D][64 + 4]; the padding staggers
-// rows across LDS banks for the 16-byte row reads and the 8-byte column reads.
+// LDS tile layouts.  Row-major tiles keep 16-byte chunks of a row; for head_dim 128 a row is
+// exactly 256 bytes and chunk c of row r sits at chunk position c ^ swz(r), with
+// swz(r) = 4*(r % 4) + (r / 4) % 4.  That permutation keeps both access patterns free of
+// bank conflicts: 16 consecutive rows reading the same logical chunk (K operand) hit 16
+// different positions, and 4 consecutive rows reading an aligned group of 4 chunks (the
+// transposing V read) land in 4 different groups.  For head_dim 64 rows are padded by 16
+// bytes instead.  The channel-major tile [D][64 + 4] is padded.
 template <int D>
 struct Lds {
-  static constexpr int RS = D + 8;       // row-major row pitch (elements)
-  static constexpr int CS = kBlock + 4;  // channel-major row pitch (elements)
+  static constexpr bool SWZ = (D == 128);
+  static constexpr int RS = SWZ ? D : D + 8;  // row-major row pitch (elements)
+  static constexpr int CS = kBlock + 4;       // channel-major row pitch (elements)
   static constexpr int ROWS = kBlock * RS;
   static constexpr int COLS = D * CS;
+  // element offset of (row, channel chunk c) in a row-major tile
+  __host__ __device__ static constexpr int chunk(int row, int c) {
+    return row * RS + 8 * (SWZ ? (c ^ (((row & 3) << 2) | ((row >> 2) & 3))) : c);
+  }
 };
 
 // An R-row x D-channel bf16 tile (R = 64 or 32) staged through registers by NT threads.
@@ -52,7 +62,7 @@ struct Tile {
 #pragma unroll
       for (int i = 0; i < RG; ++i) {
         const int row = RG * KG * q + RG * kg + i;
-        *reinterpret_cast<u32x4*>(lds + row * Lds<D>::RS + 8 * cc) = r[q][i];
+        *reinterpret_cast<u32x4*>(lds + Lds<D>::chunk(row, cc)) = r[q][i];
       }
   }
 
@@ -87,7 +97,7 @@ struct Tile {
 // 16s + 8*h2 + [0, 8)).
 template <int D>
 __device__ __forceinline__ u32x4 rd_rows(const uint16_t* lds, int tile, int s, int c32, int h2) {
-  return *reinterpret_cast<const u32x4*>(lds + (32 * tile + c32) * Lds<D>::RS + 16 * s + 8 * h2);
+  return *reinterpret_cast<const u32x4*>(lds + Lds<D>::chunk(32 * tile + c32, 2 * s + h2));
 }
 // Channel-major tile, channel rows 32*dt + c32, contraction over 16 rows of step t4 in the
 // order produced by a 32x32 accumulator: rows 16*t4 + 4*h2 + [0,4) then 16*t4 + 8 + 4*h2 +
@@ -113,10 +123,13 @@ __device__ __forceinline__ u32x4 rd_rows_tr(const uint16_t* lds, int dt, int t4,
   const int g = l >> 4, i = l & 15;
   const int d0 = 32 * dt + 16 * (g & 1);
   const int k0 = 16 * t4 + 4 * (g >> 1);
-  const int off = (k0 + (i >> 2)) * Lds<D>::RS + d0 + 4 * (i & 3);
-  lds_u16* p = (lds_u16*)(lds) + off;  // generic -> LDS address space
-  const s16x4_ lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
-  const s16x4_ hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 8 * Lds<D>::RS));
+  const int ch = d0 + 4 * (i & 3);  // this lane's 4 channels
+  const int row = k0 + (i >> 2);
+  const int off_lo = Lds<D>::chunk(row, ch >> 3) + (ch & 4);
+  const int off_hi = Lds<D>::chunk(row + 8, ch >> 3) + (ch & 4);
+  lds_u16* p = (lds_u16*)(lds);  // generic -> LDS address space
+  const s16x4_ lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + off_lo));
+  const s16x4_ hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + off_hi));
   const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
   return u32x4{a[0], a[1], b[0], b[1]};
 }

@@ -71,9 +71,13 @@ struct RowState {
 
   // S^T for the keys of one 32-row K half tile: keys acc_row(r, h2), query = this lane's row.
   __device__ __forceinline__ f32x16 scores(const uint16_t* Ks, int len, int c32, int h2) const {
+    // all K operands are read before the MFMA chain so the LDS latency is paid once
+    u32x4 kop[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) kop[s] = rd_rows<D>(Ks, 0, s, c32, h2);
     f32x16 sa = {};
 #pragma unroll
-    for (int s = 0; s < NS; ++s) sa = mfma32(rd_rows<D>(Ks, 0, s, c32, h2), qreg[s], sa);
+    for (int s = 0; s < NS; ++s) sa = mfma32(kop[s], qreg[s], sa);
     if (len < 32) {
 #pragma unroll
       for (int r = 0; r < 16; ++r)
@@ -118,9 +122,12 @@ struct RowState {
       const uint16_t* Vs = kt ? V1 : V0;
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
+        u32x4 vop[ND];
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) vop[dt] = rd_rows_tr<D>(Vs, dt, t2, l);
         const u32x4 pb = pack_step(sacc + kt, t2);
 #pragma unroll
-        for (int dt = 0; dt < ND; ++dt) acc[dt] = mfma32(rd_rows_tr<D>(Vs, dt, t2, l), pb, acc[dt]);
+        for (int dt = 0; dt < ND; ++dt) acc[dt] = mfma32(vop[dt], pb, acc[dt]);
       }
     }
   }
@@ -147,7 +154,8 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
   const int L = static_cast<int>(blockIdx.x % 8) * per + static_cast<int>(blockIdx.x / 8);
   if (L >= a.H * a.pairs) return;
   const int h = L / a.pairs, pr = L - h * a.pairs;
-  const int t = threadIdx.x, w = t >> 6, l = t & 63, h2 = l >> 5, c32 = l & 31;
+  const int t = threadIdx.x, l = t & 63, h2 = l >> 5, c32 = l & 31;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wave index, scalar
   const int mine = w >> 1;  // 0: query block A, 1: query block B
   const int rA = 2 * pr, rB = 2 * pr + 1;
   const int r = mine ? rB : rA;

@@ -38,119 +38,154 @@ __device__ __forceinline__ bool ahead(float sa, int ia, float sb, int ib) {
 __device__ __forceinline__ float order_key(float x) { return x != x ? -INFINITY : x; }
 }  // namespace
 
-// grid H, 256 threads.  Dynamic LDS: the head's block_id and len tables (2 * slots ints)
-// followed by 4 arrays of ncand_max = (C - S) + F*nb candidate entries.  Serial steps
-// (ordered enumeration, slot assignment) run on one thread over LDS only.
-__global__ void __launch_bounds__(256) memory_select_kernel(MemArgs a) {
+// grid H, one wave per head.  Candidates are listed in a fixed order (persistent non-sink
+// slots ascending, then the leaving blocks in chunk-block order, which is ascending id),
+// their memory scores are column sums of the chunk's score matrix, and one bitonic sort of
+// (score, ~id) keys finds the (C - S)-th best key tau: a candidate is kept iff its key is
+// >= tau.  Freed persistent slots (ascending) are handed to the promoted leaving blocks in
+// ascending id order.  Dynamic LDS: block_id and len of the head ([slots] each), candidate
+// slot [ncand_max], free-slot list [C].
+template <int E>
+__global__ void __launch_bounds__(64) memory_select_kernel(MemArgs a) {
   extern __shared__ int mem_smem[];
-  const int h = blockIdx.x, t = threadIdx.x;
-  const int ncand_max = (a.C - a.S) + a.F * a.nb;
-  int* sbid = mem_smem;                        // [slots]
-  int* slen = sbid + a.slots;                  // [slots]
-  int* cslot = slen + a.slots;                 // candidate's slot
-  int* cid = cslot + ncand_max;                // candidate's block id
-  float* cm = reinterpret_cast<float*>(cid + ncand_max);  // memory score
-  int* ckeep = reinterpret_cast<int*>(cm + ncand_max);    // kept?
-  __shared__ int nP, nE;
-  __shared__ int free_slots[1024];
+  const int h = blockIdx.x, l = threadIdx.x;
+  int* sbid = mem_smem;                  // [slots]
+  int* slen = sbid + a.slots;            // [slots]
+  int* cslot = slen + a.slots;           // [ncand_max]
+  int* freel = cslot + (a.C - a.S) + a.F * a.nb;  // [C]
   int32_t* bid = a.bid + static_cast<int64_t>(h) * a.slots;
   int32_t* blen = a.blen + static_cast<int64_t>(h) * a.slots;
   int32_t* dst = a.copy_dst + static_cast<int64_t>(h) * a.F * a.nb;
   const int64_t hF = a.chunk * a.F;  // frames appended so far
+  const int fnb = a.F * a.nb;
 
-  for (int b = t; b < a.F * a.nb; b += 256) dst[b] = -1;
+  for (int b = l; b < fnb; b += 64) dst[b] = -1;
   if (a.chunk == 0) {
     // empty cache: P_t becomes the sinks, written by the copy pass
-    for (int s = t; s < a.C; s += 256) {
+    for (int s = l; s < a.C; s += 64) {
       bid[s] = -1;
       blen[s] = 0;
     }
     return;
   }
-  for (int s = t; s < a.slots; s += 256) {
+  for (int s = l; s < a.slots; s += 64) {
     sbid[s] = bid[s];
     slen[s] = blen[s];
   }
   __syncthreads();
-  if (t == 0) {
-    // enumerate candidates in a fixed order: persistent non-sink slots, then leaving blocks
-    int m = 0;
-    for (int s = a.S; s < a.C; ++s)
-      if (sbid[s] >= a.S) {
-        cslot[m] = s;
-        cid[m] = sbid[s];
-        ++m;
-      }
-    nP = m;
-    for (int b = 0; b < a.F * a.nb; ++b) {
+  // candidate list (ballot compaction keeps the order)
+  int nP = 0;
+  for (int s0 = a.S; s0 < a.C; s0 += 64) {
+    const int s = s0 + l;
+    const bool on = s < a.C && sbid[s] >= a.S;
+    const unsigned long long m = __ballot(on);
+    if (on) cslot[nP + __popcll(m & ((1ull << l) - 1ull))] = s;
+    nP += __popcll(m);
+  }
+  int ncand = nP;
+  for (int b0 = 0; b0 < fnb; b0 += 64) {
+    const int b = b0 + l;
+    int s = -1;
+    if (b < fnb) {
       const int64_t f_new = hF + b / a.nb;  // chunk frame landing in this window slot
-      if (f_new < a.W) continue;           // slot was empty: nothing leaves
-      const int s = a.C + static_cast<int>(f_new % a.W) * a.nb + b % a.nb;
-      if (sbid[s] >= a.S) {
-        cslot[m] = s;
-        cid[m] = sbid[s];
-        ++m;
+      if (f_new >= a.W) {                   // otherwise the slot was empty: nothing leaves
+        s = a.C + static_cast<int>(f_new % a.W) * a.nb + b % a.nb;
+        if (sbid[s] < a.S) s = -1;
       }
     }
-    nE = m - nP;
+    const unsigned long long m = __ballot(s >= 0);
+    if (s >= 0) cslot[ncand + __popcll(m & ((1ull << l) - 1ull))] = s;
+    ncand += __popcll(m);
   }
   __syncthreads();
-  const int ncand = nP + nE;
+  // memory scores and keys; keep a copy of the keys in candidate order
   const float* sc = a.scores + static_cast<int64_t>(h) * a.nq * a.slots;
-  for (int c = t; c < ncand; c += 256) {
-    const int s = cslot[c];
-    float acc = 0.f;
-    for (int r = 0; r < a.nq; ++r) acc += sc[static_cast<int64_t>(r) * a.slots + s];
-    cm[c] = order_key(acc);
-  }
-  __syncthreads();
-  const int keep_n = a.C - a.S;
-  for (int c = t; c < ncand; c += 256) {
-    int rank = 0;
-    const float v = cm[c];
-    const int id = cid[c];
-    for (int u = 0; u < ncand; ++u) rank += ahead(cm[u], cid[u], v, id);
-    ckeep[c] = rank < keep_n;
-  }
-  __syncthreads();
-  if (t == 0) {
-    // free persistent slots (ascending): empty, or holding a block that is not kept
-    int nf = 0;
-    int c = 0;
-    for (int s = a.S; s < a.C; ++s) {
-      bool occupied_kept = false;
-      if (c < nP && cslot[c] == s) {
-        occupied_kept = ckeep[c];
-        ++c;
+  uint64_t key[E], mine[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int c = l + 64 * e;
+    key[e] = 0;
+    if (c < ncand) {
+      const int s = cslot[c];
+      float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
+      int r = 0;
+      for (; r + 4 <= a.nq; r += 4) {
+        acc0 += sc[static_cast<int64_t>(r) * a.slots + s];
+        acc1 += sc[static_cast<int64_t>(r + 1) * a.slots + s];
+        acc2 += sc[static_cast<int64_t>(r + 2) * a.slots + s];
+        acc3 += sc[static_cast<int64_t>(r + 3) * a.slots + s];
       }
-      if (!occupied_kept) free_slots[nf++] = s;
+      for (; r < a.nq; ++r) acc0 += sc[static_cast<int64_t>(r) * a.slots + s];
+      key[e] = rank_key((acc0 + acc1) + (acc2 + acc3), sbid[s]);
     }
-    // promoted leaving blocks in ascending id order take free slots in ascending order
-    int np = 0;
-    for (;;) {
-      int best = -1;
-      for (int e = nP; e < ncand; ++e)
-        if (ckeep[e] == 1 && (best < 0 || cid[e] < cid[best])) best = e;
-      if (best < 0) break;
-      ckeep[best] = 2;  // assigned
-      const int s = free_slots[np++];
-      const int b_rel = cslot[best] - a.C;
-      // chunk block whose window slot is cslot[best]
+    mine[e] = key[e];
+  }
+  const int keep_n = a.C - a.S < ncand ? a.C - a.S : ncand;
+  uint64_t tau = 0;
+  if (keep_n > 0) {
+    wave_sort_desc<E>(key, l);
+    const int e_t = (keep_n - 1) >> 6, l_t = (keep_n - 1) & 63;
+    uint64_t mykey = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (e == e_t) mykey = key[e];
+    tau = (static_cast<uint64_t>(__shfl(static_cast<uint32_t>(mykey >> 32), l_t, 64)) << 32) |
+          __shfl(static_cast<uint32_t>(mykey), l_t, 64);
+  }
+  // kept flags per candidate (in candidate order), written over cslot's sign bit
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int c = l + 64 * e;
+    if (c < ncand && keep_n > 0 && mine[e] >= tau) cslot[c] = ~cslot[c];  // kept: negative
+  }
+  __syncthreads();
+  // free list: persistent non-sink slots whose block is not kept (or that are empty)
+  int nfree = 0;
+  for (int s0 = a.S; s0 < a.C; s0 += 64) {
+    const int s = s0 + l;
+    bool fr = false;
+    if (s < a.C) {
+      fr = sbid[s] < a.S;  // empty
+      if (!fr) {
+        // the candidate for slot s: binary search over the ascending P part of cslot
+        int lo = 0, hi = nP;
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          const int cs = cslot[mid] < 0 ? ~cslot[mid] : cslot[mid];
+          if (cs < s) lo = mid + 1;
+          else hi = mid;
+        }
+        fr = cslot[lo] >= 0;  // not kept
+      }
+    }
+    const unsigned long long m = __ballot(fr);
+    if (fr) freel[nfree + __popcll(m & ((1ull << l) - 1ull))] = s;
+    nfree += __popcll(m);
+  }
+  __syncthreads();
+  // promoted leaving blocks (kept candidates past nP), in candidate order = ascending id
+  int npro = 0;
+  for (int c0 = nP; c0 < ncand; c0 += 64) {
+    const int c = c0 + l;
+    const bool pro = c < ncand && cslot[c] < 0;
+    const unsigned long long m = __ballot(pro);
+    if (pro) {
+      const int k = npro + __popcll(m & ((1ull << l) - 1ull));
+      const int src = ~cslot[c];
+      const int s = freel[k];
+      const int b_rel = src - a.C;
       const int rf = b_rel / a.nb, j = b_rel % a.nb;
       const int fb = static_cast<int>(((rf - hF % a.W) % a.W + a.W) % a.W);
       dst[fb * a.nb + j] = s;
-      sbid[s] = cid[best];
-      slen[s] = slen[cslot[best]];
+      bid[s] = sbid[src];
+      blen[s] = slen[src];
     }
-    for (int k = np; k < nf; ++k) {
-      sbid[free_slots[k]] = -1;
-      slen[free_slots[k]] = 0;
-    }
+    npro += __popcll(m);
   }
-  __syncthreads();
-  for (int s = a.S + t; s < a.C; s += 256) {
-    bid[s] = sbid[s];
-    blen[s] = slen[s];
+  // freed slots left over become empty
+  for (int k = npro + l; k < nfree; k += 64) {
+    bid[freel[k]] = -1;
+    blen[freel[k]] = 0;
   }
 }
 
@@ -241,8 +276,14 @@ hipError_t launch_memory_update(const pbsa_dims& d, const float* scores, const p
   a.nq = d.chunk_frames * nb;
   a.chunk = c.chunk_index;
   const int ncand_max = (d.capacity - d.sinks) + d.chunk_frames * nb;
-  const size_t lds = static_cast<size_t>(ncand_max) * 16 + static_cast<size_t>(a.slots) * 8;
-  hipLaunchKernelGGL(memory_select_kernel, dim3(d.heads), dim3(256), lds, s, a);
+  const size_t lds = static_cast<size_t>(2 * a.slots + ncand_max + d.capacity) * sizeof(int);
+  const int E = (ncand_max + 63) / 64;
+  if (E <= 1) hipLaunchKernelGGL(memory_select_kernel<1>, dim3(d.heads), dim3(64), lds, s, a);
+  else if (E <= 2) hipLaunchKernelGGL(memory_select_kernel<2>, dim3(d.heads), dim3(64), lds, s, a);
+  else if (E <= 4) hipLaunchKernelGGL(memory_select_kernel<4>, dim3(d.heads), dim3(64), lds, s, a);
+  else if (E <= 8) hipLaunchKernelGGL(memory_select_kernel<8>, dim3(d.heads), dim3(64), lds, s, a);
+  else if (E <= 16) hipLaunchKernelGGL(memory_select_kernel<16>, dim3(d.heads), dim3(64), lds, s, a);
+  else hipLaunchKernelGGL(memory_select_kernel<32>, dim3(d.heads), dim3(64), lds, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 grid(d.chunk_frames * nb, d.heads);

@@ -30,14 +30,20 @@ __global__ void __launch_bounds__(256) pool_blocks_kernel(TokIn x, int n, int nb
   float acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-  for (int row = l / CH; row < len; row += RPI) {
-    u32x4 v = *reinterpret_cast<const u32x4*>(base + row * x.ts);
+  // all of the block's rows are requested before any is summed (64 / RPI loads in flight)
+  u32x4 v[kBlock / RPI];
+#pragma unroll
+  for (int i = 0; i < kBlock / RPI; ++i) {
+    const int row = l / CH + RPI * i;
+    v[i] = row < len ? *reinterpret_cast<const u32x4*>(base + row * x.ts) : u32x4{0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int i = 0; i < kBlock / RPI; ++i)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      acc[2 * e] += __uint_as_float(v[e] << 16);
-      acc[2 * e + 1] += __uint_as_float(v[e] & 0xffff0000u);
+      acc[2 * e] += __uint_as_float(v[i][e] << 16);
+      acc[2 * e + 1] += __uint_as_float(v[i][e] & 0xffff0000u);
     }
-  }
   // Combine the RPI row groups (lanes l, l + CH, l + 2CH, ...).
 #pragma unroll
   for (int o = CH; o < 64; o <<= 1) {

@@ -43,43 +43,89 @@ __device__ __forceinline__ float dot_rep(const float* __restrict__ q_lds,
 
 }  // namespace
 
-// grid (Nq, H), one wave per query block.  Lane l scores persistent slots l, l + 64, ...
-// and window slots C + l + 64e (e < E), keeping the window candidates' sort keys in
-// registers; one bitonic sort picks the top K, a second orders them by id.
-template <int D, int E>
-__global__ void __launch_bounds__(64)
+// Row-parallel scores of QB query blocks against `cnt` representative rows.  Groups of
+// LPR = D/8 lanes read one row with 16-byte loads (whole rows per instruction), multiply
+// by the query blocks' matching 8 channels, and reduce across the group; the group's first
+// lane writes the QB scores of its row to out[qb * stride + row].
+template <int D, int QB>
+__device__ __forceinline__ void score_rows(const float (&qv)[QB][8], const float* __restrict__ rep,
+                                           const int32_t* __restrict__ bid, int cnt, float scale,
+                                           float* out, int stride, int l, int first, int step) {
+  constexpr int LPR = D / 8, RPI = 64 / LPR;
+  const int g = l / LPR, sub = l % LPR;
+  for (int s0 = first; s0 < cnt; s0 += step) {
+    const int s = s0 + g;
+    float acc[QB];
+#pragma unroll
+    for (int q = 0; q < QB; ++q) acc[q] = 0.f;
+    const bool on = s < cnt;
+    const int id = on ? bid[s] : -1;
+    if (on) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(rep + static_cast<int64_t>(s) * D + 8 * sub);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(rep + static_cast<int64_t>(s) * D + 8 * sub + 4);
+#pragma unroll
+      for (int q = 0; q < QB; ++q) {
+        acc[q] = qv[q][0] * a[0] + qv[q][1] * a[1] + qv[q][2] * a[2] + qv[q][3] * a[3] +
+                 qv[q][4] * b[0] + qv[q][5] * b[1] + qv[q][6] * b[2] + qv[q][7] * b[3];
+      }
+    }
+#pragma unroll
+    for (int o = 1; o < LPR; o <<= 1)
+#pragma unroll
+      for (int q = 0; q < QB; ++q) acc[q] += __shfl_xor(acc[q], o, 64);
+    if (on && sub == 0) {
+#pragma unroll
+      for (int q = 0; q < QB; ++q) out[q * stride + s] = id >= 0 ? scale * acc[q] : -INFINITY;
+    }
+  }
+}
+
+// grid (ceil(Nq / QB), H), QB waves scoring QB query blocks together: every representative
+// row is read once per QB query blocks, whole rows per load instruction, the waves taking
+// interleaved row groups.  Then wave q sorts query block q's window candidates: a bitonic
+// sort of their keys picks the top K and a second sort orders them by id.  Dynamic LDS:
+// [QB][slots] floats.
+template <int D, int E, int QB>
+__global__ void __launch_bounds__(64 * QB)
     score_topk_kernel(const float* __restrict__ q_rep, const float* __restrict__ rep,
                       const int32_t* __restrict__ block_id, int slots, int C, int S, int K,
                       int nq, float scale, float* __restrict__ scores,
                       int32_t* __restrict__ sel) {
-  __shared__ float q_lds[D];
-  const int r = blockIdx.x, h = blockIdx.y, l = threadIdx.x;
-  const float* qr = q_rep + (static_cast<int64_t>(h) * nq + r) * D;
-  for (int c = l; c < D; c += 64) q_lds[c] = qr[c];
-  __syncthreads();
+  extern __shared__ float sc_lds[];  // [QB][slots]
+  const int r0 = blockIdx.x * QB, h = blockIdx.y, t = threadIdx.x, w = t >> 6, l = t & 63;
+  const int nrows = nq - r0 < QB ? nq - r0 : QB;
+  constexpr int LPR = D / 8, RPI = 64 / LPR;
+  float qv[QB][8];
+#pragma unroll
+  for (int q = 0; q < QB; ++q) {
+    const int r = r0 + (q < nrows ? q : 0);
+    const float* qr = q_rep + (static_cast<int64_t>(h) * nq + r) * D + 8 * (l % LPR);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qv[q][e] = qr[e];
+  }
   const int32_t* bid = block_id + static_cast<int64_t>(h) * slots;
   const float* rp = rep + static_cast<int64_t>(h) * slots * D;
-  float* srow = scores + (static_cast<int64_t>(h) * nq + r) * slots;
-  for (int s = l; s < C; s += 64) {
-    const int id = bid[s];
-    srow[s] = id >= 0 ? scale * dot_rep<D>(q_lds, rp + static_cast<int64_t>(s) * D) : -INFINITY;
+  score_rows<D, QB>(qv, rp, bid, slots, scale, sc_lds, slots, l, w * RPI, QB * RPI);
+  __syncthreads();
+  // scores out (coalesced rows)
+  for (int q = 0; q < nrows; ++q) {
+    float* srow = scores + (static_cast<int64_t>(h) * nq + r0 + q) * slots;
+    for (int s = t; s < slots; s += 64 * QB) srow[s] = sc_lds[q * slots + s];
   }
+  const int q = w;
+  if (q >= nrows) return;
+  // window candidates: occupied ring slots holding non-sink blocks
   const int nwin = slots - C;
   uint64_t key[E];
   int nvalid = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const int w = l + 64 * e;
+    const int wi = l + 64 * e;
     key[e] = 0;
-    if (w < nwin) {
-      const int s = C + w;
-      const int id = bid[s];
-      float v = -INFINITY;
-      if (id >= 0) v = scale * dot_rep<D>(q_lds, rp + static_cast<int64_t>(s) * D);
-      srow[s] = v;
-      // window candidates: occupied ring slots holding non-sink blocks
+    if (wi < nwin) {
+      const int id = bid[C + wi];
       if (id >= S) {
-        key[e] = rank_key(v, id);
+        key[e] = rank_key(sc_lds[q * slots + C + wi], id);
         ++nvalid;
       }
     }
@@ -95,7 +141,7 @@ __global__ void __launch_bounds__(64)
     key[e] = i < nsel ? static_cast<uint64_t>(~static_cast<uint32_t>(rank_key_id(key[e]))) : 0;
   }
   wave_sort_desc<E>(key, l);
-  int32_t* out = sel + (static_cast<int64_t>(h) * nq + r) * K;
+  int32_t* out = sel + (static_cast<int64_t>(h) * nq + r0 + q) * K;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int i = 64 * e + l;
@@ -107,14 +153,17 @@ __global__ void __launch_bounds__(64)
 template <int D>
 static hipError_t launch_score_d(const pbsa_dims& d, const float* q_rep, const pbsa_cache& c,
                                  float* scores, int32_t* sel, hipStream_t s) {
+  constexpr int QB = 4;
   const int nb = nb_of(d);
   const int nq = d.chunk_frames * nb;
   const int slots = static_cast<int>(slots_of(d));
   const int nwin = slots - d.capacity;
-  dim3 grid(nq, d.heads);
+  const size_t lds = static_cast<size_t>(QB) * slots * sizeof(float);
+  dim3 grid(cdiv(nq, QB), d.heads);
 #define PBSA_SCORE_E(EE)                                                                    \
-  hipLaunchKernelGGL((score_topk_kernel<D, EE>), grid, dim3(64), 0, s, q_rep, c.rep,         \
-                     c.block_id, slots, d.capacity, d.sinks, d.topk, nq, d.scale, scores, sel)
+  hipLaunchKernelGGL((score_topk_kernel<D, EE, QB>), grid, dim3(64 * QB), lds, s, q_rep,     \
+                     c.rep, c.block_id, slots, d.capacity, d.sinks, d.topk, nq, d.scale, scores, \
+                     sel)
   if (nwin <= 64) PBSA_SCORE_E(1);
   else if (nwin <= 128) PBSA_SCORE_E(2);
   else if (nwin <= 256) PBSA_SCORE_E(4);
