@@ -33,9 +33,15 @@ def sources():
                   if f.endswith((".hip", ".cpp")))
 
 
+# Per-file flags.  The backward keeps large MFMA accumulators live across its loops; the
+# VGPR form of MFMA keeps them out of AGPR<->VGPR copies.
+FILE_FLAGS = {"attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    extra = FILE_FLAGS.get(os.path.basename(src), [])
+    cmd = [HIPCC, *FLAGS, *extra, "-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -7,14 +7,30 @@
 //   dQ = scale * dS K,  dK = scale * dS^T Q.
 //
 // gfx950 design (no atomics, so results are bit-reproducible):
-//   dq pass  -- one workgroup per (query block, head): walks its selected KV blocks like the
-//               forward, recomputes S^T and dP^T on MFMA, accumulates dQ^T in registers;
-//               it also writes D for its rows.
-//   inverse  -- one workgroup per (KV block, head): lists, in ascending order, the query
-//               blocks that selected the KV block (binary search in their sorted lists).
-//   dkdv pass -- one workgroup per (KV block, head): walks that list, recomputes S and dP
-//               with keys as MFMA columns, accumulates dK^T and dV^T in registers.
+//   dq pass   -- one workgroup per pair of query blocks of a head (four waves of 32 rows);
+//                like the forward it walks each query block's selected KV blocks in 32-key
+//                half tiles, recomputes S^T = K Q^T and dP^T = V dO^T on MFMA (Q, dO in
+//                registers) and accumulates dQ^T = K^T dS^T, reading K channel-major with
+//                the transposing LDS read.  It also writes D for its rows.
+//   inverse   -- one workgroup per (KV block, head): lists, in ascending order, the query
+//                blocks that selected the KV block (binary search in their sorted lists).
+//   plan      -- one workgroup: cuts every inverse list into work items of at most
+//                kSplitQ query blocks (a few KV blocks are selected by every query block,
+//                most by a few dozen), numbering items and partial-sum slots by prefix sums.
+//   dkdv pass -- work items in a grid-stride loop, two waves of 32 keys each; the KV block
+//                stays in LDS; an item walks its part of the list in 32-query half tiles:
+//                S = Q K^T and dP = dO V^T with keys as MFMA columns, then dV^T += dO^T P
+//                and dK^T += Q^T dS (dO, Q read channel-major with the transposing read).
+//                A block with one item writes dK, dV; otherwise each item writes an fp32
+//                partial and
+//   reduce    -- sums a split block's partials in item order and writes dK, dV.
 #include "attn_common.h"
+
+// Waves per SIMD the dK/dV pass is compiled for: its two accumulators (dK^T, dV^T) take
+// 128 VGPRs, so one wave per SIMD gives it the whole register file without spills.
+#ifndef PBSA_DKDV_WPE
+#define PBSA_DKDV_WPE 1
+#endif
 
 namespace pbsa {
 
@@ -31,25 +47,55 @@ struct BwdArgs {
   float* Dw;            // workspace [H][T]
   int32_t* inv_cnt;     // workspace [H][nq]
   int32_t* inv;         // workspace [H][nq][nq]
+  int2* items;          // workspace: work item -> (h*nq + g, split)
+  int32_t* nsplit;      // workspace [H*nq]
+  int32_t* part_base;   // workspace [H*nq]: first partial slot of a split block
+  int32_t* long_list;   // workspace: split blocks
+  int32_t* counts;      // workspace: [0] items, [1] split blocks
+  float* part;          // workspace: partial slots of 2 * 64 * D floats (dK^T, dV^T)
   int64_t T;
-  int nq, nb, n, F, max_sel;
+  int nq, nb, n, F, max_sel, H, pairs;
   float scale;
 };
+
+// A half tile (32 rows) of a block of a frame-major token tensor, rows [32*half, +32).
+struct Half {
+  const uint16_t* p;
+  int len;  // valid rows (0 = none)
+};
+
+__device__ __forceinline__ Half half_of(const uint16_t* base, int64_t ts, int g, int half, int nb,
+                                        int n) {
+  const int len = block_len(g % nb, n) - 32 * half;
+  return Half{base + (block_token0(g, nb, n) + 32 * half) * ts, len < 0 ? 0 : (len < 32 ? len : 32)};
+}
 
 }  // namespace
 
 // ------------------------------------------------------------------ dQ pass (+ D)
+// 1-D grid, 8 * ceil(H * pairs / 8) workgroups of 256 threads (XCD-aware numbering as in the
+// forward).  Wave w: query block 2*pair + w/2, rows 32*(w%2) + [0, 32).
 template <int D>
-__global__ void __launch_bounds__(128) attn_bwd_dq_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
   constexpr int NS = D / 16, ND = D / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[Lds<D>::ROWS];
-  __shared__ __attribute__((aligned(16))) uint16_t Kt[Lds<D>::COLS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[Lds<D>::ROWS];
-  const int r = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
-  const int w = t >> 6, l = t & 63, h2 = l >> 5, c32 = l & 31;
-  const int qrow = 32 * w + c32;
-  const int64_t t0 = block_token0(r, a.nb, a.n);
-  const int qlen = block_len(r % a.nb, a.n);
+  constexpr int HT = 32 * Lds<D>::RS;
+  __shared__ __attribute__((aligned(16))) uint16_t KsX[HT];
+  __shared__ __attribute__((aligned(16))) uint16_t VsX[HT];
+  __shared__ __attribute__((aligned(16))) uint16_t KsY[HT];
+  __shared__ __attribute__((aligned(16))) uint16_t VsY[HT];
+
+  const int per = gridDim.x / 8;
+  const int L = static_cast<int>(blockIdx.x % 8) * per + static_cast<int>(blockIdx.x / 8);
+  if (L >= a.H * a.pairs) return;
+  const int h = L / a.pairs, pr = L - h * a.pairs;
+  const int t = threadIdx.x, l = t & 63, h2 = l >> 5, c32 = l & 31;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int mine = w >> 1;
+  const int rA = 2 * pr, rB = 2 * pr + 1;
+  const int r = mine ? rB : rA;
+  const int qlen = r < a.nq ? block_len(r % a.nb, a.n) : 0;
+  const int qrow = 32 * (w & 1) + c32;
+  const int64_t t0 = r < a.nq ? block_token0(r, a.nb, a.n) : 0;
   const float c = a.scale * kLog2e;
 
   u32x4 qreg[NS], dreg[NS];
@@ -70,64 +116,94 @@ __global__ void __launch_bounds__(128) attn_bwd_dq_kernel(BwdArgs a) {
       }
   }
   dsum += __shfl_xor(dsum, 32, 64);
-  const float* lse_h = a.lse + h * a.T + t0;
-  const float lse2 = qrow < qlen ? lse_h[qrow] * kLog2e : 0.f;
+  const float lse2 = qrow < qlen ? a.lse[h * a.T + t0 + qrow] * kLog2e : 0.f;
   if (qrow < qlen && h2 == 0) a.Dw[h * a.T + t0 + qrow] = dsum;
 
   f32x16 acc[ND];
 #pragma unroll
   for (int i = 0; i < ND; ++i) acc[i] = f32x16{};
 
-  const int32_t* sel = a.sel + (static_cast<int64_t>(h) * a.nq + r) * a.max_sel;
-  const int cnt = a.nsel[static_cast<int64_t>(h) * a.nq + r];
+  const int32_t* selA = a.sel + (static_cast<int64_t>(h) * a.nq + rA) * a.max_sel;
+  const int32_t* selB = a.sel + (static_cast<int64_t>(h) * a.nq + rB) * a.max_sel;
+  const int cntA = a.nsel[static_cast<int64_t>(h) * a.nq + rA];
+  const int cntB = rB < a.nq ? a.nsel[static_cast<int64_t>(h) * a.nq + rB] : 0;
+  const int nsteps = 2 * (cntA > cntB ? cntA : cntB);
   const uint16_t* kh = a.k + h * a.khs;
   const uint16_t* vh = a.v + h * a.vhs;
-  Tile<D> tk, tv;
-  int g = cnt > 0 ? sel[0] : 0;
-  if (cnt > 0) {
-    const int64_t k0 = block_token0(g, a.nb, a.n);
-    const int len = block_len(g % a.nb, a.n);
-    tk.load(kh + k0 * a.kts, a.kts, len, t);
-    tv.load(vh + k0 * a.vts, a.vts, len, t);
+
+  // step s: half (s & 1) of A's and B's (s >> 1)-th selected block
+  auto refs = [&](int s, Half& kx, Half& vx, Half& ky, Half& vy) {
+    const int j = s >> 1, half = s & 1;
+    kx.len = vx.len = ky.len = vy.len = 0;
+    if (j < cntA) {
+      const int g = __builtin_amdgcn_readfirstlane(selA[j]);
+      kx = half_of(kh, a.kts, g, half, a.nb, a.n);
+      vx = half_of(vh, a.vts, g, half, a.nb, a.n);
+    }
+    if (j < cntB) {
+      const int g = __builtin_amdgcn_readfirstlane(selB[j]);
+      ky = half_of(kh, a.kts, g, half, a.nb, a.n);
+      vy = half_of(vh, a.vts, g, half, a.nb, a.n);
+    }
+  };
+
+  Tile<D, 256, 32> tkx, tvx, tky, tvy;
+  Half kx, vx, ky, vy;
+  if (nsteps > 0) {
+    refs(0, kx, vx, ky, vy);
+    tkx.load(kx.p, a.kts, kx.len, t);
+    tvx.load(vx.p, a.vts, vx.len, t);
+    tky.load(ky.p, a.kts, ky.len, t);
+    tvy.load(vy.p, a.vts, vy.len, t);
   }
-  for (int i = 0; i < cnt; ++i) {
+  for (int s = 0; s < nsteps; ++s) {
     __syncthreads();
-    tk.store_rows(Ks, t);
-    tk.store_cols(Kt, t);
-    tv.store_rows(Vs, t);
-    const int len = block_len(g % a.nb, a.n);
+    tkx.store_rows(KsX, t);
+    tvx.store_rows(VsX, t);
+    tky.store_rows(KsY, t);
+    tvy.store_rows(VsY, t);
+    const int lenX = kx.len, lenY = ky.len;
     __syncthreads();
-    if (i + 1 < cnt) {
-      g = sel[i + 1];
-      const int64_t k0 = block_token0(g, a.nb, a.n);
-      const int ln = block_len(g % a.nb, a.n);
-      tk.load(kh + k0 * a.kts, a.kts, ln, t);
-      tv.load(vh + k0 * a.vts, a.vts, ln, t);
+    if (s + 1 < nsteps) {
+      refs(s + 1, kx, vx, ky, vy);
+      tkx.load(kx.p, a.kts, kx.len, t);
+      tvx.load(vx.p, a.vts, vx.len, t);
+      tky.load(ky.p, a.kts, ky.len, t);
+      tvy.load(vy.p, a.vts, vy.len, t);
     }
-    f32x16 sacc[2], pacc[2];
+    const int len = mine ? lenY : lenX;
+    if (qlen > 0 && len > 0) {
+      const uint16_t* Ks = mine ? KsY : KsX;
+      const uint16_t* Vs = mine ? VsY : VsX;
+      u32x4 op[NS];
+      f32x16 sacc[1], pacc = {};
+      sacc[0] = f32x16{};
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      sacc[kt] = f32x16{};
-      pacc[kt] = f32x16{};
+      for (int st = 0; st < NS; ++st) op[st] = rd_rows<D>(Ks, 0, st, c32, h2);
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        sacc[kt] = mfma32(rd_rows<D>(Ks, kt, s, c32, h2), qreg[s], sacc[kt]);
-        pacc[kt] = mfma32(rd_rows<D>(Vs, kt, s, c32, h2), dreg[s], pacc[kt]);
-      }
-    }
+      for (int st = 0; st < NS; ++st) sacc[0] = mfma32(op[st], qreg[st], sacc[0]);
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+      for (int st = 0; st < NS; ++st) op[st] = rd_rows<D>(Vs, 0, st, c32, h2);
+#pragma unroll
+      for (int st = 0; st < NS; ++st) pacc = mfma32(op[st], dreg[st], pacc);
+      // dS^T = P^T * (dP^T - D); keys past the block length contribute nothing
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
-        const bool ok = 32 * kt + acc_row(rr, h2) < len;
-        const float p = ok ? exp2f(fmaf(sacc[kt][rr], c, -lse2)) : 0.f;
-        sacc[kt][rr] = p * (pacc[kt][rr] - dsum);  // dS^T
+        const float p = acc_row(rr, h2) < len
+                            ? __builtin_amdgcn_exp2f(fmaf(sacc[0][rr], c, -lse2))
+                            : 0.f;
+        sacc[0][rr] = p * (pacc[rr] - dsum);
       }
+      // dQ^T += K^T dS^T (K channel-major through the transposing read)
 #pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4) {
-      const u32x4 pb = pack_step(sacc, t4);
+      for (int t2 = 0; t2 < 2; ++t2) {
+        u32x4 kop[ND];
 #pragma unroll
-      for (int dt = 0; dt < ND; ++dt) acc[dt] = mfma32(rd_cols<D>(Kt, dt, t4, c32, h2), pb, acc[dt]);
+        for (int dt = 0; dt < ND; ++dt) kop[dt] = rd_rows_tr<D>(Ks, dt, t2, l);
+        const u32x4 sb = pack_step(sacc, t2);
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) acc[dt] = mfma32(kop[dt], sb, acc[dt]);
+      }
     }
   }
   if (qrow < qlen) {
@@ -161,13 +237,14 @@ __global__ void __launch_bounds__(256) attn_bwd_inverse_kernel(BwdArgs a) {
     bool found = false;
     if (r < a.nq) {
       const int32_t* s = a.sel + (static_cast<int64_t>(h) * a.nq + r) * a.max_sel;
-      int lo = 0, hi = a.nsel[static_cast<int64_t>(h) * a.nq + r];
+      const int cnt = a.nsel[static_cast<int64_t>(h) * a.nq + r];
+      int lo = 0, hi = cnt;
       while (lo < hi) {
         const int mid = (lo + hi) >> 1;
         if (s[mid] < g) lo = mid + 1;
         else hi = mid;
       }
-      found = lo < a.nsel[static_cast<int64_t>(h) * a.nq + r] && s[lo] == g;
+      found = lo < cnt && s[lo] == g;
     }
     const unsigned long long m = __ballot(found);
     const int below = __popcll(m & ((1ull << l) - 1ull));
@@ -182,93 +259,240 @@ __global__ void __launch_bounds__(256) attn_bwd_inverse_kernel(BwdArgs a) {
   if (t == 0) a.inv_cnt[static_cast<int64_t>(h) * a.nq + g] = total;
 }
 
+// ------------------------------------------------------------------ plan
+constexpr int kSplitQ = 96;  // query blocks per dK/dV work item, at most
+
+// one workgroup of 1024 threads; thread t plans entries [t*per, (t+1)*per) of the H*nq
+// (head, KV block) pairs, in order, then three block-wide exclusive scans number the work
+// items, the partial slots and the split blocks.
+__global__ void __launch_bounds__(1024) attn_bwd_plan_kernel(BwdArgs a) {
+  __shared__ int sc[3][1024];
+  const int t = threadIdx.x;
+  const int N = a.H * a.nq;
+  const int per = (N + 1023) / 1024;
+  const int e0 = t * per, e1 = min(N, e0 + per);
+  int my_items = 0, my_parts = 0, my_long = 0;
+  for (int e = e0; e < e1; ++e) {
+    const int cnt = a.inv_cnt[e];
+    const int ns = cnt <= kSplitQ ? 1 : (cnt + kSplitQ - 1) / kSplitQ;
+    my_items += ns;
+    if (ns > 1) {
+      my_parts += ns;
+      ++my_long;
+    }
+  }
+  sc[0][t] = my_items;
+  sc[1][t] = my_parts;
+  sc[2][t] = my_long;
+  __syncthreads();
+  // Hillis-Steele inclusive scans
+  for (int o = 1; o < 1024; o <<= 1) {
+    int v0 = 0, v1 = 0, v2 = 0;
+    if (t >= o) {
+      v0 = sc[0][t - o];
+      v1 = sc[1][t - o];
+      v2 = sc[2][t - o];
+    }
+    __syncthreads();
+    sc[0][t] += v0;
+    sc[1][t] += v1;
+    sc[2][t] += v2;
+    __syncthreads();
+  }
+  int it = sc[0][t] - my_items, pt = sc[1][t] - my_parts, lg = sc[2][t] - my_long;
+  for (int e = e0; e < e1; ++e) {
+    const int cnt = a.inv_cnt[e];
+    const int ns = cnt <= kSplitQ ? 1 : (cnt + kSplitQ - 1) / kSplitQ;
+    a.nsplit[e] = ns;
+    a.part_base[e] = ns > 1 ? pt : -1;
+    for (int s = 0; s < ns; ++s) a.items[it + s] = int2{e, s};
+    it += ns;
+    if (ns > 1) {
+      a.long_list[lg++] = e;
+      pt += ns;
+    }
+  }
+  if (t == 1023) {
+    a.counts[0] = sc[0][1023];
+    a.counts[1] = sc[2][1023];
+  }
+}
+
 // ------------------------------------------------------------------ dK/dV pass
+// Grid-stride over work items, 128 threads.  Wave w owns keys 32*w + [0, 32) of the item's
+// KV block (MFMA columns).
 template <int D>
-__global__ void __launch_bounds__(128) attn_bwd_dkdv_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(128, PBSA_DKDV_WPE) attn_bwd_dkdv_kernel(BwdArgs a) {
   constexpr int NS = D / 16, ND = D / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[Lds<D>::ROWS];
-  __shared__ __attribute__((aligned(16))) uint16_t Qt[Lds<D>::COLS];
-  __shared__ __attribute__((aligned(16))) uint16_t Os[Lds<D>::ROWS];  // dO row-major
-  __shared__ __attribute__((aligned(16))) uint16_t Ot[Lds<D>::COLS];  // dO channel-major
-  __shared__ float lse2_s[kBlock], d_s[kBlock];
-  const int g = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
-  const int w = t >> 6, l = t & 63, h2 = l >> 5, c32 = l & 31;
+  constexpr int HT = 32 * Lds<D>::RS;
+  __shared__ __attribute__((aligned(16))) uint16_t Kb[Lds<D>::ROWS];
+  __shared__ __attribute__((aligned(16))) uint16_t Vb[Lds<D>::ROWS];
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[HT];
+  __shared__ __attribute__((aligned(16))) uint16_t Os[HT];  // dO half tile
+  __shared__ float lse2_s[32], d_s[32];
+  const int t = threadIdx.x;
+  const int l = t & 63, h2 = l >> 5, c32 = l & 31;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int key = 32 * w + c32;  // this lane's key (MFMA column) inside the block
+  const float c = a.scale * kLog2e;
+  const int n_items = a.counts[0];
+
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int2 it = a.items[item];
+    const int hg = __builtin_amdgcn_readfirstlane(it.x), sp = __builtin_amdgcn_readfirstlane(it.y);
+    const int h = hg / a.nq, g = hg - h * a.nq;
+    const int64_t k0 = block_token0(g, a.nb, a.n);
+    const int klen = block_len(g % a.nb, a.n);
+    __syncthreads();  // the previous item's LDS reads are done
+    {
+      Tile<D, 128> tk, tv;
+      tk.load(a.k + h * a.khs + k0 * a.kts, a.kts, klen, t);
+      tv.load(a.v + h * a.vhs + k0 * a.vts, a.vts, klen, t);
+      tk.store_rows(Kb, t);
+      tv.store_rows(Vb, t);
+    }
+    f32x16 dk[ND], dv[ND];
+#pragma unroll
+    for (int i = 0; i < ND; ++i) {
+      dk[i] = f32x16{};
+      dv[i] = f32x16{};
+    }
+    const int cnt = a.inv_cnt[hg];
+    const int q_lo = sp * kSplitQ;
+    const int q_hi = min(cnt, q_lo + kSplitQ);
+    const int32_t* lst = a.inv + static_cast<int64_t>(hg) * a.nq;
+    const int nsteps = 2 * (q_hi - q_lo);
+    const uint16_t* qh = a.q + h * a.qhs;
+    const uint16_t* dh = a.dout + h * a.dhs;
+    Tile<D, 128, 32> tq, td;
+    Half hq, hd;
+    float lse_r = INFINITY, d_r = 0.f;
+    auto fetch = [&](int s) {
+      const int rb = __builtin_amdgcn_readfirstlane(lst[q_lo + (s >> 1)]);
+      const int half = s & 1;
+      hq = half_of(qh, a.qts, rb, half, a.nb, a.n);
+      hd = half_of(dh, a.dts, rb, half, a.nb, a.n);
+      tq.load(hq.p, a.qts, hq.len, t);
+      td.load(hd.p, a.dts, hd.len, t);
+      if (t < 32) {
+        const int64_t q0 = block_token0(rb, a.nb, a.n) + 32 * half;
+        // rows past the query block's length get lse = +inf, so their P is 0
+        lse_r = t < hq.len ? a.lse[h * a.T + q0 + t] * kLog2e : INFINITY;
+        d_r = t < hq.len ? a.Dw[h * a.T + q0 + t] : 0.f;
+      }
+    };
+    if (nsteps > 0) fetch(0);
+    for (int s = 0; s < nsteps; ++s) {
+      __syncthreads();
+      tq.store_rows(Qs, t);
+      td.store_rows(Os, t);
+      if (t < 32) {
+        lse2_s[t] = lse_r;
+        d_s[t] = d_r;
+      }
+      const int qlen = hq.len;
+      __syncthreads();
+      if (s + 1 < nsteps) fetch(s + 1);
+      if (qlen > 0) {
+        f32x16 sacc[1], pacc[1];
+        sacc[0] = f32x16{};
+        pacc[0] = f32x16{};
+        // S (queries x keys): A = Q rows, B = K rows of this wave's keys; dP likewise
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+          sacc[0] = mfma32(rd_rows<D>(Qs, 0, st, c32, h2), rd_rows<D>(Kb, w, st, c32, h2), sacc[0]);
+          pacc[0] = mfma32(rd_rows<D>(Os, 0, st, c32, h2), rd_rows<D>(Vb, w, st, c32, h2), pacc[0]);
+        }
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          const int qi = acc_row(rr, h2);
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[0][rr], c, -lse2_s[qi]));
+          sacc[0][rr] = p;
+          pacc[0][rr] = p * (pacc[0][rr] - d_s[qi]);
+        }
+        // dV^T += dO^T P, dK^T += Q^T dS (dO, Q channel-major through the transposing read)
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+          const u32x4 pb = pack_step(sacc, t2);
+          const u32x4 sb = pack_step(pacc, t2);
+#pragma unroll
+          for (int dt = 0; dt < ND; ++dt) {
+            dv[dt] = mfma32(rd_rows_tr<D>(Os, dt, t2, l), pb, dv[dt]);
+            dk[dt] = mfma32(rd_rows_tr<D>(Qs, dt, t2, l), sb, dk[dt]);
+          }
+        }
+      }
+    }
+    if (a.nsplit[hg] == 1) {
+      if (key < klen) {
+        uint16_t* ko = a.dk + h * a.dkhs + (k0 + key) * a.dkts;
+        uint16_t* vo = a.dv + h * a.dvhs + (k0 + key) * a.dvts;
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int ch = 32 * dt + 8 * j + 4 * h2;
+            u32x2 pk = {pack_bf16x2(dk[dt][4 * j] * a.scale, dk[dt][4 * j + 1] * a.scale),
+                        pack_bf16x2(dk[dt][4 * j + 2] * a.scale, dk[dt][4 * j + 3] * a.scale)};
+            *reinterpret_cast<u32x2*>(ko + ch) = pk;
+            u32x2 pv = {pack_bf16x2(dv[dt][4 * j], dv[dt][4 * j + 1]),
+                        pack_bf16x2(dv[dt][4 * j + 2], dv[dt][4 * j + 3])};
+            *reinterpret_cast<u32x2*>(vo + ch) = pv;
+          }
+      }
+    } else {
+      // partial slot: [thread][dK^T registers | dV^T registers], each thread's values
+      // contiguous so the stores take immediate offsets from one address
+      f32x4* pp = reinterpret_cast<f32x4*>(
+          a.part + static_cast<int64_t>(a.part_base[hg] + sp) * (2 * kBlock * D) +
+          static_cast<int64_t>(t) * (32 * ND));
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          pp[4 * dt + r] = f32x4{dk[dt][4 * r], dk[dt][4 * r + 1], dk[dt][4 * r + 2], dk[dt][4 * r + 3]};
+          pp[4 * ND + 4 * dt + r] =
+              f32x4{dv[dt][4 * r], dv[dt][4 * r + 1], dv[dt][4 * r + 2], dv[dt][4 * r + 3]};
+        }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ reduce
+// one workgroup (128 threads) per split block: sums its partials in item order.
+template <int D>
+__global__ void __launch_bounds__(128) attn_bwd_reduce_kernel(BwdArgs a) {
+  constexpr int ND = D / 32;
+  const int j = blockIdx.x;
+  if (j >= a.counts[1]) return;
+  const int hg = a.long_list[j];
+  const int h = hg / a.nq, g = hg - h * a.nq;
+  const int t = threadIdx.x, l = t & 63, w = t >> 6, h2 = l >> 5, c32 = l & 31;
+  const int key = 32 * w + c32;
   const int64_t k0 = block_token0(g, a.nb, a.n);
   const int klen = block_len(g % a.nb, a.n);
-  const float c = a.scale * kLog2e;
-
-  u32x4 kreg[NS], vreg[NS];
-  load_row_operand<D>(kreg, a.k + h * a.khs + k0 * a.kts, a.kts, key, klen, h2);
-  load_row_operand<D>(vreg, a.v + h * a.vhs + k0 * a.vts, a.vts, key, klen, h2);
-
+  const int ns = a.nsplit[hg];
+  const float* p0 = a.part + static_cast<int64_t>(a.part_base[hg]) * (2 * kBlock * D);
   f32x16 dk[ND], dv[ND];
 #pragma unroll
-  for (int i = 0; i < ND; ++i) {
-    dk[i] = f32x16{};
-    dv[i] = f32x16{};
+  for (int dt = 0; dt < ND; ++dt) {
+    dk[dt] = f32x16{};
+    dv[dt] = f32x16{};
   }
-  const int32_t* lst = a.inv + (static_cast<int64_t>(h) * a.nq + g) * a.nq;
-  const int cnt = a.inv_cnt[static_cast<int64_t>(h) * a.nq + g];
-  const uint16_t* qh = a.q + h * a.qhs;
-  const uint16_t* dh = a.dout + h * a.dhs;
-  Tile<D> tq, td;
-  float lse_r = 0.f, d_r = 0.f;
-  int r = cnt > 0 ? lst[0] : 0;
-  auto fetch = [&](int rb) {
-    const int64_t q0 = block_token0(rb, a.nb, a.n);
-    const int ql = block_len(rb % a.nb, a.n);
-    tq.load(qh + q0 * a.qts, a.qts, ql, t);
-    td.load(dh + q0 * a.dts, a.dts, ql, t);
-    if (t < kBlock) {
-      lse_r = t < ql ? a.lse[h * a.T + q0 + t] * kLog2e : INFINITY;
-      d_r = t < ql ? a.Dw[h * a.T + q0 + t] : 0.f;
-    }
-  };
-  if (cnt > 0) fetch(r);
-  for (int i = 0; i < cnt; ++i) {
-    __syncthreads();
-    tq.store_rows(Qs, t);
-    tq.store_cols(Qt, t);
-    td.store_rows(Os, t);
-    td.store_cols(Ot, t);
-    if (t < kBlock) {
-      lse2_s[t] = lse_r;
-      d_s[t] = d_r;
-    }
-    __syncthreads();
-    if (i + 1 < cnt) fetch(lst[i + 1]);
-    f32x16 sacc[2], pacc[2];
+  for (int sp = 0; sp < ns; ++sp) {
+    const f32x4* pp = reinterpret_cast<const f32x4*>(
+        p0 + static_cast<int64_t>(sp) * (2 * kBlock * D) + static_cast<int64_t>(t) * (32 * ND));
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      sacc[qt] = f32x16{};
-      pacc[qt] = f32x16{};
+    for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        sacc[qt] = mfma32(rd_rows<D>(Qs, qt, s, c32, h2), kreg[s], sacc[qt]);
-        pacc[qt] = mfma32(rd_rows<D>(Os, qt, s, c32, h2), vreg[s], pacc[qt]);
+      for (int r = 0; r < 4; ++r) {
+        const f32x4 x = pp[4 * dt + r], y = pp[4 * ND + 4 * dt + r];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          dk[dt][4 * r + e] += x[e];
+          dv[dt][4 * r + e] += y[e];
+        }
       }
-    }
-    // rows beyond the query block's length carry lse = +inf, so their P is 0
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const int qi = 32 * qt + acc_row(rr, h2);
-        const float p = exp2f(fmaf(sacc[qt][rr], c, -lse2_s[qi]));
-        sacc[qt][rr] = p;
-        pacc[qt][rr] = p * (pacc[qt][rr] - d_s[qi]);
-      }
-#pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4) {
-      const u32x4 pb = pack_step(sacc, t4);
-      const u32x4 sb = pack_step(pacc, t4);
-#pragma unroll
-      for (int dt = 0; dt < ND; ++dt) {
-        dv[dt] = mfma32(rd_cols<D>(Ot, dt, t4, c32, h2), pb, dv[dt]);
-        dk[dt] = mfma32(rd_cols<D>(Qt, dt, t4, c32, h2), sb, dk[dt]);
-      }
-    }
   }
   if (key < klen) {
     uint16_t* ko = a.dk + h * a.dkhs + (k0 + key) * a.dkts;
@@ -276,24 +500,49 @@ __global__ void __launch_bounds__(128) attn_bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int ch = 32 * dt + 8 * j + 4 * h2;
-        u32x2 pk = {pack_bf16x2(dk[dt][4 * j] * a.scale, dk[dt][4 * j + 1] * a.scale),
-                    pack_bf16x2(dk[dt][4 * j + 2] * a.scale, dk[dt][4 * j + 3] * a.scale)};
+      for (int jj = 0; jj < 4; ++jj) {
+        const int ch = 32 * dt + 8 * jj + 4 * h2;
+        u32x2 pk = {pack_bf16x2(dk[dt][4 * jj] * a.scale, dk[dt][4 * jj + 1] * a.scale),
+                    pack_bf16x2(dk[dt][4 * jj + 2] * a.scale, dk[dt][4 * jj + 3] * a.scale)};
         *reinterpret_cast<u32x2*>(ko + ch) = pk;
-        u32x2 pv = {pack_bf16x2(dv[dt][4 * j], dv[dt][4 * j + 1]),
-                    pack_bf16x2(dv[dt][4 * j + 2], dv[dt][4 * j + 3])};
+        u32x2 pv = {pack_bf16x2(dv[dt][4 * jj], dv[dt][4 * jj + 1]),
+                    pack_bf16x2(dv[dt][4 * jj + 2], dv[dt][4 * jj + 3])};
         *reinterpret_cast<u32x2*>(vo + ch) = pv;
       }
   }
 }
 
-size_t attn_bwd_workspace(const pbsa_dims& d, int chunks, int max_sel) {
-  (void)max_sel;
+namespace {
+// Workspace layout of the backward (bytes, 256-aligned pieces).
+struct BwdWs {
+  size_t D, inv_cnt, inv, items, nsplit, part_base, long_list, counts, part, total;
+};
+BwdWs bwd_ws(const pbsa_dims& d, int chunks, int max_sel) {
   const int64_t nq = static_cast<int64_t>(chunks) * d.chunk_frames * nb_of(d);
   const int64_t T = static_cast<int64_t>(chunks) * d.chunk_frames * d.frame_tokens;
   const int64_t H = d.heads;
-  return static_cast<size_t>(H * T * 4 + H * nq * 4 + H * nq * nq * 4 + 256);
+  const int64_t pairs_max = H * nq * max_sel;                 // selected (query, KV) pairs
+  const int64_t items_max = H * nq + pairs_max / kSplitQ + 1;  // work items
+  const int64_t parts_max = 2 * (pairs_max / kSplitQ) + 2;     // partial slots
+  auto up = [](size_t x) { return (x + 255) & ~size_t{255}; };
+  BwdWs w{};
+  size_t o = 0;
+  w.D = o; o += up(H * T * 4);
+  w.inv_cnt = o; o += up(H * nq * 4);
+  w.inv = o; o += up(H * nq * nq * 4);
+  w.items = o; o += up(items_max * 8);
+  w.nsplit = o; o += up(H * nq * 4);
+  w.part_base = o; o += up(H * nq * 4);
+  w.long_list = o; o += up(H * nq * 4);
+  w.counts = o; o += up(16);
+  w.part = o; o += up(static_cast<size_t>(parts_max) * 2 * kBlock * d.head_dim * 4);
+  w.total = o;
+  return w;
+}
+}  // namespace
+
+size_t attn_bwd_workspace(const pbsa_dims& d, int chunks, int max_sel) {
+  return bwd_ws(d, chunks, max_sel).total;
 }
 
 hipError_t launch_attn_bwd(const pbsa_dims& d, int chunks, TokIn q, TokIn k, TokIn v, TokIn o,
@@ -315,33 +564,54 @@ hipError_t launch_attn_bwd(const pbsa_dims& d, int chunks, TokIn q, TokIn k, Tok
   a.lse = lse;
   a.sel = sel;
   a.nsel = nsel;
+  const BwdWs L = bwd_ws(d, chunks, max_sel);
   char* p = static_cast<char*>(ws);
-  a.Dw = reinterpret_cast<float*>(p);
-  p += static_cast<size_t>(d.heads) * T * 4;
-  a.inv_cnt = reinterpret_cast<int32_t*>(p);
-  p += static_cast<size_t>(d.heads) * nq * 4;
-  a.inv = reinterpret_cast<int32_t*>(p);
+  a.Dw = reinterpret_cast<float*>(p + L.D);
+  a.inv_cnt = reinterpret_cast<int32_t*>(p + L.inv_cnt);
+  a.inv = reinterpret_cast<int32_t*>(p + L.inv);
+  a.items = reinterpret_cast<int2*>(p + L.items);
+  a.nsplit = reinterpret_cast<int32_t*>(p + L.nsplit);
+  a.part_base = reinterpret_cast<int32_t*>(p + L.part_base);
+  a.long_list = reinterpret_cast<int32_t*>(p + L.long_list);
+  a.counts = reinterpret_cast<int32_t*>(p + L.counts);
+  a.part = reinterpret_cast<float*>(p + L.part);
   a.T = T;
   a.nq = nq;
   a.nb = nb;
   a.n = d.frame_tokens;
   a.F = d.chunk_frames;
   a.max_sel = max_sel;
+  a.H = d.heads;
+  a.pairs = cdiv(nq, 2);
   a.scale = d.scale;
-  dim3 grid(nq, d.heads);
+  const int gq = 8 * cdiv(d.heads * a.pairs, 8);
   if (d.head_dim == 128)
-    hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, grid, dim3(128), 0, s, a);
+    hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, dim3(gq), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, grid, dim3(128), 0, s, a);
+    hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, dim3(gq), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  dim3 grid(nq, d.heads);
   hipLaunchKernelGGL(attn_bwd_inverse_kernel, grid, dim3(256), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_bwd_plan_kernel, dim3(1), dim3(1024), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t items_max = static_cast<int64_t>(d.heads) * nq +
+                            static_cast<int64_t>(d.heads) * nq * max_sel / kSplitQ + 1;
+  const int gi = static_cast<int>(items_max < 2048 ? items_max : 2048);
   if (d.head_dim == 128)
-    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<128>, grid, dim3(128), 0, s, a);
+    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<128>, dim3(gi), dim3(128), 0, s, a);
   else
-    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<64>, grid, dim3(128), 0, s, a);
+    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<64>, dim3(gi), dim3(128), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int gr = d.heads * nq;
+  if (d.head_dim == 128)
+    hipLaunchKernelGGL(attn_bwd_reduce_kernel<128>, dim3(gr), dim3(128), 0, s, a);
+  else
+    hipLaunchKernelGGL(attn_bwd_reduce_kernel<64>, dim3(gr), dim3(128), 0, s, a);
   return hipGetLastError();
 }
 
