@@ -58,6 +58,7 @@ pbsa_status check_dims(const pbsa_dims* d, int mode) {
       return fail(PBSA_ERR_SHAPE, "need 0 <= sinks <= min(capacity, blocks per frame)");
     if (d->capacity < 0) return fail(PBSA_ERR_SHAPE, "capacity must be >= 0");
     if (d->topk < 1) return fail(PBSA_ERR_SHAPE, "topk must be >= 1");
+    if (d->topk > 1024) return fail(PBSA_ERR_UNSUPPORTED, "topk must be <= 1024");
     const int64_t slots = pbsa::slots_of(*d);
     if (slots > kMaxSlots)
       return fail(PBSA_ERR_UNSUPPORTED, "capacity + window blocks = %lld exceeds %lld",
@@ -84,6 +85,14 @@ pbsa_status check_tok(const pbsa_tensor& t, const char* name, int head_dim) {
     return fail(PBSA_ERR_ALIGN, "%s strides must be multiples of 8 elements", name);
   if (t.token_stride < head_dim || t.head_stride < 0)
     return fail(PBSA_ERR_SHAPE, "%s strides out of range", name);
+  return PBSA_OK;
+}
+
+// The attention kernels address a head's token rows with 32-bit byte offsets.
+pbsa_status check_span(const pbsa_tensor& t, const char* name, int64_t tokens, int head_dim) {
+  const int64_t bytes = (tokens - 1) * t.token_stride * 2 + int64_t{head_dim} * 2;
+  if (tokens > 0 && bytes > (int64_t{1} << 31))
+    return fail(PBSA_ERR_UNSUPPORTED, "%s spans more than 2 GiB per head", name);
   return PBSA_OK;
 }
 
@@ -191,6 +200,9 @@ pbsa_status pbsa_attn_fwd(const pbsa_dims* dims, pbsa_tensor q, const pbsa_cache
   PBSA_TRY(check_tok(chunk_k, "chunk_k", dims->head_dim));
   PBSA_TRY(check_tok(chunk_v, "chunk_v", dims->head_dim));
   PBSA_TRY(check_tok(o, "o", dims->head_dim));
+  const int64_t ctok = int64_t{dims->chunk_frames} * dims->frame_tokens;
+  PBSA_TRY(check_span(chunk_k, "chunk_k", ctok, dims->head_dim));
+  PBSA_TRY(check_span(chunk_v, "chunk_v", ctok, dims->head_dim));
   if (!sel || !lse) return fail(PBSA_ERR_NULL, "sel and lse are required");
   return hip_status(pbsa::launch_attn_fwd_persistent(*dims, pbsa::tok_in(q), *cache,
                                                      pbsa::tok_in(chunk_k),
@@ -262,6 +274,10 @@ pbsa_status pbsa_attn_fwd_2lvl(const pbsa_dims* dims, int32_t chunks, pbsa_tenso
   PBSA_TRY(check_tok(o, "o", dims->head_dim));
   if (!sel || !nsel || !lse) return fail(PBSA_ERR_NULL, "sel, nsel and lse are required");
   if (max_sel < 1) return fail(PBSA_ERR_SHAPE, "max_sel must be >= 1");
+  if (max_sel > 4096) return fail(PBSA_ERR_UNSUPPORTED, "max_sel must be <= 4096");
+  const int64_t ctok = int64_t{chunks} * dims->chunk_frames * dims->frame_tokens;
+  PBSA_TRY(check_span(k, "k", ctok, dims->head_dim));
+  PBSA_TRY(check_span(v, "v", ctok, dims->head_dim));
   return hip_status(pbsa::launch_attn_fwd_2lvl(*dims, chunks, pbsa::tok_in(q), pbsa::tok_in(k),
                                                pbsa::tok_in(v), sel, nsel, max_sel,
                                                pbsa::tok_out(o), lse, stream_of(stream)),

@@ -24,6 +24,8 @@
 //   * the next step's global loads are issued before the current step's math.
 // Softmax runs in base 2 with scale*log2(e) folded in (v_exp_f32), P is packed to bf16 with
 // v_cvt_pk_bf16_f32, and the running max is raised lazily; accumulators are fp32.
+#include <type_traits>
+
 #include "attn_common.h"
 
 namespace pbsa {
@@ -54,11 +56,27 @@ struct FwdArgs {
 
 namespace {
 
-struct KvRef {
-  const uint16_t* k;
-  const uint16_t* v;
-  int64_t stride;  // elements between token rows
-  int len;         // valid rows; 0 = no block
+// LDS layout of one 32-row half tile (bytes), chosen so that every LDS read is a per-lane
+// base plus an immediate and touches contiguous bytes, and every gather instruction fills
+// 1 KB of LDS:
+//   K: [row / 16][16-byte channel chunk][row % 16]: the K operand of k-step s (16 rows of
+//      one chunk per 16 lanes) is 256 contiguous bytes at base + 512 s;
+//   V: [32-channel segment][row][64 bytes]: a transposing read (8 rows x 32 channels) is
+//      512 contiguous bytes at base + 2048 dt + 1024 t4 (+ 512 for rows 8..15).
+// A gather instruction moves 16 rows x 64 bytes (four chunks of K, one segment of V).
+template <int D>
+struct HalfTile {
+  static constexpr int BYTES = 32 * D * 2;
+  static constexpr int PIECES = BYTES / 1024;  // gather instructions per half tile
+  static constexpr int KRG = 16 * D * 2;       // K: bytes per 16-row group
+};
+
+// A half tile to gather: wave-uniform base (bytes), row stride (bytes) and valid rows.
+struct HalfRef {
+  const char* k;
+  const char* v;
+  uint32_t stride;
+  int len;  // 0 = nothing to gather
 };
 
 // Online-softmax state of one wave (32 query rows, this lane's row = column c32).
@@ -69,16 +87,18 @@ struct RowState {
   f32x16 acc[ND];
   float m_run, l_run;
 
-  // S^T for the keys of one 32-row K half tile: keys acc_row(r, h2), query = this lane's row.
-  __device__ __forceinline__ f32x16 scores(const uint16_t* Ks, int len, int c32, int h2) const {
-    // all K operands are read before the MFMA chain so the LDS latency is paid once
+  // S^T for the keys of one K half tile: keys acc_row(r, h2), query = this lane's row.
+  // kb: this lane's K read address (bytes, LDS).
+  __device__ __forceinline__ f32x16 scores(const char* kb, int len, int h2) const {
     u32x4 kop[NS];
 #pragma unroll
-    for (int s = 0; s < NS; ++s) kop[s] = rd_rows<D>(Ks, 0, s, c32, h2);
+    for (int s = 0; s < NS; ++s) kop[s] = *reinterpret_cast<const u32x4*>(kb + 512 * s);
     f32x16 sa = {};
 #pragma unroll
     for (int s = 0; s < NS; ++s) sa = mfma32(kop[s], qreg[s], sa);
     if (len < 32) {
+      // rare (a frame's tail block): keep it a branch rather than 16 selects per tile
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         if (acc_row(r, h2) >= len) sa[r] = -INFINITY;
@@ -86,12 +106,32 @@ struct RowState {
     return sa;
   }
 
+  // O^T += V^T P^T for one V half tile; vb: this lane's transposing-read address.
+  __device__ __forceinline__ void pv(const f32x16& p, const char* vb) {
+    lds_u16* base = (lds_u16*)(vb);
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      u32x4 vop[ND];
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) {
+        const s16x4_ lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)(base + (2048 * dt + 1024 * t2) / 2));
+        const s16x4_ hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)(base + (2048 * dt + 1024 * t2 + 512) / 2));
+        const u32x2 x = __builtin_bit_cast(u32x2, lo), y = __builtin_bit_cast(u32x2, hi);
+        vop[dt] = u32x4{x[0], x[1], y[0], y[1]};
+      }
+      const u32x4 pb = pack_step(&p, t2);
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) acc[dt] = mfma32(vop[dt], pb, acc[dt]);
+    }
+  }
+
   // Online-softmax update with NT score tiles (32 keys each) and their V half tiles.
   // The running max only moves when some row's new max exceeds it by more than 2^8 in
   // exp2 units, so the rescale of the accumulators is rare; exp2 arguments stay <= 8.
   template <int NT>
-  __device__ __forceinline__ void update(f32x16* sacc, const uint16_t* V0, const uint16_t* V1,
-                                         float c, int l) {
+  __device__ __forceinline__ void update(f32x16* sacc, const char* v0, const char* v1, float c) {
     float mx = sacc[0][0];
 #pragma unroll
     for (int kt = 0; kt < NT; ++kt)
@@ -117,19 +157,8 @@ struct RowState {
         psum += p;
       }
     l_run += psum;
-#pragma unroll
-    for (int kt = 0; kt < NT; ++kt) {
-      const uint16_t* Vs = kt ? V1 : V0;
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        u32x4 vop[ND];
-#pragma unroll
-        for (int dt = 0; dt < ND; ++dt) vop[dt] = rd_rows_tr<D>(Vs, dt, t2, l);
-        const u32x4 pb = pack_step(sacc + kt, t2);
-#pragma unroll
-        for (int dt = 0; dt < ND; ++dt) acc[dt] = mfma32(vop[dt], pb, acc[dt]);
-      }
-    }
+    pv(sacc[0], v0);
+    if (NT > 1) pv(sacc[1], v1);
   }
 };
 
@@ -138,12 +167,11 @@ struct RowState {
 // 1-D grid of 8 * ceil(H * pairs / 8) workgroups of 256 threads.
 template <int D, bool PERSIST>
 __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
-  // two 32-key half tiles per step: X and Y, K and V row-major
-  constexpr int HT = 32 * Lds<D>::RS;
-  __shared__ __attribute__((aligned(16))) uint16_t KsX[HT];
-  __shared__ __attribute__((aligned(16))) uint16_t VsX[HT];
-  __shared__ __attribute__((aligned(16))) uint16_t KsY[HT];
-  __shared__ __attribute__((aligned(16))) uint16_t VsY[HT];
+  using HT = HalfTile<D>;
+  // Two buffers of four half tiles each (K of X, K of Y, V of X, V of Y): one step's
+  // tiles are gathered straight into LDS while the previous step's are used.
+  __shared__ __attribute__((aligned(1024))) char buf0[4][HT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char buf1[4][HT::BYTES];
   extern __shared__ int2 lists[];
   __shared__ int wave_cnt[4];
   __shared__ int n_list;
@@ -165,10 +193,17 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
   const float c = a.scale * kLog2e;
   int cntA, cntB;
 
-  // Block lists in LDS as (handle, valid rows): handle < slots is a cache slot, otherwise
-  // block (handle - slots) of the token tensors xk/xv.  Shared list (persistent mode):
-  // occupied P slots in slot order, then the chunk's blocks.  Private lists: A's and B's
-  // routed blocks.
+  // Block lists in LDS as (byte offset, valid rows | kind << 16): kind 0 is a cache slot
+  // (offset from the head's cache base), kind 1 a block of the token tensors xk/xv
+  // (offset from the head's base there).  Shared list (persistent mode): occupied P slots
+  // in slot order, then the chunk's blocks.  Private lists: A's and B's routed blocks.
+  constexpr uint32_t kCacheBlockBytes = kBlock * D * 2;
+  const uint32_t xrow = static_cast<uint32_t>(a.xts * 2);
+  auto tok_entry = [&](int g) {
+    const int f = g / a.nb, jj = g - f * a.nb;
+    const uint32_t tok = static_cast<uint32_t>(f) * a.n + kBlock * jj;
+    return int2{static_cast<int>(tok * xrow), block_len(jj, a.n) | (1 << 16)};
+  };
   int2* shared_list = lists;
   int2* listA = lists + (PERSIST ? a.C + a.nq : 0);
   int2* listB = listA + a.sel_stride;
@@ -186,14 +221,15 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
       __syncthreads();
       int off = n_list;
       for (int u = 0; u < w; ++u) off += wave_cnt[u];
-      if (valid) shared_list[off + __popcll(m & ((1ull << l) - 1ull))] = int2{s, lh[s]};
+      if (valid)
+        shared_list[off + __popcll(m & ((1ull << l) - 1ull))] =
+            int2{static_cast<int>(s * kCacheBlockBytes), lh[s]};
       __syncthreads();
       if (t == 0) n_list += wave_cnt[0] + wave_cnt[1] + wave_cnt[2] + wave_cnt[3];
       __syncthreads();
     }
     const int nP = __builtin_amdgcn_readfirstlane(n_list);
-    for (int b = t; b < a.nq; b += 256)
-      shared_list[nP + b] = int2{a.slots + b, block_len(b % a.nb, a.n)};
+    for (int b = t; b < a.nq; b += 256) shared_list[nP + b] = tok_entry(b);
     nshared = nP + a.nq;
   }
   // private lists; routed ids are ascending with -1 padding at the end (persistent) or
@@ -204,22 +240,18 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
     const int na = PERSIST ? a.sel_stride : a.nsel[static_cast<int64_t>(h) * a.nq + rA];
     const int nbb = rB >= a.nq ? 0 : PERSIST ? a.sel_stride
                                              : a.nsel[static_cast<int64_t>(h) * a.nq + rB];
+    auto entry = [&](int g) {
+      if (!PERSIST) return tok_entry(g);
+      const int f = g / a.nb, jj = g - f * a.nb;
+      const int slot = a.C + (f % a.W) * a.nb + jj;
+      return int2{static_cast<int>(slot * kCacheBlockBytes),
+                  a.blen[static_cast<int64_t>(h) * a.slots + slot]};
+    };
     for (int j = t; j < a.sel_stride; j += 256) {
-      int2 ea{-1, 0}, eb{-1, 0};
       const int ga = j < na ? sa[j] : -1;
       const int gb = j < nbb ? sb[j] : -1;
-      if (ga >= 0) {
-        const int f = ga / a.nb, jj = ga - f * a.nb;
-        ea = PERSIST ? int2{a.C + (f % a.W) * a.nb + jj, 0} : int2{a.slots + ga, block_len(jj, a.n)};
-        if (PERSIST) ea.y = a.blen[static_cast<int64_t>(h) * a.slots + ea.x];
-      }
-      if (gb >= 0) {
-        const int f = gb / a.nb, jj = gb - f * a.nb;
-        eb = PERSIST ? int2{a.C + (f % a.W) * a.nb + jj, 0} : int2{a.slots + gb, block_len(jj, a.n)};
-        if (PERSIST) eb.y = a.blen[static_cast<int64_t>(h) * a.slots + eb.x];
-      }
-      listA[j] = ea;
-      listB[j] = eb;
+      listA[j] = ga >= 0 ? entry(ga) : int2{0, 0};
+      listB[j] = gb >= 0 ? entry(gb) : int2{0, 0};
     }
     int ca = 0, cb = 0;
     for (int j = l; j < a.sel_stride; j += 64) {
@@ -236,8 +268,11 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
   }
   __syncthreads();
   // a shared step takes both halves of one shared block; a private step takes one half
-  // of A's next routed block (X) and the same half of B's (Y)
-  const int nsteps = nshared + 2 * (cntA > cntB ? cntA : cntB);
+  // of A's next routed block (X) and the same half of B's (Y).  The shared phase is
+  // padded to an even number of steps (an empty step) so that both phases alternate the
+  // two LDS buffers in a fixed order.
+  const int nsh2 = nshared + (nshared & 1);
+  const int nsteps = nsh2 + 2 * (cntA > cntB ? cntA : cntB);
 
   RowState<D> st;
   load_row_operand<D>(st.qreg, a.q + h * a.qhs + t0 * a.qts, a.qts, qrow, qlen, h2);
@@ -246,77 +281,130 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
   st.m_run = -INFINITY;
   st.l_run = 0.f;
 
-  // handles are wave-uniform: readfirstlane keeps them (and the gather base addresses)
-  // in scalar registers
-  auto ref_of = [&](int2 e, int half) {
-    KvRef o;
-    const int hd = __builtin_amdgcn_readfirstlane(e.x);
-    const int len = __builtin_amdgcn_readfirstlane(e.y) - 32 * half;
-    if (hd < a.slots) {
-      const int64_t off = (static_cast<int64_t>(h) * a.slots + hd) * kBlock * D + 32 * half * D;
-      o = KvRef{a.ck + off, a.cv + off, D, 0};
-    } else {
-      const int64_t t0b = block_token0(hd - a.slots, a.nb, a.n) + 32 * half;
-      const int64_t off = h * a.xhs + t0b * a.xts;
-      o = KvRef{a.xk + off, a.xv + off, a.xts, 0};
-    }
-    o.len = len < 0 ? 0 : (len < 32 ? len : 32);
-    return o;
+  const char* ck_h = reinterpret_cast<const char*>(a.ck) +
+                     static_cast<int64_t>(h) * a.slots * kCacheBlockBytes;
+  const char* cv_h = reinterpret_cast<const char*>(a.cv) +
+                     static_cast<int64_t>(h) * a.slots * kCacheBlockBytes;
+  const char* xk_h = reinterpret_cast<const char*>(a.xk + h * a.xhs);
+  const char* xv_h = reinterpret_cast<const char*>(a.xv + h * a.xhs);
+  // list entries are wave-uniform: readfirstlane keeps them (and the gather base
+  // addresses) in scalar registers
+  auto ref_of = [&](int2 e, int half, HalfRef& hr) {
+    const uint32_t off = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(e.x));
+    const int y = __builtin_amdgcn_readfirstlane(e.y);
+    const bool tok = (y >> 16) != 0;
+    const uint32_t stride = tok ? xrow : 2 * D;
+    const uint32_t o = off + 32 * half * stride;
+    const int len = (y & 0xffff) - 32 * half;
+    hr.k = (tok ? xk_h : ck_h) + o;
+    hr.v = (tok ? xv_h : cv_h) + o;
+    hr.stride = stride;
+    hr.len = len < 0 ? 0 : (len < 32 ? len : 32);
   };
-  auto refs = [&](int s, KvRef& x, KvRef& y) {
-    x.len = 0;
-    y.len = 0;
+  // This wave's half tile of step s (see the gather below) and the lengths of X and Y.
+  auto refs = [&](int s, HalfRef& mineref, int& lenX, int& lenY) {
+    HalfRef x{nullptr, nullptr, 0, 0}, y{nullptr, nullptr, 0, 0};
     if (s < nshared) {
       const int2 e = shared_list[s];
-      x = ref_of(e, 0);
-      y = ref_of(e, 1);
-    } else {
-      const int j = s - nshared, half = j & 1, blk = j >> 1;
-      if (blk < cntA) x = ref_of(listA[blk], half);
-      if (blk < cntB) y = ref_of(listB[blk], half);
+      ref_of(e, 0, x);
+      ref_of(e, 1, y);
+    } else if (s >= nsh2) {
+      const int j = s - nsh2, half = j & 1, blk = j >> 1;
+      if (blk < cntA) ref_of(listA[blk], half, x);
+      if (blk < cntB) ref_of(listB[blk], half, y);
+    }
+    lenX = x.len;
+    lenY = y.len;
+    const bool use_y = (w & 1) != 0;
+    mineref.k = use_y ? y.k : x.k;
+    mineref.v = use_y ? y.v : x.v;
+    mineref.stride = use_y ? y.stride : x.stride;
+    mineref.len = use_y ? y.len : x.len;
+  };
+
+  // Gather: wave w fills half tile w of a buffer (0: K of X, 1: K of Y, 2: V of X, 3: V of
+  // Y).  Rows past the valid length re-read the last valid row (finite data that the mask
+  // or a zero probability removes).
+  const bool kwave = w < 2;
+  const uint32_t rowl = kwave ? (l & 15) : (l >> 2);
+  const uint32_t colb = 16u * (kwave ? (l >> 4) : (l & 3));
+  auto gather = [&](char (*bufp)[HT::BYTES], const HalfRef& hr) {
+    if (hr.len == 0) return;
+    const char* g = kwave ? hr.k : hr.v;
+    const uint32_t last = static_cast<uint32_t>(hr.len - 1);
+    const uint32_t v0 = min(rowl, last) * hr.stride + colb;
+    const uint32_t v1 = min(16u + rowl, last) * hr.stride + colb;
+    char* dst = bufp[w];
+#pragma unroll
+    for (int p = 0; p < HT::PIECES; ++p) {
+      // K piece p: rows 16 (p / (PIECES/2)) .., chunks 4 (p % (PIECES/2)) ..
+      // V piece p: rows 16 (p % 2) .., segment p / 2
+      const int kr = p / (HT::PIECES / 2), kc = 64 * (p % (HT::PIECES / 2));
+      const int vr = p % 2, vc = 64 * (p / 2);
+      const uint32_t vo = (kwave ? kr : vr) ? v1 : v0;
+      const char* src = g + (kwave ? kc : vc) + vo;
+      __builtin_amdgcn_global_load_lds(src, dst + 1024 * p, 16, 0, 0);
     }
   };
 
-  Tile<D, 256, 32> kx, vx, ky, vy;
-  KvRef x, y;
-  if (nsteps > 0) {
-    refs(0, x, y);
-    kx.load(x.k, x.stride, x.len, t);
-    vx.load(x.v, x.stride, x.len, t);
-    ky.load(y.k, y.stride, y.len, t);
-    vy.load(y.v, y.stride, y.len, t);
-  }
-  for (int s = 0; s < nsteps; ++s) {
-    __syncthreads();  // the previous step's LDS reads are done
-    kx.store_rows(KsX, t);
-    vx.store_rows(VsX, t);
-    ky.store_rows(KsY, t);
-    vy.store_rows(VsY, t);
-    const int lenX = x.len, lenY = y.len;
-    __syncthreads();
-    if (s + 1 < nsteps) {  // next step's gathers are in flight during this step's math
-      refs(s + 1, x, y);
-      kx.load(x.k, x.stride, x.len, t);
-      vx.load(x.v, x.stride, x.len, t);
-      ky.load(y.k, y.stride, y.len, t);
-      vy.load(y.v, y.stride, y.len, t);
+  // this lane's LDS read offsets inside a half tile
+  const int kofs = (c32 >> 4) * HT::KRG + 256 * h2 + 16 * (c32 & 15);
+  const int g16 = l >> 4, i16 = l & 15;
+  const int vofs = (4 * (g16 >> 1) + (i16 >> 2)) * 64 + 32 * (g16 & 1) + 8 * (i16 & 3);
+
+  // Buffers start zeroed: a half tile that a step leaves empty is still read (its scores
+  // are masked and its probabilities are zero) and must hold finite values.
+  {
+    u32x4* z0 = reinterpret_cast<u32x4*>(&buf0[0][0]);
+    u32x4* z1 = reinterpret_cast<u32x4*>(&buf1[0][0]);
+    for (int i = t; i < 4 * HT::BYTES / 16; i += 256) {
+      z0[i] = u32x4{0, 0, 0, 0};
+      z1[i] = u32x4{0, 0, 0, 0};
     }
-    if (qlen > 0) {
-      // a shared step gives every wave both half tiles; a private step gives each wave
-      // pair its own query block's half tile
-      const bool shared_step = s < nshared;
-#pragma unroll 1
-      for (int it = 0; it < 2; ++it) {
-        const bool use_y = shared_step ? it == 1 : mine == 1;
-        const int len = (shared_step || it == 0) ? (use_y ? lenY : lenX) : 0;
-        if (len > 0) {
-          f32x16 sacc[1];
-          sacc[0] = st.scores(use_y ? KsY : KsX, len, c32, h2);
-          const uint16_t* Vs = use_y ? VsY : VsX;
-          st.template update<1>(sacc, Vs, Vs, c, l);
-        }
+  }
+  HalfRef next{nullptr, nullptr, 0, 0};
+  int nX = 0, nY = 0;
+  __syncthreads();
+  if (nsteps > 0) {
+    refs(0, next, nX, nY);
+    gather(buf0, next);
+  }
+  // One step: wait for this step's tiles (buffer cur), start the next step's gathers into
+  // the other buffer (whose readers, the previous step, have all passed the barrier), then
+  // the math.  A shared step gives every wave both half tiles (64 keys); a private step
+  // gives each wave pair its own query block's half tile.
+  auto step = [&](char (*cur)[HT::BYTES], char (*nxt)[HT::BYTES], int s, auto shared_tag) {
+    __syncthreads();
+    const int lx = nX, ly = nY;
+    if (s + 1 < nsteps) {
+      refs(s + 1, next, nX, nY);
+      gather(nxt, next);
+    }
+    if (qlen <= 0) return;
+    if constexpr (decltype(shared_tag)::value) {
+      if (lx > 0) {
+        f32x16 sacc[2];
+        sacc[0] = st.scores(cur[0] + kofs, lx, h2);
+        sacc[1] = st.scores(cur[1] + kofs, ly, h2);
+        st.template update<2>(sacc, cur[2] + vofs, cur[3] + vofs, c);
+      }
+    } else {
+      const int len = mine ? ly : lx;
+      if (len > 0) {
+        f32x16 sacc[1];
+        sacc[0] = st.scores(cur[mine] + kofs, len, h2);
+        st.template update<1>(sacc, cur[2 + mine] + vofs, cur[2 + mine] + vofs, c);
       }
     }
+  };
+  int s = 0;
+  for (; s < nsh2; s += 2) {
+    step(buf0, buf1, s, std::true_type{});
+    step(buf1, buf0, s + 1, std::true_type{});
+  }
+  for (; s < nsteps; s += 2) {
+    step(buf0, buf1, s, std::false_type{});
+    step(buf1, buf0, s + 1, std::false_type{});
   }
 
   const float l_tot = st.l_run + __shfl_xor(st.l_run, 32, 64);
