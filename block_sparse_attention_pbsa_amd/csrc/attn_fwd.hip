@@ -24,8 +24,6 @@
 //   * the next step's global loads are issued before the current step's math.
 // Softmax runs in base 2 with scale*log2(e) folded in (v_exp_f32), P is packed to bf16 with
 // v_cvt_pk_bf16_f32, and the running max is raised lazily; accumulators are fp32.
-#include <type_traits>
-
 #include "attn_common.h"
 
 namespace pbsa {
@@ -72,6 +70,20 @@ struct HalfTile {
 };
 
 // A half tile to gather: wave-uniform base (bytes), row stride (bytes) and valid rows.
+// Full scheduling fence (the compiler may not move instructions across it).
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// Wait until this wave's gathers into LDS have landed.  The barrier that follows makes
+// them visible to the other waves; the compiler does not add this wait by itself (a
+// barrier's release only covers LDS instructions), so every step barrier needs it.
+__device__ __forceinline__ void dma_wait() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
+
+// 16 bytes per lane from global memory straight into LDS (lane l writes lds + 16 l; the
+// LDS address must be wave-uniform).
+__device__ __forceinline__ void lds_dma16(const char* src, char* lds) {
+  __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+}
+
 struct HalfRef {
   const char* k;
   const char* v;
@@ -125,6 +137,209 @@ struct RowState {
 #pragma unroll
       for (int dt = 0; dt < ND; ++dt) acc[dt] = mfma32(vop[dt], pb, acc[dt]);
     }
+  }
+
+  // K operands of one half tile.
+  __device__ __forceinline__ void kread(const char* kb, u32x4 (&kop)[NS]) const {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) kop[s] = *reinterpret_cast<const u32x4*>(kb + 512 * s);
+  }
+  __device__ __forceinline__ f32x16 smma(const u32x4 (&kop)[NS]) const {
+    f32x16 sa = {};
+#pragma unroll
+    for (int s = 0; s < NS; ++s) sa = mfma32(kop[s], qreg[s], sa);
+    return sa;
+  }
+  __device__ __forceinline__ static void mask(f32x16& sa, int len, int h2) {
+    if (len < 32) {
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (acc_row(r, h2) >= len) sa[r] = -INFINITY;
+    }
+  }
+  // Online softmax of one score tile without touching the accumulators: raises the running
+  // max when some row's new max exceeds it by more than 2^8 in exp2 units (so exp2
+  // arguments stay <= 8), folds the factor into l_run and returns it through alpha (the
+  // caller rescales acc when the result is true), and packs P to bf16 for the PV step.
+  __device__ __forceinline__ bool softmax(const f32x16& sa, float c, u32x4 (&pb)[2],
+                                          float& alpha) {
+    float mx = sa[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sa[r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const bool up = __any(mx * c > m_run * c + 8.f);
+    const float m_new = up ? fmaxf(m_run, mx) : m_run;
+    alpha = up ? __builtin_amdgcn_exp2f(m_run * c - m_new * c) : 1.f;
+    m_run = m_new;
+    const float m_off = m_new * c;
+    float p[16];
+    float psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      p[r] = __builtin_amdgcn_exp2f(fmaf(sa[r], c, -m_off));
+      psum += p[r];
+    }
+    l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pb[t2][e] = pack_bf16x2(p[8 * t2 + 2 * e], p[8 * t2 + 2 * e + 1]);
+    return up;
+  }
+  __device__ __forceinline__ void rescale(float alpha) {
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt) acc[dt] *= alpha;
+  }
+  __device__ __forceinline__ void pvmma(const u32x4 (&pb)[2], const char* vb) {
+    lds_u16* base = (lds_u16*)(vb);
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      u32x4 vop[ND];
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) {
+        const s16x4_ lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)(base + (2048 * dt + 1024 * t2) / 2));
+        const s16x4_ hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)(base + (2048 * dt + 1024 * t2 + 512) / 2));
+        const u32x2 x = __builtin_bit_cast(u32x2, lo), y = __builtin_bit_cast(u32x2, hi);
+        vop[dt] = u32x4{x[0], x[1], y[0], y[1]};
+      }
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) acc[dt] = mfma32(vop[dt], pb[t2], acc[dt]);
+    }
+  }
+
+  // The transposing V reads of MFMA j (t2 = j / ND, dt = j % ND) of a PV step.
+  __device__ __forceinline__ static u32x4 vread(const char* vb, int j) {
+    const int t2 = j / ND, dt = j % ND;
+    lds_u16* base = (lds_u16*)(vb);
+    const s16x4_ lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)(base + (2048 * dt + 1024 * t2) / 2));
+    const s16x4_ hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)(base + (2048 * dt + 1024 * t2 + 512) / 2));
+    const u32x2 x = __builtin_bit_cast(u32x2, lo), y = __builtin_bit_cast(u32x2, hi);
+    return u32x4{x[0], x[1], y[0], y[1]};
+  }
+
+  // Softmax of one score tile in stages, so that the stages can ride under MFMAs of the
+  // other tile.  Stage 0: in-lane row max; 1: max with lane l^32 (gfx950 permlane swap, no
+  // LDS round trip), lazy raise of the running max (by more than 2^8 in exp2 units) and
+  // the factor alpha folded into l_run; 2..5: four exponentials each; 6: bf16 packing
+  // and the row sum.
+  struct Soft {
+    float mx, m_off, alpha, psum;
+    float p[16];
+    u32x4 pb[2];
+    bool up;
+  };
+  __device__ __forceinline__ void stage(int k, const f32x16& sa, Soft& so, float c) {
+    if (k == 0) {
+      float mx = fmaxf(sa[0], sa[1]);
+#pragma unroll
+      for (int r = 2; r < 16; ++r) mx = fmaxf(mx, sa[r]);
+      so.mx = mx;
+    } else if (k == 1) {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(so.mx),
+                                                       __float_as_uint(so.mx), false, false);
+      const float mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      so.up = __any(mx * c > m_run * c + 8.f);
+      const float m_new = so.up ? fmaxf(m_run, mx) : m_run;
+      so.alpha = so.up ? __builtin_amdgcn_exp2f(m_run * c - m_new * c) : 1.f;
+      m_run = m_new;
+      so.m_off = m_new * c;
+    } else if (k <= 5) {
+      const int r0 = 4 * (k - 2);
+#pragma unroll
+      for (int r = r0; r < r0 + 4; ++r) so.p[r] = __builtin_amdgcn_exp2f(fmaf(sa[r], c, -so.m_off));
+    } else {
+      float ps = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ps += so.p[r];
+      l_run = l_run * so.alpha + ps;
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          so.pb[t2][e] = pack_bf16x2(so.p[8 * t2 + 2 * e], so.p[8 * t2 + 2 * e + 1]);
+    }
+  }
+
+  // One half tile (a private step): the next step's gather instructions and the V reads
+  // ride under the S MFMAs; the softmax cannot overlap this wave's own MFMAs.
+  template <class Dma>
+  __device__ __forceinline__ void single(const char* kb, const char* vb, int len, float c,
+                                         int h2, Dma&& dma) {
+    u32x4 kop[NS];
+    kread(kb, kop);
+    f32x16 sa = {};
+    u32x4 vop[2 * ND];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      sa = mfma32(kop[i], qreg[i], sa);
+      dma(i);
+      if (i < 2 * ND) vop[i] = vread(vb, i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    mask(sa, len, h2);
+    Soft so;
+#pragma unroll
+    for (int k = 0; k < 7; ++k) stage(k, sa, so, c);
+    asm volatile("" ::"v"(so.pb[0]), "v"(so.pb[1]));
+    if (so.up) rescale(so.alpha);
+#pragma unroll
+    for (int j = 0; j < 2 * ND; ++j) acc[j % ND] = mfma32(vop[j], so.pb[j / ND], acc[j % ND]);
+  }
+
+  // Two half tiles (X then Y) software-pipelined inside the wave, in explicit groups the
+  // scheduler may not merge: the next step's gather instructions (dma(i)) and the K reads
+  // of Y ride under the S MFMAs of X (issued in one burst they would stall the wave); each
+  // S MFMA of Y carries one softmax stage of X and the V reads of X; each PV MFMA of X
+  // carries one softmax stage of Y and the V reads of Y.  The rare accumulator rescales
+  // and tail masks sit between the phases.
+  template <class Dma>
+  __device__ __forceinline__ void pair(const char* kx, const char* ky, const char* vx,
+                                       const char* vy, int lx, int ly, float c, int h2,
+                                       Dma&& dma) {
+    static_assert(NS == 8 && ND == 4, "the pipelined pair is laid out for head_dim 128");
+    u32x4 kop[NS], kopy[NS];
+    kread(kx, kop);
+    f32x16 sx = {};
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      sx = mfma32(kop[i], qreg[i], sx);
+      dma(i);
+      kopy[i] = *reinterpret_cast<const u32x4*>(ky + 512 * i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    mask(sx, lx, h2);
+    Soft so;
+    u32x4 vop[2 * ND];
+    f32x16 sy = {};
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      sy = mfma32(kopy[i], qreg[i], sy);
+      if (i < 7) stage(i, sx, so, c);
+      vop[i] = vread(vx, i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // the exponentials of X stay in the groups above (not sunk past the branch)
+    asm volatile("" ::"v"(so.pb[0]), "v"(so.pb[1]));
+    if (so.up) rescale(so.alpha);
+    mask(sy, ly, h2);
+    Soft sv;
+    u32x4 vopy[2 * ND];
+#pragma unroll
+    for (int j = 0; j < 2 * ND; ++j) {
+      acc[j % ND] = mfma32(vop[j], so.pb[j / ND], acc[j % ND]);
+      if (j < 7) stage(j, sy, sv, c);
+      vopy[j] = vread(vy, j);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    asm volatile("" ::"v"(sv.pb[0]), "v"(sv.pb[1]));
+    if (sv.up) rescale(sv.alpha);
+#pragma unroll
+    for (int j = 0; j < 2 * ND; ++j) acc[j % ND] = mfma32(vopy[j], sv.pb[j / ND], acc[j % ND]);
   }
 
   // Online-softmax update with NT score tiles (32 keys each) and their V half tiles.
@@ -328,6 +543,17 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
   const bool kwave = w < 2;
   const uint32_t rowl = kwave ? (l & 15) : (l >> 2);
   const uint32_t colb = 16u * (kwave ? (l >> 4) : (l & 3));
+  // One gather instruction (piece p of this wave's half tile).
+  auto gather_piece = [&](char (*bufp)[HT::BYTES], const HalfRef& hr, int p) {
+    if (hr.len == 0) return;
+    const char* g = kwave ? hr.k : hr.v;
+    const uint32_t last = static_cast<uint32_t>(hr.len - 1);
+    const int kr = p / (HT::PIECES / 2), kc = 64 * (p % (HT::PIECES / 2));
+    const int vr = p % 2, vc = 64 * (p / 2);
+    const uint32_t row = ((kwave ? kr : vr) ? 16u : 0u) + rowl;
+    const uint32_t vo = min(row, last) * hr.stride + colb;
+    lds_dma16(g + (kwave ? kc : vc) + vo, bufp[w] + 1024 * p);
+  };
   auto gather = [&](char (*bufp)[HT::BYTES], const HalfRef& hr) {
     if (hr.len == 0) return;
     const char* g = kwave ? hr.k : hr.v;
@@ -343,7 +569,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
       const int vr = p % 2, vc = 64 * (p / 2);
       const uint32_t vo = (kwave ? kr : vr) ? v1 : v0;
       const char* src = g + (kwave ? kc : vc) + vo;
-      __builtin_amdgcn_global_load_lds(src, dst + 1024 * p, 16, 0, 0);
+      lds_dma16(src, dst + 1024 * p);
     }
   };
 
@@ -373,38 +599,56 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
   // the other buffer (whose readers, the previous step, have all passed the barrier), then
   // the math.  A shared step gives every wave both half tiles (64 keys); a private step
   // gives each wave pair its own query block's half tile.
-  auto step = [&](char (*cur)[HT::BYTES], char (*nxt)[HT::BYTES], int s, auto shared_tag) {
+  auto step = [&](char (*cur)[HT::BYTES], char (*nxt)[HT::BYTES], int s, bool kShared) {
+    dma_wait();
     __syncthreads();
     const int lx = nX, ly = nY;
-    if (s + 1 < nsteps) {
-      refs(s + 1, next, nX, nY);
-      gather(nxt, next);
-    }
+    const bool more = s + 1 < nsteps;
+    if (more) refs(s + 1, next, nX, nY);
+    const int len = kShared ? lx : (mine ? ly : lx);
+    // with head_dim 128 the gathers ride inside the math (dma below); otherwise, or when
+    // this wave has no math in this step, they are issued here
+    const bool inside = D == 128 && qlen > 0 && len > 0;
+    if (more && !inside) gather(nxt, next);
+    if (!inside && D == 128) return;
     if (qlen <= 0) return;
-    if constexpr (decltype(shared_tag)::value) {
+    auto dma = [&](int p) {
+      if (more && p < HT::PIECES) {
+        sched_fence();
+        gather_piece(nxt, next, p);
+      }
+    };
+    if (kShared) {
       if (lx > 0) {
-        f32x16 sacc[2];
-        sacc[0] = st.scores(cur[0] + kofs, lx, h2);
-        sacc[1] = st.scores(cur[1] + kofs, ly, h2);
-        st.template update<2>(sacc, cur[2] + vofs, cur[3] + vofs, c);
+        if constexpr (D == 128) {
+          st.pair(cur[0] + kofs, cur[1] + kofs, cur[2] + vofs, cur[3] + vofs, lx, ly, c, h2, dma);
+        } else {
+          f32x16 sacc[2];
+          sacc[0] = st.scores(cur[0] + kofs, lx, h2);
+          sacc[1] = st.scores(cur[1] + kofs, ly, h2);
+          st.template update<2>(sacc, cur[2] + vofs, cur[3] + vofs, c);
+        }
       }
     } else {
-      const int len = mine ? ly : lx;
       if (len > 0) {
-        f32x16 sacc[1];
-        sacc[0] = st.scores(cur[mine] + kofs, len, h2);
-        st.template update<1>(sacc, cur[2 + mine] + vofs, cur[2 + mine] + vofs, c);
+        if constexpr (D == 128) {
+          st.single(cur[mine] + kofs, cur[2 + mine] + vofs, len, c, h2, dma);
+        } else {
+          f32x16 sacc[1];
+          sacc[0] = st.scores(cur[mine] + kofs, len, h2);
+          st.template update<1>(sacc, cur[2 + mine] + vofs, cur[2 + mine] + vofs, c);
+        }
       }
     }
   };
   int s = 0;
   for (; s < nsh2; s += 2) {
-    step(buf0, buf1, s, std::true_type{});
-    step(buf1, buf0, s + 1, std::true_type{});
+    step(buf0, buf1, s, true);
+    step(buf1, buf0, s + 1, true);
   }
   for (; s < nsteps; s += 2) {
-    step(buf0, buf1, s, std::false_type{});
-    step(buf1, buf0, s + 1, std::false_type{});
+    step(buf0, buf1, s, false);
+    step(buf1, buf0, s + 1, false);
   }
 
   const float l_tot = st.l_run + __shfl_xor(st.l_run, 32, 64);
