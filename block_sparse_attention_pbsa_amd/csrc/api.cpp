@@ -201,6 +201,11 @@ pbsa_status pbsa_attn_fwd(const pbsa_dims* dims, pbsa_tensor q, const pbsa_cache
   PBSA_TRY(check_tok(chunk_v, "chunk_v", dims->head_dim));
   PBSA_TRY(check_tok(o, "o", dims->head_dim));
   const int64_t ctok = int64_t{dims->chunk_frames} * dims->frame_tokens;
+  const int64_t list = int64_t{dims->capacity} + int64_t{dims->chunk_frames} * pbsa::nb_of(*dims) +
+                       2 * int64_t{dims->topk};
+  if (list > pbsa::kAttnListCap)
+    return fail(PBSA_ERR_UNSUPPORTED, "capacity + chunk blocks + 2*topk = %lld exceeds %d",
+                static_cast<long long>(list), pbsa::kAttnListCap);
   PBSA_TRY(check_span(chunk_k, "chunk_k", ctok, dims->head_dim));
   PBSA_TRY(check_span(chunk_v, "chunk_v", ctok, dims->head_dim));
   if (!sel || !lse) return fail(PBSA_ERR_NULL, "sel and lse are required");
@@ -274,7 +279,8 @@ pbsa_status pbsa_attn_fwd_2lvl(const pbsa_dims* dims, int32_t chunks, pbsa_tenso
   PBSA_TRY(check_tok(o, "o", dims->head_dim));
   if (!sel || !nsel || !lse) return fail(PBSA_ERR_NULL, "sel, nsel and lse are required");
   if (max_sel < 1) return fail(PBSA_ERR_SHAPE, "max_sel must be >= 1");
-  if (max_sel > 4096) return fail(PBSA_ERR_UNSUPPORTED, "max_sel must be <= 4096");
+  if (2 * int64_t{max_sel} > pbsa::kAttnListCap)
+    return fail(PBSA_ERR_UNSUPPORTED, "max_sel must be <= %d", pbsa::kAttnListCap / 2);
   const int64_t ctok = int64_t{chunks} * dims->chunk_frames * dims->frame_tokens;
   PBSA_TRY(check_span(k, "k", ctok, dims->head_dim));
   PBSA_TRY(check_span(v, "v", ctok, dims->head_dim));

@@ -21,7 +21,10 @@
 //   * O^T += V^T P^T on the same MFMA, P converted to bf16 straight from the S^T
 //     accumulators (the contraction order over keys is permuted identically in both
 //     operands, which leaves the sum unchanged);
-//   * the next step's global loads are issued before the current step's math.
+//   * gathers run two steps ahead for K and one step ahead for V: a step is split by a
+//     mid barrier into its S phase (reads K) and its PV phase (reads V), so K's buffer is
+//     free halfway through the step and V's at its end; the gather instructions are issued
+//     a few at a time between MFMAs (issued in one burst they stall the wave).
 // Softmax runs in base 2 with scale*log2(e) folded in (v_exp_f32), P is packed to bf16 with
 // v_cvt_pk_bf16_f32, and the running max is raised lazily; accumulators are fp32.
 #include "attn_common.h"
@@ -73,10 +76,28 @@ struct HalfTile {
 // Full scheduling fence (the compiler may not move instructions across it).
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
-// Wait until this wave's gathers into LDS have landed.  The barrier that follows makes
-// them visible to the other waves; the compiler does not add this wait by itself (a
-// barrier's release only covers LDS instructions), so every step barrier needs it.
-__device__ __forceinline__ void dma_wait() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
+// Wait until at most N of this wave's vector-memory instructions (here: gathers into LDS)
+// are outstanding; they complete in issue order.  A barrier after it makes the landed
+// tiles visible to the other waves.  The compiler does not add this wait by itself (a
+// barrier's release only covers LDS instructions), so every barrier that publishes
+// gathered tiles needs one.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0f70 | N);  // vmcnt(N), expcnt and lgkmcnt not waited
+}
+
+// Workgroup barrier that waits for this wave's LDS instructions (lgkmcnt(0)) but not for
+// its gathers into LDS.  __syncthreads() (and any workgroup fence) would also wait for
+// every outstanding gather; here the gathers are waited for explicitly (vm_wait) and only
+// as far as each barrier needs.  The empty asm statements keep the compiler from moving
+// memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt not waited
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // 16 bytes per lane from global memory straight into LDS (lane l writes lds + 16 l; the
 // LDS address must be wave-uniform).
@@ -247,7 +268,8 @@ struct RowState {
       const float m_new = so.up ? fmaxf(m_run, mx) : m_run;
       so.alpha = so.up ? __builtin_amdgcn_exp2f(m_run * c - m_new * c) : 1.f;
       m_run = m_new;
-      so.m_off = m_new * c;
+      // no valid key yet (a fully masked tile before any other): any finite offset works
+      so.m_off = m_new > -INFINITY ? m_new * c : 0.f;
     } else if (k <= 5) {
       const int r0 = 4 * (k - 2);
 #pragma unroll
@@ -265,42 +287,55 @@ struct RowState {
     }
   }
 
-  // One half tile (a private step): the next step's gather instructions and the V reads
-  // ride under the S MFMAs; the softmax cannot overlap this wave's own MFMAs.
+  // The pipelined steps (head_dim 128) come in two halves around the step's mid barrier:
+  // A = the S phase (reads K), B = the PV phase (reads V).  Scheduling groups are explicit
+  // (sched_fence) and each carries one gather instruction (dma(i)) so that the gathers are
+  // issued between MFMAs; issued in one burst they would stall the wave.
+  struct Mid {
+    f32x16 sy;  // S of the second half tile (pair)
+    Soft so;    // softmax of the first half tile
+  };
+
+  // One half tile (a private step), S phase: S MFMAs with the gathers, then the softmax
+  // (it cannot overlap this wave's own MFMAs here).
   template <class Dma>
-  __device__ __forceinline__ void single(const char* kb, const char* vb, int len, float c,
-                                         int h2, Dma&& dma) {
+  __device__ __forceinline__ void singleA(const char* kb, int len, float c, int h2, Dma&& dma,
+                                          Mid& md) {
     u32x4 kop[NS];
     kread(kb, kop);
     f32x16 sa = {};
-    u32x4 vop[2 * ND];
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       sa = mfma32(kop[i], qreg[i], sa);
       dma(i);
-      if (i < 2 * ND) vop[i] = vread(vb, i);
-      __builtin_amdgcn_sched_barrier(0);
+      sched_fence();
     }
     mask(sa, len, h2);
-    Soft so;
 #pragma unroll
-    for (int k = 0; k < 7; ++k) stage(k, sa, so, c);
-    asm volatile("" ::"v"(so.pb[0]), "v"(so.pb[1]));
-    if (so.up) rescale(so.alpha);
+    for (int k = 0; k < 7; ++k) stage(k, sa, md.so, c);
+    asm volatile("" ::"v"(md.so.pb[0]), "v"(md.so.pb[1]));
+  }
+  // PV phase of a private step: the V reads run two MFMAs ahead.
+  template <class Dma>
+  __device__ __forceinline__ void singleB(const char* vb, Dma&& dma, Mid& md) {
+    if (md.so.up) rescale(md.so.alpha);
+    u32x4 vop[2 * ND];
+    vop[0] = vread(vb, 0);
+    vop[1] = vread(vb, 1);
 #pragma unroll
-    for (int j = 0; j < 2 * ND; ++j) acc[j % ND] = mfma32(vop[j], so.pb[j / ND], acc[j % ND]);
+    for (int j = 0; j < 2 * ND; ++j) {
+      acc[j % ND] = mfma32(vop[j], md.so.pb[j / ND], acc[j % ND]);
+      if (j + 2 < 2 * ND) vop[j + 2] = vread(vb, j + 2);
+      dma(j);
+      sched_fence();
+    }
   }
 
-  // Two half tiles (X then Y) software-pipelined inside the wave, in explicit groups the
-  // scheduler may not merge: the next step's gather instructions (dma(i)) and the K reads
-  // of Y ride under the S MFMAs of X (issued in one burst they would stall the wave); each
-  // S MFMA of Y carries one softmax stage of X and the V reads of X; each PV MFMA of X
-  // carries one softmax stage of Y and the V reads of Y.  The rare accumulator rescales
-  // and tail masks sit between the phases.
+  // Two half tiles (X then Y, a shared step), S phase: the gathers and the K reads of Y
+  // ride under the S MFMAs of X; each S MFMA of Y carries one softmax stage of X.
   template <class Dma>
-  __device__ __forceinline__ void pair(const char* kx, const char* ky, const char* vx,
-                                       const char* vy, int lx, int ly, float c, int h2,
-                                       Dma&& dma) {
+  __device__ __forceinline__ void pairA(const char* kx, const char* ky, int lx, float c, int h2,
+                                        Dma&& dma, Mid& md) {
     static_assert(NS == 8 && ND == 4, "the pipelined pair is laid out for head_dim 128");
     u32x4 kop[NS], kopy[NS];
     kread(kx, kop);
@@ -310,36 +345,47 @@ struct RowState {
       sx = mfma32(kop[i], qreg[i], sx);
       dma(i);
       kopy[i] = *reinterpret_cast<const u32x4*>(ky + 512 * i);
-      __builtin_amdgcn_sched_barrier(0);
+      sched_fence();
     }
     mask(sx, lx, h2);
-    Soft so;
-    u32x4 vop[2 * ND];
-    f32x16 sy = {};
+    md.sy = f32x16{};
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
-      sy = mfma32(kopy[i], qreg[i], sy);
-      if (i < 7) stage(i, sx, so, c);
-      vop[i] = vread(vx, i);
-      __builtin_amdgcn_sched_barrier(0);
+      md.sy = mfma32(kopy[i], qreg[i], md.sy);
+      if (i < 7) stage(i, sx, md.so, c);
+      sched_fence();
     }
-    // the exponentials of X stay in the groups above (not sunk past the branch)
-    asm volatile("" ::"v"(so.pb[0]), "v"(so.pb[1]));
-    if (so.up) rescale(so.alpha);
-    mask(sy, ly, h2);
+    // the exponentials of X stay in the groups above (not sunk past later branches)
+    asm volatile("" ::"v"(md.so.pb[0]), "v"(md.so.pb[1]));
+  }
+  // PV phase of a shared step: each PV MFMA of X carries one softmax stage of Y and a
+  // gather; the V reads run two MFMAs ahead.  The rare rescales sit between the phases.
+  template <class Dma>
+  __device__ __forceinline__ void pairB(const char* vx, const char* vy, int ly, float c, int h2,
+                                        Dma&& dma, Mid& md) {
+    if (md.so.up) rescale(md.so.alpha);
+    mask(md.sy, ly, h2);
     Soft sv;
-    u32x4 vopy[2 * ND];
+    u32x4 vop[4 * ND];  // V of X (0..7), then V of Y (8..15)
+    vop[0] = vread(vx, 0);
+    vop[1] = vread(vx, 1);
 #pragma unroll
     for (int j = 0; j < 2 * ND; ++j) {
-      acc[j % ND] = mfma32(vop[j], so.pb[j / ND], acc[j % ND]);
-      if (j < 7) stage(j, sy, sv, c);
-      vopy[j] = vread(vy, j);
-      __builtin_amdgcn_sched_barrier(0);
+      acc[j % ND] = mfma32(vop[j], md.so.pb[j / ND], acc[j % ND]);
+      const int nx = j + 2;
+      vop[nx] = nx < 2 * ND ? vread(vx, nx) : vread(vy, nx - 2 * ND);
+      if (j < 7) stage(j, md.sy, sv, c);
+      dma(j);
+      sched_fence();
     }
     asm volatile("" ::"v"(sv.pb[0]), "v"(sv.pb[1]));
     if (sv.up) rescale(sv.alpha);
 #pragma unroll
-    for (int j = 0; j < 2 * ND; ++j) acc[j % ND] = mfma32(vopy[j], sv.pb[j / ND], acc[j % ND]);
+    for (int j = 0; j < 2 * ND; ++j) {
+      acc[j % ND] = mfma32(vop[2 * ND + j], sv.pb[j / ND], acc[j % ND]);
+      if (j + 2 < 2 * ND) vop[2 * ND + j + 2] = vread(vy, j + 2);
+      sched_fence();
+    }
   }
 
   // Online-softmax update with NT score tiles (32 keys each) and their V half tiles.
@@ -361,7 +407,7 @@ struct RowState {
 #pragma unroll
       for (int dt = 0; dt < ND; ++dt) acc[dt] *= alpha;
     }
-    const float m_off = m_run * c;
+    const float m_off = m_run > -INFINITY ? m_run * c : 0.f;
     float psum = 0.f;
 #pragma unroll
     for (int kt = 0; kt < NT; ++kt)
@@ -383,11 +429,16 @@ struct RowState {
 template <int D, bool PERSIST>
 __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
   using HT = HalfTile<D>;
-  // Two buffers of four half tiles each (K of X, K of Y, V of X, V of Y): one step's
-  // tiles are gathered straight into LDS while the previous step's are used.
-  __shared__ __attribute__((aligned(1024))) char buf0[4][HT::BYTES];
-  __shared__ __attribute__((aligned(1024))) char buf1[4][HT::BYTES];
-  extern __shared__ int2 lists[];
+  // K and V half tiles (X and Y) of even and odd steps, gathered straight into LDS; four
+  // distinct arrays so that the compiler can tell a gather's target from the tiles being
+  // read.
+  __shared__ __attribute__((aligned(1024))) char kb0[2][HT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char kb1[2][HT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char vb0[2][HT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char vb1[2][HT::BYTES];
+  // Block lists: static (a dynamic LDS array defeats the compiler's alias analysis, which
+  // then waits for every gather in flight before each list read).
+  __shared__ uint32_t lists[kAttnListCap];
   __shared__ int wave_cnt[4];
   __shared__ int n_list;
 
@@ -408,20 +459,23 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
   const float c = a.scale * kLog2e;
   int cntA, cntB;
 
-  // Block lists in LDS as (byte offset, valid rows | kind << 16): kind 0 is a cache slot
-  // (offset from the head's cache base), kind 1 a block of the token tensors xk/xv
-  // (offset from the head's base there).  Shared list (persistent mode): occupied P slots
-  // in slot order, then the chunk's blocks.  Private lists: A's and B's routed blocks.
+  // Block list entries (32 bits): bit 31 = token block of xk/xv (else a cache slot), bits
+  // 24..30 = valid rows, bits 0..23 = the cache slot, or frame << 10 | block-in-frame.
+  // Shared list (persistent mode): occupied P slots in slot order, then the chunk's
+  // blocks.  Private lists: A's and B's routed blocks.
   constexpr uint32_t kCacheBlockBytes = kBlock * D * 2;
   const uint32_t xrow = static_cast<uint32_t>(a.xts * 2);
   auto tok_entry = [&](int g) {
     const int f = g / a.nb, jj = g - f * a.nb;
-    const uint32_t tok = static_cast<uint32_t>(f) * a.n + kBlock * jj;
-    return int2{static_cast<int>(tok * xrow), block_len(jj, a.n) | (1 << 16)};
+    return 0x80000000u | (static_cast<uint32_t>(block_len(jj, a.n)) << 24) |
+           (static_cast<uint32_t>(f) << 10) | static_cast<uint32_t>(jj);
   };
-  int2* shared_list = lists;
-  int2* listA = lists + (PERSIST ? a.C + a.nq : 0);
-  int2* listB = listA + a.sel_stride;
+  auto slot_entry = [&](int slot, int len) {
+    return (static_cast<uint32_t>(len) << 24) | static_cast<uint32_t>(slot);
+  };
+  uint32_t* shared_list = lists;
+  uint32_t* listA = lists + (PERSIST ? a.C + a.nq : 0);
+  uint32_t* listB = listA + a.sel_stride;
   int nshared = 0;
   if (PERSIST) {
     if (t == 0) n_list = 0;
@@ -436,9 +490,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
       __syncthreads();
       int off = n_list;
       for (int u = 0; u < w; ++u) off += wave_cnt[u];
-      if (valid)
-        shared_list[off + __popcll(m & ((1ull << l) - 1ull))] =
-            int2{static_cast<int>(s * kCacheBlockBytes), lh[s]};
+      if (valid) shared_list[off + __popcll(m & ((1ull << l) - 1ull))] = slot_entry(s, lh[s]);
       __syncthreads();
       if (t == 0) n_list += wave_cnt[0] + wave_cnt[1] + wave_cnt[2] + wave_cnt[3];
       __syncthreads();
@@ -459,14 +511,13 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
       if (!PERSIST) return tok_entry(g);
       const int f = g / a.nb, jj = g - f * a.nb;
       const int slot = a.C + (f % a.W) * a.nb + jj;
-      return int2{static_cast<int>(slot * kCacheBlockBytes),
-                  a.blen[static_cast<int64_t>(h) * a.slots + slot]};
+      return slot_entry(slot, a.blen[static_cast<int64_t>(h) * a.slots + slot]);
     };
     for (int j = t; j < a.sel_stride; j += 256) {
       const int ga = j < na ? sa[j] : -1;
       const int gb = j < nbb ? sb[j] : -1;
-      listA[j] = ga >= 0 ? entry(ga) : int2{0, 0};
-      listB[j] = gb >= 0 ? entry(gb) : int2{0, 0};
+      listA[j] = ga >= 0 ? entry(ga) : 0u;
+      listB[j] = gb >= 0 ? entry(gb) : 0u;
     }
     int ca = 0, cb = 0;
     for (int j = l; j < a.sel_stride; j += 64) {
@@ -504,152 +555,200 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
   const char* xv_h = reinterpret_cast<const char*>(a.xv + h * a.xhs);
   // list entries are wave-uniform: readfirstlane keeps them (and the gather base
   // addresses) in scalar registers
-  auto ref_of = [&](int2 e, int half, HalfRef& hr) {
-    const uint32_t off = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(e.x));
-    const int y = __builtin_amdgcn_readfirstlane(e.y);
-    const bool tok = (y >> 16) != 0;
+  auto ref_of = [&](uint32_t e_, int half, HalfRef& hr) {
+    const uint32_t e = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(e_)));
+    const bool tok = (e >> 31) != 0;
+    const int full = static_cast<int>((e >> 24) & 0x7f);
+    const uint32_t id = e & 0xffffffu;
+    const uint32_t off =
+        tok ? ((id >> 10) * static_cast<uint32_t>(a.n) + kBlock * (id & 1023u)) * xrow
+            : id * kCacheBlockBytes;
     const uint32_t stride = tok ? xrow : 2 * D;
     const uint32_t o = off + 32 * half * stride;
-    const int len = (y & 0xffff) - 32 * half;
+    const int len = full - 32 * half;
     hr.k = (tok ? xk_h : ck_h) + o;
     hr.v = (tok ? xv_h : cv_h) + o;
     hr.stride = stride;
     hr.len = len < 0 ? 0 : (len < 32 ? len : 32);
   };
-  // This wave's half tile of step s (see the gather below) and the lengths of X and Y.
-  auto refs = [&](int s, HalfRef& mineref, int& lenX, int& lenY) {
-    HalfRef x{nullptr, nullptr, 0, 0}, y{nullptr, nullptr, 0, 0};
+  // Raw list entries of step s for X and Y (0 = nothing).  They are read one step before
+  // they are decoded, so the LDS read's latency is never waited for.
+  auto fetch = [&](int s, uint32_t& ex, uint32_t& ey) {
+    ex = 0;
+    ey = 0;
+    if (s >= nsteps) return;
     if (s < nshared) {
-      const int2 e = shared_list[s];
-      ref_of(e, 0, x);
-      ref_of(e, 1, y);
+      ex = shared_list[s];
+      ey = ex;
     } else if (s >= nsh2) {
-      const int j = s - nsh2, half = j & 1, blk = j >> 1;
-      if (blk < cntA) ref_of(listA[blk], half, x);
-      if (blk < cntB) ref_of(listB[blk], half, y);
+      const int blk = (s - nsh2) >> 1;
+      if (blk < cntA) ex = listA[blk];
+      if (blk < cntB) ey = listB[blk];
     }
+  };
+  // This wave's half tile of step s (see the gathers below) and the lengths of X and Y.
+  auto decode = [&](int s, uint32_t ex, uint32_t ey, HalfRef& mineref, int& lenX, int& lenY) {
+    HalfRef x{nullptr, nullptr, 0, 0}, y{nullptr, nullptr, 0, 0};
+    // a shared step takes halves 0 (X) and 1 (Y) of one block; a private step the same
+    // half of A's (X) and B's (Y) next routed block
+    const int hx = s < nshared ? 0 : ((s - nsh2) & 1);
+    const int hy = s < nshared ? 1 : hx;
+    if (ex) ref_of(ex, hx, x);
+    if (ey) ref_of(ey, hy, y);
     lenX = x.len;
     lenY = y.len;
-    const bool use_y = (w & 1) != 0;
+    const bool use_y = (w >> 1) != 0;
     mineref.k = use_y ? y.k : x.k;
     mineref.v = use_y ? y.v : x.v;
     mineref.stride = use_y ? y.stride : x.stride;
     mineref.len = use_y ? y.len : x.len;
-  };
-
-  // Gather: wave w fills half tile w of a buffer (0: K of X, 1: K of Y, 2: V of X, 3: V of
-  // Y).  Rows past the valid length re-read the last valid row (finite data that the mask
-  // or a zero probability removes).
-  const bool kwave = w < 2;
-  const uint32_t rowl = kwave ? (l & 15) : (l >> 2);
-  const uint32_t colb = 16u * (kwave ? (l >> 4) : (l & 3));
-  // One gather instruction (piece p of this wave's half tile).
-  auto gather_piece = [&](char (*bufp)[HT::BYTES], const HalfRef& hr, int p) {
-    if (hr.len == 0) return;
-    const char* g = kwave ? hr.k : hr.v;
-    const uint32_t last = static_cast<uint32_t>(hr.len - 1);
-    const int kr = p / (HT::PIECES / 2), kc = 64 * (p % (HT::PIECES / 2));
-    const int vr = p % 2, vc = 64 * (p / 2);
-    const uint32_t row = ((kwave ? kr : vr) ? 16u : 0u) + rowl;
-    const uint32_t vo = min(row, last) * hr.stride + colb;
-    lds_dma16(g + (kwave ? kc : vc) + vo, bufp[w] + 1024 * p);
-  };
-  auto gather = [&](char (*bufp)[HT::BYTES], const HalfRef& hr) {
-    if (hr.len == 0) return;
-    const char* g = kwave ? hr.k : hr.v;
-    const uint32_t last = static_cast<uint32_t>(hr.len - 1);
-    const uint32_t v0 = min(rowl, last) * hr.stride + colb;
-    const uint32_t v1 = min(16u + rowl, last) * hr.stride + colb;
-    char* dst = bufp[w];
-#pragma unroll
-    for (int p = 0; p < HT::PIECES; ++p) {
-      // K piece p: rows 16 (p / (PIECES/2)) .., chunks 4 (p % (PIECES/2)) ..
-      // V piece p: rows 16 (p % 2) .., segment p / 2
-      const int kr = p / (HT::PIECES / 2), kc = 64 * (p % (HT::PIECES / 2));
-      const int vr = p % 2, vc = 64 * (p / 2);
-      const uint32_t vo = (kwave ? kr : vr) ? v1 : v0;
-      const char* src = g + (kwave ? kc : vc) + vo;
-      lds_dma16(src, dst + 1024 * p);
+    if (mineref.len == 0) {
+      // an empty half tile still gets its gathers (of the head's first token row, so
+      // that every step issues the same number and the waits stay fixed); its rows are
+      // masked or weighted by zero
+      mineref.k = xk_h;
+      mineref.v = xv_h;
+      mineref.stride = 0;
     }
   };
+
+  // Gathers: waves 0, 1 gather half tile X of every step, waves 2, 3 half tile Y; each
+  // wave takes half of the tile's K pieces and half of its V pieces, so that every wave
+  // issues the same sequence (K(s), V(s), K(s+1), V(s+1), ...) and the waits below are
+  // exact.  Rows past the valid length re-read the last valid row (finite data that the
+  // mask or a zero probability removes).
+  constexpr int HP = HT::PIECES / 2;  // pieces of K (and of V) per wave and step
+  const int p0 = (w & 1) * HP;        // this wave's first piece
+  const int tw = w >> 1;              // this wave's half tile: 0 = X, 1 = Y
+  const uint32_t k_rowl = l & 15, k_colb = 16u * (l >> 4);
+  const uint32_t v_rowl = l >> 2, v_colb = 16u * (l & 3);
+  //   K piece p: rows 16 (p / HP) .., chunks 4 (p % HP) ..
+  //   V piece p: rows 16 (p % 2) .., 32-channel segment p / 2
+  auto gather_k = [&](char (*buf)[HT::BYTES], const HalfRef& hr, int i) {
+    const int p = p0 + i;
+    const uint32_t last = static_cast<uint32_t>(hr.len > 0 ? hr.len - 1 : 0);
+    const uint32_t row = (p / HP ? 16u : 0u) + k_rowl;
+    lds_dma16(hr.k + 64 * (p % HP) + min(row, last) * hr.stride + k_colb,
+              buf[tw] + 1024 * p);
+  };
+  auto gather_v = [&](char (*buf)[HT::BYTES], const HalfRef& hr, int i) {
+    const int p = p0 + i;
+    const uint32_t last = static_cast<uint32_t>(hr.len > 0 ? hr.len - 1 : 0);
+    const uint32_t row = (p % 2 ? 16u : 0u) + v_rowl;
+    lds_dma16(hr.v + 64 * (p / 2) + min(row, last) * hr.stride + v_colb, buf[tw] + 1024 * p);
+  };
+  // Waits before the barriers that publish gathered tiles.  Each wave's gathers in issue
+  // order: K(s), V(s), K(s+1), V(s+1), ... (HP instructions each).  Before the top barrier
+  // of step s, K(s) must have landed (V(s) and K(s+1) may be in flight); before the mid
+  // barrier V(s) (K(s+1) and V(s+1) may be in flight).
+  auto wait_keep_next = [&]() { vm_wait<2 * HP>(); };
 
   // this lane's LDS read offsets inside a half tile
   const int kofs = (c32 >> 4) * HT::KRG + 256 * h2 + 16 * (c32 & 15);
   const int g16 = l >> 4, i16 = l & 15;
   const int vofs = (4 * (g16 >> 1) + (i16 >> 2)) * 64 + 32 * (g16 & 1) + 8 * (i16 & 3);
 
-  // Buffers start zeroed: a half tile that a step leaves empty is still read (its scores
-  // are masked and its probabilities are zero) and must hold finite values.
+  // V buffers start zeroed: a V half tile that a step leaves empty is still read (with
+  // zero probabilities) and must hold finite values.  (Empty K half tiles are masked.)
   {
-    u32x4* z0 = reinterpret_cast<u32x4*>(&buf0[0][0]);
-    u32x4* z1 = reinterpret_cast<u32x4*>(&buf1[0][0]);
-    for (int i = t; i < 4 * HT::BYTES / 16; i += 256) {
+    u32x4* z0 = reinterpret_cast<u32x4*>(&vb0[0][0]);
+    u32x4* z1 = reinterpret_cast<u32x4*>(&vb1[0][0]);
+    for (int i = t; i < 2 * HT::BYTES / 16; i += 256) {
       z0[i] = u32x4{0, 0, 0, 0};
       z1[i] = u32x4{0, 0, 0, 0};
     }
   }
-  HalfRef next{nullptr, nullptr, 0, 0};
-  int nX = 0, nY = 0;
+  // r1, r2: this wave's half tile of steps s+1 and s+2; (lx0, ly0) .. (lx2, ly2): the
+  // lengths of X and Y in steps s, s+1, s+2.
+  HalfRef r0{nullptr, nullptr, 0, 0}, r1{nullptr, nullptr, 0, 0}, r2{nullptr, nullptr, 0, 0};
+  int lx0 = 0, ly0 = 0, lx1 = 0, ly1 = 0, lx2 = 0, ly2 = 0;
+  uint32_t ex = 0, ey = 0;
+  fetch(0, ex, ey);
+  decode(0, ex, ey, r0, lx0, ly0);
+  fetch(1, ex, ey);
+  decode(1, ex, ey, r1, lx1, ly1);
+  fetch(2, ex, ey);
+  vm_wait<0>();  // Q (and the list inputs) have landed: the loop's waits count gathers only
   __syncthreads();
-  if (nsteps > 0) {
-    refs(0, next, nX, nY);
-    gather(buf0, next);
-  }
-  // One step: wait for this step's tiles (buffer cur), start the next step's gathers into
-  // the other buffer (whose readers, the previous step, have all passed the barrier), then
-  // the math.  A shared step gives every wave both half tiles (64 keys); a private step
-  // gives each wave pair its own query block's half tile.
-  auto step = [&](char (*cur)[HT::BYTES], char (*nxt)[HT::BYTES], int s, bool kShared) {
-    dma_wait();
-    __syncthreads();
-    const int lx = nX, ly = nY;
-    const bool more = s + 1 < nsteps;
-    if (more) refs(s + 1, next, nX, nY);
+#pragma unroll
+  for (int i = 0; i < HP; ++i) gather_k(kb0, r0, i);
+#pragma unroll
+  for (int i = 0; i < HP; ++i) gather_v(vb0, r0, i);
+#pragma unroll
+  for (int i = 0; i < HP; ++i) gather_k(kb1, r1, i);
+  // Step s (kc/vc: its K and V buffers, vn: V buffer of step s+1):
+  //   top barrier (K(s) published) -> V(s+1) gathers under the S phase -> mid barrier
+  //   (V(s) published; every wave is done with K(s)) -> K(s+2) gathers into kc under the
+  //   PV phase.
+  // A shared step gives every wave both half tiles (64 keys); a private step gives each
+  // wave pair its own query block's half tile.
+  auto step = [&](char (*kc)[HT::BYTES], char (*vc)[HT::BYTES], char (*vn)[HT::BYTES], int s,
+                  bool kShared) {
+    wait_keep_next();
+    lds_barrier();
+    decode(s + 2, ex, ey, r2, lx2, ly2);
+    fetch(s + 3, ex, ey);
+    const int lx = lx0, ly = ly0;
     const int len = kShared ? lx : (mine ? ly : lx);
-    // with head_dim 128 the gathers ride inside the math (dma below); otherwise, or when
-    // this wave has no math in this step, they are issued here
-    const bool inside = D == 128 && qlen > 0 && len > 0;
-    if (more && !inside) gather(nxt, next);
-    if (!inside && D == 128) return;
-    if (qlen <= 0) return;
-    auto dma = [&](int p) {
-      if (more && p < HT::PIECES) {
+    // Every wave runs the math of every step (a wave without rows or without a tile
+    // computes on masked data and writes nothing), so that the gathers can sit between its
+    // MFMAs without any branch around them.
+    auto dma_v = [&](int g) {
+      if (g % 2 == 0 && g / 2 < HP) {
         sched_fence();
-        gather_piece(nxt, next, p);
+        gather_v(vn, r1, g / 2);
       }
     };
-    if (kShared) {
-      if (lx > 0) {
-        if constexpr (D == 128) {
-          st.pair(cur[0] + kofs, cur[1] + kofs, cur[2] + vofs, cur[3] + vofs, lx, ly, c, h2, dma);
-        } else {
-          f32x16 sacc[2];
-          sacc[0] = st.scores(cur[0] + kofs, lx, h2);
-          sacc[1] = st.scores(cur[1] + kofs, ly, h2);
-          st.template update<2>(sacc, cur[2] + vofs, cur[3] + vofs, c);
-        }
+    auto dma_k = [&](int g) {
+      if (g % 2 == 0 && g / 2 < HP) {
+        sched_fence();
+        gather_k(kc, r2, g / 2);
       }
+    };
+    typename RowState<D>::Mid md;
+    f32x16 sacc[2];
+    // S phase
+    if constexpr (D == 128) {
+      if (kShared) st.pairA(kc[0] + kofs, kc[1] + kofs, lx, c, h2, dma_v, md);
+      else st.singleA(kc[mine] + kofs, len, c, h2, dma_v, md);
     } else {
-      if (len > 0) {
-        if constexpr (D == 128) {
-          st.single(cur[mine] + kofs, cur[2 + mine] + vofs, len, c, h2, dma);
-        } else {
-          f32x16 sacc[1];
-          sacc[0] = st.scores(cur[mine] + kofs, len, h2);
-          st.template update<1>(sacc, cur[2 + mine] + vofs, cur[2 + mine] + vofs, c);
-        }
+#pragma unroll
+      for (int i = 0; i < HP; ++i) gather_v(vn, r1, i);
+      if (kShared) {
+        sacc[0] = st.scores(kc[0] + kofs, lx, h2);
+        sacc[1] = st.scores(kc[1] + kofs, ly, h2);
+      } else {
+        sacc[0] = st.scores(kc[mine] + kofs, len, h2);
       }
     }
+    wait_keep_next();
+    lds_barrier();
+    // PV phase
+    if constexpr (D == 128) {
+      if (kShared) st.pairB(vc[0] + vofs, vc[1] + vofs, ly, c, h2, dma_k, md);
+      else st.singleB(vc[mine] + vofs, dma_k, md);
+    } else {
+#pragma unroll
+      for (int i = 0; i < HP; ++i) gather_k(kc, r2, i);
+      if (kShared) st.template update<2>(sacc, vc[0] + vofs, vc[1] + vofs, c);
+      else st.template update<1>(sacc, vc[mine] + vofs, vc[mine] + vofs, c);
+    }
+    r1 = r2;
+    lx0 = lx1;
+    ly0 = ly1;
+    lx1 = lx2;
+    ly1 = ly2;
   };
   int s = 0;
   for (; s < nsh2; s += 2) {
-    step(buf0, buf1, s, true);
-    step(buf1, buf0, s + 1, true);
+    step(kb0, vb0, vb1, s, true);
+    step(kb1, vb1, vb0, s + 1, true);
   }
   for (; s < nsteps; s += 2) {
-    step(buf0, buf1, s, false);
-    step(buf1, buf0, s + 1, false);
+    step(kb0, vb0, vb1, s, false);
+    step(kb1, vb1, vb0, s + 1, false);
   }
+  vm_wait<0>();  // no gather may still be writing this workgroup's LDS when it exits
 
   const float l_tot = st.l_run + __shfl_xor(st.l_run, 32, 64);
   if (qrow < qlen) {
@@ -671,10 +770,10 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
 namespace {
 
 template <int D, bool PERSIST>
-hipError_t launch(const FwdArgs& a, size_t lds, hipStream_t s) {
+hipError_t launch(const FwdArgs& a, hipStream_t s) {
   const int G = a.H * a.pairs;
   const int grid = 8 * cdiv(G, 8);
-  hipLaunchKernelGGL((attn_fwd_kernel<D, PERSIST>), dim3(grid), dim3(256), lds, s, a);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, PERSIST>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -706,8 +805,7 @@ hipError_t launch_attn_fwd_persistent(const pbsa_dims& d, TokIn q, const pbsa_ca
   a.H = d.heads;
   a.pairs = cdiv(a.nq, 2);
   a.scale = d.scale;
-  const size_t lds = static_cast<size_t>(d.capacity + a.nq + 2 * d.topk) * sizeof(int2);
-  return d.head_dim == 128 ? launch<128, true>(a, lds, s) : launch<64, true>(a, lds, s);
+  return d.head_dim == 128 ? launch<128, true>(a, s) : launch<64, true>(a, s);
 }
 
 hipError_t launch_attn_fwd_2lvl(const pbsa_dims& d, int chunks, TokIn q, TokIn k, TokIn v,
@@ -730,8 +828,7 @@ hipError_t launch_attn_fwd_2lvl(const pbsa_dims& d, int chunks, TokIn q, TokIn k
   a.pairs = cdiv(a.nq, 2);
   a.scale = d.scale;
   a.slots = 0;
-  const size_t lds = static_cast<size_t>(2 * max_sel) * sizeof(int2);
-  return d.head_dim == 128 ? launch<128, false>(a, lds, s) : launch<64, false>(a, lds, s);
+  return d.head_dim == 128 ? launch<128, false>(a, s) : launch<64, false>(a, s);
 }
 
 }  // namespace pbsa

@@ -26,6 +26,10 @@ inline TokOut tok_out(const pbsa_tensor& t) {
   return TokOut{static_cast<uint16_t*>(t.data), t.token_stride, t.head_stride};
 }
 
+// Block-list entries the attention forward keeps per workgroup (persistent mode:
+// capacity + chunk blocks + 2 * topk; two-level mode: 2 * max_sel).
+constexpr int kAttnListCap = 3072;
+
 inline int nb_of(const pbsa_dims& d) { return (d.frame_tokens + d.block - 1) / d.block; }
 inline int64_t slots_of(const pbsa_dims& d) {
   return static_cast<int64_t>(d.capacity) + static_cast<int64_t>(d.window_frames) * nb_of(d);
