@@ -28,7 +28,11 @@
  *    and a status below is returned, with detail in pbsa_last_error().  A failed launch
  *    returns PBSA_ERR_HIP.  Calls are reentrant.
  *  - Supported: head_dim 64 or 128, block 64, 1 <= frame_tokens, token strides multiples
- *    of 8 elements and token pointers 16-byte aligned.
+ *    of 8 elements and token pointers 16-byte aligned.  Size limits (PBSA_ERR_UNSUPPORTED
+ *    beyond them): persistent mode: capacity + window blocks <= 4096, capacity - sinks
+ *    <= 1024, window blocks <= 1024, topk <= 1024 and, for pbsa_attn_fwd, capacity +
+ *    chunk blocks + 2*topk <= 3072; two-level mode: pbsa_attn_fwd_2lvl max_sel <= 1536;
+ *    a head's K/V token rows span at most 2 GiB.
  */
 #ifndef PBSA_H_
 #define PBSA_H_
@@ -46,7 +50,8 @@ typedef enum pbsa_status {
   PBSA_OK = 0,
   PBSA_ERR_NULL = 1,        /* a required pointer is NULL */
   PBSA_ERR_SHAPE = 2,       /* sizes inconsistent or out of range */
-  PBSA_ERR_UNSUPPORTED = 3, /* valid but not built: head_dim other than 64/128, block != 64 */
+  PBSA_ERR_UNSUPPORTED = 3, /* valid but not built: head_dim other than 64/128, block != 64,
+                               or beyond a size limit listed above */
   PBSA_ERR_ALIGN = 4,       /* token pointer or stride not aligned for 16-byte loads */
   PBSA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than pbsa_workspace_bytes */
   PBSA_ERR_STATE = 6,       /* cache bookkeeping out of range (chunk_index) */
@@ -195,7 +200,7 @@ pbsa_status pbsa_score_topk_2lvl(const pbsa_dims* dims, int32_t chunks, int32_t 
 
 /* Attention of the clip's queries over their selected blocks (sel/nsel from
  * pbsa_score_topk_2lvl): o (bf16, like q) and lse (fp32 [heads][clip tokens]).
- * q, k, v: chunks*chunk_frames*frame_tokens tokens per head. */
+ * q, k, v: chunks*chunk_frames*frame_tokens tokens per head.  max_sel <= 1536. */
 pbsa_status pbsa_attn_fwd_2lvl(const pbsa_dims* dims, int32_t chunks, pbsa_tensor q,
                                pbsa_tensor k, pbsa_tensor v, const int32_t* sel,
                                const int32_t* nsel, int32_t max_sel, pbsa_tensor o, float* lse,

@@ -69,6 +69,7 @@ def _dims(**kw):
     (dict(scale=0.0), 0, 2),
     (dict(scale=float("nan")), 1, 2),
     (dict(capacity=5000), 0, 3),
+    (dict(topk=1025), 0, 3),             # topk above the supported maximum
 ])
 def test_check_dims(kw, mode, status):
     L = ops.lib()
@@ -126,6 +127,15 @@ def test_calls_reject_bad_arguments_before_launching():
     ks = (ctypes.c_int32 * 8)(0, 8, 12, 16, 20, 24, 28, 32)
     assert L.pbsa_score_topk_2lvl(d, 8, 8, ks, *(ctypes.c_void_p(16),) * 3, 70,
                                   ctypes.c_void_p(16), ctypes.c_void_p(16), None) == 2
+    # attention lists beyond the per-workgroup cap: C + chunk blocks + 2*topk > 3072
+    big = _dims(capacity=1000, sinks=1, topk=1000, window_frames=40)
+    t = _tensor(16)
+    assert L.pbsa_attn_fwd(big, t, ctypes.byref(ops.CacheC(16, 16, 16, 16, 16, 0)), t, t,
+                           ctypes.c_void_p(16), t, ctypes.c_void_p(16), None) == 3
+    assert b"3072" in L.pbsa_last_error()
+    # two-level attention: max_sel above 1536
+    assert L.pbsa_attn_fwd_2lvl(d, 8, t, t, t, ctypes.c_void_p(16), ctypes.c_void_p(16), 1537,
+                                t, ctypes.c_void_p(16), None) == 3
     # backward without workspace
     t = _tensor(16)
     assert L.pbsa_attn_bwd(d, 8, t, t, t, t, ctypes.c_void_p(16), t, ctypes.c_void_p(16),
