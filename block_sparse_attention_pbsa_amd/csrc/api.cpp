@@ -67,9 +67,10 @@ pbsa_status check_dims(const pbsa_dims* d, int mode) {
       return fail(PBSA_ERR_UNSUPPORTED, "capacity - sinks must be <= 1024");
     if (static_cast<int64_t>(d->window_frames) * nb > 1024)
       return fail(PBSA_ERR_UNSUPPORTED, "window blocks must be <= 1024");
-    // LDS of the memory-update selection: block tables + candidate arrays
+    // LDS of the memory-update selection: block tables, candidate list and partial sums,
+    // free list (the limits above keep it under 80 KB)
     const int64_t ncand = static_cast<int64_t>(d->capacity - d->sinks) + int64_t{d->chunk_frames} * nb;
-    if (ncand * 16 + slots * 8 > 56 * 1024)
+    if ((2 * slots + 5 * ncand + d->capacity) * 4 > 150 * 1024)
       return fail(PBSA_ERR_UNSUPPORTED, "capacity/window too large for the memory update");
   } else if (mode != 1) {
     return fail(PBSA_ERR_SHAPE, "mode must be 0 (persistent) or 1 (two-level)");

@@ -38,154 +38,185 @@ __device__ __forceinline__ bool ahead(float sa, int ia, float sb, int ib) {
 __device__ __forceinline__ float order_key(float x) { return x != x ? -INFINITY : x; }
 }  // namespace
 
-// grid H, one wave per head.  Candidates are listed in a fixed order (persistent non-sink
-// slots ascending, then the leaving blocks in chunk-block order, which is ascending id),
-// their memory scores are column sums of the chunk's score matrix, and one bitonic sort of
-// (score, ~id) keys finds the (C - S)-th best key tau: a candidate is kept iff its key is
-// >= tau.  Freed persistent slots (ascending) are handed to the promoted leaving blocks in
-// ascending id order.  Dynamic LDS: block_id and len of the head ([slots] each), candidate
-// slot [ncand_max], free-slot list [C].
+// grid H, 1024 threads per head (256 when the candidate count needs more sort registers).  Candidates are listed in a fixed order (persistent
+// non-sink slots ascending, then the leaving blocks in chunk-block order, which is
+// ascending id); their memory scores are column sums of the chunk's score matrix, computed
+// by all 16 waves with coalesced row reads (row group g = t / 256 sums rows g, g+4, ... of
+// the full groups of four, group 0 also the remaining rows; the four partials are added as
+// (g0 + g1) + (g2 + g3)).  Wave 0 then sorts (score, ~id) keys once to find the (C - S)-th
+// best key tau: a candidate is kept iff its key is >= tau.  Freed persistent slots
+// (ascending) are handed to the promoted leaving blocks in ascending id order.  Dynamic
+// LDS: block_id and len of the head ([slots] each), candidate slot [ncand_max], free-slot
+// list [C], partial sums [4][ncand_max].
 template <int E>
-__global__ void __launch_bounds__(64) memory_select_kernel(MemArgs a) {
+constexpr int select_threads() { return E <= 8 ? 1024 : 256; }  // wave 0's sort keys fit
+
+template <int E>
+__global__ void __launch_bounds__(select_threads<E>()) memory_select_kernel(MemArgs a) {
+  constexpr int NT = select_threads<E>();
   extern __shared__ int mem_smem[];
-  const int h = blockIdx.x, l = threadIdx.x;
-  int* sbid = mem_smem;                  // [slots]
-  int* slen = sbid + a.slots;            // [slots]
-  int* cslot = slen + a.slots;           // [ncand_max]
-  int* freel = cslot + (a.C - a.S) + a.F * a.nb;  // [C]
+  __shared__ int s_cnt[2];  // nP, ncand
+  const int h = blockIdx.x, t = threadIdx.x, l = t & 63, w = t >> 6;
+  const int ncand_max = (a.C - a.S) + a.F * a.nb;
+  int* sbid = mem_smem;          // [slots]
+  int* slen = sbid + a.slots;    // [slots]
+  int* cslot = slen + a.slots;   // [ncand_max]
+  int* freel = cslot + ncand_max;  // [C]
+  float* part = reinterpret_cast<float*>(freel + a.C);  // [4][ncand_max]
   int32_t* bid = a.bid + static_cast<int64_t>(h) * a.slots;
   int32_t* blen = a.blen + static_cast<int64_t>(h) * a.slots;
   int32_t* dst = a.copy_dst + static_cast<int64_t>(h) * a.F * a.nb;
   const int64_t hF = a.chunk * a.F;  // frames appended so far
   const int fnb = a.F * a.nb;
 
-  for (int b = l; b < fnb; b += 64) dst[b] = -1;
+  for (int b = t; b < fnb; b += NT) dst[b] = -1;
   if (a.chunk == 0) {
     // empty cache: P_t becomes the sinks, written by the copy pass
-    for (int s = l; s < a.C; s += 64) {
+    for (int s = t; s < a.C; s += NT) {
       bid[s] = -1;
       blen[s] = 0;
     }
     return;
   }
-  for (int s = l; s < a.slots; s += 64) {
+  for (int s = t; s < a.slots; s += NT) {
     sbid[s] = bid[s];
     slen[s] = blen[s];
   }
   __syncthreads();
-  // candidate list (ballot compaction keeps the order)
-  int nP = 0;
-  for (int s0 = a.S; s0 < a.C; s0 += 64) {
-    const int s = s0 + l;
-    const bool on = s < a.C && sbid[s] >= a.S;
-    const unsigned long long m = __ballot(on);
-    if (on) cslot[nP + __popcll(m & ((1ull << l) - 1ull))] = s;
-    nP += __popcll(m);
-  }
-  int ncand = nP;
-  for (int b0 = 0; b0 < fnb; b0 += 64) {
-    const int b = b0 + l;
-    int s = -1;
-    if (b < fnb) {
-      const int64_t f_new = hF + b / a.nb;  // chunk frame landing in this window slot
-      if (f_new >= a.W) {                   // otherwise the slot was empty: nothing leaves
-        s = a.C + static_cast<int>(f_new % a.W) * a.nb + b % a.nb;
-        if (sbid[s] < a.S) s = -1;
-      }
+  if (w == 0) {
+    // candidate list (ballot compaction keeps the order)
+    int nP = 0;
+    for (int s0 = a.S; s0 < a.C; s0 += 64) {
+      const int s = s0 + l;
+      const bool on = s < a.C && sbid[s] >= a.S;
+      const unsigned long long m = __ballot(on);
+      if (on) cslot[nP + __popcll(m & ((1ull << l) - 1ull))] = s;
+      nP += __popcll(m);
     }
-    const unsigned long long m = __ballot(s >= 0);
-    if (s >= 0) cslot[ncand + __popcll(m & ((1ull << l) - 1ull))] = s;
-    ncand += __popcll(m);
-  }
-  __syncthreads();
-  // memory scores and keys; keep a copy of the keys in candidate order
-  const float* sc = a.scores + static_cast<int64_t>(h) * a.nq * a.slots;
-  uint64_t key[E], mine[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int c = l + 64 * e;
-    key[e] = 0;
-    if (c < ncand) {
-      const int s = cslot[c];
-      float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
-      int r = 0;
-      for (; r + 4 <= a.nq; r += 4) {
-        acc0 += sc[static_cast<int64_t>(r) * a.slots + s];
-        acc1 += sc[static_cast<int64_t>(r + 1) * a.slots + s];
-        acc2 += sc[static_cast<int64_t>(r + 2) * a.slots + s];
-        acc3 += sc[static_cast<int64_t>(r + 3) * a.slots + s];
-      }
-      for (; r < a.nq; ++r) acc0 += sc[static_cast<int64_t>(r) * a.slots + s];
-      key[e] = rank_key((acc0 + acc1) + (acc2 + acc3), sbid[s]);
-    }
-    mine[e] = key[e];
-  }
-  const int keep_n = a.C - a.S < ncand ? a.C - a.S : ncand;
-  uint64_t tau = 0;
-  if (keep_n > 0) {
-    wave_sort_desc<E>(key, l);
-    const int e_t = (keep_n - 1) >> 6, l_t = (keep_n - 1) & 63;
-    uint64_t mykey = 0;
-#pragma unroll
-    for (int e = 0; e < E; ++e)
-      if (e == e_t) mykey = key[e];
-    tau = (static_cast<uint64_t>(__shfl(static_cast<uint32_t>(mykey >> 32), l_t, 64)) << 32) |
-          __shfl(static_cast<uint32_t>(mykey), l_t, 64);
-  }
-  // kept flags per candidate (in candidate order), written over cslot's sign bit
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int c = l + 64 * e;
-    if (c < ncand && keep_n > 0 && mine[e] >= tau) cslot[c] = ~cslot[c];  // kept: negative
-  }
-  __syncthreads();
-  // free list: persistent non-sink slots whose block is not kept (or that are empty)
-  int nfree = 0;
-  for (int s0 = a.S; s0 < a.C; s0 += 64) {
-    const int s = s0 + l;
-    bool fr = false;
-    if (s < a.C) {
-      fr = sbid[s] < a.S;  // empty
-      if (!fr) {
-        // the candidate for slot s: binary search over the ascending P part of cslot
-        int lo = 0, hi = nP;
-        while (lo < hi) {
-          const int mid = (lo + hi) >> 1;
-          const int cs = cslot[mid] < 0 ? ~cslot[mid] : cslot[mid];
-          if (cs < s) lo = mid + 1;
-          else hi = mid;
+    int ncand = nP;
+    for (int b0 = 0; b0 < fnb; b0 += 64) {
+      const int b = b0 + l;
+      int s = -1;
+      if (b < fnb) {
+        const int64_t f_new = hF + b / a.nb;  // chunk frame landing in this window slot
+        if (f_new >= a.W) {                   // otherwise the slot was empty: nothing leaves
+          s = a.C + static_cast<int>(f_new % a.W) * a.nb + b % a.nb;
+          if (sbid[s] < a.S) s = -1;
         }
-        fr = cslot[lo] >= 0;  // not kept
       }
+      const unsigned long long m = __ballot(s >= 0);
+      if (s >= 0) cslot[ncand + __popcll(m & ((1ull << l) - 1ull))] = s;
+      ncand += __popcll(m);
     }
-    const unsigned long long m = __ballot(fr);
-    if (fr) freel[nfree + __popcll(m & ((1ull << l) - 1ull))] = s;
-    nfree += __popcll(m);
+    if (l == 0) {
+      s_cnt[0] = nP;
+      s_cnt[1] = ncand;
+    }
   }
   __syncthreads();
-  // promoted leaving blocks (kept candidates past nP), in candidate order = ascending id
-  int npro = 0;
-  for (int c0 = nP; c0 < ncand; c0 += 64) {
-    const int c = c0 + l;
-    const bool pro = c < ncand && cslot[c] < 0;
-    const unsigned long long m = __ballot(pro);
-    if (pro) {
-      const int k = npro + __popcll(m & ((1ull << l) - 1ull));
-      const int src = ~cslot[c];
-      const int s = freel[k];
-      const int b_rel = src - a.C;
-      const int rf = b_rel / a.nb, j = b_rel % a.nb;
-      const int fb = static_cast<int>(((rf - hF % a.W) % a.W + a.W) % a.W);
-      dst[fb * a.nb + j] = s;
-      bid[s] = sbid[src];
-      blen[s] = slen[src];
+  const int nP = s_cnt[0], ncand = s_cnt[1];
+  // partial column sums
+  {
+    const float* sc = a.scores + static_cast<int64_t>(h) * a.nq * a.slots;
+    const int full = a.nq & ~3;
+    for (int c = t & 255; c < ncand; c += 256) {
+      const int s = cslot[c];
+      for (int g = t >> 8; g < 4; g += NT / 256) {
+        float acc = 0.f;
+        for (int r = g; r < full; r += 4) acc += sc[static_cast<int64_t>(r) * a.slots + s];
+        if (g == 0)
+          for (int r = full; r < a.nq; ++r) acc += sc[static_cast<int64_t>(r) * a.slots + s];
+        part[g * ncand_max + c] = acc;
+      }
     }
-    npro += __popcll(m);
   }
-  // freed slots left over become empty
-  for (int k = npro + l; k < nfree; k += 64) {
-    bid[freel[k]] = -1;
-    blen[freel[k]] = 0;
+  __syncthreads();
+  if (w == 0) {
+    // memory scores and keys; keep a copy of the keys in candidate order
+    uint64_t key[E], mine[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int c = l + 64 * e;
+      key[e] = 0;
+      if (c < ncand) {
+        const float msum = (part[c] + part[ncand_max + c]) +
+                           (part[2 * ncand_max + c] + part[3 * ncand_max + c]);
+        key[e] = rank_key(msum, sbid[cslot[c]]);
+      }
+      mine[e] = key[e];
+    }
+    const int keep_n = a.C - a.S < ncand ? a.C - a.S : ncand;
+    uint64_t tau = 0;
+    if (keep_n > 0) {
+      wave_sort_desc<E>(key, l);
+      const int e_t = (keep_n - 1) >> 6, l_t = (keep_n - 1) & 63;
+      uint64_t mykey = 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (e == e_t) mykey = key[e];
+      tau = (static_cast<uint64_t>(__shfl(static_cast<uint32_t>(mykey >> 32), l_t, 64)) << 32) |
+            __shfl(static_cast<uint32_t>(mykey), l_t, 64);
+    }
+    // kept flags per candidate (in candidate order), written over cslot's sign bit
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int c = l + 64 * e;
+      if (c < ncand && keep_n > 0 && mine[e] >= tau) cslot[c] = ~cslot[c];  // kept: negative
+    }
+  }
+  __syncthreads();
+  if (w == 0) {
+    // free list: persistent non-sink slots whose block is not kept (or that are empty)
+    int nfree = 0;
+    for (int s0 = a.S; s0 < a.C; s0 += 64) {
+      const int s = s0 + l;
+      bool fr = false;
+      if (s < a.C) {
+        fr = sbid[s] < a.S;  // empty
+        if (!fr) {
+          // the candidate for slot s: binary search over the ascending P part of cslot
+          int lo = 0, hi = nP;
+          while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            const int cs = cslot[mid] < 0 ? ~cslot[mid] : cslot[mid];
+            if (cs < s) lo = mid + 1;
+            else hi = mid;
+          }
+          fr = cslot[lo] >= 0;  // not kept
+        }
+      }
+      const unsigned long long m = __ballot(fr);
+      if (fr) freel[nfree + __popcll(m & ((1ull << l) - 1ull))] = s;
+      nfree += __popcll(m);
+    }
+    // (the free list is read back by other lanes of this wave only)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // promoted leaving blocks (kept candidates past nP), in candidate order = ascending id
+    int npro = 0;
+    for (int c0 = nP; c0 < ncand; c0 += 64) {
+      const int c = c0 + l;
+      const bool pro = c < ncand && cslot[c] < 0;
+      const unsigned long long m = __ballot(pro);
+      if (pro) {
+        const int k = npro + __popcll(m & ((1ull << l) - 1ull));
+        const int src = ~cslot[c];
+        const int s = freel[k];
+        const int b_rel = src - a.C;
+        const int rf = b_rel / a.nb, j = b_rel % a.nb;
+        const int fb = static_cast<int>(((rf - hF % a.W) % a.W + a.W) % a.W);
+        dst[fb * a.nb + j] = s;
+        bid[s] = sbid[src];
+        blen[s] = slen[src];
+      }
+      npro += __popcll(m);
+    }
+    // freed slots left over become empty
+    for (int k = npro + l; k < nfree; k += 64) {
+      bid[freel[k]] = -1;
+      blen[freel[k]] = 0;
+    }
   }
 }
 
@@ -276,14 +307,14 @@ hipError_t launch_memory_update(const pbsa_dims& d, const float* scores, const p
   a.nq = d.chunk_frames * nb;
   a.chunk = c.chunk_index;
   const int ncand_max = (d.capacity - d.sinks) + d.chunk_frames * nb;
-  const size_t lds = static_cast<size_t>(2 * a.slots + ncand_max + d.capacity) * sizeof(int);
+  const size_t lds = static_cast<size_t>(2 * a.slots + 5 * ncand_max + d.capacity) * sizeof(int);
   const int E = (ncand_max + 63) / 64;
-  if (E <= 1) hipLaunchKernelGGL(memory_select_kernel<1>, dim3(d.heads), dim3(64), lds, s, a);
-  else if (E <= 2) hipLaunchKernelGGL(memory_select_kernel<2>, dim3(d.heads), dim3(64), lds, s, a);
-  else if (E <= 4) hipLaunchKernelGGL(memory_select_kernel<4>, dim3(d.heads), dim3(64), lds, s, a);
-  else if (E <= 8) hipLaunchKernelGGL(memory_select_kernel<8>, dim3(d.heads), dim3(64), lds, s, a);
-  else if (E <= 16) hipLaunchKernelGGL(memory_select_kernel<16>, dim3(d.heads), dim3(64), lds, s, a);
-  else hipLaunchKernelGGL(memory_select_kernel<32>, dim3(d.heads), dim3(64), lds, s, a);
+  if (E <= 1) hipLaunchKernelGGL(memory_select_kernel<1>, dim3(d.heads), dim3(select_threads<1>()), lds, s, a);
+  else if (E <= 2) hipLaunchKernelGGL(memory_select_kernel<2>, dim3(d.heads), dim3(select_threads<2>()), lds, s, a);
+  else if (E <= 4) hipLaunchKernelGGL(memory_select_kernel<4>, dim3(d.heads), dim3(select_threads<4>()), lds, s, a);
+  else if (E <= 8) hipLaunchKernelGGL(memory_select_kernel<8>, dim3(d.heads), dim3(select_threads<8>()), lds, s, a);
+  else if (E <= 16) hipLaunchKernelGGL(memory_select_kernel<16>, dim3(d.heads), dim3(select_threads<16>()), lds, s, a);
+  else hipLaunchKernelGGL(memory_select_kernel<32>, dim3(d.heads), dim3(select_threads<32>()), lds, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 grid(d.chunk_frames * nb, d.heads);
