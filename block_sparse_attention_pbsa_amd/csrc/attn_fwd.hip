@@ -119,6 +119,27 @@ struct RowState {
   u32x4 qreg[NS];
   f32x16 acc[ND];
   float m_run, l_run;
+  float m_off;  // m_run * c (0 while no key has been seen): the exp2 offset
+  float m_thr;  // m_run + 8 / c: a row max above it raises the running max
+
+  // Lazy raise of the running max: only when some row's new max exceeds it by more than
+  // 2^8 in exp2 units (so exp2 arguments stay <= 8).  Returns the factor for the earlier
+  // accumulators through alpha; l_run is scaled here, acc by the caller.  Rare: kept as a
+  // branch so that the common path is one compare.
+  __device__ __forceinline__ bool raise(float mx, float c, float& alpha) {
+    const bool up = __any(mx > m_thr);
+    alpha = 1.f;
+    if (up) {
+      const float m_new = fmaxf(m_run, mx);
+      alpha = m_run > -INFINITY ? __builtin_amdgcn_exp2f(m_run * c - m_new * c) : 0.f;
+      m_run = m_new;
+      l_run *= alpha;
+      // no valid key yet (a fully masked tile before any other): any finite offset works
+      m_off = m_new > -INFINITY ? m_new * c : 0.f;
+      m_thr = m_new + 8.f / c;
+    }
+    return up;
+  }
 
   // S^T for the keys of one K half tile: keys acc_row(r, h2), query = this lane's row.
   // kb: this lane's K read address (bytes, LDS).
@@ -249,7 +270,7 @@ struct RowState {
   // the factor alpha folded into l_run; 2..5: four exponentials each; 6: bf16 packing
   // and the row sum.
   struct Soft {
-    float mx, m_off, alpha, psum;
+    float mx, alpha;
     float p[16];
     u32x4 pb[2];
     bool up;
@@ -263,27 +284,21 @@ struct RowState {
     } else if (k == 1) {
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(so.mx),
                                                        __float_as_uint(so.mx), false, false);
-      const float mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-      so.up = __any(mx * c > m_run * c + 8.f);
-      const float m_new = so.up ? fmaxf(m_run, mx) : m_run;
-      so.alpha = so.up ? __builtin_amdgcn_exp2f(m_run * c - m_new * c) : 1.f;
-      m_run = m_new;
-      // no valid key yet (a fully masked tile before any other): any finite offset works
-      so.m_off = m_new > -INFINITY ? m_new * c : 0.f;
+      so.up = raise(fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])), c, so.alpha);
     } else if (k <= 5) {
       const int r0 = 4 * (k - 2);
 #pragma unroll
-      for (int r = r0; r < r0 + 4; ++r) so.p[r] = __builtin_amdgcn_exp2f(fmaf(sa[r], c, -so.m_off));
+      for (int r = r0; r < r0 + 4; ++r) so.p[r] = __builtin_amdgcn_exp2f(fmaf(sa[r], c, -m_off));
     } else {
       float ps = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) ps += so.p[r];
-      l_run = l_run * so.alpha + ps;
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           so.pb[t2][e] = pack_bf16x2(so.p[8 * t2 + 2 * e], so.p[8 * t2 + 2 * e + 1]);
+      l_run += ps;
     }
   }
 
@@ -399,15 +414,11 @@ struct RowState {
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    if (__any(mx * c > m_run * c + 8.f)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run * c - m_new * c);
-      m_run = m_new;
-      l_run *= alpha;
+    float alpha;
+    if (raise(mx, c, alpha)) {
 #pragma unroll
       for (int dt = 0; dt < ND; ++dt) acc[dt] *= alpha;
     }
-    const float m_off = m_run > -INFINITY ? m_run * c : 0.f;
     float psum = 0.f;
 #pragma unroll
     for (int kt = 0; kt < NT; ++kt)
@@ -546,6 +557,8 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
   for (int i = 0; i < RowState<D>::ND; ++i) st.acc[i] = f32x16{};
   st.m_run = -INFINITY;
   st.l_run = 0.f;
+  st.m_off = 0.f;
+  st.m_thr = -INFINITY;
 
   const char* ck_h = reinterpret_cast<const char*>(a.ck) +
                      static_cast<int64_t>(h) * a.slots * kCacheBlockBytes;
@@ -624,18 +637,26 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
   const uint32_t v_rowl = l >> 2, v_colb = 16u * (l & 3);
   //   K piece p: rows 16 (p / HP) .., chunks 4 (p % HP) ..
   //   V piece p: rows 16 (p % 2) .., 32-channel segment p / 2
-  auto gather_k = [&](char (*buf)[HT::BYTES], const HalfRef& hr, int i) {
-    const int p = p0 + i;
-    const uint32_t last = static_cast<uint32_t>(hr.len > 0 ? hr.len - 1 : 0);
-    const uint32_t row = (p / HP ? 16u : 0u) + k_rowl;
-    lds_dma16(hr.k + 64 * (p % HP) + min(row, last) * hr.stride + k_colb,
-              buf[tw] + 1024 * p);
+  // so this wave's K pieces all use rows 16 (w & 1) + (l & 15) (one lane offset per step)
+  // and its V pieces rows (l >> 2) or 16 + (l >> 2) (two lane offsets per step); the
+  // piece's chunk or segment is a scalar offset.
+  struct Offs {
+    uint32_t k, v0, v1;
   };
-  auto gather_v = [&](char (*buf)[HT::BYTES], const HalfRef& hr, int i) {
-    const int p = p0 + i;
+  auto offsets = [&](const HalfRef& hr) {
     const uint32_t last = static_cast<uint32_t>(hr.len > 0 ? hr.len - 1 : 0);
-    const uint32_t row = (p % 2 ? 16u : 0u) + v_rowl;
-    lds_dma16(hr.v + 64 * (p / 2) + min(row, last) * hr.stride + v_colb, buf[tw] + 1024 * p);
+    Offs o;
+    o.k = min(16u * (w & 1) + k_rowl, last) * hr.stride + k_colb;
+    o.v0 = min(v_rowl, last) * hr.stride + v_colb;
+    o.v1 = min(16u + v_rowl, last) * hr.stride + v_colb;
+    return o;
+  };
+  auto gather_k = [&](char (*buf)[HT::BYTES], const HalfRef& hr, const Offs& o, int i) {
+    lds_dma16(hr.k + 64 * i + o.k, buf[tw] + 1024 * (p0 + i));
+  };
+  auto gather_v = [&](char (*buf)[HT::BYTES], const HalfRef& hr, const Offs& o, int i) {
+    const int p = p0 + i;
+    lds_dma16(hr.v + 64 * (p / 2) + (p % 2 ? o.v1 : o.v0), buf[tw] + 1024 * p);
   };
   // Waits before the barriers that publish gathered tiles.  Each wave's gathers in issue
   // order: K(s), V(s), K(s+1), V(s+1), ... (HP instructions each).  Before the top barrier
@@ -670,12 +691,15 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
   fetch(2, ex, ey);
   vm_wait<0>();  // Q (and the list inputs) have landed: the loop's waits count gathers only
   __syncthreads();
+  {
+    const Offs o0 = offsets(r0), o1 = offsets(r1);
 #pragma unroll
-  for (int i = 0; i < HP; ++i) gather_k(kb0, r0, i);
+    for (int i = 0; i < HP; ++i) gather_k(kb0, r0, o0, i);
 #pragma unroll
-  for (int i = 0; i < HP; ++i) gather_v(vb0, r0, i);
+    for (int i = 0; i < HP; ++i) gather_v(vb0, r0, o0, i);
 #pragma unroll
-  for (int i = 0; i < HP; ++i) gather_k(kb1, r1, i);
+    for (int i = 0; i < HP; ++i) gather_k(kb1, r1, o1, i);
+  }
   // Step s (kc/vc: its K and V buffers, vn: V buffer of step s+1):
   //   top barrier (K(s) published) -> V(s+1) gathers under the S phase -> mid barrier
   //   (V(s) published; every wave is done with K(s)) -> K(s+2) gathers into kc under the
@@ -693,16 +717,17 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
     // Every wave runs the math of every step (a wave without rows or without a tile
     // computes on masked data and writes nothing), so that the gathers can sit between its
     // MFMAs without any branch around them.
+    const Offs o1 = offsets(r1), o2 = offsets(r2);
     auto dma_v = [&](int g) {
       if (g % 2 == 0 && g / 2 < HP) {
         sched_fence();
-        gather_v(vn, r1, g / 2);
+        gather_v(vn, r1, o1, g / 2);
       }
     };
     auto dma_k = [&](int g) {
       if (g % 2 == 0 && g / 2 < HP) {
         sched_fence();
-        gather_k(kc, r2, g / 2);
+        gather_k(kc, r2, o2, g / 2);
       }
     };
     typename RowState<D>::Mid md;
@@ -713,7 +738,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
       else st.singleA(kc[mine] + kofs, len, c, h2, dma_v, md);
     } else {
 #pragma unroll
-      for (int i = 0; i < HP; ++i) gather_v(vn, r1, i);
+      for (int i = 0; i < HP; ++i) gather_v(vn, r1, o1, i);
       if (kShared) {
         sacc[0] = st.scores(kc[0] + kofs, lx, h2);
         sacc[1] = st.scores(kc[1] + kofs, ly, h2);
@@ -729,7 +754,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
       else st.singleB(vc[mine] + vofs, dma_k, md);
     } else {
 #pragma unroll
-      for (int i = 0; i < HP; ++i) gather_k(kc, r2, i);
+      for (int i = 0; i < HP; ++i) gather_k(kc, r2, o2, i);
       if (kShared) st.template update<2>(sacc, vc[0] + vofs, vc[1] + vofs, c);
       else st.template update<1>(sacc, vc[mine] + vofs, vc[mine] + vofs, c);
     }
