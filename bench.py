@@ -45,6 +45,8 @@ def parse():
                     help="also time the trainable two-level fwd+bwd clip (extra field)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "attn_fwd_wan_5s_traffic.json"),
                     help="HBM traffic per attention launch from rocprofv3 counters (if present)")
+    ap.add_argument("--no-probes", action="store_true",
+                    help="skip the measured ceilings (MFMA, copy, gather, full-history pool)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, copy a 512 MiB buffer 3 times (calibrates the "
                          "FETCH_SIZE / WRITE_SIZE counters against known bytes)")
@@ -190,6 +192,9 @@ def main():
                      "traffic": traffic, "kernel": "attn_fwd_persistent_kernel<128>"},
     }
 
+    if not args.no_probes:
+        result["probes"] = bench_probes(torch, ops, synth, shape, layer, q, k, v, stream)
+
     if args.train:
         result["train"] = bench_train(torch, ops, runtime, synth, dev, stream)
 
@@ -204,6 +209,105 @@ def main():
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(wl, seed)
     print(json.dumps(result), flush=True)
+
+
+def _timed_reps(torch, stream, fn, reps, flush=None):
+    """Median and p10/p90 of `reps` runs of fn (ms), HIP events on `stream`; flush() runs
+    before each rep outside the timed region (cold runs)."""
+    ts = []
+    for _ in range(reps):
+        if flush is not None:
+            flush()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    return float(np.median(ts)), float(np.percentile(ts, 10)), float(np.percentile(ts, 90))
+
+
+def bench_probes(torch, ops, synth, shape, layer, q, k, v, stream):
+    """Measured ceilings next to the published peaks (extra field):
+      mfma   - independent v_mfma_f32_32x32x16_bf16 chains on every SIMD (pbsa_probe_mfma);
+      copy   - a 512 MiB device copy (read + write bytes / time);
+      gather - the attention's gathers without its math (pbsa_probe_gather) on the measured
+               chunk: bytes moved into LDS per launch (one 1 KB instruction per piece; a
+               step moves 32 KB per workgroup) / time, warm and cold;
+      pool_full_history - pbsa_pool over the 1-minute workload's whole history
+               (240 frames x 1560 tokens x 12 heads x 128, 1.15 GB read), warm and cold.
+    Cold runs first write a 512 MiB buffer (larger than the 256 MB last-level cache)."""
+    out = {}
+    flush_buf = torch.empty(256 * 1024 * 1024, dtype=torch.bfloat16, device="cuda")
+
+    def flush():
+        flush_buf.fill_(1.0)
+
+    # MFMA ceiling
+    mf = torch.empty(131072, dtype=torch.float32, device="cuda")
+    iters = 20000
+    flop = ops.pbsa_probe_mfma(iters, mf)
+    torch.cuda.synchronize()
+    med, _, _ = _timed_reps(torch, stream, lambda: ops.pbsa_probe_mfma(iters, mf), 5)
+    out["mfma"] = {"tflops": round(flop / (med * 1e-3) / 1e12, 1), "ms": round(med, 3),
+                   "frac_of_peak": round(flop / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    # copy ceiling
+    src = torch.ones(256 * 1024 * 1024, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    med, _, _ = _timed_reps(torch, stream, lambda: dst.copy_(src), 5)
+    cb = 2 * src.numel() * 2
+    out["copy"] = {"gbs": round(cb / (med * 1e-3) / 1e9, 1), "ms": round(med, 3),
+                   "frac_of_peak": round(cb / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    del src, dst
+    # gather of the measured chunk (routing already current)
+    layer.route(q)
+    bid = layer.cache.block_id.cpu().numpy()
+    sel = layer.sel.cpu().numpy()
+    C, nq = shape.capacity, shape.nq
+    steps = 0
+    for h in range(shape.heads):
+        nshared = int((bid[h, :C] >= 0).sum()) + nq
+        nsh2 = nshared + (nshared & 1)
+        for pr in range((nq + 1) // 2):
+            cnt = [int((sel[h, r] >= 0).sum()) if r < nq else 0 for r in (2 * pr, 2 * pr + 1)]
+            steps += nsh2 + 2 * max(cnt) + 2  # + the two steps gathered ahead past the end
+    gbytes = steps * 32 * 1024
+    g = lambda: ops.pbsa_probe_gather(shape, q, layer.cache, k, v, layer.sel)
+    g()
+    torch.cuda.synchronize()
+    warm, _, _ = _timed_reps(torch, stream, g, 10)
+    cold, c10, c90 = _timed_reps(torch, stream, g, 10, flush)
+    out["gather"] = {"bytes_moved_to_lds": gbytes, "ms_warm": round(warm, 4),
+                     "ms_cold": round(cold, 4), "ms_cold_p10_p90": [round(c10, 4), round(c90, 4)],
+                     "gbs_warm": round(gbytes / (warm * 1e-3) / 1e9, 1),
+                     "gbs_cold": round(gbytes / (cold * 1e-3) / 1e9, 1)}
+    # full-history pooling at the 1-minute workload's size (seeded synthetic tokens)
+    wl = synth.WORKLOADS["wan_1min"]
+    frames = wl.history_frames
+    T = frames * wl.frame_tokens
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(synth.SEEDS["wan_1min"])
+    x = torch.randn((T, wl.heads, wl.head_dim), generator=gen, device="cuda",
+                    dtype=torch.float32).to(torch.bfloat16)
+    pshape = ops.Shape(wl.heads, wl.head_dim, wl.frame_tokens, frames, scale=wl.scale)
+    brep = torch.empty((wl.heads, frames * wl.nb, wl.head_dim), dtype=torch.float32, device="cuda")
+    frep = torch.empty((wl.heads, frames, wl.head_dim), dtype=torch.float32, device="cuda")
+    p = lambda: ops.pbsa_pool(pshape, x, frames, brep, frep)
+    p()
+    torch.cuda.synchronize()
+    warm, _, _ = _timed_reps(torch, stream, p, 10)
+    cold, c10, c90 = _timed_reps(torch, stream, p, 10, flush)
+    pb = x.numel() * 2 + brep.numel() * 4 + frep.numel() * 4
+    out["pool_full_history"] = {
+        "workload": "wan_1min history: 240 frames x 1560 tokens, 12 heads, d=128",
+        "bytes": pb, "ms_warm": round(warm, 4), "ms_cold": round(cold, 4),
+        "ms_cold_p10_p90": [round(c10, 4), round(c90, 4)],
+        "gbs_warm": round(pb / (warm * 1e-3) / 1e9, 1), "gbs_cold": round(pb / (cold * 1e-3) / 1e9, 1),
+        "frac_hbm_cold": round(pb / (cold * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    del x, brep, frep, flush_buf
+    torch.cuda.empty_cache()
+    return out
 
 
 def bench_train(torch, ops, runtime, synth, dev, stream):

@@ -9,6 +9,7 @@
 #include <string>
 
 #include "../../include/pbsa.h"
+#include "../../include/pbsa_probe.h"
 #include "launch.h"
 
 namespace {
@@ -318,6 +319,43 @@ pbsa_status pbsa_attn_bwd(const pbsa_dims* dims, int32_t chunks, pbsa_tensor q, 
                                           pbsa::tok_out(dq), pbsa::tok_out(dk),
                                           pbsa::tok_out(dv), workspace, stream_of(stream)),
                     "attn_bwd");
+}
+
+// ---- measurement probes (pbsa_probe.h)
+
+int64_t pbsa_probe_mfma_flop(int64_t iters) {
+  return iters < 1 ? 0 : iters * 512 * 4 * 4 * (2 * 32 * 32 * 16);
+}
+
+pbsa_status pbsa_probe_mfma(int64_t iters, float* out, void* stream) {
+  if (!out) return fail(PBSA_ERR_NULL, "out is NULL");
+  if (iters < 1) return fail(PBSA_ERR_SHAPE, "iters must be >= 1");
+  return hip_status(pbsa::launch_probe_mfma(iters, out, stream_of(stream)), "probe_mfma");
+}
+
+pbsa_status pbsa_probe_gather(const pbsa_dims* dims, pbsa_tensor q, const pbsa_cache* cache,
+                              pbsa_tensor chunk_k, pbsa_tensor chunk_v, const int32_t* sel,
+                              void* stream) {
+  PBSA_TRY(check_dims(dims, 0));
+  PBSA_TRY(check_cache(cache));
+  PBSA_TRY(check_tok(q, "q", dims->head_dim));
+  PBSA_TRY(check_tok(chunk_k, "chunk_k", dims->head_dim));
+  PBSA_TRY(check_tok(chunk_v, "chunk_v", dims->head_dim));
+  if (!sel) return fail(PBSA_ERR_NULL, "sel is required");
+  const int64_t ctok = int64_t{dims->chunk_frames} * dims->frame_tokens;
+  const int64_t list = int64_t{dims->capacity} + int64_t{dims->chunk_frames} * pbsa::nb_of(*dims) +
+                       2 * int64_t{dims->topk};
+  if (list > pbsa::kAttnListCap)
+    return fail(PBSA_ERR_UNSUPPORTED, "capacity + chunk blocks + 2*topk = %lld exceeds %d",
+                static_cast<long long>(list), pbsa::kAttnListCap);
+  PBSA_TRY(check_span(chunk_k, "chunk_k", ctok, dims->head_dim));
+  PBSA_TRY(check_span(chunk_v, "chunk_v", ctok, dims->head_dim));
+  return hip_status(pbsa::launch_attn_fwd_persistent(*dims, pbsa::tok_in(q), *cache,
+                                                     pbsa::tok_in(chunk_k),
+                                                     pbsa::tok_in(chunk_v), sel,
+                                                     pbsa::TokOut{nullptr, 0, 0}, nullptr,
+                                                     stream_of(stream), true),
+                    "probe_gather");
 }
 
 }  // extern "C"

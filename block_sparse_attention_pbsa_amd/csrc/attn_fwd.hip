@@ -436,8 +436,10 @@ struct RowState {
 
 }  // namespace
 
-// 1-D grid of 8 * ceil(H * pairs / 8) workgroups of 256 threads.
-template <int D, bool PERSIST>
+// 1-D grid of 8 * ceil(H * pairs / 8) workgroups of 256 threads.  GATHER_ONLY builds the
+// gather probe: the same lists, gathers, waits and barriers with the math left out (no
+// output is written).
+template <int D, bool PERSIST, bool GATHER_ONLY = false>
 __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
   using HT = HalfTile<D>;
   // K and V half tiles (X and Y) of even and odd steps, gathered straight into LDS; four
@@ -732,6 +734,19 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
     };
     typename RowState<D>::Mid md;
     f32x16 sacc[2];
+    if constexpr (GATHER_ONLY) {
+#pragma unroll
+      for (int i = 0; i < HP; ++i) gather_v(vn, r1, o1, i);
+      wait_keep_next();
+      lds_barrier();
+#pragma unroll
+      for (int i = 0; i < HP; ++i) gather_k(kc, r2, o2, i);
+      (void)md;
+      (void)sacc;
+      (void)len;
+      (void)dma_v;
+      (void)dma_k;
+    } else {
     // S phase
     if constexpr (D == 128) {
       if (kShared) st.pairA(kc[0] + kofs, kc[1] + kofs, lx, c, h2, dma_v, md);
@@ -758,6 +773,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
       if (kShared) st.template update<2>(sacc, vc[0] + vofs, vc[1] + vofs, c);
       else st.template update<1>(sacc, vc[mine] + vofs, vc[mine] + vofs, c);
     }
+    }
     r1 = r2;
     lx0 = lx1;
     ly0 = ly1;
@@ -775,6 +791,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
   }
   vm_wait<0>();  // no gather may still be writing this workgroup's LDS when it exits
 
+  if constexpr (GATHER_ONLY) return;
   const float l_tot = st.l_run + __shfl_xor(st.l_run, 32, 64);
   if (qrow < qlen) {
     const float inv = 1.f / l_tot;
@@ -794,11 +811,11 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
 
 namespace {
 
-template <int D, bool PERSIST>
+template <int D, bool PERSIST, bool GATHER_ONLY = false>
 hipError_t launch(const FwdArgs& a, hipStream_t s) {
   const int G = a.H * a.pairs;
   const int grid = 8 * cdiv(G, 8);
-  hipLaunchKernelGGL((attn_fwd_kernel<D, PERSIST>), dim3(grid), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, PERSIST, GATHER_ONLY>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -806,7 +823,7 @@ hipError_t launch(const FwdArgs& a, hipStream_t s) {
 
 hipError_t launch_attn_fwd_persistent(const pbsa_dims& d, TokIn q, const pbsa_cache& c,
                                       TokIn ck, TokIn cv, const int32_t* sel, TokOut o,
-                                      float* lse, hipStream_t s) {
+                                      float* lse, hipStream_t s, bool gather_only) {
   FwdArgs a{};
   const int nb = nb_of(d);
   a.q = q.p; a.qts = q.ts; a.qhs = q.hs;
@@ -830,6 +847,8 @@ hipError_t launch_attn_fwd_persistent(const pbsa_dims& d, TokIn q, const pbsa_ca
   a.H = d.heads;
   a.pairs = cdiv(a.nq, 2);
   a.scale = d.scale;
+  if (gather_only)
+    return d.head_dim == 128 ? launch<128, true, true>(a, s) : launch<64, true, true>(a, s);
   return d.head_dim == 128 ? launch<128, true>(a, s) : launch<64, true>(a, s);
 }
 

@@ -1,0 +1,40 @@
+// Measurement probe: the MFMA rate of v_mfma_f32_32x32x16_bf16 with independent
+// accumulators on every SIMD (the instruction the attention kernels use).
+#include "common.h"
+#include "launch.h"
+
+namespace pbsa {
+
+namespace {
+constexpr int kProbeBlocks = 512, kProbeThreads = 256;
+}
+
+__global__ void __launch_bounds__(256) mfma_probe_kernel(int64_t iters, float* out) {
+  const int t = blockIdx.x * kProbeThreads + threadIdx.x;
+  // operands vary per lane (data-dependent power, as with real tiles)
+  u32x4 a, b;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[i] = 0x3c003c00u ^ ((t * 2654435761u + i * 40503u) & 0x007f007fu);
+    b[i] = 0x3b803b80u ^ ((t * 2246822519u + i * 9973u) & 0x007f007fu);
+  }
+  f32x16 acc[4] = {};
+  for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = mfma32(a, b, acc[j]);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += acc[j][r];
+  out[t] = s;
+}
+
+hipError_t launch_probe_mfma(int64_t iters, float* out, hipStream_t s) {
+  hipLaunchKernelGGL(mfma_probe_kernel, dim3(kProbeBlocks), dim3(kProbeThreads), 0, s, iters,
+                     out);
+  return hipGetLastError();
+}
+
+}  // namespace pbsa

@@ -74,6 +74,11 @@ _SIGS = {
     "pbsa_attn_bwd": ([ctypes.POINTER(Dims), _I32, Tensor, Tensor, Tensor, Tensor, _P, Tensor,
                        _P, _P, _I32, Tensor, Tensor, Tensor, _P, ctypes.c_size_t, _P],
                       ctypes.c_int),
+    # measurement probes (pbsa_probe.h)
+    "pbsa_probe_mfma": ([ctypes.c_int64, _P, _P], ctypes.c_int),
+    "pbsa_probe_mfma_flop": ([ctypes.c_int64], ctypes.c_int64),
+    "pbsa_probe_gather": ([ctypes.POINTER(Dims), Tensor, ctypes.POINTER(CacheC), Tensor, Tensor,
+                           _P, _P], ctypes.c_int),
 }
 
 
@@ -240,6 +245,25 @@ def pbsa_attn_fwd(shape: Shape, q, cache: Cache, chunk_k, chunk_v, sel, o, lse):
     _check("pbsa_attn_fwd", lib().pbsa_attn_fwd(ctypes.byref(shape.c()), qt,
                                                 ctypes.byref(cache.c()), kt, vt, _ptr(sel), ot,
                                                 _ptr(lse), _stream()))
+
+
+def pbsa_probe_gather(shape: Shape, q, cache: Cache, chunk_k, chunk_v, sel):
+    """Measurement probe: the gathers of pbsa_attn_fwd without its math (pbsa_probe.h)."""
+    H, d, T = shape.heads, shape.head_dim, shape.chunk_tokens
+    qt = _tok(q, "q", T, H, d)
+    kt = _tok(chunk_k, "chunk_k", T, H, d)
+    vt = _tok(chunk_v, "chunk_v", T, H, d)
+    _contig(sel, "sel", torch.int32, (H, shape.nq, shape.topk))
+    _check("pbsa_probe_gather", lib().pbsa_probe_gather(ctypes.byref(shape.c()), qt,
+                                                        ctypes.byref(cache.c()), kt, vt,
+                                                        _ptr(sel), _stream()))
+
+
+def pbsa_probe_mfma(iters: int, out):
+    """Measurement probe: independent bf16 MFMA chains on every SIMD; returns the FLOP."""
+    _contig(out, "out", torch.float32, (131072,))
+    _check("pbsa_probe_mfma", lib().pbsa_probe_mfma(int(iters), _ptr(out), _stream()))
+    return int(lib().pbsa_probe_mfma_flop(int(iters)))
 
 
 def pbsa_memory_update(shape: Shape, scores, cache: Cache, chunk_k, chunk_v, chunk_rep,

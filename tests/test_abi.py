@@ -10,13 +10,15 @@ from block_sparse_attention_pbsa_amd import ops, runtime
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "pbsa.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 
 pytestmark = pytest.mark.skipif(not os.path.exists(ops._LIB_PATH),
                                 reason="libpbsa.so not built (run __graft_entry__.build())")
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "\n".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(pbsa_[a-z0-9_]+)\s*\(", text)))
 
