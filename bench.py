@@ -20,6 +20,8 @@ to the 12 heads of a chunk.
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
 import os
 import sys
@@ -47,6 +49,9 @@ def parse():
                     help="HBM traffic per attention launch from rocprofv3 counters (if present)")
     ap.add_argument("--no-probes", action="store_true",
                     help="skip the measured ceilings (MFMA, copy, gather, full-history pool)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc output folders (FETCH_SIZE, WRITE_SIZE) of a "
+                         "--copy-probe run into the traffic file, then exit")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, copy a 512 MiB buffer 3 times (calibrates the "
                          "FETCH_SIZE / WRITE_SIZE counters against known bytes)")
@@ -55,6 +60,9 @@ def parse():
 
 def main():
     args = parse()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic, args.traffic)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
@@ -156,10 +164,13 @@ def main():
     }
     pool_bytes = shape.chunk_tokens * wl.heads * wl.head_dim * 2 + shape.nq * wl.heads * wl.head_dim * 4
 
+    # counters taken on another version of the kernel's sources do not count
     traffic = None
     if os.path.exists(args.traffic):
         try:
-            traffic = json.load(open(args.traffic)).get("bytes_per_launch")
+            rec = json.load(open(args.traffic))
+            if rec.get("source_sha256") == kernel_source_hash():
+                traffic = rec.get("bytes_per_launch")
         except (OSError, ValueError):
             traffic = None
 
@@ -189,7 +200,7 @@ def main():
         "pool_q_gbs": round(pool_bytes / (ops_ms["pool_q"] * 1e-3) / 1e9, 1),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "kernel": "attn_fwd_persistent_kernel<128>"},
+                     "traffic": traffic, "kernel": TRAFFIC_KERNEL},
     }
 
     if not args.no_probes:
@@ -209,6 +220,49 @@ def main():
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(wl, seed)
     print(json.dumps(result), flush=True)
+
+
+TRAFFIC_KERNEL = "attn_fwd_kernel<128, true, false>"
+KERNEL_SOURCES = ("attn_fwd.hip", "attn_common.h", "common.h", "launch.h")
+
+
+def kernel_source_hash():
+    """sha256 (first 16 hex digits) of the sources the timed attention kernel is built from."""
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "block_sparse_attention_pbsa_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def write_traffic(fetch_dir, write_dir, out_path):
+    """HBM bytes per attention launch from FETCH_SIZE and WRITE_SIZE (KiB per dispatch),
+    each scaled by what the counter reads for the 512 MiB copy of the same run."""
+    def read(d, counter):
+        rows = [r for r in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv")))
+                if r["Counter_Name"] == counter]
+        kern = [float(r["Counter_Value"]) for r in rows if TRAFFIC_KERNEL in r["Kernel_Name"]]
+        copy = max(float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"])
+        if not kern:
+            raise SystemExit(f"no {TRAFFIC_KERNEL} dispatch in {d}")
+        return float(np.mean(kern)), copy, len(kern)
+    f_k, f_c, n = read(fetch_dir, "FETCH_SIZE")
+    w_k, w_c, _ = read(write_dir, "WRITE_SIZE")
+    copy_kib = 512 * 1024  # the copy reads and writes 512 MiB
+    ff, wf = copy_kib / f_c, copy_kib / w_c
+    rd, wr = int(f_k * ff * 1024), int(w_k * wf * 1024)
+    rec = {"kernel": f"pbsa::{TRAFFIC_KERNEL}",
+           "workload": "wan_5s measured chunk (12 heads, d=128, 4680 queries, C=64, W=6, K=32)",
+           "source_sha256": kernel_source_hash(),
+           "fetch_size_kib_per_dispatch": round(f_k, 1), "write_size_kib_per_dispatch": round(w_k, 1),
+           "calibration": {"copy": "__amd_rocclr_copyBuffer of 512 MiB (bench.py --copy-probe)",
+                           "fetch_size_kib": f_c, "write_size_kib": w_c,
+                           "fetch_factor": round(ff, 4), "write_factor": round(wf, 4)},
+           "read_bytes_per_launch": rd, "write_bytes_per_launch": wr,
+           "bytes_per_launch": rd + wr, "dispatches": n}
+    with open(out_path, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec))
 
 
 def _timed_reps(torch, stream, fn, reps, flush=None):
@@ -267,11 +321,14 @@ def bench_probes(torch, ops, synth, shape, layer, q, k, v, stream):
     C, nq = shape.capacity, shape.nq
     steps = 0
     for h in range(shape.heads):
-        nshared = int((bid[h, :C] >= 0).sum()) + nq
-        nsh2 = nshared + (nshared & 1)
         for pr in range((nq + 1) // 2):
-            cnt = [int((sel[h, r] >= 0).sum()) if r < nq else 0 for r in (2 * pr, 2 * pr + 1)]
-            steps += nsh2 + 2 * max(cnt) + 2  # + the two steps gathered ahead past the end
+            # blocks routed by both query blocks of the pair join the shared steps
+            sa = {int(g) for g in sel[h, 2 * pr] if g >= 0}
+            sb = {int(g) for g in sel[h, 2 * pr + 1] if g >= 0} if 2 * pr + 1 < nq else set()
+            nshared = int((bid[h, :C] >= 0).sum()) + nq + len(sa & sb)
+            nsh2 = nshared + (nshared & 1)
+            # + the two steps gathered ahead past the end
+            steps += nsh2 + 2 * max(len(sa - sb), len(sb - sa)) + 2
     gbytes = steps * 32 * 1024
     g = lambda: ops.pbsa_probe_gather(shape, q, layer.cache, k, v, layer.sel)
     g()

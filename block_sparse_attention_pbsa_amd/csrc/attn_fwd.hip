@@ -8,9 +8,10 @@
 //
 // gfx950 design.  One workgroup = two 64-token query blocks of one head (A and B), four
 // waves of 32 query rows.  The KV blocks every query block of the head attends (the
-// persistent memory and the chunk itself) are gathered once for both; then each query
-// block's own routed window blocks.  Each step gathers two KV blocks (two shared ones, or
-// A's and B's routed ones).  Workgroups are numbered so that the eight XCDs each take a
+// persistent memory, the chunk itself, and the window blocks that A and B both routed to)
+// are gathered once for both; then each query block's remaining routed window blocks.
+// Each step gathers two half blocks (both halves of a shared block, or one half of A's and
+// the same half of B's next private block).  Workgroups are numbered so that the eight XCDs each take a
 // contiguous run of heads, keeping a head's KV in one XCD's L2.  Per KV block (64 keys,
 // possibly fewer in a frame's tail block):
 //   * the block is gathered from HBM/L2 with 16-byte loads into row-major LDS tiles; the
@@ -453,6 +454,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
   // then waits for every gather in flight before each list read).
   __shared__ uint32_t lists[kAttnListCap];
   __shared__ int wave_cnt[4];
+  __shared__ int part_cnt[4][3];
   __shared__ int n_list;
 
   // XCD-aware numbering: hardware workgroup i runs on XCD i % 8; give each XCD a
@@ -470,12 +472,13 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
   const int qrow = 32 * (w & 1) + c32;
   const int64_t t0 = r < a.nq ? block_token0(r, a.nb, a.n) : 0;
   const float c = a.scale * kLog2e;
-  int cntA, cntB;
+  int cntA, cntB, nboth = 0;
 
   // Block list entries (32 bits): bit 31 = token block of xk/xv (else a cache slot), bits
   // 24..30 = valid rows, bits 0..23 = the cache slot, or frame << 10 | block-in-frame.
   // Shared list (persistent mode): occupied P slots in slot order, then the chunk's
-  // blocks.  Private lists: A's and B's routed blocks.
+  // blocks, then the routed blocks that A and B have in common (kept at the end of A's
+  // list area, last to first).  Private lists: the routed blocks of A only and of B only.
   constexpr uint32_t kCacheBlockBytes = kBlock * D * 2;
   const uint32_t xrow = static_cast<uint32_t>(a.xts * 2);
   auto tok_entry = [&](int g) {
@@ -514,18 +517,86 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
   }
   // private lists; routed ids are ascending with -1 padding at the end (persistent) or
   // counted by nsel (two-level)
-  {
-    const int32_t* sa = a.sel + (static_cast<int64_t>(h) * a.nq + rA) * a.sel_stride;
-    const int32_t* sb = a.sel + (static_cast<int64_t>(h) * a.nq + rB) * a.sel_stride;
-    const int na = PERSIST ? a.sel_stride : a.nsel[static_cast<int64_t>(h) * a.nq + rA];
-    const int nbb = rB >= a.nq ? 0 : PERSIST ? a.sel_stride
-                                             : a.nsel[static_cast<int64_t>(h) * a.nq + rB];
-    auto entry = [&](int g) {
-      if (!PERSIST) return tok_entry(g);
-      const int f = g / a.nb, jj = g - f * a.nb;
-      const int slot = a.C + (f % a.W) * a.nb + jj;
-      return slot_entry(slot, a.blen[static_cast<int64_t>(h) * a.slots + slot]);
+  auto entry = [&](int g) {
+    if (!PERSIST) return tok_entry(g);
+    const int f = g / a.nb, jj = g - f * a.nb;
+    const int slot = a.C + (f % a.W) * a.nb + jj;
+    return slot_entry(slot, a.blen[static_cast<int64_t>(h) * a.slots + slot]);
+  };
+  const int32_t* sa = a.sel + (static_cast<int64_t>(h) * a.nq + rA) * a.sel_stride;
+  const int32_t* sb = a.sel + (static_cast<int64_t>(h) * a.nq + rB) * a.sel_stride;
+  if (PERSIST) {
+    // Split A's and B's routed sets into A only, B only and both.  The ascending ids are
+    // staged in two K tiles (no gather has targeted them yet) and looked up by binary
+    // search; each part is compacted in id order with ballots, so the lists (and the
+    // summation order) do not depend on timing.
+    int32_t* rawA = reinterpret_cast<int32_t*>(&kb0[0][0]);
+    int32_t* rawB = reinterpret_cast<int32_t*>(&kb1[0][0]);
+    const int nbb = rB >= a.nq ? 0 : a.sel_stride;
+    for (int j = t; j < a.sel_stride; j += 256) {
+      rawA[j] = sa[j];
+      rawB[j] = j < nbb ? sb[j] : -1;
+    }
+    __syncthreads();
+    int ca = 0, cb = 0;
+    for (int j = l; j < a.sel_stride; j += 64) {
+      ca += rawA[j] >= 0;
+      cb += rawB[j] >= 0;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      ca += __shfl_xor(ca, o, 64);
+      cb += __shfl_xor(cb, o, 64);
+    }
+    const int nA = __builtin_amdgcn_readfirstlane(ca);
+    const int nB = __builtin_amdgcn_readfirstlane(cb);
+    auto contains = [](const int32_t* ids, int n_ids, int g) {
+      int lo = 0, hi = n_ids;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (ids[mid] < g) lo = mid + 1;
+        else hi = mid;
+      }
+      return lo < n_ids && ids[lo] == g;
     };
+    int oa = 0, ob = 0, oi = 0;
+    const unsigned long long below = (1ull << l) - 1ull;
+    for (int j0 = 0; j0 < a.sel_stride; j0 += 256) {
+      const int j = j0 + t;
+      const int ga = j < nA ? rawA[j] : -1;
+      const int gb = j < nB ? rawB[j] : -1;
+      const bool both = ga >= 0 && contains(rawB, nB, ga);
+      const bool a_only = ga >= 0 && !both;
+      const bool b_only = gb >= 0 && !contains(rawA, nA, gb);
+      const unsigned long long ma = __ballot(a_only), mb = __ballot(b_only), mi = __ballot(both);
+      if (l == 0) {
+        part_cnt[w][0] = __popcll(ma);
+        part_cnt[w][1] = __popcll(mb);
+        part_cnt[w][2] = __popcll(mi);
+      }
+      __syncthreads();
+      int pa = oa, pb = ob, pi = oi;
+      for (int u = 0; u < 4; ++u) {
+        if (u < w) {
+          pa += part_cnt[u][0];
+          pb += part_cnt[u][1];
+          pi += part_cnt[u][2];
+        }
+        oa += part_cnt[u][0];
+        ob += part_cnt[u][1];
+        oi += part_cnt[u][2];
+      }
+      if (a_only) listA[pa + __popcll(ma & below)] = entry(ga);
+      if (b_only) listB[pb + __popcll(mb & below)] = entry(gb);
+      if (both) listA[a.sel_stride - 1 - (pi + __popcll(mi & below))] = entry(ga);
+      __syncthreads();
+    }
+    cntA = __builtin_amdgcn_readfirstlane(oa);
+    cntB = __builtin_amdgcn_readfirstlane(ob);
+    nboth = __builtin_amdgcn_readfirstlane(oi);
+  } else {
+    const int na = a.nsel[static_cast<int64_t>(h) * a.nq + rA];
+    const int nbb = rB >= a.nq ? 0 : a.nsel[static_cast<int64_t>(h) * a.nq + rB];
     for (int j = t; j < a.sel_stride; j += 256) {
       const int ga = j < na ? sa[j] : -1;
       const int gb = j < nbb ? sb[j] : -1;
@@ -545,6 +616,8 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
     cntA = __builtin_amdgcn_readfirstlane(ca);
     cntB = __builtin_amdgcn_readfirstlane(cb);
   }
+  const int nPq = nshared;  // P and chunk entries (persistent mode)
+  nshared += nboth;
   __syncthreads();
   // a shared step takes both halves of one shared block; a private step takes one half
   // of A's next routed block (X) and the same half of B's (Y).  The shared phase is
@@ -593,7 +666,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
     ey = 0;
     if (s >= nsteps) return;
     if (s < nshared) {
-      ex = shared_list[s];
+      ex = s < nPq ? shared_list[s] : listA[a.sel_stride - 1 - (s - nPq)];
       ey = ex;
     } else if (s >= nsh2) {
       const int blk = (s - nsh2) >> 1;

@@ -154,6 +154,8 @@ pbsa_status pbsa_score_topk(const pbsa_dims* dims, const float* q_rep, const pbs
  * chunk).  Writes o (bf16, same shape as q: chunk_frames*frame_tokens tokens per head)
  * and lse[h][t] = natural-log sum of exp(scale * q.k) over the attended keys (fp32
  * [heads][chunk tokens]).  q, chunk_k, chunk_v: chunk_frames*frame_tokens tokens each.
+ * sel: int32 [heads][Nq][topk] as pbsa_score_topk writes it: distinct global ids in
+ * ascending order, -1 only in the tail (other contents give undefined results).
  */
 pbsa_status pbsa_attn_fwd(const pbsa_dims* dims, pbsa_tensor q, const pbsa_cache* cache,
                           pbsa_tensor chunk_k, pbsa_tensor chunk_v, const int32_t* sel,
