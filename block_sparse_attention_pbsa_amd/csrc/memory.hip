@@ -16,6 +16,7 @@
 // empty one), and the same workgroup does both moves, so reads precede writes.
 #include "common.h"
 #include "launch.h"
+#include "select.h"
 
 namespace pbsa {
 
@@ -43,8 +44,8 @@ __device__ __forceinline__ float order_key(float x) { return x != x ? -INFINITY 
 // ascending id); their memory scores are column sums of the chunk's score matrix, computed
 // by all 16 waves with coalesced row reads (row group g = t / 256 sums rows g, g+4, ... of
 // the full groups of four, group 0 also the remaining rows; the four partials are added as
-// (g0 + g1) + (g2 + g3)).  Wave 0 then sorts (score, ~id) keys once to find the (C - S)-th
-// best key tau: a candidate is kept iff its key is >= tau.  Freed persistent slots
+// (g0 + g1) + (g2 + g3)).  Wave 0 then selects the C - S best (score, ~id) keys with an
+// exact radix select (a candidate is kept iff it is among them).  Freed persistent slots
 // (ascending) are handed to the promoted leaving blocks in ascending id order.  Dynamic
 // LDS: block_id and len of the head ([slots] each), candidate slot [ncand_max], free-slot
 // list [C], partial sums [4][ncand_max].
@@ -123,7 +124,16 @@ __global__ void __launch_bounds__(select_threads<E>()) memory_select_kernel(MemA
       const int s = cslot[c];
       for (int g = t >> 8; g < 4; g += NT / 256) {
         float acc = 0.f;
-        for (int r = g; r < full; r += 4) acc += sc[static_cast<int64_t>(r) * a.slots + s];
+        int r = g;
+        // eight rows loaded before they are added (the order of the additions is kept)
+        for (; r + 28 < full; r += 32) {
+          float v[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) v[u] = sc[static_cast<int64_t>(r + 4 * u) * a.slots + s];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) acc += v[u];
+        }
+        for (; r < full; r += 4) acc += sc[static_cast<int64_t>(r) * a.slots + s];
         if (g == 0)
           for (int r = full; r < a.nq; ++r) acc += sc[static_cast<int64_t>(r) * a.slots + s];
         part[g * ncand_max + c] = acc;
@@ -132,8 +142,8 @@ __global__ void __launch_bounds__(select_threads<E>()) memory_select_kernel(MemA
   }
   __syncthreads();
   if (w == 0) {
-    // memory scores and keys; keep a copy of the keys in candidate order
-    uint64_t key[E], mine[E];
+    // memory scores and keys (in candidate order)
+    uint64_t key[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int c = l + 64 * e;
@@ -143,25 +153,17 @@ __global__ void __launch_bounds__(select_threads<E>()) memory_select_kernel(MemA
                            (part[2 * ncand_max + c] + part[3 * ncand_max + c]);
         key[e] = rank_key(msum, sbid[cslot[c]]);
       }
-      mine[e] = key[e];
     }
     const int keep_n = a.C - a.S < ncand ? a.C - a.S : ncand;
-    uint64_t tau = 0;
     if (keep_n > 0) {
-      wave_sort_desc<E>(key, l);
-      const int e_t = (keep_n - 1) >> 6, l_t = (keep_n - 1) & 63;
-      uint64_t mykey = 0;
+      bool on[E];
+      wave_topk<E>(key, keep_n, on);
+      // kept flags per candidate (in candidate order), written over cslot's sign bit
 #pragma unroll
-      for (int e = 0; e < E; ++e)
-        if (e == e_t) mykey = key[e];
-      tau = (static_cast<uint64_t>(__shfl(static_cast<uint32_t>(mykey >> 32), l_t, 64)) << 32) |
-            __shfl(static_cast<uint32_t>(mykey), l_t, 64);
-    }
-    // kept flags per candidate (in candidate order), written over cslot's sign bit
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int c = l + 64 * e;
-      if (c < ncand && keep_n > 0 && mine[e] >= tau) cslot[c] = ~cslot[c];  // kept: negative
+      for (int e = 0; e < E; ++e) {
+        const int c = l + 64 * e;
+        if (c < ncand && on[e]) cslot[c] = ~cslot[c];  // kept: negative
+      }
     }
   }
   __syncthreads();

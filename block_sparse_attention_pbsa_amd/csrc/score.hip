@@ -10,10 +10,13 @@
 //
 // Latency-bound (~1e8 FLOP per chunk): scores are fp32 FMA dot products on the vector ALUs,
 // which keeps them within ~1e-7 of the exact value, so selections agree with an exact
-// reference wherever score gaps are larger.  Top-K is an in-register bitonic sort of
-// 64-bit (score, ~id) keys across one wave; NaN scores order as -inf.
+// reference wherever score gaps are larger.  Candidates are 64-bit (score, ~id) keys, so
+// that ties go to the lower id; NaN scores order as -inf.  The persistent mode's top-K is
+// an exact radix select over the keys held by one wave (one ballot per bit), the
+// two-level mode's an in-register bitonic sort.
 #include "common.h"
 #include "launch.h"
+#include "select.h"
 
 namespace pbsa {
 
@@ -46,45 +49,53 @@ __device__ __forceinline__ float dot_rep(const float* __restrict__ q_lds,
 // Row-parallel scores of QB query blocks against `cnt` representative rows.  Groups of
 // LPR = D/8 lanes read one row with 16-byte loads (whole rows per instruction), multiply
 // by the query blocks' matching 8 channels, and reduce across the group; the group's first
-// lane writes the QB scores of its row to out[qb * stride + row].
-template <int D, int QB>
+// lane writes the QB scores of its row to out[qb * stride + row].  U row groups are loaded
+// before any is used, so a pass over the rows waits for memory cnt / (U * step) times.
+template <int D, int QB, int U>
 __device__ __forceinline__ void score_rows(const float (&qv)[QB][8], const float* __restrict__ rep,
                                            const int32_t* __restrict__ bid, int cnt, float scale,
                                            float* out, int stride, int l, int first, int step) {
-  constexpr int LPR = D / 8, RPI = 64 / LPR;
+  constexpr int LPR = D / 8;
   const int g = l / LPR, sub = l % LPR;
-  for (int s0 = first; s0 < cnt; s0 += step) {
-    const int s = s0 + g;
-    float acc[QB];
+  for (int s0 = first; s0 < cnt; s0 += U * step) {
+    f32x4 a[U], b[U];
+    int id[U];
 #pragma unroll
-    for (int q = 0; q < QB; ++q) acc[q] = 0.f;
-    const bool on = s < cnt;
-    const int id = on ? bid[s] : -1;
-    if (on) {
-      const f32x4 a = *reinterpret_cast<const f32x4*>(rep + static_cast<int64_t>(s) * D + 8 * sub);
-      const f32x4 b = *reinterpret_cast<const f32x4*>(rep + static_cast<int64_t>(s) * D + 8 * sub + 4);
-#pragma unroll
-      for (int q = 0; q < QB; ++q) {
-        acc[q] = qv[q][0] * a[0] + qv[q][1] * a[1] + qv[q][2] * a[2] + qv[q][3] * a[3] +
-                 qv[q][4] * b[0] + qv[q][5] * b[1] + qv[q][6] * b[2] + qv[q][7] * b[3];
-      }
+    for (int u = 0; u < U; ++u) {
+      const int s = s0 + u * step + g;
+      const int sr = s < cnt ? s : 0;  // rows past the end re-read row 0, unused
+      const float* row = rep + static_cast<int64_t>(sr) * D + 8 * sub;
+      a[u] = *reinterpret_cast<const f32x4*>(row);
+      b[u] = *reinterpret_cast<const f32x4*>(row + 4);
+      id[u] = bid[sr];
     }
 #pragma unroll
-    for (int o = 1; o < LPR; o <<= 1)
+    for (int u = 0; u < U; ++u) {
+      float acc[QB];
 #pragma unroll
-      for (int q = 0; q < QB; ++q) acc[q] += __shfl_xor(acc[q], o, 64);
-    if (on && sub == 0) {
+      for (int q = 0; q < QB; ++q) {
+        acc[q] = qv[q][0] * a[u][0] + qv[q][1] * a[u][1] + qv[q][2] * a[u][2] +
+                 qv[q][3] * a[u][3] + qv[q][4] * b[u][0] + qv[q][5] * b[u][1] +
+                 qv[q][6] * b[u][2] + qv[q][7] * b[u][3];
+      }
 #pragma unroll
-      for (int q = 0; q < QB; ++q) out[q * stride + s] = id >= 0 ? scale * acc[q] : -INFINITY;
+      for (int o = 1; o < LPR; o <<= 1)
+#pragma unroll
+        for (int q = 0; q < QB; ++q) acc[q] += __shfl_xor(acc[q], o, 64);
+      const int s = s0 + u * step + g;
+      if (s < cnt && sub == 0) {
+#pragma unroll
+        for (int q = 0; q < QB; ++q) out[q * stride + s] = id[u] >= 0 ? scale * acc[q] : -INFINITY;
+      }
     }
   }
 }
 
 // grid (ceil(Nq / QB), H), QB waves scoring QB query blocks together: every representative
 // row is read once per QB query blocks, whole rows per load instruction, the waves taking
-// interleaved row groups.  Then wave q sorts query block q's window candidates: a bitonic
-// sort of their keys picks the top K and a second sort orders them by id.  Dynamic LDS:
-// [QB][slots] floats.
+// interleaved row groups.  Then wave q selects query block q's top K window candidates
+// and writes their ids in ascending order (each id's position = the number of selected ids
+// below it).  Dynamic LDS: [QB][slots] floats (a wave's row is reused for its selected ids).
 template <int D, int E, int QB>
 __global__ void __launch_bounds__(64 * QB)
     score_topk_kernel(const float* __restrict__ q_rep, const float* __restrict__ rep,
@@ -105,16 +116,15 @@ __global__ void __launch_bounds__(64 * QB)
   }
   const int32_t* bid = block_id + static_cast<int64_t>(h) * slots;
   const float* rp = rep + static_cast<int64_t>(h) * slots * D;
-  score_rows<D, QB>(qv, rp, bid, slots, scale, sc_lds, slots, l, w * RPI, QB * RPI);
+  score_rows<D, QB, 8>(qv, rp, bid, slots, scale, sc_lds, slots, l, w * RPI, QB * RPI);
   __syncthreads();
   // scores out (coalesced rows)
   for (int q = 0; q < nrows; ++q) {
     float* srow = scores + (static_cast<int64_t>(h) * nq + r0 + q) * slots;
     for (int s = t; s < slots; s += 64 * QB) srow[s] = sc_lds[q * slots + s];
   }
-  const int q = w;
-  if (q >= nrows) return;
   // window candidates: occupied ring slots holding non-sink blocks
+  const int q = w;
   const int nwin = slots - C;
   uint64_t key[E];
   int nvalid = 0;
@@ -122,7 +132,7 @@ __global__ void __launch_bounds__(64 * QB)
   for (int e = 0; e < E; ++e) {
     const int wi = l + 64 * e;
     key[e] = 0;
-    if (wi < nwin) {
+    if (q < nrows && wi < nwin) {
       const int id = bid[C + wi];
       if (id >= S) {
         key[e] = rank_key(sc_lds[q * slots + C + wi], id);
@@ -130,22 +140,38 @@ __global__ void __launch_bounds__(64 * QB)
       }
     }
   }
+  __syncthreads();  // every row has been read: a wave may now reuse its own
+  if (q >= nrows) return;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) nvalid += __shfl_xor(nvalid, o, 64);
   const int nsel = K < nvalid ? K : nvalid;
-  wave_sort_desc<E>(key, l);
-  // the first nsel keys are the selection; order them by id (ascending = ~id descending)
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int i = 64 * e + l;
-    key[e] = i < nsel ? static_cast<uint64_t>(~static_cast<uint32_t>(rank_key_id(key[e]))) : 0;
-  }
-  wave_sort_desc<E>(key, l);
   int32_t* out = sel + (static_cast<int64_t>(h) * nq + r0 + q) * K;
+  if (nsel > 0) {
+    bool on[E];
+    wave_topk<E>(key, nsel, on);
+    int* ids = reinterpret_cast<int*>(sc_lds + q * slots);  // nsel <= nwin < slots
+    int myid[E];
+    int base = 0;
+    const unsigned long long below = (1ull << l) - 1ull;
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int i = 64 * e + l;
-    if (i < nsel) out[i] = static_cast<int>(~static_cast<uint32_t>(key[e]));
+    for (int e = 0; e < E; ++e) {
+      myid[e] = rank_key_id(key[e]);
+      const unsigned long long m = __ballot(on[e]);
+      if (on[e]) ids[base + __popcll(m & below)] = myid[e];
+      base += __popcll(m);
+    }
+    // (one wave's LDS accesses complete in order: the reads below see the writes above)
+    int rk[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) rk[e] = 0;
+    for (int j = 0; j < nsel; ++j) {
+      const int v = ids[j];
+#pragma unroll
+      for (int e = 0; e < E; ++e) rk[e] += v < myid[e];
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (on[e]) out[rk[e]] = myid[e];
   }
   for (int p = nsel + l; p < K; p += 64) out[p] = -1;
 }
