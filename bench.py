@@ -4,14 +4,16 @@ One step = one chunk of one attention layer (one denoising pass) on the Wan2.1-1
 5-second workload: 12 heads, head_dim 128, 1560-token frames, 3-frame chunks (4680
 queries), 21-frame history, 64-token blocks, capacity 64 (1 sink), window 6 frames,
 top-32:
-    pool(q) + pool(k) + score_topk + attn_fwd + memory_update
+    pool(q) + score_topk + attn_fwd + memory_update (which pools k)
 on seeded synthetic bf16 inputs already resident in HBM.  The cache is bootstrapped by
 replaying the 7 history chunks; each timed step then feeds the measured chunk's tensors
-again, so the rollout keeps sliding with steady shapes.
+again, so the rollout keeps sliding with steady shapes.  The K timed steps run with no
+event between their launches.
 
 Prints one JSON line.  `roofline` is for the dominant kernel (attention forward, bf16 MFMA):
 achieved = algorithmic FLOP per launch (4 * head_dim per attended (query, key) pair)
-divided by that kernel's mean duration, measured with HIP events on the stream it runs on.
+divided by that kernel's mean duration: K back-to-back launches on the state the timed
+steps left, between two HIP events on the stream they run on.
 `cpu_baseline` times the fp64 oracle's chunk step on this host for one head and scales it
 to the 12 heads of a chunk.
 
@@ -108,59 +110,53 @@ def main():
 
     stream = torch.cuda.current_stream()
 
-    def step(ev=None):
+    def step():
         layer.route(q)
-        if ev is not None:
-            ev[0].record(stream)
         layer.attend(q, k, v)
-        if ev is not None:
-            ev[1].record(stream)
         layer.update(k, v)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    flop_before = attended_flop()
-    torch.cuda.synchronize()
 
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record(stream)
-    for i in range(args.steps):
-        step(evs[i])
+    for _ in range(args.steps):
+        step()
     t1.record(stream)
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
     ms_step = total_ms / args.steps
-    attn_ms = [a.elapsed_time(b) for a, b in evs]
-    attn_avg = float(np.mean(attn_ms))
-    flop_after = attended_flop()
-    flop = 0.5 * (flop_before + flop_after)
+
+    def timed(fn, reps):
+        """Mean duration (ms) of `reps` back-to-back launches of fn, HIP events on the
+        stream the kernels run on (no event between launches, so no gap is counted)."""
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    # The attention of the state the timed steps left (its routing refreshed first):
+    # `steps` back-to-back launches; the attended FLOP are counted for the same state.
+    flop = attended_flop()
+    torch.cuda.synchronize()
+    attn_avg = timed(lambda: layer.attend(q, k, v), args.steps)
     achieved = flop / (attn_avg * 1e-3) / 1e12
 
-    # per-op medians (separately timed, for the record)
-    def timed(fn, reps=20):
-        ts = []
-        for _ in range(reps):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            fn()
-            b.record(stream)
-            torch.cuda.synchronize()
-            ts.append(a.elapsed_time(b))
-        return float(np.median(ts))
-
     ops_ms = {
-        "pool_q": timed(lambda: ops.pbsa_pool(shape, q, wl.chunk_frames, layer.q_rep)),
-        "pool_k": timed(lambda: ops.pbsa_pool(shape, k, wl.chunk_frames, layer.k_rep)),
+        "route": timed(lambda: ops.pbsa_route(shape, q, layer.cache, layer.q_rep, layer.scores,
+                                              layer.sel), 20),
+        "pool_q": timed(lambda: ops.pbsa_pool(shape, q, wl.chunk_frames, layer.q_rep), 20),
         "score_topk": timed(lambda: ops.pbsa_score_topk(shape, layer.q_rep, layer.cache,
-                                                        layer.scores, layer.sel)),
-        # attention is timed only inside the steps above (events on its own stream), so
-        # that a profiler's per-kernel average over this run covers the same launches
-        "attn_fwd": float(np.median(attn_ms)),
+                                                        layer.scores, layer.sel), 20),
+        "attn_fwd": attn_avg,
     }
     pool_bytes = shape.chunk_tokens * wl.heads * wl.head_dim * 2 + shape.nq * wl.heads * wl.head_dim * 4
 
@@ -196,7 +192,7 @@ def main():
         "tflops_effective": round(flop / (ms_step * 1e-3) / 1e12, 2),
         "attn_fwd_flop": int(flop),
         "attn_fwd_ms": round(attn_avg, 4),
-        "ops_ms_median": {k_: round(v_, 4) for k_, v_ in ops_ms.items()},
+        "ops_ms_mean": {k_: round(v_, 4) for k_, v_ in ops_ms.items()},
         "pool_q_gbs": round(pool_bytes / (ops_ms["pool_q"] * 1e-3) / 1e9, 1),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),

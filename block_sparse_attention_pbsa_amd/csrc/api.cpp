@@ -193,6 +193,19 @@ pbsa_status pbsa_score_topk(const pbsa_dims* dims, const float* q_rep, const pbs
                     "score_topk");
 }
 
+pbsa_status pbsa_route(const pbsa_dims* dims, pbsa_tensor q, const pbsa_cache* cache,
+                       float* q_rep, float* scores, int32_t* sel, void* stream) {
+  PBSA_TRY(check_dims(dims, 0));
+  PBSA_TRY(check_cache(cache));
+  PBSA_TRY(check_tok(q, "q", dims->head_dim));
+  if (!scores || !sel) return fail(PBSA_ERR_NULL, "scores and sel are required");
+  if (reinterpret_cast<uintptr_t>(q_rep) % 16)
+    return fail(PBSA_ERR_ALIGN, "q_rep must be 16-byte aligned");
+  return hip_status(pbsa::launch_route(*dims, pbsa::tok_in(q), q_rep, *cache, scores, sel,
+                                       stream_of(stream)),
+                    "route");
+}
+
 pbsa_status pbsa_attn_fwd(const pbsa_dims* dims, pbsa_tensor q, const pbsa_cache* cache,
                           pbsa_tensor chunk_k, pbsa_tensor chunk_v, const int32_t* sel,
                           pbsa_tensor o, float* lse, void* stream) {
@@ -225,7 +238,7 @@ pbsa_status pbsa_memory_update(const pbsa_dims* dims, const float* scores, pbsa_
   PBSA_TRY(check_cache(cache));
   PBSA_TRY(check_tok(chunk_k, "chunk_k", dims->head_dim));
   PBSA_TRY(check_tok(chunk_v, "chunk_v", dims->head_dim));
-  if (!scores || !chunk_rep) return fail(PBSA_ERR_NULL, "scores and chunk_rep are required");
+  if (!scores) return fail(PBSA_ERR_NULL, "scores is required");
   const size_t need = pbsa::memory_update_workspace(*dims);
   if (!workspace || workspace_bytes < need)
     return fail(PBSA_ERR_WORKSPACE, "memory_update needs %zu workspace bytes (got %zu)", need,

@@ -43,6 +43,9 @@ hipError_t launch_cache_reset(const pbsa_dims& d, const pbsa_cache& c, hipStream
 hipError_t launch_score_topk(const pbsa_dims& d, const float* q_rep, const pbsa_cache& c,
                              float* scores, int32_t* sel, hipStream_t s);
 
+hipError_t launch_route(const pbsa_dims& d, TokIn q, float* q_rep, const pbsa_cache& c,
+                        float* scores, int32_t* sel, hipStream_t s);
+
 hipError_t launch_score_topk_2lvl(const pbsa_dims& d, int chunks, int top_frames,
                                   const int32_t* k_per_chunk, const float* q_rep,
                                   const float* block_rep, const float* frame_rep, int max_sel,

@@ -222,7 +222,8 @@ __global__ void __launch_bounds__(select_threads<E>()) memory_select_kernel(MemA
   }
 }
 
-// grid (F*nb, H), 256 threads.
+// grid (F*nb, H), 256 threads.  chunk_rep may be null: the block means of chunk_k are then
+// computed here from the rows being copied (fp32 sums).
 template <int D>
 __global__ void __launch_bounds__(256) memory_copy_kernel(MemArgs a, TokIn xk, TokIn xv,
                                                           const float* __restrict__ chunk_rep) {
@@ -258,6 +259,11 @@ __global__ void __launch_bounds__(256) memory_copy_kernel(MemArgs a, TokIn xk, T
   const bool sink = a.chunk == 0 && g < a.S;
   const int target = sink ? g : ring;
   const int64_t tok0 = static_cast<int64_t>(fl) * a.n + static_cast<int64_t>(kBlock) * j;
+  // thread t holds channels 8 (t % CH) .. of rows t / CH + (256 / CH) p; their K sums give
+  // the block's representative when the caller passes none
+  float ksum[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ksum[e] = 0.f;
 #pragma unroll
   for (int p = 0; p < PER; ++p) {
     const int q = t + 256 * p;
@@ -270,9 +276,32 @@ __global__ void __launch_bounds__(256) memory_copy_kernel(MemArgs a, TokIn xk, T
     const int64_t o = static_cast<int64_t>(target) * kBlock * D + 8 * q;
     *reinterpret_cast<u32x4*>(ck + o) = kv;
     *reinterpret_cast<u32x4*>(cv + o) = vv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ksum[2 * e] += __uint_as_float(kv[e] << 16);
+      ksum[2 * e + 1] += __uint_as_float(kv[e] & 0xffff0000u);
+    }
   }
-  const float* cr = chunk_rep + (static_cast<int64_t>(h) * a.nq + b) * D;
-  for (int c = t; c < D; c += 256) rep[static_cast<int64_t>(target) * D + c] = cr[c];
+  if (chunk_rep) {
+    const float* cr = chunk_rep + (static_cast<int64_t>(h) * a.nq + b) * D;
+    for (int c = t; c < D; c += 256) rep[static_cast<int64_t>(target) * D + c] = cr[c];
+  } else {
+    // lanes l, l ^ CH, ... of a wave share channels; then the four waves through LDS
+    __shared__ float wsum[4][D];
+    const int l = t & 63, w = t >> 6;
+#pragma unroll
+    for (int o = CH; o < 64; o <<= 1)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ksum[e] += __shfl_xor(ksum[e], o, 64);
+    if (l < CH)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) wsum[w][8 * l + e] = ksum[e];
+    __syncthreads();
+    const float inv = 1.f / static_cast<float>(len);
+    for (int c = t; c < D; c += 256)
+      rep[static_cast<int64_t>(target) * D + c] =
+          ((wsum[0][c] + wsum[1][c]) + (wsum[2][c] + wsum[3][c])) * inv;
+  }
   if (t == 0) {
     a.bid[hs + target] = g;
     a.blen[hs + target] = len;

@@ -96,9 +96,12 @@ __device__ __forceinline__ void score_rows(const float (&qv)[QB][8], const float
 // interleaved row groups.  Then wave q selects query block q's top K window candidates
 // and writes their ids in ascending order (each id's position = the number of selected ids
 // below it).  Dynamic LDS: [QB][slots] floats (a wave's row is reused for its selected ids).
-template <int D, int E, int QB>
+// POOL: wave q first pools query block q from the query tokens xq (the same arithmetic as
+// pool_blocks_kernel) and, if q_rep is not null, stores the mean there; otherwise q_rep is
+// read.
+template <int D, int E, int QB, bool POOL>
 __global__ void __launch_bounds__(64 * QB)
-    score_topk_kernel(const float* __restrict__ q_rep, const float* __restrict__ rep,
+    score_topk_kernel(TokIn xq, int n, int nb, float* q_rep, const float* __restrict__ rep,
                       const int32_t* __restrict__ block_id, int slots, int C, int S, int K,
                       int nq, float scale, float* __restrict__ scores,
                       int32_t* __restrict__ sel) {
@@ -107,12 +110,58 @@ __global__ void __launch_bounds__(64 * QB)
   const int nrows = nq - r0 < QB ? nq - r0 : QB;
   constexpr int LPR = D / 8, RPI = 64 / LPR;
   float qv[QB][8];
+  if constexpr (POOL) {
+    __shared__ float qp[QB][D];
+    if (w < nrows) {
+      const int r = r0 + w;
+      const int f = r / nb, j = r - f * nb;
+      const int len = block_len(j, n);
+      const int64_t t0 = static_cast<int64_t>(f) * n + static_cast<int64_t>(kBlock) * j;
+      const uint16_t* base = xq.p + h * xq.hs + t0 * xq.ts + 8 * (l % LPR);
+      u32x4 v[kBlock / RPI];
 #pragma unroll
-  for (int q = 0; q < QB; ++q) {
-    const int r = r0 + (q < nrows ? q : 0);
-    const float* qr = q_rep + (static_cast<int64_t>(h) * nq + r) * D + 8 * (l % LPR);
+      for (int i = 0; i < kBlock / RPI; ++i) {
+        const int row = l / LPR + RPI * i;
+        v[i] = row < len ? *reinterpret_cast<const u32x4*>(base + row * xq.ts) : u32x4{0, 0, 0, 0};
+      }
+      float acc[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) qv[q][e] = qr[e];
+      for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll
+      for (int i = 0; i < kBlock / RPI; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] += __uint_as_float(v[i][e] << 16);
+          acc[2 * e + 1] += __uint_as_float(v[i][e] & 0xffff0000u);
+        }
+#pragma unroll
+      for (int o = LPR; o < 64; o <<= 1)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], o, 64);
+      const float inv = 1.f / static_cast<float>(len);
+      if (l < LPR) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qp[w][8 * l + e] = acc[e] * inv;
+        if (q_rep) {
+          float* out = q_rep + (static_cast<int64_t>(h) * nq + r) * D + 8 * l;
+          reinterpret_cast<f32x4*>(out)[0] = f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+          reinterpret_cast<f32x4*>(out)[1] = f32x4{acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < QB; ++q)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qv[q][e] = qp[q < nrows ? q : 0][8 * (l % LPR) + e];
+  } else {
+#pragma unroll
+    for (int q = 0; q < QB; ++q) {
+      const int r = r0 + (q < nrows ? q : 0);
+      const float* qr = q_rep + (static_cast<int64_t>(h) * nq + r) * D + 8 * (l % LPR);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qv[q][e] = qr[e];
+    }
   }
   const int32_t* bid = block_id + static_cast<int64_t>(h) * slots;
   const float* rp = rep + static_cast<int64_t>(h) * slots * D;
@@ -176,8 +225,8 @@ __global__ void __launch_bounds__(64 * QB)
   for (int p = nsel + l; p < K; p += 64) out[p] = -1;
 }
 
-template <int D>
-static hipError_t launch_score_d(const pbsa_dims& d, const float* q_rep, const pbsa_cache& c,
+template <int D, bool POOL>
+static hipError_t launch_score_d(const pbsa_dims& d, TokIn xq, float* q_rep, const pbsa_cache& c,
                                  float* scores, int32_t* sel, hipStream_t s) {
   constexpr int QB = 4;
   const int nb = nb_of(d);
@@ -186,10 +235,10 @@ static hipError_t launch_score_d(const pbsa_dims& d, const float* q_rep, const p
   const int nwin = slots - d.capacity;
   const size_t lds = static_cast<size_t>(QB) * slots * sizeof(float);
   dim3 grid(cdiv(nq, QB), d.heads);
-#define PBSA_SCORE_E(EE)                                                                    \
-  hipLaunchKernelGGL((score_topk_kernel<D, EE, QB>), grid, dim3(64 * QB), lds, s, q_rep,     \
-                     c.rep, c.block_id, slots, d.capacity, d.sinks, d.topk, nq, d.scale, scores, \
-                     sel)
+#define PBSA_SCORE_E(EE)                                                                     \
+  hipLaunchKernelGGL((score_topk_kernel<D, EE, QB, POOL>), grid, dim3(64 * QB), lds, s, xq,     \
+                     d.frame_tokens, nb, q_rep, c.rep, c.block_id, slots, d.capacity, d.sinks, \
+                     d.topk, nq, d.scale, scores, sel)
   if (nwin <= 64) PBSA_SCORE_E(1);
   else if (nwin <= 128) PBSA_SCORE_E(2);
   else if (nwin <= 256) PBSA_SCORE_E(4);
@@ -201,8 +250,16 @@ static hipError_t launch_score_d(const pbsa_dims& d, const float* q_rep, const p
 
 hipError_t launch_score_topk(const pbsa_dims& d, const float* q_rep, const pbsa_cache& c,
                              float* scores, int32_t* sel, hipStream_t s) {
-  return d.head_dim == 128 ? launch_score_d<128>(d, q_rep, c, scores, sel, s)
-                           : launch_score_d<64>(d, q_rep, c, scores, sel, s);
+  const TokIn none{nullptr, 0, 0};
+  float* qr = const_cast<float*>(q_rep);  // read only when not pooling
+  return d.head_dim == 128 ? launch_score_d<128, false>(d, none, qr, c, scores, sel, s)
+                           : launch_score_d<64, false>(d, none, qr, c, scores, sel, s);
+}
+
+hipError_t launch_route(const pbsa_dims& d, TokIn q, float* q_rep, const pbsa_cache& c,
+                        float* scores, int32_t* sel, hipStream_t s) {
+  return d.head_dim == 128 ? launch_score_d<128, true>(d, q, q_rep, c, scores, sel, s)
+                           : launch_score_d<64, true>(d, q, q_rep, c, scores, sel, s);
 }
 
 // ---------------------------------------------------------------- two-level selection

@@ -63,6 +63,8 @@ _SIGS = {
     "pbsa_pool": ([ctypes.POINTER(Dims), Tensor, _I32, _P, _P, _P], ctypes.c_int),
     "pbsa_score_topk": ([ctypes.POINTER(Dims), _P, ctypes.POINTER(CacheC), _P, _P, _P],
                         ctypes.c_int),
+    "pbsa_route": ([ctypes.POINTER(Dims), Tensor, ctypes.POINTER(CacheC), _P, _P, _P, _P],
+                   ctypes.c_int),
     "pbsa_attn_fwd": ([ctypes.POINTER(Dims), Tensor, ctypes.POINTER(CacheC), Tensor, Tensor, _P,
                        Tensor, _P, _P], ctypes.c_int),
     "pbsa_memory_update": ([ctypes.POINTER(Dims), _P, ctypes.POINTER(CacheC), Tensor, Tensor, _P,
@@ -234,6 +236,18 @@ def pbsa_score_topk(shape: Shape, q_rep, cache: Cache, scores, sel):
                                                     _ptr(sel), _stream()))
 
 
+def pbsa_route(shape: Shape, q, cache: Cache, q_rep, scores, sel):
+    """pbsa_pool of q and pbsa_score_topk in one launch; q_rep may be None."""
+    H, d, T = shape.heads, shape.head_dim, shape.chunk_tokens
+    qt = _tok(q, "q", T, H, d)
+    if q_rep is not None:
+        _contig(q_rep, "q_rep", torch.float32, (H, shape.nq, d))
+    _contig(scores, "scores", torch.float32, (H, shape.nq, shape.slots))
+    _contig(sel, "sel", torch.int32, (H, shape.nq, shape.topk))
+    _check("pbsa_route", lib().pbsa_route(ctypes.byref(shape.c()), qt, ctypes.byref(cache.c()),
+                                          _ptr(q_rep), _ptr(scores), _ptr(sel), _stream()))
+
+
 def pbsa_attn_fwd(shape: Shape, q, cache: Cache, chunk_k, chunk_v, sel, o, lse):
     H, d, T = shape.heads, shape.head_dim, shape.chunk_tokens
     qt = _tok(q, "q", T, H, d)
@@ -268,11 +282,13 @@ def pbsa_probe_mfma(iters: int, out):
 
 def pbsa_memory_update(shape: Shape, scores, cache: Cache, chunk_k, chunk_v, chunk_rep,
                        workspace):
+    """chunk_rep=None: the chunk's block means are computed from chunk_k in the update."""
     H, d, T = shape.heads, shape.head_dim, shape.chunk_tokens
     _contig(scores, "scores", torch.float32, (H, shape.nq, shape.slots))
     kt = _tok(chunk_k, "chunk_k", T, H, d)
     vt = _tok(chunk_v, "chunk_v", T, H, d)
-    _contig(chunk_rep, "chunk_rep", torch.float32, (H, shape.nq, d))
+    if chunk_rep is not None:
+        _contig(chunk_rep, "chunk_rep", torch.float32, (H, shape.nq, d))
     _dev(workspace, "workspace", torch.uint8)
     cc = cache.c()
     _check("pbsa_memory_update", lib().pbsa_memory_update(

@@ -2,8 +2,9 @@
 library calls on torch's current stream, with every buffer allocated once up front.
 
 Per chunk (Sparse Forcing, gist.science, 2.C):
-    pool(q) -> q_rep;  pool(k) -> k_rep;  score_topk(q_rep, cache) -> scores, sel;
-    attn_fwd(q, cache, k, v, sel) -> o, lse;  memory_update(scores, cache, k, v, k_rep).
+    route(q, cache) -> q_rep, scores, sel  (pool of q, scores, top-K in one launch);
+    attn_fwd(q, cache, k, v, sel) -> o, lse;
+    memory_update(scores, cache, k, v) (which pools k into the cache's representatives).
 With several denoising passes per chunk the persistent memory is shared: only the last
 pass (the one whose K/V enter the cache) calls memory_update.
 """
@@ -20,7 +21,6 @@ class PersistentLayer:
         H, d, nq, T = shape.heads, shape.head_dim, shape.nq, shape.chunk_tokens
         self.cache = ops.Cache(shape, device)
         self.q_rep = torch.empty(H, nq, d, dtype=torch.float32, device=device)
-        self.k_rep = torch.empty(H, nq, d, dtype=torch.float32, device=device)
         self.scores = torch.empty(H, nq, shape.slots, dtype=torch.float32, device=device)
         self.sel = torch.empty(H, nq, shape.topk, dtype=torch.int32, device=device)
         self.o = torch.empty(T, H, d, dtype=torch.bfloat16, device=device)
@@ -32,17 +32,14 @@ class PersistentLayer:
         ops.pbsa_cache_reset(self.shape, self.cache)
 
     def route(self, q):
-        s = self.shape
-        ops.pbsa_pool(s, q, s.chunk_frames, self.q_rep)
-        ops.pbsa_score_topk(s, self.q_rep, self.cache, self.scores, self.sel)
+        ops.pbsa_route(self.shape, q, self.cache, self.q_rep, self.scores, self.sel)
 
     def attend(self, q, k, v):
         ops.pbsa_attn_fwd(self.shape, q, self.cache, k, v, self.sel, self.o, self.lse)
 
     def update(self, k, v):
         s = self.shape
-        ops.pbsa_pool(s, k, s.chunk_frames, self.k_rep)
-        ops.pbsa_memory_update(s, self.scores, self.cache, k, v, self.k_rep, self.workspace)
+        ops.pbsa_memory_update(s, self.scores, self.cache, k, v, None, self.workspace)
 
     def step(self, q, k, v, attend=True):
         """One chunk: route, attend (optional), update the memory and append the chunk."""

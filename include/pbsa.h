@@ -146,6 +146,15 @@ pbsa_status pbsa_pool(const pbsa_dims* dims, pbsa_tensor x, int32_t frames, floa
 pbsa_status pbsa_score_topk(const pbsa_dims* dims, const float* q_rep, const pbsa_cache* cache,
                             float* scores, int32_t* sel, void* stream);
 
+/* Steps 1 and 2 of the query side in one launch: pools the chunk's query blocks (as
+ * pbsa_pool of q) and scores and routes them (as pbsa_score_topk), with the same results.
+ * q: chunk_frames*frame_tokens tokens per head.  q_rep: fp32 [heads][Nq][head_dim], 16-byte
+ * aligned, receives the query block means, or NULL when they are not needed.  scores, sel:
+ * as pbsa_score_topk.
+ */
+pbsa_status pbsa_route(const pbsa_dims* dims, pbsa_tensor q, const pbsa_cache* cache,
+                       float* q_rep, float* scores, int32_t* sel, void* stream);
+
 /* ---- step 3: attention over the selected blocks (persistent mode) --------------------
  * Sparse Forcing 2.C and the Chinese page's 2.2 (fine-grained attention, hybrid mask):
  * every query token t of query block r attends, with softmax scale dims.scale, to the
@@ -171,7 +180,9 @@ pbsa_status pbsa_attn_fwd(const pbsa_dims* dims, pbsa_tensor q, const pbsa_cache
  * by (memory score desc, id asc).  Kept blocks stay in their slots, promoted blocks are
  * copied (K, V, rep, len) into the freed slots in ascending id order, and the chunk's K/V
  * and chunk_rep (fp32 [heads][Nq][head_dim], pbsa_pool of chunk_k) are written into the
- * window slots of the frames that left.  On chunk 0 the sink blocks go to slots [0, S).
+ * window slots of the frames that left.  chunk_rep may be NULL: the block means of chunk_k
+ * are then computed from the rows being copied (fp32, equal to pbsa_pool's up to the order
+ * of the additions).  On chunk 0 the sink blocks go to slots [0, S).
  * Finally cache->chunk_index is incremented (host).
  * workspace: device, >= pbsa_workspace_bytes(dims, PBSA_OP_MEMORY_UPDATE, 0, 0) bytes.
  */

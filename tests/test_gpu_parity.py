@@ -217,6 +217,65 @@ def test_rollout_wan_1min_parity():
     say(f"  wan_1min: {stats}")
 
 
+@pytest.mark.parametrize("name", ["small64", "wan_5s"])
+def test_route_equals_pool_then_score_topk(name):
+    """pbsa_route (pooling fused into the routing launch) gives bit-identical q_rep, scores
+    and selections to pbsa_pool followed by pbsa_score_topk, with and without q_rep."""
+    wl = (synth.Workload("small64", 2, 64, 64, 100, 2, 8, 4, 3, 1, 3) if name == "small64"
+          else synth.WORKLOADS[name])
+    shape = shape_of(wl)
+    layer = runtime.PersistentLayer(shape)
+    layer.reset()
+    H, nq, d = wl.heads, shape.nq, wl.head_dim
+    q_rep = torch.empty(H, nq, d, dtype=torch.float32, device="cuda")
+    scores = torch.empty(H, nq, shape.slots, dtype=torch.float32, device="cuda")
+    sel = torch.empty(H, nq, wl.topk, dtype=torch.int32, device="cuda")
+    for c in range(wl.measured_chunk + 1):
+        say(f"[route {name}] chunk {c}")
+        q, k, v = (dev(x) for x in synth.chunk_qkv(wl, 5, c))
+        ops.pbsa_pool(shape, q, shape.chunk_frames, q_rep)
+        ops.pbsa_score_topk(shape, q_rep, layer.cache, scores, sel)
+        layer.route(q)
+        torch.cuda.synchronize()
+        assert torch.equal(layer.q_rep, q_rep)
+        assert torch.equal(layer.scores, scores)
+        assert torch.equal(layer.sel, sel)
+        layer.scores.zero_()
+        layer.sel.fill_(-7)
+        ops.pbsa_route(shape, q, layer.cache, None, layer.scores, layer.sel)
+        torch.cuda.synchronize()
+        assert torch.equal(layer.scores, scores) and torch.equal(layer.sel, sel)
+        layer.update(k, v)
+
+
+@pytest.mark.parametrize("head_dim", [128, 64])
+def test_memory_update_pooled_rep_matches_given_rep(head_dim):
+    """memory_update with chunk_rep = pbsa_pool(chunk_k) and with chunk_rep = NULL (block
+    means taken in the update) leave the same cache: identical ids, lengths and K/V bytes,
+    representatives equal up to fp32 rounding.  Both updates use the same scores, so that
+    rounding in the representatives cannot change a selection."""
+    wl = synth.Workload("rep", 2, head_dim, 64, 100, 2, 8, 4, 3, 1, 3)
+    shape = shape_of(wl)
+    a, b = runtime.PersistentLayer(shape), runtime.PersistentLayer(shape)
+    a.reset()
+    b.reset()
+    k_rep = torch.empty(wl.heads, shape.nq, head_dim, dtype=torch.float32, device="cuda")
+    for c in range(wl.measured_chunk + 1):
+        say(f"[rep d={head_dim}] chunk {c}")
+        q, k, v = (dev(x) for x in synth.chunk_qkv(wl, 91, c))
+        a.route(q)
+        ops.pbsa_pool(shape, k, shape.chunk_frames, k_rep)
+        ops.pbsa_memory_update(shape, a.scores, a.cache, k, v, k_rep, a.workspace)
+        ops.pbsa_memory_update(shape, a.scores, b.cache, k, v, None, b.workspace)
+        torch.cuda.synchronize()
+        assert torch.equal(a.cache.block_id, b.cache.block_id)
+        assert torch.equal(a.cache.len, b.cache.len)
+        assert torch.equal(a.cache.k.view(torch.int16), b.cache.k.view(torch.int16))
+        assert torch.equal(a.cache.v.view(torch.int16), b.cache.v.view(torch.int16))
+        occ = a.cache.block_id >= 0
+        assert (a.cache.rep[occ] - b.cache.rep[occ]).abs().max().item() < 1e-6
+
+
 def test_attn_fwd_d64_ragged_small():
     # head_dim 64, 100-token frames (64 + 36), window smaller than the history
     wl = synth.Workload("small64", 2, 64, 64, 100, 2, 8, 4, 3, 1, 3)
