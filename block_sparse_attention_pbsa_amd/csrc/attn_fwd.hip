@@ -106,6 +106,27 @@ __device__ __forceinline__ void lds_dma16(const char* src, char* lds) {
   __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
 }
 
+// Piece i (0..3) of a run of 1 KB LDS pieces: the instruction's immediate offset 1024 i is
+// added to both the global and the LDS address, so a run shares one LDS base (M0) and
+// one scalar global base, and each piece costs one vector add for its lane offsets.
+// src must already be lowered by 1024 i.
+__device__ __forceinline__ void lds_dma16_piece(int i, __amdgpu_buffer_rsrc_t rs, uint32_t voff,
+                                                char* lds) {
+  switch (i) {
+    case 0: __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds, 16, voff, 0, 0, 0); break;
+    case 1: __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds, 16, voff, 0, 1024, 0); break;
+    case 2: __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds, 16, voff, 0, 2048, 0); break;
+    default: __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds, 16, voff, 0, 3072, 0); break;
+  }
+}
+// Scalar base 3 KB below p: per-piece lane offsets (up to 3 KB lower for piece 3) then
+// stay non-negative.  The empty asm keeps the base in scalar registers as a value of its
+// own, so that the compiler cannot fold the bias back into each lane's address.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t dma_base(const char* p) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p - 3072), (short)0, 0x7fffffff,
+                                           0x00020000);
+}
+
 struct HalfRef {
   const char* k;
   const char* v;
@@ -715,23 +736,32 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
   // so this wave's K pieces all use rows 16 (w & 1) + (l & 15) (one lane offset per step)
   // and its V pieces rows (l >> 2) or 16 + (l >> 2) (two lane offsets per step); the
   // piece's chunk or segment is a scalar offset.
+  // The wave's HP pieces of a tile form one run (lds_dma16_piece): one LDS base, one
+  // scalar global base (dma_base, 3 KB low) and per-piece lane offsets raised by 3 KB and
+  // lowered by the piece's 1 KB immediate offset.
   struct Offs {
-    uint32_t k, v0, v1;
+    __amdgpu_buffer_rsrc_t kb, vb;  // dma_base(hr.k), dma_base(hr.v)
+    uint32_t k, v0, v1;   // lane offsets of K, and of V rows (l >> 2) and 16 + (l >> 2)
   };
   auto offsets = [&](const HalfRef& hr) {
     const uint32_t last = static_cast<uint32_t>(hr.len > 0 ? hr.len - 1 : 0);
     Offs o;
-    o.k = min(16u * (w & 1) + k_rowl, last) * hr.stride + k_colb;
-    o.v0 = min(v_rowl, last) * hr.stride + v_colb;
-    o.v1 = min(16u + v_rowl, last) * hr.stride + v_colb;
+    o.kb = dma_base(hr.k);
+    o.vb = dma_base(hr.v);
+    o.k = min(16u * (w & 1) + k_rowl, last) * hr.stride + k_colb + 3072u;
+    // this wave's V pieces p0 + i lie in segments (p0 + i) / 2 = p0 / 2 + i / 2
+    o.v0 = min(v_rowl, last) * hr.stride + v_colb + 32u * p0 + 3072u;
+    o.v1 = min(16u + v_rowl, last) * hr.stride + v_colb + 32u * p0 + 3072u;
     return o;
   };
   auto gather_k = [&](char (*buf)[HT::BYTES], const HalfRef& hr, const Offs& o, int i) {
-    lds_dma16(hr.k + 64 * i + o.k, buf[tw] + 1024 * (p0 + i));
+    (void)hr;
+    lds_dma16_piece(i, o.kb, o.k + 64u * i - 1024u * i, buf[tw] + 1024 * p0);
   };
   auto gather_v = [&](char (*buf)[HT::BYTES], const HalfRef& hr, const Offs& o, int i) {
-    const int p = p0 + i;
-    lds_dma16(hr.v + 64 * (p / 2) + (p % 2 ? o.v1 : o.v0), buf[tw] + 1024 * p);
+    (void)hr;
+    lds_dma16_piece(i, o.vb, (i % 2 ? o.v1 : o.v0) + 64u * (i / 2) - 1024u * i,
+                    buf[tw] + 1024 * p0);
   };
   // Waits before the barriers that publish gathered tiles.  Each wave's gathers in issue
   // order: K(s), V(s), K(s+1), V(s+1), ... (HP instructions each).  Before the top barrier
