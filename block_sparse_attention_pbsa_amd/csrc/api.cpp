@@ -90,11 +90,14 @@ pbsa_status check_tok(const pbsa_tensor& t, const char* name, int head_dim) {
   return PBSA_OK;
 }
 
-// The attention kernels address a head's token rows with 32-bit byte offsets.
+// The attention kernels address a head's token rows with 32-bit byte offsets and name a
+// token block by its first token in 24 bits.
 pbsa_status check_span(const pbsa_tensor& t, const char* name, int64_t tokens, int head_dim) {
   const int64_t bytes = (tokens - 1) * t.token_stride * 2 + int64_t{head_dim} * 2;
   if (tokens > 0 && bytes > (int64_t{1} << 31))
     return fail(PBSA_ERR_UNSUPPORTED, "%s spans more than 2 GiB per head", name);
+  if (tokens > (int64_t{1} << 24))
+    return fail(PBSA_ERR_UNSUPPORTED, "%s has more than 2^24 tokens", name);
   return PBSA_OK;
 }
 

@@ -496,7 +496,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
   int cntA, cntB, nboth = 0;
 
   // Block list entries (32 bits): bit 31 = token block of xk/xv (else a cache slot), bits
-  // 24..30 = valid rows, bits 0..23 = the cache slot, or frame << 10 | block-in-frame.
+  // 24..30 = valid rows, bits 0..23 = the cache slot, or the block's first token.
   // Shared list (persistent mode): occupied P slots in slot order, then the chunk's
   // blocks, then the routed blocks that A and B have in common (kept at the end of A's
   // list area, last to first).  Private lists: the routed blocks of A only and of B only.
@@ -505,7 +505,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
   auto tok_entry = [&](int g) {
     const int f = g / a.nb, jj = g - f * a.nb;
     return 0x80000000u | (static_cast<uint32_t>(block_len(jj, a.n)) << 24) |
-           (static_cast<uint32_t>(f) << 10) | static_cast<uint32_t>(jj);
+           static_cast<uint32_t>(f * a.n + kBlock * jj);
   };
   auto slot_entry = [&](int slot, int len) {
     return (static_cast<uint32_t>(len) << 24) | static_cast<uint32_t>(slot);
@@ -662,23 +662,28 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
                      static_cast<int64_t>(h) * a.slots * kCacheBlockBytes;
   const char* xk_h = reinterpret_cast<const char*>(a.xk + h * a.xhs);
   const char* xv_h = reinterpret_cast<const char*>(a.xv + h * a.xhs);
-  // list entries are wave-uniform: readfirstlane keeps them (and the gather base
-  // addresses) in scalar registers
-  auto ref_of = [&](uint32_t e_, int half, HalfRef& hr) {
-    const uint32_t e = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(e_)));
+  auto half_len = [](uint32_t e, int half) {  // valid rows of half tile `half` (0 if e = 0)
+    const int len = static_cast<int>((e >> 24) & 0x7f) - 32 * half;
+    return len < 0 ? 0 : (len < 32 ? len : 32);
+  };
+  auto ref_of = [&](uint32_t e, int half, HalfRef& hr) {
     const bool tok = (e >> 31) != 0;
-    const int full = static_cast<int>((e >> 24) & 0x7f);
     const uint32_t id = e & 0xffffffu;
-    const uint32_t off =
-        tok ? ((id >> 10) * static_cast<uint32_t>(a.n) + kBlock * (id & 1023u)) * xrow
-            : id * kCacheBlockBytes;
     const uint32_t stride = tok ? xrow : 2 * D;
-    const uint32_t o = off + 32 * half * stride;
-    const int len = full - 32 * half;
-    hr.k = (tok ? xk_h : ck_h) + o;
-    hr.v = (tok ? xv_h : cv_h) + o;
-    hr.stride = stride;
-    hr.len = len < 0 ? 0 : (len < 32 ? len : 32);
+    const uint32_t o = (tok ? id * xrow : id * kCacheBlockBytes) + 32 * half * stride;
+    hr.len = half_len(e, half);
+    if (hr.len > 0) {
+      hr.k = (tok ? xk_h : ck_h) + o;
+      hr.v = (tok ? xv_h : cv_h) + o;
+      hr.stride = stride;
+    } else {
+      // an empty half tile still gets its gathers (of the head's first token row, so
+      // that every step issues the same number and the waits stay fixed); its rows are
+      // masked or weighted by zero
+      hr.k = xk_h;
+      hr.v = xv_h;
+      hr.stride = 0;
+    }
   };
   // Raw list entries of step s for X and Y (0 = nothing).  They are read one step before
   // they are decoded, so the LDS read's latency is never waited for.
@@ -696,29 +701,20 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
     }
   };
   // This wave's half tile of step s (see the gathers below) and the lengths of X and Y.
-  auto decode = [&](int s, uint32_t ex, uint32_t ey, HalfRef& mineref, int& lenX, int& lenY) {
-    HalfRef x{nullptr, nullptr, 0, 0}, y{nullptr, nullptr, 0, 0};
+  // Only this wave's half tile is decoded into addresses; of the other, its length.
+  auto decode = [&](int s, uint32_t ex_, uint32_t ey_, HalfRef& mineref, int& lenX, int& lenY) {
+    // list entries are wave-uniform: readfirstlane keeps them (and the gather base
+    // addresses) in scalar registers
+    const uint32_t ex = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(ex_)));
+    const uint32_t ey = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(ey_)));
     // a shared step takes halves 0 (X) and 1 (Y) of one block; a private step the same
     // half of A's (X) and B's (Y) next routed block
     const int hx = s < nshared ? 0 : ((s - nsh2) & 1);
     const int hy = s < nshared ? 1 : hx;
-    if (ex) ref_of(ex, hx, x);
-    if (ey) ref_of(ey, hy, y);
-    lenX = x.len;
-    lenY = y.len;
+    lenX = half_len(ex, hx);
+    lenY = half_len(ey, hy);
     const bool use_y = (w >> 1) != 0;
-    mineref.k = use_y ? y.k : x.k;
-    mineref.v = use_y ? y.v : x.v;
-    mineref.stride = use_y ? y.stride : x.stride;
-    mineref.len = use_y ? y.len : x.len;
-    if (mineref.len == 0) {
-      // an empty half tile still gets its gathers (of the head's first token row, so
-      // that every step issues the same number and the waits stay fixed); its rows are
-      // masked or weighted by zero
-      mineref.k = xk_h;
-      mineref.v = xv_h;
-      mineref.stride = 0;
-    }
+    ref_of(use_y ? ey : ex, use_y ? hy : hx, mineref);
   };
 
   // Gathers: waves 0, 1 gather half tile X of every step, waves 2, 3 half tile Y; each

@@ -32,7 +32,7 @@
  *    beyond them): persistent mode: capacity + window blocks <= 4096, capacity - sinks
  *    <= 1024, window blocks <= 1024, topk <= 1024 and, for pbsa_attn_fwd, capacity +
  *    chunk blocks + 2*topk <= 3072; two-level mode: pbsa_attn_fwd_2lvl max_sel <= 1536;
- *    a head's K/V token rows span at most 2 GiB.
+ *    a head's K/V token rows span at most 2 GiB and 2^24 tokens.
  */
 #ifndef PBSA_H_
 #define PBSA_H_
