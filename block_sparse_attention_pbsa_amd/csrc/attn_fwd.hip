@@ -687,17 +687,20 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
   };
   // Raw list entries of step s for X and Y (0 = nothing).  They are read one step before
   // they are decoded, so the LDS read's latency is never waited for.
+  // (Indices into `lists` itself, not pointers chosen at run time: the compiler then still
+  // sees that these reads cannot touch a tile being gathered and adds no wait for them.)
+  const int offA = static_cast<int>(listA - lists), offB = offA + a.sel_stride;
   auto fetch = [&](int s, uint32_t& ex, uint32_t& ey) {
     ex = 0;
     ey = 0;
     if (s >= nsteps) return;
     if (s < nshared) {
-      ex = s < nPq ? shared_list[s] : listA[a.sel_stride - 1 - (s - nPq)];
+      ex = lists[s < nPq ? s : offB - 1 - (s - nPq)];
       ey = ex;
     } else if (s >= nsh2) {
       const int blk = (s - nsh2) >> 1;
-      if (blk < cntA) ex = listA[blk];
-      if (blk < cntB) ey = listB[blk];
+      if (blk < cntA) ex = lists[offA + blk];
+      if (blk < cntB) ey = lists[offB + blk];
     }
   };
   // This wave's half tile of step s (see the gathers below) and the lengths of X and Y.
