@@ -222,58 +222,10 @@ struct RowState {
         if (acc_row(r, h2) >= len) sa[r] = -INFINITY;
     }
   }
-  // Online softmax of one score tile without touching the accumulators: raises the running
-  // max when some row's new max exceeds it by more than 2^8 in exp2 units (so exp2
-  // arguments stay <= 8), folds the factor into l_run and returns it through alpha (the
-  // caller rescales acc when the result is true), and packs P to bf16 for the PV step.
-  __device__ __forceinline__ bool softmax(const f32x16& sa, float c, u32x4 (&pb)[2],
-                                          float& alpha) {
-    float mx = sa[0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sa[r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const bool up = __any(mx * c > m_run * c + 8.f);
-    const float m_new = up ? fmaxf(m_run, mx) : m_run;
-    alpha = up ? __builtin_amdgcn_exp2f(m_run * c - m_new * c) : 1.f;
-    m_run = m_new;
-    const float m_off = m_new * c;
-    float p[16];
-    float psum = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      p[r] = __builtin_amdgcn_exp2f(fmaf(sa[r], c, -m_off));
-      psum += p[r];
-    }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) pb[t2][e] = pack_bf16x2(p[8 * t2 + 2 * e], p[8 * t2 + 2 * e + 1]);
-    return up;
-  }
   __device__ __forceinline__ void rescale(float alpha) {
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt) acc[dt] *= alpha;
   }
-  __device__ __forceinline__ void pvmma(const u32x4 (&pb)[2], const char* vb) {
-    lds_u16* base = (lds_u16*)(vb);
-#pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2) {
-      u32x4 vop[ND];
-#pragma unroll
-      for (int dt = 0; dt < ND; ++dt) {
-        const s16x4_ lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4*)(base + (2048 * dt + 1024 * t2) / 2));
-        const s16x4_ hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4*)(base + (2048 * dt + 1024 * t2 + 512) / 2));
-        const u32x2 x = __builtin_bit_cast(u32x2, lo), y = __builtin_bit_cast(u32x2, hi);
-        vop[dt] = u32x4{x[0], x[1], y[0], y[1]};
-      }
-#pragma unroll
-      for (int dt = 0; dt < ND; ++dt) acc[dt] = mfma32(vop[dt], pb[t2], acc[dt]);
-    }
-  }
-
   // The transposing V reads of MFMA j (t2 = j / ND, dt = j % ND) of a PV step.
   __device__ __forceinline__ static u32x4 vread(const char* vb, int j) {
     const int t2 = j / ND, dt = j % ND;
