@@ -1,0 +1,196 @@
+"""Routing and memory-update selections at sizes that take the wide register paths of the
+wave top-K (window of 600 blocks: 16 keys per lane; 1047 memory candidates: 32 keys per
+lane), on synthetic cache states built directly, checked against the fp64 oracle.
+
+Selections must match exactly wherever the exact score gap at the selection boundary
+exceeds 1e-5 (near ties: any correct set); exact ties must go to the lower id."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+from block_sparse_attention_pbsa_amd import ops, synth
+from parity import check_topk, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ops.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+N_TOK, NB = 1600, 25  # 25 blocks per frame
+
+
+def _window_state(shape, f_last, rng, drop=0.05):
+    """block_id [H][slots] for a window holding frames (f_last - W, f_last] in their ring
+    slots, a few slots empty, and P slots [0, C) holding the sinks and older ids."""
+    H, C, S, W = shape.heads, shape.capacity, shape.sinks, shape.window_frames
+    bid = np.full((H, C + W * NB), -1, np.int32)
+    for h in range(H):
+        old = rng.choice(np.arange(S, (f_last - W + 1) * NB), C - S, replace=False)
+        bid[h, :S] = np.arange(S)
+        bid[h, S:C] = np.sort(old)
+        for f in range(f_last - W + 1, f_last + 1):
+            for j in range(NB):
+                if rng.random() >= drop:
+                    bid[h, C + (f % W) * NB + j] = f * NB + j
+    return bid
+
+
+@pytest.mark.parametrize("topk,tie_all", [(1, False), (100, False), (600, False), (37, True)])
+def test_score_topk_600_window_blocks(topk, tie_all):
+    H, D = 2, 128
+    shape = ops.Shape(H, D, N_TOK, 1, 24, 64, 1, topk)
+    rng = np.random.default_rng(600 + topk)
+    cache = ops.Cache(shape)
+    bid = _window_state(shape, f_last=60, rng=rng)
+    rep = rng.standard_normal((H, shape.slots, D)).astype(np.float32)
+    if tie_all:
+        rep[:, shape.capacity:] = rep[:, shape.capacity:shape.capacity + 1]  # one row for all
+    else:
+        # a few exact duplicates, so some scores tie bit for bit
+        for h in range(H):
+            src = rng.choice(np.arange(shape.capacity, shape.slots), 40)
+            dst = rng.choice(np.arange(shape.capacity, shape.slots), 40)
+            rep[h, dst] = rep[h, src]
+    cache.block_id.copy_(torch.from_numpy(bid))
+    cache.len.copy_(torch.from_numpy(np.where(bid >= 0, 64, 0).astype(np.int32)))
+    cache.rep.copy_(torch.from_numpy(rep))
+    q_rep = torch.from_numpy(rng.standard_normal((H, shape.nq, D)).astype(np.float32)).cuda()
+    scores = torch.empty(H, shape.nq, shape.slots, dtype=torch.float32, device="cuda")
+    sel = torch.full((H, shape.nq, topk), -7, dtype=torch.int32, device="cuda")
+    say(f"[score_topk wide] K={topk} ties={tie_all}")
+    ops.pbsa_score_topk(shape, q_rep, cache, scores, sel)
+    torch.cuda.synchronize()
+    sc, sl, qr = scores.cpu().numpy(), sel.cpu().numpy(), q_rep.cpu().numpy()
+    for h in range(H):
+        occ = np.nonzero(bid[h] >= 0)[0]
+        exact = orc.coarse_scores(qr[h].astype(np.float64), rep[h, occ].astype(np.float64),
+                                  shape.c().scale)
+        assert np.abs(sc[h][:, occ] - exact).max() < 1e-5
+        assert np.all(np.isneginf(sc[h][:, bid[h] < 0]))
+        win = [s for s in occ if s >= shape.capacity]
+        ids = bid[h, win]
+        for r in range(shape.nq):
+            got = [int(g) for g in sl[h, r] if g >= 0]
+            assert all(g == -1 for g in sl[h, r, len(got):])
+            ws = exact[r, [list(occ).index(s) for s in win]]
+            check_topk(got, ids, ws, topk)
+            if tie_all:
+                assert got == sorted(ids)[:topk]
+
+
+def test_memory_update_1047_candidates():
+    H, D, C, S, W = 2, 128, 1024, 2, 4
+    shape = ops.Shape(H, D, N_TOK, 1, W, C, S, 8)
+    rng = np.random.default_rng(1047)
+    chunk = 50                       # appending frame 50 pushes frame 46 out of the window
+    cache = ops.Cache(shape)
+    bid = _window_state(shape, f_last=chunk - 1, rng=rng, drop=0.0)
+    ln = np.where(bid >= 0, 64, 0).astype(np.int32)
+    kbits = rng.integers(0, 1 << 15, (H, shape.slots, 64, D), dtype=np.int16)
+    vbits = rng.integers(0, 1 << 15, (H, shape.slots, 64, D), dtype=np.int16)
+    rep = rng.standard_normal((H, shape.slots, D)).astype(np.float32)
+    cache.block_id.copy_(torch.from_numpy(bid))
+    cache.len.copy_(torch.from_numpy(ln))
+    cache.k.view(torch.int16).copy_(torch.from_numpy(kbits))
+    cache.v.view(torch.int16).copy_(torch.from_numpy(vbits))
+    cache.rep.copy_(torch.from_numpy(rep))
+    cache.chunk_index = chunk
+    scores = rng.standard_normal((H, shape.nq, shape.slots)).astype(np.float32)
+    kc = synth.round_bf16(rng.standard_normal((N_TOK, H, D)).astype(np.float32))
+    vc = synth.round_bf16(rng.standard_normal((N_TOK, H, D)).astype(np.float32))
+    ws = torch.empty(max(ops.pbsa_workspace_bytes(shape, ops.PBSA_OP_MEMORY_UPDATE), 16),
+                     dtype=torch.uint8, device="cuda")
+    say("[memory_update wide] C=1024")
+    ops.pbsa_memory_update(shape, torch.from_numpy(scores).cuda(), cache,
+                           torch.from_numpy(kc).cuda().to(torch.bfloat16),
+                           torch.from_numpy(vc).cuda().to(torch.bfloat16), None, ws)
+    torch.cuda.synchronize()
+    assert cache.chunk_index == chunk + 1
+    nb2 = cache.block_id.cpu().numpy()
+    k2 = cache.k.view(torch.int16).cpu().numpy()
+    leave = [C + ((chunk - W) % W) * NB + j for j in range(NB)]  # ring slots of frame 46
+    for h in range(H):
+        P = [int(g) for g in bid[h, :C] if g >= 0]
+        cols_P = [s for s in range(C) if bid[h, s] >= 0]
+        ev = [int(bid[h, s]) for s in leave]
+        cand, msum = orc.memory_scores(P, list(range(S)), scores[h][:, cols_P].astype(np.float64),
+                                       ev, scores[h][:, leave].astype(np.float64))
+        newP = sorted(int(g) for g in nb2[h, :C] if g >= 0)
+        assert newP[:S] == list(range(S))
+        check_topk(newP[S:], cand, msum, C - S)
+        # promoted blocks carry their K bytes from the window slot they left
+        slot_of = {int(g): s for s, g in enumerate(bid[h])}
+        for s in range(C):
+            g = int(nb2[h, s])
+            if g >= 0 and slot_of.get(g, -1) != s:
+                assert np.array_equal(k2[h, s], kbits[h, slot_of[g]])
+        # the chunk's blocks now sit in the freed window slots
+        for j, s in enumerate(leave):
+            assert nb2[h, s] == chunk * NB + j
+            ref = synth.bf16_bits(kc[64 * j:64 * j + 64, h]).view(np.int16)
+            assert np.array_equal(k2[h, s], ref)
+
+
+@pytest.mark.parametrize("topk", [300, 600])
+def test_attn_fwd_long_routed_lists(topk):
+    """Attention over P_t, top-300/600 routed window blocks and the chunk: the split of each
+    query-block pair's routed sets (shared / A only / B only) runs over several 256-id
+    rounds.  Sampled rows against the fp64 definition on the GPU's own routing."""
+    H, D, n = 1, 128, 1560          # 24 full blocks + a 24-row tail per frame
+    shape = ops.Shape(H, D, n, 1, 24, 64, 1, topk)
+    rng = np.random.default_rng(7000 + topk)
+    cache = ops.Cache(shape)
+    bid = _window_state(shape, f_last=60, rng=rng)
+    blen = np.where(bid >= 0, np.where(bid % NB == NB - 1, n - 64 * (NB - 1), 64), 0)
+    kc = synth.round_bf16(rng.standard_normal((H, shape.slots, 64, D)).astype(np.float32))
+    vc = synth.round_bf16(rng.standard_normal((H, shape.slots, 64, D)).astype(np.float32))
+    for h in range(H):
+        for s in range(shape.slots):
+            kc[h, s, blen[h, s]:] = 0
+            vc[h, s, blen[h, s]:] = 0
+    rep = np.stack([kc[h].mean(axis=1) for h in range(H)]).astype(np.float32)
+    cache.block_id.copy_(torch.from_numpy(bid))
+    cache.len.copy_(torch.from_numpy(blen.astype(np.int32)))
+    cache.k.copy_(torch.from_numpy(kc).to(torch.bfloat16))
+    cache.v.copy_(torch.from_numpy(vc).to(torch.bfloat16))
+    cache.rep.copy_(torch.from_numpy(rep))
+    cache.chunk_index = 61
+    q = synth.round_bf16(rng.standard_normal((n, H, D)).astype(np.float32))
+    k = synth.round_bf16(rng.standard_normal((n, H, D)).astype(np.float32))
+    v = synth.round_bf16(rng.standard_normal((n, H, D)).astype(np.float32))
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda().to(torch.bfloat16)
+    scores = torch.empty(H, shape.nq, shape.slots, dtype=torch.float32, device="cuda")
+    sel = torch.empty(H, shape.nq, topk, dtype=torch.int32, device="cuda")
+    o = torch.empty(n, H, D, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(H, n, dtype=torch.float32, device="cuda")
+    say(f"[attn long lists] K={topk}")
+    ops.pbsa_route(shape, dev(q), cache, None, scores, sel)
+    ops.pbsa_attn_fwd(shape, dev(q), cache, dev(k), dev(v), sel, o, lse)
+    torch.cuda.synchronize()
+    sl = sel.cpu().numpy()
+    og = o.float().cpu().numpy()
+    lg = lse.cpu().numpy()
+    scale = shape.c().scale
+    rows = sorted(set(rng.choice(n, 96, replace=False).tolist()) | {0, 63, 64, n - 1})
+    slot_of = {int(g): s for s, g in enumerate(bid[0])}
+    P = [s for s in range(shape.capacity) if bid[0, s] >= 0]
+    for t in rows:
+        r = t // 64
+        picked = [slot_of[int(g)] for g in sl[0, r] if g >= 0]
+        assert len(picked) == min(topk, int((bid[0, shape.capacity:] >= 0).sum()))
+        kk = [kc[0, s, :blen[0, s]] for s in P + picked] + [k[:, 0]]
+        vv = [vc[0, s, :blen[0, s]] for s in P + picked] + [v[:, 0]]
+        K = np.concatenate(kk).astype(np.float64)
+        V = np.concatenate(vv).astype(np.float64)
+        o_ref, lse_ref = orc.masked_attention(q[t:t + 1, 0].astype(np.float64), K, V,
+                                              np.ones((1, len(K)), bool), scale)
+        assert np.abs(og[t, 0] - o_ref[0]).max() < 2e-2
+        assert abs(lg[0, t] - lse_ref[0]) < 1e-3
