@@ -112,9 +112,10 @@ def check_slots(layer, ro, h, wl):
         assert np.abs(rep[s] - ro.krep[int(g)]).max() < 2e-6
 
 
-def rollout_parity(name, attn_rows=None, slot_check_every=1, dense_check=False):
-    wl = synth.WORKLOADS[name]
-    seed = synth.SEEDS[name]
+def rollout_parity(name, attn_rows=None, slot_check_every=1, dense_check=False, wl=None,
+                   seed=None):
+    wl = wl if wl is not None else synth.WORKLOADS[name]
+    seed = seed if seed is not None else synth.SEEDS[name]
     shape = shape_of(wl)
     sch = schedule_of(wl)
     H, C, K = wl.heads, wl.capacity, wl.topk
@@ -274,6 +275,21 @@ def test_memory_update_pooled_rep_matches_given_rep(head_dim):
         assert torch.equal(a.cache.v.view(torch.int16), b.cache.v.view(torch.int16))
         occ = a.cache.block_id >= 0
         assert (a.cache.rep[occ] - b.cache.rep[occ]).abs().max().item() < 1e-6
+
+
+# Degenerate shapes: no persistent memory at all (C = S = 0), a window no longer than the
+# chunk, frames shorter than one block, frames an exact multiple of the block, one head.
+EDGE = {
+    "no_memory": synth.Workload("no_memory", 2, 64, 64, 100, 2, 8, 2, 0, 0, 2),
+    "short_frames": synth.Workload("short_frames", 1, 128, 64, 40, 1, 6, 3, 2, 1, 1),
+    "exact_blocks": synth.Workload("exact_blocks", 2, 128, 64, 128, 2, 8, 4, 3, 1, 3),
+}
+
+
+@pytest.mark.parametrize("name", sorted(EDGE))
+def test_rollout_edge_shapes(name):
+    stats, _, _ = rollout_parity(name, wl=EDGE[name], seed=4242, dense_check=True)
+    say(f"[{name}] {stats}")
 
 
 def test_attn_fwd_d64_ragged_small():
