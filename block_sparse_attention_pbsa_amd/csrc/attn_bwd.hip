@@ -330,6 +330,10 @@ __global__ void __launch_bounds__(128, PBSA_DKDV_WPE) attn_bwd_dkdv_kernel(BwdAr
   __shared__ __attribute__((aligned(16))) uint16_t Qs[HT];
   __shared__ __attribute__((aligned(16))) uint16_t Os[HT];  // dO half tile
   __shared__ float lse2_s[32], d_s[32];
+  // this item's query blocks: first token and valid rows, staged once per item so that a
+  // step's fetch reads LDS instead of waiting on global memory
+  __shared__ int64_t qtok_s[kSplitQ];
+  __shared__ int qlen_s[kSplitQ];
   const int t = threadIdx.x;
   const int l = t & 63, h2 = l >> 5, c32 = l & 31;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -362,20 +366,28 @@ __global__ void __launch_bounds__(128, PBSA_DKDV_WPE) attn_bwd_dkdv_kernel(BwdAr
     const int q_hi = min(cnt, q_lo + kSplitQ);
     const int32_t* lst = a.inv + static_cast<int64_t>(hg) * a.nq;
     const int nsteps = 2 * (q_hi - q_lo);
+    for (int i = t; i < q_hi - q_lo; i += 128) {
+      const int rb = lst[q_lo + i];
+      qtok_s[i] = block_token0(rb, a.nb, a.n);
+      qlen_s[i] = block_len(rb % a.nb, a.n);
+    }
+    __syncthreads();
     const uint16_t* qh = a.q + h * a.qhs;
     const uint16_t* dh = a.dout + h * a.dhs;
     Tile<D, 128, 32> tq, td;
     Half hq, hd;
     float lse_r = INFINITY, d_r = 0.f;
     auto fetch = [&](int s) {
-      const int rb = __builtin_amdgcn_readfirstlane(lst[q_lo + (s >> 1)]);
       const int half = s & 1;
-      hq = half_of(qh, a.qts, rb, half, a.nb, a.n);
-      hd = half_of(dh, a.dts, rb, half, a.nb, a.n);
+      const int64_t qt0 = qtok_s[s >> 1] + 32 * half;
+      const int hl = qlen_s[s >> 1] - 32 * half;
+      const int hlen = __builtin_amdgcn_readfirstlane(hl < 0 ? 0 : (hl < 32 ? hl : 32));
+      hq = Half{qh + qt0 * a.qts, hlen};
+      hd = Half{dh + qt0 * a.dts, hlen};
       tq.load(hq.p, a.qts, hq.len, t);
       td.load(hd.p, a.dts, hd.len, t);
       if (t < 32) {
-        const int64_t q0 = block_token0(rb, a.nb, a.n) + 32 * half;
+        const int64_t q0 = qt0;
         // rows past the query block's length get lse = +inf, so their P is 0
         lse_r = t < hq.len ? a.lse[h * a.T + q0 + t] * kLog2e : INFINITY;
         d_r = t < hq.len ? a.Dw[h * a.T + q0 + t] : 0.f;
