@@ -150,6 +150,15 @@ def main():
     attn_avg = timed(lambda: layer.attend(q, k, v), args.steps)
     achieved = flop / (attn_avg * 1e-3) / 1e12
 
+    # the memory update, timed on a copy of the cache (each call appends the chunk again)
+    import copy
+    cache2 = copy.copy(layer.cache)
+    for name_ in ("k", "v", "rep", "block_id", "len"):
+        setattr(cache2, name_, getattr(layer.cache, name_).clone())
+    upd_ms = timed(lambda: ops.pbsa_memory_update(shape, layer.scores, cache2, k, v, None,
+                                                  layer.workspace), 20)
+    del cache2
+
     ops_ms = {
         "route": timed(lambda: ops.pbsa_route(shape, q, layer.cache, layer.q_rep, layer.scores,
                                               layer.sel), 20),
@@ -157,6 +166,7 @@ def main():
         "score_topk": timed(lambda: ops.pbsa_score_topk(shape, layer.q_rep, layer.cache,
                                                         layer.scores, layer.sel), 20),
         "attn_fwd": attn_avg,
+        "memory_update": upd_ms,
     }
     pool_bytes = shape.chunk_tokens * wl.heads * wl.head_dim * 2 + shape.nq * wl.heads * wl.head_dim * 4
 
@@ -193,6 +203,9 @@ def main():
         "attn_fwd_flop": int(flop),
         "attn_fwd_ms": round(attn_avg, 4),
         "ops_ms_mean": {k_: round(v_, 4) for k_, v_ in ops_ms.items()},
+        # derived, not measured as one run: T = 4 denoising passes per chunk (route + attention
+        # each) sharing the memory, then one update
+        "derived_ms_per_chunk_T4": round(4 * (ops_ms["route"] + attn_avg) + upd_ms, 4),
         "pool_q_gbs": round(pool_bytes / (ops_ms["pool_q"] * 1e-3) / 1e9, 1),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
@@ -316,7 +329,10 @@ def bench_probes(torch, ops, synth, shape, layer, q, k, v, stream):
     sel = layer.sel.cpu().numpy()
     C, nq = shape.capacity, shape.nq
     steps = 0
+    unique_slots = 0  # distinct cache slots the launch reads (P, and routed window blocks)
     for h in range(shape.heads):
+        routed = {int(g) for g in sel[h].ravel() if g >= 0}
+        unique_slots += int((bid[h, :C] >= 0).sum()) + len(routed)
         for pr in range((nq + 1) // 2):
             # blocks routed by both query blocks of the pair join the shared steps
             sa = {int(g) for g in sel[h, 2 * pr] if g >= 0}
@@ -331,10 +347,15 @@ def bench_probes(torch, ops, synth, shape, layer, q, k, v, stream):
     torch.cuda.synchronize()
     warm, _, _ = _timed_reps(torch, stream, g, 10)
     cold, c10, c90 = _timed_reps(torch, stream, g, 10, flush)
-    out["gather"] = {"bytes_moved_to_lds": gbytes, "ms_warm": round(warm, 4),
+    # unique KV bytes: each distinct slot's K and V (64 rows) plus the chunk's own K and V
+    ubytes = unique_slots * 2 * 64 * shape.head_dim * 2 + \
+        2 * shape.chunk_tokens * shape.heads * shape.head_dim * 2
+    out["gather"] = {"bytes_moved_to_lds": gbytes, "unique_kv_bytes": ubytes,
+                     "ms_warm": round(warm, 4),
                      "ms_cold": round(cold, 4), "ms_cold_p10_p90": [round(c10, 4), round(c90, 4)],
                      "gbs_warm": round(gbytes / (warm * 1e-3) / 1e9, 1),
-                     "gbs_cold": round(gbytes / (cold * 1e-3) / 1e9, 1)}
+                     "gbs_cold": round(gbytes / (cold * 1e-3) / 1e9, 1),
+                     "unique_gbs_cold": round(ubytes / (cold * 1e-3) / 1e9, 1)}
     # full-history pooling at the 1-minute workload's size (seeded synthetic tokens)
     wl = synth.WORKLOADS["wan_1min"]
     frames = wl.history_frames
@@ -358,7 +379,35 @@ def bench_probes(torch, ops, synth, shape, layer, q, k, v, stream):
         "ms_cold_p10_p90": [round(c10, 4), round(c90, 4)],
         "gbs_warm": round(pb / (warm * 1e-3) / 1e9, 1), "gbs_cold": round(pb / (cold * 1e-3) / 1e9, 1),
         "frac_hbm_cold": round(pb / (cold * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
-    del x, brep, frep, flush_buf
+    del x, brep, frep
+    # the training clip's queries and keys (block and frame representatives of each)
+    wl = synth.WORKLOADS["wan_train"]
+    frames = wl.clip_chunks * wl.chunk_frames
+    T = frames * wl.frame_tokens
+    gen.manual_seed(synth.SEEDS["wan_train"])
+    xs = [torch.randn((T, wl.heads, wl.head_dim), generator=gen, device="cuda",
+                      dtype=torch.float32).to(torch.bfloat16) for _ in range(2)]
+    pshape = ops.Shape(wl.heads, wl.head_dim, wl.frame_tokens, frames, scale=wl.scale)
+    reps = [(torch.empty((wl.heads, frames * wl.nb, wl.head_dim), dtype=torch.float32,
+                         device="cuda"),
+             torch.empty((wl.heads, frames, wl.head_dim), dtype=torch.float32, device="cuda"))
+            for _ in range(2)]
+
+    def pc():
+        for x_, (b_, f_) in zip(xs, reps):
+            ops.pbsa_pool(pshape, x_, frames, b_, f_)
+    pc()
+    torch.cuda.synchronize()
+    warm, _, _ = _timed_reps(torch, stream, pc, 10)
+    cold, c10, c90 = _timed_reps(torch, stream, pc, 10, flush)
+    pb = sum(x_.numel() * 2 for x_ in xs) + sum(b_.numel() * 4 + f_.numel() * 4 for b_, f_ in reps)
+    out["pool_train_clip"] = {
+        "workload": "wan_train clip q and k: 24 frames x 1560 tokens, 12 heads, d=128 (2 launches)",
+        "bytes": pb, "ms_warm": round(warm, 4), "ms_cold": round(cold, 4),
+        "ms_cold_p10_p90": [round(c10, 4), round(c90, 4)],
+        "gbs_cold": round(pb / (cold * 1e-3) / 1e9, 1),
+        "frac_hbm_cold": round(pb / (cold * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    del xs, reps, flush_buf
     torch.cuda.empty_cache()
     return out
 
@@ -433,10 +482,18 @@ def cpu_baseline(wl, seed):
     ro.attend(qh, kh, vh, rt["sel"])
     ro.update(rt, kh, vh)
     sec = time.perf_counter() - t
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")),
+                         model)
+    except OSError:
+        pass
     return {"value": round(sec * 1e3 * wl.heads, 1), "unit": "ms/chunk", "cores": threads,
             "kind": "oracle",
             "sample": "one head of the wan_5s measured chunk (pool, score, route, gathered "
-                      "fp64 attention over all 4680 queries, Top-C update), scaled x12 heads"}
+                      "fp64 attention over all 4680 queries, Top-C update), scaled x12 heads; "
+                      f"{os.cpu_count()} logical CPUs ({model})"}
 
 
 if __name__ == "__main__":

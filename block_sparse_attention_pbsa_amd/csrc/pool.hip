@@ -11,7 +11,9 @@
 
 namespace pbsa {
 
-// grid (ceil(frames*nb / 4), H), 256 threads: wave w pools global block 4*blockIdx.x + w.
+// 1-D grid of ceil(frames*nb / 4) * H workgroups, head fastest (neighbouring workgroups
+// read the same token rows' other heads, so the rows in flight are read whole), 256
+// threads: wave w pools global block 4*(blockIdx.x / H) + w of head blockIdx.x % H.
 // Lane l owns channels [8*(l % CH), +8) of rows l / CH, l / CH + RPI, ... (CH = D / 8
 // chunks per row, RPI = 64 / CH rows per pass).
 template <int D>
@@ -20,8 +22,9 @@ __global__ void __launch_bounds__(256) pool_blocks_kernel(TokIn x, int n, int nb
   constexpr int CH = D / 8;
   constexpr int RPI = 64 / CH;
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-  const int g = blockIdx.x * 4 + w;
-  const int h = blockIdx.y;
+  const int H = static_cast<int>(gridDim.x) / ((nblocks + 3) / 4);
+  const int g = (static_cast<int>(blockIdx.x) / H) * 4 + w;
+  const int h = static_cast<int>(blockIdx.x) % H;
   if (g >= nblocks) return;
   const int f = g / nb, j = g - f * nb;
   const int len = block_len(j, n);
@@ -67,7 +70,16 @@ __global__ void pool_frames_kernel(const float* __restrict__ block_rep, int n, i
   const int nblocks = frames * nb;
   const float* s = block_rep + (static_cast<int64_t>(h) * nblocks + f * nb) * D + c;
   float acc = 0.f;
-  for (int j = 0; j < nb; ++j) acc += s[j * D] * static_cast<float>(block_len(j, n));
+  int j = 0;
+  // eight block means loaded before they are added (the order of the additions is kept)
+  for (; j + 8 <= nb; j += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = s[(j + u) * D];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += v[u] * static_cast<float>(block_len(j + u, n));
+  }
+  for (; j < nb; ++j) acc += s[j * D] * static_cast<float>(block_len(j, n));
   frame_rep[(static_cast<int64_t>(h) * frames + f) * D + c] = acc / static_cast<float>(n);
 }
 
@@ -76,7 +88,7 @@ hipError_t launch_pool(const pbsa_dims& d, TokIn x, int frames, float* block_rep
   const int nb = nb_of(d);
   const int nblocks = frames * nb;
   if (nblocks == 0) return hipSuccess;
-  dim3 grid(cdiv(nblocks, 4), d.heads);
+  dim3 grid(cdiv(nblocks, 4) * d.heads);
   if (d.head_dim == 128)
     hipLaunchKernelGGL(pool_blocks_kernel<128>, grid, dim3(256), 0, s, x, d.frame_tokens, nb,
                        nblocks, block_rep);
