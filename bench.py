@@ -299,12 +299,15 @@ def bench_probes(torch, ops, synth, shape, layer, q, k, v, stream):
                step moves 32 KB per workgroup) / time, warm and cold;
       pool_full_history - pbsa_pool over the 1-minute workload's whole history
                (240 frames x 1560 tokens x 12 heads x 128, 1.15 GB read), warm and cold.
-    Cold runs first write a 512 MiB buffer (larger than the 256 MB last-level cache)."""
+    Cold runs first read a 512 MiB buffer (larger than the 256 MB last-level cache)."""
     out = {}
-    flush_buf = torch.empty(256 * 1024 * 1024, dtype=torch.bfloat16, device="cuda")
+    flush_buf = torch.ones(256 * 1024 * 1024, dtype=torch.bfloat16, device="cuda")
+    flush_sink = torch.empty((), dtype=torch.bfloat16, device="cuda")
 
     def flush():
-        flush_buf.fill_(1.0)
+        # a 512 MiB read (not a write: dirty lines would be written back during the timed
+        # launch and charged to it)
+        flush_sink.copy_(flush_buf.sum())
 
     # MFMA ceiling
     mf = torch.empty(131072, dtype=torch.float32, device="cuda")
