@@ -32,13 +32,6 @@ struct MemArgs {
   int64_t chunk;        // chunk index being appended
 };
 
-namespace {
-__device__ __forceinline__ bool ahead(float sa, int ia, float sb, int ib) {
-  return sa > sb || (sa == sb && ia < ib);
-}
-__device__ __forceinline__ float order_key(float x) { return x != x ? -INFINITY : x; }
-}  // namespace
-
 // grid H, 1024 threads per head (256 when the candidate count needs more sort registers).  Candidates are listed in a fixed order (persistent
 // non-sink slots ascending, then the leaving blocks in chunk-block order, which is
 // ascending id); their memory scores are column sums of the chunk's score matrix, computed

@@ -11,40 +11,14 @@
 // Latency-bound (~1e8 FLOP per chunk): scores are fp32 FMA dot products on the vector ALUs,
 // which keeps them within ~1e-7 of the exact value, so selections agree with an exact
 // reference wherever score gaps are larger.  Candidates are 64-bit (score, ~id) keys, so
-// that ties go to the lower id; NaN scores order as -inf.  The persistent mode's top-K is
-// an exact radix select over the keys held by one wave (one ballot per bit), the
-// two-level mode's an in-register bitonic sort.
+// that ties go to the lower id; NaN scores order as -inf.  Every top-K is an exact radix
+// select over the keys held by one wave (one ballot per bit).
 #include "common.h"
 #include "launch.h"
 #include "select.h"
 
 namespace pbsa {
 
-namespace {
-
-__device__ __forceinline__ float order_key(float x) {  // NaN -> -inf
-  return x != x ? -INFINITY : x;
-}
-__device__ __forceinline__ bool ahead(float sa, int ia, float sb, int ib) {
-  return sa > sb || (sa == sb && ia < ib);
-}
-
-template <int D>
-__device__ __forceinline__ float dot_rep(const float* __restrict__ q_lds,
-                                         const float* __restrict__ rep) {
-  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-#pragma unroll 8
-  for (int c = 0; c < D; c += 4) {
-    f32x4 r = *reinterpret_cast<const f32x4*>(rep + c);
-    a0 = fmaf(q_lds[c], r[0], a0);
-    a1 = fmaf(q_lds[c + 1], r[1], a1);
-    a2 = fmaf(q_lds[c + 2], r[2], a2);
-    a3 = fmaf(q_lds[c + 3], r[3], a3);
-  }
-  return (a0 + a1) + (a2 + a3);
-}
-
-}  // namespace
 
 // Row-parallel scores of QB query blocks against `cnt` representative rows.  Groups of
 // LPR = D/8 lanes read one row with 16-byte loads (whole rows per instruction), multiply
@@ -269,87 +243,136 @@ struct ChunkBudgets {
   int32_t k[kMaxChunks];
 };
 
-// grid (Nq_total, H), one wave per query block.  Frame stage: lane l scores history frames
-// l + 64e; a bitonic sort picks the top_frames; chosen and forced frames are flagged in LDS.
-// Block stage: candidates (every block of the flagged frames, ascending) are scored into
-// sort keys, sorted, the first k kept and re-sorted by id.
+// scale * <q_rep row, rep row> for rows [0, cnt) (row_ptr(i): row i's D floats) into
+// out[i], by the 256 threads of a workgroup: groups of D/8 lanes take one row each (whole
+// rows per load instruction), U row groups loaded before any is used.  qv: this lane's 8
+// channels of the query representative.
+template <int D, int U, class RowPtr>
+__device__ __forceinline__ void rows_dot(const float (&qv)[8], int cnt, RowPtr row_ptr,
+                                         float scale, float* out, int t) {
+  constexpr int LPR = D / 8, RPI = 64 / LPR, STEP = 4 * RPI;
+  const int w = t >> 6, l = t & 63, sub = l % LPR, g = l / LPR;
+  for (int r0 = w * RPI; r0 < cnt; r0 += U * STEP) {
+    f32x4 a[U], b[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int row = r0 + u * STEP + g;
+      const float* p = row_ptr(row < cnt ? row : 0) + 8 * sub;
+      a[u] = *reinterpret_cast<const f32x4*>(p);
+      b[u] = *reinterpret_cast<const f32x4*>(p + 4);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float acc = qv[0] * a[u][0] + qv[1] * a[u][1] + qv[2] * a[u][2] + qv[3] * a[u][3] +
+                  qv[4] * b[u][0] + qv[5] * b[u][1] + qv[6] * b[u][2] + qv[7] * b[u][3];
+#pragma unroll
+      for (int o = 1; o < LPR; o <<= 1) acc += __shfl_xor(acc, o, 64);
+      const int row = r0 + u * STEP + g;
+      if (row < cnt && sub == 0) out[row] = scale * acc;
+    }
+  }
+}
+
+// grid (Nq_total, H), 256 threads per query block.  Frame stage: the history frames' scores
+// (rows_dot), then wave 0 selects the top_frames by radix select; chosen and forced frames
+// are flagged in LDS and listed in ascending order.  Block stage: every block of the listed
+// frames is a candidate (ascending ids); their scores (rows_dot), then wave 0 selects the
+// top k and writes them in candidate order, which is ascending.  Dynamic LDS: frame scores,
+// flags and list ([frames_total] each), candidate scores [64 E].
 template <int D, int EF, int E>
-__global__ void __launch_bounds__(64)
+__global__ void __launch_bounds__(256)
     score_topk_2lvl_kernel(const float* __restrict__ q_rep, const float* __restrict__ block_rep,
                            const float* __restrict__ frame_rep, int F, int nb, int chunks,
                            int top_frames, ChunkBudgets budgets, float scale, int max_sel,
                            int32_t* __restrict__ sel, int32_t* __restrict__ nsel_out) {
-  extern __shared__ int fflag[];  // [chunks * F]: frame chosen?  then the chosen list
-  __shared__ float q_lds[D];
-  const int r = blockIdx.x, h = blockIdx.y, l = threadIdx.x;
+  extern __shared__ float sel_lds[];
+  __shared__ int s_nfr;
+  const int r = blockIdx.x, h = blockIdx.y, t = threadIdx.x, w = t >> 6, l = t & 63;
   const int nq = chunks * F * nb;
   const int frames_total = chunks * F;
+  float* fsc = sel_lds;                                          // [frames_total]
+  int* fflag = reinterpret_cast<int*>(fsc + frames_total);       // [frames_total]
+  int* flist = fflag + frames_total;                             // [frames_total]
+  float* bsc = reinterpret_cast<float*>(flist + frames_total);   // [64 E]
   const int i = r / (F * nb) + 1;  // 1-based chunk of this query block
   int32_t* out = sel + (static_cast<int64_t>(h) * nq + r) * max_sel;
   if (i == 1) {
-    for (int g = l; g < F * nb; g += 64) out[g] = g;
-    if (l == 0) nsel_out[static_cast<int64_t>(h) * nq + r] = F * nb;
+    for (int g = t; g < F * nb; g += 256) out[g] = g;
+    if (t == 0) nsel_out[static_cast<int64_t>(h) * nq + r] = F * nb;
     return;
   }
-  const float* qr = q_rep + (static_cast<int64_t>(h) * nq + r) * D;
-  for (int c = l; c < D; c += 64) q_lds[c] = qr[c];
+  constexpr int LPR = D / 8;
+  float qv[8];
+  {
+    const float* qr = q_rep + (static_cast<int64_t>(h) * nq + r) * D + 8 * (l % LPR);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qv[e] = qr[e];
+  }
   const int hist = F * (i - 1);
   const int vis = hist + F;  // frames this chunk can see
-  int* flist = fflag + frames_total;
   // forced: sink frame, latest history frame, the chunk's own frames
-  for (int f = l; f < vis; f += 64) fflag[f] = (f == 0 || f >= hist - 1);
-  __syncthreads();
+  for (int f = t; f < vis; f += 256) fflag[f] = (f == 0 || f >= hist - 1);
   const float* fr = frame_rep + static_cast<int64_t>(h) * frames_total * D;
-  uint64_t fk[EF];
-#pragma unroll
-  for (int e = 0; e < EF; ++e) {
-    const int f = l + 64 * e;
-    fk[e] = f < hist ? rank_key(scale * dot_rep<D>(q_lds, fr + static_cast<int64_t>(f) * D), f) : 0;
-  }
-  wave_sort_desc<EF>(fk, l);
+  rows_dot<D, 4>(qv, hist, [&](int f) { return fr + static_cast<int64_t>(f) * D; }, scale, fsc, t);
+  __syncthreads();
   const int ntop = top_frames < hist ? top_frames : hist;
+  if (w == 0 && ntop > 0) {
+    uint64_t fk[EF];
 #pragma unroll
-  for (int e = 0; e < EF; ++e)
-    if (64 * e + l < ntop) fflag[rank_key_id(fk[e])] = 1;
-  __syncthreads();
-  // chosen frames in ascending order (ballot compaction over the visible frames)
-  int nfr = 0;
-  for (int f0 = 0; f0 < vis; f0 += 64) {
-    const int f = f0 + l;
-    const bool on = f < vis && fflag[f];
-    const unsigned long long m = __ballot(on);
-    if (on) flist[nfr + __popcll(m & ((1ull << l) - 1ull))] = f;
-    nfr += __popcll(m);
-  }
-  __syncthreads();
-  const int ncand = nfr * nb;
-  const float* br = block_rep + static_cast<int64_t>(h) * nq * D;
-  uint64_t key[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int c = l + 64 * e;
-    key[e] = 0;
-    if (c < ncand) {
-      const int g = flist[c / nb] * nb + (c % nb);
-      key[e] = rank_key(scale * dot_rep<D>(q_lds, br + static_cast<int64_t>(g) * D), g);
+    for (int e = 0; e < EF; ++e) {
+      const int f = l + 64 * e;
+      fk[e] = f < hist ? rank_key(fsc[f], f) : 0;
     }
-  }
-  int k = budgets.k[i - 1];
-  if (k > ncand) k = ncand;
-  if (k < 1) k = 1;
-  wave_sort_desc<E>(key, l);
+    bool on[EF];
+    wave_topk<EF>(fk, ntop, on);
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int idx = 64 * e + l;
-    key[e] = idx < k ? static_cast<uint64_t>(~static_cast<uint32_t>(rank_key_id(key[e]))) : 0;
+    for (int e = 0; e < EF; ++e)
+      if (on[e]) fflag[l + 64 * e] = 1;
   }
-  wave_sort_desc<E>(key, l);
+  __syncthreads();
+  if (w == 0) {
+    // chosen frames in ascending order (ballot compaction over the visible frames)
+    int nfr = 0;
+    for (int f0 = 0; f0 < vis; f0 += 64) {
+      const int f = f0 + l;
+      const bool on = f < vis && fflag[f];
+      const unsigned long long m = __ballot(on);
+      if (on) flist[nfr + __popcll(m & ((1ull << l) - 1ull))] = f;
+      nfr += __popcll(m);
+    }
+    if (l == 0) s_nfr = nfr;
+  }
+  __syncthreads();
+  const int ncand = s_nfr * nb;
+  const float* br = block_rep + static_cast<int64_t>(h) * nq * D;
+  auto cand_id = [&](int c) { return flist[c / nb] * nb + (c % nb); };
+  rows_dot<D, 8>(qv, ncand, [&](int c) { return br + static_cast<int64_t>(cand_id(c)) * D; },
+                 scale, bsc, t);
+  __syncthreads();
+  if (w == 0) {
+    uint64_t key[E];
+    int gid[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int idx = 64 * e + l;
-    if (idx < k) out[idx] = static_cast<int>(~static_cast<uint32_t>(key[e]));
+    for (int e = 0; e < E; ++e) {
+      const int c = l + 64 * e;
+      gid[e] = c < ncand ? cand_id(c) : -1;
+      key[e] = c < ncand ? rank_key(bsc[c], gid[e]) : 0;
+    }
+    int k = budgets.k[i - 1];
+    if (k > ncand) k = ncand;
+    if (k < 1) k = 1;
+    bool on[E];
+    wave_topk<E>(key, k, on);
+    int base = 0;
+    const unsigned long long below = (1ull << l) - 1ull;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const unsigned long long m = __ballot(on[e]);
+      if (on[e]) out[base + __popcll(m & below)] = gid[e];
+      base += __popcll(m);
+    }
+    if (l == 0) nsel_out[static_cast<int64_t>(h) * nq + r] = k;
   }
-  if (l == 0) nsel_out[static_cast<int64_t>(h) * nq + r] = k;
 }
 
 template <int D, int EF>
@@ -358,7 +381,7 @@ static hipError_t launch_2lvl_e(int E, dim3 grid, size_t lds, hipStream_t s, con
                                 int chunks, int top_frames, const ChunkBudgets& b, float scale,
                                 int max_sel, int32_t* sel, int32_t* nsel) {
 #define PBSA_2LVL_E(EE)                                                                      \
-  hipLaunchKernelGGL((score_topk_2lvl_kernel<D, EF, EE>), grid, dim3(64), lds, s, q_rep,       \
+  hipLaunchKernelGGL((score_topk_2lvl_kernel<D, EF, EE>), grid, dim3(256), lds, s, q_rep,      \
                      block_rep, frame_rep, F, nb, chunks, top_frames, b, scale, max_sel, sel, \
                      nsel)
   if (E <= 1) PBSA_2LVL_E(1);
@@ -385,7 +408,7 @@ static hipError_t launch_2lvl_d(const pbsa_dims& d, int chunks, int top_frames,
   const int ncand = fr_max * nb;
   const int E = (ncand + 63) / 64;
   const int EF = (frames_total + 63) / 64;
-  const size_t lds = static_cast<size_t>(2 * frames_total) * sizeof(int);
+  const size_t lds = static_cast<size_t>(3 * frames_total + 64 * E) * sizeof(int);
   dim3 grid(nq, d.heads);
   if (EF <= 1)
     return launch_2lvl_e<D, 1>(E, grid, lds, s, q_rep, block_rep, frame_rep, F, nb, chunks,
