@@ -325,6 +325,8 @@ pbsa_status pbsa_attn_bwd(const pbsa_dims* dims, int32_t chunks, pbsa_tensor q, 
   PBSA_TRY(check_tok(dv, "dv", dims->head_dim));
   if (!lse || !sel || !nsel) return fail(PBSA_ERR_NULL, "lse, sel and nsel are required");
   if (max_sel < 1) return fail(PBSA_ERR_SHAPE, "max_sel must be >= 1");
+  if (max_sel > pbsa::kAttnListCap / 2)
+    return fail(PBSA_ERR_UNSUPPORTED, "max_sel must be <= %d", pbsa::kAttnListCap / 2);
   const size_t need = pbsa::attn_bwd_workspace(*dims, chunks, max_sel);
   if (!workspace || workspace_bytes < need)
     return fail(PBSA_ERR_WORKSPACE, "attn_bwd needs %zu workspace bytes (got %zu)", need,

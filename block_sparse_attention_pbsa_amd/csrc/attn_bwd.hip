@@ -64,11 +64,6 @@ struct Half {
   int len;  // valid rows (0 = none)
 };
 
-__device__ __forceinline__ Half half_of(const uint16_t* base, int64_t ts, int g, int half, int nb,
-                                        int n) {
-  const int len = block_len(g % nb, n) - 32 * half;
-  return Half{base + (block_token0(g, nb, n) + 32 * half) * ts, len < 0 ? 0 : (len < 32 ? len : 32)};
-}
 
 }  // namespace
 
@@ -83,6 +78,8 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t VsX[HT];
   __shared__ __attribute__((aligned(16))) uint16_t KsY[HT];
   __shared__ __attribute__((aligned(16))) uint16_t VsY[HT];
+  // A's and B's selected blocks as (first token | valid rows << 24), staged once
+  __shared__ uint32_t lstA[kAttnListCap / 2], lstB[kAttnListCap / 2];
 
   const int per = gridDim.x / 8;
   const int L = static_cast<int>(blockIdx.x % 8) * per + static_cast<int>(blockIdx.x / 8);
@@ -130,21 +127,29 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
   const int nsteps = 2 * (cntA > cntB ? cntA : cntB);
   const uint16_t* kh = a.k + h * a.khs;
   const uint16_t* vh = a.v + h * a.vhs;
+  auto entry = [&](int g) {
+    return static_cast<uint32_t>(block_token0(g, a.nb, a.n)) |
+           (static_cast<uint32_t>(block_len(g % a.nb, a.n)) << 24);
+  };
+  for (int j = t; j < (cntA > cntB ? cntA : cntB); j += 256) {
+    if (j < cntA) lstA[j] = entry(selA[j]);
+    if (j < cntB) lstB[j] = entry(selB[j]);
+  }
+  __syncthreads();
 
   // step s: half (s & 1) of A's and B's (s >> 1)-th selected block
+  auto half_ref = [&](uint32_t e_, int half, Half& k_, Half& v_) {
+    const uint32_t e = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(e_)));
+    const int64_t tk = (e & 0xffffffu) + 32 * half;
+    const int len = static_cast<int>(e >> 24) - 32 * half;
+    k_ = Half{kh + tk * a.kts, len < 0 ? 0 : (len < 32 ? len : 32)};
+    v_ = Half{vh + tk * a.vts, k_.len};
+  };
   auto refs = [&](int s, Half& kx, Half& vx, Half& ky, Half& vy) {
     const int j = s >> 1, half = s & 1;
     kx.len = vx.len = ky.len = vy.len = 0;
-    if (j < cntA) {
-      const int g = __builtin_amdgcn_readfirstlane(selA[j]);
-      kx = half_of(kh, a.kts, g, half, a.nb, a.n);
-      vx = half_of(vh, a.vts, g, half, a.nb, a.n);
-    }
-    if (j < cntB) {
-      const int g = __builtin_amdgcn_readfirstlane(selB[j]);
-      ky = half_of(kh, a.kts, g, half, a.nb, a.n);
-      vy = half_of(vh, a.vts, g, half, a.nb, a.n);
-    }
+    if (j < cntA) half_ref(lstA[j], half, kx, vx);
+    if (j < cntB) half_ref(lstB[j], half, ky, vy);
   };
 
   Tile<D, 256, 32> tkx, tvx, tky, tvy;

@@ -31,7 +31,8 @@
  *    of 8 elements and token pointers 16-byte aligned.  Size limits (PBSA_ERR_UNSUPPORTED
  *    beyond them): persistent mode: capacity + window blocks <= 4096, capacity - sinks
  *    <= 1024, window blocks <= 1024, topk <= 1024 and, for pbsa_attn_fwd, capacity +
- *    chunk blocks + 2*topk <= 3072; two-level mode: pbsa_attn_fwd_2lvl max_sel <= 1536;
+ *    chunk blocks + 2*topk <= 3072; two-level mode: pbsa_attn_fwd_2lvl and pbsa_attn_bwd
+ *    max_sel <= 1536;
  *    a head's K/V token rows span at most 2 GiB and 2^24 tokens.
  */
 #ifndef PBSA_H_

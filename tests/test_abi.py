@@ -142,6 +142,10 @@ def test_calls_reject_bad_arguments_before_launching():
     t = _tensor(16)
     assert L.pbsa_attn_bwd(d, 8, t, t, t, t, ctypes.c_void_p(16), t, ctypes.c_void_p(16),
                            ctypes.c_void_p(16), 75, t, t, t, None, 0, None) == 5
+    # backward: max_sel above 1536
+    assert L.pbsa_attn_bwd(d, 8, t, t, t, t, ctypes.c_void_p(16), t, ctypes.c_void_p(16),
+                           ctypes.c_void_p(16), 1537, t, t, t, None, 0, None) == 3
+    assert b"1536" in L.pbsa_last_error()
 
 
 def test_python_binding_rejects_host_tensors():
