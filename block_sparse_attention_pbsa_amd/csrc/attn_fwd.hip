@@ -4,7 +4,8 @@
 // persistent blocks and to its query block's top-K window blocks (plus, here, the current
 // chunk); with the selection fixed this is softmax attention restricted by a block mask,
 // computed block by block with a running max and sum (flash-style).  The trainable
-// two-level mode attends to a per-query-block list over the whole clip instead.
+// two-level mode attends to a per-query-block list over the whole clip instead (there the
+// shared blocks below are only those both query blocks selected).
 //
 // gfx950 design.  One workgroup = two 64-token query blocks of one head (A and B), four
 // waves of 32 query rows.  The KV blocks every query block of the head attends (the
@@ -498,16 +499,18 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
   };
   const int32_t* sa = a.sel + (static_cast<int64_t>(h) * a.nq + rA) * a.sel_stride;
   const int32_t* sb = a.sel + (static_cast<int64_t>(h) * a.nq + rB) * a.sel_stride;
-  if (PERSIST) {
+  {
     // Split A's and B's routed sets into A only, B only and both.  The ascending ids are
     // staged in two K tiles (no gather has targeted them yet) and looked up by binary
     // search; each part is compacted in id order with ballots, so the lists (and the
     // summation order) do not depend on timing.
     int32_t* rawA = reinterpret_cast<int32_t*>(&kb0[0][0]);
     int32_t* rawB = reinterpret_cast<int32_t*>(&kb1[0][0]);
-    const int nbb = rB >= a.nq ? 0 : a.sel_stride;
+    const int na = PERSIST ? a.sel_stride : a.nsel[static_cast<int64_t>(h) * a.nq + rA];
+    const int nbb = rB >= a.nq ? 0 : PERSIST ? a.sel_stride
+                                             : a.nsel[static_cast<int64_t>(h) * a.nq + rB];
     for (int j = t; j < a.sel_stride; j += 256) {
-      rawA[j] = sa[j];
+      rawA[j] = j < na ? sa[j] : -1;
       rawB[j] = j < nbb ? sb[j] : -1;
     }
     __syncthreads();
@@ -567,27 +570,6 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
     cntA = __builtin_amdgcn_readfirstlane(oa);
     cntB = __builtin_amdgcn_readfirstlane(ob);
     nboth = __builtin_amdgcn_readfirstlane(oi);
-  } else {
-    const int na = a.nsel[static_cast<int64_t>(h) * a.nq + rA];
-    const int nbb = rB >= a.nq ? 0 : a.nsel[static_cast<int64_t>(h) * a.nq + rB];
-    for (int j = t; j < a.sel_stride; j += 256) {
-      const int ga = j < na ? sa[j] : -1;
-      const int gb = j < nbb ? sb[j] : -1;
-      listA[j] = ga >= 0 ? entry(ga) : 0u;
-      listB[j] = gb >= 0 ? entry(gb) : 0u;
-    }
-    int ca = 0, cb = 0;
-    for (int j = l; j < a.sel_stride; j += 64) {
-      ca += (j < na) && sa[j] >= 0;
-      cb += (j < nbb) && sb[j] >= 0;
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      ca += __shfl_xor(ca, o, 64);
-      cb += __shfl_xor(cb, o, 64);
-    }
-    cntA = __builtin_amdgcn_readfirstlane(ca);
-    cntB = __builtin_amdgcn_readfirstlane(cb);
   }
   const int nPq = nshared;  // P and chunk entries (persistent mode)
   nshared += nboth;
