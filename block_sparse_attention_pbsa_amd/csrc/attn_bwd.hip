@@ -17,7 +17,9 @@
 //   plan      -- one workgroup: cuts every inverse list into work items of at most
 //                kSplitQ query blocks (a few KV blocks are selected by every query block,
 //                most by a few dozen), numbering items and partial-sum slots by prefix sums.
-//   dkdv pass -- work items in a grid-stride loop, two waves of 32 keys each; the KV block
+//   dkdv pass -- work items taken largest first from a counter (the plan pass orders them
+//                by size; each item writes only its own outputs, so results do not depend on
+//                which workgroup takes it), two waves of 32 keys each; the KV block
 //                stays in LDS; an item walks its part of the list in 32-query half tiles:
 //                S = Q K^T and dP = dO V^T with keys as MFMA columns, then dV^T += dO^T P
 //                and dK^T += Q^T dS (dO, Q read channel-major with the transposing read).
@@ -48,6 +50,7 @@ struct BwdArgs {
   int32_t* inv_cnt;     // workspace [H][nq]
   int32_t* inv;         // workspace [H][nq][nq]
   int2* items;          // workspace: work item -> (h*nq + g, split)
+  int2* sorted;         // workspace: the same items by decreasing number of query blocks
   int32_t* nsplit;      // workspace [H*nq]
   int32_t* part_base;   // workspace [H*nq]: first partial slot of a split block
   int32_t* long_list;   // workspace: split blocks
@@ -321,10 +324,46 @@ __global__ void __launch_bounds__(1024) attn_bwd_plan_kernel(BwdArgs a) {
     a.counts[0] = sc[0][1023];
     a.counts[1] = sc[2][1023];
   }
+  // The same items by decreasing size (query blocks, at most kSplitQ) for the dK/dV pass,
+  // which takes them largest first from a counter (cleared here): a counting sort.  Items of
+  // equal size may land in any order; each item writes only its own outputs, so the
+  // results do not depend on it.
+  __shared__ int hist[kSplitQ + 1], fill[kSplitQ + 1];
+  for (int b = t; b <= kSplitQ; b += 1024) {
+    hist[b] = 0;
+    fill[b] = 0;
+  }
+  if (t == 0) a.counts[2] = 0;
+  __syncthreads();
+  auto size_of = [&](int cnt, int sp) {
+    const int q = cnt - sp * kSplitQ;
+    return q < kSplitQ ? q : kSplitQ;
+  };
+  for (int e = e0; e < e1; ++e) {
+    const int cnt = a.inv_cnt[e];
+    for (int sp = 0; sp < a.nsplit[e]; ++sp) atomicAdd(&hist[kSplitQ - size_of(cnt, sp)], 1);
+  }
+  __syncthreads();
+  if (t == 0) {
+    int run = 0;
+    for (int b = 0; b <= kSplitQ; ++b) {
+      const int c = hist[b];
+      hist[b] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  for (int e = e0; e < e1; ++e) {
+    const int cnt = a.inv_cnt[e];
+    for (int sp = 0; sp < a.nsplit[e]; ++sp) {
+      const int b = kSplitQ - size_of(cnt, sp);
+      a.sorted[hist[b] + atomicAdd(&fill[b], 1)] = int2{e, sp};
+    }
+  }
 }
 
 // ------------------------------------------------------------------ dK/dV pass
-// Grid-stride over work items, 128 threads.  Wave w owns keys 32*w + [0, 32) of the item's
+// Work items from a counter, largest first, 128 threads.  Wave w owns keys 32*w + [0, 32) of the item's
 // KV block (MFMA columns).
 template <int D>
 __global__ void __launch_bounds__(128, PBSA_DKDV_WPE) attn_bwd_dkdv_kernel(BwdArgs a) {
@@ -346,8 +385,14 @@ __global__ void __launch_bounds__(128, PBSA_DKDV_WPE) attn_bwd_dkdv_kernel(BwdAr
   const float c = a.scale * kLog2e;
   const int n_items = a.counts[0];
 
-  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-    const int2 it = a.items[item];
+  __shared__ int s_item;
+  for (;;) {
+    // the next item, largest first (the counter is cleared by the plan pass)
+    if (t == 0) s_item = atomicAdd(&a.counts[2], 1);
+    __syncthreads();
+    const int item = s_item;
+    if (item >= n_items) break;
+    const int2 it = a.sorted[item];
     const int hg = __builtin_amdgcn_readfirstlane(it.x), sp = __builtin_amdgcn_readfirstlane(it.y);
     const int h = hg / a.nq, g = hg - h * a.nq;
     const int64_t k0 = block_token0(g, a.nb, a.n);
@@ -532,7 +577,7 @@ __global__ void __launch_bounds__(128) attn_bwd_reduce_kernel(BwdArgs a) {
 namespace {
 // Workspace layout of the backward (bytes, 256-aligned pieces).
 struct BwdWs {
-  size_t D, inv_cnt, inv, items, nsplit, part_base, long_list, counts, part, total;
+  size_t D, inv_cnt, inv, items, sorted, nsplit, part_base, long_list, counts, part, total;
 };
 BwdWs bwd_ws(const pbsa_dims& d, int chunks, int max_sel) {
   const int64_t nq = static_cast<int64_t>(chunks) * d.chunk_frames * nb_of(d);
@@ -548,6 +593,7 @@ BwdWs bwd_ws(const pbsa_dims& d, int chunks, int max_sel) {
   w.inv_cnt = o; o += up(H * nq * 4);
   w.inv = o; o += up(H * nq * nq * 4);
   w.items = o; o += up(items_max * 8);
+  w.sorted = o; o += up(items_max * 8);
   w.nsplit = o; o += up(H * nq * 4);
   w.part_base = o; o += up(H * nq * 4);
   w.long_list = o; o += up(H * nq * 4);
@@ -587,6 +633,7 @@ hipError_t launch_attn_bwd(const pbsa_dims& d, int chunks, TokIn q, TokIn k, Tok
   a.inv_cnt = reinterpret_cast<int32_t*>(p + L.inv_cnt);
   a.inv = reinterpret_cast<int32_t*>(p + L.inv);
   a.items = reinterpret_cast<int2*>(p + L.items);
+  a.sorted = reinterpret_cast<int2*>(p + L.sorted);
   a.nsplit = reinterpret_cast<int32_t*>(p + L.nsplit);
   a.part_base = reinterpret_cast<int32_t*>(p + L.part_base);
   a.long_list = reinterpret_cast<int32_t*>(p + L.long_list);
@@ -617,7 +664,8 @@ hipError_t launch_attn_bwd(const pbsa_dims& d, int chunks, TokIn q, TokIn k, Tok
   if (e != hipSuccess) return e;
   const int64_t items_max = static_cast<int64_t>(d.heads) * nq +
                             static_cast<int64_t>(d.heads) * nq * max_sel / kSplitQ + 1;
-  const int gi = static_cast<int>(items_max < 2048 ? items_max : 2048);
+  // enough workgroups to fill every CU; they take items from the counter until none is left
+  const int gi = static_cast<int>(items_max < 1024 ? items_max : 1024);
   if (d.head_dim == 128)
     hipLaunchKernelGGL(attn_bwd_dkdv_kernel<128>, dim3(gi), dim3(128), 0, s, a);
   else
