@@ -14,14 +14,12 @@ constexpr float kLog2e = 1.4426950408889634f;
 // bank conflicts: 16 consecutive rows reading the same logical chunk (K operand) hit 16
 // different positions, and 4 consecutive rows reading an aligned group of 4 chunks (the
 // transposing V read) land in 4 different groups.  For head_dim 64 rows are padded by 16
-// bytes instead.  The channel-major tile [D][64 + 4] is padded.
+// bytes instead.
 template <int D>
 struct Lds {
   static constexpr bool SWZ = (D == 128);
   static constexpr int RS = SWZ ? D : D + 8;  // row-major row pitch (elements)
-  static constexpr int CS = kBlock + 4;       // channel-major row pitch (elements)
   static constexpr int ROWS = kBlock * RS;
-  static constexpr int COLS = D * CS;
   // element offset of (row, channel chunk c) in a row-major tile
   __host__ __device__ static constexpr int chunk(int row, int c) {
     return row * RS + 8 * (SWZ ? (c ^ (((row & 3) << 2) | ((row >> 2) & 3))) : c);
@@ -31,7 +29,7 @@ struct Lds {
 // An R-row x D-channel bf16 tile (R = 64 or 32) staged through registers by NT threads.
 // Thread t owns channels [8*(t % CH), +8) of RG consecutive rows RG*KG*q + RG*(t / CH) + i
 // (i < RG): each load instruction reads whole 2*D-byte rows, and each thread holds RG
-// consecutive rows of one channel chunk, which it can write row-major or transposed.
+// consecutive rows of one channel chunk.
 template <int D, int NT = 128, int R = kBlock>
 struct Tile {
   static constexpr int CH = D / 8;                       // 16-byte chunks per row
@@ -65,31 +63,6 @@ struct Tile {
         *reinterpret_cast<u32x4*>(lds + Lds<D>::chunk(row, cc)) = r[q][i];
       }
   }
-
-  __device__ __forceinline__ static uint32_t pair(uint32_t x, uint32_t y, int odd) {
-    return odd ? (x >> 16) | (y & 0xffff0000u) : (x & 0xffffu) | (y << 16);
-  }
-
-  // channel-major copy [D][R + 4] (used where a transposed operand must also be written)
-  __device__ __forceinline__ void store_cols(uint16_t* lds, int t) const {
-    static_assert(R == kBlock, "column stores are laid out for 64-row tiles");
-    const int cc = t % CH, kg = t / CH;
-#pragma unroll
-    for (int q = 0; q < NP; ++q) {
-      const int row0 = RG * KG * q + RG * kg;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int w = e >> 1, odd = e & 1;
-        uint16_t* dst = lds + (8 * cc + e) * Lds<D>::CS + row0;
-        if constexpr (RG == 4) {
-          *reinterpret_cast<u32x2*>(dst) =
-              u32x2{pair(r[q][0][w], r[q][1][w], odd), pair(r[q][2][w], r[q][3][w], odd)};
-        } else {
-          *reinterpret_cast<uint32_t*>(dst) = pair(r[q][0][w], r[q][1][w], odd);
-        }
-      }
-    }
-  }
 };
 
 // MFMA operand reads from LDS for a wave whose lane l has half h2 = l / 32, c32 = l % 32.
@@ -99,22 +72,13 @@ template <int D>
 __device__ __forceinline__ u32x4 rd_rows(const uint16_t* lds, int tile, int s, int c32, int h2) {
   return *reinterpret_cast<const u32x4*>(lds + Lds<D>::chunk(32 * tile + c32, 2 * s + h2));
 }
-// Channel-major tile, channel rows 32*dt + c32, contraction over 16 rows of step t4 in the
-// order produced by a 32x32 accumulator: rows 16*t4 + 4*h2 + [0,4) then 16*t4 + 8 + 4*h2 +
-// [0,4).
-template <int D>
-__device__ __forceinline__ u32x4 rd_cols(const uint16_t* lds, int dt, int t4, int c32, int h2) {
-  const uint16_t* p = lds + (32 * dt + c32) * Lds<D>::CS + 16 * t4 + 4 * h2;
-  const u32x2 lo = *reinterpret_cast<const u32x2*>(p);
-  const u32x2 hi = *reinterpret_cast<const u32x2*>(p + 8);
-  return u32x4{lo[0], lo[1], hi[0], hi[1]};
-}
 // Channel-major view of a ROW-major tile through gfx950's transposing LDS read
 // (ds_read_b64_tr_b16).  Within each 16-lane group the instruction returns to lane i the
 // element (4e + i/4, i%4) of the 16 x 4 matrix formed by the lanes' 64-bit reads, e = 0..3.
 // Lane j = 4e + m of a group therefore addresses row K0 + e, channels D0 + 4m .. +3, and
-// lane i receives rows K0..K0+3 of channel D0 + i.  Same operand as rd_cols on a
-// channel-major copy: channel row 32*dt + c32, rows 16*t4 + 4*h2 + [0,4) then +8.
+// lane i receives rows K0..K0+3 of channel D0 + i.  The operand a wave gets: lane l holds
+// channel 32*dt + l % 32, contraction rows 16*t4 + 4*(l / 32) + [0,4) then the same + 8,
+// the row order of a 32x32 accumulator.
 typedef short s16x4_ __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_ lds_s16x4;
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
@@ -135,7 +99,7 @@ __device__ __forceinline__ u32x4 rd_rows_tr(const uint16_t* lds, int dt, int t4,
 }
 
 // B/A operand from two 32-row accumulator tiles: k-step t4 (16 rows) packed to bf16 in the
-// order rd_cols expects.
+// order rd_rows_tr produces.
 __device__ __forceinline__ u32x4 pack_step(const f32x16* acc, int t4) {
   const int kt = t4 >> 1, rb = 8 * (t4 & 1);
   u32x4 pb;

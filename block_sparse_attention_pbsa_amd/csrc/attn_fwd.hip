@@ -101,16 +101,11 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// 16 bytes per lane from global memory straight into LDS (lane l writes lds + 16 l; the
-// LDS address must be wave-uniform).
-__device__ __forceinline__ void lds_dma16(const char* src, char* lds) {
-  __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
-}
-
-// Piece i (0..3) of a run of 1 KB LDS pieces: the instruction's immediate offset 1024 i is
-// added to both the global and the LDS address, so a run shares one LDS base (M0) and
-// one scalar global base, and each piece costs one vector add for its lane offsets.
-// src must already be lowered by 1024 i.
+// 16 bytes per lane from global memory straight into LDS (lane l writes lds + 16 l; the LDS
+// address must be wave-uniform), as piece i (0..3) of a run of 1 KB LDS pieces: the
+// instruction's immediate offset 1024 i is added to both the global and the LDS address,
+// so a run shares one LDS base (M0) and one scalar global base, and each piece costs one
+// vector add for its lane offsets.  src must already be lowered by 1024 i.
 __device__ __forceinline__ void lds_dma16_piece(int i, __amdgpu_buffer_rsrc_t rs, uint32_t voff,
                                                 char* lds) {
   switch (i) {

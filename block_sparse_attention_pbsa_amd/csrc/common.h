@@ -63,48 +63,6 @@ __device__ __forceinline__ int rank_key_id(uint64_t k) {
   return static_cast<int>(~static_cast<uint32_t>(k & 0xffffffffu));
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-  const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), m, 64);
-  const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), m, 64);
-  return (static_cast<uint64_t>(hi) << 32) | lo;
-}
-
-// Bitonic sort, descending, of the 64*E keys held by one wave: element i = 64*e + lane is
-// v[e] of that lane.  Partners closer than 64 are exchanged across lanes, farther ones
-// inside a lane's registers.
-template <int E>
-__device__ __forceinline__ void wave_sort_desc(uint64_t (&v)[E], int lane) {
-  constexpr int N = 64 * E;
-#pragma unroll
-  for (int k = 2; k <= N; k <<= 1) {
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      if (j >= 64) {
-        const int je = j >> 6;
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          if (e & je) continue;
-          const int ep = e | je;
-          const bool desc = ((64 * e + lane) & k) == 0;
-          const uint64_t a = v[e], b = v[ep];
-          const uint64_t hi = a > b ? a : b, lo = a > b ? b : a;
-          v[e] = desc ? hi : lo;
-          v[ep] = desc ? lo : hi;
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const uint64_t o = shfl_xor_u64(v[e], j);
-          const bool lower = (lane & j) == 0;
-          const bool desc = ((64 * e + lane) & k) == 0;
-          const uint64_t hi = v[e] > o ? v[e] : o, lo = v[e] > o ? o : v[e];
-          v[e] = (lower == desc) ? hi : lo;
-        }
-      }
-    }
-  }
-}
-
 // Ceil division.
 __host__ __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
 
