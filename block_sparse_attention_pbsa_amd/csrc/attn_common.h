@@ -7,6 +7,7 @@
 namespace pbsa {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.69314718055994531f;
 
 // LDS tile layouts.  Row-major tiles keep 16-byte chunks of a row; for head_dim 128 a row is
 // exactly 256 bytes and chunk c of row r sits at chunk position c ^ swz(r), with

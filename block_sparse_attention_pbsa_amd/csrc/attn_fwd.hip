@@ -28,7 +28,8 @@
 //     free halfway through the step and V's at its end; the gather instructions are issued
 //     a few at a time between MFMAs (issued in one burst they stall the wave).
 // Softmax runs in base 2 with scale*log2(e) folded in (v_exp_f32), P is packed to bf16 with
-// v_cvt_pk_bf16_f32, and the running max is raised lazily; accumulators are fp32.
+// v_cvt_pk_bf16_f32, and the running max is raised lazily (checked on the row sums after
+// the exponentials, not by a max before them); accumulators are fp32.
 #include "attn_common.h"
 
 namespace pbsa {
@@ -136,26 +137,32 @@ struct RowState {
   static constexpr int NS = D / 16, ND = D / 32;
   u32x4 qreg[NS];
   f32x16 acc[ND];
-  float m_run, l_run;
-  float m_off;  // m_run * c (0 while no key has been seen): the exp2 offset
-  float m_thr;  // m_run + 8 / c: a row max above it raises the running max
+  // exp2 offset (the running max times c = scale * log2 e); before the first key it is a
+  // huge negative number, so that every exponential overflows and the first tile always
+  // sets it from its own row max
+  float m_off;
+  float l_run;  // this lane's share of the row sum (its 16 keys of each 32-key tile)
+  static constexpr float kNoOffset = -3.0e38f;
+  // A tile whose exponentials sum to more than this in one lane was computed against an
+  // offset too far below its scores: the offset is raised and the tile redone.
+  static constexpr float kRaiseSum = 1099511627776.f;  // 2^40
 
-  // Lazy raise of the running max: only when some row's new max exceeds it by more than
-  // 2^8 in exp2 units (so exp2 arguments stay <= 8).  Returns the factor for the earlier
-  // accumulators through alpha; l_run is scaled here, acc by the caller.  Rare: kept as a
-  // branch so that the common path is one compare.
-  __device__ __forceinline__ bool raise(float mx, float c, float& alpha) {
-    const bool up = __any(mx > m_thr);
+  // Raise the offset of every row to at least its max mx (times c).  Returns the factor
+  // for the earlier accumulators through alpha (0 before the first key: exp2 of a huge
+  // negative number); l_run is scaled here, acc by the caller.
+  __device__ __forceinline__ void raise(float mx, float c, float& alpha) {
+    const float m_new = fmaxf(m_off, mx * c);
+    alpha = __builtin_amdgcn_exp2f(m_off - m_new);
+    m_off = m_new;
+    l_run *= alpha;
+  }
+  // Lazy form for the unpipelined path: only when some row's max exceeds the offset by
+  // more than 2^8 in exp2 units (so exp2 arguments stay <= 8); the common path is one
+  // compare.
+  __device__ __forceinline__ bool raise_lazy(float mx, float c, float& alpha) {
+    const bool up = __any(mx * c > m_off + 8.f);
     alpha = 1.f;
-    if (up) {
-      const float m_new = fmaxf(m_run, mx);
-      alpha = m_run > -INFINITY ? __builtin_amdgcn_exp2f(m_run * c - m_new * c) : 0.f;
-      m_run = m_new;
-      l_run *= alpha;
-      // no valid key yet (a fully masked tile before any other): any finite offset works
-      m_off = m_new > -INFINITY ? m_new * c : 0.f;
-      m_thr = m_new + 8.f / c;
-    }
+    if (up) raise(mx, c, alpha);
     return up;
   }
 
@@ -235,41 +242,50 @@ struct RowState {
   }
 
   // Softmax of one score tile in stages, so that the stages can ride under MFMAs of the
-  // other tile.  Stage 0: in-lane row max; 1: max with lane l^32 (gfx950 permlane swap, no
-  // LDS round trip), lazy raise of the running max (by more than 2^8 in exp2 units) and
-  // the factor alpha folded into l_run; 2..5: four exponentials each; 6: bf16 packing
-  // and the row sum.
+  // other tile.  The exponentials use the current offset without looking at the tile's
+  // max first: stage k takes the exponentials of pair k of this lane's 16 scores and adds
+  // and packs (bf16) pair k - 1; finish() takes the last pair and then checks the sums: a
+  // lane whose 16 exponentials sum to more than kRaiseSum (one of them overflowed, or the
+  // offset lags the scores by more than 2^40) sends the whole wave down the rare branch,
+  // which takes the row max (in-lane plus the other lane half through gfx950's permlane
+  // swap), raises the offset and redoes the tile.  The first tile of every row takes that
+  // branch.
+  static constexpr int kStages = 8;
   struct Soft {
-    float mx, alpha;
+    float alpha, ps;
     float p[16];
     u32x4 pb[2];
     bool up;
   };
+  __device__ __forceinline__ void sum_pack(int j, Soft& so) {
+    const float s2 = so.p[2 * j] + so.p[2 * j + 1];
+    so.ps = j == 0 ? s2 : so.ps + s2;
+    so.pb[j >> 2][j & 3] = pack_bf16x2(so.p[2 * j], so.p[2 * j + 1]);
+  }
   __device__ __forceinline__ void stage(int k, const f32x16& sa, Soft& so, float c) {
-    if (k == 0) {
-      float mx = fmaxf(sa[0], sa[1]);
+    so.p[2 * k] = __builtin_amdgcn_exp2f(fmaf(sa[2 * k], c, -m_off));
+    so.p[2 * k + 1] = __builtin_amdgcn_exp2f(fmaf(sa[2 * k + 1], c, -m_off));
+    if (k > 0) sum_pack(k - 1, so);
+  }
+  __device__ __forceinline__ void finish(const f32x16& sa, Soft& so, float c) {
+    sum_pack(kStages - 1, so);
+    // the packing stays in the stages' scheduling groups (not sunk into the common branch)
+    asm volatile("" ::"v"(so.pb[0]), "v"(so.pb[1]), "v"(so.ps));
+    so.up = __any(so.ps > kRaiseSum);
+    so.alpha = 1.f;
+    if (so.up) {
+      __builtin_amdgcn_sched_barrier(0);
+      float mx = sa[0];
 #pragma unroll
-      for (int r = 2; r < 16; ++r) mx = fmaxf(mx, sa[r]);
-      so.mx = mx;
-    } else if (k == 1) {
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(so.mx),
-                                                       __float_as_uint(so.mx), false, false);
-      so.up = raise(fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])), c, so.alpha);
-    } else if (k <= 5) {
-      const int r0 = 4 * (k - 2);
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sa[r]);
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                       false, false);
+      raise(fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])), c, so.alpha);
 #pragma unroll
-      for (int r = r0; r < r0 + 4; ++r) so.p[r] = __builtin_amdgcn_exp2f(fmaf(sa[r], c, -m_off));
-    } else {
-      float ps = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) ps += so.p[r];
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          so.pb[t2][e] = pack_bf16x2(so.p[8 * t2 + 2 * e], so.p[8 * t2 + 2 * e + 1]);
-      l_run += ps;
+      for (int k = 0; k < kStages; ++k) stage(k, sa, so, c);
+      sum_pack(kStages - 1, so);
     }
+    l_run += so.ps;
   }
 
   // The pipelined steps (head_dim 128) come in two halves around the step's mid barrier:
@@ -297,7 +313,8 @@ struct RowState {
     }
     mask(sa, len, h2);
 #pragma unroll
-    for (int k = 0; k < 7; ++k) stage(k, sa, md.so, c);
+    for (int k = 0; k < kStages; ++k) stage(k, sa, md.so, c);
+    finish(sa, md.so, c);
     asm volatile("" ::"v"(md.so.pb[0]), "v"(md.so.pb[1]));
   }
   // PV phase of a private step: the V reads run two MFMAs ahead.
@@ -337,9 +354,10 @@ struct RowState {
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       md.sy = mfma32(kopy[i], qreg[i], md.sy);
-      if (i < 7) stage(i, sx, md.so, c);
+      if (i < kStages) stage(i, sx, md.so, c);
       sched_fence();
     }
+    finish(sx, md.so, c);
     // the exponentials of X stay in the groups above (not sunk past later branches)
     asm volatile("" ::"v"(md.so.pb[0]), "v"(md.so.pb[1]));
   }
@@ -359,10 +377,11 @@ struct RowState {
       acc[j % ND] = mfma32(vop[j], md.so.pb[j / ND], acc[j % ND]);
       const int nx = j + 2;
       vop[nx] = nx < 2 * ND ? vread(vx, nx) : vread(vy, nx - 2 * ND);
-      if (j < 7) stage(j, md.sy, sv, c);
+      if (j < kStages) stage(j, md.sy, sv, c);
       dma(j);
       sched_fence();
     }
+    finish(md.sy, sv, c);
     asm volatile("" ::"v"(sv.pb[0]), "v"(sv.pb[1]));
     if (sv.up) rescale(sv.alpha);
 #pragma unroll
@@ -374,8 +393,8 @@ struct RowState {
   }
 
   // Online-softmax update with NT score tiles (32 keys each) and their V half tiles.
-  // The running max only moves when some row's new max exceeds it by more than 2^8 in
-  // exp2 units, so the rescale of the accumulators is rare; exp2 arguments stay <= 8.
+  // The offset only moves when some row's new max exceeds it by more than 2^8 in exp2
+  // units, so the rescale of the accumulators is rare; exp2 arguments stay <= 8.
   template <int NT>
   __device__ __forceinline__ void update(f32x16* sacc, const char* v0, const char* v1, float c) {
     float mx = sacc[0][0];
@@ -385,7 +404,7 @@ struct RowState {
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     float alpha;
-    if (raise(mx, c, alpha)) {
+    if (raise_lazy(mx, c, alpha)) {
 #pragma unroll
       for (int dt = 0; dt < ND; ++dt) acc[dt] *= alpha;
     }
@@ -580,10 +599,8 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
   load_row_operand<D>(st.qreg, a.q + h * a.qhs + t0 * a.qts, a.qts, qrow, qlen, h2);
 #pragma unroll
   for (int i = 0; i < RowState<D>::ND; ++i) st.acc[i] = f32x16{};
-  st.m_run = -INFINITY;
+  st.m_off = RowState<D>::kNoOffset;
   st.l_run = 0.f;
-  st.m_off = 0.f;
-  st.m_thr = -INFINITY;
 
   const char* ck_h = reinterpret_cast<const char*>(a.ck) +
                      static_cast<int64_t>(h) * a.slots * kCacheBlockBytes;
@@ -836,7 +853,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
                     pack_bf16x2(st.acc[dt][4 * j + 2] * inv, st.acc[dt][4 * j + 3] * inv)};
         *reinterpret_cast<u32x2*>(orow + ch) = pk;
       }
-    if (h2 == 0) a.lse[h * a.lse_hs + t0 + qrow] = st.m_run * a.scale + logf(l_tot);
+    if (h2 == 0) a.lse[h * a.lse_hs + t0 + qrow] = st.m_off * kLn2 + logf(l_tot);
   }
 }
 
