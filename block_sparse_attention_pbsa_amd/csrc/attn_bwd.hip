@@ -19,8 +19,9 @@
 //                most by a few dozen), numbering items and partial-sum slots by prefix sums.
 //   dkdv pass -- work items taken largest first from a counter (the plan pass orders them
 //                by size; each item writes only its own outputs, so results do not depend on
-//                which workgroup takes it), two waves of 32 keys each; the KV block
-//                stays in LDS; an item walks its part of the list in 32-query half tiles:
+//                which workgroup takes it), two waves of 32 keys each; each lane keeps
+//                its key's K and V rows in registers (the MFMA B operands) for the whole
+//                item, which walks its part of the list in 32-query half tiles:
 //                S = Q K^T and dP = dO V^T with keys as MFMA columns, then dV^T += dO^T P
 //                and dK^T += Q^T dS (dO, Q read channel-major with the transposing read).
 //                A block with one item writes dK, dV; otherwise each item writes an fp32
@@ -369,8 +370,6 @@ template <int D>
 __global__ void __launch_bounds__(128, PBSA_DKDV_WPE) attn_bwd_dkdv_kernel(BwdArgs a) {
   constexpr int NS = D / 16, ND = D / 32;
   constexpr int HT = 32 * Lds<D>::RS;
-  __shared__ __attribute__((aligned(16))) uint16_t Kb[Lds<D>::ROWS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vb[Lds<D>::ROWS];
   __shared__ __attribute__((aligned(16))) uint16_t Qs[HT];
   __shared__ __attribute__((aligned(16))) uint16_t Os[HT];  // dO half tile
   __shared__ float lse2_s[32], d_s[32];
@@ -398,13 +397,11 @@ __global__ void __launch_bounds__(128, PBSA_DKDV_WPE) attn_bwd_dkdv_kernel(BwdAr
     const int64_t k0 = block_token0(g, a.nb, a.n);
     const int klen = block_len(g % a.nb, a.n);
     __syncthreads();  // the previous item's LDS reads are done
-    {
-      Tile<D, 128> tk, tv;
-      tk.load(a.k + h * a.khs + k0 * a.kts, a.kts, klen, t);
-      tv.load(a.v + h * a.vhs + k0 * a.vts, a.vts, klen, t);
-      tk.store_rows(Kb, t);
-      tv.store_rows(Vb, t);
-    }
+    // this lane's key row of K and V as MFMA B operands for the whole item (rows past the
+    // block's length read as zero)
+    u32x4 kop[NS], vop[NS];
+    load_row_operand<D>(kop, a.k + h * a.khs + k0 * a.kts, a.kts, key, klen, h2);
+    load_row_operand<D>(vop, a.v + h * a.vhs + k0 * a.vts, a.vts, key, klen, h2);
     f32x16 dk[ND], dv[ND];
 #pragma unroll
     for (int i = 0; i < ND; ++i) {
@@ -462,8 +459,8 @@ __global__ void __launch_bounds__(128, PBSA_DKDV_WPE) attn_bwd_dkdv_kernel(BwdAr
         // S (queries x keys): A = Q rows, B = K rows of this wave's keys; dP likewise
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
-          sacc[0] = mfma32(rd_rows<D>(Qs, 0, st, c32, h2), rd_rows<D>(Kb, w, st, c32, h2), sacc[0]);
-          pacc[0] = mfma32(rd_rows<D>(Os, 0, st, c32, h2), rd_rows<D>(Vb, w, st, c32, h2), pacc[0]);
+          sacc[0] = mfma32(rd_rows<D>(Qs, 0, st, c32, h2), kop[st], sacc[0]);
+          pacc[0] = mfma32(rd_rows<D>(Os, 0, st, c32, h2), vop[st], pacc[0]);
         }
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
