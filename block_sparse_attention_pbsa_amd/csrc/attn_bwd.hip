@@ -29,12 +29,6 @@
 //   reduce    -- sums a split block's partials in item order and writes dK, dV.
 #include "attn_common.h"
 
-// Waves per SIMD the dK/dV pass is compiled for: its two accumulators (dK^T, dV^T) take
-// 128 VGPRs, so one wave per SIMD gives it the whole register file without spills.
-#ifndef PBSA_DKDV_WPE
-#define PBSA_DKDV_WPE 1
-#endif
-
 namespace pbsa {
 
 namespace {
@@ -364,23 +358,36 @@ __global__ void __launch_bounds__(1024) attn_bwd_plan_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------------------ dK/dV pass
-// Work items from a counter, largest first, 128 threads.  Wave w owns keys 32*w + [0, 32) of the item's
-// KV block (MFMA columns).
+// Work items from a counter, largest first; 256 threads, two workgroups (two waves per
+// SIMD) per CU, so that one wave's softmax, LDS reads and staging run under the other's
+// MFMAs.  Wave w owns keys 32*(w & 1) + [0, 32) of the item's KV block (MFMA columns) and
+// rows 32*(w >> 1) + [0, 32) of each step's query block; at the end of the item the two
+// waves that share keys add their dK^T/dV^T sums through LDS (wave w + 2 into wave w, a
+// fixed order).
 template <int D>
-__global__ void __launch_bounds__(128, PBSA_DKDV_WPE) attn_bwd_dkdv_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdArgs a) {
   constexpr int NS = D / 16, ND = D / 32;
-  constexpr int HT = 32 * Lds<D>::RS;
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[HT];
-  __shared__ __attribute__((aligned(16))) uint16_t Os[HT];  // dO half tile
-  __shared__ float lse2_s[32], d_s[32];
+  constexpr int TB = Lds<D>::ROWS;                   // elements of one 64-row tile
+  constexpr int kSlot = 8 * ND * 64;                 // f32x4 per wave of dK^T | dV^T sums
+  constexpr int kSmem = 8 * TB > 2 * kSlot * 16 ? 8 * TB : 2 * kSlot * 16;
+  // K, V of the item's block and Q, dO of the step's query block (row-major tiles); at
+  // the end of an item the same bytes hold the sums of waves 2 and 3
+  __shared__ __attribute__((aligned(16))) char smem[kSmem];
+  uint16_t* Kb = reinterpret_cast<uint16_t*>(smem);
+  uint16_t* Vb = Kb + TB;
+  uint16_t* Qs = Vb + TB;
+  uint16_t* Os = Qs + TB;
+  __shared__ __attribute__((aligned(16))) float lse2_s[kBlock];
+  __shared__ __attribute__((aligned(16))) float d_s[kBlock];
   // this item's query blocks: first token and valid rows, staged once per item so that a
-  // step's fetch reads LDS instead of waiting on global memory
+  // step's loads do not wait on a global read of the list
   __shared__ int64_t qtok_s[kSplitQ];
   __shared__ int qlen_s[kSplitQ];
   const int t = threadIdx.x;
   const int l = t & 63, h2 = l >> 5, c32 = l & 31;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int key = 32 * w + c32;  // this lane's key (MFMA column) inside the block
+  const int kt = w & 1, qh = w >> 1;
+  const int key = 32 * kt + c32;  // this lane's key (MFMA column) inside the block
   const float c = a.scale * kLog2e;
   const int n_items = a.counts[0];
 
@@ -396,12 +403,14 @@ __global__ void __launch_bounds__(128, PBSA_DKDV_WPE) attn_bwd_dkdv_kernel(BwdAr
     const int h = hg / a.nq, g = hg - h * a.nq;
     const int64_t k0 = block_token0(g, a.nb, a.n);
     const int klen = block_len(g % a.nb, a.n);
-    __syncthreads();  // the previous item's LDS reads are done
-    // this lane's key row of K and V as MFMA B operands for the whole item (rows past the
-    // block's length read as zero)
-    u32x4 kop[NS], vop[NS];
-    load_row_operand<D>(kop, a.k + h * a.khs + k0 * a.kts, a.kts, key, klen, h2);
-    load_row_operand<D>(vop, a.v + h * a.vhs + k0 * a.vts, a.vts, key, klen, h2);
+    __syncthreads();  // s_item is read and the previous item's sums are consumed
+    {
+      Tile<D, 256> tk, tv;
+      tk.load(a.k + h * a.khs + k0 * a.kts, a.kts, klen, t);
+      tv.load(a.v + h * a.vhs + k0 * a.vts, a.vts, klen, t);
+      tk.store_rows(Kb, t);
+      tv.store_rows(Vb, t);
+    }
     f32x16 dk[ND], dv[ND];
 #pragma unroll
     for (int i = 0; i < ND; ++i) {
@@ -412,59 +421,46 @@ __global__ void __launch_bounds__(128, PBSA_DKDV_WPE) attn_bwd_dkdv_kernel(BwdAr
     const int q_lo = sp * kSplitQ;
     const int q_hi = min(cnt, q_lo + kSplitQ);
     const int32_t* lst = a.inv + static_cast<int64_t>(hg) * a.nq;
-    const int nsteps = 2 * (q_hi - q_lo);
-    for (int i = t; i < q_hi - q_lo; i += 128) {
+    const int nsteps = q_hi - q_lo;  // one query block per step
+    for (int i = t; i < nsteps; i += 256) {
       const int rb = lst[q_lo + i];
       qtok_s[i] = block_token0(rb, a.nb, a.n);
       qlen_s[i] = block_len(rb % a.nb, a.n);
     }
-    __syncthreads();
-    const uint16_t* qh = a.q + h * a.qhs;
-    const uint16_t* dh = a.dout + h * a.dhs;
-    Tile<D, 128, 32> tq, td;
-    Half hq, hd;
-    float lse_r = INFINITY, d_r = 0.f;
-    auto fetch = [&](int s) {
-      const int half = s & 1;
-      const int64_t qt0 = qtok_s[s >> 1] + 32 * half;
-      const int hl = qlen_s[s >> 1] - 32 * half;
-      const int hlen = __builtin_amdgcn_readfirstlane(hl < 0 ? 0 : (hl < 32 ? hl : 32));
-      hq = Half{qh + qt0 * a.qts, hlen};
-      hd = Half{dh + qt0 * a.dts, hlen};
-      tq.load(hq.p, a.qts, hq.len, t);
-      td.load(hd.p, a.dts, hd.len, t);
-      if (t < 32) {
-        const int64_t q0 = qt0;
-        // rows past the query block's length get lse = +inf, so their P is 0
-        lse_r = t < hq.len ? a.lse[h * a.T + q0 + t] * kLog2e : INFINITY;
-        d_r = t < hq.len ? a.Dw[h * a.T + q0 + t] : 0.f;
-      }
-    };
-    if (nsteps > 0) fetch(0);
+    const uint16_t* qhp = a.q + h * a.qhs;
+    const uint16_t* dhp = a.dout + h * a.dhs;
     for (int s = 0; s < nsteps; ++s) {
+      // K, V and the list are stored; every wave is done with the previous step's tiles
       __syncthreads();
-      tq.store_rows(Qs, t);
-      td.store_rows(Os, t);
-      if (t < 32) {
-        lse2_s[t] = lse_r;
-        d_s[t] = d_r;
+      const int64_t q0 = qtok_s[s];
+      const int qlen = __builtin_amdgcn_readfirstlane(qlen_s[s]);
+      {
+        Tile<D, 256> tq, td;
+        tq.load(qhp + q0 * a.qts, a.qts, qlen, t);
+        td.load(dhp + q0 * a.dts, a.dts, qlen, t);
+        if (t < kBlock) {
+          // rows past the query block's length get lse = +inf, so their P is 0
+          lse2_s[t] = t < qlen ? a.lse[h * a.T + q0 + t] * kLog2e : INFINITY;
+          d_s[t] = t < qlen ? a.Dw[h * a.T + q0 + t] : 0.f;
+        }
+        tq.store_rows(Qs, t);
+        td.store_rows(Os, t);
       }
-      const int qlen = hq.len;
       __syncthreads();
-      if (s + 1 < nsteps) fetch(s + 1);
-      if (qlen > 0) {
+      if (32 * qh < qlen) {
+        // S (queries x keys): A = Q rows of this wave's half, B = K rows of its keys; dP
+        // likewise from dO and V
         f32x16 sacc[1], pacc[1];
         sacc[0] = f32x16{};
         pacc[0] = f32x16{};
-        // S (queries x keys): A = Q rows, B = K rows of this wave's keys; dP likewise
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
-          sacc[0] = mfma32(rd_rows<D>(Qs, 0, st, c32, h2), kop[st], sacc[0]);
-          pacc[0] = mfma32(rd_rows<D>(Os, 0, st, c32, h2), vop[st], pacc[0]);
+          sacc[0] = mfma32(rd_rows<D>(Qs, qh, st, c32, h2), rd_rows<D>(Kb, kt, st, c32, h2), sacc[0]);
+          pacc[0] = mfma32(rd_rows<D>(Os, qh, st, c32, h2), rd_rows<D>(Vb, kt, st, c32, h2), pacc[0]);
         }
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
-          const int qi = acc_row(rr, h2);
+          const int qi = 32 * qh + acc_row(rr, h2);
           const float p = __builtin_amdgcn_exp2f(fmaf(sacc[0][rr], c, -lse2_s[qi]));
           sacc[0][rr] = p;
           pacc[0][rr] = p * (pacc[0][rr] - d_s[qi]);
@@ -476,12 +472,41 @@ __global__ void __launch_bounds__(128, PBSA_DKDV_WPE) attn_bwd_dkdv_kernel(BwdAr
           const u32x4 sb = pack_step(pacc, t2);
 #pragma unroll
           for (int dt = 0; dt < ND; ++dt) {
-            dv[dt] = mfma32(rd_rows_tr<D>(Os, dt, t2, l), pb, dv[dt]);
-            dk[dt] = mfma32(rd_rows_tr<D>(Qs, dt, t2, l), sb, dk[dt]);
+            dv[dt] = mfma32(rd_rows_tr<D>(Os, dt, 2 * qh + t2, l), pb, dv[dt]);
+            dk[dt] = mfma32(rd_rows_tr<D>(Qs, dt, 2 * qh + t2, l), sb, dk[dt]);
           }
         }
       }
     }
+    // waves 2 and 3 hand their sums to waves 0 and 1: slot kt, f32x4 j of lane l at
+    // [j][l] (dK^T registers first, then dV^T)
+    __syncthreads();  // every wave is done with the tiles
+    f32x4* slot = reinterpret_cast<f32x4*>(smem) + kt * kSlot;
+    if (qh == 1) {
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          slot[(4 * dt + r) * 64 + l] =
+              f32x4{dk[dt][4 * r], dk[dt][4 * r + 1], dk[dt][4 * r + 2], dk[dt][4 * r + 3]};
+          slot[(4 * ND + 4 * dt + r) * 64 + l] =
+              f32x4{dv[dt][4 * r], dv[dt][4 * r + 1], dv[dt][4 * r + 2], dv[dt][4 * r + 3]};
+        }
+    }
+    __syncthreads();
+    if (qh == 1) continue;
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const f32x4 ok = slot[(4 * dt + r) * 64 + l];
+        const f32x4 ov = slot[(4 * ND + 4 * dt + r) * 64 + l];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          dk[dt][4 * r + e] += ok[e];
+          dv[dt][4 * r + e] += ov[e];
+        }
+      }
     if (a.nsplit[hg] == 1) {
       if (key < klen) {
         uint16_t* ko = a.dk + h * a.dkhs + (k0 + key) * a.dkts;
@@ -500,8 +525,9 @@ __global__ void __launch_bounds__(128, PBSA_DKDV_WPE) attn_bwd_dkdv_kernel(BwdAr
           }
       }
     } else {
-      // partial slot: [thread][dK^T registers | dV^T registers], each thread's values
-      // contiguous so the stores take immediate offsets from one address
+      // partial slot: [thread][dK^T registers | dV^T registers] for threads 0..127 (waves
+      // 0 and 1), each thread's values contiguous so the stores take immediate offsets
+      // from one address
       f32x4* pp = reinterpret_cast<f32x4*>(
           a.part + static_cast<int64_t>(a.part_base[hg] + sp) * (2 * kBlock * D) +
           static_cast<int64_t>(t) * (32 * ND));
@@ -664,9 +690,9 @@ hipError_t launch_attn_bwd(const pbsa_dims& d, int chunks, TokIn q, TokIn k, Tok
   // enough workgroups to fill every CU; they take items from the counter until none is left
   const int gi = static_cast<int>(items_max < 1024 ? items_max : 1024);
   if (d.head_dim == 128)
-    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<128>, dim3(gi), dim3(128), 0, s, a);
+    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<128>, dim3(gi), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<64>, dim3(gi), dim3(128), 0, s, a);
+    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<64>, dim3(gi), dim3(256), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int gr = d.heads * nq;
