@@ -75,9 +75,13 @@ struct HalfTile {
   static constexpr int KRG = 16 * D * 2;       // K: bytes per 16-row group
 };
 
-// A half tile to gather: wave-uniform base (bytes), row stride (bytes) and valid rows.
 // Full scheduling fence (the compiler may not move instructions across it).
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+// Issue priority of a wave while it runs its MFMA groups: ahead of the other wave on its SIMD
+// (whose softmax, LDS reads and gathers then fill in behind it), which keeps the matrix pipe
+// fed (about 2% on the persistent-mode chunk).
+__device__ __forceinline__ void prio_mfma() { __builtin_amdgcn_s_setprio(1); }
+__device__ __forceinline__ void prio_rest() { __builtin_amdgcn_s_setprio(0); }
 
 // Wait until at most N of this wave's vector-memory instructions (here: gathers into LDS)
 // are outstanding; they complete in issue order.  A barrier after it makes the landed
@@ -124,6 +128,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t dma_base(const char* p) {
                                            0x00020000);
 }
 
+// A half tile to gather: wave-uniform base (bytes), row stride (bytes) and valid rows.
 struct HalfRef {
   const char* k;
   const char* v;
@@ -304,6 +309,7 @@ struct RowState {
                                           Mid& md) {
     u32x4 kop[NS];
     kread(kb, kop);
+    prio_mfma();
     f32x16 sa = {};
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
@@ -311,6 +317,7 @@ struct RowState {
       dma(i);
       sched_fence();
     }
+    prio_rest();
     mask(sa, len, h2);
 #pragma unroll
     for (int k = 0; k < kStages; ++k) stage(k, sa, md.so, c);
@@ -324,6 +331,7 @@ struct RowState {
     u32x4 vop[2 * ND];
     vop[0] = vread(vb, 0);
     vop[1] = vread(vb, 1);
+    prio_mfma();
 #pragma unroll
     for (int j = 0; j < 2 * ND; ++j) {
       acc[j % ND] = mfma32(vop[j], md.so.pb[j / ND], acc[j % ND]);
@@ -331,6 +339,7 @@ struct RowState {
       dma(j);
       sched_fence();
     }
+    prio_rest();
   }
 
   // Two half tiles (X then Y, a shared step), S phase: the gathers and the K reads of Y
@@ -341,6 +350,7 @@ struct RowState {
     static_assert(NS == 8 && ND == 4, "the pipelined pair is laid out for head_dim 128");
     u32x4 kop[NS], kopy[NS];
     kread(kx, kop);
+    prio_mfma();
     f32x16 sx = {};
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
@@ -357,6 +367,7 @@ struct RowState {
       if (i < kStages) stage(i, sx, md.so, c);
       sched_fence();
     }
+    prio_rest();
     finish(sx, md.so, c);
     // the exponentials of X stay in the groups above (not sunk past later branches)
     asm volatile("" ::"v"(md.so.pb[0]), "v"(md.so.pb[1]));
@@ -372,6 +383,7 @@ struct RowState {
     u32x4 vop[4 * ND];  // V of X (0..7), then V of Y (8..15)
     vop[0] = vread(vx, 0);
     vop[1] = vread(vx, 1);
+    prio_mfma();
 #pragma unroll
     for (int j = 0; j < 2 * ND; ++j) {
       acc[j % ND] = mfma32(vop[j], md.so.pb[j / ND], acc[j % ND]);
@@ -390,6 +402,7 @@ struct RowState {
       if (j + 2 < 2 * ND) vop[2 * ND + j + 2] = vread(vy, j + 2);
       sched_fence();
     }
+    prio_rest();
   }
 
   // Online-softmax update with NT score tiles (32 keys each) and their V half tiles.
