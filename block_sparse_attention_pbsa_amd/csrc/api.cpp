@@ -90,14 +90,17 @@ pbsa_status check_tok(const pbsa_tensor& t, const char* name, int head_dim) {
   return PBSA_OK;
 }
 
-// The attention kernels address a head's token rows with 32-bit byte offsets and name a
-// token block by its first token in 24 bits.
+// The attention kernels address a head's token rows with 32-bit byte offsets (a 64-row
+// block with 32-bit offsets from its first row, hence the stride limit) and name a token
+// block by its first token in 24 bits.
 pbsa_status check_span(const pbsa_tensor& t, const char* name, int64_t tokens, int head_dim) {
   const int64_t bytes = (tokens - 1) * t.token_stride * 2 + int64_t{head_dim} * 2;
   if (tokens > 0 && bytes > (int64_t{1} << 31))
     return fail(PBSA_ERR_UNSUPPORTED, "%s spans more than 2 GiB per head", name);
   if (tokens > (int64_t{1} << 24))
     return fail(PBSA_ERR_UNSUPPORTED, "%s has more than 2^24 tokens", name);
+  if (t.token_stride > (int64_t{1} << 24))
+    return fail(PBSA_ERR_UNSUPPORTED, "%s token stride exceeds 2^24 elements", name);
   return PBSA_OK;
 }
 
@@ -323,6 +326,11 @@ pbsa_status pbsa_attn_bwd(const pbsa_dims* dims, int32_t chunks, pbsa_tensor q, 
   PBSA_TRY(check_tok(dq, "dq", dims->head_dim));
   PBSA_TRY(check_tok(dk, "dk", dims->head_dim));
   PBSA_TRY(check_tok(dv, "dv", dims->head_dim));
+  const int64_t ttok = int64_t{chunks} * dims->chunk_frames * dims->frame_tokens;
+  PBSA_TRY(check_span(q, "q", ttok, dims->head_dim));
+  PBSA_TRY(check_span(k, "k", ttok, dims->head_dim));
+  PBSA_TRY(check_span(v, "v", ttok, dims->head_dim));
+  PBSA_TRY(check_span(dout, "dout", ttok, dims->head_dim));
   if (!lse || !sel || !nsel) return fail(PBSA_ERR_NULL, "lse, sel and nsel are required");
   if (max_sel < 1) return fail(PBSA_ERR_SHAPE, "max_sel must be >= 1");
   if (max_sel > pbsa::kAttnListCap / 2)

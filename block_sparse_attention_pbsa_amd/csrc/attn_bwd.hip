@@ -63,6 +63,43 @@ struct Half {
 };
 
 
+// Rows [0, len) of a tile from p (row stride stride_b bytes, p wave-uniform) into the
+// tile's registers through a buffer resource whose extent is len rows: rows past len read
+// as zero with no branch, and every load takes a 32-bit offset from one scalar base (the
+// host limits strides to 2^24 elements, so 64 rows of offsets fit).
+template <int D, int NT, int R>
+__device__ __forceinline__ void load_tile(Tile<D, NT, R>& tl, const uint16_t* p,
+                                          uint32_t stride_b, int len, int t) {
+  using TT = Tile<D, NT, R>;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(p), 0, static_cast<uint32_t>(len) * stride_b, 0x00020000);
+  const int cc = t % TT::CH, kg = t / TT::CH;
+#pragma unroll
+  for (int q = 0; q < TT::NP; ++q) {
+    // one lane offset per row group; the group's rows differ by scalar offsets
+    const uint32_t voff = (TT::RG * TT::KG * q + TT::RG * kg) * stride_b + 16u * cc;
+#pragma unroll
+    for (int i = 0; i < TT::RG; ++i)
+      tl.r[q][i] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, i * stride_b, 0));
+  }
+}
+
+// Element t of an fp32 row of n valid values from p (p wave-uniform); 0 past n.
+__device__ __forceinline__ float load_row_f32(const float* p, int n, int t) {
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(p), 0, static_cast<uint32_t>(n) * 4u, 0x00020000);
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, 4u * t, 0, 0));
+}
+
+// A wave-uniform 64-bit value kept in scalar registers.
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(v)));
+  const uint32_t hi =
+      static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(v >> 32)));
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------ dQ pass (+ D)
@@ -406,8 +443,8 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdArgs a) {
     __syncthreads();  // s_item is read and the previous item's sums are consumed
     {
       Tile<D, 256> tk, tv;
-      tk.load(a.k + h * a.khs + k0 * a.kts, a.kts, klen, t);
-      tv.load(a.v + h * a.vhs + k0 * a.vts, a.vts, klen, t);
+      load_tile(tk, a.k + h * a.khs + k0 * a.kts, static_cast<uint32_t>(2 * a.kts), klen, t);
+      load_tile(tv, a.v + h * a.vhs + k0 * a.vts, static_cast<uint32_t>(2 * a.vts), klen, t);
       tk.store_rows(Kb, t);
       tv.store_rows(Vb, t);
     }
@@ -429,24 +466,37 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdArgs a) {
     }
     const uint16_t* qhp = a.q + h * a.qhs;
     const uint16_t* dhp = a.dout + h * a.dhs;
+    // a step's Q and dO rows, lse and D are loaded into registers one step ahead
+    Tile<D, 256> tq, td;
+    float lse_r = INFINITY, d_r = 0.f;
+    int len_next = 0;
+    auto fetch = [&](int s) {
+      const int64_t q0 = uniform64(qtok_s[s]);
+      const int ql = __builtin_amdgcn_readfirstlane(qlen_s[s]);
+      load_tile(tq, qhp + q0 * a.qts, static_cast<uint32_t>(2 * a.qts), ql, t);
+      load_tile(td, dhp + q0 * a.dts, static_cast<uint32_t>(2 * a.dts), ql, t);
+      if (t < kBlock) {
+        // raw values: nothing may wait for these loads before the next step stores them
+        lse_r = load_row_f32(a.lse + h * a.T + q0, ql, t);
+        d_r = load_row_f32(a.Dw + h * a.T + q0, ql, t);
+      }
+      len_next = ql;
+    };
+    __syncthreads();  // the list is staged
+    if (nsteps > 0) fetch(0);
     for (int s = 0; s < nsteps; ++s) {
-      // K, V and the list are stored; every wave is done with the previous step's tiles
+      // K and V are stored; every wave is done with the previous step's tiles
       __syncthreads();
-      const int64_t q0 = qtok_s[s];
-      const int qlen = __builtin_amdgcn_readfirstlane(qlen_s[s]);
-      {
-        Tile<D, 256> tq, td;
-        tq.load(qhp + q0 * a.qts, a.qts, qlen, t);
-        td.load(dhp + q0 * a.dts, a.dts, qlen, t);
-        if (t < kBlock) {
-          // rows past the query block's length get lse = +inf, so their P is 0
-          lse2_s[t] = t < qlen ? a.lse[h * a.T + q0 + t] * kLog2e : INFINITY;
-          d_s[t] = t < qlen ? a.Dw[h * a.T + q0 + t] : 0.f;
-        }
-        tq.store_rows(Qs, t);
-        td.store_rows(Os, t);
+      tq.store_rows(Qs, t);
+      td.store_rows(Os, t);
+      const int qlen = len_next;
+      if (t < kBlock) {
+        // rows past the query block's length get lse = +inf, so their P is 0 (and D 0)
+        lse2_s[t] = t < qlen ? lse_r * kLog2e : INFINITY;
+        d_s[t] = d_r;
       }
       __syncthreads();
+      if (s + 1 < nsteps) fetch(s + 1);
       if (32 * qh < qlen) {
         // S (queries x keys): A = Q rows of this wave's half, B = K rows of its keys; dP
         // likewise from dO and V
@@ -458,12 +508,18 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdArgs a) {
           sacc[0] = mfma32(rd_rows<D>(Qs, qh, st, c32, h2), rd_rows<D>(Kb, kt, st, c32, h2), sacc[0]);
           pacc[0] = mfma32(rd_rows<D>(Os, qh, st, c32, h2), rd_rows<D>(Vb, kt, st, c32, h2), pacc[0]);
         }
+        // lse and D of the lane's rows 8 j + 4 h2 + [0, 4), four at a time
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          const int qi = 32 * qh + acc_row(rr, h2);
-          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[0][rr], c, -lse2_s[qi]));
-          sacc[0][rr] = p;
-          pacc[0][rr] = p * (pacc[0][rr] - d_s[qi]);
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2_s + 32 * qh + 8 * j + 4 * h2);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(d_s + 32 * qh + 8 * j + 4 * h2);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int rr = 4 * j + e;
+            const float p = __builtin_amdgcn_exp2f(fmaf(sacc[0][rr], c, -l4[e]));
+            sacc[0][rr] = p;
+            pacc[0][rr] = p * (pacc[0][rr] - d4[e]);
+          }
         }
         // dV^T += dO^T P, dK^T += Q^T dS (dO, Q channel-major through the transposing read)
 #pragma unroll

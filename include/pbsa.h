@@ -33,7 +33,8 @@
  *    <= 1024, window blocks <= 1024, topk <= 1024 and, for pbsa_attn_fwd, capacity +
  *    chunk blocks + 2*topk <= 3072; two-level mode: pbsa_attn_fwd_2lvl and pbsa_attn_bwd
  *    max_sel <= 1536;
- *    a head's K/V token rows span at most 2 GiB and 2^24 tokens.
+ *    a head's token rows of q, k, v and dout span at most 2 GiB and 2^24 tokens, and
+ *    token strides are at most 2^24 elements.
  */
 #ifndef PBSA_H_
 #define PBSA_H_
