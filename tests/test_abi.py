@@ -146,6 +146,13 @@ def test_calls_reject_bad_arguments_before_launching():
     assert L.pbsa_attn_bwd(d, 8, t, t, t, t, ctypes.c_void_p(16), t, ctypes.c_void_p(16),
                            ctypes.c_void_p(16), 1537, t, t, t, None, 0, None) == 3
     assert b"1536" in L.pbsa_last_error()
+    # backward: a token stride above 2^24 elements (32-bit row offsets inside a block)
+    wide = _tensor(16, ts=(1 << 24) + 8)
+    short = ctypes.byref(_dims(frame_tokens=16, chunk_frames=1))  # 16 tokens: span < 2 GiB
+    assert L.pbsa_attn_bwd(short, 1, wide, t, t, t, ctypes.c_void_p(16), t,
+                           ctypes.c_void_p(16), ctypes.c_void_p(16), 1, t, t, t, None, 0,
+                           None) == 3
+    assert b"stride" in L.pbsa_last_error()
 
 
 def test_python_binding_rejects_host_tensors():
