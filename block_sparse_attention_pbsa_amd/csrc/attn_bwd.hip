@@ -189,12 +189,14 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
 
   Tile<D, 256, 32> tkx, tvx, tky, tvy;
   Half kx, vx, ky, vy;
+  const uint32_t kstride_b = static_cast<uint32_t>(2 * a.kts);
+  const uint32_t vstride_b = static_cast<uint32_t>(2 * a.vts);
   if (nsteps > 0) {
     refs(0, kx, vx, ky, vy);
-    tkx.load(kx.p, a.kts, kx.len, t);
-    tvx.load(vx.p, a.vts, vx.len, t);
-    tky.load(ky.p, a.kts, ky.len, t);
-    tvy.load(vy.p, a.vts, vy.len, t);
+    load_tile(tkx, kx.p, kstride_b, kx.len, t);
+    load_tile(tvx, vx.p, vstride_b, vx.len, t);
+    load_tile(tky, ky.p, kstride_b, ky.len, t);
+    load_tile(tvy, vy.p, vstride_b, vy.len, t);
   }
   for (int s = 0; s < nsteps; ++s) {
     __syncthreads();
@@ -206,10 +208,10 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
     __syncthreads();
     if (s + 1 < nsteps) {
       refs(s + 1, kx, vx, ky, vy);
-      tkx.load(kx.p, a.kts, kx.len, t);
-      tvx.load(vx.p, a.vts, vx.len, t);
-      tky.load(ky.p, a.kts, ky.len, t);
-      tvy.load(vy.p, a.vts, vy.len, t);
+      load_tile(tkx, kx.p, kstride_b, kx.len, t);
+      load_tile(tvx, vx.p, vstride_b, vx.len, t);
+      load_tile(tky, ky.p, kstride_b, ky.len, t);
+      load_tile(tvy, vy.p, vstride_b, vy.len, t);
     }
     const int len = mine ? lenY : lenX;
     if (qlen > 0 && len > 0) {
