@@ -63,28 +63,6 @@ struct Half {
 };
 
 
-// Rows [0, len) of a tile from p (row stride stride_b bytes, p wave-uniform) into the
-// tile's registers through a buffer resource whose extent is len rows: rows past len read
-// as zero with no branch, and every load takes a 32-bit offset from one scalar base (the
-// host limits strides to 2^24 elements, so 64 rows of offsets fit).
-template <int D, int NT, int R>
-__device__ __forceinline__ void load_tile(Tile<D, NT, R>& tl, const uint16_t* p,
-                                          uint32_t stride_b, int len, int t) {
-  using TT = Tile<D, NT, R>;
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(p), 0, static_cast<uint32_t>(len) * stride_b, 0x00020000);
-  const int cc = t % TT::CH, kg = t / TT::CH;
-#pragma unroll
-  for (int q = 0; q < TT::NP; ++q) {
-    // one lane offset per row group; the group's rows differ by scalar offsets
-    const uint32_t voff = (TT::RG * TT::KG * q + TT::RG * kg) * stride_b + 16u * cc;
-#pragma unroll
-    for (int i = 0; i < TT::RG; ++i)
-      tl.r[q][i] = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, i * stride_b, 0));
-  }
-}
-
 // Element t of an fp32 row of n valid values from p (p wave-uniform); 0 past n.
 __device__ __forceinline__ float load_row_f32(const float* p, int n, int t) {
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
@@ -193,10 +171,10 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
   const uint32_t vstride_b = static_cast<uint32_t>(2 * a.vts);
   if (nsteps > 0) {
     refs(0, kx, vx, ky, vy);
-    load_tile(tkx, kx.p, kstride_b, kx.len, t);
-    load_tile(tvx, vx.p, vstride_b, vx.len, t);
-    load_tile(tky, ky.p, kstride_b, ky.len, t);
-    load_tile(tvy, vy.p, vstride_b, vy.len, t);
+    tkx.load(kx.p, kstride_b, kx.len, t);
+    tvx.load(vx.p, vstride_b, vx.len, t);
+    tky.load(ky.p, kstride_b, ky.len, t);
+    tvy.load(vy.p, vstride_b, vy.len, t);
   }
   for (int s = 0; s < nsteps; ++s) {
     __syncthreads();
@@ -208,10 +186,10 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
     __syncthreads();
     if (s + 1 < nsteps) {
       refs(s + 1, kx, vx, ky, vy);
-      load_tile(tkx, kx.p, kstride_b, kx.len, t);
-      load_tile(tvx, vx.p, vstride_b, vx.len, t);
-      load_tile(tky, ky.p, kstride_b, ky.len, t);
-      load_tile(tvy, vy.p, vstride_b, vy.len, t);
+      tkx.load(kx.p, kstride_b, kx.len, t);
+      tvx.load(vx.p, vstride_b, vx.len, t);
+      tky.load(ky.p, kstride_b, ky.len, t);
+      tvy.load(vy.p, vstride_b, vy.len, t);
     }
     const int len = mine ? lenY : lenX;
     if (qlen > 0 && len > 0) {
@@ -445,8 +423,8 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdArgs a) {
     __syncthreads();  // s_item is read and the previous item's sums are consumed
     {
       Tile<D, 256> tk, tv;
-      load_tile(tk, a.k + h * a.khs + k0 * a.kts, static_cast<uint32_t>(2 * a.kts), klen, t);
-      load_tile(tv, a.v + h * a.vhs + k0 * a.vts, static_cast<uint32_t>(2 * a.vts), klen, t);
+      tk.load(a.k + h * a.khs + k0 * a.kts, static_cast<uint32_t>(2 * a.kts), klen, t);
+      tv.load(a.v + h * a.vhs + k0 * a.vts, static_cast<uint32_t>(2 * a.vts), klen, t);
       tk.store_rows(Kb, t);
       tv.store_rows(Vb, t);
     }
@@ -475,8 +453,8 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdArgs a) {
     auto fetch = [&](int s) {
       const int64_t q0 = uniform64(qtok_s[s]);
       const int ql = __builtin_amdgcn_readfirstlane(qlen_s[s]);
-      load_tile(tq, qhp + q0 * a.qts, static_cast<uint32_t>(2 * a.qts), ql, t);
-      load_tile(td, dhp + q0 * a.dts, static_cast<uint32_t>(2 * a.dts), ql, t);
+      tq.load(qhp + q0 * a.qts, static_cast<uint32_t>(2 * a.qts), ql, t);
+      td.load(dhp + q0 * a.dts, static_cast<uint32_t>(2 * a.dts), ql, t);
       if (t < kBlock) {
         // raw values: nothing may wait for these loads before the next step stores them
         lse_r = load_row_f32(a.lse + h * a.T + q0, ql, t);

@@ -41,17 +41,22 @@ struct Tile {
   static_assert(CPT >= 1 && RG * KG * NP == R, "unsupported tile split");
   u32x4 r[NP][RG];
 
-  // rows [0, len) from p (row stride `stride` elements); rows past len read as zero
-  __device__ __forceinline__ void load(const uint16_t* p, int64_t stride, int len, int t) {
+  // Rows [0, len) from p (row stride stride_b bytes; p wave-uniform) through a buffer
+  // resource whose extent is len rows: rows past len read as zero with no branch, and each
+  // row group takes one 32-bit lane offset plus scalar row offsets (callers keep 64 rows
+  // of offsets under 2^32).
+  __device__ __forceinline__ void load(const uint16_t* p, uint32_t stride_b, int len, int t) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(p), 0, static_cast<uint32_t>(len) * stride_b, 0x00020000);
     const int cc = t % CH, kg = t / CH;
 #pragma unroll
-    for (int q = 0; q < NP; ++q)
+    for (int q = 0; q < NP; ++q) {
+      const uint32_t voff = (RG * KG * q + RG * kg) * stride_b + 16u * cc;
 #pragma unroll
-      for (int i = 0; i < RG; ++i) {
-        const int row = RG * KG * q + RG * kg + i;
-        r[q][i] = row < len ? *reinterpret_cast<const u32x4*>(p + row * stride + 8 * cc)
-                            : u32x4{0, 0, 0, 0};
-      }
+      for (int i = 0; i < RG; ++i)
+        r[q][i] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, i * stride_b, 0));
+    }
   }
 
   __device__ __forceinline__ void store_rows(uint16_t* lds, int t) const {
