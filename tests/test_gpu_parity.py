@@ -511,3 +511,31 @@ def test_bwd_is_deterministic():
         outs.append([t.view(torch.int16).clone() for t in (clip.dq, clip.dk, clip.dv)])
     for a, b in zip(*outs):
         assert torch.equal(a, b)
+
+
+def test_head_major_inputs_give_identical_training_results():
+    """q, k, v and dO stored head-major ([H][T][d]: token stride d, head stride T*d) instead
+    of token-major: forward and backward read them through other strides (the backward's
+    row offsets and buffer extents scale with the token stride), so the outputs must be
+    bit-identical."""
+    wl = synth.Workload("layout", 2, 128, 64, 200, 2, 0, 0, 0, 0, 6, clip_chunks=4, top_frames=2)
+    shape = shape_of(wl)
+    q, k, v = synth.clip_qkv(wl, 51)
+    ks = runtime.cag_budgets(synth.clip_alphas(wl, 51), wl.topk, wl.clip_chunks)
+    clip = runtime.TwoLevelClip(shape, wl.clip_chunks, wl.top_frames, max(max(ks), 8))
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    dod = dev(synth.clip_dout(wl, 51, q.shape[0]))
+    head_major = lambda x: x.permute(1, 0, 2).contiguous().permute(1, 0, 2)
+    qh, kh, vh, doh = (head_major(x) for x in (qd, kd, vd, dod))
+    assert qh.stride(0) == wl.head_dim and qh.stride(1) == q.shape[0] * wl.head_dim
+    say("[layout] token-major vs head-major")
+    clip.select(qd, kd, ks)
+    outs = []
+    for a, b, c, g in ((qd, kd, vd, dod), (qh, kh, vh, doh)):
+        clip.forward(a, b, c)
+        clip.backward(a, b, c, g)
+        torch.cuda.synchronize()
+        outs.append([t.view(torch.int16).clone() for t in (clip.o, clip.dq, clip.dk, clip.dv)]
+                    + [clip.lse.clone()])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
