@@ -66,7 +66,7 @@ def main():
         write_traffic(*args.write_traffic, args.traffic)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "the library runs on one GPU (no sharding across GPUs); --gpus must be 1"}))
         sys.exit(2)
     import torch
     from block_sparse_attention_pbsa_amd import ops, runtime, synth
