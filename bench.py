@@ -111,9 +111,7 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step():
-        layer.route(q)
-        layer.attend(q, k, v)
-        layer.update(k, v)
+        layer.step(q, k, v)
 
     for _ in range(args.warmup):
         step()

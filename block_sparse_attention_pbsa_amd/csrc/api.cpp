@@ -237,6 +237,49 @@ pbsa_status pbsa_attn_fwd(const pbsa_dims* dims, pbsa_tensor q, const pbsa_cache
                     "attn_fwd");
 }
 
+namespace {
+
+pbsa_status check_memory_ws(const pbsa_dims* dims, const pbsa_cache* cache, void* workspace,
+                            size_t workspace_bytes, const char* name) {
+  const size_t need = pbsa::memory_update_workspace(*dims);
+  if (!workspace || workspace_bytes < need)
+    return fail(PBSA_ERR_WORKSPACE, "%s needs %zu workspace bytes (got %zu)", name, need,
+                workspace ? workspace_bytes : static_cast<size_t>(0));
+  if (cache->chunk_index > (int64_t{1} << 40) / (dims->chunk_frames * pbsa::nb_of(*dims)))
+    return fail(PBSA_ERR_STATE, "chunk_index out of range");
+  return PBSA_OK;
+}
+
+}  // namespace
+
+pbsa_status pbsa_memory_select(const pbsa_dims* dims, const float* scores,
+                               const pbsa_cache* cache, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  PBSA_TRY(check_dims(dims, 0));
+  PBSA_TRY(check_cache(cache));
+  if (!scores) return fail(PBSA_ERR_NULL, "scores is required");
+  PBSA_TRY(check_memory_ws(dims, cache, workspace, workspace_bytes, "memory_select"));
+  return hip_status(pbsa::launch_memory_select(*dims, scores, *cache, workspace, true,
+                                               stream_of(stream)),
+                    "memory_select");
+}
+
+pbsa_status pbsa_memory_apply(const pbsa_dims* dims, pbsa_cache* cache, pbsa_tensor chunk_k,
+                              pbsa_tensor chunk_v, const float* chunk_rep, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  PBSA_TRY(check_dims(dims, 0));
+  PBSA_TRY(check_cache(cache));
+  PBSA_TRY(check_tok(chunk_k, "chunk_k", dims->head_dim));
+  PBSA_TRY(check_tok(chunk_v, "chunk_v", dims->head_dim));
+  PBSA_TRY(check_memory_ws(dims, cache, workspace, workspace_bytes, "memory_apply"));
+  pbsa_status st = hip_status(
+      pbsa::launch_memory_apply(*dims, *cache, pbsa::tok_in(chunk_k), pbsa::tok_in(chunk_v),
+                                chunk_rep, workspace, stream_of(stream)),
+      "memory_apply");
+  if (st == PBSA_OK) cache->chunk_index += 1;
+  return st;
+}
+
 pbsa_status pbsa_memory_update(const pbsa_dims* dims, const float* scores, pbsa_cache* cache,
                                pbsa_tensor chunk_k, pbsa_tensor chunk_v, const float* chunk_rep,
                                void* workspace, size_t workspace_bytes, void* stream) {
@@ -245,12 +288,7 @@ pbsa_status pbsa_memory_update(const pbsa_dims* dims, const float* scores, pbsa_
   PBSA_TRY(check_tok(chunk_k, "chunk_k", dims->head_dim));
   PBSA_TRY(check_tok(chunk_v, "chunk_v", dims->head_dim));
   if (!scores) return fail(PBSA_ERR_NULL, "scores is required");
-  const size_t need = pbsa::memory_update_workspace(*dims);
-  if (!workspace || workspace_bytes < need)
-    return fail(PBSA_ERR_WORKSPACE, "memory_update needs %zu workspace bytes (got %zu)", need,
-                workspace ? workspace_bytes : static_cast<size_t>(0));
-  if (cache->chunk_index > (int64_t{1} << 40) / (dims->chunk_frames * pbsa::nb_of(*dims)))
-    return fail(PBSA_ERR_STATE, "chunk_index out of range");
+  PBSA_TRY(check_memory_ws(dims, cache, workspace, workspace_bytes, "memory_update"));
   pbsa_status st = hip_status(
       pbsa::launch_memory_update(*dims, scores, *cache, pbsa::tok_in(chunk_k),
                                  pbsa::tok_in(chunk_v), chunk_rep, workspace, stream_of(stream)),

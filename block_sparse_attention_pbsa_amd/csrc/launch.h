@@ -68,6 +68,10 @@ hipError_t launch_attn_bwd(const pbsa_dims& d, int chunks, TokIn q, TokIn k, Tok
                            void* ws, hipStream_t s);
 
 size_t memory_update_workspace(const pbsa_dims& d);
+hipError_t launch_memory_select(const pbsa_dims& d, const float* scores, const pbsa_cache& c,
+                                void* ws, bool beside, hipStream_t s);
+hipError_t launch_memory_apply(const pbsa_dims& d, const pbsa_cache& c, TokIn ck, TokIn cv,
+                               const float* chunk_rep, void* ws, hipStream_t s);
 hipError_t launch_memory_update(const pbsa_dims& d, const float* scores, const pbsa_cache& c,
                                 TokIn ck, TokIn cv, const float* chunk_rep, void* ws,
                                 hipStream_t s);

@@ -7,13 +7,18 @@
 // sum over the chunk's query blocks of its coarse score; candidates are the non-sink
 // blocks of P_t and the leaving blocks; the C - S best by (score desc, id asc) are kept.
 //
-// Two launches on the caller's stream:
-//   select (one workgroup per head): column sums, rank, new P_t table, copy list;
-//   copy   (one workgroup per chunk block and head): move each promoted block from its
-//          window slot into its new persistent slot, then overwrite that window slot with
-//          the chunk's block (tokens, zero-padded rows, representative, id, length).
+// Two launches:
+//   select (one workgroup per head): column sums, rank, new P_t table and copy list, both
+//          into the workspace; it only reads the cache, so it may run on another stream
+//          while the chunk's attention still reads the cache (pbsa_memory_select);
+//   copy   (one workgroup per chunk block and head; pbsa_memory_apply): write the new P_t
+//          table, move each promoted block from its window slot into its new persistent
+//          slot, then overwrite that window slot with the chunk's block (tokens,
+//          zero-padded rows, representative, id, length).
 // The window slot a chunk block lands in is exactly the slot of a leaving block (or an
 // empty one), and the same workgroup does both moves, so reads precede writes.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 #include "select.h"
@@ -27,7 +32,9 @@ struct MemArgs {
   float* rep;           // [H][slots][D]
   int32_t* bid;         // [H][slots]
   int32_t* blen;        // [H][slots]
-  int32_t* copy_dst;    // workspace [H][F*nb]
+  int32_t* copy_dst;    // workspace [H][F*nb]: persistent slot of each leaving block kept
+  int32_t* pbid;        // workspace [H][C]: the new persistent table (block ids) ...
+  int32_t* plen;        // ... and lengths, written by the select, applied by the copy
   int slots, C, S, W, F, nb, n, nq;
   int64_t chunk;        // chunk index being appended
 };
@@ -42,12 +49,15 @@ struct MemArgs {
 // (ascending) are handed to the promoted leaving blocks in ascending id order.  Dynamic
 // LDS: block_id and len of the head ([slots] each), candidate slot [ncand_max], free-slot
 // list [C], partial sums [4][ncand_max].
+// NT threads: 1024 when the selection runs alone (more rows of the column sums in flight),
+// 256 when it runs beside the attention (four waves and a few KB of LDS fit next to two
+// attention workgroups on a CU, so it takes no attention workgroup's place); 256 also when
+// wave 0's sort keys need the registers.  The sums are the same either way.
 template <int E>
-constexpr int select_threads() { return E <= 8 ? 1024 : 256; }  // wave 0's sort keys fit
+constexpr int select_threads(bool beside) { return E <= 8 && !beside ? 1024 : 256; }
 
-template <int E>
-__global__ void __launch_bounds__(select_threads<E>()) memory_select_kernel(MemArgs a) {
-  constexpr int NT = select_threads<E>();
+template <int E, int NT>
+__global__ void __launch_bounds__(NT) memory_select_kernel(MemArgs a) {
   extern __shared__ int mem_smem[];
   __shared__ int s_cnt[2];  // nP, ncand
   const int h = blockIdx.x, t = threadIdx.x, l = t & 63, w = t >> 6;
@@ -57,18 +67,20 @@ __global__ void __launch_bounds__(select_threads<E>()) memory_select_kernel(MemA
   int* cslot = slen + a.slots;   // [ncand_max]
   int* freel = cslot + ncand_max;  // [C]
   float* part = reinterpret_cast<float*>(freel + a.C);  // [4][ncand_max]
-  int32_t* bid = a.bid + static_cast<int64_t>(h) * a.slots;
-  int32_t* blen = a.blen + static_cast<int64_t>(h) * a.slots;
+  const int32_t* bid = a.bid + static_cast<int64_t>(h) * a.slots;
+  const int32_t* blen = a.blen + static_cast<int64_t>(h) * a.slots;
   int32_t* dst = a.copy_dst + static_cast<int64_t>(h) * a.F * a.nb;
   const int64_t hF = a.chunk * a.F;  // frames appended so far
   const int fnb = a.F * a.nb;
 
   for (int b = t; b < fnb; b += NT) dst[b] = -1;
+  int32_t* pbid = a.pbid + static_cast<int64_t>(h) * a.C;
+  int32_t* plen = a.plen + static_cast<int64_t>(h) * a.C;
   if (a.chunk == 0) {
-    // empty cache: P_t becomes the sinks, written by the copy pass
+    // empty cache: P_t becomes the sinks (block g in slot g; the copy pass moves them)
     for (int s = t; s < a.C; s += NT) {
-      bid[s] = -1;
-      blen[s] = 0;
+      pbid[s] = s < a.S ? s : -1;
+      plen[s] = s < a.S ? block_len(s % a.nb, a.n) : 0;
     }
     return;
   }
@@ -202,16 +214,24 @@ __global__ void __launch_bounds__(select_threads<E>()) memory_select_kernel(MemA
         const int rf = b_rel / a.nb, j = b_rel % a.nb;
         const int fb = static_cast<int>(((rf - hF % a.W) % a.W + a.W) % a.W);
         dst[fb * a.nb + j] = s;
-        bid[s] = sbid[src];
-        blen[s] = slen[src];
+        // (persistent slots only: the window slots read above are not written)
+        sbid[s] = sbid[src];
+        slen[s] = slen[src];
       }
       npro += __popcll(m);
     }
     // freed slots left over become empty
     for (int k = npro + l; k < nfree; k += 64) {
-      bid[freel[k]] = -1;
-      blen[freel[k]] = 0;
+      sbid[freel[k]] = -1;
+      slen[freel[k]] = 0;
     }
+  }
+  __syncthreads();
+  // the new persistent table goes to the workspace; the cache itself is not written here,
+  // so this selection may run while other kernels still read the cache
+  for (int s = t; s < a.C; s += NT) {
+    pbid[s] = sbid[s];
+    plen[s] = slen[s];
   }
 }
 
@@ -295,23 +315,26 @@ __global__ void __launch_bounds__(256) memory_copy_kernel(MemArgs a, TokIn xk, T
       rep[static_cast<int64_t>(target) * D + c] =
           ((wsum[0][c] + wsum[1][c]) + (wsum[2][c] + wsum[3][c])) * inv;
   }
-  if (t == 0) {
-    a.bid[hs + target] = g;
-    a.blen[hs + target] = len;
-    if (sink) {
-      a.bid[hs + ring] = -1;
-      a.blen[hs + ring] = 0;
+  // the persistent table (selected by the select pass, sinks included) by one workgroup
+  // per head; every other id written here is a window slot's
+  if (b == 0)
+    for (int s = t; s < a.C; s += 256) {
+      a.bid[hs + s] = a.pbid[static_cast<int64_t>(h) * a.C + s];
+      a.blen[hs + s] = a.plen[static_cast<int64_t>(h) * a.C + s];
     }
+  if (t == 0) {
+    a.bid[hs + ring] = sink ? -1 : g;
+    a.blen[hs + ring] = sink ? 0 : len;
   }
 }
 
-size_t memory_update_workspace(const pbsa_dims& d) {
-  return sizeof(int32_t) * static_cast<size_t>(d.heads) * d.chunk_frames * nb_of(d);
-}
+namespace {
 
-hipError_t launch_memory_update(const pbsa_dims& d, const float* scores, const pbsa_cache& c,
-                                TokIn ck, TokIn cv, const float* chunk_rep, void* ws,
-                                hipStream_t s) {
+// Workspace: copy list [H][F*nb], then the new persistent table [H][C] (ids, lengths),
+// each piece 256-byte aligned.
+size_t ws_up(size_t x) { return (x + 255) & ~size_t{255}; }
+
+MemArgs mem_args(const pbsa_dims& d, const float* scores, const pbsa_cache& c, void* ws) {
   const int nb = nb_of(d);
   MemArgs a;
   a.scores = scores;
@@ -320,7 +343,12 @@ hipError_t launch_memory_update(const pbsa_dims& d, const float* scores, const p
   a.rep = c.rep;
   a.bid = c.block_id;
   a.blen = c.len;
-  a.copy_dst = static_cast<int32_t*>(ws);
+  char* p = static_cast<char*>(ws);
+  const size_t ncopy = ws_up(sizeof(int32_t) * static_cast<size_t>(d.heads) * d.chunk_frames * nb);
+  const size_t ntab = ws_up(sizeof(int32_t) * static_cast<size_t>(d.heads) * d.capacity);
+  a.copy_dst = reinterpret_cast<int32_t*>(p);
+  a.pbid = reinterpret_cast<int32_t*>(p + ncopy);
+  a.plen = reinterpret_cast<int32_t*>(p + ncopy + ntab);
   a.slots = static_cast<int>(slots_of(d));
   a.C = d.capacity;
   a.S = d.sinks;
@@ -330,23 +358,57 @@ hipError_t launch_memory_update(const pbsa_dims& d, const float* scores, const p
   a.n = d.frame_tokens;
   a.nq = d.chunk_frames * nb;
   a.chunk = c.chunk_index;
-  const int ncand_max = (d.capacity - d.sinks) + d.chunk_frames * nb;
+  return a;
+}
+
+}  // namespace
+
+size_t memory_update_workspace(const pbsa_dims& d) {
+  return ws_up(sizeof(int32_t) * static_cast<size_t>(d.heads) * d.chunk_frames * nb_of(d)) +
+         2 * ws_up(sizeof(int32_t) * static_cast<size_t>(d.heads) * d.capacity);
+}
+
+hipError_t launch_memory_select(const pbsa_dims& d, const float* scores, const pbsa_cache& c,
+                                void* ws, bool beside, hipStream_t s) {
+  const MemArgs a = mem_args(d, scores, c, ws);
+  const int ncand_max = (d.capacity - d.sinks) + d.chunk_frames * a.nb;
   const size_t lds = static_cast<size_t>(2 * a.slots + 5 * ncand_max + d.capacity) * sizeof(int);
   const int E = (ncand_max + 63) / 64;
-  if (E <= 1) hipLaunchKernelGGL(memory_select_kernel<1>, dim3(d.heads), dim3(select_threads<1>()), lds, s, a);
-  else if (E <= 2) hipLaunchKernelGGL(memory_select_kernel<2>, dim3(d.heads), dim3(select_threads<2>()), lds, s, a);
-  else if (E <= 4) hipLaunchKernelGGL(memory_select_kernel<4>, dim3(d.heads), dim3(select_threads<4>()), lds, s, a);
-  else if (E <= 8) hipLaunchKernelGGL(memory_select_kernel<8>, dim3(d.heads), dim3(select_threads<8>()), lds, s, a);
-  else if (E <= 16) hipLaunchKernelGGL(memory_select_kernel<16>, dim3(d.heads), dim3(select_threads<16>()), lds, s, a);
-  else hipLaunchKernelGGL(memory_select_kernel<32>, dim3(d.heads), dim3(select_threads<32>()), lds, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  dim3 grid(d.chunk_frames * nb, d.heads);
+  auto go = [&](auto e_tag) {
+    constexpr int EE = decltype(e_tag)::value;
+    if (beside)
+      hipLaunchKernelGGL((memory_select_kernel<EE, select_threads<EE>(true)>), dim3(d.heads),
+                         dim3(select_threads<EE>(true)), lds, s, a);
+    else
+      hipLaunchKernelGGL((memory_select_kernel<EE, select_threads<EE>(false)>), dim3(d.heads),
+                         dim3(select_threads<EE>(false)), lds, s, a);
+  };
+  if (E <= 1) go(std::integral_constant<int, 1>{});
+  else if (E <= 2) go(std::integral_constant<int, 2>{});
+  else if (E <= 4) go(std::integral_constant<int, 4>{});
+  else if (E <= 8) go(std::integral_constant<int, 8>{});
+  else if (E <= 16) go(std::integral_constant<int, 16>{});
+  else go(std::integral_constant<int, 32>{});
+  return hipGetLastError();
+}
+
+hipError_t launch_memory_apply(const pbsa_dims& d, const pbsa_cache& c, TokIn ck, TokIn cv,
+                               const float* chunk_rep, void* ws, hipStream_t s) {
+  const MemArgs a = mem_args(d, nullptr, c, ws);
+  dim3 grid(d.chunk_frames * a.nb, d.heads);
   if (d.head_dim == 128)
     hipLaunchKernelGGL(memory_copy_kernel<128>, grid, dim3(256), 0, s, a, ck, cv, chunk_rep);
   else
     hipLaunchKernelGGL(memory_copy_kernel<64>, grid, dim3(256), 0, s, a, ck, cv, chunk_rep);
   return hipGetLastError();
+}
+
+hipError_t launch_memory_update(const pbsa_dims& d, const float* scores, const pbsa_cache& c,
+                                TokIn ck, TokIn cv, const float* chunk_rep, void* ws,
+                                hipStream_t s) {
+  const hipError_t e = launch_memory_select(d, scores, c, ws, false, s);
+  if (e != hipSuccess) return e;
+  return launch_memory_apply(d, c, ck, cv, chunk_rep, ws, s);
 }
 
 }  // namespace pbsa

@@ -69,6 +69,10 @@ _SIGS = {
                        Tensor, _P, _P], ctypes.c_int),
     "pbsa_memory_update": ([ctypes.POINTER(Dims), _P, ctypes.POINTER(CacheC), Tensor, Tensor, _P,
                             _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "pbsa_memory_select": ([ctypes.POINTER(Dims), _P, ctypes.POINTER(CacheC), _P, ctypes.c_size_t,
+                            _P], ctypes.c_int),
+    "pbsa_memory_apply": ([ctypes.POINTER(Dims), ctypes.POINTER(CacheC), Tensor, Tensor, _P, _P,
+                           ctypes.c_size_t, _P], ctypes.c_int),
     "pbsa_score_topk_2lvl": ([ctypes.POINTER(Dims), _I32, _I32, ctypes.POINTER(_I32), _P, _P, _P,
                               _I32, _P, _P, _P], ctypes.c_int),
     "pbsa_attn_fwd_2lvl": ([ctypes.POINTER(Dims), _I32, Tensor, Tensor, Tensor, _P, _P, _I32,
@@ -294,6 +298,34 @@ def pbsa_memory_update(shape: Shape, scores, cache: Cache, chunk_k, chunk_v, chu
     _check("pbsa_memory_update", lib().pbsa_memory_update(
         ctypes.byref(shape.c()), _ptr(scores), ctypes.byref(cc), kt, vt, _ptr(chunk_rep),
         _ptr(workspace), workspace.numel(), _stream()))
+    cache.chunk_index = cc.chunk_index
+
+
+def pbsa_memory_select(shape: Shape, scores, cache: Cache, workspace):
+    """First half of pbsa_memory_update: the selection into the workspace (reads the cache
+    only; may run on another stream while the chunk's attention reads the cache)."""
+    H = shape.heads
+    _contig(scores, "scores", torch.float32, (H, shape.nq, shape.slots))
+    _dev(workspace, "workspace", torch.uint8)
+    cc = cache.c()
+    _check("pbsa_memory_select", lib().pbsa_memory_select(
+        ctypes.byref(shape.c()), _ptr(scores), ctypes.byref(cc), _ptr(workspace),
+        workspace.numel(), _stream()))
+
+
+def pbsa_memory_apply(shape: Shape, cache: Cache, chunk_k, chunk_v, chunk_rep, workspace):
+    """Second half of pbsa_memory_update: writes the workspace's selection and the chunk into
+    the cache and advances cache.chunk_index."""
+    H, d, T = shape.heads, shape.head_dim, shape.chunk_tokens
+    kt = _tok(chunk_k, "chunk_k", T, H, d)
+    vt = _tok(chunk_v, "chunk_v", T, H, d)
+    if chunk_rep is not None:
+        _contig(chunk_rep, "chunk_rep", torch.float32, (H, shape.nq, d))
+    _dev(workspace, "workspace", torch.uint8)
+    cc = cache.c()
+    _check("pbsa_memory_apply", lib().pbsa_memory_apply(
+        ctypes.byref(shape.c()), ctypes.byref(cc), kt, vt, _ptr(chunk_rep), _ptr(workspace),
+        workspace.numel(), _stream()))
     cache.chunk_index = cc.chunk_index
 
 

@@ -5,6 +5,10 @@ Per chunk (Sparse Forcing, gist.science, 2.C):
     route(q, cache) -> q_rep, scores, sel  (pool of q, scores, top-K in one launch);
     attn_fwd(q, cache, k, v, sel) -> o, lse;
     memory_update(scores, cache, k, v) (which pools k into the cache's representatives).
+`step(..., overlap=True)` runs the memory update's selection (which only reads the cache
+and the scores) on a second stream while the attention reads the cache, and its apply half
+after both; on the GPU this hides the selection, but from Python the two extra stream
+synchronisations cost about what it saves, so the default is the plain sequence.
 With several denoising passes per chunk the persistent memory is shared: only the last
 pass (the one whose K/V enter the cache) calls memory_update.
 """
@@ -27,6 +31,7 @@ class PersistentLayer:
         self.lse = torch.empty(H, T, dtype=torch.float32, device=device)
         nbytes = ops.pbsa_workspace_bytes(shape, ops.PBSA_OP_MEMORY_UPDATE)
         self.workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+        self.side = torch.cuda.Stream(device=device)  # default priority
 
     def reset(self):
         ops.pbsa_cache_reset(self.shape, self.cache)
@@ -41,12 +46,25 @@ class PersistentLayer:
         s = self.shape
         ops.pbsa_memory_update(s, self.scores, self.cache, k, v, None, self.workspace)
 
-    def step(self, q, k, v, attend=True):
-        """One chunk: route, attend (optional), update the memory and append the chunk."""
+    def step(self, q, k, v, attend=True, overlap=False):
+        """One chunk: route, attend (optional), update the memory and append the chunk.
+        overlap: the memory selection runs on the side stream beside the attention."""
         self.route(q)
-        if attend:
-            self.attend(q, k, v)
-        self.update(k, v)
+        if not overlap:
+            if attend:
+                self.attend(q, k, v)
+            self.update(k, v)
+            return
+        if not attend:
+            self.update(k, v)
+            return
+        main = torch.cuda.current_stream()
+        self.side.wait_stream(main)            # the scores of this chunk are complete
+        with torch.cuda.stream(self.side):
+            ops.pbsa_memory_select(self.shape, self.scores, self.cache, self.workspace)
+        self.attend(q, k, v)
+        main.wait_stream(self.side)            # selection done; attention done (same stream)
+        ops.pbsa_memory_apply(self.shape, self.cache, k, v, None, self.workspace)
 
 
 class TwoLevelClip:

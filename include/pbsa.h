@@ -192,6 +192,24 @@ pbsa_status pbsa_memory_update(const pbsa_dims* dims, const float* scores, pbsa_
                                pbsa_tensor chunk_k, pbsa_tensor chunk_v, const float* chunk_rep,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/* The two halves of pbsa_memory_update, for callers that overlap the selection with the
+ * chunk's attention; select then apply on the same cache state and workspace give exactly
+ * the result of pbsa_memory_update.
+ * pbsa_memory_select: the candidate scores, the new P_t and the copy list, written to the
+ *   workspace only; it reads the cache (block_id, len, chunk_index) and `scores`, and
+ *   writes nothing the attention reads, so it may run on another stream while
+ *   pbsa_attn_fwd of the same chunk reads the cache (after `scores` are complete).
+ * pbsa_memory_apply: writes the new P_t, the promotion copies and the chunk into the cache
+ *   from that workspace (it must follow the select and every reader of the cache), then
+ *   increments cache->chunk_index (host).  Errors as pbsa_memory_update; the workspace
+ *   must hold a select of the same cache state and chunk_index. */
+pbsa_status pbsa_memory_select(const pbsa_dims* dims, const float* scores,
+                               const pbsa_cache* cache, void* workspace, size_t workspace_bytes,
+                               void* stream);
+pbsa_status pbsa_memory_apply(const pbsa_dims* dims, pbsa_cache* cache, pbsa_tensor chunk_k,
+                              pbsa_tensor chunk_v, const float* chunk_rep, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
 /* ---- trainable path: two-level selection ---------------------------------------------
  * Light Forcing, hierarchical sparse attention (steps 2 and 3) with the chunk-aware
  * budget.  A clip of `chunks` chunks (chunk_frames frames each) is processed as one

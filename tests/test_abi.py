@@ -86,7 +86,10 @@ def test_null_dims_and_sizes():
     assert L.pbsa_check_dims(None, 0) == 1
     assert L.pbsa_cache_slots(ctypes.byref(_dims())) == 64 + 6 * 25
     assert L.pbsa_cache_slots(ctypes.byref(_dims(head_dim=3))) == 0
-    assert ops.pbsa_workspace_bytes(WAN, ops.PBSA_OP_MEMORY_UPDATE) == 4 * 12 * 75
+    # copy list [H][F*nb] then the new persistent table [H][C] twice, 256-byte pieces
+    up = lambda x: (x + 255) // 256 * 256
+    assert ops.pbsa_workspace_bytes(WAN, ops.PBSA_OP_MEMORY_UPDATE) == (
+        up(4 * 12 * 75) + 2 * up(4 * 12 * 64))
     assert ops.pbsa_workspace_bytes(WAN, ops.PBSA_OP_ATTN_BWD, 8, 75) > 12 * 600 * 600 * 4
     assert ops.pbsa_workspace_bytes(WAN, 77) == 0
 
@@ -117,7 +120,13 @@ def test_calls_reject_bad_arguments_before_launching():
     cache = ops.CacheC(16, 16, 16, 16, 16, 0)
     st = L.pbsa_memory_update(d, ctypes.c_void_p(16), ctypes.byref(cache), _tensor(16),
                               _tensor(16), ctypes.c_void_p(16), ctypes.c_void_p(16), 8, None)
-    assert st == 5 and b"3600" in L.pbsa_last_error()
+    assert st == 5 and b"9984" in L.pbsa_last_error()
+    assert cache.chunk_index == 0
+    # its two halves check the same workspace; a failed apply leaves chunk_index alone
+    assert L.pbsa_memory_select(d, ctypes.c_void_p(16), ctypes.byref(cache), ctypes.c_void_p(16),
+                                8, None) == 5
+    assert L.pbsa_memory_apply(d, ctypes.byref(cache), _tensor(16), _tensor(16),
+                               ctypes.c_void_p(16), ctypes.c_void_p(16), 8, None) == 5
     assert cache.chunk_index == 0
     # two-level: budget above max_sel, too many chunks
     ks = (ctypes.c_int32 * 8)(0, 8, 12, 16, 20, 24, 28, 80)

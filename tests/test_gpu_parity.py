@@ -539,3 +539,31 @@ def test_head_major_inputs_give_identical_training_results():
                     + [clip.lse.clone()])
     for a, b in zip(*outs):
         assert torch.equal(a, b)
+
+
+def test_overlapped_step_equals_sequential_calls():
+    """PersistentLayer.step(overlap=True) runs the memory selection (pbsa_memory_select,
+    256 threads) on a second stream beside the attention and applies it after
+    (pbsa_memory_apply); over a rollout its outputs and cache must be bit-identical to
+    route, attention and pbsa_memory_update (1024-thread selection) in sequence."""
+    wl = synth.WORKLOADS["wan_5s"]
+    shape = shape_of(wl)
+    seed = synth.SEEDS["wan_5s"]
+    a, b = runtime.PersistentLayer(shape), runtime.PersistentLayer(shape)
+    a.reset()
+    b.reset()
+    for c in range(wl.measured_chunk + 2):
+        say(f"[overlap] chunk {c}")
+        q, k, v = (dev(x) for x in synth.chunk_qkv(wl, seed, c))
+        a.step(q, k, v, overlap=True)
+        b.route(q)
+        b.attend(q, k, v)
+        b.update(k, v)
+        torch.cuda.synchronize()
+        assert a.cache.chunk_index == b.cache.chunk_index == c + 1
+        assert torch.equal(a.o.view(torch.int16), b.o.view(torch.int16))
+        assert torch.equal(a.lse, b.lse)
+        for name in ("block_id", "len", "rep"):
+            assert torch.equal(getattr(a.cache, name), getattr(b.cache, name)), name
+        assert torch.equal(a.cache.k.view(torch.int16), b.cache.k.view(torch.int16))
+        assert torch.equal(a.cache.v.view(torch.int16), b.cache.v.view(torch.int16))
