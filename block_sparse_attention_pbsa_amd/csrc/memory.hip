@@ -255,7 +255,9 @@ __global__ void __launch_bounds__(256) memory_copy_kernel(MemArgs a, TokIn xk, T
   constexpr int CH = D / 8;                 // 16-byte chunks per row
   constexpr int PER = kBlock * CH / 256;    // chunks per thread
   const int dst = a.copy_dst[static_cast<int64_t>(h) * a.F * a.nb + b];
-  if (dst >= 0) {
+  // (a persistent slot or -1; checked so that a workspace that holds no selection of this
+  // cache cannot send the copy outside the persistent slots)
+  if (dst >= 0 && dst < a.C) {
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
       const int q = t + 256 * p;

@@ -202,7 +202,8 @@ pbsa_status pbsa_memory_update(const pbsa_dims* dims, const float* scores, pbsa_
  * pbsa_memory_apply: writes the new P_t, the promotion copies and the chunk into the cache
  *   from that workspace (it must follow the select and every reader of the cache), then
  *   increments cache->chunk_index (host).  Errors as pbsa_memory_update; the workspace
- *   must hold a select of the same cache state and chunk_index. */
+ *   must hold a select of the same cache state and chunk_index (otherwise the cache's
+ *   contents are undefined, though every write stays inside the cache). */
 pbsa_status pbsa_memory_select(const pbsa_dims* dims, const float* scores,
                                const pbsa_cache* cache, void* workspace, size_t workspace_bytes,
                                void* stream);
