@@ -63,6 +63,20 @@ struct Half {
 };
 
 
+// 16 bytes per lane from a buffer straight into LDS (lane l writes lds + 1024 i + 16 l):
+// piece i (0..3) of a run that shares one LDS base; the instruction's immediate offset
+// 1024 i is added to both the global and the LDS address, so voff must already be lowered
+// by it.
+__device__ __forceinline__ void dma_piece(int i, __amdgpu_buffer_rsrc_t rs, uint32_t voff,
+                                          char* lds) {
+  switch (i) {
+    case 0: __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds, 16, voff, 0, 0, 0); break;
+    case 1: __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds, 16, voff, 0, 1024, 0); break;
+    case 2: __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds, 16, voff, 0, 2048, 0); break;
+    default: __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds, 16, voff, 0, 3072, 0); break;
+  }
+}
+
 // Element t of an fp32 row of n valid values from p (p wave-uniform); 0 past n.
 __device__ __forceinline__ float load_row_f32(const float* p, int n, int t) {
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
@@ -87,12 +101,20 @@ template <int D>
 __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
   constexpr int NS = D / 16, ND = D / 32;
   constexpr int HT = 32 * Lds<D>::RS;
-  __shared__ __attribute__((aligned(16))) uint16_t KsX[HT];
-  __shared__ __attribute__((aligned(16))) uint16_t VsX[HT];
-  __shared__ __attribute__((aligned(16))) uint16_t KsY[HT];
-  __shared__ __attribute__((aligned(16))) uint16_t VsY[HT];
+  // K and V half tiles of X and Y; head_dim 128 has a second set, gathered a step ahead
+  // (two arrays rather than one indexed at run time, so that the compiler sees that the
+  // reads of one set never touch the gathers in flight into the other)
+  __shared__ __attribute__((aligned(1024))) uint16_t tiles0[4 * HT];
+  __shared__ __attribute__((aligned(1024))) uint16_t tiles1[D == 128 ? 4 * HT : 8];
+  uint16_t* KsX = tiles0;
+  uint16_t* VsX = tiles0 + HT;
+  uint16_t* KsY = tiles0 + 2 * HT;
+  uint16_t* VsY = tiles0 + 3 * HT;
   // A's and B's selected blocks as (first token | valid rows << 24), staged once
-  __shared__ uint32_t lstA[kAttnListCap / 2], lstB[kAttnListCap / 2];
+  constexpr int kHalfCap = kAttnListCap / 2;
+  __shared__ uint32_t lst[kAttnListCap];
+  uint32_t* lstA = lst;
+  uint32_t* lstB = lst + kHalfCap;
 
   const int per = gridDim.x / 8;
   const int L = static_cast<int>(blockIdx.x % 8) * per + static_cast<int>(blockIdx.x / 8);
@@ -165,65 +187,136 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
     if (j < cntB) half_ref(lstB[j], half, ky, vy);
   };
 
-  Tile<D, 256, 32> tkx, tvx, tky, tvy;
-  Half kx, vx, ky, vy;
   const uint32_t kstride_b = static_cast<uint32_t>(2 * a.kts);
   const uint32_t vstride_b = static_cast<uint32_t>(2 * a.vts);
-  if (nsteps > 0) {
-    refs(0, kx, vx, ky, vy);
-    tkx.load(kx.p, kstride_b, kx.len, t);
-    tvx.load(vx.p, vstride_b, vx.len, t);
-    tky.load(ky.p, kstride_b, ky.len, t);
-    tvy.load(vy.p, vstride_b, vy.len, t);
+  // This lane's transposing-read offsets, opaque to the optimizer: it would otherwise split
+  // each read's address into a chain of steps too long for the compiler to still see which
+  // LDS array the read is from, and make the read wait for every gather in flight.
+  int trlo[ND], trhi[ND];
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt) {
+    tr_offsets<D>(dt, l, trlo[dt], trhi[dt]);
+    asm("" : "+v"(trlo[dt]), "+v"(trhi[dt]));
   }
-  for (int s = 0; s < nsteps; ++s) {
-    __syncthreads();
-    tkx.store_rows(KsX, t);
-    tvx.store_rows(VsX, t);
-    tky.store_rows(KsY, t);
-    tvy.store_rows(VsY, t);
-    const int lenX = kx.len, lenY = ky.len;
-    __syncthreads();
-    if (s + 1 < nsteps) {
-      refs(s + 1, kx, vx, ky, vy);
+  // this wave's rows against one K/V half tile of len keys: K at set + kb, V at set + kb + HT
+  // (offsets from the LDS array itself, so that the compiler can tell these reads from the
+  // gathers in flight into the other set)
+  auto half_step = [&](const uint16_t* set, int kb, int len) {
+    const int vb = kb + HT;
+    u32x4 op[NS];
+    f32x16 sacc[1], pacc = {};
+    sacc[0] = f32x16{};
+#pragma unroll
+    for (int st = 0; st < NS; ++st) op[st] = rd_rows<D>(set, 0, st, c32, h2, kb);
+#pragma unroll
+    for (int st = 0; st < NS; ++st) sacc[0] = mfma32(op[st], qreg[st], sacc[0]);
+#pragma unroll
+    for (int st = 0; st < NS; ++st) op[st] = rd_rows<D>(set, 0, st, c32, h2, vb);
+#pragma unroll
+    for (int st = 0; st < NS; ++st) pacc = mfma32(op[st], dreg[st], pacc);
+    // dS^T = P^T * (dP^T - D); keys past the block length contribute nothing
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      const float p = acc_row(rr, h2) < len
+                          ? __builtin_amdgcn_exp2f(fmaf(sacc[0][rr], c, -lse2))
+                          : 0.f;
+      sacc[0][rr] = p * (pacc[rr] - dsum);
+    }
+    // dQ^T += K^T dS^T (K channel-major through the transposing read)
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      u32x4 kop[ND];
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt)
+        kop[dt] = rd_tr(set, kb + trlo[dt] + 16 * t2 * Lds<D>::RS,
+                        kb + trhi[dt] + 16 * t2 * Lds<D>::RS);
+      const u32x4 sb = pack_step(sacc, t2);
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) acc[dt] = mfma32(kop[dt], sb, acc[dt]);
+    }
+  };
+
+  if constexpr (D == 128) {
+    // Gathers straight into LDS (buffer loads with an LDS destination), one step ahead into
+    // the other set: wave w fills tile w of the step (K of X, V of X, K of Y, V of Y) as
+    // eight 1 KB pieces of four rows.  Lane l of piece i writes LDS bytes 1024 i + 16 l of
+    // the tile, i.e. row 4 i + l / 16 at chunk position l % 16, which holds logical chunk
+    // (l % 16) ^ swz(row) of the swizzled row-major layout.  Rows past the valid length
+    // re-read the last valid row (finite data that a zero probability removes); an empty
+    // half tile is not gathered, and no wave reads it.
+    auto gather = [&](int st, uint16_t* set) {
+      const int j = st >> 1, half = st & 1;
+      if (j >= (mine ? cntB : cntA)) return;
+      // (one list array indexed by mine, not a pointer chosen at run time: the compiler
+      // then still sees that this read cannot touch a gather in flight)
+      const uint32_t e = static_cast<uint32_t>(
+          __builtin_amdgcn_readfirstlane(static_cast<int>(lst[mine * kHalfCap + j])));
+      const int tl = static_cast<int>(e >> 24) - 32 * half;
+      const int len = tl < 0 ? 0 : (tl < 32 ? tl : 32);
+      if (len == 0) return;
+      const int64_t tk = (e & 0xffffffu) + 32 * half;
+      const uint32_t sb = (w & 1) ? vstride_b : kstride_b;
+      const char* p = (w & 1) ? reinterpret_cast<const char*>(vh + tk * a.vts)
+                              : reinterpret_cast<const char*>(kh + tk * a.kts);
+      // scalar base 3 KB below the half tile: lane offsets lowered by a piece's immediate
+      // offset (up to 3 KB) stay non-negative
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<char*>(p - 3072), 0, 0x7fffffff, 0x00020000);
+      char* dst = reinterpret_cast<char*>(set + w * HT);
+      const uint32_t q = static_cast<uint32_t>(l >> 4);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t row = 4 * i + q;
+        const uint32_t rc = row < static_cast<uint32_t>(len) ? row : len - 1;
+        const uint32_t cch = static_cast<uint32_t>(l & 15) ^ (4 * q + (i & 3));
+        const uint32_t voff = 3072 + rc * sb + 16 * cch - 1024 * (i & 3);
+        dma_piece(i & 3, rs, voff, dst + 4096 * (i >> 2));
+      }
+    };
+    // step st: its tiles are in `cur`; the next step's go into `nxt`
+    auto run = [&](int st, const uint16_t* cur, uint16_t* nxt) {
+      // (the barrier waits for this wave's gathers too) step st's tiles have landed, and
+      // every wave is done with the set step st - 1 read
+      __syncthreads();
+      if (st + 1 < nsteps) gather(st + 1, nxt);
+      Half kx, vx, ky, vy;
+      refs(st, kx, vx, ky, vy);
+      const int len = mine ? ky.len : kx.len;
+      if (qlen > 0 && len > 0) half_step(cur, 2 * mine * HT, len);
+    };
+    if (nsteps > 0) gather(0, tiles0);
+    // nsteps is even (two halves per block)
+    for (int st = 0; st < nsteps; st += 2) {
+      run(st, tiles0, tiles1);
+      run(st + 1, tiles1, tiles0);
+    }
+  } else {
+    Tile<D, 256, 32> tkx, tvx, tky, tvy;
+    Half kx, vx, ky, vy;
+    if (nsteps > 0) {
+      refs(0, kx, vx, ky, vy);
       tkx.load(kx.p, kstride_b, kx.len, t);
       tvx.load(vx.p, vstride_b, vx.len, t);
       tky.load(ky.p, kstride_b, ky.len, t);
       tvy.load(vy.p, vstride_b, vy.len, t);
     }
-    const int len = mine ? lenY : lenX;
-    if (qlen > 0 && len > 0) {
-      const uint16_t* Ks = mine ? KsY : KsX;
-      const uint16_t* Vs = mine ? VsY : VsX;
-      u32x4 op[NS];
-      f32x16 sacc[1], pacc = {};
-      sacc[0] = f32x16{};
-#pragma unroll
-      for (int st = 0; st < NS; ++st) op[st] = rd_rows<D>(Ks, 0, st, c32, h2);
-#pragma unroll
-      for (int st = 0; st < NS; ++st) sacc[0] = mfma32(op[st], qreg[st], sacc[0]);
-#pragma unroll
-      for (int st = 0; st < NS; ++st) op[st] = rd_rows<D>(Vs, 0, st, c32, h2);
-#pragma unroll
-      for (int st = 0; st < NS; ++st) pacc = mfma32(op[st], dreg[st], pacc);
-      // dS^T = P^T * (dP^T - D); keys past the block length contribute nothing
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const float p = acc_row(rr, h2) < len
-                            ? __builtin_amdgcn_exp2f(fmaf(sacc[0][rr], c, -lse2))
-                            : 0.f;
-        sacc[0][rr] = p * (pacc[rr] - dsum);
+    for (int st = 0; st < nsteps; ++st) {
+      __syncthreads();
+      tkx.store_rows(KsX, t);
+      tvx.store_rows(VsX, t);
+      tky.store_rows(KsY, t);
+      tvy.store_rows(VsY, t);
+      const int lenX = kx.len, lenY = ky.len;
+      __syncthreads();
+      if (st + 1 < nsteps) {
+        refs(st + 1, kx, vx, ky, vy);
+        tkx.load(kx.p, kstride_b, kx.len, t);
+        tvx.load(vx.p, vstride_b, vx.len, t);
+        tky.load(ky.p, kstride_b, ky.len, t);
+        tvy.load(vy.p, vstride_b, vy.len, t);
       }
-      // dQ^T += K^T dS^T (K channel-major through the transposing read)
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        u32x4 kop[ND];
-#pragma unroll
-        for (int dt = 0; dt < ND; ++dt) kop[dt] = rd_rows_tr<D>(Ks, dt, t2, l);
-        const u32x4 sb = pack_step(sacc, t2);
-#pragma unroll
-        for (int dt = 0; dt < ND; ++dt) acc[dt] = mfma32(kop[dt], sb, acc[dt]);
-      }
+      const int len = mine ? lenY : lenX;
+      if (qlen > 0 && len > 0) half_step(tiles0, 2 * mine * HT, len);
     }
   }
   if (qrow < qlen) {
