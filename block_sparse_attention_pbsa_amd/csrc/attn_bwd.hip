@@ -77,6 +77,25 @@ __device__ __forceinline__ void dma_piece(int i, __amdgpu_buffer_rsrc_t rs, uint
   }
 }
 
+// The transposing read of rd_rows_tr split into this lane's two element offsets for k-step
+// 0 (lo: rows 0..3 of its group, hi: rows 8..11) and the read itself; k-step t4 adds 16 t4
+// rows to both (swz(r) depends on r % 16 only).
+template <int D>
+__device__ __forceinline__ void tr_offsets(int dt, int l, int& lo, int& hi) {
+  const int g = l >> 4, i = l & 15;
+  const int ch = 32 * dt + 16 * (g & 1) + 4 * (i & 3);
+  const int row = 4 * (g >> 1) + (i >> 2);
+  lo = Lds<D>::chunk(row, ch >> 3) + (ch & 4);
+  hi = Lds<D>::chunk(row + 8, ch >> 3) + (ch & 4);
+}
+__device__ __forceinline__ u32x4 rd_tr(const uint16_t* lds, int lo, int hi) {
+  lds_u16* p = (lds_u16*)(lds);
+  const s16x4_ a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + lo));
+  const s16x4_ b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + hi));
+  const u32x2 x = __builtin_bit_cast(u32x2, a), y = __builtin_bit_cast(u32x2, b);
+  return u32x4{x[0], x[1], y[0], y[1]};
+}
+
 // Element t of an fp32 row of n valid values from p (p wave-uniform); 0 past n.
 __device__ __forceinline__ float load_row_f32(const float* p, int n, int t) {
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
@@ -207,11 +226,11 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
     f32x16 sacc[1], pacc = {};
     sacc[0] = f32x16{};
 #pragma unroll
-    for (int st = 0; st < NS; ++st) op[st] = rd_rows<D>(set, 0, st, c32, h2, kb);
+    for (int st = 0; st < NS; ++st) op[st] = rd_rows<D>(set + kb, 0, st, c32, h2);
 #pragma unroll
     for (int st = 0; st < NS; ++st) sacc[0] = mfma32(op[st], qreg[st], sacc[0]);
 #pragma unroll
-    for (int st = 0; st < NS; ++st) op[st] = rd_rows<D>(set, 0, st, c32, h2, vb);
+    for (int st = 0; st < NS; ++st) op[st] = rd_rows<D>(set + vb, 0, st, c32, h2);
 #pragma unroll
     for (int st = 0; st < NS; ++st) pacc = mfma32(op[st], dreg[st], pacc);
     // dS^T = P^T * (dP^T - D); keys past the block length contribute nothing

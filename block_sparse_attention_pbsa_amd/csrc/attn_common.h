@@ -74,12 +74,9 @@ struct Tile {
 // MFMA operand reads from LDS for a wave whose lane l has half h2 = l / 32, c32 = l % 32.
 // Row-major tile, rows 32*tile + c32, contraction over channels (k-step s: channels
 // 16s + 8*h2 + [0, 8)).
-// (base: an element offset added to lds in the same index, so that the read's address stays
-// one step from lds)
 template <int D>
-__device__ __forceinline__ u32x4 rd_rows(const uint16_t* lds, int tile, int s, int c32, int h2,
-                                         int base = 0) {
-  return *reinterpret_cast<const u32x4*>(lds + (base + Lds<D>::chunk(32 * tile + c32, 2 * s + h2)));
+__device__ __forceinline__ u32x4 rd_rows(const uint16_t* lds, int tile, int s, int c32, int h2) {
+  return *reinterpret_cast<const u32x4*>(lds + Lds<D>::chunk(32 * tile + c32, 2 * s + h2));
 }
 // Channel-major view of a ROW-major tile through gfx950's transposing LDS read
 // (ds_read_b64_tr_b16).  Within each 16-lane group the instruction returns to lane i the
@@ -105,25 +102,6 @@ __device__ __forceinline__ u32x4 rd_rows_tr(const uint16_t* lds, int dt, int t4,
   const s16x4_ hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + off_hi));
   const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
   return u32x4{a[0], a[1], b[0], b[1]};
-}
-
-// The same read split into this lane's two element offsets for k-step 0 (lo: rows 0..3 of
-// its group, hi: rows 8..11) and the read itself; k-step t4 adds 16 t4 rows to both
-// (swz(r) depends on r % 16 only).
-template <int D>
-__device__ __forceinline__ void tr_offsets(int dt, int l, int& lo, int& hi) {
-  const int g = l >> 4, i = l & 15;
-  const int ch = 32 * dt + 16 * (g & 1) + 4 * (i & 3);
-  const int row = 4 * (g >> 1) + (i >> 2);
-  lo = Lds<D>::chunk(row, ch >> 3) + (ch & 4);
-  hi = Lds<D>::chunk(row + 8, ch >> 3) + (ch & 4);
-}
-__device__ __forceinline__ u32x4 rd_tr(const uint16_t* lds, int lo, int hi) {
-  lds_u16* p = (lds_u16*)(lds);
-  const s16x4_ a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + lo));
-  const s16x4_ b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + hi));
-  const u32x2 x = __builtin_bit_cast(u32x2, a), y = __builtin_bit_cast(u32x2, b);
-  return u32x4{x[0], x[1], y[0], y[1]};
 }
 
 // B/A operand from two 32-row accumulator tiles: k-step t4 (16 rows) packed to bf16 in the
