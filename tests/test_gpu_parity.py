@@ -477,6 +477,14 @@ def test_two_level_small_d64_full_gradients():
     two_level_check(wl, 32)
 
 
+def test_two_level_small_ragged_second_half_full_gradients():
+    # 100-token frames: one full block and a 36-token tail, so the tail's second 32-key
+    # half tile holds 4 rows (head_dim 128, the gathered dQ path)
+    wl = synth.Workload("train_small_r", 2, 128, 64, 100, 2, 0, 0, 0, 0, 3, clip_chunks=3,
+                        top_frames=1)
+    two_level_check(wl, 33)
+
+
 def test_two_level_wan_train_sampled():
     wl = synth.WORKLOADS["wan_train"]
 
