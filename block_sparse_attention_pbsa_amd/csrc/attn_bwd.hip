@@ -12,8 +12,9 @@
 //                half tiles, recomputes S^T = K Q^T and dP^T = V dO^T on MFMA (Q, dO in
 //                registers) and accumulates dQ^T = K^T dS^T, reading K channel-major with
 //                the transposing LDS read.  It also writes D for its rows.
-//   inverse   -- one workgroup per (KV block, head): lists, in ascending order, the query
-//                blocks that selected the KV block (binary search in their sorted lists).
+//   inverse   -- the query blocks that selected each KV block, in ascending order: every
+//                query block sets its bit in a bitmap row per selected KV block, then one
+//                workgroup per (KV block, head) turns its row into the list.
 //   plan      -- one workgroup: cuts every inverse list into work items of at most
 //                kSplitQ query blocks (a few KV blocks are selected by every query block,
 //                most by a few dozen), numbering items and partial-sum slots by prefix sums.
@@ -354,38 +355,70 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
 
 // ------------------------------------------------------------------ inverse lists
 // grid (nq, H), 256 threads: inv[h][g] = ascending query blocks whose list holds g.
-__global__ void __launch_bounds__(256) attn_bwd_inverse_kernel(BwdArgs a) {
-  __shared__ int wave_cnt[4];
+// The inverse lists go through bitmaps: bit r of row (h, g) is set when query block r of
+// head h selected KV block g.  A row's W = ceil(nq / 32) words sit in the tail of that row's
+// own inverse list, which the list pass reads whole before writing the list over it.
+__global__ void __launch_bounds__(256) attn_bwd_bits_clear_kernel(BwdArgs a) {
+  const int W = (a.nq + 31) >> 5;
+  const int64_t n = static_cast<int64_t>(a.H) * a.nq * W;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t row = i / W;
+    a.inv[row * a.nq + (a.nq - W) + (i - row * W)] = 0;
+  }
+}
+
+// one workgroup per (query block, head): sets the query block's bit in the row of every
+// KV block it selected (a query block of chunk i sees frames < F*i only; other entries,
+// like ids outside the clip, are not listed)
+__global__ void __launch_bounds__(128) attn_bwd_bits_set_kernel(BwdArgs a) {
+  const int r = blockIdx.x, h = blockIdx.y;
+  const int W = (a.nq + 31) >> 5;
+  const int64_t hr = static_cast<int64_t>(h) * a.nq + r;
+  const int cnt = a.nsel[hr];
+  const int32_t* s = a.sel + hr * a.max_sel;
+  for (int j = threadIdx.x; j < cnt; j += 128) {
+    const int g = s[j];
+    if (g < 0 || g >= a.nq) continue;
+    const int f = g / a.nb;
+    if (r < (f / a.F) * a.F * a.nb) continue;
+    int32_t* row = a.inv + (static_cast<int64_t>(h) * a.nq + g) * a.nq + (a.nq - W);
+    atomicOr(reinterpret_cast<unsigned int*>(row + (r >> 5)), 1u << (r & 31));
+  }
+}
+
+// one workgroup per (KV block, head): the row's set bits in ascending order become its
+// inverse list (query blocks that selected the KV block) and count
+constexpr int kMaxBitWords = 2048;  // nq <= 65536
+__global__ void __launch_bounds__(256) attn_bwd_bits_list_kernel(BwdArgs a) {
+  __shared__ uint32_t bits[kMaxBitWords];
+  __shared__ int wsum[4];
   const int g = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
   const int w = t >> 6, l = t & 63;
-  // a query block of chunk i (1-based) sees frames < F*i, so frame f is first visible to
-  // chunk f/F + 1
-  const int f = g / a.nb;
-  const int r0 = (f / a.F) * a.F * a.nb;
+  const int W = (a.nq + 31) >> 5;
   int32_t* out = a.inv + (static_cast<int64_t>(h) * a.nq + g) * a.nq;
+  for (int j = t; j < W; j += 256) bits[j] = static_cast<uint32_t>(out[a.nq - W + j]);
+  __syncthreads();  // every word is read before the list overwrites the row's tail
   int total = 0;
-  for (int base = r0; base < a.nq; base += 256) {
-    const int r = base + t;
-    bool found = false;
-    if (r < a.nq) {
-      const int32_t* s = a.sel + (static_cast<int64_t>(h) * a.nq + r) * a.max_sel;
-      const int cnt = a.nsel[static_cast<int64_t>(h) * a.nq + r];
-      int lo = 0, hi = cnt;
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (s[mid] < g) lo = mid + 1;
-        else hi = mid;
-      }
-      found = lo < cnt && s[lo] == g;
+  for (int base = 0; base < W; base += 256) {
+    const int j = base + t;
+    uint32_t m = j < W ? bits[j] : 0u;
+    const int pc = __popc(m);
+    int x = pc;  // inclusive scan over the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o, 64);
+      if (l >= o) x += y;
     }
-    const unsigned long long m = __ballot(found);
-    const int below = __popcll(m & ((1ull << l) - 1ull));
-    if (l == 0) wave_cnt[w] = __popcll(m);
+    if (l == 63) wsum[w] = x;
     __syncthreads();
-    int off = total;
-    for (int u = 0; u < w; ++u) off += wave_cnt[u];
-    if (found) out[off + below] = r;
-    total += wave_cnt[0] + wave_cnt[1] + wave_cnt[2] + wave_cnt[3];
+    int off = total + x - pc;
+    for (int u = 0; u < w; ++u) off += wsum[u];
+    while (m) {
+      out[off++] = 32 * j + (__ffs(m) - 1);
+      m &= m - 1;
+    }
+    total += wsum[0] + wsum[1] + wsum[2] + wsum[3];
     __syncthreads();
   }
   if (t == 0) a.inv_cnt[static_cast<int64_t>(h) * a.nq + g] = total;
@@ -826,8 +859,16 @@ hipError_t launch_attn_bwd(const pbsa_dims& d, int chunks, TokIn q, TokIn k, Tok
     hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, dim3(gq), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (nq > 32 * kMaxBitWords) return hipErrorInvalidValue;
+  {
+    const int64_t words = static_cast<int64_t>(d.heads) * nq * ((nq + 31) / 32);
+    const int64_t blocks = (words + 255) / 256;
+    const int gc = static_cast<int>(blocks < 2048 ? blocks : 2048);
+    hipLaunchKernelGGL(attn_bwd_bits_clear_kernel, dim3(gc), dim3(256), 0, s, a);
+  }
   dim3 grid(nq, d.heads);
-  hipLaunchKernelGGL(attn_bwd_inverse_kernel, grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL(attn_bwd_bits_set_kernel, grid, dim3(128), 0, s, a);
+  hipLaunchKernelGGL(attn_bwd_bits_list_kernel, grid, dim3(256), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_bwd_plan_kernel, dim3(1), dim3(1024), 0, s, a);
