@@ -248,6 +248,115 @@ def test_memory_update_brute_force_and_invariants(seed):
         assert set(newP) == set(P) | set(E)
 
 
+
+def _dominates(col_a, col_b):
+    """Column a scores at least as high as column b for every query block, higher for one."""
+    return bool(np.all(col_a >= col_b) and np.any(col_a > col_b))
+
+
+def _check_dominance(P, sinks, sP, E, sE, newP):
+    """No candidate is dropped while a candidate it dominates is kept."""
+    cols = {g: sP[:, i] for i, g in enumerate(P) if g not in sinks}
+    cols.update({g: sE[:, i] for i, g in enumerate(E)})
+    kept = set(newP)
+    for a, ca in cols.items():
+        for b, cb in cols.items():
+            if a != b and _dominates(ca, cb):
+                assert not (b in kept and a not in kept), (a, b)
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_memory_update_respects_score_dominance(seed):
+    # Sparse Forcing 2.C "Dynamic Update": the blocks the chunk's queries score highest are
+    # the ones promoted.  Whatever the aggregate over query blocks, a candidate that every
+    # query block scores at least as high as another (and one strictly higher) is at least
+    # as important, and strictly so: it is never dropped while the other is kept.  Query
+    # blocks are at least as many as candidates, so that a sum over the wrong axis still
+    # runs (and must fail here), and each case plants dominance pairs.
+    rs = np.random.default_rng(500 + seed)
+    S = int(rs.integers(0, 3))
+    sinks = list(range(S))
+    nP = int(rs.integers(1, 6))
+    P = sinks + sorted(rs.choice(np.arange(S, 40), size=nP, replace=False).tolist())
+    E = sorted(rs.choice(np.arange(40, 70), size=int(rs.integers(1, 6)), replace=False).tolist())
+    C = S + int(rs.integers(1, nP + len(E)))
+    ncand = nP + len(E)
+    Nq = ncand + int(rs.integers(0, 4))
+    sP = rs.integers(-3, 4, size=(Nq, len(P))).astype(float)
+    sE = rs.integers(-3, 4, size=(Nq, len(E))).astype(float)
+    # plant: a few candidates are copies of another plus non-negative bumps (one positive)
+    cand = [(0, i) for i, g in enumerate(P) if g >= S] + [(1, i) for i in range(len(E))]
+    for _ in range(3):
+        (ta, ia), (tb, ib) = (cand[j] for j in rs.choice(len(cand), size=2, replace=False))
+        src = (sP, sE)[tb][:, ib]
+        bump = rs.integers(0, 2, size=Nq).astype(float)
+        bump[rs.integers(0, Nq)] = 1.0
+        (sP, sE)[ta][:, ia] = src + bump
+    newP = orc.memory_update(P, sinks, sP, E, sE, C)
+    _check_dominance(P, sinks, sP, E, sE, newP)
+    # the sinks' own scores never matter
+    sP2 = sP.copy()
+    sP2[:, :S] = rs.integers(-100, 100, size=(Nq, S))
+    assert orc.memory_update(P, sinks, sP2, E, sE, C) == newP
+
+
+def test_memory_update_strict_dominance_breaks_equal_maxima():
+    # Two candidates with the same best score over the query blocks; the higher id one is
+    # scored higher by the other query blocks.  Only one place is free: it must go to the
+    # dominating candidate, even though the tie rule favours the lower id when only the
+    # best query block is looked at.
+    P, sinks = [0, 5], [0]
+    E = [9]
+    sP = np.array([[7.0, 4.0], [0.0, 1.0], [0.0, 1.0]])   # sink 0, block 5
+    sE = np.array([[4.0], [2.0], [3.0]])                     # block 9: >= block 5 everywhere
+    assert orc.memory_update(P, sinks, sP, E, sE, 2) == [0, 9]
+    # and with the roles swapped the lower id wins
+    assert orc.memory_update([0, 9], sinks, np.array([[7.0, 4.0], [0.0, 2.0], [0.0, 3.0]]), [5],
+                             np.array([[4.0], [1.0], [1.0]]), 2) == [0, 9]
+
+
+def test_memory_scores_are_column_aggregates_of_the_chunk():
+    # Orientation: the memory score of a candidate depends on its own column only (the
+    # scores all query blocks give that candidate), never on other candidates' columns,
+    # and reordering the chunk's query blocks changes nothing.
+    rs = np.random.default_rng(9)
+    P, sinks, E = [0, 3, 8, 12], [0], [20, 21, 22]
+    Nq = 6
+    sP, sE = rs.standard_normal((Nq, 4)), rs.standard_normal((Nq, 3))
+    ids, m = orc.memory_scores(P, sinks, sP, E, sE)
+    assert ids == [3, 8, 12, 20, 21, 22]
+    perm = rs.permutation(Nq)
+    _, m_perm = orc.memory_scores(P, sinks, sP[perm], E, sE[perm])
+    np.testing.assert_allclose(m_perm, m, atol=1e-14, rtol=0)
+    sP3 = sP.copy()
+    sP3[:, 2] += 5.0      # only block 8's column changes
+    _, m3 = orc.memory_scores(P, sinks, sP3, E, sE)
+    changed = [i for i in range(len(ids)) if m3[i] != m[i]]
+    assert changed == [1] and m3[1] > m[1]
+
+
+def test_rollout_updates_respect_score_dominance():
+    # the same dominance check on the candidates of every update of a small rollout (six
+    # query blocks per chunk, so dominance pairs do occur among the real candidates)
+    wl = synth.Workload("dom", 1, 16, 8, 24, 2, 16, 4, 4, 1, 3)
+    sch = orc.Schedule(wl.frame_tokens, wl.block, wl.chunk_frames, wl.window_frames,
+                       wl.capacity, wl.sinks, wl.topk, wl.scale)
+    ro = orc.PersistentRollout(sch, wl.head_dim)
+    pairs = 0
+    for c in range(wl.measured_chunk):
+        q, k, v = (a[:, 0] for a in synth.chunk_qkv(wl, 31, c))
+        routed = ro.select(q)
+        E = sch.evicted_blocks(ro.chunk)
+        col = {g: i for i, g in enumerate(routed["L"])}
+        sE = routed["scores_L"][:, [col[g] for g in E]] if E else np.zeros((len(q), 0))
+        before = list(ro.P)
+        ro.update(routed, k, v)
+        _check_dominance(before, list(range(sch.S)), routed["scores_P"], E, sE, ro.P)
+        cols = [routed["scores_P"][:, i] for i, g in enumerate(before) if g >= sch.S] + \
+            [sE[:, i] for i in range(len(E))]
+        pairs += sum(_dominates(a, b) for a in cols for b in cols if a is not b)
+    assert pairs > 0
+
 def _rollout(wl, seed, heads=(0,), chunks=None):
     sch = orc.Schedule(wl.frame_tokens, wl.block, wl.chunk_frames, wl.window_frames,
                        wl.capacity, wl.sinks, wl.topk, wl.scale)
