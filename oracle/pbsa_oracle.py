@@ -352,6 +352,40 @@ class PersistentRollout:
             o[idx], lse[idx] = oo, ll
         return o, lse
 
+    def attend_grad(self, q_chunk, k_chunk, v_chunk, sel, dout):
+        """Gradient of attend's output O (dout = dL/dO) with the selection held constant
+        ([SF] 2.D: training runs the same sparse cache as inference).
+
+        The keys are every block whose tokens are stored (P_t and the window) followed by
+        the chunk; each query block's allowed keys are those of attend; masked_attention_grad
+        gives the gradients.  Returns (dq [F*n, d], dk_chunk, dv_chunk [F*n, d],
+        dk_blocks, dv_blocks) where dk_blocks[g] / dv_blocks[g] are [len(g), d] for every
+        stored block g (zero for a block no query attends)."""
+        s = self.sch
+        stored = sorted(set(self.P) | set(s.window_blocks(self.chunk)))
+        Ks = [np.asarray(self.tok_k[g], np.float64) for g in stored] + [np.asarray(k_chunk, np.float64)]
+        Vs = [np.asarray(self.tok_v[g], np.float64) for g in stored] + [np.asarray(v_chunk, np.float64)]
+        K, V = np.concatenate(Ks), np.concatenate(Vs)
+        off, o = {}, 0
+        for g, kk in zip(stored, Ks):
+            off[g] = (o, o + kk.shape[0])
+            o += kk.shape[0]
+        base = self.chunk * s.F * s.nb
+        for b in range(s.F * s.nb):
+            a0, b0 = block_token_range(b, s.n, s.B)
+            off[base + b] = (o + a0, o + b0)
+        q = np.asarray(q_chunk, np.float64)
+        mask = np.zeros((q.shape[0], K.shape[0]), dtype=bool)
+        for r, allowed in enumerate(self.attended_blocks(sel)):
+            a, b = block_token_range(r, s.n, s.B)
+            for g in allowed:
+                ka, kb = off[g]
+                mask[a:b, ka:kb] = True
+        dq, dk, dv = masked_attention_grad(q, K, V, mask, s.scale, dout)
+        dk_blocks = {g: dk[off[g][0]:off[g][1]] for g in stored}
+        dv_blocks = {g: dv[off[g][0]:off[g][1]] for g in stored}
+        return dq, dk[o:], dv[o:], dk_blocks, dv_blocks
+
     def attend_dense(self, q_chunk, k_chunk, v_chunk, sel):
         """Parity form: dense attention over the whole history + chunk with the block mask
         (needs keep_history=True)."""

@@ -410,6 +410,57 @@ def test_full_selection_is_textbook_block_causal_attention():
         ro.update(routed, k, v)
 
 
+def test_persistent_gradient_with_full_selection_is_textbook_autograd():
+    # capacity and top-K keep every block: the gradient of the persistent-mode attention is
+    # the gradient of dense softmax attention over the whole history plus the chunk
+    wl = synth.Workload("fullg", 1, 8, 4, 12, 1, 4, 2, 100, 1, 100)
+    sch = orc.Schedule(wl.frame_tokens, wl.block, wl.chunk_frames, wl.window_frames,
+                       wl.capacity, wl.sinks, wl.topk, wl.scale)
+    ro = orc.PersistentRollout(sch, wl.head_dim)
+    Kc, Vc = [], []
+    rs = np.random.default_rng(4)
+    for c in range(wl.measured_chunk + 1):
+        q, k, v = (a[:, 0].astype(np.float64) for a in synth.chunk_qkv(wl, 12, c))
+        routed = ro.select(q)
+        if c == wl.measured_chunk:
+            do = rs.standard_normal(q.shape)
+            dq, dkc, dvc, dkb, dvb = ro.attend_grad(q, k, v, routed["sel"], do)
+            Kall, Vall = np.concatenate(Kc + [k]), np.concatenate(Vc + [v])
+            tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, Kall, Vall))
+            out = torch.nn.functional.scaled_dot_product_attention(
+                tq[None], tk[None], tv[None], scale=wl.scale)[0]
+            out.backward(torch.tensor(do))
+            np.testing.assert_allclose(dq, tq.grad.numpy(), atol=1e-12, rtol=0)
+            hist = c * sch.F * sch.n
+            np.testing.assert_allclose(dkc, tk.grad.numpy()[hist:], atol=1e-12, rtol=0)
+            np.testing.assert_allclose(dvc, tv.grad.numpy()[hist:], atol=1e-12, rtol=0)
+            assert sorted(dkb) == list(range(c * sch.F * sch.nb))
+            for g in dkb:
+                a, b = orc.block_token_range(g, sch.n, sch.B)
+                np.testing.assert_allclose(dkb[g], tk.grad.numpy()[a:b], atol=1e-12, rtol=0)
+                np.testing.assert_allclose(dvb[g], tv.grad.numpy()[a:b], atol=1e-12, rtol=0)
+        else:
+            ro.update(routed, k, v)
+            Kc.append(k)
+            Vc.append(v)
+
+
+def test_persistent_gradient_of_unattended_blocks_is_zero():
+    # a window block that no query block routes to gets no gradient; P blocks always do
+    wl = synth.WORKLOADS["tiny"]
+    sch, ros, (q, k, v, routed) = _rollout(wl, 6)
+    ro = ros[0]
+    sel = [row[:1] for row in routed["sel"]]   # one routed block per query block
+    do = np.random.default_rng(0).standard_normal((q.shape[0], wl.head_dim))
+    _, _, _, dkb, dvb = ro.attend_grad(q[:, 0], k[:, 0], v[:, 0], sel, do)
+    routed_any = {g for row in sel for g in row}
+    for g in sch.window_blocks(ro.chunk):
+        if g not in routed_any:
+            assert not dkb[g].any() and not dvb[g].any()
+    for g in ro.P:
+        assert np.abs(dvb[g]).sum() > 0
+
+
 def test_gathered_and_dense_masked_forms_agree():
     wl = synth.WORKLOADS["tiny"]
     sch, ros, (q, k, v, routed) = _rollout(wl, 5)
@@ -431,7 +482,7 @@ def test_planted_blocks_are_routed_and_retained():
                         segment_frames=6, q_align=2.0, kv_shift=6.0)
     seed = 21
     sch, ros, (q, k, v, routed_last) = _rollout(wl, seed, heads=(0, 1))
-    planted = set(synth.planted_blocks(wl, seed, wl.history_frames + wl.chunk_frames).tolist())
+    planted = set(synth.planted_blocks(wl, seed, wl.plant_frames).tolist())
     c = wl.measured_chunk
     win = set(sch.window_blocks(c))
     out_of_window = {g for g in planted if g < c * sch.F * sch.nb and g not in win}
