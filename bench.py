@@ -1,23 +1,31 @@
 """PBSA benchmark on one MI355X: ms per chunk of the persistent-mode hot path.
 
-One step = one chunk of one attention layer (one denoising pass) on the Wan2.1-1.3B-shaped
-5-second workload: 12 heads, head_dim 128, 1560-token frames, 3-frame chunks (4680
-queries), 21-frame history, 64-token blocks, capacity 64 (1 sink), window 6 frames,
-top-32:
-    pool(q) + score_topk + attn_fwd + memory_update (which pools k)
-on seeded synthetic bf16 inputs already resident in HBM.  The cache is bootstrapped by
-replaying the 7 history chunks; each timed step then feeds the measured chunk's tensors
-again, so the rollout keeps sliding with steady shapes.  The K timed steps run with no
-event between their launches.
+One step = one chunk of one attention layer (one denoising pass) of an autoregressive
+rollout:
+    route(q)  [pool of q, coarse scores against P_t and the window, top-K]
+    attn_fwd  [attention over P_t, the routed window blocks and the chunk]
+    memory_update  [Top-C update, sinks pinned; pools k into the appended blocks]
+on seeded synthetic bf16 inputs already resident in HBM.  The default workload is the
+1-minute rollout (12 heads, d=128, 1560-token frames, 3-frame chunks = 4680 queries,
+240-frame history, 64-token blocks, capacity 256 with 1 sink, window 6 frames, top-64).
+The cache is built by replaying the history chunks (route + update); then K successive
+chunks -- the measured chunk (the one right after the history) and the ones after it,
+drawn beforehand and resident in HBM -- are timed back to back.  The W warm-up chunks run
+from the same state, which is restored afterwards, so the timed chunks, their routing and
+their attended FLOP depend on neither K nor W.
 
-Prints one JSON line.  `roofline` is for the dominant kernel (attention forward, bf16 MFMA):
-achieved = algorithmic FLOP per launch (4 * head_dim per attended (query, key) pair)
-divided by that kernel's mean duration: K back-to-back launches on the state the timed
-steps left, between two HIP events on the stream they run on.
-`cpu_baseline` times the fp64 oracle's chunk step on this host for one head and scales it
-to the 12 heads of a chunk.
+Prints one JSON line.  `roofline` is for the dominant kernel (attention forward, bf16
+MFMA): achieved = algorithmic FLOP of the timed chunks (4 * head_dim per attended
+(query, key) pair, counted from each chunk's cache state and routing) divided by the sum
+of that kernel's durations, each measured with HIP events around its launch inside the
+timed region, on the stream it runs on.  `cpu_baseline` times the fp64 oracle's chunk
+step on this host for a sample of heads of the measured chunk, scaled to all heads.
+Extra fields: the other persistent workloads (5 s line; 20 s per-chunk times over the
+whole rollout), the trainable path's forward + backward, the dense-vs-persistent KV
+footprint, the T-pass chunk step, and measured device ceilings (probes).
 
-  python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--train]
+  python bench.py [--config NAME] [--steps K] [--warmup W] [--gpus 1] [--no-cpu]
+                  [--no-extras] [--no-probes]
 """
 from __future__ import annotations
 
@@ -28,6 +36,7 @@ import json
 import os
 import sys
 import time
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -37,138 +46,397 @@ sys.path.insert(0, ROOT)
 METRIC = "PBSA ms/chunk + effective TFLOP/s & % MFMA/HBM roofline, 1 MI355X"
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
+PERSISTENT = ("tiny", "wan_5s", "wan_20s", "wan_1min")
+DESCR = {
+    "tiny": "tiny: 1 head, d=64, 256-token frames, 1-frame chunks, 4-frame history, C=4, W=2, K=4",
+    "wan_5s": "wan_5s: Wan2.1-1.3B-shaped 5 s rollout, one layer, one chunk after a 21-frame history",
+    "wan_20s": "wan_20s: Wan2.1-1.3B-shaped 20 s rollout, one layer, one chunk after an 81-frame history",
+    "wan_1min": "wan_1min: Wan2.1-1.3B-shaped 1 min rollout, one layer, one chunk after a 240-frame history",
+}
 
 
 def parse():
     ap = argparse.ArgumentParser()
+    ap.add_argument("--config", default="wan_1min", choices=PERSISTENT,
+                    help="persistent-mode workload of the headline line")
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--train", action="store_true",
-                    help="also time the trainable two-level fwd+bwd clip (extra field)")
-    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "attn_fwd_wan_5s_traffic.json"),
-                    help="HBM traffic per attention launch from rocprofv3 counters (if present)")
+    ap.add_argument("--cpu-heads", type=int, default=0,
+                    help="heads of the measured chunk the oracle times (0: by workload)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="headline line only (no other workloads, training path, T passes)")
     ap.add_argument("--no-probes", action="store_true",
                     help="skip the measured ceilings (MFMA, copy, gather, full-history pool)")
+    ap.add_argument("--passes", type=int, default=4,
+                    help="denoising passes per chunk of the multi-pass extra field")
+    ap.add_argument("--traffic", default=None,
+                    help="HBM traffic per attention launch from rocprofv3 counters "
+                         "(default profiles/attn_fwd_<config>_traffic.json, if present)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc output folders (FETCH_SIZE, WRITE_SIZE) of a "
                          "--copy-probe run into the traffic file, then exit")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, copy a 512 MiB buffer 3 times (calibrates the "
                          "FETCH_SIZE / WRITE_SIZE counters against known bytes)")
-    return ap.parse_args()
+    a = ap.parse_args()
+    if a.traffic is None:
+        a.traffic = os.path.join(ROOT, "profiles", f"attn_fwd_{a.config}_traffic.json")
+    a.steps = max(1, a.steps)
+    a.warmup = max(0, a.warmup)
+    return a
 
 
+# ------------------------------------------------------------------------------ helpers
+class Ctx:
+    """torch, the package modules, the stream and host->device helpers."""
+
+    def __init__(self):
+        import torch
+        from block_sparse_attention_pbsa_amd import ops, runtime, synth
+        self.torch, self.ops, self.runtime, self.synth = torch, ops, runtime, synth
+        torch.cuda.set_device(0)
+        self.stream = torch.cuda.current_stream()
+
+    def dev(self, x):
+        return self.torch.from_numpy(np.ascontiguousarray(x)).cuda().to(self.torch.bfloat16)
+
+    def sync(self):
+        self.torch.cuda.synchronize()
+
+    def event(self):
+        return self.torch.cuda.Event(enable_timing=True)
+
+    def timed(self, fn, reps):
+        """Mean duration (ms) of `reps` back-to-back runs of fn between two HIP events on
+        the stream the kernels run on (no event between runs)."""
+        fn()
+        self.sync()
+        a, b = self.event(), self.event()
+        a.record(self.stream)
+        for _ in range(reps):
+            fn()
+        b.record(self.stream)
+        self.sync()
+        return a.elapsed_time(b) / reps
+
+
+def shape_of(ops, wl):
+    return ops.Shape(wl.heads, wl.head_dim, wl.frame_tokens, wl.chunk_frames, wl.window_frames,
+                     wl.capacity, wl.sinks, wl.topk, wl.scale)
+
+
+def gen_chunks(synth, wl, seed, idxs, passes=1):
+    """Host Q, K, V of the given chunks (all `passes` denoising passes of each, the last one
+    the chunk's own), drawn on worker threads, yielded in order."""
+    idxs = list(idxs)
+
+    def one(c):
+        if passes == 1:
+            return synth.chunk_qkv(wl, seed, c)
+        return [synth.pass_qkv(wl, seed, c, p, passes) for p in range(passes)]
+    with ThreadPoolExecutor(8) as ex:
+        yield from ex.map(one, idxs)
+
+
+def _cache_tensors(cache):
+    ts = [cache.k, cache.v, cache.rep, cache.block_id, cache.len]
+    return ts + ([cache.chunk_dev] if cache.chunk_dev is not None else [])
+
+
+def snapshot(cache):
+    return [t.clone() for t in _cache_tensors(cache)], cache.chunk_index
+
+
+def restore(cache, snap):
+    ts, idx = snap
+    for t, s in zip(_cache_tensors(cache), ts):
+        t.copy_(s)
+    cache.chunk_index = idx
+
+
+def attended(wl, shape, bid, ln, sel):
+    """(attended (query, key) pairs summed over heads and query tokens, distinct cache
+    slots read) for one chunk, from the cache state (block ids and lengths per slot) and
+    the routing the attention sees."""
+    H, C, nb, n, W, F = wl.heads, wl.capacity, wl.nb, wl.frame_tokens, wl.window_frames, \
+        wl.chunk_frames
+    occ = bid[:, :C] >= 0
+    pkeys = (ln[:, :C] * occ).sum(1)
+    g = sel.astype(np.int64)
+    valid = g >= 0
+    gs = np.where(valid, g, 0)
+    slot = C + ((gs // nb) % W) * nb + gs % nb
+    rl = np.take_along_axis(ln.astype(np.int64), slot.reshape(H, -1), axis=1).reshape(sel.shape)
+    keys = pkeys[:, None] + F * n + (rl * valid).sum(2)
+    r = np.arange(shape.nq)
+    qlen = np.minimum(64, n - 64 * (r % nb))
+    slots_read = int(occ.sum()) + sum(len(set(gs[h][valid[h]].tolist())) for h in range(H))
+    return int((keys * qlen[None, :]).sum()), slots_read
+
+
+def attn_bytes(wl, shape, slots_read):
+    """Algorithmic HBM bytes of one attention launch: the distinct KV blocks it reads (64
+    padded rows of K and V each), the chunk's K and V, Q, O and LSE."""
+    d, H, T = wl.head_dim, wl.heads, shape.chunk_tokens
+    return slots_read * 2 * 64 * d * 2 + 2 * T * H * d * 2 + 2 * T * H * d * 2 + T * H * 4
+
+
+# ------------------------------------------------------------------------------ headline
+def persistent_line(cx, name, steps, warmup, oracle_heads=()):
+    """Bootstrap `name`'s rollout to its measured chunk, then time `steps` successive
+    chunks.  Returns (result dict, layer, device chunks, oracle rollouts, host measured chunk)."""
+    ops, runtime, synth = cx.ops, cx.runtime, cx.synth
+    wl, seed = synth.WORKLOADS[name], synth.SEEDS[name]
+    shape = shape_of(ops, wl)
+    layer = runtime.PersistentLayer(shape)
+    layer.reset()
+    m = wl.measured_chunk
+    ros = {}
+    if oracle_heads:
+        import oracle as orc
+        sch = orc.Schedule(wl.frame_tokens, wl.block, wl.chunk_frames, wl.window_frames,
+                           wl.capacity, wl.sinks, wl.topk, wl.scale)
+        ros = {h: orc.PersistentRollout(sch, wl.head_dim) for h in oracle_heads}
+    t_boot = time.perf_counter()
+    for q, k, v in gen_chunks(synth, wl, seed, range(m)):
+        layer.step(cx.dev(q), cx.dev(k), cx.dev(v), attend=False)
+        for h, ro in ros.items():
+            ro.update(ro.select(q[:, h]), k[:, h], v[:, h])
+    n_dev = max(steps, warmup)
+    chunks, measured_host = [], None
+    for i, (q, k, v) in enumerate(gen_chunks(synth, wl, seed, range(m, m + n_dev))):
+        chunks.append((cx.dev(q), cx.dev(k), cx.dev(v)))
+        if i == 0:
+            measured_host = (q, k, v)
+    cx.sync()
+    print(f"{name}: bootstrapped {m} chunks in {time.perf_counter() - t_boot:.1f} s",
+          file=sys.stderr, flush=True)
+    snap = snapshot(layer.cache)
+
+    # counting pass: each timed chunk's attended pairs from its cache state and routing
+    pairs, slots = [], []
+    for i in range(steps):
+        q, k, v = chunks[i]
+        layer.route(q)
+        cx.sync()
+        p_, s_ = attended(wl, shape, layer.cache.block_id.cpu().numpy(),
+                          layer.cache.len.cpu().numpy(), layer.sel.cpu().numpy())
+        pairs.append(p_)
+        slots.append(s_)
+        layer.attend(q, k, v)
+        layer.update(k, v)
+    restore(layer.cache, snap)
+    for i in range(warmup):
+        layer.step(*chunks[i])
+    restore(layer.cache, snap)
+    cx.sync()
+
+    # timed region: `steps` successive chunks back to back; events around each attention
+    ev = [(cx.event(), cx.event()) for _ in range(steps)]
+    t0, t1 = cx.event(), cx.event()
+    t0.record(cx.stream)
+    for i in range(steps):
+        q, k, v = chunks[i]
+        layer.route(q)
+        ev[i][0].record(cx.stream)
+        layer.attend(q, k, v)
+        ev[i][1].record(cx.stream)
+        layer.update(k, v)
+    t1.record(cx.stream)
+    cx.sync()
+    ms_step = t0.elapsed_time(t1) / steps
+    attn_ms = [a.elapsed_time(b) for a, b in ev]
+    flop = [4 * wl.head_dim * p_ for p_ in pairs]
+    achieved = sum(flop) / (sum(attn_ms) * 1e-3) / 1e12
+    abytes = [attn_bytes(wl, shape, s_) for s_ in slots]
+
+    # each op alone at the measured chunk's state (diagnostic)
+    restore(layer.cache, snap)
+    q, k, v = chunks[0]
+    layer.route(q)
+    cx.sync()
+    cache2 = cx.ops.Cache(shape)
+    for nm in ("k", "v", "rep", "block_id", "len"):
+        getattr(cache2, nm).copy_(getattr(layer.cache, nm))
+    cache2.chunk_index = layer.cache.chunk_index
+    ops_ms = {
+        "route": cx.timed(lambda: ops.pbsa_route(shape, q, layer.cache, layer.q_rep, layer.scores,
+                                                 layer.sel), 20),
+        "pool_q": cx.timed(lambda: ops.pbsa_pool(shape, q, wl.chunk_frames, layer.q_rep), 20),
+        "score_topk": cx.timed(lambda: ops.pbsa_score_topk(shape, layer.q_rep, layer.cache,
+                                                           layer.scores, layer.sel), 20),
+        "attn_fwd": cx.timed(lambda: layer.attend(q, k, v), 20),
+        # repeated on a copy of the cache (each call appends the chunk again)
+        "memory_update": cx.timed(lambda: ops.pbsa_memory_update(
+            shape, layer.scores, cache2, k, v, None, layer.workspace), 20),
+    }
+    del cache2
+    res = {
+        "workload": DESCR[name],
+        "ms_per_chunk": round(ms_step, 4),
+        "chunks_timed": [m, m + steps - 1],
+        "attn_fwd_ms_mean": round(float(np.mean(attn_ms)), 4),
+        "attn_fwd_ms_min_max": [round(min(attn_ms), 4), round(max(attn_ms), 4)],
+        "attn_fwd_flop_mean": int(np.mean(flop)),
+        "attn_fwd_tflops": round(achieved, 2),
+        "attn_fwd_frac_bf16_peak": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "attn_fwd_algorithmic_bytes_mean": int(np.mean(abytes)),
+        "tflops_effective_step": round(sum(flop) / (ms_step * steps * 1e-3) / 1e12, 2),
+        "ops_ms_alone": {k_: round(v_, 4) for k_, v_ in ops_ms.items()},
+    }
+    restore(layer.cache, snap)
+    cx.sync()
+    return res, layer, chunks, ros, measured_host, (sum(flop), sum(attn_ms), ms_step, abytes)
+
+
+def rollout_per_chunk(cx, name):
+    """Every chunk of `name`'s rollout with attention (route, attention, update), each
+    chunk timed with events around its step; the rollout runs twice and the second run is
+    reported (the first warms up).  Returns per-chunk ms."""
+    ops, runtime, synth = cx.ops, cx.runtime, cx.synth
+    wl, seed = synth.WORKLOADS[name], synth.SEEDS[name]
+    shape = shape_of(ops, wl)
+    layer = runtime.PersistentLayer(shape)
+    m = wl.measured_chunk
+    chunks = [(cx.dev(q), cx.dev(k), cx.dev(v)) for q, k, v in gen_chunks(synth, wl, seed,
+                                                                         range(m + 1))]
+    ms = []
+    for rep in range(2):
+        layer.reset()
+        ev = [(cx.event(), cx.event()) for _ in chunks]
+        for (q, k, v), (a, b) in zip(chunks, ev):
+            a.record(cx.stream)
+            layer.step(q, k, v)
+            b.record(cx.stream)
+        cx.sync()
+        ms = [a.elapsed_time(b) for a, b in ev]
+    del chunks
+    full = -(-wl.window_frames // wl.chunk_frames)   # first chunk with a full window
+    return {"workload": DESCR[name] + "; every chunk of the rollout",
+            "last_chunk_ms": round(ms[m], 4),
+            "mean_ms_window_full": round(float(np.mean(ms[full:])), 4),
+            "chunks_in_mean": [full, m],
+            "first_chunks_ms": [round(x, 4) for x in ms[:full]]}
+
+
+def multi_pass(cx, name, passes, chunks_n):
+    """T denoising passes per chunk sharing the persistent memory: T x (route, attention)
+    on each pass's own Q, K, V, then one memory update with the last pass's scores and
+    K/V; `chunks_n` successive chunks from the measured one, timed back to back, through
+    the plain call sequence and through the captured chunk step."""
+    ops, runtime, synth = cx.ops, cx.runtime, cx.synth
+    wl, seed = synth.WORKLOADS[name], synth.SEEDS[name]
+    shape = shape_of(ops, wl)
+    layer = runtime.PersistentLayer(shape, passes=passes, device_counter=True)
+    layer.reset()
+    m = wl.measured_chunk
+    for q, k, v in gen_chunks(synth, wl, seed, range(m)):
+        layer.step(cx.dev(q), cx.dev(k), cx.dev(v), attend=False)
+    chunks = [[tuple(cx.dev(x) for x in qkv) for qkv in ps]
+              for ps in gen_chunks(synth, wl, seed, range(m, m + chunks_n), passes)]
+    cx.sync()
+    snap = snapshot(layer.cache)
+    out = {"workload": DESCR[name], "passes": passes, "chunks_timed": [m, m + chunks_n - 1]}
+    for mode in ("sequence", "fused_call", "graph"):
+        run = {"sequence": layer.step_passes, "fused_call": layer.step_fused,
+               "graph": layer.step_graph}[mode]
+        for ps in chunks:        # warm (and, for the graph, capture) every chunk first
+            run(ps)
+        restore(layer.cache, snap)
+        cx.sync()
+        a, b = cx.event(), cx.event()
+        a.record(cx.stream)
+        for ps in chunks:
+            run(ps)
+        b.record(cx.stream)
+        cx.sync()
+        out[f"ms_per_chunk_{mode}"] = round(a.elapsed_time(b) / chunks_n, 4)
+        restore(layer.cache, snap)
+        cx.sync()
+    layer.close_graphs()
+    del chunks
+    return out
+
+
+def persistent_backward(cx, name):
+    """Sparse Forcing's own trainable layout: forward and backward of the persistent-mode
+    attention (P_t, the routed window blocks and the chunk) at `name`'s measured chunk, with
+    the gradient of every cache slot (extra field)."""
+    ops, runtime, synth = cx.ops, cx.runtime, cx.synth
+    wl, seed = synth.WORKLOADS[name], synth.SEEDS[name]
+    shape = shape_of(ops, wl)
+    layer = runtime.PersistentLayer(shape)
+    layer.reset()
+    m = wl.measured_chunk
+    for q, k, v in gen_chunks(synth, wl, seed, range(m)):
+        layer.step(cx.dev(q), cx.dev(k), cx.dev(v), attend=False)
+    q, k, v = (cx.dev(x) for x in synth.chunk_qkv(wl, seed, m))
+    dout = cx.dev(synth.clip_dout(wl, seed, shape.chunk_tokens))
+    layer.route(q)
+    cx.sync()
+    pairs, _ = attended(wl, shape, layer.cache.block_id.cpu().numpy(),
+                        layer.cache.len.cpu().numpy(), layer.sel.cpu().numpy())
+    T, H, d = shape.chunk_tokens, wl.heads, wl.head_dim
+    dq, dk, dv = (cx.torch.empty(T, H, d, dtype=cx.torch.bfloat16, device="cuda")
+                  for _ in range(3))
+    dkc, dvc = cx.torch.empty_like(layer.cache.k), cx.torch.empty_like(layer.cache.v)
+    ws = cx.torch.empty(ops.pbsa_workspace_bytes(shape, ops.PBSA_OP_ATTN_BWD_PERSISTENT),
+                        dtype=cx.torch.uint8, device="cuda")
+    fwd_ms = cx.timed(lambda: layer.attend(q, k, v), 10)
+    bwd_ms = cx.timed(lambda: ops.pbsa_attn_bwd_persistent(
+        shape, q, layer.cache, k, v, layer.sel, layer.o, layer.lse, dout, dq, dk, dv, dkc, dvc,
+        ws), 10)
+    bwd_flop = 8 * d * pairs
+    return {"workload": DESCR[name] + "; gradient of the persistent-mode attention",
+            "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
+            "fwd_bwd_ms_per_chunk": round(fwd_ms + bwd_ms, 4),
+            "bwd_flop": int(bwd_flop),
+            "bwd_tflops": round(bwd_flop / (bwd_ms * 1e-3) / 1e12, 2),
+            "bwd_frac_bf16_peak": round(bwd_flop / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
+def footprint(synth, ops):
+    """Per layer: a dense KV cache of the whole history plus the chunk, against the
+    persistent cache (P_t and the window in 64-row slots, plus representatives, ids and
+    lengths) plus the chunk."""
+    out = {}
+    for name in ("wan_5s", "wan_20s", "wan_1min"):
+        wl = synth.WORKLOADS[name]
+        shape = shape_of(ops, wl)
+        kv_tok = wl.heads * wl.head_dim * 2 * 2   # K and V bytes per token
+        dense = (wl.history_frames + wl.chunk_frames) * wl.frame_tokens * kv_tok
+        cache = wl.heads * shape.slots * (2 * 64 * wl.head_dim * 2 + wl.head_dim * 4 + 8)
+        chunk = shape.chunk_tokens * kv_tok
+        out[name] = {"dense_bytes": dense, "persistent_bytes": cache + chunk,
+                     "persistent_cache_bytes": cache,
+                     "persistent_over_dense": round((cache + chunk) / dense, 4)}
+    return out
+
+
+# ------------------------------------------------------------------------------ main
 def main():
     args = parse()
     if args.write_traffic:
-        write_traffic(*args.write_traffic, args.traffic)
+        write_traffic(*args.write_traffic, args.traffic, args.config)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "the library runs on one GPU (no sharding across GPUs); --gpus must be 1"}))
+        print(json.dumps({"error": "PBSA runs on one GPU here: the path is sharded by head "
+                                   "across GPUs only by design (no collectives are built); "
+                                   "--gpus must be 1"}))
         sys.exit(2)
-    import torch
-    from block_sparse_attention_pbsa_amd import ops, runtime, synth
+    cx = Ctx()
+    name = args.config
+    wl = cx.synth.WORKLOADS[name]
+    cpu_heads = ()
+    if not args.no_cpu:
+        n_h = args.cpu_heads or {"tiny": 1, "wan_5s": 12, "wan_20s": 8, "wan_1min": 8}[name]
+        cpu_heads = tuple(range(min(n_h, wl.heads)))
+    res, layer, chunks, ros, measured_host, (flop_sum, attn_ms_sum, ms_step, abytes) = \
+        persistent_line(cx, name, args.steps, args.warmup, cpu_heads)
+    achieved = flop_sum / (attn_ms_sum * 1e-3) / 1e12
 
-    wl = synth.WORKLOADS["wan_5s"]
-    seed = synth.SEEDS["wan_5s"]
-    shape = ops.Shape(wl.heads, wl.head_dim, wl.frame_tokens, wl.chunk_frames, wl.window_frames,
-                      wl.capacity, wl.sinks, wl.topk, wl.scale)
-    torch.cuda.set_device(0)
-
-    def dev(x):
-        return torch.from_numpy(np.ascontiguousarray(x)).cuda().to(torch.bfloat16)
-
-    layer = runtime.PersistentLayer(shape)
-    layer.reset()
-    for c in range(wl.measured_chunk):
-        q, k, v = synth.chunk_qkv(wl, seed, c)
-        layer.step(dev(q), dev(k), dev(v), attend=False)
-    qn, kn, vn = synth.chunk_qkv(wl, seed, wl.measured_chunk)
-    q, k, v = dev(qn), dev(kn), dev(vn)
-    torch.cuda.synchronize()
-    print(f"bootstrapped {wl.measured_chunk} chunks", file=sys.stderr, flush=True)
-
-    def attended_flop():
-        """4*d * sum over (head, query token) of attended keys, from the current state."""
-        bid = layer.cache.block_id.cpu().numpy()
-        ln = layer.cache.len.cpu().numpy()
-        C, nb, n = wl.capacity, wl.nb, wl.frame_tokens
-        total = 0
-        layer.route(q)  # routing for the current state (outside any timed region)
-        sels = layer.sel.cpu().numpy()
-        for h in range(wl.heads):
-            p_keys = int(ln[h, :C][bid[h, :C] >= 0].sum())
-            ring = {int(g): int(l) for g, l in zip(bid[h, C:], ln[h, C:]) if g >= 0}
-            sel = sels[h]
-            for r in range(shape.nq):
-                keys = p_keys + wl.chunk_frames * n + sum(ring[int(g)] for g in sel[r] if g >= 0)
-                qlen = min(64, n - 64 * (r % nb))
-                total += qlen * keys
-        return 4 * wl.head_dim * total
-
-    stream = torch.cuda.current_stream()
-
-    def step():
-        layer.step(q, k, v)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record(stream)
-    for _ in range(args.steps):
-        step()
-    t1.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t0.elapsed_time(t1)
-    ms_step = total_ms / args.steps
-
-    def timed(fn, reps):
-        """Mean duration (ms) of `reps` back-to-back launches of fn, HIP events on the
-        stream the kernels run on (no event between launches, so no gap is counted)."""
-        fn()
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(reps):
-            fn()
-        b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / reps
-
-    # The attention of the state the timed steps left (its routing refreshed first):
-    # `steps` back-to-back launches; the attended FLOP are counted for the same state.
-    flop = attended_flop()
-    torch.cuda.synchronize()
-    attn_avg = timed(lambda: layer.attend(q, k, v), args.steps)
-    achieved = flop / (attn_avg * 1e-3) / 1e12
-
-    # the memory update, timed on a copy of the cache (each call appends the chunk again)
-    import copy
-    cache2 = copy.copy(layer.cache)
-    for name_ in ("k", "v", "rep", "block_id", "len"):
-        setattr(cache2, name_, getattr(layer.cache, name_).clone())
-    upd_ms = timed(lambda: ops.pbsa_memory_update(shape, layer.scores, cache2, k, v, None,
-                                                  layer.workspace), 20)
-    del cache2
-
-    ops_ms = {
-        "route": timed(lambda: ops.pbsa_route(shape, q, layer.cache, layer.q_rep, layer.scores,
-                                              layer.sel), 20),
-        "pool_q": timed(lambda: ops.pbsa_pool(shape, q, wl.chunk_frames, layer.q_rep), 20),
-        "score_topk": timed(lambda: ops.pbsa_score_topk(shape, layer.q_rep, layer.cache,
-                                                        layer.scores, layer.sel), 20),
-        "attn_fwd": attn_avg,
-        "memory_update": upd_ms,
-    }
-    pool_bytes = shape.chunk_tokens * wl.heads * wl.head_dim * 2 + shape.nq * wl.heads * wl.head_dim * 4
-
-    # counters taken on another version of the kernel's sources do not count
     traffic = None
     if os.path.exists(args.traffic):
         try:
@@ -177,7 +445,7 @@ def main():
                 traffic = rec.get("bytes_per_launch")
         except (OSError, ValueError):
             traffic = None
-
+    shape = shape_of(cx.ops, wl)
     result = {
         "metric": METRIC,
         "value": round(ms_step, 4),
@@ -191,41 +459,55 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "wan_5s: Wan2.1-1.3B-shaped 5 s rollout, one layer, one chunk",
-                   "heads": wl.heads, "head_dim": wl.head_dim, "frame_tokens": wl.frame_tokens,
-                   "chunk_frames": wl.chunk_frames, "query_tokens": shape.chunk_tokens,
-                   "history_frames": wl.history_frames, "block": wl.block,
-                   "capacity": wl.capacity, "sinks": wl.sinks,
+        "config": {"workload": DESCR[name], "heads": wl.heads, "head_dim": wl.head_dim,
+                   "frame_tokens": wl.frame_tokens, "chunk_frames": wl.chunk_frames,
+                   "query_tokens": shape.chunk_tokens, "history_frames": wl.history_frames,
+                   "block": wl.block, "capacity": wl.capacity, "sinks": wl.sinks,
                    "window_frames": wl.window_frames, "topk": wl.topk},
-        "tflops_effective": round(flop / (ms_step * 1e-3) / 1e12, 2),
-        "attn_fwd_flop": int(flop),
-        "attn_fwd_ms": round(attn_avg, 4),
-        "ops_ms_mean": {k_: round(v_, 4) for k_, v_ in ops_ms.items()},
-        # derived, not measured as one run: T = 4 denoising passes per chunk (route + attention
-        # each) sharing the memory, then one update
-        "derived_ms_per_chunk_T4": round(4 * (ops_ms["route"] + attn_avg) + upd_ms, 4),
-        "pool_q_gbs": round(pool_bytes / (ops_ms["pool_q"] * 1e-3) / 1e9, 1),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "kernel": TRAFFIC_KERNEL},
+                     "traffic": traffic, "kernel": TRAFFIC_KERNEL,
+                     "algorithmic_bytes": int(np.mean(abytes))},
     }
+    result.update({k_: v_ for k_, v_ in res.items() if k_ != "workload"})
 
     if not args.no_probes:
-        result["probes"] = bench_probes(torch, ops, synth, shape, layer, q, k, v, stream)
+        q, k, v = chunks[0]
+        result["probes"] = bench_probes(cx, shape, layer, q, k, v)
+    del chunks, layer
+    cx.torch.cuda.empty_cache()
 
-    if args.train:
-        result["train"] = bench_train(torch, ops, runtime, synth, dev, stream)
+    if not args.no_extras:
+        extras = {}
+        for other in ("wan_5s", "wan_20s", "wan_1min"):
+            if other == name:
+                continue
+            r, lay, ch, _, _, _ = persistent_line(cx, other, 10, 3)
+            extras[other] = r
+            del lay, ch
+            cx.torch.cuda.empty_cache()
+        extras["wan_20s_rollout"] = rollout_per_chunk(cx, "wan_20s")
+        cx.torch.cuda.empty_cache()
+        extras[f"{name}_T{args.passes}"] = multi_pass(cx, name, args.passes, 6)
+        cx.torch.cuda.empty_cache()
+        extras["wan_train"] = bench_train(cx)
+        cx.torch.cuda.empty_cache()
+        for nm in ("wan_5s", name):
+            extras[f"{nm}_persistent_fwd_bwd"] = persistent_backward(cx, nm)
+            cx.torch.cuda.empty_cache()
+        result["extras"] = extras
+        result["footprint"] = footprint(cx.synth, cx.ops)
 
     if args.copy_probe:
-        src = torch.ones(256 * 1024 * 1024, dtype=torch.bfloat16, device="cuda")
-        dst = torch.empty_like(src)
+        src = cx.torch.ones(256 * 1024 * 1024, dtype=cx.torch.bfloat16, device="cuda")
+        dst = cx.torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)
-        torch.cuda.synchronize()
+        cx.sync()
         result["copy_probe_bytes"] = src.numel() * 2
 
-    if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(wl, seed)
+    if cpu_heads:
+        result["cpu_baseline"] = cpu_baseline(wl, cx.synth.SEEDS[name], ros, measured_host)
     print(json.dumps(result), flush=True)
 
 
@@ -242,7 +524,7 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def write_traffic(fetch_dir, write_dir, out_path):
+def write_traffic(fetch_dir, write_dir, out_path, config):
     """HBM bytes per attention launch from FETCH_SIZE and WRITE_SIZE (KiB per dispatch),
     each scaled by what the counter reads for the 512 MiB copy of the same run."""
     def read(d, counter):
@@ -259,7 +541,7 @@ def write_traffic(fetch_dir, write_dir, out_path):
     ff, wf = copy_kib / f_c, copy_kib / w_c
     rd, wr = int(f_k * ff * 1024), int(w_k * wf * 1024)
     rec = {"kernel": f"pbsa::{TRAFFIC_KERNEL}",
-           "workload": "wan_5s measured chunk (12 heads, d=128, 4680 queries, C=64, W=6, K=32)",
+           "workload": DESCR[config] + " (every attention launch of the run)",
            "source_sha256": kernel_source_hash(),
            "fetch_size_kib_per_dispatch": round(f_k, 1), "write_size_kib_per_dispatch": round(w_k, 1),
            "calibration": {"copy": "__amd_rocclr_copyBuffer of 512 MiB (bench.py --copy-probe)",
@@ -272,23 +554,23 @@ def write_traffic(fetch_dir, write_dir, out_path):
     print(json.dumps(rec))
 
 
-def _timed_reps(torch, stream, fn, reps, flush=None):
-    """Median and p10/p90 of `reps` runs of fn (ms), HIP events on `stream`; flush() runs
+def _timed_reps(cx, fn, reps, flush=None):
+    """Median and p10/p90 of `reps` runs of fn (ms), HIP events on the stream; flush() runs
     before each rep outside the timed region (cold runs)."""
     ts = []
     for _ in range(reps):
         if flush is not None:
             flush()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
+        a, b = cx.event(), cx.event()
+        a.record(cx.stream)
         fn()
-        b.record(stream)
-        torch.cuda.synchronize()
+        b.record(cx.stream)
+        cx.sync()
         ts.append(a.elapsed_time(b))
     return float(np.median(ts)), float(np.percentile(ts, 10)), float(np.percentile(ts, 90))
 
 
-def bench_probes(torch, ops, synth, shape, layer, q, k, v, stream):
+def bench_probes(cx, shape, layer, q, k, v):
     """Measured ceilings next to the published peaks (extra field):
       mfma   - independent v_mfma_f32_32x32x16_bf16 chains on every SIMD (pbsa_probe_mfma);
       copy   - a 512 MiB device copy (read + write bytes / time);
@@ -296,8 +578,10 @@ def bench_probes(torch, ops, synth, shape, layer, q, k, v, stream):
                chunk: bytes moved into LDS per launch (one 1 KB instruction per piece; a
                step moves 32 KB per workgroup) / time, warm and cold;
       pool_full_history - pbsa_pool over the 1-minute workload's whole history
-               (240 frames x 1560 tokens x 12 heads x 128, 1.15 GB read), warm and cold.
+               (240 frames x 1560 tokens x 12 heads x 128, 1.15 GB read), warm and cold;
+      pool_train_clip - the training clip's q and k (block and frame representatives).
     Cold runs first read a 512 MiB buffer (larger than the 256 MB last-level cache)."""
+    torch, ops, synth = cx.torch, cx.ops, cx.synth
     out = {}
     flush_buf = torch.ones(256 * 1024 * 1024, dtype=torch.bfloat16, device="cuda")
     flush_sink = torch.empty((), dtype=torch.bfloat16, device="cuda")
@@ -307,48 +591,43 @@ def bench_probes(torch, ops, synth, shape, layer, q, k, v, stream):
         # launch and charged to it)
         flush_sink.copy_(flush_buf.sum())
 
-    # MFMA ceiling
     mf = torch.empty(131072, dtype=torch.float32, device="cuda")
     iters = 20000
     flop = ops.pbsa_probe_mfma(iters, mf)
-    torch.cuda.synchronize()
-    med, _, _ = _timed_reps(torch, stream, lambda: ops.pbsa_probe_mfma(iters, mf), 5)
+    cx.sync()
+    med, _, _ = _timed_reps(cx, lambda: ops.pbsa_probe_mfma(iters, mf), 5)
     out["mfma"] = {"tflops": round(flop / (med * 1e-3) / 1e12, 1), "ms": round(med, 3),
                    "frac_of_peak": round(flop / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
-    # copy ceiling
     src = torch.ones(256 * 1024 * 1024, dtype=torch.bfloat16, device="cuda")
     dst = torch.empty_like(src)
     dst.copy_(src)
-    med, _, _ = _timed_reps(torch, stream, lambda: dst.copy_(src), 5)
+    med, _, _ = _timed_reps(cx, lambda: dst.copy_(src), 5)
     cb = 2 * src.numel() * 2
     out["copy"] = {"gbs": round(cb / (med * 1e-3) / 1e9, 1), "ms": round(med, 3),
                    "frac_of_peak": round(cb / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
     del src, dst
-    # gather of the measured chunk (routing already current)
+    # gather of the measured chunk (its routing made current)
     layer.route(q)
     bid = layer.cache.block_id.cpu().numpy()
     sel = layer.sel.cpu().numpy()
     C, nq = shape.capacity, shape.nq
     steps = 0
-    unique_slots = 0  # distinct cache slots the launch reads (P, and routed window blocks)
+    unique_slots = 0
     for h in range(shape.heads):
         routed = {int(g) for g in sel[h].ravel() if g >= 0}
         unique_slots += int((bid[h, :C] >= 0).sum()) + len(routed)
         for pr in range((nq + 1) // 2):
-            # blocks routed by both query blocks of the pair join the shared steps
             sa = {int(g) for g in sel[h, 2 * pr] if g >= 0}
             sb = {int(g) for g in sel[h, 2 * pr + 1] if g >= 0} if 2 * pr + 1 < nq else set()
             nshared = int((bid[h, :C] >= 0).sum()) + nq + len(sa & sb)
             nsh2 = nshared + (nshared & 1)
-            # + the two steps gathered ahead past the end
             steps += nsh2 + 2 * max(len(sa - sb), len(sb - sa)) + 2
     gbytes = steps * 32 * 1024
     g = lambda: ops.pbsa_probe_gather(shape, q, layer.cache, k, v, layer.sel)
     g()
-    torch.cuda.synchronize()
-    warm, _, _ = _timed_reps(torch, stream, g, 10)
-    cold, c10, c90 = _timed_reps(torch, stream, g, 10, flush)
-    # unique KV bytes: each distinct slot's K and V (64 rows) plus the chunk's own K and V
+    cx.sync()
+    warm, _, _ = _timed_reps(cx, g, 10)
+    cold, c10, c90 = _timed_reps(cx, g, 10, flush)
     ubytes = unique_slots * 2 * 64 * shape.head_dim * 2 + \
         2 * shape.chunk_tokens * shape.heads * shape.head_dim * 2
     out["gather"] = {"bytes_moved_to_lds": gbytes, "unique_kv_bytes": ubytes,
@@ -357,7 +636,6 @@ def bench_probes(torch, ops, synth, shape, layer, q, k, v, stream):
                      "gbs_warm": round(gbytes / (warm * 1e-3) / 1e9, 1),
                      "gbs_cold": round(gbytes / (cold * 1e-3) / 1e9, 1),
                      "unique_gbs_cold": round(ubytes / (cold * 1e-3) / 1e9, 1)}
-    # full-history pooling at the 1-minute workload's size (seeded synthetic tokens)
     wl = synth.WORKLOADS["wan_1min"]
     frames = wl.history_frames
     T = frames * wl.frame_tokens
@@ -370,9 +648,9 @@ def bench_probes(torch, ops, synth, shape, layer, q, k, v, stream):
     frep = torch.empty((wl.heads, frames, wl.head_dim), dtype=torch.float32, device="cuda")
     p = lambda: ops.pbsa_pool(pshape, x, frames, brep, frep)
     p()
-    torch.cuda.synchronize()
-    warm, _, _ = _timed_reps(torch, stream, p, 10)
-    cold, c10, c90 = _timed_reps(torch, stream, p, 10, flush)
+    cx.sync()
+    warm, _, _ = _timed_reps(cx, p, 10)
+    cold, c10, c90 = _timed_reps(cx, p, 10, flush)
     pb = x.numel() * 2 + brep.numel() * 4 + frep.numel() * 4
     out["pool_full_history"] = {
         "workload": "wan_1min history: 240 frames x 1560 tokens, 12 heads, d=128",
@@ -381,7 +659,6 @@ def bench_probes(torch, ops, synth, shape, layer, q, k, v, stream):
         "gbs_warm": round(pb / (warm * 1e-3) / 1e9, 1), "gbs_cold": round(pb / (cold * 1e-3) / 1e9, 1),
         "frac_hbm_cold": round(pb / (cold * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
     del x, brep, frep
-    # the training clip's queries and keys (block and frame representatives of each)
     wl = synth.WORKLOADS["wan_train"]
     frames = wl.clip_chunks * wl.chunk_frames
     T = frames * wl.frame_tokens
@@ -398,9 +675,9 @@ def bench_probes(torch, ops, synth, shape, layer, q, k, v, stream):
         for x_, (b_, f_) in zip(xs, reps):
             ops.pbsa_pool(pshape, x_, frames, b_, f_)
     pc()
-    torch.cuda.synchronize()
-    warm, _, _ = _timed_reps(torch, stream, pc, 10)
-    cold, c10, c90 = _timed_reps(torch, stream, pc, 10, flush)
+    cx.sync()
+    warm, _, _ = _timed_reps(cx, pc, 10)
+    cold, c10, c90 = _timed_reps(cx, pc, 10, flush)
     pb = sum(x_.numel() * 2 for x_ in xs) + sum(b_.numel() * 4 + f_.numel() * 4 for b_, f_ in reps)
     out["pool_train_clip"] = {
         "workload": "wan_train clip q and k: 24 frames x 1560 tokens, 12 heads, d=128 (2 launches)",
@@ -413,72 +690,58 @@ def bench_probes(torch, ops, synth, shape, layer, q, k, v, stream):
     return out
 
 
-def bench_train(torch, ops, runtime, synth, dev, stream):
-    """Trainable two-level path on the 24-frame clip: fwd+bwd ms per clip (extra field)."""
+def bench_train(cx):
+    """Trainable two-level path on the 24-frame clip: selection, forward and backward, ms
+    per clip and per chunk (extra field)."""
+    ops, runtime, synth = cx.ops, cx.runtime, cx.synth
     wl = synth.WORKLOADS["wan_train"]
     seed = synth.SEEDS["wan_train"]
     shape = ops.Shape(wl.heads, wl.head_dim, wl.frame_tokens, wl.chunk_frames, scale=wl.scale)
     qn, kn, vn = synth.clip_qkv(wl, seed)
-    q, k, v = dev(qn), dev(kn), dev(vn)
-    dout = dev(synth.clip_dout(wl, seed, qn.shape[0]))
+    q, k, v = cx.dev(qn), cx.dev(kn), cx.dev(vn)
+    dout = cx.dev(synth.clip_dout(wl, seed, qn.shape[0]))
     ks = runtime.cag_budgets(synth.clip_alphas(wl, seed), wl.topk, wl.clip_chunks)
     clip = runtime.TwoLevelClip(shape, wl.clip_chunks, wl.top_frames,
                                 max(max(ks), wl.chunk_frames * wl.nb))
     clip.select(q, k, ks)
-    torch.cuda.synchronize()
+    cx.sync()
     sel, nsel = clip.sel.cpu().numpy(), clip.nsel.cpu().numpy()
     n, nb = wl.frame_tokens, wl.nb
+    blen = np.minimum(64, n - 64 * (np.arange(sel.shape[1]) % nb))
     keys = 0
     for h in range(wl.heads):
         for r in range(nsel.shape[1]):
-            qlen = min(64, n - 64 * (r % nb))
-            keys += qlen * sum(min(64, n - 64 * (int(g) % nb)) for g in sel[h, r, :nsel[h, r]])
+            keys += int(blen[r]) * int(blen[sel[h, r, :nsel[h, r]]].sum())
     fwd_flop = 4 * wl.head_dim * keys
     bwd_flop = 8 * wl.head_dim * keys
-
-    def run(fn, reps=10):
-        for _ in range(3):
-            fn()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        a.record(stream)
-        for _ in range(reps):
-            fn()
-        b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / reps
-
-    sel_ms = run(lambda: clip.select(q, k, ks))
-    fwd_ms = run(lambda: clip.forward(q, k, v))
-    bwd_ms = run(lambda: clip.backward(q, k, v, dout))
-    return {"workload": "wan_train: 24-frame clip, 8 chunks, two-level top-8 frames",
-            "select_ms": round(sel_ms, 4), "fwd_ms": round(fwd_ms, 4),
-            "bwd_ms": round(bwd_ms, 4),
+    sel_ms = cx.timed(lambda: clip.select(q, k, ks), 10)
+    fwd_ms = cx.timed(lambda: clip.forward(q, k, v), 10)
+    bwd_ms = cx.timed(lambda: clip.backward(q, k, v, dout), 10)
+    C = wl.clip_chunks
+    return {"workload": "wan_train: 24-frame clip (8 chunks of 3 frames, 37,440 tokens), "
+                        "two-level top-8 frames, per-chunk budgets",
+            "select_ms": round(sel_ms, 4), "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
+            "fwd_bwd_ms_per_clip": round(sel_ms + fwd_ms + bwd_ms, 4),
+            "fwd_bwd_ms_per_chunk": round((sel_ms + fwd_ms + bwd_ms) / C, 4),
             "fwd_tflops": round(fwd_flop / (fwd_ms * 1e-3) / 1e12, 2),
             "bwd_tflops": round(bwd_flop / (bwd_ms * 1e-3) / 1e12, 2),
+            "bwd_frac_bf16_peak": round(bwd_flop / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "fwd_flop": int(fwd_flop), "bwd_flop": int(bwd_flop)}
 
 
-def cpu_baseline(wl, seed):
-    """The fp64 oracle's chunk step (select, gathered attention, update) for every head of
-    the measured chunk, on this host: each head's state is built untimed, then its chunk
-    step is timed; the value is the sum over heads in ms per chunk."""
-    import oracle as orc
-    from block_sparse_attention_pbsa_amd import synth
+def cpu_baseline(wl, seed, ros, measured_host):
+    """The fp64 oracle's chunk step (pool, score, route, gathered attention over all the
+    chunk's queries, Top-C update) on this host, for the heads whose rollout state was
+    built (untimed) during the bootstrap; scaled to all heads, in ms per chunk."""
+    import oracle  # noqa: F401  (test infrastructure: the CPU-baseline leg only)
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover - reporting only
         threads = os.cpu_count() or 1
-    sch = orc.Schedule(wl.frame_tokens, wl.block, wl.chunk_frames, wl.window_frames,
-                       wl.capacity, wl.sinks, wl.topk, wl.scale)
-    history = [synth.chunk_qkv(wl, seed, c) for c in range(wl.measured_chunk)]
-    q, k, v = synth.chunk_qkv(wl, seed, wl.measured_chunk)
+    q, k, v = measured_host
     sec = 0.0
-    for h in range(wl.heads):
-        ro = orc.PersistentRollout(sch, wl.head_dim)
-        for qc, kc, vc in history:
-            ro.update(ro.select(qc[:, h]), kc[:, h], vc[:, h])
+    for h, ro in ros.items():
         qh, kh, vh = q[:, h].copy(), k[:, h].copy(), v[:, h].copy()
         t = time.perf_counter()
         rt = ro.select(qh)
@@ -492,12 +755,13 @@ def cpu_baseline(wl, seed):
                          model)
     except OSError:
         pass
-    return {"value": round(sec * 1e3, 1), "unit": "ms/chunk", "cores": threads,
+    n = len(ros)
+    return {"value": round(sec * 1e3 * wl.heads / n, 1), "unit": "ms/chunk", "cores": threads,
             "kind": "oracle",
-            "sample": f"all {wl.heads} heads of the wan_5s measured chunk (pool, score, route, "
-                      "gathered fp64 attention over all 4680 queries, Top-C update), each "
-                      "head's chunk step timed after its rollout state was built untimed; "
-                      f"{os.cpu_count()} logical CPUs ({model})"}
+            "sample": f"{n} of {wl.heads} heads of the {wl.name} measured chunk (pool, score, "
+                      "route, gathered fp64 attention over all the chunk's queries, Top-C update), "
+                      f"timed {sec:.1f} s after each head's rollout state was built untimed, "
+                      f"scaled to {wl.heads} heads; {os.cpu_count()} logical CPUs ({model})"}
 
 
 if __name__ == "__main__":

@@ -11,8 +11,10 @@
 #include "../../include/pbsa.h"
 #include "../../include/pbsa_probe.h"
 #include "launch.h"
+#include "step_internal.h"
 
-namespace {
+namespace pbsa {
+namespace api {
 
 thread_local std::string g_err;
 
@@ -104,12 +106,6 @@ pbsa_status check_span(const pbsa_tensor& t, const char* name, int64_t tokens, i
   return PBSA_OK;
 }
 
-#define PBSA_TRY(x)                  \
-  do {                               \
-    pbsa_status st__ = (x);          \
-    if (st__ != PBSA_OK) return st__; \
-  } while (0)
-
 pbsa_status check_cache(const pbsa_cache* c) {
   if (!c) return fail(PBSA_ERR_NULL, "cache is NULL");
   if (!c->k || !c->v || !c->rep || !c->block_id || !c->len)
@@ -118,12 +114,17 @@ pbsa_status check_cache(const pbsa_cache* c) {
       reinterpret_cast<uintptr_t>(c->rep) % 16)
     return fail(PBSA_ERR_ALIGN, "cache k, v and rep must be 16-byte aligned");
   if (c->chunk_index < 0) return fail(PBSA_ERR_STATE, "chunk_index is negative");
+  if (reinterpret_cast<uintptr_t>(c->chunk_index_dev) % 8)
+    return fail(PBSA_ERR_ALIGN, "chunk_index_dev must be 8-byte aligned");
   return PBSA_OK;
 }
 
 hipStream_t stream_of(void* s) { return static_cast<hipStream_t>(s); }
 
-}  // namespace
+}  // namespace api
+}  // namespace pbsa
+
+using namespace pbsa::api;
 
 extern "C" {
 
@@ -160,6 +161,10 @@ size_t pbsa_workspace_bytes(const pbsa_dims* dims, int32_t op, int32_t arg, int3
   if (op == PBSA_OP_MEMORY_UPDATE) {
     if (check_dims(dims, 0) != PBSA_OK) return 0;
     return pbsa::memory_update_workspace(*dims);
+  }
+  if (op == PBSA_OP_ATTN_BWD_PERSISTENT) {
+    if (check_dims(dims, 0) != PBSA_OK) return 0;
+    return pbsa::attn_bwd_persistent_workspace(*dims);
   }
   if (op == PBSA_OP_ATTN_BWD) {
     if (check_dims(dims, 1) != PBSA_OK || arg < 1 || arg2 < 1) return 0;
@@ -237,7 +242,10 @@ pbsa_status pbsa_attn_fwd(const pbsa_dims* dims, pbsa_tensor q, const pbsa_cache
                     "attn_fwd");
 }
 
-namespace {
+}  // extern "C"
+
+namespace pbsa {
+namespace api {
 
 pbsa_status check_memory_ws(const pbsa_dims* dims, const pbsa_cache* cache, void* workspace,
                             size_t workspace_bytes, const char* name) {
@@ -250,7 +258,38 @@ pbsa_status check_memory_ws(const pbsa_dims* dims, const pbsa_cache* cache, void
   return PBSA_OK;
 }
 
-}  // namespace
+pbsa_status check_chunk_args(const pbsa_dims* dims, const pbsa_chunk_args* a,
+                             const pbsa_cache* cache) {
+  PBSA_TRY(check_dims(dims, 0));
+  PBSA_TRY(check_cache(cache));
+  if (!a) return fail(PBSA_ERR_NULL, "args is NULL");
+  if (a->passes < 1 || a->passes > PBSA_MAX_PASSES)
+    return fail(PBSA_ERR_SHAPE, "passes must be in [1, %d]", PBSA_MAX_PASSES);
+  const int64_t ctok = int64_t{dims->chunk_frames} * dims->frame_tokens;
+  const int64_t list = int64_t{dims->capacity} + int64_t{dims->chunk_frames} * pbsa::nb_of(*dims) +
+                       2 * int64_t{dims->topk};
+  if (list > pbsa::kAttnListCap)
+    return fail(PBSA_ERR_UNSUPPORTED, "capacity + chunk blocks + 2*topk = %lld exceeds %d",
+                static_cast<long long>(list), pbsa::kAttnListCap);
+  for (int p = 0; p < a->passes; ++p) {
+    PBSA_TRY(check_tok(a->q[p], "q", dims->head_dim));
+    PBSA_TRY(check_tok(a->k[p], "k", dims->head_dim));
+    PBSA_TRY(check_tok(a->v[p], "v", dims->head_dim));
+    PBSA_TRY(check_tok(a->o[p], "o", dims->head_dim));
+    PBSA_TRY(check_span(a->k[p], "k", ctok, dims->head_dim));
+    PBSA_TRY(check_span(a->v[p], "v", ctok, dims->head_dim));
+    if (!a->lse[p]) return fail(PBSA_ERR_NULL, "lse of pass %d is NULL", p);
+  }
+  if (!a->scores || !a->sel) return fail(PBSA_ERR_NULL, "scores and sel are required");
+  if (reinterpret_cast<uintptr_t>(a->q_rep) % 16)
+    return fail(PBSA_ERR_ALIGN, "q_rep must be 16-byte aligned");
+  return check_memory_ws(dims, cache, a->workspace, a->workspace_bytes, "chunk_step");
+}
+
+}  // namespace api
+}  // namespace pbsa
+
+extern "C" {
 
 pbsa_status pbsa_memory_select(const pbsa_dims* dims, const float* scores,
                                const pbsa_cache* cache, void* workspace, size_t workspace_bytes,
@@ -383,6 +422,44 @@ pbsa_status pbsa_attn_bwd(const pbsa_dims* dims, int32_t chunks, pbsa_tensor q, 
                                           pbsa::tok_out(dq), pbsa::tok_out(dk),
                                           pbsa::tok_out(dv), workspace, stream_of(stream)),
                     "attn_bwd");
+}
+
+pbsa_status pbsa_attn_bwd_persistent(const pbsa_dims* dims, pbsa_tensor q,
+                                     const pbsa_cache* cache, pbsa_tensor chunk_k,
+                                     pbsa_tensor chunk_v, const int32_t* sel, pbsa_tensor o,
+                                     const float* lse, pbsa_tensor dout, pbsa_tensor dq,
+                                     pbsa_tensor dk, pbsa_tensor dv, void* dk_cache,
+                                     void* dv_cache, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+  PBSA_TRY(check_dims(dims, 0));
+  PBSA_TRY(check_cache(cache));
+  const char* names[] = {"q", "chunk_k", "chunk_v", "o", "dout", "dq", "dk", "dv"};
+  const pbsa_tensor* ts[] = {&q, &chunk_k, &chunk_v, &o, &dout, &dq, &dk, &dv};
+  const int64_t ctok = int64_t{dims->chunk_frames} * dims->frame_tokens;
+  for (int i = 0; i < 8; ++i) {
+    PBSA_TRY(check_tok(*ts[i], names[i], dims->head_dim));
+    if (i < 5) PBSA_TRY(check_span(*ts[i], names[i], ctok, dims->head_dim));
+  }
+  if (!sel || !lse || !dk_cache || !dv_cache)
+    return fail(PBSA_ERR_NULL, "sel, lse, dk_cache and dv_cache are required");
+  if (reinterpret_cast<uintptr_t>(dk_cache) % 16 || reinterpret_cast<uintptr_t>(dv_cache) % 16)
+    return fail(PBSA_ERR_ALIGN, "dk_cache and dv_cache must be 16-byte aligned");
+  const int64_t list = int64_t{dims->capacity} + dims->topk +
+                       int64_t{dims->chunk_frames} * pbsa::nb_of(*dims);
+  if (list > pbsa::kAttnListCap / 2)
+    return fail(PBSA_ERR_UNSUPPORTED, "capacity + topk + chunk blocks = %lld exceeds %d",
+                static_cast<long long>(list), pbsa::kAttnListCap / 2);
+  const size_t need = pbsa::attn_bwd_persistent_workspace(*dims);
+  if (!workspace || workspace_bytes < need)
+    return fail(PBSA_ERR_WORKSPACE, "attn_bwd_persistent needs %zu workspace bytes (got %zu)",
+                need, workspace ? workspace_bytes : static_cast<size_t>(0));
+  return hip_status(pbsa::launch_attn_bwd_persistent(
+                        *dims, pbsa::tok_in(q), *cache, pbsa::tok_in(chunk_k),
+                        pbsa::tok_in(chunk_v), sel, pbsa::tok_in(o), lse, pbsa::tok_in(dout),
+                        pbsa::tok_out(dq), pbsa::tok_out(dk), pbsa::tok_out(dv),
+                        static_cast<uint16_t*>(dk_cache), static_cast<uint16_t*>(dv_cache),
+                        workspace, stream_of(stream)),
+                    "attn_bwd_persistent");
 }
 
 // ---- measurement probes (pbsa_probe.h)

@@ -6,7 +6,8 @@
 //   dV = P^T dO,  dP = dO V^T,  D = rowsum(dO * O),  dS = P * (dP - D),
 //   dQ = scale * dS K,  dK = scale * dS^T Q.
 //
-// gfx950 design (no atomics, so results are bit-reproducible):
+// gfx950 design (atomics only build integer lists and hand out work; every floating-point
+// sum runs in a fixed order, so results are bit-reproducible):
 //   dq pass   -- one workgroup per pair of query blocks of a head (four waves of 32 rows);
 //                like the forward it walks each query block's selected KV blocks in 32-key
 //                half tiles, recomputes S^T = K Q^T and dP^T = V dO^T on MFMA (Q, dO in
@@ -55,13 +56,37 @@ struct BwdArgs {
   int64_t T;
   int nq, nb, n, F, max_sel, H, pairs;
   float scale;
+  // KV blocks per head: the clip's blocks (two-level mode, nkv = nq), or, in persistent
+  // mode, the cache's slots 0..slots-1 followed by the chunk's nq blocks (k, v above are
+  // then the chunk's tokens)
+  int nkv;
+  int persist;
+  const uint16_t *ck, *cv;     // persistent: cache K/V [H][slots][64][D]
+  const int32_t *cbid, *clen;  // persistent: cache block ids and lengths [H][slots]
+  int slots, C, W, K;
+  const int32_t* rsel;         // persistent: routed window ids [H][nq][K]
+  uint16_t *dkc, *dvc;         // persistent: gradients of the cache slots [H][slots][64][D]
 };
 
-// A half tile (32 rows) of a block of a frame-major token tensor, rows [32*half, +32).
+// A half tile (32 rows) of a KV block, rows [32*half, +32): its first row, the row stride
+// of K and V in bytes, and the valid rows.
 struct Half {
   const uint16_t* p;
-  int len;  // valid rows (0 = none)
+  int len;      // valid rows (0 = none)
+  uint32_t sb;  // row stride (bytes)
 };
+
+// KV block list entries (32 bits): bit 31 set = a cache slot (bits 0..23 the slot), else
+// a token block (bits 0..23 its first token); bits 24..30 the valid rows.
+__device__ __forceinline__ uint32_t kv_entry(const BwdArgs& a, int h, int g) {
+  if (a.persist && g < a.slots)
+    return 0x80000000u | (static_cast<uint32_t>(a.clen[static_cast<int64_t>(h) * a.slots + g]) << 24) |
+           static_cast<uint32_t>(g);
+  const int b = a.persist ? g - a.slots : g;
+  return static_cast<uint32_t>(block_token0(b, a.nb, a.n)) |
+         (static_cast<uint32_t>(block_len(b % a.nb, a.n)) << 24);
+}
+__device__ __forceinline__ int entry_len(uint32_t e) { return static_cast<int>((e >> 24) & 0x7f); }
 
 
 // 16 bytes per lane from a buffer straight into LDS (lane l writes lds + 1024 i + 16 l):
@@ -182,23 +207,31 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
   const int nsteps = 2 * (cntA > cntB ? cntA : cntB);
   const uint16_t* kh = a.k + h * a.khs;
   const uint16_t* vh = a.v + h * a.vhs;
-  auto entry = [&](int g) {
-    return static_cast<uint32_t>(block_token0(g, a.nb, a.n)) |
-           (static_cast<uint32_t>(block_len(g % a.nb, a.n)) << 24);
-  };
+  // (persistent mode) this head's cache slots
+  const uint16_t* ckh = a.persist ? a.ck + static_cast<int64_t>(h) * a.slots * kBlock * D : nullptr;
+  const uint16_t* cvh = a.persist ? a.cv + static_cast<int64_t>(h) * a.slots * kBlock * D : nullptr;
   for (int j = t; j < (cntA > cntB ? cntA : cntB); j += 256) {
-    if (j < cntA) lstA[j] = entry(selA[j]);
-    if (j < cntB) lstB[j] = entry(selB[j]);
+    if (j < cntA) lstA[j] = kv_entry(a, h, selA[j]);
+    if (j < cntB) lstB[j] = kv_entry(a, h, selB[j]);
   }
   __syncthreads();
 
+  const uint32_t kstride_b = static_cast<uint32_t>(2 * a.kts);
+  const uint32_t vstride_b = static_cast<uint32_t>(2 * a.vts);
   // step s: half (s & 1) of A's and B's (s >> 1)-th selected block
   auto half_ref = [&](uint32_t e_, int half, Half& k_, Half& v_) {
     const uint32_t e = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(e_)));
-    const int64_t tk = (e & 0xffffffu) + 32 * half;
-    const int len = static_cast<int>(e >> 24) - 32 * half;
-    k_ = Half{kh + tk * a.kts, len < 0 ? 0 : (len < 32 ? len : 32)};
-    v_ = Half{vh + tk * a.vts, k_.len};
+    const int len = entry_len(e) - 32 * half;
+    const int hl = len < 0 ? 0 : (len < 32 ? len : 32);
+    if (e >> 31) {
+      const int64_t row0 = static_cast<int64_t>(e & 0xffffffu) * kBlock + 32 * half;
+      k_ = Half{ckh + row0 * D, hl, 2u * D};
+      v_ = Half{cvh + row0 * D, hl, 2u * D};
+    } else {
+      const int64_t tk = (e & 0xffffffu) + 32 * half;
+      k_ = Half{kh + tk * a.kts, hl, kstride_b};
+      v_ = Half{vh + tk * a.vts, hl, vstride_b};
+    }
   };
   auto refs = [&](int s, Half& kx, Half& vx, Half& ky, Half& vy) {
     const int j = s >> 1, half = s & 1;
@@ -207,8 +240,6 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
     if (j < cntB) half_ref(lstB[j], half, ky, vy);
   };
 
-  const uint32_t kstride_b = static_cast<uint32_t>(2 * a.kts);
-  const uint32_t vstride_b = static_cast<uint32_t>(2 * a.vts);
   // This lane's transposing-read offsets, opaque to the optimizer: it would otherwise split
   // each read's address into a chain of steps too long for the compiler to still see which
   // LDS array the read is from, and make the read wait for every gather in flight.
@@ -271,13 +302,21 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
       // then still sees that this read cannot touch a gather in flight)
       const uint32_t e = static_cast<uint32_t>(
           __builtin_amdgcn_readfirstlane(static_cast<int>(lst[mine * kHalfCap + j])));
-      const int tl = static_cast<int>(e >> 24) - 32 * half;
+      const int tl = entry_len(e) - 32 * half;
       const int len = tl < 0 ? 0 : (tl < 32 ? tl : 32);
       if (len == 0) return;
-      const int64_t tk = (e & 0xffffffu) + 32 * half;
-      const uint32_t sb = (w & 1) ? vstride_b : kstride_b;
-      const char* p = (w & 1) ? reinterpret_cast<const char*>(vh + tk * a.vts)
-                              : reinterpret_cast<const char*>(kh + tk * a.kts);
+      uint32_t sb;
+      const char* p;
+      if (e >> 31) {  // a cache slot (persistent mode)
+        const int64_t row0 = static_cast<int64_t>(e & 0xffffffu) * kBlock + 32 * half;
+        sb = 2u * D;
+        p = reinterpret_cast<const char*>(((w & 1) ? cvh : ckh) + row0 * D);
+      } else {
+        const int64_t tk = (e & 0xffffffu) + 32 * half;
+        sb = (w & 1) ? vstride_b : kstride_b;
+        p = (w & 1) ? reinterpret_cast<const char*>(vh + tk * a.vts)
+                    : reinterpret_cast<const char*>(kh + tk * a.kts);
+      }
       // scalar base 3 KB below the half tile: lane offsets lowered by a piece's immediate
       // offset (up to 3 KB) stay non-negative
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
@@ -315,10 +354,10 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
     Half kx, vx, ky, vy;
     if (nsteps > 0) {
       refs(0, kx, vx, ky, vy);
-      tkx.load(kx.p, kstride_b, kx.len, t);
-      tvx.load(vx.p, vstride_b, vx.len, t);
-      tky.load(ky.p, kstride_b, ky.len, t);
-      tvy.load(vy.p, vstride_b, vy.len, t);
+      tkx.load(kx.p, kx.sb, kx.len, t);
+      tvx.load(vx.p, vx.sb, vx.len, t);
+      tky.load(ky.p, ky.sb, ky.len, t);
+      tvy.load(vy.p, vy.sb, vy.len, t);
     }
     for (int st = 0; st < nsteps; ++st) {
       __syncthreads();
@@ -330,10 +369,10 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
       __syncthreads();
       if (st + 1 < nsteps) {
         refs(st + 1, kx, vx, ky, vy);
-        tkx.load(kx.p, kstride_b, kx.len, t);
-        tvx.load(vx.p, vstride_b, vx.len, t);
-        tky.load(ky.p, kstride_b, ky.len, t);
-        tvy.load(vy.p, vstride_b, vy.len, t);
+        tkx.load(kx.p, kx.sb, kx.len, t);
+        tvx.load(vx.p, vx.sb, vx.len, t);
+        tky.load(ky.p, ky.sb, ky.len, t);
+        tvy.load(vy.p, vy.sb, vy.len, t);
       }
       const int len = mine ? lenY : lenX;
       if (qlen > 0 && len > 0) half_step(tiles0, 2 * mine * HT, len);
@@ -360,7 +399,7 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
 // own inverse list, which the list pass reads whole before writing the list over it.
 __global__ void __launch_bounds__(256) attn_bwd_bits_clear_kernel(BwdArgs a) {
   const int W = (a.nq + 31) >> 5;
-  const int64_t n = static_cast<int64_t>(a.H) * a.nq * W;
+  const int64_t n = static_cast<int64_t>(a.H) * a.nkv * W;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
        i += static_cast<int64_t>(gridDim.x) * 256) {
     const int64_t row = i / W;
@@ -369,8 +408,8 @@ __global__ void __launch_bounds__(256) attn_bwd_bits_clear_kernel(BwdArgs a) {
 }
 
 // one workgroup per (query block, head): sets the query block's bit in the row of every
-// KV block it selected (a query block of chunk i sees frames < F*i only; other entries,
-// like ids outside the clip, are not listed)
+// KV block it selected (two-level mode: a query block of chunk i sees frames < F*i only;
+// other entries, like ids outside the clip, are not listed)
 __global__ void __launch_bounds__(128) attn_bwd_bits_set_kernel(BwdArgs a) {
   const int r = blockIdx.x, h = blockIdx.y;
   const int W = (a.nq + 31) >> 5;
@@ -379,10 +418,12 @@ __global__ void __launch_bounds__(128) attn_bwd_bits_set_kernel(BwdArgs a) {
   const int32_t* s = a.sel + hr * a.max_sel;
   for (int j = threadIdx.x; j < cnt; j += 128) {
     const int g = s[j];
-    if (g < 0 || g >= a.nq) continue;
-    const int f = g / a.nb;
-    if (r < (f / a.F) * a.F * a.nb) continue;
-    int32_t* row = a.inv + (static_cast<int64_t>(h) * a.nq + g) * a.nq + (a.nq - W);
+    if (g < 0 || g >= a.nkv) continue;
+    if (!a.persist) {
+      const int f = g / a.nb;
+      if (r < (f / a.F) * a.F * a.nb) continue;
+    }
+    int32_t* row = a.inv + (static_cast<int64_t>(h) * a.nkv + g) * a.nq + (a.nq - W);
     atomicOr(reinterpret_cast<unsigned int*>(row + (r >> 5)), 1u << (r & 31));
   }
 }
@@ -396,7 +437,7 @@ __global__ void __launch_bounds__(256) attn_bwd_bits_list_kernel(BwdArgs a) {
   const int g = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
   const int w = t >> 6, l = t & 63;
   const int W = (a.nq + 31) >> 5;
-  int32_t* out = a.inv + (static_cast<int64_t>(h) * a.nq + g) * a.nq;
+  int32_t* out = a.inv + (static_cast<int64_t>(h) * a.nkv + g) * a.nq;
   for (int j = t; j < W; j += 256) bits[j] = static_cast<uint32_t>(out[a.nq - W + j]);
   __syncthreads();  // every word is read before the list overwrites the row's tail
   int total = 0;
@@ -421,7 +462,7 @@ __global__ void __launch_bounds__(256) attn_bwd_bits_list_kernel(BwdArgs a) {
     total += wsum[0] + wsum[1] + wsum[2] + wsum[3];
     __syncthreads();
   }
-  if (t == 0) a.inv_cnt[static_cast<int64_t>(h) * a.nq + g] = total;
+  if (t == 0) a.inv_cnt[static_cast<int64_t>(h) * a.nkv + g] = total;
 }
 
 // ------------------------------------------------------------------ plan
@@ -433,7 +474,7 @@ constexpr int kSplitQ = 96;  // query blocks per dK/dV work item, at most
 __global__ void __launch_bounds__(1024) attn_bwd_plan_kernel(BwdArgs a) {
   __shared__ int sc[3][1024];
   const int t = threadIdx.x;
-  const int N = a.H * a.nq;
+  const int N = a.H * a.nkv;
   const int per = (N + 1023) / 1024;
   const int e0 = t * per, e1 = min(N, e0 + per);
   int my_items = 0, my_parts = 0, my_long = 0;
@@ -562,14 +603,23 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdArgs a) {
     if (item >= n_items) break;
     const int2 it = a.sorted[item];
     const int hg = __builtin_amdgcn_readfirstlane(it.x), sp = __builtin_amdgcn_readfirstlane(it.y);
-    const int h = hg / a.nq, g = hg - h * a.nq;
-    const int64_t k0 = block_token0(g, a.nb, a.n);
-    const int klen = block_len(g % a.nb, a.n);
+    const int h = hg / a.nkv, g = hg - h * a.nkv;
+    // the item's KV block: a cache slot (persistent mode, g < slots) or a token block
+    const bool is_slot = a.persist && g < a.slots;
+    const int b = a.persist && !is_slot ? g - a.slots : g;
+    const int64_t k0 = is_slot ? 0 : block_token0(b, a.nb, a.n);
+    const int klen = is_slot ? a.clen[static_cast<int64_t>(h) * a.slots + g] : block_len(b % a.nb, a.n);
     __syncthreads();  // s_item is read and the previous item's sums are consumed
     {
       Tile<D, 256> tk, tv;
-      tk.load(a.k + h * a.khs + k0 * a.kts, static_cast<uint32_t>(2 * a.kts), klen, t);
-      tv.load(a.v + h * a.vhs + k0 * a.vts, static_cast<uint32_t>(2 * a.vts), klen, t);
+      if (is_slot) {
+        const int64_t so = (static_cast<int64_t>(h) * a.slots + g) * kBlock * D;
+        tk.load(a.ck + so, 2u * D, klen, t);
+        tv.load(a.cv + so, 2u * D, klen, t);
+      } else {
+        tk.load(a.k + h * a.khs + k0 * a.kts, static_cast<uint32_t>(2 * a.kts), klen, t);
+        tv.load(a.v + h * a.vhs + k0 * a.vts, static_cast<uint32_t>(2 * a.vts), klen, t);
+      }
       tk.store_rows(Kb, t);
       tv.store_rows(Vb, t);
     }
@@ -689,9 +739,18 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdArgs a) {
         }
       }
     if (a.nsplit[hg] == 1) {
-      if (key < klen) {
-        uint16_t* ko = a.dk + h * a.dkhs + (k0 + key) * a.dkts;
-        uint16_t* vo = a.dv + h * a.dvhs + (k0 + key) * a.dvts;
+      // a cache slot's gradient covers all 64 rows (zero past its length)
+      if (key < klen || is_slot) {
+        if (key >= klen) {
+#pragma unroll
+          for (int dt = 0; dt < ND; ++dt) {
+            dk[dt] = f32x16{};
+            dv[dt] = f32x16{};
+          }
+        }
+        const int64_t so = (static_cast<int64_t>(h) * a.slots + g) * kBlock * D + key * D;
+        uint16_t* ko = is_slot ? a.dkc + so : a.dk + h * a.dkhs + (k0 + key) * a.dkts;
+        uint16_t* vo = is_slot ? a.dvc + so : a.dv + h * a.dvhs + (k0 + key) * a.dvts;
 #pragma unroll
         for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
@@ -732,11 +791,13 @@ __global__ void __launch_bounds__(128) attn_bwd_reduce_kernel(BwdArgs a) {
   const int j = blockIdx.x;
   if (j >= a.counts[1]) return;
   const int hg = a.long_list[j];
-  const int h = hg / a.nq, g = hg - h * a.nq;
+  const int h = hg / a.nkv, g = hg - h * a.nkv;
   const int t = threadIdx.x, l = t & 63, w = t >> 6, h2 = l >> 5, c32 = l & 31;
   const int key = 32 * w + c32;
-  const int64_t k0 = block_token0(g, a.nb, a.n);
-  const int klen = block_len(g % a.nb, a.n);
+  const bool is_slot = a.persist && g < a.slots;
+  const int b = a.persist && !is_slot ? g - a.slots : g;
+  const int64_t k0 = is_slot ? 0 : block_token0(b, a.nb, a.n);
+  const int klen = is_slot ? a.clen[static_cast<int64_t>(h) * a.slots + g] : block_len(b % a.nb, a.n);
   const int ns = a.nsplit[hg];
   const float* p0 = a.part + static_cast<int64_t>(a.part_base[hg]) * (2 * kBlock * D);
   f32x16 dk[ND], dv[ND];
@@ -760,9 +821,17 @@ __global__ void __launch_bounds__(128) attn_bwd_reduce_kernel(BwdArgs a) {
         }
       }
   }
-  if (key < klen) {
-    uint16_t* ko = a.dk + h * a.dkhs + (k0 + key) * a.dkts;
-    uint16_t* vo = a.dv + h * a.dvhs + (k0 + key) * a.dvts;
+  if (key < klen || is_slot) {
+    if (key >= klen) {
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) {
+        dk[dt] = f32x16{};
+        dv[dt] = f32x16{};
+      }
+    }
+    const int64_t so = (static_cast<int64_t>(h) * a.slots + g) * kBlock * D + key * D;
+    uint16_t* ko = is_slot ? a.dkc + so : a.dk + h * a.dkhs + (k0 + key) * a.dkts;
+    uint16_t* vo = is_slot ? a.dvc + so : a.dv + h * a.dvhs + (k0 + key) * a.dvts;
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
@@ -778,60 +847,76 @@ __global__ void __launch_bounds__(128) attn_bwd_reduce_kernel(BwdArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ persistent lists
+// grid (nq, H), one wave: query block r's KV list in persistent mode, as virtual block ids
+// (cache slots, then the chunk's blocks at slots + b): the occupied persistent slots in
+// slot order, the window slots of its routed blocks in routed order, then every block of
+// the chunk -- exactly the blocks pbsa_attn_fwd attends.
+__global__ void __launch_bounds__(64) attn_bwd_lists_persist_kernel(BwdArgs a, int32_t* sel,
+                                                                    int32_t* nsel) {
+  const int r = blockIdx.x, h = blockIdx.y, l = threadIdx.x;
+  const int64_t hr = static_cast<int64_t>(h) * a.nq + r;
+  int32_t* out = sel + hr * a.max_sel;
+  const int32_t* bid = a.cbid + static_cast<int64_t>(h) * a.slots;
+  const unsigned long long below = (1ull << l) - 1ull;
+  int n = 0;
+  for (int s0 = 0; s0 < a.C; s0 += 64) {
+    const int s = s0 + l;
+    const bool on = s < a.C && bid[s] >= 0;
+    const unsigned long long m = __ballot(on);
+    if (on) out[n + __popcll(m & below)] = s;
+    n += __popcll(m);
+  }
+  const int32_t* rs = a.rsel + hr * a.K;
+  for (int j0 = 0; j0 < a.K; j0 += 64) {
+    const int j = j0 + l;
+    const int g = j < a.K ? rs[j] : -1;
+    const bool on = g >= 0;
+    const unsigned long long m = __ballot(on);
+    if (on) out[n + __popcll(m & below)] = a.C + ((g / a.nb) % a.W) * a.nb + g % a.nb;
+    n += __popcll(m);
+  }
+  for (int b = l; b < a.nq; b += 64) out[n + b] = a.slots + b;
+  n += a.nq;
+  if (l == 0) nsel[hr] = n;
+}
+
 namespace {
-// Workspace layout of the backward (bytes, 256-aligned pieces).
+// Workspace layout of the backward (bytes, 256-aligned pieces).  Persistent mode adds the
+// query blocks' KV lists and their lengths.
 struct BwdWs {
-  size_t D, inv_cnt, inv, items, sorted, nsplit, part_base, long_list, counts, part, total;
+  size_t D, inv_cnt, inv, items, sorted, nsplit, part_base, long_list, counts, part, lists,
+      nlists, total;
 };
-BwdWs bwd_ws(const pbsa_dims& d, int chunks, int max_sel) {
-  const int64_t nq = static_cast<int64_t>(chunks) * d.chunk_frames * nb_of(d);
-  const int64_t T = static_cast<int64_t>(chunks) * d.chunk_frames * d.frame_tokens;
-  const int64_t H = d.heads;
-  const int64_t pairs_max = H * nq * max_sel;                 // selected (query, KV) pairs
-  const int64_t items_max = H * nq + pairs_max / kSplitQ + 1;  // work items
-  const int64_t parts_max = 2 * (pairs_max / kSplitQ) + 2;     // partial slots
+BwdWs bwd_ws(int64_t H, int64_t nq, int64_t nkv, int64_t T, int64_t max_sel, int head_dim,
+             bool persist) {
+  const int64_t pairs_max = H * nq * max_sel;                  // selected (query, KV) pairs
+  const int64_t items_max = H * nkv + pairs_max / kSplitQ + 1;  // work items
+  const int64_t parts_max = 2 * (pairs_max / kSplitQ) + 2;      // partial slots
   auto up = [](size_t x) { return (x + 255) & ~size_t{255}; };
   BwdWs w{};
   size_t o = 0;
   w.D = o; o += up(H * T * 4);
-  w.inv_cnt = o; o += up(H * nq * 4);
-  w.inv = o; o += up(H * nq * nq * 4);
+  w.inv_cnt = o; o += up(H * nkv * 4);
+  w.inv = o; o += up(H * nkv * nq * 4);
   w.items = o; o += up(items_max * 8);
   w.sorted = o; o += up(items_max * 8);
-  w.nsplit = o; o += up(H * nq * 4);
-  w.part_base = o; o += up(H * nq * 4);
-  w.long_list = o; o += up(H * nq * 4);
+  w.nsplit = o; o += up(H * nkv * 4);
+  w.part_base = o; o += up(H * nkv * 4);
+  w.long_list = o; o += up(H * nkv * 4);
   w.counts = o; o += up(16);
-  w.part = o; o += up(static_cast<size_t>(parts_max) * 2 * kBlock * d.head_dim * 4);
+  w.part = o; o += up(static_cast<size_t>(parts_max) * 2 * kBlock * head_dim * 4);
+  w.lists = o; o += persist ? up(H * nq * max_sel * 4) : 0;
+  w.nlists = o; o += persist ? up(H * nq * 4) : 0;
   w.total = o;
   return w;
 }
-}  // namespace
 
-size_t attn_bwd_workspace(const pbsa_dims& d, int chunks, int max_sel) {
-  return bwd_ws(d, chunks, max_sel).total;
+int64_t persist_max_sel(const pbsa_dims& d) {
+  return static_cast<int64_t>(d.capacity) + d.topk + static_cast<int64_t>(d.chunk_frames) * nb_of(d);
 }
 
-hipError_t launch_attn_bwd(const pbsa_dims& d, int chunks, TokIn q, TokIn k, TokIn v, TokIn o,
-                           const float* lse, TokIn dout, const int32_t* sel,
-                           const int32_t* nsel, int max_sel, TokOut dq, TokOut dk, TokOut dv,
-                           void* ws, hipStream_t s) {
-  const int nb = nb_of(d);
-  const int nq = chunks * d.chunk_frames * nb;
-  const int64_t T = static_cast<int64_t>(chunks) * d.chunk_frames * d.frame_tokens;
-  BwdArgs a;
-  a.q = q.p; a.qts = q.ts; a.qhs = q.hs;
-  a.k = k.p; a.kts = k.ts; a.khs = k.hs;
-  a.v = v.p; a.vts = v.ts; a.vhs = v.hs;
-  a.o = o.p; a.ots = o.ts; a.ohs = o.hs;
-  a.dout = dout.p; a.dts = dout.ts; a.dhs = dout.hs;
-  a.dq = dq.p; a.dqts = dq.ts; a.dqhs = dq.hs;
-  a.dk = dk.p; a.dkts = dk.ts; a.dkhs = dk.hs;
-  a.dv = dv.p; a.dvts = dv.ts; a.dvhs = dv.hs;
-  a.lse = lse;
-  a.sel = sel;
-  a.nsel = nsel;
-  const BwdWs L = bwd_ws(d, chunks, max_sel);
+void bind_ws(BwdArgs& a, const BwdWs& L, void* ws) {
   char* p = static_cast<char*>(ws);
   a.Dw = reinterpret_cast<float*>(p + L.D);
   a.inv_cnt = reinterpret_cast<int32_t*>(p + L.inv_cnt);
@@ -843,8 +928,92 @@ hipError_t launch_attn_bwd(const pbsa_dims& d, int chunks, TokIn q, TokIn k, Tok
   a.long_list = reinterpret_cast<int32_t*>(p + L.long_list);
   a.counts = reinterpret_cast<int32_t*>(p + L.counts);
   a.part = reinterpret_cast<float*>(p + L.part);
+}
+
+void bind_tokens(BwdArgs& a, TokIn q, TokIn k, TokIn v, TokIn o, const float* lse, TokIn dout,
+                 TokOut dq, TokOut dk, TokOut dv) {
+  a.q = q.p; a.qts = q.ts; a.qhs = q.hs;
+  a.k = k.p; a.kts = k.ts; a.khs = k.hs;
+  a.v = v.p; a.vts = v.ts; a.vhs = v.hs;
+  a.o = o.p; a.ots = o.ts; a.ohs = o.hs;
+  a.dout = dout.p; a.dts = dout.ts; a.dhs = dout.hs;
+  a.dq = dq.p; a.dqts = dq.ts; a.dqhs = dq.hs;
+  a.dk = dk.p; a.dkts = dk.ts; a.dkhs = dk.hs;
+  a.dv = dv.p; a.dvts = dv.ts; a.dvhs = dv.hs;
+  a.lse = lse;
+}
+
+// dQ pass, inverse lists, plan, dK/dV pass, reduce (a fully set up).
+hipError_t launch_bwd_passes(const BwdArgs& a, int head_dim, hipStream_t s) {
+  const int gq = 8 * cdiv(a.H * a.pairs, 8);
+  if (head_dim == 128)
+    hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, dim3(gq), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, dim3(gq), dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.nq > 32 * kMaxBitWords) return hipErrorInvalidValue;
+  {
+    const int64_t words = static_cast<int64_t>(a.H) * a.nkv * ((a.nq + 31) / 32);
+    const int64_t blocks = (words + 255) / 256;
+    const int gc = static_cast<int>(blocks < 2048 ? blocks : 2048);
+    hipLaunchKernelGGL(attn_bwd_bits_clear_kernel, dim3(gc), dim3(256), 0, s, a);
+  }
+  hipLaunchKernelGGL(attn_bwd_bits_set_kernel, dim3(a.nq, a.H), dim3(128), 0, s, a);
+  hipLaunchKernelGGL(attn_bwd_bits_list_kernel, dim3(a.nkv, a.H), dim3(256), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_bwd_plan_kernel, dim3(1), dim3(1024), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t items_max = static_cast<int64_t>(a.H) * a.nkv +
+                            static_cast<int64_t>(a.H) * a.nq * a.max_sel / kSplitQ + 1;
+  // enough workgroups to fill every CU; they take items from the counter until none is left
+  const int gi = static_cast<int>(items_max < 1024 ? items_max : 1024);
+  if (head_dim == 128)
+    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<128>, dim3(gi), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<64>, dim3(gi), dim3(256), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int gr = a.H * a.nkv;
+  if (head_dim == 128)
+    hipLaunchKernelGGL(attn_bwd_reduce_kernel<128>, dim3(gr), dim3(128), 0, s, a);
+  else
+    hipLaunchKernelGGL(attn_bwd_reduce_kernel<64>, dim3(gr), dim3(128), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t attn_bwd_workspace(const pbsa_dims& d, int chunks, int max_sel) {
+  const int64_t nq = static_cast<int64_t>(chunks) * d.chunk_frames * nb_of(d);
+  const int64_t T = static_cast<int64_t>(chunks) * d.chunk_frames * d.frame_tokens;
+  return bwd_ws(d.heads, nq, nq, T, max_sel, d.head_dim, false).total;
+}
+
+size_t attn_bwd_persistent_workspace(const pbsa_dims& d) {
+  const int64_t nq = static_cast<int64_t>(d.chunk_frames) * nb_of(d);
+  const int64_t T = static_cast<int64_t>(d.chunk_frames) * d.frame_tokens;
+  return bwd_ws(d.heads, nq, slots_of(d) + nq, T, persist_max_sel(d), d.head_dim, true).total;
+}
+
+hipError_t launch_attn_bwd(const pbsa_dims& d, int chunks, TokIn q, TokIn k, TokIn v, TokIn o,
+                           const float* lse, TokIn dout, const int32_t* sel,
+                           const int32_t* nsel, int max_sel, TokOut dq, TokOut dk, TokOut dv,
+                           void* ws, hipStream_t s) {
+  const int nb = nb_of(d);
+  const int nq = chunks * d.chunk_frames * nb;
+  const int64_t T = static_cast<int64_t>(chunks) * d.chunk_frames * d.frame_tokens;
+  BwdArgs a{};
+  bind_tokens(a, q, k, v, o, lse, dout, dq, dk, dv);
+  a.sel = sel;
+  a.nsel = nsel;
+  bind_ws(a, bwd_ws(d.heads, nq, nq, T, max_sel, d.head_dim, false), ws);
   a.T = T;
   a.nq = nq;
+  a.nkv = nq;
+  a.persist = 0;
   a.nb = nb;
   a.n = d.frame_tokens;
   a.F = d.chunk_frames;
@@ -852,44 +1021,55 @@ hipError_t launch_attn_bwd(const pbsa_dims& d, int chunks, TokIn q, TokIn k, Tok
   a.H = d.heads;
   a.pairs = cdiv(nq, 2);
   a.scale = d.scale;
-  const int gq = 8 * cdiv(d.heads * a.pairs, 8);
-  if (d.head_dim == 128)
-    hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, dim3(gq), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, dim3(gq), dim3(256), 0, s, a);
-  hipError_t e = hipGetLastError();
+  return launch_bwd_passes(a, d.head_dim, s);
+}
+
+hipError_t launch_attn_bwd_persistent(const pbsa_dims& d, TokIn q, const pbsa_cache& c,
+                                      TokIn ck, TokIn cv, const int32_t* sel, TokIn o,
+                                      const float* lse, TokIn dout, TokOut dq, TokOut dk,
+                                      TokOut dv, uint16_t* dk_cache, uint16_t* dv_cache,
+                                      void* ws, hipStream_t s) {
+  const int nb = nb_of(d);
+  const int nq = d.chunk_frames * nb;
+  const int64_t T = static_cast<int64_t>(d.chunk_frames) * d.frame_tokens;
+  const int slots = static_cast<int>(slots_of(d));
+  const int max_sel = static_cast<int>(persist_max_sel(d));
+  BwdArgs a{};
+  bind_tokens(a, q, ck, cv, o, lse, dout, dq, dk, dv);
+  const BwdWs L = bwd_ws(d.heads, nq, slots + nq, T, max_sel, d.head_dim, true);
+  bind_ws(a, L, ws);
+  char* p = static_cast<char*>(ws);
+  int32_t* lists = reinterpret_cast<int32_t*>(p + L.lists);
+  int32_t* nlists = reinterpret_cast<int32_t*>(p + L.nlists);
+  a.sel = lists;
+  a.nsel = nlists;
+  a.T = T;
+  a.nq = nq;
+  a.nkv = slots + nq;
+  a.persist = 1;
+  a.ck = static_cast<const uint16_t*>(c.k);
+  a.cv = static_cast<const uint16_t*>(c.v);
+  a.cbid = c.block_id;
+  a.clen = c.len;
+  a.slots = slots;
+  a.C = d.capacity;
+  a.W = d.window_frames;
+  a.K = d.topk;
+  a.rsel = sel;
+  a.dkc = dk_cache;
+  a.dvc = dv_cache;
+  a.nb = nb;
+  a.n = d.frame_tokens;
+  a.F = d.chunk_frames;
+  a.max_sel = max_sel;
+  a.H = d.heads;
+  a.pairs = cdiv(nq, 2);
+  a.scale = d.scale;
+  hipLaunchKernelGGL(attn_bwd_lists_persist_kernel, dim3(nq, d.heads), dim3(64), 0, s, a, lists,
+                     nlists);
+  const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (nq > 32 * kMaxBitWords) return hipErrorInvalidValue;
-  {
-    const int64_t words = static_cast<int64_t>(d.heads) * nq * ((nq + 31) / 32);
-    const int64_t blocks = (words + 255) / 256;
-    const int gc = static_cast<int>(blocks < 2048 ? blocks : 2048);
-    hipLaunchKernelGGL(attn_bwd_bits_clear_kernel, dim3(gc), dim3(256), 0, s, a);
-  }
-  dim3 grid(nq, d.heads);
-  hipLaunchKernelGGL(attn_bwd_bits_set_kernel, grid, dim3(128), 0, s, a);
-  hipLaunchKernelGGL(attn_bwd_bits_list_kernel, grid, dim3(256), 0, s, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_bwd_plan_kernel, dim3(1), dim3(1024), 0, s, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int64_t items_max = static_cast<int64_t>(d.heads) * nq +
-                            static_cast<int64_t>(d.heads) * nq * max_sel / kSplitQ + 1;
-  // enough workgroups to fill every CU; they take items from the counter until none is left
-  const int gi = static_cast<int>(items_max < 1024 ? items_max : 1024);
-  if (d.head_dim == 128)
-    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<128>, dim3(gi), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<64>, dim3(gi), dim3(256), 0, s, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int gr = d.heads * nq;
-  if (d.head_dim == 128)
-    hipLaunchKernelGGL(attn_bwd_reduce_kernel<128>, dim3(gr), dim3(128), 0, s, a);
-  else
-    hipLaunchKernelGGL(attn_bwd_reduce_kernel<64>, dim3(gr), dim3(128), 0, s, a);
-  return hipGetLastError();
+  return launch_bwd_passes(a, d.head_dim, s);
 }
 
 }  // namespace pbsa

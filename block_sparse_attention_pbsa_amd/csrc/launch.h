@@ -62,6 +62,12 @@ hipError_t launch_attn_fwd_2lvl(const pbsa_dims& d, int chunks, TokIn q, TokIn k
                                 float* lse, hipStream_t s);
 
 size_t attn_bwd_workspace(const pbsa_dims& d, int chunks, int max_sel);
+size_t attn_bwd_persistent_workspace(const pbsa_dims& d);
+hipError_t launch_attn_bwd_persistent(const pbsa_dims& d, TokIn q, const pbsa_cache& c,
+                                      TokIn ck, TokIn cv, const int32_t* sel, TokIn o,
+                                      const float* lse, TokIn dout, TokOut dq, TokOut dk,
+                                      TokOut dv, uint16_t* dk_cache, uint16_t* dv_cache,
+                                      void* ws, hipStream_t s);
 hipError_t launch_attn_bwd(const pbsa_dims& d, int chunks, TokIn q, TokIn k, TokIn v, TokIn o,
                            const float* lse, TokIn dout, const int32_t* sel,
                            const int32_t* nsel, int max_sel, TokOut dq, TokOut dk, TokOut dv,

@@ -36,8 +36,23 @@ struct MemArgs {
   int32_t* pbid;        // workspace [H][C]: the new persistent table (block ids) ...
   int32_t* plen;        // ... and lengths, written by the select, applied by the copy
   int slots, C, S, W, F, nb, n, nq;
-  int64_t chunk;        // chunk index being appended
+  int64_t chunk;        // chunk index being appended (host copy)
+  // Optional device chunk counter (NULL: the host copy above is used).  The select reads
+  // it and records the value it used in ws_chunk; the copy pass reads ws_chunk and one of
+  // its threads advances the counter when done, so a captured update replays correctly
+  // for successive chunks.
+  int64_t* chunk_dev;
+  int64_t* ws_chunk;    // workspace: the chunk index the select used
 };
+
+// The chunk index of this update, as the select sees it.
+__device__ __forceinline__ int64_t select_chunk(const MemArgs& a) {
+  return a.chunk_dev ? *a.chunk_dev : a.chunk;
+}
+// ... and as the copy pass sees it (what the select recorded).
+__device__ __forceinline__ int64_t copy_chunk(const MemArgs& a) {
+  return a.chunk_dev ? *a.ws_chunk : a.chunk;
+}
 
 // grid H, 1024 threads per head (256 when the candidate count needs more sort registers).  Candidates are listed in a fixed order (persistent
 // non-sink slots ascending, then the leaving blocks in chunk-block order, which is
@@ -70,13 +85,15 @@ __global__ void __launch_bounds__(NT) memory_select_kernel(MemArgs a) {
   const int32_t* bid = a.bid + static_cast<int64_t>(h) * a.slots;
   const int32_t* blen = a.blen + static_cast<int64_t>(h) * a.slots;
   int32_t* dst = a.copy_dst + static_cast<int64_t>(h) * a.F * a.nb;
-  const int64_t hF = a.chunk * a.F;  // frames appended so far
+  const int64_t chunk = select_chunk(a);
+  if (a.chunk_dev && h == 0 && t == 0) *a.ws_chunk = chunk;
+  const int64_t hF = chunk * a.F;  // frames appended so far
   const int fnb = a.F * a.nb;
 
   for (int b = t; b < fnb; b += NT) dst[b] = -1;
   int32_t* pbid = a.pbid + static_cast<int64_t>(h) * a.C;
   int32_t* plen = a.plen + static_cast<int64_t>(h) * a.C;
-  if (a.chunk == 0) {
+  if (chunk == 0) {
     // empty cache: P_t becomes the sinks (block g in slot g; the copy pass moves them)
     for (int s = t; s < a.C; s += NT) {
       pbid[s] = s < a.S ? s : -1;
@@ -241,7 +258,8 @@ template <int D>
 __global__ void __launch_bounds__(256) memory_copy_kernel(MemArgs a, TokIn xk, TokIn xv,
                                                           const float* __restrict__ chunk_rep) {
   const int b = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
-  const int64_t hF = a.chunk * a.F;
+  const int64_t chunk = copy_chunk(a);
+  const int64_t hF = chunk * a.F;
   const int fl = b / a.nb, j = b - fl * a.nb;  // chunk-local frame, block
   const int64_t f = hF + fl;
   const int ring = a.C + static_cast<int>(f % a.W) * a.nb + j;
@@ -271,7 +289,7 @@ __global__ void __launch_bounds__(256) memory_copy_kernel(MemArgs a, TokIn xk, T
   }
   __syncthreads();
   // chunk 0's sink blocks go straight to their persistent slots; the window slot stays empty
-  const bool sink = a.chunk == 0 && g < a.S;
+  const bool sink = chunk == 0 && g < a.S;
   const int target = sink ? g : ring;
   const int64_t tok0 = static_cast<int64_t>(fl) * a.n + static_cast<int64_t>(kBlock) * j;
   // thread t holds channels 8 (t % CH) .. of rows t / CH + (256 / CH) p; their K sums give
@@ -327,13 +345,16 @@ __global__ void __launch_bounds__(256) memory_copy_kernel(MemArgs a, TokIn xk, T
   if (t == 0) {
     a.bid[hs + ring] = sink ? -1 : g;
     a.blen[hs + ring] = sink ? 0 : len;
+    // the device counter moves on (only this workgroup writes it; the others read the
+    // index the select recorded)
+    if (a.chunk_dev && b == 0 && h == 0) *a.chunk_dev = chunk + 1;
   }
 }
 
 namespace {
 
 // Workspace: copy list [H][F*nb], then the new persistent table [H][C] (ids, lengths),
-// each piece 256-byte aligned.
+// then the chunk index the select used, each piece 256-byte aligned.
 size_t ws_up(size_t x) { return (x + 255) & ~size_t{255}; }
 
 MemArgs mem_args(const pbsa_dims& d, const float* scores, const pbsa_cache& c, void* ws) {
@@ -351,6 +372,8 @@ MemArgs mem_args(const pbsa_dims& d, const float* scores, const pbsa_cache& c, v
   a.copy_dst = reinterpret_cast<int32_t*>(p);
   a.pbid = reinterpret_cast<int32_t*>(p + ncopy);
   a.plen = reinterpret_cast<int32_t*>(p + ncopy + ntab);
+  a.ws_chunk = reinterpret_cast<int64_t*>(p + ncopy + 2 * ntab);
+  a.chunk_dev = c.chunk_index_dev;
   a.slots = static_cast<int>(slots_of(d));
   a.C = d.capacity;
   a.S = d.sinks;
@@ -367,7 +390,8 @@ MemArgs mem_args(const pbsa_dims& d, const float* scores, const pbsa_cache& c, v
 
 size_t memory_update_workspace(const pbsa_dims& d) {
   return ws_up(sizeof(int32_t) * static_cast<size_t>(d.heads) * d.chunk_frames * nb_of(d)) +
-         2 * ws_up(sizeof(int32_t) * static_cast<size_t>(d.heads) * d.capacity);
+         2 * ws_up(sizeof(int32_t) * static_cast<size_t>(d.heads) * d.capacity) +
+         ws_up(sizeof(int64_t));
 }
 
 hipError_t launch_memory_select(const pbsa_dims& d, const float* scores, const pbsa_cache& c,
@@ -417,19 +441,21 @@ hipError_t launch_memory_update(const pbsa_dims& d, const float* scores, const p
 
 namespace pbsa {
 
-__global__ void cache_reset_kernel(int32_t* bid, int32_t* blen, int64_t total) {
+__global__ void cache_reset_kernel(int32_t* bid, int32_t* blen, int64_t total,
+                                   int64_t* chunk_dev) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i < total) {
     bid[i] = -1;
     blen[i] = 0;
   }
+  if (chunk_dev && i == 0) *chunk_dev = 0;
 }
 
 hipError_t launch_cache_reset(const pbsa_dims& d, const pbsa_cache& c, hipStream_t s) {
   const int64_t total = static_cast<int64_t>(d.heads) * slots_of(d);
   if (total == 0) return hipSuccess;
   hipLaunchKernelGGL(cache_reset_kernel, dim3(static_cast<unsigned>((total + 255) / 256)),
-                     dim3(256), 0, s, c.block_id, c.len, total);
+                     dim3(256), 0, s, c.block_id, c.len, total, c.chunk_index_dev);
   return hipGetLastError();
 }
 

@@ -23,6 +23,7 @@ _lib = None
 PBSA_OK = 0
 PBSA_OP_MEMORY_UPDATE = 1
 PBSA_OP_ATTN_BWD = 2
+PBSA_OP_ATTN_BWD_PERSISTENT = 3
 
 
 class PbsaError(RuntimeError):
@@ -47,7 +48,18 @@ class Tensor(ctypes.Structure):
 class CacheC(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("rep", ctypes.c_void_p),
                 ("block_id", ctypes.c_void_p), ("len", ctypes.c_void_p),
-                ("chunk_index", ctypes.c_int64)]
+                ("chunk_index", ctypes.c_int64), ("chunk_index_dev", ctypes.c_void_p)]
+
+
+MAX_PASSES = 8
+
+
+class ChunkArgs(ctypes.Structure):
+    _fields_ = [("passes", ctypes.c_int32), ("q", Tensor * MAX_PASSES),
+                ("k", Tensor * MAX_PASSES), ("v", Tensor * MAX_PASSES),
+                ("o", Tensor * MAX_PASSES), ("lse", ctypes.c_void_p * MAX_PASSES),
+                ("q_rep", ctypes.c_void_p), ("scores", ctypes.c_void_p), ("sel", ctypes.c_void_p),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
 
 
 _P = ctypes.c_void_p
@@ -80,6 +92,15 @@ _SIGS = {
     "pbsa_attn_bwd": ([ctypes.POINTER(Dims), _I32, Tensor, Tensor, Tensor, Tensor, _P, Tensor,
                        _P, _P, _I32, Tensor, Tensor, Tensor, _P, ctypes.c_size_t, _P],
                       ctypes.c_int),
+    "pbsa_attn_bwd_persistent": ([ctypes.POINTER(Dims), Tensor, ctypes.POINTER(CacheC), Tensor,
+                                  Tensor, _P, Tensor, _P, Tensor, Tensor, Tensor, Tensor, _P, _P,
+                                  _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "pbsa_chunk_step": ([ctypes.POINTER(Dims), ctypes.POINTER(ChunkArgs), ctypes.POINTER(CacheC),
+                         _P], ctypes.c_int),
+    "pbsa_chunk_graph_create": ([ctypes.POINTER(Dims), ctypes.POINTER(ChunkArgs),
+                                 ctypes.POINTER(CacheC), ctypes.POINTER(_P)], ctypes.c_int),
+    "pbsa_chunk_graph_launch": ([_P, ctypes.POINTER(CacheC), _P], ctypes.c_int),
+    "pbsa_chunk_graph_destroy": ([_P], None),
     # measurement probes (pbsa_probe.h)
     "pbsa_probe_mfma": ([ctypes.c_int64, _P, _P], ctypes.c_int),
     "pbsa_probe_mfma_flop": ([ctypes.c_int64], ctypes.c_int64),
@@ -185,7 +206,7 @@ class Shape:
 class Cache:
     """Device buffers of one layer's persistent-mode KV cache (see pbsa_cache in pbsa.h)."""
 
-    def __init__(self, shape: Shape, device="cuda"):
+    def __init__(self, shape: Shape, device="cuda", device_counter: bool = False):
         H, S, d = shape.heads, shape.slots, shape.head_dim
         self.shape = shape
         self.k = torch.zeros(H, S, shape.block, d, dtype=torch.bfloat16, device=device)
@@ -194,10 +215,14 @@ class Cache:
         self.block_id = torch.full((H, S), -1, dtype=torch.int32, device=device)
         self.len = torch.zeros(H, S, dtype=torch.int32, device=device)
         self.chunk_index = 0
+        # device copy of chunk_index (needed by captured chunk steps), or None
+        self.chunk_dev = torch.zeros(1, dtype=torch.int64, device=device) if device_counter \
+            else None
 
     def c(self) -> CacheC:
         return CacheC(self.k.data_ptr(), self.v.data_ptr(), self.rep.data_ptr(),
-                      self.block_id.data_ptr(), self.len.data_ptr(), self.chunk_index)
+                      self.block_id.data_ptr(), self.len.data_ptr(), self.chunk_index,
+                      self.chunk_dev.data_ptr() if self.chunk_dev is not None else None)
 
     def nbytes(self) -> int:
         return sum(t.numel() * t.element_size() for t in
@@ -373,4 +398,90 @@ def pbsa_attn_bwd(shape: Shape, chunks: int, q, k, v, o, lse, dout, sel, nsel, d
     _check("pbsa_attn_bwd", lib().pbsa_attn_bwd(
         ctypes.byref(shape.c()), chunks, ts[0], ts[1], ts[2], ts[3], _ptr(lse), ts[4],
         _ptr(sel), _ptr(nsel), sel.shape[2], ts[5], ts[6], ts[7], _ptr(workspace),
+        workspace.numel(), _stream()))
+
+
+def chunk_args(shape: Shape, passes, q_rep, scores, sel, os_, lses, workspace) -> ChunkArgs:
+    """pbsa_chunk_args for `passes` = [(q, k, v), ...] (the last pass's K/V enter the cache),
+    per-pass outputs os_[p], lses[p] and the shared routing / update buffers."""
+    H, d, T = shape.heads, shape.head_dim, shape.chunk_tokens
+    n = len(passes)
+    if not 1 <= n <= MAX_PASSES or len(os_) < n or len(lses) < n:
+        raise ValueError(f"need 1..{MAX_PASSES} passes with an output each")
+    a = ChunkArgs()
+    a.passes = n
+    for p, (q, k, v) in enumerate(passes):
+        a.q[p] = _tok(q, "q", T, H, d)
+        a.k[p] = _tok(k, "k", T, H, d)
+        a.v[p] = _tok(v, "v", T, H, d)
+        a.o[p] = _tok(os_[p], "o", T, H, d)
+        _contig(lses[p], "lse", torch.float32, (H, T))
+        a.lse[p] = lses[p].data_ptr()
+    if q_rep is not None:
+        _contig(q_rep, "q_rep", torch.float32, (H, shape.nq, d))
+    _contig(scores, "scores", torch.float32, (H, shape.nq, shape.slots))
+    _contig(sel, "sel", torch.int32, (H, shape.nq, shape.topk))
+    _dev(workspace, "workspace", torch.uint8)
+    a.q_rep = q_rep.data_ptr() if q_rep is not None else None
+    a.scores, a.sel = scores.data_ptr(), sel.data_ptr()
+    a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
+    return a
+
+
+def pbsa_chunk_step(shape: Shape, args: ChunkArgs, cache: Cache):
+    """The chunk step (all passes, then the memory update) as one call."""
+    cc = cache.c()
+    _check("pbsa_chunk_step", lib().pbsa_chunk_step(ctypes.byref(shape.c()), ctypes.byref(args),
+                                                    ctypes.byref(cc), _stream()))
+    cache.chunk_index = cc.chunk_index
+
+
+class ChunkGraph:
+    """The chunk step captured once as a HIP graph (pbsa_chunk_graph_*).  The tensors
+    behind `args` must stay alive as long as the graph: it keeps references to them."""
+
+    def __init__(self, shape: Shape, args: ChunkArgs, cache: Cache, keep=()):
+        if cache.chunk_dev is None:
+            raise ValueError("the cache needs a device chunk counter (device_counter=True)")
+        self._keep = tuple(keep)
+        h = ctypes.c_void_p()
+        _check("pbsa_chunk_graph_create", lib().pbsa_chunk_graph_create(
+            ctypes.byref(shape.c()), ctypes.byref(args), ctypes.byref(cache.c()),
+            ctypes.byref(h)))
+        self._h = h
+
+    def launch(self, cache: Cache):
+        cc = cache.c()
+        _check("pbsa_chunk_graph_launch", lib().pbsa_chunk_graph_launch(self._h, ctypes.byref(cc),
+                                                                        _stream()))
+        cache.chunk_index = cc.chunk_index
+
+    def close(self):
+        if self._h:
+            lib().pbsa_chunk_graph_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # interpreter shutdown
+            pass
+
+
+def pbsa_attn_bwd_persistent(shape: Shape, q, cache: Cache, chunk_k, chunk_v, sel, o, lse, dout,
+                             dq, dk, dv, dk_cache, dv_cache, workspace):
+    """Gradient of pbsa_attn_fwd: dq, the chunk's dk/dv, and every cache slot's dk/dv
+    (dk_cache, dv_cache shaped like cache.k)."""
+    H, d, T = shape.heads, shape.head_dim, shape.chunk_tokens
+    ts = [_tok(t, nm, T, H, d) for t, nm in ((q, "q"), (chunk_k, "chunk_k"), (chunk_v, "chunk_v"),
+                                              (o, "o"), (dout, "dout"), (dq, "dq"), (dk, "dk"),
+                                              (dv, "dv"))]
+    _contig(sel, "sel", torch.int32, (H, shape.nq, shape.topk))
+    _contig(lse, "lse", torch.float32, (H, T))
+    for t, nm in ((dk_cache, "dk_cache"), (dv_cache, "dv_cache")):
+        _contig(t, nm, torch.bfloat16, tuple(cache.k.shape))
+    _dev(workspace, "workspace", torch.uint8)
+    _check("pbsa_attn_bwd_persistent", lib().pbsa_attn_bwd_persistent(
+        ctypes.byref(shape.c()), ts[0], ctypes.byref(cache.c()), ts[1], ts[2], _ptr(sel), ts[3],
+        _ptr(lse), ts[4], ts[5], ts[6], ts[7], _ptr(dk_cache), _ptr(dv_cache), _ptr(workspace),
         workspace.numel(), _stream()))

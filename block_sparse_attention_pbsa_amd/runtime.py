@@ -20,15 +20,22 @@ from . import ops
 
 
 class PersistentLayer:
-    def __init__(self, shape: ops.Shape, device="cuda"):
+    def __init__(self, shape: ops.Shape, device="cuda", passes: int = 1,
+                 device_counter: bool = False):
         self.shape = shape
         H, d, nq, T = shape.heads, shape.head_dim, shape.nq, shape.chunk_tokens
-        self.cache = ops.Cache(shape, device)
+        # device_counter: the cache keeps a device copy of its chunk index (needed by the
+        # captured chunk step, step_graph)
+        self.cache = ops.Cache(shape, device, device_counter=device_counter)
+        self._graphs = {}
         self.q_rep = torch.empty(H, nq, d, dtype=torch.float32, device=device)
         self.scores = torch.empty(H, nq, shape.slots, dtype=torch.float32, device=device)
         self.sel = torch.empty(H, nq, shape.topk, dtype=torch.int32, device=device)
-        self.o = torch.empty(T, H, d, dtype=torch.bfloat16, device=device)
-        self.lse = torch.empty(H, T, dtype=torch.float32, device=device)
+        # one output per denoising pass of a chunk
+        self.os = [torch.empty(T, H, d, dtype=torch.bfloat16, device=device)
+                   for _ in range(passes)]
+        self.lses = [torch.empty(H, T, dtype=torch.float32, device=device) for _ in range(passes)]
+        self.o, self.lse = self.os[0], self.lses[0]
         nbytes = ops.pbsa_workspace_bytes(shape, ops.PBSA_OP_MEMORY_UPDATE)
         self.workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
         self.side = torch.cuda.Stream(device=device)  # default priority
@@ -39,8 +46,8 @@ class PersistentLayer:
     def route(self, q):
         ops.pbsa_route(self.shape, q, self.cache, self.q_rep, self.scores, self.sel)
 
-    def attend(self, q, k, v):
-        ops.pbsa_attn_fwd(self.shape, q, self.cache, k, v, self.sel, self.o, self.lse)
+    def attend(self, q, k, v, p: int = 0):
+        ops.pbsa_attn_fwd(self.shape, q, self.cache, k, v, self.sel, self.os[p], self.lses[p])
 
     def update(self, k, v):
         s = self.shape
@@ -65,6 +72,43 @@ class PersistentLayer:
         self.attend(q, k, v)
         main.wait_stream(self.side)            # selection done; attention done (same stream)
         ops.pbsa_memory_apply(self.shape, self.cache, k, v, None, self.workspace)
+
+
+    def step_passes(self, passes):
+        """One chunk with len(passes) denoising passes sharing the memory: each pass
+        (q, k, v) is routed and attended (outputs in os[p], lses[p]); then the memory is
+        updated with the last pass's scores and its K/V enter the cache."""
+        for p, (q, k, v) in enumerate(passes):
+            self.route(q)
+            self.attend(q, k, v, p)
+        q, k, v = passes[-1]
+        self.update(k, v)
+
+    def _args(self, passes):
+        return ops.chunk_args(self.shape, passes, self.q_rep, self.scores, self.sel, self.os,
+                              self.lses, self.workspace)
+
+    def step_fused(self, passes):
+        """step_passes as one library call (pbsa_chunk_step)."""
+        ops.pbsa_chunk_step(self.shape, self._args(passes), self.cache)
+
+    def step_graph(self, passes):
+        """step_passes replayed from a HIP graph captured for these input tensors (one
+        capture per distinct set of input buffers; later chunks reuse it when their inputs
+        are written into the same buffers).  The selection of the memory update runs on a
+        captured side branch beside the last pass's attention."""
+        key = tuple(t.data_ptr() for qkv in passes for t in qkv)
+        g = self._graphs.get(key)
+        if g is None:
+            g = ops.ChunkGraph(self.shape, self._args(passes), self.cache,
+                               keep=[t for qkv in passes for t in qkv])
+            self._graphs[key] = g
+        g.launch(self.cache)
+
+    def close_graphs(self):
+        for g in self._graphs.values():
+            g.close()
+        self._graphs.clear()
 
 
 class TwoLevelClip:

@@ -67,6 +67,13 @@ class Workload:
         """Index of the chunk generated right after the history (history / chunk frames)."""
         return self.history_frames // self.chunk_frames
 
+    @property
+    def plant_frames(self) -> int:
+        """Frames over which the planted blocks are laid out: the history, the measured
+        chunk and EXTRA_CHUNKS chunks after it (the rollout continues past the measured
+        chunk when successive chunks are timed)."""
+        return self.history_frames + self.chunk_frames * (1 + EXTRA_CHUNKS)
+
 
 WORKLOADS = {
     "tiny": Workload("tiny", 1, 64, 64, 256, 1, 4, 2, 4, 1, 4),
@@ -82,9 +89,12 @@ WORKLOADS = {
                           kv_shift=3.0, clip_chunks=8, top_frames=8),
 }
 
+# chunks after the measured one that keep the same planted layout
+EXTRA_CHUNKS = 128
+
 SEEDS = {"tiny": 1001, "wan_5s": 1002, "wan_20s": 1003, "wan_1min": 1004, "wan_train": 1005}
 
-_TAGS = {"u": 1, "plant": 2, "qkv": 3, "alpha": 4, "dout": 5}
+_TAGS = {"u": 1, "plant": 2, "qkv": 3, "alpha": 4, "dout": 5, "pass": 6}
 
 
 def rng(seed: int, tag: str, index: int = 0) -> np.random.Generator:
@@ -93,12 +103,22 @@ def rng(seed: int, tag: str, index: int = 0) -> np.random.Generator:
                                                                        index])))
 
 
+def _rne_high_half(x) -> np.ndarray:
+    """uint32 words whose high half is x rounded to bf16 (nearest, ties to even) and whose
+    low half is zero.  Finite inputs only (the sum cannot carry out of 32 bits for them)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    r = u >> 16
+    r &= 1
+    r += 0x7FFF
+    r += u
+    r &= np.uint32(0xFFFF0000)
+    return r
+
+
 def bf16_bits(x) -> np.ndarray:
     """Round float32 values to bf16 (nearest, ties to even); return the raw uint16 bits."""
-    x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return r.astype(np.uint16)
+    return (_rne_high_half(x) >> 16).astype(np.uint16)
 
 
 def bf16_value(bits) -> np.ndarray:
@@ -109,7 +129,7 @@ def bf16_value(bits) -> np.ndarray:
 
 def round_bf16(x) -> np.ndarray:
     """float32 array holding x rounded to bf16."""
-    return bf16_value(bf16_bits(x))
+    return _rne_high_half(x).view(np.float32)
 
 
 def directions(wl: Workload, seed: int) -> np.ndarray:
@@ -154,14 +174,26 @@ def _plant_mask_tokens(wl: Workload, planted: np.ndarray, f0: int, frames: int) 
 def chunk_qkv(wl: Workload, seed: int, c: int, total_frames: int | None = None):
     """Q, K, V of chunk c as float32 [F*n, H, d] arrays holding bf16 values.
 
-    total_frames: frames over which planted blocks are laid out (default: history + the
-    measured chunk).
+    total_frames: frames over which planted blocks are laid out (default:
+    wl.plant_frames).
     """
+    return _draw_qkv(wl, seed, c, rng(seed, "qkv", c), total_frames)
+
+
+def pass_qkv(wl: Workload, seed: int, c: int, p: int, passes: int, total_frames: int | None = None):
+    """Q, K, V of denoising pass p (0-based, of `passes`) of chunk c.  The last pass is the
+    chunk itself (chunk_qkv: the pass whose K/V enter the cache); earlier passes draw their
+    own tokens with the same structure."""
+    if p == passes - 1:
+        return chunk_qkv(wl, seed, c, total_frames)
+    return _draw_qkv(wl, seed, c, rng(seed, "pass", 64 * c + p), total_frames)
+
+
+def _draw_qkv(wl: Workload, seed: int, c: int, g, total_frames):
     F, n, H, d = wl.chunk_frames, wl.frame_tokens, wl.heads, wl.head_dim
-    g = rng(seed, "qkv", c)
     q, k, v = (g.standard_normal((F * n, H, d), dtype=np.float32) for _ in range(3))
     if wl.planted_per_segment:
-        tf = total_frames if total_frames is not None else wl.history_frames + F
+        tf = total_frames if total_frames is not None else wl.plant_frames
         u = directions(wl, seed)
         pm = _plant_mask_tokens(wl, planted_blocks(wl, seed, tf), c * F, F)
         k[pm] += wl.kv_shift * u[None, :, :]

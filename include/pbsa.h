@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define PBSA_ABI_VERSION 1
+#define PBSA_ABI_VERSION 2
 
 typedef enum pbsa_status {
   PBSA_OK = 0,
@@ -93,7 +93,13 @@ typedef struct pbsa_tensor {
  *   rep       fp32 [heads][slots][head_dim]   the block's mean key (its representative)
  *   block_id  int32 [heads][slots]            global block id, -1 = empty
  *   len       int32 [heads][slots]            valid tokens of the block
- * chunk_index counts the chunks appended so far; pbsa_memory_update advances it. */
+ * chunk_index counts the chunks appended so far; pbsa_memory_update advances it.
+ * chunk_index_dev (optional, device int64, 8-byte aligned): a device copy of that count.
+ * When it is not NULL the update kernels take the chunk index from it and advance it on
+ * the device, so that an update captured once in a graph (pbsa_chunk_graph_create) is
+ * right for every later chunk it is replayed for; the calls still advance chunk_index,
+ * and the caller keeps the two equal (a graph replay advances only the device copy;
+ * pbsa_chunk_graph_launch advances chunk_index as well).  pbsa_cache_reset zeroes both. */
 typedef struct pbsa_cache {
   void* k;
   void* v;
@@ -101,6 +107,7 @@ typedef struct pbsa_cache {
   int32_t* block_id;
   int32_t* len;
   int64_t chunk_index;
+  int64_t* chunk_index_dev;
 } pbsa_cache;
 
 /* ---- helpers ---------------------------------------------------------------------- */
@@ -116,9 +123,9 @@ pbsa_status pbsa_check_dims(const pbsa_dims* dims, int32_t mode);
 /* Slots per head of the persistent cache: capacity + window_frames * nb (0 if invalid). */
 int64_t pbsa_cache_slots(const pbsa_dims* dims);
 
-enum { PBSA_OP_MEMORY_UPDATE = 1, PBSA_OP_ATTN_BWD = 2 };
-/* Workspace bytes a call needs.  MEMORY_UPDATE: `arg` unused.  ATTN_BWD: `arg` = clip
- * chunks, `arg2` = max_sel. */
+enum { PBSA_OP_MEMORY_UPDATE = 1, PBSA_OP_ATTN_BWD = 2, PBSA_OP_ATTN_BWD_PERSISTENT = 3 };
+/* Workspace bytes a call needs.  MEMORY_UPDATE and ATTN_BWD_PERSISTENT: `arg`, `arg2`
+ * unused.  ATTN_BWD: `arg` = clip chunks, `arg2` = max_sel. */
 size_t pbsa_workspace_bytes(const pbsa_dims* dims, int32_t op, int32_t arg, int32_t arg2);
 
 /* Empties the cache (block_id = -1, len = 0, chunk_index = 0).  K/V/rep are left as they
@@ -211,6 +218,68 @@ pbsa_status pbsa_memory_apply(const pbsa_dims* dims, pbsa_cache* cache, pbsa_ten
                               pbsa_tensor chunk_v, const float* chunk_rep, void* workspace,
                               size_t workspace_bytes, void* stream);
 
+/* Gradient of pbsa_attn_fwd (persistent mode) with the selection held constant: Sparse
+ * Forcing's own trainable layout (English page, 2.D: the model is trained with the same
+ * dynamic sparse cache it uses at inference; 3: one kernel family for decoding and
+ * training).  Same arguments as pbsa_attn_fwd (the cache state and `sel` it attended),
+ * plus its o and lse and the upstream gradient dout (like q).  Writes dq (like q), dk and
+ * dv for the chunk's own keys and values (like chunk_k), and dk_cache, dv_cache: bf16
+ * [heads][slots][block][head_dim], the gradient of every cache slot's K and V (all block
+ * rows written: zero past the slot's length, and for slots no query attended).  No
+ * gradient flows through routing, pooling or the memory update.  Deterministic: atomics
+ * only build integer lists and hand out work; every floating-point sum runs in a fixed
+ * order.  Limit: capacity + topk + chunk blocks <= 1536.
+ * workspace: >= pbsa_workspace_bytes(dims, PBSA_OP_ATTN_BWD_PERSISTENT, 0, 0) bytes. */
+pbsa_status pbsa_attn_bwd_persistent(const pbsa_dims* dims, pbsa_tensor q,
+                                     const pbsa_cache* cache, pbsa_tensor chunk_k,
+                                     pbsa_tensor chunk_v, const int32_t* sel, pbsa_tensor o,
+                                     const float* lse, pbsa_tensor dout, pbsa_tensor dq,
+                                     pbsa_tensor dk, pbsa_tensor dv, void* dk_cache,
+                                     void* dv_cache, void* workspace, size_t workspace_bytes,
+                                     void* stream);
+
+/* ---- the chunk step: T denoising passes sharing the memory --------------------------
+ * Sparse Forcing 2.B (P_t and the window persist while a chunk is denoised; the Chinese
+ * page's 2.1: the memory is shared between diffusion steps) with the update of 2.C.  For
+ * p = 0 .. passes-1: pbsa_route(q[p]) then pbsa_attn_fwd(q[p], k[p], v[p]) -> o[p], lse[p];
+ * then pbsa_memory_update with the last pass's scores and k/v (chunk_rep = NULL): the last
+ * pass is the one whose K/V enter the cache.  Every buffer is as in those calls (q_rep may
+ * be NULL); scores and sel are shared by the passes and end up holding the last pass's.
+ * workspace: >= pbsa_workspace_bytes(dims, PBSA_OP_MEMORY_UPDATE, 0, 0) bytes. */
+#define PBSA_MAX_PASSES 8
+typedef struct pbsa_chunk_args {
+  int32_t passes;
+  pbsa_tensor q[PBSA_MAX_PASSES];
+  pbsa_tensor k[PBSA_MAX_PASSES];
+  pbsa_tensor v[PBSA_MAX_PASSES];
+  pbsa_tensor o[PBSA_MAX_PASSES];
+  float* lse[PBSA_MAX_PASSES];
+  float* q_rep;
+  float* scores;
+  int32_t* sel;
+  void* workspace;
+  size_t workspace_bytes;
+} pbsa_chunk_args;
+
+/* The chunk step as one call: the launches above in order on `stream`; advances
+ * cache->chunk_index. */
+pbsa_status pbsa_chunk_step(const pbsa_dims* dims, const pbsa_chunk_args* args,
+                            pbsa_cache* cache, void* stream);
+
+/* The same step captured once as a HIP graph (host object, created by the library and
+ * released by pbsa_chunk_graph_destroy; it owns two streams and two events, no device
+ * memory).  The update's selection runs on a second branch beside the last pass's
+ * attention.  The cache must carry chunk_index_dev: the captured update reads the chunk
+ * index there, so one graph serves every later chunk whose inputs are written into the
+ * captured buffers (args' pointers are baked in; the buffers must outlive the graph).
+ * pbsa_chunk_graph_launch replays it on `stream` for the cache it was captured on
+ * (PBSA_ERR_STATE otherwise) and advances cache->chunk_index. */
+typedef struct pbsa_chunk_graph pbsa_chunk_graph;
+pbsa_status pbsa_chunk_graph_create(const pbsa_dims* dims, const pbsa_chunk_args* args,
+                                    const pbsa_cache* cache, pbsa_chunk_graph** out);
+pbsa_status pbsa_chunk_graph_launch(pbsa_chunk_graph* graph, pbsa_cache* cache, void* stream);
+void pbsa_chunk_graph_destroy(pbsa_chunk_graph* graph);
+
 /* ---- trainable path: two-level selection ---------------------------------------------
  * Light Forcing, hierarchical sparse attention (steps 2 and 3) with the chunk-aware
  * budget.  A clip of `chunks` chunks (chunk_frames frames each) is processed as one
@@ -242,7 +311,8 @@ pbsa_status pbsa_attn_fwd_2lvl(const pbsa_dims* dims, int32_t chunks, pbsa_tenso
 
 /* Gradient of pbsa_attn_fwd_2lvl's output with the selection held constant (no gradient
  * through routing or pooling): given o, lse from the forward and the upstream gradient
- * dout, writes dq, dk, dv (bf16, same shapes as q, k, v).  Deterministic: no atomics.
+ * dout, writes dq, dk, dv (bf16, same shapes as q, k, v).  Deterministic: atomics only build
+ * integer lists and hand out work; every floating-point sum runs in a fixed order.
  * workspace: device, >= pbsa_workspace_bytes(dims, PBSA_OP_ATTN_BWD, chunks, max_sel). */
 pbsa_status pbsa_attn_bwd(const pbsa_dims* dims, int32_t chunks, pbsa_tensor q, pbsa_tensor k,
                           pbsa_tensor v, pbsa_tensor o, const float* lse, pbsa_tensor dout,

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     L = ops.lib()
-    assert L.pbsa_abi_version() == 1
+    assert L.pbsa_abi_version() == 2
     assert L.pbsa_status_str(0) == b"ok"
     assert L.pbsa_status_str(5) == b"workspace too small"
     assert L.pbsa_status_str(99) == b"unknown status"
@@ -86,10 +86,11 @@ def test_null_dims_and_sizes():
     assert L.pbsa_check_dims(None, 0) == 1
     assert L.pbsa_cache_slots(ctypes.byref(_dims())) == 64 + 6 * 25
     assert L.pbsa_cache_slots(ctypes.byref(_dims(head_dim=3))) == 0
-    # copy list [H][F*nb] then the new persistent table [H][C] twice, 256-byte pieces
+    # copy list [H][F*nb], the new persistent table [H][C] twice, the chunk index used,
+    # 256-byte pieces
     up = lambda x: (x + 255) // 256 * 256
     assert ops.pbsa_workspace_bytes(WAN, ops.PBSA_OP_MEMORY_UPDATE) == (
-        up(4 * 12 * 75) + 2 * up(4 * 12 * 64))
+        up(4 * 12 * 75) + 2 * up(4 * 12 * 64) + up(8))
     assert ops.pbsa_workspace_bytes(WAN, ops.PBSA_OP_ATTN_BWD, 8, 75) > 12 * 600 * 600 * 4
     assert ops.pbsa_workspace_bytes(WAN, 77) == 0
 
@@ -120,7 +121,7 @@ def test_calls_reject_bad_arguments_before_launching():
     cache = ops.CacheC(16, 16, 16, 16, 16, 0)
     st = L.pbsa_memory_update(d, ctypes.c_void_p(16), ctypes.byref(cache), _tensor(16),
                               _tensor(16), ctypes.c_void_p(16), ctypes.c_void_p(16), 8, None)
-    assert st == 5 and b"9984" in L.pbsa_last_error()
+    assert st == 5 and b"10240" in L.pbsa_last_error()
     assert cache.chunk_index == 0
     # its two halves check the same workspace; a failed apply leaves chunk_index alone
     assert L.pbsa_memory_select(d, ctypes.c_void_p(16), ctypes.byref(cache), ctypes.c_void_p(16),
@@ -180,3 +181,32 @@ def test_host_budget_matches_oracle_budget():
     for _ in range(50):
         a = rs.uniform(0, 1, size=8)
         assert runtime.cag_budgets(a, 32, 8)[1:] == oracle.cag_budgets(a, 32, 8)[1:]
+
+
+def test_chunk_step_checks_before_launching():
+    L = ops.lib()
+    d = ctypes.byref(_dims())
+    cache = ops.CacheC(16, 16, 16, 16, 16, 0, None)
+    a = ops.ChunkArgs()
+    for p in range(ops.MAX_PASSES):
+        a.q[p] = a.k[p] = a.v[p] = a.o[p] = _tensor(16)
+        a.lse[p] = 16
+    a.scores, a.sel, a.workspace = 16, 16, 16
+    a.workspace_bytes = ops.pbsa_workspace_bytes(WAN, ops.PBSA_OP_MEMORY_UPDATE)
+    for bad in (0, ops.MAX_PASSES + 1):
+        a.passes = bad
+        assert L.pbsa_chunk_step(d, ctypes.byref(a), ctypes.byref(cache), None) == 2
+    a.passes = 2
+    a.lse[1] = None
+    assert L.pbsa_chunk_step(d, ctypes.byref(a), ctypes.byref(cache), None) == 1
+    a.lse[1] = 16
+    a.workspace_bytes = 8
+    assert L.pbsa_chunk_step(d, ctypes.byref(a), ctypes.byref(cache), None) == 5
+    a.workspace_bytes = 1 << 20
+    # a captured step needs the device chunk counter; a misaligned one is refused
+    h = ctypes.c_void_p()
+    assert L.pbsa_chunk_graph_create(d, ctypes.byref(a), ctypes.byref(cache), ctypes.byref(h)) == 6
+    assert not h.value
+    cache = ops.CacheC(16, 16, 16, 16, 16, 0, 12)
+    assert L.pbsa_chunk_graph_create(d, ctypes.byref(a), ctypes.byref(cache), ctypes.byref(h)) == 4
+    assert L.pbsa_chunk_graph_launch(None, ctypes.byref(cache), None) == 1
