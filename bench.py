@@ -512,7 +512,7 @@ def main():
 
 
 TRAFFIC_KERNEL = "attn_fwd_kernel<128, true, false>"
-KERNEL_SOURCES = ("attn_fwd.hip", "attn_common.h", "common.h", "launch.h")
+KERNEL_SOURCES = ("attn_fwd.hip", "attn_common.h", "common.h")
 
 
 def kernel_source_hash():

@@ -8,6 +8,22 @@ namespace pbsa {
 
 constexpr int kBlock = 64;  // tokens per block (the only block size built)
 
+// Block-list entries the attention forward keeps per workgroup (persistent mode:
+// capacity + chunk blocks + 2 * topk; two-level mode: 2 * max_sel).
+constexpr int kAttnListCap = 3072;
+
+// A bf16 token tensor (see pbsa_tensor): base, token stride and head stride in elements.
+struct TokIn {
+  const uint16_t* p;
+  int64_t ts;  // token stride (elements)
+  int64_t hs;  // head stride (elements)
+};
+struct TokOut {
+  uint16_t* p;
+  int64_t ts;
+  int64_t hs;
+};
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));

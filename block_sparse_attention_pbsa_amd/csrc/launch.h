@@ -5,19 +5,9 @@
 #include <stdint.h>
 
 #include "../../include/pbsa.h"
+#include "common.h"
 
 namespace pbsa {
-
-struct TokIn {
-  const uint16_t* p;
-  int64_t ts;  // token stride (elements)
-  int64_t hs;  // head stride (elements)
-};
-struct TokOut {
-  uint16_t* p;
-  int64_t ts;
-  int64_t hs;
-};
 
 inline TokIn tok_in(const pbsa_tensor& t) {
   return TokIn{static_cast<const uint16_t*>(t.data), t.token_stride, t.head_stride};
@@ -25,10 +15,6 @@ inline TokIn tok_in(const pbsa_tensor& t) {
 inline TokOut tok_out(const pbsa_tensor& t) {
   return TokOut{static_cast<uint16_t*>(t.data), t.token_stride, t.head_stride};
 }
-
-// Block-list entries the attention forward keeps per workgroup (persistent mode:
-// capacity + chunk blocks + 2 * topk; two-level mode: 2 * max_sel).
-constexpr int kAttnListCap = 3072;
 
 inline int nb_of(const pbsa_dims& d) { return (d.frame_tokens + d.block - 1) / d.block; }
 inline int64_t slots_of(const pbsa_dims& d) {
