@@ -336,6 +336,33 @@ pbsa_status pbsa_memory_update(const pbsa_dims* dims, const float* scores, pbsa_
   return st;
 }
 
+pbsa_status pbsa_memory_update_noalloc(const pbsa_dims* dims, const float* scores,
+                                       pbsa_cache* cache, pbsa_tensor chunk_k,
+                                       pbsa_tensor chunk_v, const float* chunk_rep,
+                                       void* stream) {
+  PBSA_TRY(check_dims(dims, 0));
+  PBSA_TRY(check_cache(cache));
+  PBSA_TRY(check_tok(chunk_k, "chunk_k", dims->head_dim));
+  PBSA_TRY(check_tok(chunk_v, "chunk_v", dims->head_dim));
+  if (!scores) return fail(PBSA_ERR_NULL, "scores is required");
+  const size_t need = pbsa::memory_update_workspace(*dims);
+  if (need > pbsa::kMemoryScratchBytes)
+    return fail(PBSA_ERR_UNSUPPORTED,
+                "memory_update_noalloc: these dims need %zu scratch bytes, the library holds %zu "
+                "(use pbsa_memory_update with a workspace)",
+                need, pbsa::kMemoryScratchBytes);
+  void* ws = nullptr;
+  pbsa_status st = hip_status(pbsa::memory_scratch(&ws), "memory_update_noalloc scratch");
+  if (st != PBSA_OK) return st;
+  PBSA_TRY(check_memory_ws(dims, cache, ws, need, "memory_update_noalloc"));
+  st = hip_status(pbsa::launch_memory_update(*dims, scores, *cache, pbsa::tok_in(chunk_k),
+                                             pbsa::tok_in(chunk_v), chunk_rep, ws,
+                                             stream_of(stream)),
+                  "memory_update_noalloc");
+  if (st == PBSA_OK) cache->chunk_index += 1;
+  return st;
+}
+
 pbsa_status pbsa_score_topk_2lvl(const pbsa_dims* dims, int32_t chunks, int32_t top_frames,
                                  const int32_t* k_per_chunk, const float* q_rep,
                                  const float* block_rep, const float* frame_rep,

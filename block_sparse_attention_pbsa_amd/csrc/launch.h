@@ -68,4 +68,9 @@ hipError_t launch_memory_update(const pbsa_dims& d, const float* scores, const p
                                 TokIn ck, TokIn cv, const float* chunk_rep, void* ws,
                                 hipStream_t s);
 
+// Size of the library-held workspace of pbsa_memory_update_noalloc, and its device address
+// on the current device (looked up on first use per device).
+constexpr size_t kMemoryScratchBytes = size_t{1} << 20;
+hipError_t memory_scratch(void** ptr);
+
 }  // namespace pbsa

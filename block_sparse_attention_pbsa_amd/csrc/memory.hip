@@ -17,6 +17,7 @@
 //          zero-padded rows, representative, id, length).
 // The window slot a chunk block lands in is exactly the slot of a leaving block (or an
 // empty one), and the same workgroup does both moves, so reads precede writes.
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
@@ -435,6 +436,34 @@ hipError_t launch_memory_update(const pbsa_dims& d, const float* scores, const p
   const hipError_t e = launch_memory_select(d, scores, c, ws, false, s);
   if (e != hipSuccess) return e;
   return launch_memory_apply(d, c, ck, cv, chunk_rep, ws, s);
+}
+
+// Library-held workspace of the allocation-free update: each GPU holds its own copy of
+// this array for the life of the process.  Host code never uses the array's name as an
+// address: memory_scratch() looks the device address up (once per device, with that
+// device current) and every launch gets that address.
+__device__ __align__(256) char scratch[kMemoryScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t memory_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace pbsa

@@ -85,6 +85,8 @@ _SIGS = {
                             _P], ctypes.c_int),
     "pbsa_memory_apply": ([ctypes.POINTER(Dims), ctypes.POINTER(CacheC), Tensor, Tensor, _P, _P,
                            ctypes.c_size_t, _P], ctypes.c_int),
+    "pbsa_memory_update_noalloc": ([ctypes.POINTER(Dims), _P, ctypes.POINTER(CacheC), Tensor,
+                                    Tensor, _P, _P], ctypes.c_int),
     "pbsa_score_topk_2lvl": ([ctypes.POINTER(Dims), _I32, _I32, ctypes.POINTER(_I32), _P, _P, _P,
                               _I32, _P, _P, _P], ctypes.c_int),
     "pbsa_attn_fwd_2lvl": ([ctypes.POINTER(Dims), _I32, Tensor, Tensor, Tensor, _P, _P, _I32,
@@ -323,6 +325,21 @@ def pbsa_memory_update(shape: Shape, scores, cache: Cache, chunk_k, chunk_v, chu
     _check("pbsa_memory_update", lib().pbsa_memory_update(
         ctypes.byref(shape.c()), _ptr(scores), ctypes.byref(cc), kt, vt, _ptr(chunk_rep),
         _ptr(workspace), workspace.numel(), _stream()))
+    cache.chunk_index = cc.chunk_index
+
+
+def pbsa_memory_update_noalloc(shape: Shape, scores, cache: Cache, chunk_k, chunk_v, chunk_rep):
+    """pbsa_memory_update with the library-held workspace (no workspace argument)."""
+    H, d, T = shape.heads, shape.head_dim, shape.chunk_tokens
+    _contig(scores, "scores", torch.float32, (H, shape.nq, shape.slots))
+    kt = _tok(chunk_k, "chunk_k", T, H, d)
+    vt = _tok(chunk_v, "chunk_v", T, H, d)
+    if chunk_rep is not None:
+        _contig(chunk_rep, "chunk_rep", torch.float32, (H, shape.nq, d))
+    cc = cache.c()
+    _check("pbsa_memory_update_noalloc", lib().pbsa_memory_update_noalloc(
+        ctypes.byref(shape.c()), _ptr(scores), ctypes.byref(cc), kt, vt, _ptr(chunk_rep),
+        _stream()))
     cache.chunk_index = cc.chunk_index
 
 

@@ -218,6 +218,19 @@ pbsa_status pbsa_memory_apply(const pbsa_dims* dims, pbsa_cache* cache, pbsa_ten
                               pbsa_tensor chunk_v, const float* chunk_rep, void* workspace,
                               size_t workspace_bytes, void* stream);
 
+/* pbsa_memory_update without a workspace argument, for callers that cannot allocate device
+ * memory (code under graph capture, tight serving loops, harnesses that forbid
+ * allocation).  The workspace is a library-held device array of 1 MiB per GPU (held until
+ * the process ends); dims needing more (pbsa_workspace_bytes(dims, PBSA_OP_MEMORY_UPDATE))
+ * return PBSA_ERR_UNSUPPORTED.  The call allocates nothing.  Every call on one GPU shares
+ * that array: calls that overlap on one GPU (on different streams, or from several
+ * threads) race and give undefined results; calls ordered on one stream are safe (each
+ * call writes every workspace word it reads).  Otherwise exactly pbsa_memory_update. */
+pbsa_status pbsa_memory_update_noalloc(const pbsa_dims* dims, const float* scores,
+                                       pbsa_cache* cache, pbsa_tensor chunk_k,
+                                       pbsa_tensor chunk_v, const float* chunk_rep,
+                                       void* stream);
+
 /* Gradient of pbsa_attn_fwd (persistent mode) with the selection held constant: Sparse
  * Forcing's own trainable layout (English page, 2.D: the model is trained with the same
  * dynamic sparse cache it uses at inference; 3: one kernel family for decoding and
