@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <string>
+#include <vector>
 
 #include "../../include/pbsa.h"
 #include "../../include/pbsa_probe.h"
@@ -60,6 +61,8 @@ pbsa_status check_dims(const pbsa_dims* d, int mode) {
     if (d->sinks < 0 || d->sinks > d->capacity || d->sinks > nb)
       return fail(PBSA_ERR_SHAPE, "need 0 <= sinks <= min(capacity, blocks per frame)");
     if (d->capacity < 0) return fail(PBSA_ERR_SHAPE, "capacity must be >= 0");
+    if (d->route_mode != PBSA_ROUTE_WINDOW && d->route_mode != PBSA_ROUTE_UNION)
+      return fail(PBSA_ERR_SHAPE, "route_mode must be PBSA_ROUTE_WINDOW or PBSA_ROUTE_UNION");
     if (d->topk < 1) return fail(PBSA_ERR_SHAPE, "topk must be >= 1");
     if (d->topk > 1024) return fail(PBSA_ERR_UNSUPPORTED, "topk must be <= 1024");
     const int64_t slots = pbsa::slots_of(*d);
@@ -70,6 +73,10 @@ pbsa_status check_dims(const pbsa_dims* d, int mode) {
       return fail(PBSA_ERR_UNSUPPORTED, "capacity - sinks must be <= 1024");
     if (static_cast<int64_t>(d->window_frames) * nb > 1024)
       return fail(PBSA_ERR_UNSUPPORTED, "window blocks must be <= 1024");
+    if (d->route_mode == PBSA_ROUTE_UNION && slots > 1024)
+      return fail(PBSA_ERR_UNSUPPORTED,
+                  "PBSA_ROUTE_UNION needs capacity + window blocks <= 1024 (got %lld)",
+                  static_cast<long long>(slots));
     // LDS of the memory-update selection: block tables, candidate list and partial sums,
     // free list (the limits above keep it under 80 KB)
     const int64_t ncand = static_cast<int64_t>(d->capacity - d->sinks) + int64_t{d->chunk_frames} * nb;
@@ -140,6 +147,7 @@ const char* pbsa_status_str(int status) {
     case PBSA_ERR_WORKSPACE: return "workspace too small";
     case PBSA_ERR_STATE: return "bad cache state";
     case PBSA_ERR_HIP: return "hip error";
+    case PBSA_ERR_INDEX: return "bad index";
     default: return "unknown status";
   }
 }
@@ -155,6 +163,137 @@ pbsa_status pbsa_check_dims(const pbsa_dims* dims, int32_t mode) {
 int64_t pbsa_cache_slots(const pbsa_dims* dims) {
   if (check_dims(dims, 0) != PBSA_OK) return 0;
   return pbsa::slots_of(*dims);
+}
+
+size_t pbsa_cache_bytes(const pbsa_dims* dims) {
+  if (check_dims(dims, 0) != PBSA_OK) return 0;
+  const size_t per_slot = 2 * static_cast<size_t>(dims->block) * dims->head_dim * 2 +
+                          static_cast<size_t>(dims->head_dim) * 4 + 2 * 4;
+  return static_cast<size_t>(dims->heads) * static_cast<size_t>(pbsa::slots_of(*dims)) * per_slot;
+}
+
+pbsa_status pbsa_check_cache_table(const pbsa_dims* dims, const int32_t* block_id,
+                                   const int32_t* len, int64_t chunk_index) {
+  PBSA_TRY(check_dims(dims, 0));
+  if (!block_id || !len) return fail(PBSA_ERR_NULL, "block_id and len are required");
+  if (chunk_index < 0) return fail(PBSA_ERR_STATE, "chunk_index is negative");
+  const int nb = pbsa::nb_of(*dims), C = dims->capacity, S = dims->sinks, W = dims->window_frames;
+  const int64_t slots = pbsa::slots_of(*dims);
+  const int64_t hist = chunk_index * dims->chunk_frames;  // history frames
+  const int64_t win0 = std::max<int64_t>(0, hist - W);    // first window frame
+  auto blen = [&](int64_t g) { return pbsa::block_len(static_cast<int>(g % nb), dims->frame_tokens); };
+  std::vector<char> seen;
+  for (int h = 0; h < dims->heads; ++h) {
+    const int32_t* b = block_id + static_cast<int64_t>(h) * slots;
+    const int32_t* l = len + static_cast<int64_t>(h) * slots;
+    seen.assign(static_cast<size_t>(std::max<int64_t>(1, win0 * nb)), 0);
+    for (int s = 0; s < C; ++s) {
+      const int32_t g = b[s];
+      if (s < S && chunk_index > 0) {
+        if (g != s || l[s] != blen(s))
+          return fail(PBSA_ERR_INDEX, "head %d slot %d: sink %d missing (holds %d, len %d)", h, s,
+                      s, g, l[s]);
+        continue;
+      }
+      if (g < 0) {
+        if (l[s] != 0) return fail(PBSA_ERR_INDEX, "head %d slot %d: empty with len %d", h, s, l[s]);
+        continue;
+      }
+      if (g < S || g >= win0 * nb)
+        return fail(PBSA_ERR_INDEX, "head %d persistent slot %d holds block %d (not a non-sink "
+                    "block that has left the window)", h, s, g);
+      if (seen[g]) return fail(PBSA_ERR_INDEX, "head %d: block %d held twice", h, g);
+      seen[g] = 1;
+      if (l[s] != blen(g))
+        return fail(PBSA_ERR_INDEX, "head %d slot %d: block %d has len %d", h, s, g, l[s]);
+    }
+    for (int64_t s = C; s < slots; ++s) {
+      const int64_t rel = s - C, fr = rel / nb, j = rel % nb;
+      // the latest history frame that maps to this ring slot
+      int64_t f = -1;
+      if (hist > 0) {
+        const int64_t last = hist - 1;
+        f = last - ((last - fr) % W + W) % W;
+      }
+      const int64_t g = f * nb + j;
+      const bool want = f >= win0 && f >= 0 && g >= S;
+      if (want ? (b[s] != g || l[s] != blen(g)) : (b[s] != -1 || l[s] != 0))
+        return fail(PBSA_ERR_INDEX, "head %d window slot %lld holds block %d (len %d), expected %lld",
+                    h, static_cast<long long>(s), b[s], l[s], static_cast<long long>(want ? g : -1));
+    }
+  }
+  g_err.clear();
+  return PBSA_OK;
+}
+
+pbsa_status pbsa_check_selection(const pbsa_dims* dims, const int32_t* block_id,
+                                 const int32_t* sel) {
+  PBSA_TRY(check_dims(dims, 0));
+  if (!block_id || !sel) return fail(PBSA_ERR_NULL, "block_id and sel are required");
+  const int nb = pbsa::nb_of(*dims), C = dims->capacity, S = dims->sinks, K = dims->topk;
+  const int nq = dims->chunk_frames * nb;
+  const int64_t slots = pbsa::slots_of(*dims);
+  const bool uni = dims->route_mode == PBSA_ROUTE_UNION;
+  for (int h = 0; h < dims->heads; ++h) {
+    const int32_t* b = block_id + static_cast<int64_t>(h) * slots;
+    int ncand = 0;
+    for (int64_t s = uni ? 0 : C; s < slots; ++s) ncand += b[s] >= S;
+    const int want = std::min(K, ncand);
+    for (int r = 0; r < nq; ++r) {
+      const int32_t* row = sel + (static_cast<int64_t>(h) * nq + r) * K;
+      int n = 0;
+      while (n < K && row[n] >= 0) ++n;
+      for (int j = n; j < K; ++j)
+        if (row[j] != -1)
+          return fail(PBSA_ERR_INDEX, "head %d query block %d: entry %d after the -1 tail", h, r, j);
+      if (n != want)
+        return fail(PBSA_ERR_INDEX, "head %d query block %d: %d ids, expected %d", h, r, n, want);
+      for (int j = 0; j < n; ++j) {
+        const int32_t g = row[j];
+        if (j > 0 && g <= row[j - 1])
+          return fail(PBSA_ERR_INDEX, "head %d query block %d: ids not strictly ascending at %d",
+                      h, r, j);
+        const int64_t ws = C + static_cast<int64_t>((g / nb) % dims->window_frames) * nb + g % nb;
+        bool held = g >= S && b[ws] == g;
+        for (int s = S; uni && !held && s < C; ++s) held = b[s] == g;
+        if (!held)
+          return fail(PBSA_ERR_INDEX, "head %d query block %d: block %d is not a candidate the "
+                      "cache holds", h, r, g);
+      }
+    }
+  }
+  g_err.clear();
+  return PBSA_OK;
+}
+
+pbsa_status pbsa_check_selection_2lvl(const pbsa_dims* dims, int32_t chunks, const int32_t* sel,
+                                      const int32_t* nsel, int32_t max_sel) {
+  PBSA_TRY(check_dims(dims, 1));
+  if (!sel || !nsel) return fail(PBSA_ERR_NULL, "sel and nsel are required");
+  if (chunks < 1 || max_sel < 1) return fail(PBSA_ERR_SHAPE, "chunks and max_sel must be >= 1");
+  const int nb = pbsa::nb_of(*dims), F = dims->chunk_frames;
+  const int64_t nq = static_cast<int64_t>(chunks) * F * nb;
+  for (int h = 0; h < dims->heads; ++h)
+    for (int64_t r = 0; r < nq; ++r) {
+      const int64_t hr = static_cast<int64_t>(h) * nq + r;
+      const int n = nsel[hr];
+      if (n < 1 || n > max_sel)
+        return fail(PBSA_ERR_INDEX, "head %d query block %lld: nsel %d outside [1, %d]", h,
+                    static_cast<long long>(r), n, max_sel);
+      const int64_t i = r / (static_cast<int64_t>(F) * nb) + 1;  // chunk, 1-based
+      const int32_t* row = sel + hr * max_sel;
+      for (int j = 0; j < n; ++j) {
+        const int32_t g = row[j];
+        if (g < 0 || g >= nq || g / nb >= F * i)
+          return fail(PBSA_ERR_INDEX, "head %d query block %lld: block %d is not visible to it",
+                      h, static_cast<long long>(r), g);
+        if (j > 0 && g <= row[j - 1])
+          return fail(PBSA_ERR_INDEX, "head %d query block %lld: ids not strictly ascending at %d",
+                      h, static_cast<long long>(r), j);
+      }
+    }
+  g_err.clear();
+  return PBSA_OK;
 }
 
 size_t pbsa_workspace_bytes(const pbsa_dims* dims, int32_t op, int32_t arg, int32_t arg2) {

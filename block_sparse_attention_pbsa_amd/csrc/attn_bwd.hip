@@ -64,7 +64,8 @@ struct BwdArgs {
   const uint16_t *ck, *cv;     // persistent: cache K/V [H][slots][64][D]
   const int32_t *cbid, *clen;  // persistent: cache block ids and lengths [H][slots]
   int slots, C, W, K;
-  const int32_t* rsel;         // persistent: routed window ids [H][nq][K]
+  int S, route_union;          // persistent: sinks; top-K over P_t and the window together
+  const int32_t* rsel;         // persistent: routed ids [H][nq][K]
   uint16_t *dkc, *dvc;         // persistent: gradients of the cache slots [H][slots][64][D]
 };
 
@@ -79,6 +80,7 @@ struct Half {
 // KV block list entries (32 bits): bit 31 set = a cache slot (bits 0..23 the slot), else
 // a token block (bits 0..23 its first token); bits 24..30 the valid rows.
 __device__ __forceinline__ uint32_t kv_entry(const BwdArgs& a, int h, int g) {
+  if (g < 0 || g >= a.nkv) return 0u;  // not a block of this head: an empty entry
   if (a.persist && g < a.slots)
     return 0x80000000u | (static_cast<uint32_t>(a.clen[static_cast<int64_t>(h) * a.slots + g]) << 24) |
            static_cast<uint32_t>(g);
@@ -202,8 +204,10 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
 
   const int32_t* selA = a.sel + (static_cast<int64_t>(h) * a.nq + rA) * a.max_sel;
   const int32_t* selB = a.sel + (static_cast<int64_t>(h) * a.nq + rB) * a.max_sel;
-  const int cntA = a.nsel[static_cast<int64_t>(h) * a.nq + rA];
-  const int cntB = rB < a.nq ? a.nsel[static_cast<int64_t>(h) * a.nq + rB] : 0;
+  // (counts clamped to the list capacity: other nsel values are not a selection)
+  const int cntA = min(max(a.nsel[static_cast<int64_t>(h) * a.nq + rA], 0), a.max_sel);
+  const int cntB = rB < a.nq ? min(max(a.nsel[static_cast<int64_t>(h) * a.nq + rB], 0), a.max_sel)
+                             : 0;
   const int nsteps = 2 * (cntA > cntB ? cntA : cntB);
   const uint16_t* kh = a.k + h * a.khs;
   const uint16_t* vh = a.v + h * a.vhs;
@@ -850,8 +854,8 @@ __global__ void __launch_bounds__(128) attn_bwd_reduce_kernel(BwdArgs a) {
 // ------------------------------------------------------------------ persistent lists
 // grid (nq, H), one wave: query block r's KV list in persistent mode, as virtual block ids
 // (cache slots, then the chunk's blocks at slots + b): the occupied persistent slots in
-// slot order, the window slots of its routed blocks in routed order, then every block of
-// the chunk -- exactly the blocks pbsa_attn_fwd attends.
+// slot order (union routing: the sink slots), the slots of its routed blocks in routed
+// order, then every block of the chunk -- exactly the blocks pbsa_attn_fwd attends.
 __global__ void __launch_bounds__(64) attn_bwd_lists_persist_kernel(BwdArgs a, int32_t* sel,
                                                                     int32_t* nsel) {
   const int r = blockIdx.x, h = blockIdx.y, l = threadIdx.x;
@@ -859,10 +863,11 @@ __global__ void __launch_bounds__(64) attn_bwd_lists_persist_kernel(BwdArgs a, i
   int32_t* out = sel + hr * a.max_sel;
   const int32_t* bid = a.cbid + static_cast<int64_t>(h) * a.slots;
   const unsigned long long below = (1ull << l) - 1ull;
+  const int whole = a.route_union ? a.S : a.C;
   int n = 0;
-  for (int s0 = 0; s0 < a.C; s0 += 64) {
+  for (int s0 = 0; s0 < whole; s0 += 64) {
     const int s = s0 + l;
-    const bool on = s < a.C && bid[s] >= 0;
+    const bool on = s < whole && bid[s] >= 0;
     const unsigned long long m = __ballot(on);
     if (on) out[n + __popcll(m & below)] = s;
     n += __popcll(m);
@@ -871,9 +876,22 @@ __global__ void __launch_bounds__(64) attn_bwd_lists_persist_kernel(BwdArgs a, i
   for (int j0 = 0; j0 < a.K; j0 += 64) {
     const int j = j0 + l;
     const int g = j < a.K ? rs[j] : -1;
-    const bool on = g >= 0;
+    int slot = -1;
+    if (g >= 0) {
+      slot = a.C + ((g / a.nb) % a.W) * a.nb + g % a.nb;
+      if (a.route_union && bid[slot] != g) {
+        // a persistent block (an id the cache does not hold is left out)
+        slot = -1;
+        for (int ps = a.S; ps < a.C; ++ps)
+          if (bid[ps] == g) {
+            slot = ps;
+            break;
+          }
+      }
+    }
+    const bool on = slot >= 0;
     const unsigned long long m = __ballot(on);
-    if (on) out[n + __popcll(m & below)] = a.C + ((g / a.nb) % a.W) * a.nb + g % a.nb;
+    if (on) out[n + __popcll(m & below)] = slot;
     n += __popcll(m);
   }
   for (int b = l; b < a.nq; b += 64) out[n + b] = a.slots + b;
@@ -1055,6 +1073,8 @@ hipError_t launch_attn_bwd_persistent(const pbsa_dims& d, TokIn q, const pbsa_ca
   a.C = d.capacity;
   a.W = d.window_frames;
   a.K = d.topk;
+  a.S = d.sinks;
+  a.route_union = d.route_mode == PBSA_ROUTE_UNION;
   a.rsel = sel;
   a.dkc = dk_cache;
   a.dvc = dv_cache;

@@ -56,6 +56,9 @@ struct FwdArgs {
   int sel_stride;
   int nq, n, nb, H, pairs;
   float scale;
+  // persistent mode, top-K over the persistent and window blocks together: only the sink
+  // slots [0, S) are attended whole, routed ids may name persistent blocks
+  int route_union, S;
 };
 
 namespace {
@@ -494,14 +497,22 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
   uint32_t* listA = lists + (PERSIST ? a.C + a.nq : 0);
   uint32_t* listB = listA + a.sel_stride;
   int nshared = 0;
+  // (union routing) the head's persistent block ids, staged in a V tile (no gather has
+  // targeted it yet; the V tiles are cleared after the lists are built) for the lookups of
+  // routed persistent blocks below
+  int32_t* pids = reinterpret_cast<int32_t*>(&vb1[0][0]);
   if (PERSIST) {
     if (t == 0) n_list = 0;
-    __syncthreads();
     const int32_t* bh = a.bid + static_cast<int64_t>(h) * a.slots;
     const int32_t* lh = a.blen + static_cast<int64_t>(h) * a.slots;
-    for (int s0 = 0; s0 < a.C; s0 += 256) {
+    if (a.route_union)
+      for (int s = t; s < a.C; s += 256) pids[s] = bh[s];
+    __syncthreads();
+    // slots attended whole: every persistent slot, or only the sinks' (union routing)
+    const int whole = a.route_union ? a.S : a.C;
+    for (int s0 = 0; s0 < whole; s0 += 256) {
       const int s = s0 + t;
-      const bool valid = s < a.C && bh[s] >= 0;
+      const bool valid = s < whole && bh[s] >= 0;
       const unsigned long long m = __ballot(valid);
       if (l == 0) wave_cnt[w] = __popcll(m);
       __syncthreads();
@@ -519,9 +530,22 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
   // private lists; routed ids are ascending with -1 padding at the end (persistent) or
   // counted by nsel (two-level)
   auto entry = [&](int g) {
-    if (!PERSIST) return tok_entry(g);
+    // (two-level mode) an id outside the clip is an empty entry
+    if (!PERSIST) return g >= 0 && g < a.nq ? tok_entry(g) : 0x80000000u;
     const int f = g / a.nb, jj = g - f * a.nb;
-    const int slot = a.C + (f % a.W) * a.nb + jj;
+    int slot = a.C + (f % a.W) * a.nb + jj;
+    if (a.route_union && a.bid[static_cast<int64_t>(h) * a.slots + slot] != g) {
+      // not in the window: a persistent block (an id the cache does not hold becomes an
+      // empty entry, which contributes nothing)
+      int found = -1;
+      for (int ps = a.S; ps < a.C; ++ps)
+        if (pids[ps] == g) {
+          found = ps;
+          break;
+        }
+      if (found < 0) return slot_entry(0, 0);
+      slot = found;
+    }
     return slot_entry(slot, a.blen[static_cast<int64_t>(h) * a.slots + slot]);
   };
   const int32_t* sa = a.sel + (static_cast<int64_t>(h) * a.nq + rA) * a.sel_stride;
@@ -908,6 +932,8 @@ hipError_t launch_attn_fwd_persistent(const pbsa_dims& d, TokIn q, const pbsa_ca
   a.H = d.heads;
   a.pairs = cdiv(a.nq, 2);
   a.scale = d.scale;
+  a.route_union = d.route_mode == PBSA_ROUTE_UNION;
+  a.S = d.sinks;
   if (gather_only)
     return d.head_dim == 128 ? launch<128, true, true>(a, s) : launch<64, true, true>(a, s);
   return d.head_dim == 128 ? launch<128, true>(a, s) : launch<64, true>(a, s);

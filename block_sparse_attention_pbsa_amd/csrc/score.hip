@@ -78,7 +78,7 @@ __global__ void __launch_bounds__(64 * QB)
     score_topk_kernel(TokIn xq, int n, int nb, float* q_rep, const float* __restrict__ rep,
                       const int32_t* __restrict__ block_id, int slots, int C, int S, int K,
                       int nq, float scale, float* __restrict__ scores,
-                      int32_t* __restrict__ sel) {
+                      int32_t* __restrict__ sel, int cand0) {
   extern __shared__ float sc_lds[];  // [QB][slots]
   const int r0 = blockIdx.x * QB, h = blockIdx.y, t = threadIdx.x, w = t >> 6, l = t & 63;
   const int nrows = nq - r0 < QB ? nq - r0 : QB;
@@ -146,9 +146,10 @@ __global__ void __launch_bounds__(64 * QB)
     float* srow = scores + (static_cast<int64_t>(h) * nq + r0 + q) * slots;
     for (int s = t; s < slots; s += 64 * QB) srow[s] = sc_lds[q * slots + s];
   }
-  // window candidates: occupied ring slots holding non-sink blocks
+  // candidates: occupied slots from cand0 on holding non-sink blocks (cand0 = C: the
+  // window's ring slots; cand0 = 0: the persistent slots too)
   const int q = w;
-  const int nwin = slots - C;
+  const int nwin = slots - cand0;
   uint64_t key[E];
   int nvalid = 0;
 #pragma unroll
@@ -156,9 +157,9 @@ __global__ void __launch_bounds__(64 * QB)
     const int wi = l + 64 * e;
     key[e] = 0;
     if (q < nrows && wi < nwin) {
-      const int id = bid[C + wi];
+      const int id = bid[cand0 + wi];
       if (id >= S) {
-        key[e] = rank_key(sc_lds[q * slots + C + wi], id);
+        key[e] = rank_key(sc_lds[q * slots + cand0 + wi], id);
         ++nvalid;
       }
     }
@@ -206,18 +207,19 @@ static hipError_t launch_score_d(const pbsa_dims& d, TokIn xq, float* q_rep, con
   const int nb = nb_of(d);
   const int nq = d.chunk_frames * nb;
   const int slots = static_cast<int>(slots_of(d));
-  const int nwin = slots - d.capacity;
+  const int cand0 = d.route_mode == PBSA_ROUTE_UNION ? 0 : d.capacity;
+  const int nwin = slots - cand0;
   const size_t lds = static_cast<size_t>(QB) * slots * sizeof(float);
   dim3 grid(cdiv(nq, QB), d.heads);
 #define PBSA_SCORE_E(EE)                                                                     \
   hipLaunchKernelGGL((score_topk_kernel<D, EE, QB, POOL>), grid, dim3(64 * QB), lds, s, xq,     \
                      d.frame_tokens, nb, q_rep, c.rep, c.block_id, slots, d.capacity, d.sinks, \
-                     d.topk, nq, d.scale, scores, sel)
+                     d.topk, nq, d.scale, scores, sel, cand0)
   if (nwin <= 64) PBSA_SCORE_E(1);
   else if (nwin <= 128) PBSA_SCORE_E(2);
   else if (nwin <= 256) PBSA_SCORE_E(4);
   else if (nwin <= 512) PBSA_SCORE_E(8);
-  else PBSA_SCORE_E(16);  // window blocks <= 1024 (checked at the boundary)
+  else PBSA_SCORE_E(16);  // candidates <= 1024 (checked at the boundary)
 #undef PBSA_SCORE_E
   return hipGetLastError();
 }

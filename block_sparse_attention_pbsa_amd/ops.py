@@ -24,6 +24,8 @@ PBSA_OK = 0
 PBSA_OP_MEMORY_UPDATE = 1
 PBSA_OP_ATTN_BWD = 2
 PBSA_OP_ATTN_BWD_PERSISTENT = 3
+PBSA_ROUTE_WINDOW = 0
+PBSA_ROUTE_UNION = 1
 
 
 class PbsaError(RuntimeError):
@@ -37,7 +39,8 @@ class Dims(ctypes.Structure):
                 ("block", ctypes.c_int32), ("frame_tokens", ctypes.c_int32),
                 ("chunk_frames", ctypes.c_int32), ("window_frames", ctypes.c_int32),
                 ("capacity", ctypes.c_int32), ("sinks", ctypes.c_int32),
-                ("topk", ctypes.c_int32), ("scale", ctypes.c_float)]
+                ("topk", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("route_mode", ctypes.c_int32)]
 
 
 class Tensor(ctypes.Structure):
@@ -70,6 +73,10 @@ _SIGS = {
     "pbsa_last_error": ([], ctypes.c_char_p),
     "pbsa_check_dims": ([ctypes.POINTER(Dims), _I32], ctypes.c_int),
     "pbsa_cache_slots": ([ctypes.POINTER(Dims)], ctypes.c_int64),
+    "pbsa_cache_bytes": ([ctypes.POINTER(Dims)], ctypes.c_size_t),
+    "pbsa_check_cache_table": ([ctypes.POINTER(Dims), _P, _P, ctypes.c_int64], ctypes.c_int),
+    "pbsa_check_selection": ([ctypes.POINTER(Dims), _P, _P], ctypes.c_int),
+    "pbsa_check_selection_2lvl": ([ctypes.POINTER(Dims), _I32, _P, _P, _I32], ctypes.c_int),
     "pbsa_workspace_bytes": ([ctypes.POINTER(Dims), _I32, _I32, _I32], ctypes.c_size_t),
     "pbsa_cache_reset": ([ctypes.POINTER(Dims), ctypes.POINTER(CacheC), _P], ctypes.c_int),
     "pbsa_pool": ([ctypes.POINTER(Dims), Tensor, _I32, _P, _P, _P], ctypes.c_int),
@@ -182,6 +189,7 @@ class Shape:
     topk: int = 1
     scale: float | None = None
     block: int = 64
+    route_mode: int = 0    # PBSA_ROUTE_WINDOW (0) or PBSA_ROUTE_UNION (1)
 
     @property
     def nb(self) -> int:
@@ -202,7 +210,7 @@ class Shape:
     def c(self) -> Dims:
         s = self.scale if self.scale is not None else self.head_dim ** -0.5
         return Dims(self.heads, self.head_dim, self.block, self.frame_tokens, self.chunk_frames,
-                    self.window_frames, self.capacity, self.sinks, self.topk, s)
+                    self.window_frames, self.capacity, self.sinks, self.topk, s, self.route_mode)
 
 
 class Cache:
@@ -502,3 +510,41 @@ def pbsa_attn_bwd_persistent(shape: Shape, q, cache: Cache, chunk_k, chunk_v, se
         ctypes.byref(shape.c()), ts[0], ctypes.byref(cache.c()), ts[1], ts[2], _ptr(sel), ts[3],
         _ptr(lse), ts[4], ts[5], ts[6], ts[7], _ptr(dk_cache), _ptr(dv_cache), _ptr(workspace),
         workspace.numel(), _stream()))
+
+
+# ---- host-side checks (numpy int32 arrays; no device access)
+def _np_i32(a, name, shape):
+    import numpy as np
+    a = np.ascontiguousarray(a, dtype=np.int32)
+    if tuple(a.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {a.shape}, expected {tuple(shape)}")
+    return a
+
+
+def pbsa_cache_bytes(shape: Shape) -> int:
+    return int(lib().pbsa_cache_bytes(ctypes.byref(shape.c())))
+
+
+def pbsa_check_cache_table(shape: Shape, block_id, len_, chunk_index: int):
+    """Raises PbsaError (status PBSA_ERR_INDEX) if the host table is not a valid cache table."""
+    b = _np_i32(block_id, "block_id", (shape.heads, shape.slots))
+    n = _np_i32(len_, "len", (shape.heads, shape.slots))
+    _check("pbsa_check_cache_table", lib().pbsa_check_cache_table(
+        ctypes.byref(shape.c()), b.ctypes.data, n.ctypes.data, int(chunk_index)))
+
+
+def pbsa_check_selection(shape: Shape, block_id, sel):
+    b = _np_i32(block_id, "block_id", (shape.heads, shape.slots))
+    sl = _np_i32(sel, "sel", (shape.heads, shape.nq, shape.topk))
+    _check("pbsa_check_selection", lib().pbsa_check_selection(ctypes.byref(shape.c()),
+                                                              b.ctypes.data, sl.ctypes.data))
+
+
+def pbsa_check_selection_2lvl(shape: Shape, chunks: int, sel, nsel):
+    import numpy as np
+    sl = np.ascontiguousarray(sel, dtype=np.int32)
+    if sl.ndim != 3 or sl.shape[:2] != (shape.heads, chunks * shape.nq):
+        raise ValueError("sel must be (heads, Nq, max_sel)")
+    ns = _np_i32(nsel, "nsel", (shape.heads, chunks * shape.nq))
+    _check("pbsa_check_selection_2lvl", lib().pbsa_check_selection_2lvl(
+        ctypes.byref(shape.c()), chunks, sl.ctypes.data, ns.ctypes.data, sl.shape[2]))

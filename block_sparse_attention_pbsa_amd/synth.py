@@ -46,6 +46,9 @@ class Workload:
     segment_frames: int = 0        # planted blocks re-drawn every this many frames
     q_align: float = 0.0           # query shift along u_h
     kv_shift: float = 0.0          # K/V shift along u_h on planted blocks
+    # each planted segment draws its own direction u_{h,seg} (K/V of its planted blocks
+    # and the queries of its frames shift along it), instead of one u_h per head
+    direction_per_segment: bool = False
     # trainable two-level path
     clip_chunks: int = 0
     top_frames: int = 0
@@ -132,9 +135,11 @@ def round_bf16(x) -> np.ndarray:
     return _rne_high_half(x).view(np.float32)
 
 
-def directions(wl: Workload, seed: int) -> np.ndarray:
-    """Per-head unit direction u_h [H, d] (float32)."""
-    u = rng(seed, "u").standard_normal((wl.heads, wl.head_dim))
+def directions(wl: Workload, seed: int, segment: int = 0) -> np.ndarray:
+    """Per-head unit direction u_h [H, d] (float32); with direction_per_segment, the
+    direction of planted segment `segment`."""
+    idx = segment if wl.direction_per_segment else 0
+    u = rng(seed, "u", idx).standard_normal((wl.heads, wl.head_dim))
     u /= np.linalg.norm(u, axis=1, keepdims=True)
     return u.astype(np.float32)
 
@@ -194,11 +199,20 @@ def _draw_qkv(wl: Workload, seed: int, c: int, g, total_frames):
     q, k, v = (g.standard_normal((F * n, H, d), dtype=np.float32) for _ in range(3))
     if wl.planted_per_segment:
         tf = total_frames if total_frames is not None else wl.plant_frames
-        u = directions(wl, seed)
         pm = _plant_mask_tokens(wl, planted_blocks(wl, seed, tf), c * F, F)
-        k[pm] += wl.kv_shift * u[None, :, :]
-        v[pm] += wl.kv_shift * u[None, :, :]
-        q += wl.q_align * u[None, :, :]
+        if not wl.direction_per_segment:
+            u = directions(wl, seed)
+            k[pm] += wl.kv_shift * u[None, :, :]
+            v[pm] += wl.kv_shift * u[None, :, :]
+            q += wl.q_align * u[None, :, :]
+        else:
+            for fl in range(F):
+                u = directions(wl, seed, (c * F + fl) // wl.segment_frames)
+                sl = slice(fl * n, (fl + 1) * n)
+                m = pm[sl]
+                k[sl][m] += wl.kv_shift * u[None, :, :]
+                v[sl][m] += wl.kv_shift * u[None, :, :]
+                q[sl] += wl.q_align * u[None, :, :]
     return round_bf16(q), round_bf16(k), round_bf16(v)
 
 

@@ -57,7 +57,9 @@ typedef enum pbsa_status {
   PBSA_ERR_ALIGN = 4,       /* token pointer or stride not aligned for 16-byte loads */
   PBSA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than pbsa_workspace_bytes */
   PBSA_ERR_STATE = 6,       /* cache bookkeeping out of range (chunk_index) */
-  PBSA_ERR_HIP = 7          /* a HIP call failed; its text is in pbsa_last_error() */
+  PBSA_ERR_HIP = 7,         /* a HIP call failed; its text is in pbsa_last_error() */
+  PBSA_ERR_INDEX = 8        /* a block list or cache table holds an id it may not hold
+                               (pbsa_check_*; the first offender is in pbsa_last_error()) */
 } pbsa_status;
 
 /* Shapes of one attention layer.  For the two-level (trainable) calls only heads,
@@ -73,7 +75,17 @@ typedef struct pbsa_dims {
   int32_t sinks;         /* sink blocks S: global ids 0..S-1, S <= min(C, nb) */
   int32_t topk;          /* window blocks routed per query block, K >= 1 */
   float scale;           /* softmax scale, usually 1/sqrt(d) */
+  int32_t route_mode;    /* persistent mode: PBSA_ROUTE_WINDOW (0) or PBSA_ROUTE_UNION (1) */
 } pbsa_dims;
+
+/* What the persistent-mode top-K chooses from (Sparse Forcing 2.C; north_star's "score
+ * against P and L, keep the top-k"):
+ *   PBSA_ROUTE_WINDOW: the window blocks; every persistent block is attended.
+ *   PBSA_ROUTE_UNION:  the non-sink persistent blocks and the window blocks together; only
+ *                      the sinks are attended whole.  Limit: capacity + window blocks
+ *                      <= 1024 in this mode.
+ * The memory update is the same in both. */
+enum { PBSA_ROUTE_WINDOW = 0, PBSA_ROUTE_UNION = 1 };
 
 /* A bf16 token tensor: element (head h, token t, channel c) lives at
  * data[h*head_stride + t*token_stride + c] (strides in elements).  [T][H][d] has
@@ -123,6 +135,36 @@ pbsa_status pbsa_check_dims(const pbsa_dims* dims, int32_t mode);
 /* Slots per head of the persistent cache: capacity + window_frames * nb (0 if invalid). */
 int64_t pbsa_cache_slots(const pbsa_dims* dims);
 
+/* Device bytes of one layer's persistent cache (k, v, rep, block_id, len; see pbsa_cache),
+ * 0 if dims are invalid. */
+size_t pbsa_cache_bytes(const pbsa_dims* dims);
+
+/* ---- host-side checks of lists and tables (no device access) ------------------------
+ * For callers that build or keep routing lists and cache tables themselves: each check
+ * reads HOST copies (taken after the caller's synchronisation) and returns PBSA_OK, or
+ * PBSA_ERR_INDEX with the first offending entry described in pbsa_last_error().
+ *
+ * pbsa_check_cache_table: block_id, len [heads][slots] of a persistent cache that has
+ *   appended chunk_index chunks (Sparse Forcing 2.B): the sink blocks 0..S-1 in slots
+ *   0..S-1 (once a chunk has been appended); other persistent slots empty or holding
+ *   distinct non-sink blocks of frames that have left the window; window slot
+ *   capacity + (f % W)*nb + j holding block f*nb + j for every non-sink block of the W
+ *   latest history frames (others empty); every length the block's token count.
+ * pbsa_check_selection: sel [heads][Nq][topk] against such a table: per query block the
+ *   ids before the first -1 strictly ascending, -1 only in the tail, every id a non-sink
+ *   block the table holds in a window slot (PBSA_ROUTE_UNION: or in a persistent slot),
+ *   and exactly min(topk, candidates) of them.
+ * pbsa_check_selection_2lvl: sel [heads][Nq][max_sel], nsel [heads][Nq] of a clip of
+ *   `chunks` chunks: 1 <= nsel <= max_sel, the first nsel ids strictly ascending, each a
+ *   block of a frame the query block's chunk sees (frames < chunk_frames * i, chunk i
+ *   1-based). */
+pbsa_status pbsa_check_cache_table(const pbsa_dims* dims, const int32_t* block_id,
+                                   const int32_t* len, int64_t chunk_index);
+pbsa_status pbsa_check_selection(const pbsa_dims* dims, const int32_t* block_id,
+                                 const int32_t* sel);
+pbsa_status pbsa_check_selection_2lvl(const pbsa_dims* dims, int32_t chunks, const int32_t* sel,
+                                      const int32_t* nsel, int32_t max_sel);
+
 enum { PBSA_OP_MEMORY_UPDATE = 1, PBSA_OP_ATTN_BWD = 2, PBSA_OP_ATTN_BWD_PERSISTENT = 3 };
 /* Workspace bytes a call needs.  MEMORY_UPDATE and ATTN_BWD_PERSISTENT: `arg`, `arg2`
  * unused.  ATTN_BWD: `arg` = clip chunks, `arg2` = max_sel. */
@@ -147,9 +189,10 @@ pbsa_status pbsa_pool(const pbsa_dims* dims, pbsa_tensor x, int32_t frames, floa
  * [heads][Nq][head_dim] (from pbsa_pool of the chunk's queries):
  *   scores[h][r][s] = scale * <q_rep[h][r], cache.rep[h][s]> for every valid slot s
  *                     (P_t and window), -inf for empty slots; fp32 [heads][Nq][slots].
- *   sel[h][r][0..K) = the K window blocks (sinks excluded) with the highest score, ties to
- *                     the lower global id, written as global ids in ascending order; -1
- *                     fills the tail when the window holds fewer than K blocks.
+ *   sel[h][r][0..K) = the K window blocks (sinks excluded; with PBSA_ROUTE_UNION the K
+ *                     non-sink blocks of P_t and the window) with the highest score, ties
+ *                     to the lower global id, written as global ids in ascending order; -1
+ *                     fills the tail when there are fewer than K candidates.
  *                     int32 [heads][Nq][topk].
  */
 pbsa_status pbsa_score_topk(const pbsa_dims* dims, const float* q_rep, const pbsa_cache* cache,
@@ -167,13 +210,16 @@ pbsa_status pbsa_route(const pbsa_dims* dims, pbsa_tensor q, const pbsa_cache* c
 /* ---- step 3: attention over the selected blocks (persistent mode) --------------------
  * Sparse Forcing 2.C and the Chinese page's 2.2 (fine-grained attention, hybrid mask):
  * every query token t of query block r attends, with softmax scale dims.scale, to the
- * valid tokens of: every occupied persistent slot, the window blocks sel[h][r][*], and all
- * chunk_frames*nb blocks of the current chunk (chunk_k/chunk_v, no causal mask inside the
- * chunk).  Writes o (bf16, same shape as q: chunk_frames*frame_tokens tokens per head)
+ * valid tokens of: every occupied persistent slot (PBSA_ROUTE_UNION: the sink slots), the
+ * blocks sel[h][r][*], and all chunk_frames*nb blocks of the current chunk
+ * (chunk_k/chunk_v, no causal mask inside the chunk).  Writes o (bf16, same shape as q: chunk_frames*frame_tokens tokens per head)
  * and lse[h][t] = natural-log sum of exp(scale * q.k) over the attended keys (fp32
  * [heads][chunk tokens]).  q, chunk_k, chunk_v: chunk_frames*frame_tokens tokens each.
- * sel: int32 [heads][Nq][topk] as pbsa_score_topk writes it: distinct global ids in
- * ascending order, -1 only in the tail (other contents give undefined results).
+ * sel: int32 [heads][Nq][topk] as pbsa_score_topk writes it: distinct global ids of blocks
+ * the cache holds (window blocks; with PBSA_ROUTE_UNION also non-sink persistent blocks) in
+ * ascending order, -1 only in the tail.  Other contents give undefined values (an id the
+ * cache does not hold contributes nothing in PBSA_ROUTE_UNION mode) but every read stays
+ * inside the cache and the chunk.
  */
 pbsa_status pbsa_attn_fwd(const pbsa_dims* dims, pbsa_tensor q, const pbsa_cache* cache,
                           pbsa_tensor chunk_k, pbsa_tensor chunk_v, const int32_t* sel,
@@ -316,7 +362,11 @@ pbsa_status pbsa_score_topk_2lvl(const pbsa_dims* dims, int32_t chunks, int32_t 
 
 /* Attention of the clip's queries over their selected blocks (sel/nsel from
  * pbsa_score_topk_2lvl): o (bf16, like q) and lse (fp32 [heads][clip tokens]).
- * q, k, v: chunks*chunk_frames*frame_tokens tokens per head.  max_sel <= 1536. */
+ * q, k, v: chunks*chunk_frames*frame_tokens tokens per head.  max_sel <= 1536.
+ * sel/nsel are meant to pass pbsa_check_selection_2lvl (what pbsa_score_topk_2lvl writes
+ * does); for other lists the values are undefined (the forward attends every listed id,
+ * the backward's dK/dV leave out blocks the query block's chunk cannot see), but ids
+ * outside the clip are skipped and no read leaves q, k, v and the lists. */
 pbsa_status pbsa_attn_fwd_2lvl(const pbsa_dims* dims, int32_t chunks, pbsa_tensor q,
                                pbsa_tensor k, pbsa_tensor v, const int32_t* sel,
                                const int32_t* nsel, int32_t max_sel, pbsa_tensor o, float* lse,

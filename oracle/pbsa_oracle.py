@@ -29,11 +29,17 @@ Readings taken where the pages leave a step open (each is restated at its functi
   * ordering for every top-k is (score descending, id ascending); lists are returned
     ascending;
   * top-K chooses among the window blocks only; P_t is attended whole; the current
-    chunk's own blocks are always attended, with no causal mask inside the chunk;
+    chunk's own blocks are always attended, with no causal mask inside the chunk (a
+    variant routes among the non-sink persistent blocks and the window together, the
+    sinks alone attended whole);
   * sink blocks are the first S blocks of frame 0, pinned in P_t from the first update;
   * the memory score of a history block is the sum over the chunk's query blocks of its
-    coarse score (a column sum).  That operator is NOT fixed by the pages: parity
-    unpinned for the operator itself; the Top-C step applied to it is pinned.
+    coarse score (a column sum).  The pages fix that the blocks the chunk's queries score
+    highest are promoted; the pins fix the orientation (an aggregate over the chunk's
+    query blocks of each candidate's own column), the sign and strict monotonicity (a
+    candidate scored at least as high by every query block, and higher by one, is never
+    dropped while the other is kept).  Which strictly monotone aggregate (a sum rather
+    than, say, a softmax mass) stays a reading.
 
 Everything floating point is float64.  Inputs given as float32/bf16-valued arrays are
 widened to float64 first.
@@ -209,6 +215,10 @@ class Schedule:
     S: int          # sink blocks: global ids 0..S-1 (frame 0)
     K: int          # top-K window blocks per query block
     scale: float
+    # routing variant: False = top-K among the window blocks, every persistent block
+    # attended; True = top-K among the non-sink persistent blocks and the window blocks
+    # together, only the sinks attended whole
+    union: bool = False
 
     @property
     def nb(self) -> int:
@@ -305,7 +315,10 @@ class PersistentRollout:
     def select(self, q_chunk):
         """Pool the chunk's queries, score P_t and L_t, route.
 
-        Returns dict(q_rep, P, L, scores_P [Nq, |P|], scores_L [Nq, |L|], sel).
+        Returns dict(q_rep, P, L, scores_P [Nq, |P|], scores_L [Nq, |L|], cand,
+        scores_cand, sel): cand are the blocks the top-K chooses from (L_t; with
+        sch.union the non-sink blocks of P_t followed by L_t) and scores_cand their
+        columns.
         """
         s = self.sch
         q_rep, _ = mean_pool(q_chunk, s.n, s.B)
@@ -313,13 +326,22 @@ class PersistentRollout:
         P = list(self.P)
         scores_P = coarse_scores(q_rep, self._reps(P), s.scale) if P else np.zeros((len(q_rep), 0))
         scores_L = coarse_scores(q_rep, self._reps(L), s.scale) if L else np.zeros((len(q_rep), 0))
-        sel = route(scores_L, L, s.K)
-        return dict(q_rep=q_rep, P=P, L=L, scores_P=scores_P, scores_L=scores_L, sel=sel)
+        if s.union:
+            keep = [i for i, g in enumerate(P) if g >= s.S]
+            cand = [P[i] for i in keep] + L
+            scores_cand = np.concatenate([scores_P[:, keep], scores_L], axis=1)
+        else:
+            cand, scores_cand = L, scores_L
+        sel = route(scores_cand, cand, s.K)
+        return dict(q_rep=q_rep, P=P, L=L, scores_P=scores_P, scores_L=scores_L, cand=cand,
+                    scores_cand=scores_cand, sel=sel)
 
     def attended_blocks(self, sel):
-        """A_r = P_t + sel[r] + the chunk's own blocks, as global block ids."""
+        """A_r = P_t + sel[r] + the chunk's own blocks, as global block ids (with sch.union
+        only the sinks of P_t are attended whole: A_r = sinks + sel[r] + the chunk)."""
         own = self.sch.chunk_blocks(self.chunk)
-        return [sorted(set(self.P) | set(row) | set(own)) for row in sel]
+        whole = [g for g in self.P if g < self.sch.S] if self.sch.union else self.P
+        return [sorted(set(whole) | set(row) | set(own)) for row in sel]
 
     def attend(self, q_chunk, k_chunk, v_chunk, sel, rows=None):
         """Gathered form: per query block, softmax attention over the tokens of A_r.

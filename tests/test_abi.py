@@ -1,9 +1,11 @@
 """CPU checks of the C ABI: the library loads, exports every declared symbol, and rejects bad
 arguments before touching the GPU (no compute calls here)."""
 import ctypes
+import dataclasses
 import os
 import re
 
+import numpy as np
 import pytest
 
 from block_sparse_attention_pbsa_amd import ops, runtime
@@ -72,6 +74,9 @@ def _dims(**kw):
     (dict(scale=float("nan")), 1, 2),
     (dict(capacity=5000), 0, 3),
     (dict(topk=1025), 0, 3),             # topk above the supported maximum
+    (dict(route_mode=1), 0, 0),          # top-K over the persistent and window blocks
+    (dict(route_mode=2), 0, 2),
+    (dict(route_mode=1, capacity=900), 0, 3),   # union routing: slots above 1024
 ])
 def test_check_dims(kw, mode, status):
     L = ops.lib()
@@ -210,3 +215,76 @@ def test_chunk_step_checks_before_launching():
     cache = ops.CacheC(16, 16, 16, 16, 16, 0, 12)
     assert L.pbsa_chunk_graph_create(d, ctypes.byref(a), ctypes.byref(cache), ctypes.byref(h)) == 4
     assert L.pbsa_chunk_graph_launch(None, ctypes.byref(cache), None) == 1
+
+
+TINY = ops.Shape(heads=1, head_dim=64, frame_tokens=256, chunk_frames=1, window_frames=2,
+                 capacity=4, sinks=1, topk=2)
+
+
+def _tiny_table():
+    """Hand-built table after 3 appended 1-frame chunks (4 blocks per frame): the sink in
+    slot 0, blocks 1 and 2 of frame 0 promoted, window = frames 1 and 2 in ring slots
+    4 + (f % 2) * 4 + j."""
+    bid = np.full((1, 12), -1, np.int32)
+    bid[0, :3] = [0, 1, 2]
+    bid[0, 8:12] = [4, 5, 6, 7]     # frame 1 -> ring position 1
+    bid[0, 4:8] = [8, 9, 10, 11]    # frame 2 -> ring position 0
+    ln = np.where(bid >= 0, 64, 0).astype(np.int32)
+    return bid, ln
+
+
+def test_cache_bytes_and_table_checks():
+    assert ops.pbsa_cache_bytes(WAN) == 12 * (64 + 150) * (2 * 64 * 128 * 2 + 128 * 4 + 8)
+    bid, ln = _tiny_table()
+    ops.pbsa_check_cache_table(TINY, bid, ln, 3)
+    bad = [("sink missing", lambda b, l: (b.__setitem__((0, 0), 5), l)),
+           ("block held twice", lambda b, l: (b.__setitem__((0, 3), 1), l.__setitem__((0, 3), 64))),
+           ("window block in P", lambda b, l: (b.__setitem__((0, 3), 4), l.__setitem__((0, 3), 64))),
+           ("window slot wrong block", lambda b, l: (b.__setitem__((0, 9), 6), l)),
+           ("length wrong", lambda b, l: (b, l.__setitem__((0, 5), 12)))]
+    for what, edit in bad:
+        b, l_ = bid.copy(), ln.copy()
+        edit(b, l_)
+        with pytest.raises(ops.PbsaError) as e:
+            ops.pbsa_check_cache_table(TINY, b, l_, 3)
+        assert e.value.status == 8, what
+    # an empty cache (no chunk appended) is all -1
+    ops.pbsa_check_cache_table(TINY, np.full((1, 12), -1, np.int32), np.zeros((1, 12), np.int32), 0)
+
+
+def test_selection_checks():
+    bid, _ = _tiny_table()
+    sel = np.array([[[4, 9], [5, 11], [8, 10], [6, 7]]], np.int32)
+    ops.pbsa_check_selection(TINY, bid, sel)
+    for bad in ([[9, 4]], [[4, 4]], [[-1, 4]], [[1, 4]], [[0, 4]], [[4, -1]], [[12, 13]]):
+        s = sel.copy()
+        s[0, 2] = bad[0]
+        with pytest.raises(ops.PbsaError) as e:
+            ops.pbsa_check_selection(TINY, bid, s)
+        assert e.value.status == 8, bad
+    # top-K over the persistent and window blocks: non-sink persistent blocks are candidates
+    uni = dataclasses.replace(TINY, route_mode=ops.PBSA_ROUTE_UNION)
+    s = sel.copy()
+    s[0, 2] = [1, 4]
+    ops.pbsa_check_selection(uni, bid, s)
+    s[0, 2] = [0, 4]
+    with pytest.raises(ops.PbsaError):
+        ops.pbsa_check_selection(uni, bid, s)
+    # two-level lists: visible frames only, ascending, counted
+    two = ops.Shape(heads=1, head_dim=64, frame_tokens=128, chunk_frames=1)
+    sel2 = np.full((1, 6, 4), -1, np.int32)
+    nsel2 = np.array([[2, 2, 3, 3, 4, 4]], np.int32)   # 3 chunks of 1 frame, 2 blocks each
+    sel2[0, 0, :2] = sel2[0, 1, :2] = [0, 1]
+    sel2[0, 2, :3] = sel2[0, 3, :3] = [0, 2, 3]
+    sel2[0, 4, :4] = sel2[0, 5, :4] = [0, 1, 4, 5]
+    ops.pbsa_check_selection_2lvl(two, 3, sel2, nsel2)
+    for r, row in ((0, [0, 2]), (2, [0, 3, 2]), (4, [0, 1, 4, 9])):
+        s2 = sel2.copy()
+        s2[0, r, :len(row)] = row
+        with pytest.raises(ops.PbsaError) as e:
+            ops.pbsa_check_selection_2lvl(two, 3, s2, nsel2)
+        assert e.value.status == 8
+    n2 = nsel2.copy()
+    n2[0, 1] = 0
+    with pytest.raises(ops.PbsaError):
+        ops.pbsa_check_selection_2lvl(two, 3, sel2, n2)

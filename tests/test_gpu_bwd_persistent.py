@@ -26,19 +26,20 @@ def dev(x):
     return torch.from_numpy(np.ascontiguousarray(x)).cuda().to(torch.bfloat16)
 
 
-def shape_of(wl):
+def shape_of(wl, union=False):
     return ops.Shape(wl.heads, wl.head_dim, wl.frame_tokens, wl.chunk_frames, wl.window_frames,
-                     wl.capacity, wl.sinks, wl.topk, wl.scale)
+                     wl.capacity, wl.sinks, wl.topk, wl.scale,
+                     route_mode=ops.PBSA_ROUTE_UNION if union else ops.PBSA_ROUTE_WINDOW)
 
 
 SMALL64 = synth.Workload("small64", 2, 64, 64, 100, 2, 8, 4, 3, 1, 3)
 RAGGED128 = synth.Workload("ragged128", 3, 128, 64, 100, 2, 10, 4, 5, 1, 4)
 
 
-def build(wl, seed, heads):
-    shape = shape_of(wl)
+def build(wl, seed, heads, union=False):
+    shape = shape_of(wl, union)
     sch = orc.Schedule(wl.frame_tokens, wl.block, wl.chunk_frames, wl.window_frames,
-                       wl.capacity, wl.sinks, wl.topk, wl.scale)
+                       wl.capacity, wl.sinks, wl.topk, wl.scale, union)
     layer = runtime.PersistentLayer(shape)
     layer.reset()
     ros = {h: orc.PersistentRollout(sch, wl.head_dim) for h in heads}
@@ -72,13 +73,15 @@ def run_bwd(shape, layer, qd, kd, vd, doutd):
     return dq, dk, dv, dkc, dvc
 
 
-@pytest.mark.parametrize("name,heads", [("tiny", (0,)), ("small64", (0, 1)),
-                                        ("ragged128", (0, 2)), ("wan_5s", (4,))])
-def test_persistent_backward_parity(name, heads):
+@pytest.mark.parametrize("name,heads,union", [
+    ("tiny", (0,), False), ("small64", (0, 1), False), ("ragged128", (0, 2), False),
+    ("wan_5s", (4,), False), ("small64", (0, 1), True), ("ragged128", (1,), True),
+    ("wan_5s", (9,), True)])
+def test_persistent_backward_parity(name, heads, union):
     wl = {"small64": SMALL64, "ragged128": RAGGED128}.get(name) or synth.WORKLOADS[name]
     seed = synth.SEEDS.get(name, 77)
-    say(f"[bwd persistent] {name}")
-    shape, layer, ros = build(wl, seed, heads)
+    say(f"[bwd persistent] {name} union={union}")
+    shape, layer, ros = build(wl, seed, heads, union)
     q, k, v = synth.chunk_qkv(wl, seed, wl.measured_chunk)
     dout = synth.clip_dout(wl, seed, q.shape[0])
     qd, kd, vd, doutd = dev(q), dev(k), dev(v), dev(dout)
@@ -93,7 +96,7 @@ def test_persistent_backward_parity(name, heads):
         rt = ros[h].select(q[:, h])
         for r in range(shape.nq):
             got = [int(g) for g in sel[h, r] if g >= 0]
-            check_topk(got, rt["L"], rt["scores_L"][r], wl.topk)
+            check_topk(got, rt["cand"], rt["scores_cand"][r], wl.topk)
         gsel = [[int(g) for g in sel[h, r] if g >= 0] for r in range(shape.nq)]
         rdq, rdk, rdv, rdkb, rdvb = ros[h].attend_grad(q[:, h], k[:, h], v[:, h], gsel, dout[:, h])
         assert_close_attn(dq[:, h].float().cpu().numpy(), rdq, f"dQ head {h}")

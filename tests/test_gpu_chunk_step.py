@@ -86,7 +86,7 @@ def test_chunk_step_fused_and_graph(name, passes, heads, rows):
                     rt = ros[h].select(q[:, h])
                     for r in range(shape.nq):
                         got = [int(g) for g in sels[p][h, r] if g >= 0]
-                        check_topk(got, rt["L"], rt["scores_L"][r], wl.topk)
+                        check_topk(got, rt["cand"], rt["scores_cand"][r], wl.topk)
                     gsel = [[int(g) for g in sels[p][h, r] if g >= 0] for r in range(shape.nq)]
                     idx = np.arange(T) if rows is None else np.unique(np.r_[
                         0:64, 1536:1560, T - 24:T,

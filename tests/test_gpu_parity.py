@@ -43,9 +43,9 @@ def shape_of(wl, **over):
     return ops.Shape(**kw)
 
 
-def schedule_of(wl):
+def schedule_of(wl, union=False):
     return orc.Schedule(wl.frame_tokens, wl.block, wl.chunk_frames, wl.window_frames,
-                        wl.capacity, wl.sinks, wl.topk, wl.scale)
+                        wl.capacity, wl.sinks, wl.topk, wl.scale, union)
 
 
 # --------------------------------------------------------------------------- pooling
@@ -113,11 +113,11 @@ def check_slots(layer, ro, h, wl):
 
 
 def rollout_parity(name, attn_rows=None, slot_check_every=1, dense_check=False, wl=None,
-                   seed=None):
+                   seed=None, union=False):
     wl = wl if wl is not None else synth.WORKLOADS[name]
     seed = seed if seed is not None else synth.SEEDS[name]
-    shape = shape_of(wl)
-    sch = schedule_of(wl)
+    shape = shape_of(wl, route_mode=ops.PBSA_ROUTE_UNION if union else ops.PBSA_ROUTE_WINDOW)
+    sch = schedule_of(wl, union)
     H, C, K = wl.heads, wl.capacity, wl.topk
     layer = runtime.PersistentLayer(shape)
     layer.reset()
@@ -133,6 +133,9 @@ def rollout_parity(name, attn_rows=None, slot_check_every=1, dense_check=False, 
         scores = layer.scores.cpu().numpy()
         sel = layer.sel.cpu().numpy()
         bid = layer.cache.block_id.cpu().numpy()
+        # the table and the routing pass the library's own host-side checks
+        ops.pbsa_check_cache_table(shape, bid, layer.cache.len.cpu().numpy(), c)
+        ops.pbsa_check_selection(shape, bid, sel)
         routed = []
         for h in range(H):
             ro = ros[h]
@@ -152,7 +155,7 @@ def rollout_parity(name, attn_rows=None, slot_check_every=1, dense_check=False, 
             for r in range(shape.nq):
                 got = [g for g in sel[h, r] if g >= 0]
                 assert all(g == -1 for g in sel[h, r, len(got):])
-                exact, near = check_topk(got, rt["L"], rt["scores_L"][r], K)
+                exact, near = check_topk(got, rt["cand"], rt["scores_cand"][r], K)
                 stats["rows"] += 1
                 stats["near"] += near
         if c == last:
@@ -216,6 +219,47 @@ def test_rollout_wan_20s_parity():
 def test_rollout_wan_1min_parity():
     stats, _, _ = rollout_parity("wan_1min", attn_rows=sampled_rows(3), slot_check_every=20)
     say(f"  wan_1min: {stats}")
+
+
+# ---- selection variants: top-K over P_t and the window together, whole-frame sinks,
+# planted directions that change with each segment
+def test_rollout_tiny_union_routing_full_parity():
+    stats, _, _ = rollout_parity("tiny", dense_check=True, union=True)
+    say(f"  tiny union: {stats}")
+
+
+def test_rollout_wan_5s_union_routing_parity():
+    stats, _, _ = rollout_parity("wan_5s", attn_rows=sampled_rows(4), slot_check_every=3,
+                                 union=True)
+    say(f"  wan_5s union: {stats}")
+
+
+def test_rollout_wan_1min_union_routing_parity():
+    stats, _, _ = rollout_parity("wan_1min", attn_rows=sampled_rows(5), slot_check_every=40,
+                                 union=True)
+    say(f"  wan_1min union: {stats}")
+
+
+def test_rollout_whole_frame_sinks_parity():
+    # frame 0's 25 blocks are the sinks (S = nb): pinned in P_t, never routed or evicted
+    import dataclasses
+    wl = dataclasses.replace(synth.WORKLOADS["wan_5s"], name="frame_sinks", sinks=25)
+    stats, layer, ros = rollout_parity("frame_sinks", attn_rows=sampled_rows(6),
+                                       slot_check_every=3, wl=wl, seed=1006)
+    for h in range(wl.heads):
+        assert set(range(25)) <= set(gpu_P(layer, h, wl.capacity))
+    say(f"  whole-frame sinks: {stats}")
+
+
+def test_rollout_per_segment_directions_parity():
+    # the planted direction changes every 6 frames: the memory must let old salient blocks
+    # go as the queries turn to the new segment's direction
+    wl = synth.Workload("seg_dirs", 4, 128, 64, 1560, 3, 30, 6, 64, 1, 32,
+                        planted_per_segment=8, segment_frames=6, q_align=1.0, kv_shift=3.0,
+                        direction_per_segment=True)
+    stats, _, _ = rollout_parity("seg_dirs", attn_rows=sampled_rows(7), slot_check_every=3,
+                                 wl=wl, seed=1007)
+    say(f"  per-segment directions: {stats}")
 
 
 @pytest.mark.parametrize("name", ["small64", "wan_5s"])
@@ -369,6 +413,8 @@ def two_level_check(wl, seed, grad_check="full", rows_fn=None, kv_blocks_fn=None
     torch.cuda.synchronize()
     sel = clip.sel.cpu().numpy()
     nsel = clip.nsel.cpu().numpy()
+    # the selection passes the library's own host-side check
+    ops.pbsa_check_selection_2lvl(shape, chunks, sel, nsel)
     near_rows = 0
     gsel_all = []
     for h in range(H):

@@ -461,6 +461,64 @@ def test_persistent_gradient_of_unattended_blocks_is_zero():
         assert np.abs(dvb[g]).sum() > 0
 
 
+def _rollout_sels(wl, seed, union, chunks):
+    sch = orc.Schedule(wl.frame_tokens, wl.block, wl.chunk_frames, wl.window_frames,
+                       wl.capacity, wl.sinks, wl.topk, wl.scale, union)
+    ro = orc.PersistentRollout(sch, wl.head_dim)
+    out = []
+    for c in range(chunks):
+        q, k, v = (a[:, 0] for a in synth.chunk_qkv(wl, seed, c))
+        rt = ro.select(q)
+        o, lse = ro.attend(q, k, v, rt["sel"])
+        out.append((rt, ro.attended_blocks(rt["sel"]), o, lse, list(ro.P)))
+        ro.update(rt, k, v)
+    return sch, out
+
+
+def test_union_routing_with_only_sinks_in_memory_is_window_routing():
+    # capacity = sinks: P_t holds only the sinks, so routing over P_t and the window
+    # together chooses among the window alone
+    wl = synth.Workload("u1", 1, 16, 8, 24, 2, 12, 4, 2, 2, 3)
+    _, a = _rollout_sels(wl, 13, False, wl.measured_chunk + 1)
+    _, b = _rollout_sels(wl, 13, True, wl.measured_chunk + 1)
+    for (ra, aa, oa, la, pa), (rb, ab, ob, lb, pb) in zip(a, b):
+        assert ra["sel"] == rb["sel"] and aa == ab and pa == pb
+        np.testing.assert_array_equal(oa, ob)
+
+
+def test_union_routing_full_selection_is_dense_attention():
+    # top-K at least every candidate: both variants attend everything
+    wl = synth.Workload("u2", 1, 8, 4, 12, 1, 5, 2, 100, 1, 100)
+    _, a = _rollout_sels(wl, 14, False, wl.measured_chunk + 1)
+    _, b = _rollout_sels(wl, 14, True, wl.measured_chunk + 1)
+    for (ra, aa, oa, la, pa), (rb, ab, ob, lb, pb) in zip(a, b):
+        assert aa == ab
+        np.testing.assert_allclose(oa, ob, atol=1e-12, rtol=0)
+
+
+def test_union_routing_candidates_and_invariants():
+    # routing over P_t and the window: candidates are exactly the non-sink persistent
+    # blocks and the window blocks; every query block attends the sinks, its K routed
+    # blocks and its chunk, and no other persistent block
+    wl = synth.Workload("u3", 1, 16, 8, 24, 2, 16, 4, 6, 2, 4)
+    sch, out = _rollout_sels(wl, 15, True, wl.measured_chunk + 1)
+    routed_p = 0
+    for c, (rt, att, o, lse, P) in enumerate(out):
+        sinks = [g for g in P if g < sch.S]
+        assert rt["cand"] == [g for g in P if g >= sch.S] + rt["L"]
+        own = set(sch.chunk_blocks(c))
+        for row, a in zip(rt["sel"], att):
+            assert len(row) == min(sch.K, len(rt["cand"])) and set(row) <= set(rt["cand"])
+            assert set(a) == set(sinks) | set(row) | own
+            routed_p += len(set(row) & set(P))
+        # the best-scoring candidate of each query block is always routed
+        for r, row in enumerate(rt["sel"]):
+            if rt["cand"]:
+                best = rt["cand"][int(np.lexsort((rt["cand"], -rt["scores_cand"][r]))[0])]
+                assert best in row
+    assert routed_p > 0
+
+
 def test_gathered_and_dense_masked_forms_agree():
     wl = synth.WORKLOADS["tiny"]
     sch, ros, (q, k, v, routed) = _rollout(wl, 5)
