@@ -289,6 +289,77 @@ def memory_update(P, sinks, scores_P, evicted_ids, scores_E, C: int):
     return sorted(sinks + keep)
 
 
+# --------------------------------------------------------------------------------------
+# FP8 KV cache.  Light Forcing ("Key findings"): FP8 deployment of the sparse attention.
+# Reading: each stored block's K and V are kept in the OCP float8 E4M3 format (1 sign bit,
+# 4 exponent bits with bias 7, 3 mantissa bits; no infinities; largest finite value 448)
+# with one power-of-two scale per block and tensor, the smallest 2^e with amax <= 448 * 2^e
+# (amax = the largest |value| of the block's valid tokens; 1 for an all-zero block), and
+# round-to-nearest-even.  Attention then runs on the decoded values code * scale, which
+# are exact in bf16 (four significant bits times a power of two).
+# --------------------------------------------------------------------------------------
+
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(code):
+    """Value of E4M3 codes (uint8 array): normal (-1)^s 2^(e-7) (1 + m/8), subnormal
+    (-1)^s 2^-6 m/8; exponent 15 with mantissa 7 is NaN."""
+    c = np.asarray(code, dtype=np.int64)
+    sgn = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    val = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * 2.0 ** (e - 7.0))
+    val = np.where((e == 15) & (m == 7), np.nan, val)
+    return sgn * val
+
+
+def e4m3_encode(y):
+    """Nearest E4M3 code to each value of y (|y| <= 448), ties to the even mantissa."""
+    y = np.asarray(y, dtype=np.float64)
+    if np.any(np.abs(y) > E4M3_MAX) or np.any(~np.isfinite(y)):
+        raise ValueError("value outside the E4M3 range")
+    sign = np.signbit(y).astype(np.int64) << 7
+    a = np.abs(y)
+    out = np.zeros(a.shape, dtype=np.int64)
+    sub = a < 2.0 ** -6
+    # subnormal range: a multiple of 2^-9, rounded to nearest even (np.rint), 8 -> 2^-6
+    out[sub] = np.rint(a[sub] * 2.0 ** 9).astype(np.int64)
+    nrm = ~sub
+    if np.any(nrm):
+        e = np.floor(np.log2(a[nrm])).astype(np.int64)
+        # guard the logarithm's rounding: a = f * 2^e with f in [1, 2)
+        e = np.where(a[nrm] < 2.0 ** e, e - 1, e)
+        e = np.where(a[nrm] >= 2.0 ** (e + 1), e + 1, e)
+        f = a[nrm] / 2.0 ** e
+        m = np.rint((f - 1.0) * 8.0).astype(np.int64)
+        carry = m == 8
+        m = np.where(carry, 0, m)
+        e = np.where(carry, e + 1, e)
+        out[nrm] = ((e + 7) << 3) | m
+    return (out | sign).astype(np.uint8)
+
+
+def e4m3_block_scale(x):
+    """Power-of-two scale of a block: the smallest 2^e with max|x| <= 448 * 2^e (1 when the
+    block is all zero)."""
+    amax = float(np.max(np.abs(np.asarray(x, dtype=np.float64)))) if np.size(x) else 0.0
+    if amax == 0.0:
+        return 1.0
+    e = math.ceil(math.log2(amax / E4M3_MAX))
+    while amax > E4M3_MAX * 2.0 ** e:
+        e += 1
+    while amax <= E4M3_MAX * 2.0 ** (e - 1):
+        e -= 1
+    return 2.0 ** e
+
+
+def e4m3_quantize_block(x):
+    """(codes, scale) of one block [len, d]."""
+    sc = e4m3_block_scale(x)
+    return e4m3_encode(np.asarray(x, dtype=np.float64) / sc), sc
+
+
 @dataclass
 class PersistentRollout:
     """Oracle state of one head's rollout: P_t plus the tokens of the blocks it can still use.
@@ -301,6 +372,9 @@ class PersistentRollout:
     sch: Schedule
     d: int
     keep_history: bool = False
+    # stored blocks keep their K and V as E4M3 codes with a power-of-two scale per block
+    # (tok_k / tok_v then hold the decoded values; codes and scales in fp8_codes)
+    kv_fp8: bool = False
     chunk: int = 0
     P: list = field(default_factory=list)
     tok_k: dict = field(default_factory=dict)   # global block id -> [len, d]
@@ -308,6 +382,7 @@ class PersistentRollout:
     krep: dict = field(default_factory=dict)    # global block id -> [d] float64
     hist_k: list = field(default_factory=list)  # keep_history: per chunk [F*n, d]
     hist_v: list = field(default_factory=list)
+    fp8_codes: dict = field(default_factory=dict)  # kv_fp8: block -> (k codes, k scale, v codes, v scale)
 
     def _reps(self, ids):
         return np.array([self.krep[g] for g in ids]).reshape(len(ids), self.d)
@@ -457,6 +532,12 @@ class PersistentRollout:
             self.tok_k[base + b] = k_chunk[a0:b0]
             self.tok_v[base + b] = v_chunk[a0:b0]
             self.krep[base + b] = krep[b]
+            if self.kv_fp8:
+                kc, ks = e4m3_quantize_block(k_chunk[a0:b0])
+                vc, vs = e4m3_quantize_block(v_chunk[a0:b0])
+                self.fp8_codes[base + b] = (kc, ks, vc, vs)
+                self.tok_k[base + b] = e4m3_decode(kc) * ks
+                self.tok_v[base + b] = e4m3_decode(vc) * vs
         if self.keep_history:
             self.hist_k.append(k_chunk)
             self.hist_v.append(v_chunk)
@@ -464,6 +545,7 @@ class PersistentRollout:
         live = set(self.P) | set(s.window_blocks(self.chunk))
         for g in [g for g in self.tok_k if g not in live]:
             del self.tok_k[g], self.tok_v[g], self.krep[g]
+            self.fp8_codes.pop(g, None)
 
 
 # --------------------------------------------------------------------------------------

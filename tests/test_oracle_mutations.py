@@ -33,7 +33,8 @@ def _fails(calls):
 
 _orig = {n: getattr(po, n) for n in ("memory_scores", "top_ids", "mean_pool", "coarse_scores",
                                       "masked_attention_grad", "masked_attention",
-                                      "two_level_frames", "cag_budgets")}
+                                      "two_level_frames", "cag_budgets", "e4m3_encode",
+                                      "e4m3_block_scale")}
 
 
 def _memory_negated(P, sinks, sP, E, sE):
@@ -101,6 +102,33 @@ def _budget_floor(alphas, k_ref, i_ref):
                   for i, a in enumerate(alphas[1:], start=2)]
 
 
+def _encode_truncating(y):
+    # rounds the magnitude toward zero instead of to nearest
+    y = np.asarray(y, float)
+    codes = _orig["e4m3_encode"](y)
+    vals = po.e4m3_decode(codes)
+    over = np.abs(vals) > np.abs(y)
+    dn = np.where(over & ((codes & 0x7F) > 0), codes - 1, codes).astype(np.uint8)
+    return dn
+
+
+def _encode_ties_odd(y):
+    y = np.asarray(y, float)
+    codes = _orig["e4m3_encode"](y)
+    vals = po.e4m3_decode(codes)
+    out = codes.copy()
+    for i, (c, v, t) in enumerate(zip(codes.ravel(), vals.ravel(), y.ravel())):
+        for nb in (int(c) - 1, int(c) + 1):
+            if 0 <= nb < 256 and (nb & 0x7F) != 0x7F and (nb & 0x80) == (c & 0x80):
+                if abs(po.e4m3_decode(np.uint8(nb)) - t) == abs(v - t) and nb & 1:
+                    out.ravel()[i] = nb
+    return out
+
+
+def _scale_doubled(x):
+    return 2.0 * _orig["e4m3_block_scale"](x)
+
+
 def _dominance_calls():
     return [lambda s=s: pins.test_memory_update_respects_score_dominance(s) for s in range(30)] + \
         [pins.test_memory_update_strict_dominance_breaks_equal_maxima,
@@ -126,6 +154,12 @@ CASES = {
         pins.test_two_level_reduces_to_dense_and_forces_frames]),
     "budget truncated instead of rounded": ("cag_budgets", _budget_floor, lambda: [
         pins.test_cag_budget_reading_and_identity_closed_form]),
+    "fp8 encode truncating": ("e4m3_encode", _encode_truncating, lambda: [
+        pins.test_e4m3_encode_is_nearest_with_ties_to_even]),
+    "fp8 encode ties to odd": ("e4m3_encode", _encode_ties_odd, lambda: [
+        pins.test_e4m3_encode_is_nearest_with_ties_to_even]),
+    "fp8 block scale one step large": ("e4m3_block_scale", _scale_doubled, lambda: [
+        pins.test_e4m3_block_scale_is_the_smallest_power_of_two]),
 }
 
 

@@ -613,3 +613,60 @@ def test_cag_budget_reading_and_identity_closed_form():
     for a in (0.0, 0.3, 1.0):
         st = orc.cag_target_sparsity([a] * 8, s_base=1 - 32 / 600, beta=32 / 600, lq=lq, lk=lk)
         assert st == pytest.approx((1 - 32 / 600) - a * 32 / 600, abs=1e-12)
+
+
+# ----------------------------------------------------------------------------- FP8 cache
+def test_e4m3_decode_table_landmarks():
+    # OCP E4M3: bias 7, 3 mantissa bits, no infinities, S.1111.111 is NaN
+    v = orc.e4m3_decode(np.arange(256, dtype=np.uint8))
+    assert v[0x38] == 1.0 and v[0x7E] == 448.0 and v[0x08] == 2.0 ** -6
+    assert v[0x01] == 2.0 ** -9 and v[0x07] == 7 * 2.0 ** -9 and v[0x3C] == 1.5
+    assert np.isnan(v[0x7F]) and np.isnan(v[0xFF]) and v[0xB8] == -1.0
+    pos = v[:0x7F]
+    assert np.all(np.diff(pos) > 0)           # codes 0..126 increase strictly
+    assert np.array_equal(v[0x80:0xFF], -pos)
+
+
+def test_e4m3_encode_is_nearest_with_ties_to_even():
+    codes = np.arange(256, dtype=np.uint8)
+    vals = orc.e4m3_decode(codes)
+    fin = ~np.isnan(vals)
+    cv, vv = codes[fin], vals[fin]
+    rs = np.random.default_rng(3)
+    pos = np.sort(np.unique(vv[vv >= 0]))
+    mids = (pos[1:] + pos[:-1]) / 2                      # exact ties
+    ys = np.concatenate([rs.uniform(-448, 448, 4000), rs.uniform(-0.05, 0.05, 2000), mids,
+                         -mids, pos, -pos])
+    got = orc.e4m3_encode(ys)
+    for y, g in zip(ys, got):
+        d = np.abs(vv - y)
+        best = cv[d == d.min()]
+        if len(best) > 1:                                # a tie: the even mantissa wins
+            best = best[(best & 1) == 0]
+            best = best[np.signbit(orc.e4m3_decode(best)) == np.signbit(y)] if len(best) > 1 else best
+        assert g in best, (y, g, best)
+
+
+def test_e4m3_block_scale_is_the_smallest_power_of_two():
+    rs = np.random.default_rng(4)
+    for _ in range(200):
+        x = rs.standard_normal((64, 8)) * 10.0 ** rs.uniform(-4, 4)
+        sc = orc.e4m3_block_scale(x)
+        e = np.log2(sc)
+        assert e == np.round(e)
+        amax = np.abs(x).max()
+        assert amax <= 448 * sc and amax > 448 * sc / 2
+    assert orc.e4m3_block_scale(np.zeros((3, 4))) == 1.0
+    assert orc.e4m3_block_scale(np.full((1, 1), 448.0)) == 1.0
+    assert orc.e4m3_block_scale(np.full((1, 1), 448.5)) == 2.0
+
+
+def test_e4m3_dequantized_values_are_exact_in_bf16():
+    rs = np.random.default_rng(5)
+    x = synth.round_bf16(rs.standard_normal((64, 128)).astype(np.float32) * 3)
+    codes, sc = orc.e4m3_quantize_block(x)
+    deq = orc.e4m3_decode(codes) * sc
+    assert np.array_equal(synth.round_bf16(deq.astype(np.float32)).astype(np.float64), deq)
+    # relative error of the nearest code: at most half a mantissa step (2^-4)
+    big = np.abs(x) >= 2.0 ** -6 * sc
+    assert np.all(np.abs(deq - x)[big] <= 2.0 ** -4 * np.abs(x)[big] + 1e-30)
