@@ -122,9 +122,10 @@ class Ctx:
         return a.elapsed_time(b) / reps
 
 
-def shape_of(ops, wl):
+def shape_of(ops, wl, kv_format=0, route_mode=0):
     return ops.Shape(wl.heads, wl.head_dim, wl.frame_tokens, wl.chunk_frames, wl.window_frames,
-                     wl.capacity, wl.sinks, wl.topk, wl.scale)
+                     wl.capacity, wl.sinks, wl.topk, wl.scale, route_mode=route_mode,
+                     kv_format=kv_format)
 
 
 def gen_chunks(synth, wl, seed, idxs, passes=1):
@@ -162,17 +163,28 @@ def attended(wl, shape, bid, ln, sel):
     the routing the attention sees."""
     H, C, nb, n, W, F = wl.heads, wl.capacity, wl.nb, wl.frame_tokens, wl.window_frames, \
         wl.chunk_frames
-    occ = bid[:, :C] >= 0
-    pkeys = (ln[:, :C] * occ).sum(1)
+    whole = wl.sinks if shape.route_mode == 1 else C   # slots attended whole
+    occ = bid[:, :whole] >= 0
+    pkeys = (ln[:, :whole] * occ).sum(1)
     g = sel.astype(np.int64)
     valid = g >= 0
     gs = np.where(valid, g, 0)
     slot = C + ((gs // nb) % W) * nb + gs % nb
+    if shape.route_mode == 1:
+        # routed ids may be persistent blocks: their slot from the table
+        ring_ok = np.take_along_axis(bid, slot.reshape(H, -1), axis=1).reshape(sel.shape) == gs
+        for h in range(H):
+            where = {int(x): i for i, x in enumerate(bid[h, :C]) if x >= 0}
+            bad = valid[h] & ~ring_ok[h]
+            slot[h][bad] = [where.get(int(x), 0) for x in gs[h][bad]]
     rl = np.take_along_axis(ln.astype(np.int64), slot.reshape(H, -1), axis=1).reshape(sel.shape)
     keys = pkeys[:, None] + F * n + (rl * valid).sum(2)
     r = np.arange(shape.nq)
     qlen = np.minimum(64, n - 64 * (r % nb))
     slots_read = int(occ.sum()) + sum(len(set(gs[h][valid[h]].tolist())) for h in range(H))
+    if shape.route_mode == 1:
+        # routed persistent blocks are read in their slots (counted once per head)
+        slots_read = int(occ.sum()) + sum(len(set(slot[h][valid[h]].tolist())) for h in range(H))
     return int((keys * qlen[None, :]).sum()), slots_read
 
 
@@ -184,12 +196,12 @@ def attn_bytes(wl, shape, slots_read):
 
 
 # ------------------------------------------------------------------------------ headline
-def persistent_line(cx, name, steps, warmup, oracle_heads=()):
+def persistent_line(cx, name, steps, warmup, oracle_heads=(), kv_format=0, route_mode=0):
     """Bootstrap `name`'s rollout to its measured chunk, then time `steps` successive
     chunks.  Returns (result dict, layer, device chunks, oracle rollouts, host measured chunk)."""
     ops, runtime, synth = cx.ops, cx.runtime, cx.synth
     wl, seed = synth.WORKLOADS[name], synth.SEEDS[name]
-    shape = shape_of(ops, wl)
+    shape = shape_of(ops, wl, kv_format, route_mode)
     layer = runtime.PersistentLayer(shape)
     layer.reset()
     m = wl.measured_chunk
@@ -285,6 +297,7 @@ def persistent_line(cx, name, steps, warmup, oracle_heads=()):
         "attn_fwd_algorithmic_bytes_mean": int(np.mean(abytes)),
         "tflops_effective_step": round(sum(flop) / (ms_step * steps * 1e-3) / 1e12, 2),
         "ops_ms_alone": {k_: round(v_, 4) for k_, v_ in ops_ms.items()},
+        "cache_bytes": ops.pbsa_cache_bytes(shape),
     }
     restore(layer.cache, snap)
     cx.sync()
@@ -484,6 +497,14 @@ def main():
                 continue
             r, lay, ch, _, _, _ = persistent_line(cx, other, 10, 3)
             extras[other] = r
+            del lay, ch
+            cx.torch.cuda.empty_cache()
+        # FP8 cache (E4M3 codes, power-of-two scale per block) and routing over P and the
+        # window together, on the headline workload
+        for tag, kvf, rm in (("fp8_cache", 1, 0), ("union_routing", 0, 1)):
+            r, lay, ch, _, _, _ = persistent_line(cx, name, 10, 3, kv_format=kvf, route_mode=rm)
+            r["workload"] += f"; {tag.replace('_', ' ')}"
+            extras[f"{name}_{tag}"] = r
             del lay, ch
             cx.torch.cuda.empty_cache()
         extras["wan_20s_rollout"] = rollout_per_chunk(cx, "wan_20s")

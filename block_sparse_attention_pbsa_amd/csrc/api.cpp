@@ -63,6 +63,15 @@ pbsa_status check_dims(const pbsa_dims* d, int mode) {
     if (d->capacity < 0) return fail(PBSA_ERR_SHAPE, "capacity must be >= 0");
     if (d->route_mode != PBSA_ROUTE_WINDOW && d->route_mode != PBSA_ROUTE_UNION)
       return fail(PBSA_ERR_SHAPE, "route_mode must be PBSA_ROUTE_WINDOW or PBSA_ROUTE_UNION");
+    if (d->kv_format != PBSA_KV_BF16 && d->kv_format != PBSA_KV_FP8)
+      return fail(PBSA_ERR_SHAPE, "kv_format must be PBSA_KV_BF16 or PBSA_KV_FP8");
+    if (d->kv_format == PBSA_KV_FP8 && d->head_dim != 128)
+      return fail(PBSA_ERR_UNSUPPORTED, "the FP8 cache is built for head_dim 128");
+    if (d->kv_format == PBSA_KV_FP8 &&
+        int64_t{d->capacity} + d->topk + int64_t{d->chunk_frames} * pbsa::nb_of(*d) >
+            pbsa::kAttnListCap / 2)
+      return fail(PBSA_ERR_UNSUPPORTED, "FP8 cache: capacity + topk + chunk blocks must be <= %d",
+                  pbsa::kAttnListCap / 2);
     if (d->topk < 1) return fail(PBSA_ERR_SHAPE, "topk must be >= 1");
     if (d->topk > 1024) return fail(PBSA_ERR_UNSUPPORTED, "topk must be <= 1024");
     const int64_t slots = pbsa::slots_of(*d);
@@ -113,8 +122,13 @@ pbsa_status check_span(const pbsa_tensor& t, const char* name, int64_t tokens, i
   return PBSA_OK;
 }
 
-pbsa_status check_cache(const pbsa_cache* c) {
+pbsa_status check_cache(const pbsa_cache* c, const pbsa_dims* d) {
   if (!c) return fail(PBSA_ERR_NULL, "cache is NULL");
+  if (d && d->kv_format == PBSA_KV_FP8) {
+    if (!c->kv_scale) return fail(PBSA_ERR_NULL, "an FP8 cache needs kv_scale");
+    if (reinterpret_cast<uintptr_t>(c->kv_scale) % 8)
+      return fail(PBSA_ERR_ALIGN, "kv_scale must be 8-byte aligned");
+  }
   if (!c->k || !c->v || !c->rep || !c->block_id || !c->len)
     return fail(PBSA_ERR_NULL, "a cache buffer is NULL");
   if (reinterpret_cast<uintptr_t>(c->k) % 16 || reinterpret_cast<uintptr_t>(c->v) % 16 ||
@@ -167,8 +181,9 @@ int64_t pbsa_cache_slots(const pbsa_dims* dims) {
 
 size_t pbsa_cache_bytes(const pbsa_dims* dims) {
   if (check_dims(dims, 0) != PBSA_OK) return 0;
-  const size_t per_slot = 2 * static_cast<size_t>(dims->block) * dims->head_dim * 2 +
-                          static_cast<size_t>(dims->head_dim) * 4 + 2 * 4;
+  const bool fp8 = dims->kv_format == PBSA_KV_FP8;
+  const size_t per_slot = 2 * static_cast<size_t>(dims->block) * dims->head_dim * (fp8 ? 1 : 2) +
+                          static_cast<size_t>(dims->head_dim) * 4 + 2 * 4 + (fp8 ? 2 * 4 : 0);
   return static_cast<size_t>(dims->heads) * static_cast<size_t>(pbsa::slots_of(*dims)) * per_slot;
 }
 
@@ -314,7 +329,7 @@ size_t pbsa_workspace_bytes(const pbsa_dims* dims, int32_t op, int32_t arg, int3
 
 pbsa_status pbsa_cache_reset(const pbsa_dims* dims, pbsa_cache* cache, void* stream) {
   PBSA_TRY(check_dims(dims, 0));
-  PBSA_TRY(check_cache(cache));
+  PBSA_TRY(check_cache(cache, dims));
   cache->chunk_index = 0;
   return hip_status(pbsa::launch_cache_reset(*dims, *cache, stream_of(stream)), "cache_reset");
 }
@@ -335,7 +350,7 @@ pbsa_status pbsa_pool(const pbsa_dims* dims, pbsa_tensor x, int32_t frames, floa
 pbsa_status pbsa_score_topk(const pbsa_dims* dims, const float* q_rep, const pbsa_cache* cache,
                             float* scores, int32_t* sel, void* stream) {
   PBSA_TRY(check_dims(dims, 0));
-  PBSA_TRY(check_cache(cache));
+  PBSA_TRY(check_cache(cache, dims));
   if (!q_rep || !scores || !sel) return fail(PBSA_ERR_NULL, "q_rep, scores and sel are required");
   if (reinterpret_cast<uintptr_t>(q_rep) % 16)
     return fail(PBSA_ERR_ALIGN, "q_rep must be 16-byte aligned");
@@ -346,7 +361,7 @@ pbsa_status pbsa_score_topk(const pbsa_dims* dims, const float* q_rep, const pbs
 pbsa_status pbsa_route(const pbsa_dims* dims, pbsa_tensor q, const pbsa_cache* cache,
                        float* q_rep, float* scores, int32_t* sel, void* stream) {
   PBSA_TRY(check_dims(dims, 0));
-  PBSA_TRY(check_cache(cache));
+  PBSA_TRY(check_cache(cache, dims));
   PBSA_TRY(check_tok(q, "q", dims->head_dim));
   if (!scores || !sel) return fail(PBSA_ERR_NULL, "scores and sel are required");
   if (reinterpret_cast<uintptr_t>(q_rep) % 16)
@@ -360,7 +375,7 @@ pbsa_status pbsa_attn_fwd(const pbsa_dims* dims, pbsa_tensor q, const pbsa_cache
                           pbsa_tensor chunk_k, pbsa_tensor chunk_v, const int32_t* sel,
                           pbsa_tensor o, float* lse, void* stream) {
   PBSA_TRY(check_dims(dims, 0));
-  PBSA_TRY(check_cache(cache));
+  PBSA_TRY(check_cache(cache, dims));
   PBSA_TRY(check_tok(q, "q", dims->head_dim));
   PBSA_TRY(check_tok(chunk_k, "chunk_k", dims->head_dim));
   PBSA_TRY(check_tok(chunk_v, "chunk_v", dims->head_dim));
@@ -374,6 +389,11 @@ pbsa_status pbsa_attn_fwd(const pbsa_dims* dims, pbsa_tensor q, const pbsa_cache
   PBSA_TRY(check_span(chunk_k, "chunk_k", ctok, dims->head_dim));
   PBSA_TRY(check_span(chunk_v, "chunk_v", ctok, dims->head_dim));
   if (!sel || !lse) return fail(PBSA_ERR_NULL, "sel and lse are required");
+  if (dims->kv_format == PBSA_KV_FP8)
+    return hip_status(pbsa::launch_attn_fwd_fp8(*dims, pbsa::tok_in(q), *cache,
+                                                pbsa::tok_in(chunk_k), pbsa::tok_in(chunk_v),
+                                                sel, pbsa::tok_out(o), lse, stream_of(stream)),
+                      "attn_fwd (fp8 cache)");
   return hip_status(pbsa::launch_attn_fwd_persistent(*dims, pbsa::tok_in(q), *cache,
                                                      pbsa::tok_in(chunk_k),
                                                      pbsa::tok_in(chunk_v), sel,
@@ -400,7 +420,7 @@ pbsa_status check_memory_ws(const pbsa_dims* dims, const pbsa_cache* cache, void
 pbsa_status check_chunk_args(const pbsa_dims* dims, const pbsa_chunk_args* a,
                              const pbsa_cache* cache) {
   PBSA_TRY(check_dims(dims, 0));
-  PBSA_TRY(check_cache(cache));
+  PBSA_TRY(check_cache(cache, dims));
   if (!a) return fail(PBSA_ERR_NULL, "args is NULL");
   if (a->passes < 1 || a->passes > PBSA_MAX_PASSES)
     return fail(PBSA_ERR_SHAPE, "passes must be in [1, %d]", PBSA_MAX_PASSES);
@@ -434,7 +454,7 @@ pbsa_status pbsa_memory_select(const pbsa_dims* dims, const float* scores,
                                const pbsa_cache* cache, void* workspace, size_t workspace_bytes,
                                void* stream) {
   PBSA_TRY(check_dims(dims, 0));
-  PBSA_TRY(check_cache(cache));
+  PBSA_TRY(check_cache(cache, dims));
   if (!scores) return fail(PBSA_ERR_NULL, "scores is required");
   PBSA_TRY(check_memory_ws(dims, cache, workspace, workspace_bytes, "memory_select"));
   return hip_status(pbsa::launch_memory_select(*dims, scores, *cache, workspace, true,
@@ -446,7 +466,7 @@ pbsa_status pbsa_memory_apply(const pbsa_dims* dims, pbsa_cache* cache, pbsa_ten
                               pbsa_tensor chunk_v, const float* chunk_rep, void* workspace,
                               size_t workspace_bytes, void* stream) {
   PBSA_TRY(check_dims(dims, 0));
-  PBSA_TRY(check_cache(cache));
+  PBSA_TRY(check_cache(cache, dims));
   PBSA_TRY(check_tok(chunk_k, "chunk_k", dims->head_dim));
   PBSA_TRY(check_tok(chunk_v, "chunk_v", dims->head_dim));
   PBSA_TRY(check_memory_ws(dims, cache, workspace, workspace_bytes, "memory_apply"));
@@ -462,7 +482,7 @@ pbsa_status pbsa_memory_update(const pbsa_dims* dims, const float* scores, pbsa_
                                pbsa_tensor chunk_k, pbsa_tensor chunk_v, const float* chunk_rep,
                                void* workspace, size_t workspace_bytes, void* stream) {
   PBSA_TRY(check_dims(dims, 0));
-  PBSA_TRY(check_cache(cache));
+  PBSA_TRY(check_cache(cache, dims));
   PBSA_TRY(check_tok(chunk_k, "chunk_k", dims->head_dim));
   PBSA_TRY(check_tok(chunk_v, "chunk_v", dims->head_dim));
   if (!scores) return fail(PBSA_ERR_NULL, "scores is required");
@@ -480,7 +500,7 @@ pbsa_status pbsa_memory_update_noalloc(const pbsa_dims* dims, const float* score
                                        pbsa_tensor chunk_v, const float* chunk_rep,
                                        void* stream) {
   PBSA_TRY(check_dims(dims, 0));
-  PBSA_TRY(check_cache(cache));
+  PBSA_TRY(check_cache(cache, dims));
   PBSA_TRY(check_tok(chunk_k, "chunk_k", dims->head_dim));
   PBSA_TRY(check_tok(chunk_v, "chunk_v", dims->head_dim));
   if (!scores) return fail(PBSA_ERR_NULL, "scores is required");
@@ -598,7 +618,9 @@ pbsa_status pbsa_attn_bwd_persistent(const pbsa_dims* dims, pbsa_tensor q,
                                      void* dv_cache, void* workspace, size_t workspace_bytes,
                                      void* stream) {
   PBSA_TRY(check_dims(dims, 0));
-  PBSA_TRY(check_cache(cache));
+  PBSA_TRY(check_cache(cache, dims));
+  if (dims->kv_format != PBSA_KV_BF16)
+    return fail(PBSA_ERR_UNSUPPORTED, "attn_bwd_persistent takes a bf16 cache");
   const char* names[] = {"q", "chunk_k", "chunk_v", "o", "dout", "dq", "dk", "dv"};
   const pbsa_tensor* ts[] = {&q, &chunk_k, &chunk_v, &o, &dout, &dq, &dk, &dv};
   const int64_t ctok = int64_t{dims->chunk_frames} * dims->frame_tokens;
@@ -630,6 +652,16 @@ pbsa_status pbsa_attn_bwd_persistent(const pbsa_dims* dims, pbsa_tensor q,
 
 // ---- measurement probes (pbsa_probe.h)
 
+pbsa_status pbsa_probe_fp8_decode(const uint8_t* codes, const float* scales, uint16_t* out,
+                                  int32_t n, void* stream) {
+  if (!codes || !scales || !out) return fail(PBSA_ERR_NULL, "codes, scales and out are required");
+  if (n < 0 || n % 16) return fail(PBSA_ERR_SHAPE, "n must be a non-negative multiple of 16");
+  if (reinterpret_cast<uintptr_t>(codes) % 16 || reinterpret_cast<uintptr_t>(out) % 16)
+    return fail(PBSA_ERR_ALIGN, "codes and out must be 16-byte aligned");
+  return hip_status(pbsa::launch_probe_fp8_decode(codes, scales, out, n, stream_of(stream)),
+                    "probe_fp8_decode");
+}
+
 int64_t pbsa_probe_mfma_flop(int64_t iters) {
   return iters < 1 ? 0 : iters * 512 * 4 * 4 * (2 * 32 * 32 * 16);
 }
@@ -644,7 +676,9 @@ pbsa_status pbsa_probe_gather(const pbsa_dims* dims, pbsa_tensor q, const pbsa_c
                               pbsa_tensor chunk_k, pbsa_tensor chunk_v, const int32_t* sel,
                               void* stream) {
   PBSA_TRY(check_dims(dims, 0));
-  PBSA_TRY(check_cache(cache));
+  PBSA_TRY(check_cache(cache, dims));
+  if (dims->kv_format != PBSA_KV_BF16)
+    return fail(PBSA_ERR_UNSUPPORTED, "probe_gather takes a bf16 cache");
   PBSA_TRY(check_tok(q, "q", dims->head_dim));
   PBSA_TRY(check_tok(chunk_k, "chunk_k", dims->head_dim));
   PBSA_TRY(check_tok(chunk_v, "chunk_v", dims->head_dim));

@@ -105,25 +105,6 @@ __device__ __forceinline__ void dma_piece(int i, __amdgpu_buffer_rsrc_t rs, uint
   }
 }
 
-// The transposing read of rd_rows_tr split into this lane's two element offsets for k-step
-// 0 (lo: rows 0..3 of its group, hi: rows 8..11) and the read itself; k-step t4 adds 16 t4
-// rows to both (swz(r) depends on r % 16 only).
-template <int D>
-__device__ __forceinline__ void tr_offsets(int dt, int l, int& lo, int& hi) {
-  const int g = l >> 4, i = l & 15;
-  const int ch = 32 * dt + 16 * (g & 1) + 4 * (i & 3);
-  const int row = 4 * (g >> 1) + (i >> 2);
-  lo = Lds<D>::chunk(row, ch >> 3) + (ch & 4);
-  hi = Lds<D>::chunk(row + 8, ch >> 3) + (ch & 4);
-}
-__device__ __forceinline__ u32x4 rd_tr(const uint16_t* lds, int lo, int hi) {
-  lds_u16* p = (lds_u16*)(lds);
-  const s16x4_ a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + lo));
-  const s16x4_ b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + hi));
-  const u32x2 x = __builtin_bit_cast(u32x2, a), y = __builtin_bit_cast(u32x2, b);
-  return u32x4{x[0], x[1], y[0], y[1]};
-}
-
 // Element t of an fp32 row of n valid values from p (p wave-uniform); 0 past n.
 __device__ __forceinline__ float load_row_f32(const float* p, int n, int t) {
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
@@ -338,8 +319,12 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
     };
     // step st: its tiles are in `cur`; the next step's go into `nxt`
     auto run = [&](int st, const uint16_t* cur, uint16_t* nxt) {
-      // (the barrier waits for this wave's gathers too) step st's tiles have landed, and
-      // every wave is done with the set step st - 1 read
+      // Every wave waits for its own gathers into `cur` (vmcnt(0)) before the barrier, so
+      // that after it every tile of step st has landed; the barrier's own release covers
+      // LDS instructions only, and the compiler, left to itself, may let the last gathers
+      // of a step still be in flight at the barrier.  After the barrier every wave is also
+      // done with the set step st - 1 read.
+      __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0); expcnt and lgkmcnt not waited
       __syncthreads();
       if (st + 1 < nsteps) gather(st + 1, nxt);
       Half kx, vx, ky, vy;

@@ -116,6 +116,44 @@ __device__ __forceinline__ u32x4 pack_step(const f32x16* acc, int t4) {
 // Row index (0..31 within a 32-row accumulator tile) of accumulator register r in half h2.
 __device__ __forceinline__ int acc_row(int r, int h2) { return 8 * (r >> 2) + 4 * h2 + (r & 3); }
 
+// The transposing read of rd_rows_tr split into this lane's two element offsets for k-step
+// 0 (lo: rows 0..3 of its group, hi: rows 8..11) and the read itself; k-step t4 adds 16 t4
+// rows to both (swz(r) depends on r % 16 only).
+template <int D>
+__device__ __forceinline__ void tr_offsets(int dt, int l, int& lo, int& hi) {
+  const int g = l >> 4, i = l & 15;
+  const int ch = 32 * dt + 16 * (g & 1) + 4 * (i & 3);
+  const int row = 4 * (g >> 1) + (i >> 2);
+  lo = Lds<D>::chunk(row, ch >> 3) + (ch & 4);
+  hi = Lds<D>::chunk(row + 8, ch >> 3) + (ch & 4);
+}
+__device__ __forceinline__ u32x4 rd_tr(const uint16_t* lds, int lo, int hi) {
+  lds_u16* p = (lds_u16*)(lds);
+  const s16x4_ a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + lo));
+  const s16x4_ b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + hi));
+  const u32x2 x = __builtin_bit_cast(u32x2, a), y = __builtin_bit_cast(u32x2, b);
+  return u32x4{x[0], x[1], y[0], y[1]};
+}
+
+// Sixteen OCP E4M3 codes (bytes of raw, lowest first) times a power-of-two scale, as
+// sixteen bf16 values (exact: four significant bits times a power of two) in two 8-value
+// chunks, with gfx950's scaled conversion (two codes per instruction).
+__device__ __forceinline__ void decode_e4m3x16(u32x4 raw, float scale, u32x4& lo, u32x4& hi) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[i], scale, false);
+    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[i], scale, true);
+    const uint32_t wa = __builtin_bit_cast(uint32_t, a), wb = __builtin_bit_cast(uint32_t, b);
+    if (i < 2) {
+      lo[2 * i] = wa;
+      lo[2 * i + 1] = wb;
+    } else {
+      hi[2 * (i - 2)] = wa;
+      hi[2 * (i - 2) + 1] = wb;
+    }
+  }
+}
+
 // Register-resident operand: D channels of row `row` (< len) in k-step chunks.
 template <int D>
 __device__ __forceinline__ void load_row_operand(u32x4* dst, const uint16_t* p, int64_t stride,

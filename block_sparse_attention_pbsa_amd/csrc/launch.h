@@ -41,7 +41,13 @@ hipError_t launch_attn_fwd_persistent(const pbsa_dims& d, TokIn q, const pbsa_ca
                                       TokIn ck, TokIn cv, const int32_t* sel, TokOut o,
                                       float* lse, hipStream_t s, bool gather_only = false);
 
+hipError_t launch_attn_fwd_fp8(const pbsa_dims& d, TokIn q, const pbsa_cache& c, TokIn ck,
+                               TokIn cv, const int32_t* sel, TokOut o, float* lse,
+                               hipStream_t s);
+
 hipError_t launch_probe_mfma(int64_t iters, float* out, hipStream_t s);
+hipError_t launch_probe_fp8_decode(const uint8_t* codes, const float* scales, uint16_t* out,
+                                   int n, hipStream_t s);
 
 hipError_t launch_attn_fwd_2lvl(const pbsa_dims& d, int chunks, TokIn q, TokIn k, TokIn v,
                                 const int32_t* sel, const int32_t* nsel, int max_sel, TokOut o,

@@ -44,7 +44,42 @@ struct MemArgs {
   // for successive chunks.
   int64_t* chunk_dev;
   int64_t* ws_chunk;    // workspace: the chunk index the select used
+  float* kv_scale;      // FP8 cache: [H][slots][2] K and V scale of each slot
 };
+
+// OCP E4M3 code of y (|y| <= 448, finite) nearest to it, ties to the even mantissa: the
+// subnormal codes are the multiples of 2^-9 below 2^-6 (rounded by v_rndne), the normal
+// ones keep 3 mantissa bits of y's fp32 mantissa, rounded to nearest even.
+__device__ __forceinline__ uint32_t e4m3_code(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  uint32_t code;
+  if (a < 0x3c800000u) {  // |y| < 2^-6
+    code = static_cast<uint32_t>(__builtin_rintf(__uint_as_float(a) * 512.f));
+  } else {
+    int ee = static_cast<int>(a >> 23) - 127 + 7;  // biased E4M3 exponent, >= 1
+    uint32_t m = (a >> 20) & 7u;
+    const uint32_t rem = a & 0xfffffu;
+    if (rem > 0x80000u || (rem == 0x80000u && (m & 1u))) ++m;
+    if (m == 8u) {
+      m = 0;
+      ++ee;
+    }
+    code = (static_cast<uint32_t>(ee) << 3) | m;
+  }
+  return sign | code;
+}
+
+// The smallest power of two 2^e with amax <= 448 * 2^e (1 for amax = 0): with
+// amax = f * 2^E, f in [0.5, 1), and 448 = 0.875 * 2^9, e = E - 9 when f <= 0.875, else
+// E - 8.
+__device__ __forceinline__ int e4m3_scale_exp(float amax) {
+  if (!(amax > 0.f)) return 0;
+  int E;
+  const float f = frexpf(amax, &E);
+  return f <= 0.875f ? E - 9 : E - 8;
+}
 
 // The chunk index of this update, as the select sees it.
 __device__ __forceinline__ int64_t select_chunk(const MemArgs& a) {
@@ -352,6 +387,139 @@ __global__ void __launch_bounds__(256) memory_copy_kernel(MemArgs a, TokIn xk, T
   }
 }
 
+// The copy pass for an FP8 cache (same grid and duties as memory_copy_kernel): promoted
+// blocks move as codes with their scales; the chunk's blocks are quantized on the way in:
+// per block and tensor the power-of-two scale of its largest |value|, then each value's
+// nearest E4M3 code (rows past the block length stay code 0).  The representative is the
+// mean of the chunk's bf16 keys, as in the bf16 cache.
+template <int D>
+__global__ void __launch_bounds__(256) memory_copy_fp8_kernel(MemArgs a, TokIn xk, TokIn xv,
+                                                              const float* __restrict__ chunk_rep) {
+  const int b = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+  const int l = t & 63, w = t >> 6;
+  const int64_t chunk = copy_chunk(a);
+  const int64_t hF = chunk * a.F;
+  const int fl = b / a.nb, j = b - fl * a.nb;
+  const int64_t f = hF + fl;
+  const int ring = a.C + static_cast<int>(f % a.W) * a.nb + j;
+  const int g = static_cast<int>(f * a.nb + j);
+  const int len = block_len(j, a.n);
+  const int64_t hs = static_cast<int64_t>(h) * a.slots;
+  uint8_t* ck = reinterpret_cast<uint8_t*>(a.ck) + hs * kBlock * D;
+  uint8_t* cv = reinterpret_cast<uint8_t*>(a.cv) + hs * kBlock * D;
+  float* rep = a.rep + hs * D;
+  float* ksc = a.kv_scale + hs * 2;
+  constexpr int CH = D / 8;               // 8-value chunks per row
+  constexpr int PER = kBlock * CH / 256;  // chunks per thread
+  constexpr int CB = kBlock * D / 16;     // 16-byte pieces of a slot's codes
+  const int dst = a.copy_dst[static_cast<int64_t>(h) * a.F * a.nb + b];
+  if (dst >= 0 && dst < a.C) {
+    for (int q = t; q < CB; q += 256) {
+      const int64_t so = static_cast<int64_t>(ring) * kBlock * D + 16 * q;
+      const int64_t dof = static_cast<int64_t>(dst) * kBlock * D + 16 * q;
+      *reinterpret_cast<u32x4*>(ck + dof) = *reinterpret_cast<const u32x4*>(ck + so);
+      *reinterpret_cast<u32x4*>(cv + dof) = *reinterpret_cast<const u32x4*>(cv + so);
+    }
+    for (int c = t; c < D; c += 256)
+      rep[static_cast<int64_t>(dst) * D + c] = rep[static_cast<int64_t>(ring) * D + c];
+    if (t < 2) ksc[2 * dst + t] = ksc[2 * ring + t];
+  }
+  __syncthreads();
+  const bool sink = chunk == 0 && g < a.S;
+  const int target = sink ? g : ring;
+  const int64_t tok0 = static_cast<int64_t>(fl) * a.n + static_cast<int64_t>(kBlock) * j;
+  u32x4 kv[PER], vv[PER];
+  float ksum[8], kmax = 0.f, vmax = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ksum[e] = 0.f;
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const int q = t + 256 * p;
+    const int row = q / CH, cc = q % CH;
+    kv[p] = u32x4{0, 0, 0, 0};
+    vv[p] = u32x4{0, 0, 0, 0};
+    if (row < len) {
+      kv[p] = *reinterpret_cast<const u32x4*>(xk.p + h * xk.hs + (tok0 + row) * xk.ts + 8 * cc);
+      vv[p] = *reinterpret_cast<const u32x4*>(xv.p + h * xv.hs + (tok0 + row) * xv.ts + 8 * cc);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float k0 = __uint_as_float(kv[p][e] << 16), k1 = __uint_as_float(kv[p][e] & 0xffff0000u);
+      const float v0 = __uint_as_float(vv[p][e] << 16), v1 = __uint_as_float(vv[p][e] & 0xffff0000u);
+      ksum[2 * e] += k0;
+      ksum[2 * e + 1] += k1;
+      kmax = fmaxf(kmax, fmaxf(fabsf(k0), fabsf(k1)));
+      vmax = fmaxf(vmax, fmaxf(fabsf(v0), fabsf(v1)));
+    }
+  }
+  // block maxima: the wave, then the four waves through LDS
+  __shared__ float wmax[2][4];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    kmax = fmaxf(kmax, __shfl_xor(kmax, o, 64));
+    vmax = fmaxf(vmax, __shfl_xor(vmax, o, 64));
+  }
+  if (l == 0) {
+    wmax[0][w] = kmax;
+    wmax[1][w] = vmax;
+  }
+  __syncthreads();
+  kmax = fmaxf(fmaxf(wmax[0][0], wmax[0][1]), fmaxf(wmax[0][2], wmax[0][3]));
+  vmax = fmaxf(fmaxf(wmax[1][0], wmax[1][1]), fmaxf(wmax[1][2], wmax[1][3]));
+  const int ek = e4m3_scale_exp(kmax), ev = e4m3_scale_exp(vmax);
+  const float ik = ldexpf(1.f, -ek), iv = ldexpf(1.f, -ev);  // exact reciprocals
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const int q = t + 256 * p;
+    const int row = q / CH, cc = q % CH;
+    u32x2 kc = {0, 0}, vc = {0, 0};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t k2 = e4m3_code(__uint_as_float(kv[p][e] << 16) * ik) |
+                          (e4m3_code(__uint_as_float(kv[p][e] & 0xffff0000u) * ik) << 8);
+      const uint32_t v2 = e4m3_code(__uint_as_float(vv[p][e] << 16) * iv) |
+                          (e4m3_code(__uint_as_float(vv[p][e] & 0xffff0000u) * iv) << 8);
+      kc[e >> 1] |= k2 << (16 * (e & 1));
+      vc[e >> 1] |= v2 << (16 * (e & 1));
+    }
+    const int64_t o = static_cast<int64_t>(target) * kBlock * D + static_cast<int64_t>(row) * D + 8 * cc;
+    *reinterpret_cast<u32x2*>(ck + o) = kc;
+    *reinterpret_cast<u32x2*>(cv + o) = vc;
+  }
+  if (t == 0) {
+    ksc[2 * target] = ldexpf(1.f, ek);
+    ksc[2 * target + 1] = ldexpf(1.f, ev);
+  }
+  if (chunk_rep) {
+    const float* cr = chunk_rep + (static_cast<int64_t>(h) * a.nq + b) * D;
+    for (int c = t; c < D; c += 256) rep[static_cast<int64_t>(target) * D + c] = cr[c];
+  } else {
+    __shared__ float wsum[4][D];
+#pragma unroll
+    for (int o = CH; o < 64; o <<= 1)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ksum[e] += __shfl_xor(ksum[e], o, 64);
+    if (l < CH)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) wsum[w][8 * l + e] = ksum[e];
+    __syncthreads();
+    const float inv = 1.f / static_cast<float>(len);
+    for (int c = t; c < D; c += 256)
+      rep[static_cast<int64_t>(target) * D + c] =
+          ((wsum[0][c] + wsum[1][c]) + (wsum[2][c] + wsum[3][c])) * inv;
+  }
+  if (b == 0)
+    for (int s = t; s < a.C; s += 256) {
+      a.bid[hs + s] = a.pbid[static_cast<int64_t>(h) * a.C + s];
+      a.blen[hs + s] = a.plen[static_cast<int64_t>(h) * a.C + s];
+    }
+  if (t == 0) {
+    a.bid[hs + ring] = sink ? -1 : g;
+    a.blen[hs + ring] = sink ? 0 : len;
+    if (a.chunk_dev && b == 0 && h == 0) *a.chunk_dev = chunk + 1;
+  }
+}
+
 namespace {
 
 // Workspace: copy list [H][F*nb], then the new persistent table [H][C] (ids, lengths),
@@ -375,6 +543,7 @@ MemArgs mem_args(const pbsa_dims& d, const float* scores, const pbsa_cache& c, v
   a.plen = reinterpret_cast<int32_t*>(p + ncopy + ntab);
   a.ws_chunk = reinterpret_cast<int64_t*>(p + ncopy + 2 * ntab);
   a.chunk_dev = c.chunk_index_dev;
+  a.kv_scale = c.kv_scale;
   a.slots = static_cast<int>(slots_of(d));
   a.C = d.capacity;
   a.S = d.sinks;
@@ -423,6 +592,10 @@ hipError_t launch_memory_apply(const pbsa_dims& d, const pbsa_cache& c, TokIn ck
                                const float* chunk_rep, void* ws, hipStream_t s) {
   const MemArgs a = mem_args(d, nullptr, c, ws);
   dim3 grid(d.chunk_frames * a.nb, d.heads);
+  if (d.kv_format == PBSA_KV_FP8) {  // head_dim 128 (checked at the boundary)
+    hipLaunchKernelGGL(memory_copy_fp8_kernel<128>, grid, dim3(256), 0, s, a, ck, cv, chunk_rep);
+    return hipGetLastError();
+  }
   if (d.head_dim == 128)
     hipLaunchKernelGGL(memory_copy_kernel<128>, grid, dim3(256), 0, s, a, ck, cv, chunk_rep);
   else

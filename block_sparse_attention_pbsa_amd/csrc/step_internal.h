@@ -21,7 +21,7 @@ pbsa_status hip_status(hipError_t e, const char* where);
 pbsa_status check_dims(const pbsa_dims* d, int mode);
 pbsa_status check_tok(const pbsa_tensor& t, const char* name, int head_dim);
 pbsa_status check_span(const pbsa_tensor& t, const char* name, int64_t tokens, int head_dim);
-pbsa_status check_cache(const pbsa_cache* c);
+pbsa_status check_cache(const pbsa_cache* c, const pbsa_dims* d);
 pbsa_status check_memory_ws(const pbsa_dims* dims, const pbsa_cache* cache, void* workspace,
                             size_t workspace_bytes, const char* name);
 // Everything pbsa_chunk_step reads: dims, cache, every pass's tensors, the routing and

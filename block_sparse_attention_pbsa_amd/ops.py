@@ -26,6 +26,8 @@ PBSA_OP_ATTN_BWD = 2
 PBSA_OP_ATTN_BWD_PERSISTENT = 3
 PBSA_ROUTE_WINDOW = 0
 PBSA_ROUTE_UNION = 1
+PBSA_KV_BF16 = 0
+PBSA_KV_FP8 = 1
 
 
 class PbsaError(RuntimeError):
@@ -40,7 +42,7 @@ class Dims(ctypes.Structure):
                 ("chunk_frames", ctypes.c_int32), ("window_frames", ctypes.c_int32),
                 ("capacity", ctypes.c_int32), ("sinks", ctypes.c_int32),
                 ("topk", ctypes.c_int32), ("scale", ctypes.c_float),
-                ("route_mode", ctypes.c_int32)]
+                ("route_mode", ctypes.c_int32), ("kv_format", ctypes.c_int32)]
 
 
 class Tensor(ctypes.Structure):
@@ -51,7 +53,8 @@ class Tensor(ctypes.Structure):
 class CacheC(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("rep", ctypes.c_void_p),
                 ("block_id", ctypes.c_void_p), ("len", ctypes.c_void_p),
-                ("chunk_index", ctypes.c_int64), ("chunk_index_dev", ctypes.c_void_p)]
+                ("chunk_index", ctypes.c_int64), ("chunk_index_dev", ctypes.c_void_p),
+                ("kv_scale", ctypes.c_void_p)]
 
 
 MAX_PASSES = 8
@@ -113,6 +116,7 @@ _SIGS = {
     # measurement probes (pbsa_probe.h)
     "pbsa_probe_mfma": ([ctypes.c_int64, _P, _P], ctypes.c_int),
     "pbsa_probe_mfma_flop": ([ctypes.c_int64], ctypes.c_int64),
+    "pbsa_probe_fp8_decode": ([_P, _P, _P, _I32, _P], ctypes.c_int),
     "pbsa_probe_gather": ([ctypes.POINTER(Dims), Tensor, ctypes.POINTER(CacheC), Tensor, Tensor,
                            _P, _P], ctypes.c_int),
 }
@@ -190,6 +194,7 @@ class Shape:
     scale: float | None = None
     block: int = 64
     route_mode: int = 0    # PBSA_ROUTE_WINDOW (0) or PBSA_ROUTE_UNION (1)
+    kv_format: int = 0     # PBSA_KV_BF16 (0) or PBSA_KV_FP8 (1)
 
     @property
     def nb(self) -> int:
@@ -210,7 +215,8 @@ class Shape:
     def c(self) -> Dims:
         s = self.scale if self.scale is not None else self.head_dim ** -0.5
         return Dims(self.heads, self.head_dim, self.block, self.frame_tokens, self.chunk_frames,
-                    self.window_frames, self.capacity, self.sinks, self.topk, s, self.route_mode)
+                    self.window_frames, self.capacity, self.sinks, self.topk, s, self.route_mode,
+                    self.kv_format)
 
 
 class Cache:
@@ -219,8 +225,12 @@ class Cache:
     def __init__(self, shape: Shape, device="cuda", device_counter: bool = False):
         H, S, d = shape.heads, shape.slots, shape.head_dim
         self.shape = shape
-        self.k = torch.zeros(H, S, shape.block, d, dtype=torch.bfloat16, device=device)
+        kv_dtype = torch.uint8 if shape.kv_format == PBSA_KV_FP8 else torch.bfloat16
+        self.k = torch.zeros(H, S, shape.block, d, dtype=kv_dtype, device=device)
         self.v = torch.zeros_like(self.k)
+        # FP8 cache: K and V scale of every slot
+        self.kv_scale = torch.ones(H, S, 2, dtype=torch.float32, device=device) \
+            if shape.kv_format == PBSA_KV_FP8 else None
         self.rep = torch.zeros(H, S, d, dtype=torch.float32, device=device)
         self.block_id = torch.full((H, S), -1, dtype=torch.int32, device=device)
         self.len = torch.zeros(H, S, dtype=torch.int32, device=device)
@@ -232,11 +242,14 @@ class Cache:
     def c(self) -> CacheC:
         return CacheC(self.k.data_ptr(), self.v.data_ptr(), self.rep.data_ptr(),
                       self.block_id.data_ptr(), self.len.data_ptr(), self.chunk_index,
-                      self.chunk_dev.data_ptr() if self.chunk_dev is not None else None)
+                      self.chunk_dev.data_ptr() if self.chunk_dev is not None else None,
+                      self.kv_scale.data_ptr() if self.kv_scale is not None else None)
 
     def nbytes(self) -> int:
-        return sum(t.numel() * t.element_size() for t in
-                   (self.k, self.v, self.rep, self.block_id, self.len))
+        ts = [self.k, self.v, self.rep, self.block_id, self.len]
+        if self.kv_scale is not None:
+            ts.append(self.kv_scale)
+        return sum(t.numel() * t.element_size() for t in ts)
 
 
 # ------------------------------------------------------------------------------ calls
@@ -548,3 +561,16 @@ def pbsa_check_selection_2lvl(shape: Shape, chunks: int, sel, nsel):
     ns = _np_i32(nsel, "nsel", (shape.heads, chunks * shape.nq))
     _check("pbsa_check_selection_2lvl", lib().pbsa_check_selection_2lvl(
         ctypes.byref(shape.c()), chunks, sl.ctypes.data, ns.ctypes.data, sl.shape[2]))
+
+
+def pbsa_probe_fp8_decode(codes, scales, out):
+    """The FP8 attention's decode (pbsa_probe.h): codes uint8 [n], scales fp32 [n / 16],
+    out int16 [n] (bf16 bits)."""
+    _dev(codes, "codes", torch.uint8)
+    _dev(scales, "scales", torch.float32)
+    _dev(out, "out", torch.int16)
+    n = codes.numel()
+    if scales.numel() * 16 != n or out.numel() != n:
+        raise ValueError("need n codes, n / 16 scales and n outputs")
+    _check("pbsa_probe_fp8_decode", lib().pbsa_probe_fp8_decode(_ptr(codes), _ptr(scales),
+                                                                _ptr(out), n, _stream()))

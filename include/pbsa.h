@@ -76,7 +76,19 @@ typedef struct pbsa_dims {
   int32_t topk;          /* window blocks routed per query block, K >= 1 */
   float scale;           /* softmax scale, usually 1/sqrt(d) */
   int32_t route_mode;    /* persistent mode: PBSA_ROUTE_WINDOW (0) or PBSA_ROUTE_UNION (1) */
+  int32_t kv_format;     /* persistent cache K/V: PBSA_KV_BF16 (0) or PBSA_KV_FP8 (1) */
 } pbsa_dims;
+
+/* How the persistent cache keeps K and V (Light Forcing, "Key findings": FP8 deployment):
+ *   PBSA_KV_BF16: bf16 values.
+ *   PBSA_KV_FP8:  OCP float8 E4M3 codes (1 sign, 4 exponent bits with bias 7, 3 mantissa
+ *                 bits; largest value 448), one byte per value, with one power-of-two scale
+ *                 per slot and tensor, the smallest 2^e with max|x| <= 448 * 2^e over the
+ *                 block's tokens (1 for an all-zero block); codes are the nearest to
+ *                 x / 2^e, ties to the even mantissa.  The value a code stands for is
+ *                 code * scale.  head_dim 128 only; the chunk's own K/V stay bf16.
+ *                 pbsa_attn_bwd_persistent and pbsa_probe_gather do not take this format. */
+enum { PBSA_KV_BF16 = 0, PBSA_KV_FP8 = 1 };
 
 /* What the persistent-mode top-K chooses from (Sparse Forcing 2.C; north_star's "score
  * against P and L, keep the top-k"):
@@ -101,7 +113,7 @@ typedef struct pbsa_tensor {
  * holds window block j of history frame f.  A slot keeps its block's tokens row-major,
  * rows past len zero.  The struct itself is host memory; its pointers are device memory
  * of these sizes:
- *   k, v      bf16 [heads][slots][block][head_dim]
+ *   k, v      bf16 [heads][slots][block][head_dim] (PBSA_KV_FP8: uint8 E4M3 codes)
  *   rep       fp32 [heads][slots][head_dim]   the block's mean key (its representative)
  *   block_id  int32 [heads][slots]            global block id, -1 = empty
  *   len       int32 [heads][slots]            valid tokens of the block
@@ -111,7 +123,9 @@ typedef struct pbsa_tensor {
  * the device, so that an update captured once in a graph (pbsa_chunk_graph_create) is
  * right for every later chunk it is replayed for; the calls still advance chunk_index,
  * and the caller keeps the two equal (a graph replay advances only the device copy;
- * pbsa_chunk_graph_launch advances chunk_index as well).  pbsa_cache_reset zeroes both. */
+ * pbsa_chunk_graph_launch advances chunk_index as well).  pbsa_cache_reset zeroes both.
+ * kv_scale (PBSA_KV_FP8 only, else unused): fp32 [heads][slots][2], the K and V scale of
+ * each slot. */
 typedef struct pbsa_cache {
   void* k;
   void* v;
@@ -120,6 +134,7 @@ typedef struct pbsa_cache {
   int32_t* len;
   int64_t chunk_index;
   int64_t* chunk_index_dev;
+  float* kv_scale;
 } pbsa_cache;
 
 /* ---- helpers ---------------------------------------------------------------------- */
@@ -135,8 +150,8 @@ pbsa_status pbsa_check_dims(const pbsa_dims* dims, int32_t mode);
 /* Slots per head of the persistent cache: capacity + window_frames * nb (0 if invalid). */
 int64_t pbsa_cache_slots(const pbsa_dims* dims);
 
-/* Device bytes of one layer's persistent cache (k, v, rep, block_id, len; see pbsa_cache),
- * 0 if dims are invalid. */
+/* Device bytes of one layer's persistent cache (k, v, rep, block_id, len and, for
+ * PBSA_KV_FP8, kv_scale; see pbsa_cache), 0 if dims are invalid. */
 size_t pbsa_cache_bytes(const pbsa_dims* dims);
 
 /* ---- host-side checks of lists and tables (no device access) ------------------------

@@ -33,6 +33,12 @@ pbsa_status pbsa_probe_gather(const pbsa_dims* dims, pbsa_tensor q, const pbsa_c
                               pbsa_tensor chunk_k, pbsa_tensor chunk_v, const int32_t* sel,
                               void* stream);
 
+/* The FP8 cache's decode as the attention runs it: out[16 i + j] = bf16 bits of
+ * E4M3(codes[16 i + j]) * scales[i] for n codes (n a multiple of 16; codes 16-byte
+ * aligned).  For checking the decode against the format's definition. */
+pbsa_status pbsa_probe_fp8_decode(const uint8_t* codes, const float* scales, uint16_t* out,
+                                  int32_t n, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

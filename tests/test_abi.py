@@ -288,3 +288,26 @@ def test_selection_checks():
     n2[0, 1] = 0
     with pytest.raises(ops.PbsaError):
         ops.pbsa_check_selection_2lvl(two, 3, sel2, n2)
+
+
+def test_fp8_cache_checks():
+    L = ops.lib()
+    assert L.pbsa_check_dims(ctypes.byref(_dims(kv_format=1)), 0) == 0
+    assert L.pbsa_check_dims(ctypes.byref(_dims(kv_format=2)), 0) == 2
+    assert L.pbsa_check_dims(ctypes.byref(_dims(kv_format=1, head_dim=64)), 0) == 3
+    fp8 = dataclasses.replace(WAN, kv_format=ops.PBSA_KV_FP8)
+    assert ops.pbsa_cache_bytes(fp8) == 12 * (64 + 150) * (2 * 64 * 128 + 128 * 4 + 8 + 8)
+    d = ctypes.byref(_dims(kv_format=1))
+    t = _tensor(16)
+    # an FP8 cache without its scales
+    assert L.pbsa_attn_fwd(d, t, ctypes.byref(ops.CacheC(16, 16, 16, 16, 16, 0)), t, t,
+                           ctypes.c_void_p(16), t, ctypes.c_void_p(16), None) == 1
+    # the persistent backward and the gather probe take bf16 caches only
+    cache = ops.CacheC(16, 16, 16, 16, 16, 0, None, 16)
+    assert L.pbsa_attn_bwd_persistent(d, t, ctypes.byref(cache), t, t, ctypes.c_void_p(16), t,
+                                      ctypes.c_void_p(16), t, t, t, t, ctypes.c_void_p(16),
+                                      ctypes.c_void_p(16), ctypes.c_void_p(16), 1 << 30,
+                                      None) == 3
+    assert L.pbsa_probe_gather(d, t, ctypes.byref(cache), t, t, ctypes.c_void_p(16), None) == 3
+    assert L.pbsa_probe_fp8_decode(ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.c_void_p(16),
+                                   17, None) == 2

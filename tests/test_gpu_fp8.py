@@ -1,0 +1,152 @@
+"""The FP8 KV cache (PBSA_KV_FP8) against the fp64 oracle's reading of it.
+
+Light Forcing (papernotes.org), "Key findings": the sparse attention deployed with FP8.
+The cache keeps each block's K and V as OCP E4M3 codes with a power-of-two scale per block
+and tensor.  Checked here: the attention's decode of every code against the format's
+definition (bit for bit); rollouts whose persistent sets, routing, slot codes and scales
+match the oracle's after every update (codes and scales bit for bit); and the attention at
+the measured chunk against the oracle's attention over the decoded blocks (the stated
+tolerance; the chunk's own K/V stay bf16).
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+from block_sparse_attention_pbsa_amd import ops, runtime, synth
+from parity import assert_close_attn, check_topk, say
+
+pytestmark = pytest.mark.gpu
+
+
+def dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda().to(torch.bfloat16)
+
+
+def test_fp8_decode_matches_the_format():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)] * 2, np.uint8)
+    pad = (-len(codes)) % 16
+    codes = np.concatenate([codes, np.zeros(pad, np.uint8)])
+    n = len(codes)
+    rs = np.random.default_rng(1)
+    scales = (2.0 ** rs.integers(-12, 12, n // 16)).astype(np.float32)
+    out = torch.empty(n, dtype=torch.int16, device="cuda")
+    ops.pbsa_probe_fp8_decode(torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda(), out)
+    torch.cuda.synchronize()
+    ref = orc.e4m3_decode(codes) * np.repeat(scales.astype(np.float64), 16)
+    want = synth.bf16_bits(ref.astype(np.float32)).view(np.int16)
+    assert np.array_equal(synth.round_bf16(ref.astype(np.float32)).astype(np.float64), ref)
+    assert np.array_equal(out.cpu().numpy(), want)
+
+
+TINY128 = synth.Workload("tiny128", 1, 128, 64, 256, 1, 4, 2, 4, 1, 4)
+
+
+def fp8_rollout(wl, seed, heads, rows, union=False):
+    shape = ops.Shape(wl.heads, wl.head_dim, wl.frame_tokens, wl.chunk_frames, wl.window_frames,
+                      wl.capacity, wl.sinks, wl.topk, wl.scale,
+                      route_mode=ops.PBSA_ROUTE_UNION if union else ops.PBSA_ROUTE_WINDOW,
+                      kv_format=ops.PBSA_KV_FP8)
+    sch = orc.Schedule(wl.frame_tokens, wl.block, wl.chunk_frames, wl.window_frames,
+                       wl.capacity, wl.sinks, wl.topk, wl.scale, union)
+    layer = runtime.PersistentLayer(shape)
+    layer.reset()
+    ros = {h: orc.PersistentRollout(sch, wl.head_dim, kv_fp8=True) for h in heads}
+    last = wl.measured_chunk
+    T = shape.chunk_tokens
+    for c in range(last + 1):
+        say(f"[fp8 {wl.name}] chunk {c}")
+        q, k, v = synth.chunk_qkv(wl, seed, c)
+        qd, kd, vd = dev(q), dev(k), dev(v)
+        layer.route(qd)
+        torch.cuda.synchronize()
+        sel = layer.sel.cpu().numpy()
+        routed = {}
+        for h in heads:
+            rt = ros[h].select(q[:, h])
+            routed[h] = rt
+            for r in range(shape.nq):
+                got = [int(g) for g in sel[h, r] if g >= 0]
+                check_topk(got, rt["cand"], rt["scores_cand"][r], wl.topk)
+        if c == last:
+            layer.attend(qd, kd, vd)
+            torch.cuda.synchronize()
+            for h in heads:
+                gsel = [[int(g) for g in sel[h, r] if g >= 0] for r in range(shape.nq)]
+                idx = np.arange(T) if rows is None else rows(h, T)
+                o_ref, l_ref = ros[h].attend(q[:, h], k[:, h], v[:, h], gsel, rows=idx)
+                o = layer.o[:, h].float().cpu().numpy()
+                assert_close_attn(o[idx], o_ref[idx], f"O head {h}")
+                assert np.abs(layer.lse[h].cpu().numpy()[idx] - l_ref[idx]).max() < 1e-3
+            return layer, ros
+        layer.update(kd, vd)
+        torch.cuda.synchronize()
+        bid = layer.cache.block_id.cpu().numpy()
+        kk, vv = layer.cache.k.cpu().numpy(), layer.cache.v.cpu().numpy()
+        sc = layer.cache.kv_scale.cpu().numpy()
+        ln = layer.cache.len.cpu().numpy()
+        for h in heads:
+            ro = ros[h]
+            cand, m = ro.update_candidates(routed[h])
+            gp = sorted(int(g) for g in bid[h, :wl.capacity] if g >= 0)
+            exact, _ = check_topk([g for g in gp if g >= wl.sinks], cand, m,
+                                  wl.capacity - wl.sinks)
+            ro.update(routed[h], k[:, h], v[:, h], P_override=None if exact else gp)
+            assert gp == ro.P
+            for s_ in range(shape.slots):
+                g = int(bid[h, s_])
+                if g < 0:
+                    continue
+                kc, ks, vc, vs = ro.fp8_codes[g]
+                n_ = int(ln[h, s_])
+                assert np.array_equal(kk[h, s_, :n_], kc), f"slot {s_} block {g}: K codes"
+                assert np.array_equal(vv[h, s_, :n_], vc), f"slot {s_} block {g}: V codes"
+                assert not kk[h, s_, n_:].any() and not vv[h, s_, n_:].any()
+                assert sc[h, s_, 0] == ks and sc[h, s_, 1] == vs, f"slot {s_}: scales"
+    raise AssertionError("unreachable")
+
+
+def _sampled(seed):
+    def pick(h, T):
+        rs = np.random.default_rng(seed + h)
+        fixed = list(range(0, 64)) + list(range(1536, 1560)) + list(range(T - 24, T))
+        return np.array(sorted(set(fixed) | set(rs.choice(T, 64, replace=False).tolist())))
+    return pick
+
+
+def test_fp8_rollout_tiny128_all_rows():
+    fp8_rollout(TINY128, 41, (0,), None)
+
+
+def test_fp8_rollout_wan_5s():
+    fp8_rollout(synth.WORKLOADS["wan_5s"], synth.SEEDS["wan_5s"], (0, 5, 11), _sampled(8))
+
+
+def test_fp8_rollout_wan_5s_union_routing():
+    wl = dataclasses.replace(synth.WORKLOADS["wan_5s"], name="wan_5s_union")
+    fp8_rollout(wl, synth.SEEDS["wan_5s"], (2,), _sampled(9), union=True)
+
+
+def test_fp8_cache_step_matches_bf16_routing_and_halves_bytes():
+    # same seeded chunks through a bf16 and an FP8 cache: identical routing and persistent
+    # sets (the representatives are the bf16 keys' means in both), half the K/V bytes
+    wl = synth.WORKLOADS["wan_5s"]
+    base = ops.Shape(wl.heads, wl.head_dim, wl.frame_tokens, wl.chunk_frames, wl.window_frames,
+                     wl.capacity, wl.sinks, wl.topk, wl.scale)
+    a = runtime.PersistentLayer(base)
+    b = runtime.PersistentLayer(dataclasses.replace(base, kv_format=ops.PBSA_KV_FP8))
+    a.reset()
+    b.reset()
+    for c in range(wl.measured_chunk + 1):
+        q, k, v = (dev(x) for x in synth.chunk_qkv(wl, synth.SEEDS["wan_5s"], c))
+        a.step(q, k, v)
+        b.step(q, k, v)
+        torch.cuda.synchronize()
+        assert torch.equal(a.sel, b.sel) and torch.equal(a.cache.block_id, b.cache.block_id)
+        assert torch.equal(a.scores, b.scores)
+    err = (a.o.float() - b.o.float()).abs()
+    say(f"  fp8 vs bf16 cache: O max-abs {err.max().item():.3e} mean-abs {err.mean().item():.3e}")
+    assert b.cache.k.element_size() * 2 == a.cache.k.element_size()
+    assert ops.pbsa_cache_bytes(b.shape) < 0.53 * ops.pbsa_cache_bytes(a.shape)

@@ -393,7 +393,48 @@ def test_tie_goes_to_lower_id_on_gpu():
 
 
 # --------------------------------------------------------------------------- two-level
-def two_level_check(wl, seed, grad_check="full", rows_fn=None, kv_blocks_fn=None):
+def decomposed_reference(q, k, v, dout, allowed, n, B, scale, qblocks=None, kv_blocks=None):
+    """The oracle's attention and gradient for one head, one query block at a time.
+
+    Each query block's rows attend exactly its own selected keys, so O, LSE and dQ of its
+    rows come from masked_attention(_grad) over those keys alone, and the gradient of the
+    keys and values is the sum over the query blocks of their contributions (dK = scale
+    dS^T Q and dV = P^T dO are sums over query rows).  Returns O, LSE, dQ for the rows of
+    `qblocks` (default: all) and dK, dV summed over every query block for the token rows of
+    `kv_blocks` (default: all), as full-size arrays (other rows NaN)."""
+    T, d = q.shape
+    nqb = len(allowed)
+    qblocks = range(nqb) if qblocks is None else qblocks
+    O = np.full((T, d), np.nan)
+    L = np.full(T, np.nan)
+    dQ = np.full((T, d), np.nan)
+    dK = np.zeros((T, d))
+    dV = np.zeros((T, d))
+    want_kv = None if kv_blocks is None else set(kv_blocks)
+    need_q = set(qblocks)
+    for r in range(nqb):
+        if want_kv is not None and r not in need_q and not (want_kv & set(allowed[r])):
+            continue
+        a, b = orc.block_token_range(r, n, B)
+        toks = np.concatenate([np.arange(*orc.block_token_range(g, n, B)) for g in allowed[r]])
+        m = np.ones((b - a, len(toks)), bool)
+        rq, rk, rv = orc.masked_attention_grad(q[a:b], k[toks], v[toks], m, scale, dout[a:b])
+        if r in need_q:
+            O[a:b], L[a:b] = orc.masked_attention(q[a:b], k[toks], v[toks], m, scale)
+            dQ[a:b] = rq
+        np.add.at(dK, toks, rk)
+        np.add.at(dV, toks, rv)
+    if want_kv is not None:
+        keep = np.zeros(T, bool)
+        for g in want_kv:
+            keep[slice(*orc.block_token_range(g, n, B))] = True
+        dK[~keep] = np.nan
+        dV[~keep] = np.nan
+    return O, L, dQ, dK, dV
+
+
+def two_level_check(wl, seed, grad_check="full", rows_fn=None, kv_blocks_fn=None,
+                    whole_heads=()):
     F, n, nb, H, d = wl.chunk_frames, wl.frame_tokens, wl.nb, wl.heads, wl.head_dim
     chunks = wl.clip_chunks
     shape = shape_of(wl)
@@ -474,6 +515,15 @@ def two_level_check(wl, seed, grad_check="full", rows_fn=None, kv_blocks_fn=None
             assert_close_attn(dq[:, h], rq, f"dQ head {h}")
             assert_close_attn(dk[:, h], rk, f"dK head {h}")
             assert_close_attn(dv[:, h], rv, f"dV head {h}")
+        elif h in whole_heads or grad_check == "decomposed":
+            # every row and every key of this head, one query block at a time
+            ro, rl, rq, rk, rv = decomposed_reference(q[:, h], k[:, h], v[:, h], dout[:, h],
+                                                      allowed, n, wl.block, wl.scale)
+            assert_close_attn(o[:, h], ro, f"O head {h} (all rows)")
+            assert np.abs(lse[h] - rl).max() < 1e-3
+            assert_close_attn(dq[:, h], rq, f"dQ head {h} (all rows)")
+            assert_close_attn(dk[:, h], rk, f"dK head {h} (all keys)")
+            assert_close_attn(dv[:, h], rv, f"dV head {h} (all keys)")
         else:
             # sampled query rows: O, LSE and dQ from the rows' own selected keys
             rows = rows_fn(h, T)
@@ -488,24 +538,16 @@ def two_level_check(wl, seed, grad_check="full", rows_fn=None, kv_blocks_fn=None
                 rq, _, _ = orc.masked_attention_grad(q[a:b, h], k[toks, h], v[toks, h], m,
                                                      wl.scale, dout[a:b, h])
                 assert_close_attn(dq[a:b, h], rq, f"dQ head {h} qblock {r}")
-            # sampled KV blocks: dK/dV from every query block that selected them
-            for g in kv_blocks_fn(h, nqb):
-                users = [r for r in range(nqb) if g in allowed[r]]
-                if not users:
-                    continue
-                qrows = np.concatenate([np.arange(*orc.block_token_range(r, n, wl.block))
-                                        for r in users])
-                keys = sorted(set().union(*[allowed[r] for r in users]))
-                ktoks = np.concatenate([np.arange(*orc.block_token_range(x, n, wl.block))
-                                        for x in keys])
-                m = orc.block_mask(users, [allowed[r] for r in users], n, wl.block, T, T)
-                m = m[qrows][:, ktoks]
-                _, rk, rv = orc.masked_attention_grad(q[qrows, h], k[ktoks, h], v[ktoks, h], m,
-                                                      wl.scale, dout[qrows, h])
+            # sampled KV blocks: dK/dV summed over every query block that selected them
+            blocks = kv_blocks_fn(h, nqb)
+            _, _, _, rk, rv = decomposed_reference(q[:, h], k[:, h], v[:, h], dout[:, h],
+                                                   allowed, n, wl.block, wl.scale,
+                                                   qblocks=[], kv_blocks=blocks)
+            for g in blocks:
+                users = sum(g in allowed[r] for r in range(nqb))
                 a, b = orc.block_token_range(g, n, wl.block)
-                sl = np.searchsorted(ktoks, np.arange(a, b))
-                assert_close_attn(dk[a:b, h], rk[sl], f"dK head {h} block {g}")
-                assert_close_attn(dv[a:b, h], rv[sl], f"dV head {h} block {g}")
+                assert_close_attn(dk[a:b, h], rk[a:b], f"dK head {h} block {g} ({users} users)")
+                assert_close_attn(dv[a:b, h], rv[a:b], f"dV head {h} block {g} ({users} users)")
     return near_rows
 
 
@@ -539,12 +581,26 @@ def test_two_level_wan_train_sampled():
         return rs.choice(T, 6, replace=False).tolist() + [T - 1, 1559]
 
     def kv_blocks(h, nqb):
-        # a block of the last chunk's own frames and one of the newest history frame
-        return [nqb - 3, nqb - 75 - 2]
+        # a block of the last chunk's own frames and one of the newest history frame; on
+        # heads 3 and 11 also blocks of frame 0 (forced for every chunk from the second on,
+        # so selected by up to 525 query blocks: their dK/dV are summed from up to six work
+        # items)
+        return [nqb - 3, nqb - 75 - 2] + ([0, 1, 12, 24] if h in (3, 11) else [])
 
+    # heads 0 and 7: every row and every key, one query block at a time
     near = two_level_check(wl, synth.SEEDS["wan_train"], grad_check="sampled", rows_fn=rows,
-                           kv_blocks_fn=kv_blocks)
+                           kv_blocks_fn=kv_blocks, whole_heads=(0, 7))
     say(f"  near-tie rows: {near}")
+
+
+def test_two_level_long_clip_split_items_full_gradients():
+    # 64-token frames (one block each), 4-frame chunks, 64 chunks: 256 query blocks, top-2
+    # frames with frame 0 forced and budgets up to every candidate, so frame 0's block is
+    # selected by more than 2 x 96 query blocks (three dK/dV work items and their fixed-order
+    # reduce); every gradient of both heads compared
+    wl = synth.Workload("train_long", 2, 128, 64, 64, 4, 0, 0, 0, 0, 64, clip_chunks=64,
+                        top_frames=2)
+    two_level_check(wl, 34, grad_check="decomposed")
 
 
 def test_bwd_is_deterministic():
