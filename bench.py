@@ -77,6 +77,8 @@ def parse():
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc output folders (FETCH_SIZE, WRITE_SIZE) of a "
                          "--copy-probe run into the traffic file, then exit")
+    ap.add_argument("--train-only", action="store_true",
+                    help="only the trainable path's extra field (for profiling its kernels)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, copy a 512 MiB buffer 3 times (calibrates the "
                          "FETCH_SIZE / WRITE_SIZE counters against known bytes)")
@@ -440,6 +442,16 @@ def main():
                                    "--gpus must be 1"}))
         sys.exit(2)
     cx = Ctx()
+    if args.train_only:
+        out = {"wan_train": bench_train(cx)}
+        if args.copy_probe:
+            src = cx.torch.ones(256 * 1024 * 1024, dtype=cx.torch.bfloat16, device="cuda")
+            dst = cx.torch.empty_like(src)
+            for _ in range(3):
+                dst.copy_(src)
+            cx.sync()
+        print(json.dumps(out), flush=True)
+        return
     name = args.config
     wl = cx.synth.WORKLOADS[name]
     cpu_heads = ()
