@@ -241,6 +241,7 @@ hipError_t launch_route(const pbsa_dims& d, TokIn q, float* q_rep, const pbsa_ca
 // ---------------------------------------------------------------- two-level selection
 
 constexpr int kMaxChunks = 256;
+constexpr size_t kScoreMfmaLds = 150 * 1024;  // dynamic LDS of the matrix-core selection
 struct ChunkBudgets {
   int32_t k[kMaxChunks];
 };
@@ -377,6 +378,177 @@ __global__ void __launch_bounds__(256)
   }
 }
 
+// Matrix-core form of the same selection for clips whose scores fit in LDS.  One
+// workgroup (512 threads) per group of up to 32 query blocks of one chunk and head: first
+// the scores of the group against every history frame and every block the chunk can see,
+// as 32 x 32 tiles of fp32 MFMAs (v_mfma_f32_32x32x2_f32: the products and sums stay in
+// fp32, like the dot products above, only in another order), each representative row read
+// once per group instead of once per query block; then each wave selects for its query
+// blocks from the scores in LDS, with the same radix selects and order as
+// score_topk_2lvl_kernel.  Dynamic LDS: block scores [32][nvis_pad], frame scores
+// [32][hist_pad], and per wave the frame flags and list ([frames_total] each).
+template <int D, int EF, int E>
+__global__ void __launch_bounds__(512, 1)
+    score_2lvl_mfma_kernel(const float* __restrict__ q_rep, const float* __restrict__ block_rep,
+                           const float* __restrict__ frame_rep, int F, int nb, int chunks,
+                           int top_frames, ChunkBudgets budgets, float scale, int max_sel,
+                           int groups_per_chunk, int nvis_pad, int hist_pad,
+                           int32_t* __restrict__ sel, int32_t* __restrict__ nsel_out) {
+  extern __shared__ float sel_lds[];
+  constexpr int KH = D / 2;  // channels per lane half: MFMA k-step s pairs channel s (lanes
+                             // 0..31) with channel KH + s (lanes 32..63)
+  const int h = blockIdx.y, t = threadIdx.x, w = t >> 6, l = t & 63;
+  const int h2 = l >> 5, c32 = l & 31;
+  const int nqc = F * nb;                        // query blocks per chunk
+  const int nq = chunks * nqc;
+  const int frames_total = chunks * F;
+  const int ci = blockIdx.x / groups_per_chunk;  // 0-based chunk
+  const int i = ci + 1;
+  const int r0 = ci * nqc + 32 * (blockIdx.x % groups_per_chunk);
+  const int G = nqc - 32 * static_cast<int>(blockIdx.x % groups_per_chunk) < 32
+                    ? nqc - 32 * static_cast<int>(blockIdx.x % groups_per_chunk)
+                    : 32;
+  if (i == 1) {
+    for (int j = t; j < G * nqc; j += 512) {
+      const int q = j / nqc, g = j - q * nqc;
+      sel[(static_cast<int64_t>(h) * nq + r0 + q) * max_sel + g] = g;
+    }
+    if (t < G) nsel_out[static_cast<int64_t>(h) * nq + r0 + t] = nqc;
+    return;
+  }
+  const int hist = F * (i - 1);
+  const int vis = hist + F;           // frames this chunk can see
+  const int nvis = vis * nb;          // blocks this chunk can see
+  float* bsc = sel_lds;                                      // [32][nvis_pad]
+  float* fsc = bsc + 32 * nvis_pad;                          // [32][hist_pad]
+  int* fflag = reinterpret_cast<int*>(fsc + 32 * hist_pad) + 2 * frames_total * w;
+  int* flist = fflag + frames_total;
+
+  // ---- scores: tiles of 32 rows (frames, then blocks) against the group's 32 query blocks
+  {
+    float qa[KH];
+    const float* qr = q_rep + (static_cast<int64_t>(h) * nq + r0 + c32) * D + KH * h2;
+#pragma unroll
+    for (int s4 = 0; s4 < KH / 4; ++s4) {
+      const f32x4 v = c32 < G ? *reinterpret_cast<const f32x4*>(qr + 4 * s4) : f32x4{0, 0, 0, 0};
+      qa[4 * s4] = v[0];
+      qa[4 * s4 + 1] = v[1];
+      qa[4 * s4 + 2] = v[2];
+      qa[4 * s4 + 3] = v[3];
+    }
+    const int ntf = (hist + 31) / 32, ntb = (nvis + 31) / 32;
+    const float* fr = frame_rep + static_cast<int64_t>(h) * frames_total * D;
+    const float* br = block_rep + static_cast<int64_t>(h) * nq * D;
+    for (int tt = w; tt < ntf + ntb; tt += 8) {
+      const bool is_f = tt < ntf;
+      const int row0 = 32 * (is_f ? tt : tt - ntf);
+      const int nrow = is_f ? hist : nvis;
+      const int row = row0 + c32;
+      const float* rp = (is_f ? fr : br) + static_cast<int64_t>(row < nrow ? row : 0) * D + KH * h2;
+      float kb[KH];
+#pragma unroll
+      for (int s4 = 0; s4 < KH / 4; ++s4) {
+        const f32x4 v = row < nrow ? *reinterpret_cast<const f32x4*>(rp + 4 * s4)
+                                   : f32x4{0, 0, 0, 0};
+        kb[4 * s4] = v[0];
+        kb[4 * s4 + 1] = v[1];
+        kb[4 * s4 + 2] = v[2];
+        kb[4 * s4 + 3] = v[3];
+      }
+      f32x16 acc = {};
+#pragma unroll
+      for (int s = 0; s < KH; ++s)
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[s], kb[s], acc, 0, 0, 0);
+      // lane: column (row of the tile) c32, query blocks acc_row(e, h2)
+      float* dst = is_f ? fsc : bsc;
+      const int pitch = is_f ? hist_pad : nvis_pad;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int qb = 8 * (e >> 2) + 4 * h2 + (e & 3);
+        dst[qb * pitch + row0 + c32] = scale * acc[e];
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- selection: wave w takes query blocks w, w + 8, ... of the group
+  for (int q = w; q < G; q += 8) {
+    const int r = r0 + q;
+    int32_t* out = sel + (static_cast<int64_t>(h) * nq + r) * max_sel;
+    const float* fq = fsc + q * hist_pad;
+    const float* bq = bsc + q * nvis_pad;
+    // forced: sink frame, latest history frame, the chunk's own frames
+    for (int f = l; f < vis; f += 64) fflag[f] = (f == 0 || f >= hist - 1);
+    const int ntop = top_frames < hist ? top_frames : hist;
+    if (ntop > 0) {
+      uint64_t fk[EF];
+#pragma unroll
+      for (int e = 0; e < EF; ++e) {
+        const int f = l + 64 * e;
+        fk[e] = f < hist ? rank_key(fq[f], f) : 0;
+      }
+      bool on[EF];
+      wave_topk<EF>(fk, ntop, on);
+#pragma unroll
+      for (int e = 0; e < EF; ++e)
+        if (on[e]) fflag[l + 64 * e] = 1;
+    }
+    // chosen frames in ascending order (ballot compaction over the visible frames)
+    int nfr = 0;
+    for (int f0 = 0; f0 < vis; f0 += 64) {
+      const int f = f0 + l;
+      const bool on = f < vis && fflag[f];
+      const unsigned long long m = __ballot(on);
+      if (on) flist[nfr + __popcll(m & ((1ull << l) - 1ull))] = f;
+      nfr += __popcll(m);
+    }
+    const int ncand = nfr * nb;
+    auto cand_id = [&](int cc) { return flist[cc / nb] * nb + (cc % nb); };
+    uint64_t key[E];
+    int gid[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int cc = l + 64 * e;
+      gid[e] = cc < ncand ? cand_id(cc) : -1;
+      key[e] = cc < ncand ? rank_key(bq[gid[e]], gid[e]) : 0;
+    }
+    int k = budgets.k[i - 1];
+    if (k > ncand) k = ncand;
+    if (k < 1) k = 1;
+    bool on[E];
+    wave_topk<E>(key, k, on);
+    int base = 0;
+    const unsigned long long below = (1ull << l) - 1ull;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const unsigned long long m = __ballot(on[e]);
+      if (on[e]) out[base + __popcll(m & below)] = gid[e];
+      base += __popcll(m);
+    }
+    if (l == 0) nsel_out[static_cast<int64_t>(h) * nq + r] = k;
+  }
+}
+
+template <int D, int EF>
+static hipError_t launch_2lvl_mfma_e(int E, dim3 grid, size_t lds, hipStream_t s,
+                                     const float* q_rep, const float* block_rep,
+                                     const float* frame_rep, int F, int nb, int chunks,
+                                     int top_frames, const ChunkBudgets& b, float scale,
+                                     int max_sel, int gpc, int nvis_pad, int hist_pad,
+                                     int32_t* sel, int32_t* nsel) {
+#define PBSA_2LVL_M(EE)                                                                       \
+  hipLaunchKernelGGL((score_2lvl_mfma_kernel<D, EF, EE>), grid, dim3(512), lds, s, q_rep,      \
+                     block_rep, frame_rep, F, nb, chunks, top_frames, b, scale, max_sel, gpc, \
+                     nvis_pad, hist_pad, sel, nsel)
+  if (E <= 1) PBSA_2LVL_M(1);
+  else if (E <= 2) PBSA_2LVL_M(2);
+  else if (E <= 4) PBSA_2LVL_M(4);
+  else if (E <= 8) PBSA_2LVL_M(8);
+  else PBSA_2LVL_M(16);
+#undef PBSA_2LVL_M
+  return hipGetLastError();
+}
+
 template <int D, int EF>
 static hipError_t launch_2lvl_e(int E, dim3 grid, size_t lds, hipStream_t s, const float* q_rep,
                                 const float* block_rep, const float* frame_rep, int F, int nb,
@@ -410,6 +582,26 @@ static hipError_t launch_2lvl_d(const pbsa_dims& d, int chunks, int top_frames,
   const int ncand = fr_max * nb;
   const int E = (ncand + 63) / 64;
   const int EF = (frames_total + 63) / 64;
+  // the matrix-core form when the group's scores fit in LDS
+  const int nvis_pad = 32 * ((frames_total * nb + 31) / 32);
+  const int hist_pad = 32 * ((frames_total - F + 31) / 32 > 0 ? (frames_total - F + 31) / 32 : 1);
+  const size_t lds_m = (static_cast<size_t>(32) * (nvis_pad + hist_pad) +
+                        static_cast<size_t>(8) * 2 * frames_total) * sizeof(float);
+  if (lds_m <= kScoreMfmaLds) {
+    const int gpc = (F * nb + 31) / 32;
+    dim3 grid_m(chunks * gpc, d.heads);
+    if (EF <= 1)
+      return launch_2lvl_mfma_e<D, 1>(E, grid_m, lds_m, s, q_rep, block_rep, frame_rep, F, nb,
+                                      chunks, top_frames, b, d.scale, max_sel, gpc, nvis_pad,
+                                      hist_pad, sel, nsel);
+    if (EF <= 2)
+      return launch_2lvl_mfma_e<D, 2>(E, grid_m, lds_m, s, q_rep, block_rep, frame_rep, F, nb,
+                                      chunks, top_frames, b, d.scale, max_sel, gpc, nvis_pad,
+                                      hist_pad, sel, nsel);
+    return launch_2lvl_mfma_e<D, 4>(E, grid_m, lds_m, s, q_rep, block_rep, frame_rep, F, nb,
+                                    chunks, top_frames, b, d.scale, max_sel, gpc, nvis_pad,
+                                    hist_pad, sel, nsel);
+  }
   const size_t lds = static_cast<size_t>(3 * frames_total + 64 * E) * sizeof(int);
   dim3 grid(nq, d.heads);
   if (EF <= 1)
