@@ -14,11 +14,13 @@
 //                registers) and accumulates dQ^T = K^T dS^T, reading K channel-major with
 //                the transposing LDS read.  It also writes D for its rows.
 //   inverse   -- the query blocks that selected each KV block, in ascending order: every
-//                query block sets its bit in a bitmap row per selected KV block, then one
-//                workgroup per (KV block, head) turns its row into the list.
+//                query block sets its bit in a bitmap row per selected KV block and the rows'
+//                bits are counted; after the plan pass one workgroup per (KV block, head)
+//                writes its row's list at its offset (the lists are stored back to back).
 //   plan      -- one workgroup: cuts every inverse list into work items of at most
 //                kSplitQ query blocks (a few KV blocks are selected by every query block,
-//                most by a few dozen), numbering items and partial-sum slots by prefix sums.
+//                most by a few dozen), numbering items, partial-sum slots and list offsets
+//                by prefix sums.
 //   dkdv pass -- work items taken largest first from a counter (the plan pass orders them
 //                by size; each item writes only its own outputs, so results do not depend on
 //                which workgroup takes it), two waves of 32 keys each; each lane keeps
@@ -44,8 +46,10 @@ struct BwdArgs {
   const int32_t* sel;   // [H][nq][max_sel]
   const int32_t* nsel;  // [H][nq]
   float* Dw;            // workspace [H][T]
-  int32_t* inv_cnt;     // workspace [H][nq]
-  int32_t* inv;         // workspace [H][nq][nq]
+  int32_t* inv_cnt;     // workspace [H][nkv]: query blocks that selected each KV block
+  int32_t* inv_off;     // workspace [H][nkv]: start of each KV block's list in inv
+  int32_t* inv;         // workspace: the inverse lists back to back (at most H*nq*max_sel)
+  uint32_t* bits;       // workspace [H][nkv][ceil(nq / 32)]: bit r = query block r selected
   int2* items;          // workspace: work item -> (h*nq + g, split)
   int2* sorted;         // workspace: the same items by decreasing number of query blocks
   int32_t* nsplit;      // workspace [H*nq]
@@ -382,18 +386,16 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------------------ inverse lists
-// grid (nq, H), 256 threads: inv[h][g] = ascending query blocks whose list holds g.
-// The inverse lists go through bitmaps: bit r of row (h, g) is set when query block r of
-// head h selected KV block g.  A row's W = ceil(nq / 32) words sit in the tail of that row's
-// own inverse list, which the list pass reads whole before writing the list over it.
+// inv holds, for every (head, KV block), the ascending query blocks whose list holds the KV
+// block, back to back (offsets inv_off from the plan pass), so it grows with the number of
+// selections, not with nq * nkv.  They go through bitmaps: bit r of row (h, g) is set when
+// query block r of head h selected KV block g.
 __global__ void __launch_bounds__(256) attn_bwd_bits_clear_kernel(BwdArgs a) {
   const int W = (a.nq + 31) >> 5;
   const int64_t n = static_cast<int64_t>(a.H) * a.nkv * W;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
-       i += static_cast<int64_t>(gridDim.x) * 256) {
-    const int64_t row = i / W;
-    a.inv[row * a.nq + (a.nq - W) + (i - row * W)] = 0;
-  }
+       i += static_cast<int64_t>(gridDim.x) * 256)
+    a.bits[i] = 0u;
 }
 
 // one workgroup per (query block, head): sets the query block's bit in the row of every
@@ -412,13 +414,24 @@ __global__ void __launch_bounds__(128) attn_bwd_bits_set_kernel(BwdArgs a) {
       const int f = g / a.nb;
       if (r < (f / a.F) * a.F * a.nb) continue;
     }
-    int32_t* row = a.inv + (static_cast<int64_t>(h) * a.nkv + g) * a.nq + (a.nq - W);
-    atomicOr(reinterpret_cast<unsigned int*>(row + (r >> 5)), 1u << (r & 31));
+    uint32_t* row = a.bits + (static_cast<int64_t>(h) * a.nkv + g) * W;
+    atomicOr(row + (r >> 5), 1u << (r & 31));
   }
 }
 
-// one workgroup per (KV block, head): the row's set bits in ascending order become its
-// inverse list (query blocks that selected the KV block) and count
+// one thread per (head, KV block): the number of query blocks that selected it
+__global__ void __launch_bounds__(256) attn_bwd_bits_count_kernel(BwdArgs a) {
+  const int W = (a.nq + 31) >> 5;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (row >= static_cast<int64_t>(a.H) * a.nkv) return;
+  const uint32_t* b = a.bits + row * W;
+  int n = 0;
+  for (int j = 0; j < W; ++j) n += __popc(b[j]);
+  a.inv_cnt[row] = n;
+}
+
+// one workgroup per (KV block, head), after the plan pass: the row's set bits in ascending
+// order become its inverse list at inv + inv_off
 constexpr int kMaxBitWords = 2048;  // nq <= 65536
 __global__ void __launch_bounds__(256) attn_bwd_bits_list_kernel(BwdArgs a) {
   __shared__ uint32_t bits[kMaxBitWords];
@@ -426,9 +439,10 @@ __global__ void __launch_bounds__(256) attn_bwd_bits_list_kernel(BwdArgs a) {
   const int g = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
   const int w = t >> 6, l = t & 63;
   const int W = (a.nq + 31) >> 5;
-  int32_t* out = a.inv + (static_cast<int64_t>(h) * a.nkv + g) * a.nq;
-  for (int j = t; j < W; j += 256) bits[j] = static_cast<uint32_t>(out[a.nq - W + j]);
-  __syncthreads();  // every word is read before the list overwrites the row's tail
+  const int64_t row = static_cast<int64_t>(h) * a.nkv + g;
+  int32_t* out = a.inv + a.inv_off[row];
+  for (int j = t; j < W; j += 256) bits[j] = a.bits[row * W + j];
+  __syncthreads();
   int total = 0;
   for (int base = 0; base < W; base += 256) {
     const int j = base + t;
@@ -451,7 +465,6 @@ __global__ void __launch_bounds__(256) attn_bwd_bits_list_kernel(BwdArgs a) {
     total += wsum[0] + wsum[1] + wsum[2] + wsum[3];
     __syncthreads();
   }
-  if (t == 0) a.inv_cnt[static_cast<int64_t>(h) * a.nkv + g] = total;
 }
 
 // ------------------------------------------------------------------ plan
@@ -461,14 +474,15 @@ constexpr int kSplitQ = 96;  // query blocks per dK/dV work item, at most
 // (head, KV block) pairs, in order, then three block-wide exclusive scans number the work
 // items, the partial slots and the split blocks.
 __global__ void __launch_bounds__(1024) attn_bwd_plan_kernel(BwdArgs a) {
-  __shared__ int sc[3][1024];
+  __shared__ int sc[4][1024];
   const int t = threadIdx.x;
   const int N = a.H * a.nkv;
   const int per = (N + 1023) / 1024;
   const int e0 = t * per, e1 = min(N, e0 + per);
-  int my_items = 0, my_parts = 0, my_long = 0;
+  int my_items = 0, my_parts = 0, my_long = 0, my_cnt = 0;
   for (int e = e0; e < e1; ++e) {
     const int cnt = a.inv_cnt[e];
+    my_cnt += cnt;
     const int ns = cnt <= kSplitQ ? 1 : (cnt + kSplitQ - 1) / kSplitQ;
     my_items += ns;
     if (ns > 1) {
@@ -479,24 +493,30 @@ __global__ void __launch_bounds__(1024) attn_bwd_plan_kernel(BwdArgs a) {
   sc[0][t] = my_items;
   sc[1][t] = my_parts;
   sc[2][t] = my_long;
+  sc[3][t] = my_cnt;
   __syncthreads();
   // Hillis-Steele inclusive scans
   for (int o = 1; o < 1024; o <<= 1) {
-    int v0 = 0, v1 = 0, v2 = 0;
+    int v0 = 0, v1 = 0, v2 = 0, v3 = 0;
     if (t >= o) {
       v0 = sc[0][t - o];
       v1 = sc[1][t - o];
       v2 = sc[2][t - o];
+      v3 = sc[3][t - o];
     }
     __syncthreads();
     sc[0][t] += v0;
     sc[1][t] += v1;
     sc[2][t] += v2;
+    sc[3][t] += v3;
     __syncthreads();
   }
   int it = sc[0][t] - my_items, pt = sc[1][t] - my_parts, lg = sc[2][t] - my_long;
+  int io = sc[3][t] - my_cnt;
   for (int e = e0; e < e1; ++e) {
     const int cnt = a.inv_cnt[e];
+    a.inv_off[e] = io;
+    io += cnt;
     const int ns = cnt <= kSplitQ ? 1 : (cnt + kSplitQ - 1) / kSplitQ;
     a.nsplit[e] = ns;
     a.part_base[e] = ns > 1 ? pt : -1;
@@ -621,7 +641,7 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdArgs a) {
     const int cnt = a.inv_cnt[hg];
     const int q_lo = sp * kSplitQ;
     const int q_hi = min(cnt, q_lo + kSplitQ);
-    const int32_t* lst = a.inv + static_cast<int64_t>(hg) * a.nq;
+    const int32_t* lst = a.inv + a.inv_off[hg];
     const int nsteps = q_hi - q_lo;  // one query block per step
     for (int i = t; i < nsteps; i += 256) {
       const int rb = lst[q_lo + i];
@@ -888,8 +908,8 @@ namespace {
 // Workspace layout of the backward (bytes, 256-aligned pieces).  Persistent mode adds the
 // query blocks' KV lists and their lengths.
 struct BwdWs {
-  size_t D, inv_cnt, inv, items, sorted, nsplit, part_base, long_list, counts, part, lists,
-      nlists, total;
+  size_t D, inv_cnt, inv_off, inv, bits, items, sorted, nsplit, part_base, long_list, counts,
+      part, lists, nlists, total;
 };
 BwdWs bwd_ws(int64_t H, int64_t nq, int64_t nkv, int64_t T, int64_t max_sel, int head_dim,
              bool persist) {
@@ -901,7 +921,9 @@ BwdWs bwd_ws(int64_t H, int64_t nq, int64_t nkv, int64_t T, int64_t max_sel, int
   size_t o = 0;
   w.D = o; o += up(H * T * 4);
   w.inv_cnt = o; o += up(H * nkv * 4);
-  w.inv = o; o += up(H * nkv * nq * 4);
+  w.inv_off = o; o += up(H * nkv * 4);
+  w.inv = o; o += up(pairs_max * 4);
+  w.bits = o; o += up(H * nkv * ((nq + 31) / 32) * 4);
   w.items = o; o += up(items_max * 8);
   w.sorted = o; o += up(items_max * 8);
   w.nsplit = o; o += up(H * nkv * 4);
@@ -923,7 +945,9 @@ void bind_ws(BwdArgs& a, const BwdWs& L, void* ws) {
   char* p = static_cast<char*>(ws);
   a.Dw = reinterpret_cast<float*>(p + L.D);
   a.inv_cnt = reinterpret_cast<int32_t*>(p + L.inv_cnt);
+  a.inv_off = reinterpret_cast<int32_t*>(p + L.inv_off);
   a.inv = reinterpret_cast<int32_t*>(p + L.inv);
+  a.bits = reinterpret_cast<uint32_t*>(p + L.bits);
   a.items = reinterpret_cast<int2*>(p + L.items);
   a.sorted = reinterpret_cast<int2*>(p + L.sorted);
   a.nsplit = reinterpret_cast<int32_t*>(p + L.nsplit);
@@ -963,10 +987,12 @@ hipError_t launch_bwd_passes(const BwdArgs& a, int head_dim, hipStream_t s) {
     hipLaunchKernelGGL(attn_bwd_bits_clear_kernel, dim3(gc), dim3(256), 0, s, a);
   }
   hipLaunchKernelGGL(attn_bwd_bits_set_kernel, dim3(a.nq, a.H), dim3(128), 0, s, a);
-  hipLaunchKernelGGL(attn_bwd_bits_list_kernel, dim3(a.nkv, a.H), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(attn_bwd_bits_count_kernel, dim3(cdiv(a.H * a.nkv, 256)), dim3(256), 0, s,
+                     a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_bwd_plan_kernel, dim3(1), dim3(1024), 0, s, a);
+  hipLaunchKernelGGL(attn_bwd_bits_list_kernel, dim3(a.nkv, a.H), dim3(256), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t items_max = static_cast<int64_t>(a.H) * a.nkv +
