@@ -544,7 +544,7 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-TRAFFIC_KERNEL = "attn_fwd_kernel<128, true, false>"
+TRAFFIC_KERNEL = "attn_fwd_kernel<128, true, false, false>"
 KERNEL_SOURCES = ("attn_fwd.hip", "attn_common.h", "common.h")
 
 

@@ -30,6 +30,16 @@
 // Softmax runs in base 2 with scale*log2(e) folded in (v_exp_f32), P is packed to bf16 with
 // v_cvt_pk_bf16_f32, and the running max is raised lazily (checked on the row sums after
 // the exponentials, not by a max before them); accumulators are fp32.
+//
+// FP8 cache (Light Forcing, papernotes.org, "Key findings": the sparse attention deployed
+// with FP8).  The cache holds OCP E4M3 codes with one power-of-two scale per block and
+// tensor; the chunk's own K/V stay bf16.  The FP8 instance keeps this pipeline: a cache
+// slot's half tile is loaded as codes into registers (as many load instructions as the bf16
+// gathers, so the waits stay exact), decoded with gfx950's scaled FP8 -> bf16 conversion
+// (exact: the scale is a power of two) and stored into the same LDS layout before the
+// barrier that publishes the tile -- K two steps ahead (loaded under a PV phase, stored at
+// the end of the next S phase), V one step ahead (loaded under the S phase, stored at the
+// end of the PV phase).  Chunk blocks still go straight into LDS.
 #include "attn_common.h"
 
 namespace pbsa {
@@ -59,6 +69,9 @@ struct FwdArgs {
   // persistent mode, top-K over the persistent and window blocks together: only the sink
   // slots [0, S) are attended whole, routed ids may name persistent blocks
   int route_union, S;
+  // FP8 cache: ck / cv hold E4M3 codes [H][slots][64][D] (one byte each), kv_scale the
+  // power-of-two scale of every slot's K and V ([H][slots][2])
+  const float* kv_scale;
 };
 
 namespace {
@@ -136,7 +149,9 @@ struct HalfRef {
   const char* k;
   const char* v;
   uint32_t stride;
-  int len;  // 0 = nothing to gather
+  int len;      // 0 = nothing to gather
+  bool f8;      // E4M3 codes of an FP8 cache slot (loaded into registers and decoded)
+  float ks, vs; // their K and V scales
 };
 
 // Online-softmax state of one wave (32 query rows, this lane's row = column c32).
@@ -444,7 +459,7 @@ struct RowState {
 // 1-D grid of 8 * ceil(H * pairs / 8) workgroups of 256 threads.  GATHER_ONLY builds the
 // gather probe: the same lists, gathers, waits and barriers with the math left out (no
 // output is written).
-template <int D, bool PERSIST, bool GATHER_ONLY = false>
+template <int D, bool PERSIST, bool GATHER_ONLY = false, bool FP8 = false>
 __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
   using HT = HalfTile<D>;
   // K and V half tiles (X and Y) of even and odd steps, gathered straight into LDS; four
@@ -483,7 +498,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
   // Shared list (persistent mode): occupied P slots in slot order, then the chunk's
   // blocks, then the routed blocks that A and B have in common (kept at the end of A's
   // list area, last to first).  Private lists: the routed blocks of A only and of B only.
-  constexpr uint32_t kCacheBlockBytes = kBlock * D * 2;
+  constexpr uint32_t kCacheBlockBytes = kBlock * D * (FP8 ? 1 : 2);
   const uint32_t xrow = static_cast<uint32_t>(a.xts * 2);
   auto tok_entry = [&](int g) {
     const int f = g / a.nb, jj = g - f * a.nb;
@@ -652,13 +667,20 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
   auto ref_of = [&](uint32_t e, int half, HalfRef& hr) {
     const bool tok = (e >> 31) != 0;
     const uint32_t id = e & 0xffffffu;
-    const uint32_t stride = tok ? xrow : 2 * D;
+    const uint32_t stride = tok ? xrow : (FP8 ? D : 2 * D);
     const uint32_t o = (tok ? id * xrow : id * kCacheBlockBytes) + 32 * half * stride;
     hr.len = half_len(e, half);
+    hr.f8 = false;
     if (hr.len > 0) {
       hr.k = (tok ? xk_h : ck_h) + o;
       hr.v = (tok ? xv_h : cv_h) + o;
       hr.stride = stride;
+      if (FP8 && !tok) {
+        hr.f8 = true;
+        const float* sc = a.kv_scale + (static_cast<int64_t>(h) * a.slots + id) * 2;
+        hr.ks = sc[0];
+        hr.vs = sc[1];
+      }
     } else {
       // an empty half tile still gets its gathers (of the head's first token row, so
       // that every step issues the same number and the waits stay fixed); its rows are
@@ -724,6 +746,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
   struct Offs {
     __amdgpu_buffer_rsrc_t kb, vb;  // dma_base(hr.k), dma_base(hr.v)
     uint32_t k, v0, v1;   // lane offsets of K, and of V rows (l >> 2) and 16 + (l >> 2)
+    uint32_t fk, fv;      // (FP8 slot) lane offsets of this lane's 32 K and 32 V codes
   };
   auto offsets = [&](const HalfRef& hr) {
     const uint32_t last = static_cast<uint32_t>(hr.len > 0 ? hr.len - 1 : 0);
@@ -734,16 +757,82 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
     // this wave's V pieces p0 + i lie in segments (p0 + i) / 2 = p0 / 2 + i / 2
     o.v0 = min(v_rowl, last) * hr.stride + v_colb + 32u * p0 + 3072u;
     o.v1 = min(16u + v_rowl, last) * hr.stride + v_colb + 32u * p0 + 3072u;
+    if constexpr (FP8) {
+      // the same rows and channels as the wave's bf16 pieces, as codes: K rows
+      // 16 (w & 1) + (l & 15), channels 32 (l >> 4) + [0, 32); V rows l >> 1, channels
+      // 64 (w & 1) + 32 (l & 1) + [0, 32)
+      o.fk = min(16u * (w & 1) + k_rowl, last) * hr.stride + 32u * (l >> 4) + 3072u;
+      o.fv = min(static_cast<uint32_t>(l >> 1), last) * hr.stride + 64u * (w & 1) +
+             32u * (l & 1) + 3072u;
+    }
     return o;
   };
+  // (FP8) codes of this wave's pieces in flight: K of the step two ahead (loaded under a
+  // PV phase, decoded into LDS at the end of the next S phase), V of the next step (loaded
+  // under an S phase, decoded at the end of the same step's PV phase)
+  u32x2 kpend[HP], vpend[HP];
+  float kscale = 1.f, vscale = 1.f;
+  bool kp8 = false, vp8 = false;
   auto gather_k = [&](char (*buf)[HT::BYTES], const HalfRef& hr, const Offs& o, int i) {
-    (void)hr;
+    if constexpr (FP8) {
+      if (i == 0) {
+        kp8 = hr.f8;
+        kscale = hr.ks;
+      }
+      if (hr.f8) {
+        // as many instructions as the bf16 pieces, so the waits below stay exact
+        kpend[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                 o.kb, o.fk + 8u * i, 0, 0));
+        return;
+      }
+    }
     lds_dma16_piece(i, o.kb, o.k + 64u * i - 1024u * i, buf[tw] + 1024 * p0);
   };
   auto gather_v = [&](char (*buf)[HT::BYTES], const HalfRef& hr, const Offs& o, int i) {
-    (void)hr;
+    if constexpr (FP8) {
+      if (i == 0) {
+        vp8 = hr.f8;
+        vscale = hr.vs;
+      }
+      if (hr.f8) {
+        vpend[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                 o.vb, o.fv + 8u * i, 0, 0));
+        return;
+      }
+    }
     lds_dma16_piece(i, o.vb, (i % 2 ? o.v1 : o.v0) + 64u * (i / 2) - 1024u * i,
                     buf[tw] + 1024 * p0);
+  };
+  // (FP8) decode the pending codes (exact in bf16: a power-of-two scale) and store them
+  // into the tile layouts the bf16 gathers fill
+  auto store_k = [&](char (*buf)[HT::BYTES]) {
+    if constexpr (FP8) {
+      if (kp8) {
+        u32x4 d[4];
+        decode_e4m3x16(u32x4{kpend[0][0], kpend[0][1], kpend[1][0], kpend[1][1]}, kscale,
+                       d[0], d[1]);
+        decode_e4m3x16(u32x4{kpend[2][0], kpend[2][1], kpend[3][0], kpend[3][1]}, kscale,
+                       d[2], d[3]);
+        const int R = 16 * (w & 1) + (l & 15);
+        char* base = buf[tw] + (R >> 4) * HT::KRG + 16 * (R & 15) + 256 * 4 * (l >> 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(base + 256 * j) = d[j];
+      }
+    }
+  };
+  auto store_v = [&](char (*buf)[HT::BYTES]) {
+    if constexpr (FP8) {
+      if (vp8) {
+        u32x4 d[4];
+        decode_e4m3x16(u32x4{vpend[0][0], vpend[0][1], vpend[1][0], vpend[1][1]}, vscale,
+                       d[0], d[1]);
+        decode_e4m3x16(u32x4{vpend[2][0], vpend[2][1], vpend[3][0], vpend[3][1]}, vscale,
+                       d[2], d[3]);
+        char* base = buf[tw] + 2048 * (2 * (w & 1) + (l & 1)) + 64 * (l >> 1);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(base + 16 * j) = d[j];
+      }
+    }
   };
   // Waits before the barriers that publish gathered tiles.  Each wave's gathers in issue
   // order: K(s), V(s), K(s+1), V(s+1), ... (HP instructions each).  Before the top barrier
@@ -782,10 +871,14 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
     const Offs o0 = offsets(r0), o1 = offsets(r1);
 #pragma unroll
     for (int i = 0; i < HP; ++i) gather_k(kb0, r0, o0, i);
+    store_k(kb0);
 #pragma unroll
     for (int i = 0; i < HP; ++i) gather_v(vb0, r0, o0, i);
+    store_v(vb0);
 #pragma unroll
     for (int i = 0; i < HP; ++i) gather_k(kb1, r1, o1, i);
+    store_k(kb1);
+    kp8 = false;  // (K of step 1 is stored)
   }
   // Step s (kc/vc: its K and V buffers, vn: V buffer of step s+1):
   //   top barrier (K(s) published) -> V(s+1) gathers under the S phase -> mid barrier
@@ -793,8 +886,10 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
   //   PV phase.
   // A shared step gives every wave both half tiles (64 keys); a private step gives each
   // wave pair its own query block's half tile.
-  auto step = [&](char (*kc)[HT::BYTES], char (*vc)[HT::BYTES], char (*vn)[HT::BYTES], int s,
-                  bool kShared) {
+  // (FP8: kn is K of step s+1, decoded into LDS at the end of the S phase; V of step s+1
+  // is decoded into vn at the end of the PV phase)
+  auto step = [&](char (*kc)[HT::BYTES], char (*kn)[HT::BYTES], char (*vc)[HT::BYTES],
+                  char (*vn)[HT::BYTES], int s, bool kShared) {
     wait_keep_next();
     lds_barrier();
     decode(s + 2, ex, ey, r2, lx2, ly2);
@@ -846,6 +941,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
         sacc[0] = st.scores(kc[mine] + kofs, len, h2);
       }
     }
+    store_k(kn);
     wait_keep_next();
     lds_barrier();
     // PV phase
@@ -858,6 +954,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
       if (kShared) st.template update<2>(sacc, vc[0] + vofs, vc[1] + vofs, c);
       else st.template update<1>(sacc, vc[mine] + vofs, vc[mine] + vofs, c);
     }
+    store_v(vn);
     }
     r1 = r2;
     lx0 = lx1;
@@ -867,12 +964,12 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
   };
   int s = 0;
   for (; s < nsh2; s += 2) {
-    step(kb0, vb0, vb1, s, true);
-    step(kb1, vb1, vb0, s + 1, true);
+    step(kb0, kb1, vb0, vb1, s, true);
+    step(kb1, kb0, vb1, vb0, s + 1, true);
   }
   for (; s < nsteps; s += 2) {
-    step(kb0, vb0, vb1, s, false);
-    step(kb1, vb1, vb0, s + 1, false);
+    step(kb0, kb1, vb0, vb1, s, false);
+    step(kb1, kb0, vb1, vb0, s + 1, false);
   }
   vm_wait<0>();  // no gather may still be writing this workgroup's LDS when it exits
 
@@ -937,6 +1034,41 @@ hipError_t launch_attn_fwd_persistent(const pbsa_dims& d, TokIn q, const pbsa_ca
   if (gather_only)
     return d.head_dim == 128 ? launch<128, true, true>(a, s) : launch<64, true, true>(a, s);
   return d.head_dim == 128 ? launch<128, true>(a, s) : launch<64, true>(a, s);
+}
+
+hipError_t launch_attn_fwd_fp8(const pbsa_dims& d, TokIn q, const pbsa_cache& c, TokIn ck,
+                               TokIn cv, const int32_t* sel, TokOut o, float* lse,
+                               hipStream_t s) {
+  FwdArgs a{};
+  const int nb = nb_of(d);
+  a.q = q.p; a.qts = q.ts; a.qhs = q.hs;
+  a.o = o.p; a.ots = o.ts; a.ohs = o.hs;
+  a.lse = lse;
+  a.lse_hs = static_cast<int64_t>(d.chunk_frames) * d.frame_tokens;
+  a.ck = static_cast<const uint16_t*>(c.k);  // E4M3 codes, addressed in bytes
+  a.cv = static_cast<const uint16_t*>(c.v);
+  a.kv_scale = c.kv_scale;
+  a.bid = c.block_id;
+  a.blen = c.len;
+  a.slots = static_cast<int>(slots_of(d));
+  a.C = d.capacity;
+  a.W = d.window_frames;
+  a.xk = ck.p; a.xv = cv.p; a.xts = ck.ts; a.xhs = ck.hs;
+  a.sel = sel;
+  a.nsel = nullptr;
+  a.sel_stride = d.topk;
+  a.nq = d.chunk_frames * nb;
+  a.n = d.frame_tokens;
+  a.nb = nb;
+  a.H = d.heads;
+  a.pairs = cdiv(a.nq, 2);
+  a.scale = d.scale;
+  a.route_union = d.route_mode == PBSA_ROUTE_UNION;
+  a.S = d.sinks;
+  const int G = a.H * a.pairs;
+  hipLaunchKernelGGL((attn_fwd_kernel<128, true, false, true>), dim3(8 * cdiv(G, 8)), dim3(256),
+                     0, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_attn_fwd_2lvl(const pbsa_dims& d, int chunks, TokIn q, TokIn k, TokIn v,
