@@ -368,7 +368,10 @@ void pbsa_chunk_graph_destroy(pbsa_chunk_graph* graph);
  * left untouched) and nsel[h][r] (int32 [heads][Nq]), Nq = chunks*chunk_frames*nb.
  * q_rep, block_rep: fp32 [heads][Nq][head_dim]; frame_rep fp32 [heads][chunks*F][head_dim].
  * k_per_chunk: HOST int32 [chunks] (entry 0 unused), chunks <= 256.  max_sel must be at
- * least chunk_frames*nb and every k_per_chunk entry.
+ * least chunk_frames*nb and every k_per_chunk entry.  Scores are fp32 products summed in
+ * fp32 (on the matrix cores, 32 query blocks at a time, when a chunk's scores fit in LDS;
+ * else as per-row dot products), so selections are exact up to the order of the fp32
+ * additions (near-ties).
  */
 pbsa_status pbsa_score_topk_2lvl(const pbsa_dims* dims, int32_t chunks, int32_t top_frames,
                                  const int32_t* k_per_chunk, const float* q_rep,

@@ -25,23 +25,26 @@ def dev(x):
     return torch.from_numpy(np.ascontiguousarray(x)).cuda().to(torch.bfloat16)
 
 
-def shape_of(wl):
+def shape_of(wl, fp8=False):
     return ops.Shape(wl.heads, wl.head_dim, wl.frame_tokens, wl.chunk_frames, wl.window_frames,
-                     wl.capacity, wl.sinks, wl.topk, wl.scale)
+                     wl.capacity, wl.sinks, wl.topk, wl.scale,
+                     kv_format=ops.PBSA_KV_FP8 if fp8 else ops.PBSA_KV_BF16)
 
 
 def caches_equal(a, b):
-    return all(torch.equal(getattr(a, nm), getattr(b, nm))
-               for nm in ("k", "v", "rep", "block_id", "len"))
+    names = ("k", "v", "rep", "block_id", "len") + (("kv_scale",) if a.kv_scale is not None
+                                                    else ())
+    return all(torch.equal(getattr(a, nm), getattr(b, nm)) for nm in names)
 
 
-@pytest.mark.parametrize("name,passes,heads,rows", [
-    ("tiny", 3, (0,), None),
-    ("wan_5s", 4, (0, 7), "sampled"),
+@pytest.mark.parametrize("name,passes,heads,rows,fp8", [
+    ("tiny", 3, (0,), None, False),
+    ("wan_5s", 4, (0, 7), "sampled", False),
+    ("wan_5s", 2, (3,), "sampled", True),
 ])
-def test_chunk_step_fused_and_graph(name, passes, heads, rows):
+def test_chunk_step_fused_and_graph(name, passes, heads, rows, fp8):
     wl, seed = synth.WORKLOADS[name], synth.SEEDS[name]
-    shape = shape_of(wl)
+    shape = shape_of(wl, fp8)
     sch = orc.Schedule(wl.frame_tokens, wl.block, wl.chunk_frames, wl.window_frames,
                        wl.capacity, wl.sinks, wl.topk, wl.scale)
     seq = runtime.PersistentLayer(shape, passes=passes)
@@ -52,11 +55,11 @@ def test_chunk_step_fused_and_graph(name, passes, heads, rows):
     T = shape.chunk_tokens
     staging = [tuple(torch.empty(T, wl.heads, wl.head_dim, dtype=torch.bfloat16, device="cuda")
                      for _ in range(3)) for _ in range(passes)]
-    ros = {h: orc.PersistentRollout(sch, wl.head_dim) for h in heads}
+    ros = {h: orc.PersistentRollout(sch, wl.head_dim, kv_fp8=fp8) for h in heads}
     last = wl.measured_chunk
     resync = 0
     for c in range(last + 1):
-        say(f"[chunk step {name}, {passes} passes] chunk {c}")
+        say(f"[chunk step {name}{' fp8' if fp8 else ''}, {passes} passes] chunk {c}")
         host = [synth.pass_qkv(wl, seed, c, p, passes) for p in range(passes)]
         ps = [tuple(dev(x) for x in qkv) for qkv in host]
         for buf, src in zip(staging, ps):

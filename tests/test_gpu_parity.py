@@ -433,29 +433,12 @@ def decomposed_reference(q, k, v, dout, allowed, n, B, scale, qblocks=None, kv_b
     return O, L, dQ, dK, dV
 
 
-def two_level_check(wl, seed, grad_check="full", rows_fn=None, kv_blocks_fn=None,
-                    whole_heads=()):
-    F, n, nb, H, d = wl.chunk_frames, wl.frame_tokens, wl.nb, wl.heads, wl.head_dim
+def check_two_level_selection(wl, q, k, clip, sel, nsel, ks):
+    """Every query block's two-level selection against the oracle's (frame-level near-ties:
+    every valid frame set is a candidate explanation; block-level near-ties through
+    check_topk); also the pooled representatives.  Returns (near-tie rows, selections)."""
+    F, n, nb, H = wl.chunk_frames, wl.frame_tokens, wl.nb, wl.heads
     chunks = wl.clip_chunks
-    shape = shape_of(wl)
-    q, k, v = synth.clip_qkv(wl, seed)
-    T = q.shape[0]
-    alphas = synth.clip_alphas(wl, seed)
-    ks = runtime.cag_budgets(alphas, wl.topk, chunks)
-    max_sel = max(max(ks), F * nb)
-    clip = runtime.TwoLevelClip(shape, chunks, wl.top_frames, max_sel)
-    qd, kd, vd = dev(q), dev(k), dev(v)
-    dout = synth.clip_dout(wl, seed, T)
-    dod = dev(dout)
-    say(f"[two-level {wl.name}] select/forward/backward")
-    clip.select(qd, kd, ks)
-    clip.forward(qd, kd, vd)
-    clip.backward(qd, kd, vd, dod)
-    torch.cuda.synchronize()
-    sel = clip.sel.cpu().numpy()
-    nsel = clip.nsel.cpu().numpy()
-    # the selection passes the library's own host-side check
-    ops.pbsa_check_selection_2lvl(shape, chunks, sel, nsel)
     near_rows = 0
     gsel_all = []
     for h in range(H):
@@ -499,6 +482,33 @@ def two_level_check(wl, seed, grad_check="full", rows_fn=None, kv_blocks_fn=None
                     continue
             assert ok, f"head {h} row {r}: selection {got} not a valid two-level top-k"
         gsel_all.append(gsel)
+    return near_rows, gsel_all
+
+
+def two_level_check(wl, seed, grad_check="full", rows_fn=None, kv_blocks_fn=None,
+                    whole_heads=()):
+    F, n, nb, H, d = wl.chunk_frames, wl.frame_tokens, wl.nb, wl.heads, wl.head_dim
+    chunks = wl.clip_chunks
+    shape = shape_of(wl)
+    q, k, v = synth.clip_qkv(wl, seed)
+    T = q.shape[0]
+    alphas = synth.clip_alphas(wl, seed)
+    ks = runtime.cag_budgets(alphas, wl.topk, chunks)
+    max_sel = max(max(ks), F * nb)
+    clip = runtime.TwoLevelClip(shape, chunks, wl.top_frames, max_sel)
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    dout = synth.clip_dout(wl, seed, T)
+    dod = dev(dout)
+    say(f"[two-level {wl.name}] select/forward/backward")
+    clip.select(qd, kd, ks)
+    clip.forward(qd, kd, vd)
+    clip.backward(qd, kd, vd, dod)
+    torch.cuda.synchronize()
+    sel = clip.sel.cpu().numpy()
+    nsel = clip.nsel.cpu().numpy()
+    # the selection passes the library's own host-side check
+    ops.pbsa_check_selection_2lvl(shape, chunks, sel, nsel)
+    near_rows, gsel_all = check_two_level_selection(wl, q, k, clip, sel, nsel, ks)
     o = host(clip.o)
     lse = clip.lse.cpu().numpy()
     dq, dk, dv = host(clip.dq), host(clip.dk), host(clip.dv)
@@ -601,6 +611,26 @@ def test_two_level_long_clip_split_items_full_gradients():
     wl = synth.Workload("train_long", 2, 128, 64, 64, 4, 0, 0, 0, 0, 64, clip_chunks=64,
                         top_frames=2)
     two_level_check(wl, 34, grad_check="decomposed")
+
+
+def test_two_level_selection_long_clip_row_parallel():
+    # 16 chunks of 3 frames of 1560 tokens: 1200 blocks a late chunk can see, more than the
+    # matrix-core selection keeps in LDS for 32 query blocks, so the row-parallel selection
+    # runs; every query block of both heads against the oracle
+    wl = synth.Workload("train_wide", 2, 64, 64, 1560, 3, 0, 0, 0, 0, 48, clip_chunks=16,
+                        top_frames=8)
+    F, nb = wl.chunk_frames, wl.nb
+    q, k, _ = synth.clip_qkv(wl, 36)
+    ks = runtime.cag_budgets(synth.clip_alphas(wl, 36), wl.topk, wl.clip_chunks)
+    clip = runtime.TwoLevelClip(shape_of(wl), wl.clip_chunks, wl.top_frames,
+                                max(max(ks), F * nb))
+    say("[two-level selection, 48 frames]")
+    clip.select(dev(q), dev(k), ks)
+    torch.cuda.synchronize()
+    sel, nsel = clip.sel.cpu().numpy(), clip.nsel.cpu().numpy()
+    ops.pbsa_check_selection_2lvl(shape_of(wl), wl.clip_chunks, sel, nsel)
+    near, _ = check_two_level_selection(wl, q, k, clip, sel, nsel, ks)
+    say(f"  near-tie rows: {near}")
 
 
 def test_bwd_is_deterministic():
