@@ -671,6 +671,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
     const uint32_t o = (tok ? id * xrow : id * kCacheBlockBytes) + 32 * half * stride;
     hr.len = half_len(e, half);
     hr.f8 = false;
+    hr.ks = hr.vs = 1.f;
     if (hr.len > 0) {
       hr.k = (tok ? xk_h : ck_h) + o;
       hr.v = (tok ? xv_h : cv_h) + o;
