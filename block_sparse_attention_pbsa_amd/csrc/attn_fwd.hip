@@ -748,6 +748,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
     __amdgpu_buffer_rsrc_t kb, vb;  // dma_base(hr.k), dma_base(hr.v)
     uint32_t k, v0, v1;   // lane offsets of K, and of V rows (l >> 2) and 16 + (l >> 2)
     uint32_t fk, fv;      // (FP8 slot) lane offsets of this lane's 32 K and 32 V codes
+    uint32_t flast;       // (FP8 slot) the last valid row
   };
   auto offsets = [&](const HalfRef& hr) {
     const uint32_t last = static_cast<uint32_t>(hr.len > 0 ? hr.len - 1 : 0);
@@ -760,11 +761,12 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
     o.v1 = min(16u + v_rowl, last) * hr.stride + v_colb + 32u * p0 + 3072u;
     if constexpr (FP8) {
       // the same rows and channels as the wave's bf16 pieces, as codes: K rows
-      // 16 (w & 1) + (l & 15), channels 32 (l >> 4) + [0, 32); V rows l >> 1, channels
-      // 64 (w & 1) + 32 (l & 1) + [0, 32)
+      // 16 (w & 1) + (l & 15), channels 32 (l >> 4) + [0, 32); V rows (l >> 3) + 8 i
+      // (load i), channels 64 (w & 1) + 8 (l & 7) + [0, 8), so that each decoded V store
+      // of the wave fills two contiguous 512-byte runs of the tile
       o.fk = min(16u * (w & 1) + k_rowl, last) * hr.stride + 32u * (l >> 4) + 3072u;
-      o.fv = min(static_cast<uint32_t>(l >> 1), last) * hr.stride + 64u * (w & 1) +
-             32u * (l & 1) + 3072u;
+      o.fv = 64u * (w & 1) + 8u * (l & 7) + 3072u;  // + row offset per load
+      o.flast = last;
     }
     return o;
   };
@@ -796,8 +798,9 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
         vscale = hr.vs;
       }
       if (hr.f8) {
+        const uint32_t row = min(static_cast<uint32_t>(l >> 3) + 8u * i, o.flast);
         vpend[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                                                 o.vb, o.fv + 8u * i, 0, 0));
+                                                 o.vb, o.fv + row * hr.stride, 0, 0));
         return;
       }
     }
@@ -829,9 +832,11 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
                        d[0], d[1]);
         decode_e4m3x16(u32x4{vpend[2][0], vpend[2][1], vpend[3][0], vpend[3][1]}, vscale,
                        d[2], d[3]);
-        char* base = buf[tw] + 2048 * (2 * (w & 1) + (l & 1)) + 64 * (l >> 1);
+        // row (l >> 3) + 8 j, segment 2 (w & 1) + ((l & 7) >> 2), 16-byte chunk l & 3
+        char* base = buf[tw] + 2048 * (2 * (w & 1) + ((l & 7) >> 2)) + 64 * (l >> 3) +
+                     16 * (l & 3);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(base + 16 * j) = d[j];
+        for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(base + 512 * j) = d[j];
       }
     }
   };
