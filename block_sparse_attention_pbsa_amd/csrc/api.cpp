@@ -320,6 +320,10 @@ size_t pbsa_workspace_bytes(const pbsa_dims* dims, int32_t op, int32_t arg, int3
     if (check_dims(dims, 0) != PBSA_OK) return 0;
     return pbsa::attn_bwd_persistent_workspace(*dims);
   }
+  if (op == PBSA_OP_ATTN_FWD_FP8) {
+    if (check_dims(dims, 0) != PBSA_OK || dims->kv_format != PBSA_KV_FP8) return 0;
+    return pbsa::attn_fwd_f8_workspace(*dims);
+  }
   if (op == PBSA_OP_ATTN_BWD) {
     if (check_dims(dims, 1) != PBSA_OK || arg < 1 || arg2 < 1) return 0;
     return pbsa::attn_bwd_workspace(*dims, arg, arg2);
@@ -399,6 +403,41 @@ pbsa_status pbsa_attn_fwd(const pbsa_dims* dims, pbsa_tensor q, const pbsa_cache
                                                      pbsa::tok_in(chunk_v), sel,
                                                      pbsa::tok_out(o), lse, stream_of(stream)),
                     "attn_fwd");
+}
+
+pbsa_status pbsa_attn_fwd_fp8(const pbsa_dims* dims, pbsa_tensor q, const pbsa_cache* cache,
+                              pbsa_tensor chunk_k, pbsa_tensor chunk_v, const int32_t* sel,
+                              pbsa_tensor o, float* lse, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  PBSA_TRY(check_dims(dims, 0));
+  if (dims->kv_format != PBSA_KV_FP8)
+    return fail(PBSA_ERR_UNSUPPORTED, "attn_fwd_fp8 takes an FP8 cache (kv_format PBSA_KV_FP8)");
+  PBSA_TRY(check_cache(cache, dims));
+  PBSA_TRY(check_tok(q, "q", dims->head_dim));
+  PBSA_TRY(check_tok(chunk_k, "chunk_k", dims->head_dim));
+  PBSA_TRY(check_tok(chunk_v, "chunk_v", dims->head_dim));
+  PBSA_TRY(check_tok(o, "o", dims->head_dim));
+  const int64_t ctok = int64_t{dims->chunk_frames} * dims->frame_tokens;
+  const int64_t list = int64_t{dims->capacity} + int64_t{dims->chunk_frames} * pbsa::nb_of(*dims) +
+                       2 * int64_t{dims->topk};
+  if (list > pbsa::kAttnListCap)
+    return fail(PBSA_ERR_UNSUPPORTED, "capacity + chunk blocks + 2*topk = %lld exceeds %d",
+                static_cast<long long>(list), pbsa::kAttnListCap);
+  PBSA_TRY(check_span(q, "q", ctok, dims->head_dim));
+  PBSA_TRY(check_span(chunk_k, "chunk_k", ctok, dims->head_dim));
+  PBSA_TRY(check_span(chunk_v, "chunk_v", ctok, dims->head_dim));
+  if (!sel || !lse) return fail(PBSA_ERR_NULL, "sel and lse are required");
+  const size_t need = pbsa::attn_fwd_f8_workspace(*dims);
+  if (!workspace || workspace_bytes < need)
+    return fail(PBSA_ERR_WORKSPACE, "attn_fwd_fp8 needs %zu workspace bytes (got %zu)", need,
+                workspace ? workspace_bytes : static_cast<size_t>(0));
+  if (reinterpret_cast<uintptr_t>(workspace) % 16)
+    return fail(PBSA_ERR_ALIGN, "workspace must be 16-byte aligned");
+  return hip_status(pbsa::launch_attn_fwd_f8(*dims, pbsa::tok_in(q), *cache,
+                                             pbsa::tok_in(chunk_k), pbsa::tok_in(chunk_v), sel,
+                                             pbsa::tok_out(o), lse, workspace,
+                                             stream_of(stream)),
+                    "attn_fwd_fp8");
 }
 
 }  // extern "C"

@@ -40,39 +40,10 @@
 // barrier that publishes the tile -- K two steps ahead (loaded under a PV phase, stored at
 // the end of the next S phase), V one step ahead (loaded under the S phase, stored at the
 // end of the PV phase).  Chunk blocks still go straight into LDS.
-#include "attn_common.h"
+#include "attn_lists.h"
 
 namespace pbsa {
 
-struct FwdArgs {
-  const uint16_t* q;
-  int64_t qts, qhs;
-  uint16_t* o;
-  int64_t ots, ohs;
-  float* lse;
-  int64_t lse_hs;      // tokens per head in lse
-  // persistent-mode cache (unused in the two-level mode)
-  const uint16_t* ck;
-  const uint16_t* cv;
-  const int32_t* bid;
-  const int32_t* blen;
-  int slots, C, W;
-  // token-layout K/V: the current chunk (persistent mode) or the clip (two-level mode)
-  const uint16_t* xk;
-  const uint16_t* xv;
-  int64_t xts, xhs;
-  const int32_t* sel;   // [H][nq][sel_stride]
-  const int32_t* nsel;  // two-level: [H][nq]
-  int sel_stride;
-  int nq, n, nb, H, pairs;
-  float scale;
-  // persistent mode, top-K over the persistent and window blocks together: only the sink
-  // slots [0, S) are attended whole, routed ids may name persistent blocks
-  int route_union, S;
-  // FP8 cache: ck / cv hold E4M3 codes [H][slots][64][D] (one byte each), kv_scale the
-  // power-of-two scale of every slot's K and V ([H][slots][2])
-  const float* kv_scale;
-};
 
 namespace {
 
@@ -491,155 +462,15 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
   const int qrow = 32 * (w & 1) + c32;
   const int64_t t0 = r < a.nq ? block_token0(r, a.nb, a.n) : 0;
   const float c = a.scale * kLog2e;
-  int cntA, cntB, nboth = 0;
-
-  // Block list entries (32 bits): bit 31 = token block of xk/xv (else a cache slot), bits
-  // 24..30 = valid rows, bits 0..23 = the cache slot, or the block's first token.
-  // Shared list (persistent mode): occupied P slots in slot order, then the chunk's
-  // blocks, then the routed blocks that A and B have in common (kept at the end of A's
-  // list area, last to first).  Private lists: the routed blocks of A only and of B only.
+  // (pids: union routing's lookups of persistent block ids, staged in a V tile; rawA/rawB:
+  // the routed ids, staged in two K tiles; no gather has targeted them yet, and the V tiles
+  // are cleared after the lists are built)
+  const FwdLists fl = build_lists<PERSIST, false>(
+      a, h, rA, rB, lists, wave_cnt, part_cnt, n_list, reinterpret_cast<int32_t*>(&kb0[0][0]),
+      reinterpret_cast<int32_t*>(&kb1[0][0]), reinterpret_cast<int32_t*>(&vb1[0][0]));
+  const int cntA = fl.cntA, cntB = fl.cntB, nPq = fl.nPq, nshared = fl.nshared;
   constexpr uint32_t kCacheBlockBytes = kBlock * D * (FP8 ? 1 : 2);
   const uint32_t xrow = static_cast<uint32_t>(a.xts * 2);
-  auto tok_entry = [&](int g) {
-    const int f = g / a.nb, jj = g - f * a.nb;
-    return 0x80000000u | (static_cast<uint32_t>(block_len(jj, a.n)) << 24) |
-           static_cast<uint32_t>(f * a.n + kBlock * jj);
-  };
-  auto slot_entry = [&](int slot, int len) {
-    return (static_cast<uint32_t>(len) << 24) | static_cast<uint32_t>(slot);
-  };
-  uint32_t* shared_list = lists;
-  uint32_t* listA = lists + (PERSIST ? a.C + a.nq : 0);
-  uint32_t* listB = listA + a.sel_stride;
-  int nshared = 0;
-  // (union routing) the head's persistent block ids, staged in a V tile (no gather has
-  // targeted it yet; the V tiles are cleared after the lists are built) for the lookups of
-  // routed persistent blocks below
-  int32_t* pids = reinterpret_cast<int32_t*>(&vb1[0][0]);
-  if (PERSIST) {
-    if (t == 0) n_list = 0;
-    const int32_t* bh = a.bid + static_cast<int64_t>(h) * a.slots;
-    const int32_t* lh = a.blen + static_cast<int64_t>(h) * a.slots;
-    if (a.route_union)
-      for (int s = t; s < a.C; s += 256) pids[s] = bh[s];
-    __syncthreads();
-    // slots attended whole: every persistent slot, or only the sinks' (union routing)
-    const int whole = a.route_union ? a.S : a.C;
-    for (int s0 = 0; s0 < whole; s0 += 256) {
-      const int s = s0 + t;
-      const bool valid = s < whole && bh[s] >= 0;
-      const unsigned long long m = __ballot(valid);
-      if (l == 0) wave_cnt[w] = __popcll(m);
-      __syncthreads();
-      int off = n_list;
-      for (int u = 0; u < w; ++u) off += wave_cnt[u];
-      if (valid) shared_list[off + __popcll(m & ((1ull << l) - 1ull))] = slot_entry(s, lh[s]);
-      __syncthreads();
-      if (t == 0) n_list += wave_cnt[0] + wave_cnt[1] + wave_cnt[2] + wave_cnt[3];
-      __syncthreads();
-    }
-    const int nP = __builtin_amdgcn_readfirstlane(n_list);
-    for (int b = t; b < a.nq; b += 256) shared_list[nP + b] = tok_entry(b);
-    nshared = nP + a.nq;
-  }
-  // private lists; routed ids are ascending with -1 padding at the end (persistent) or
-  // counted by nsel (two-level)
-  auto entry = [&](int g) {
-    // (two-level mode) an id outside the clip is an empty entry
-    if (!PERSIST) return g >= 0 && g < a.nq ? tok_entry(g) : 0x80000000u;
-    const int f = g / a.nb, jj = g - f * a.nb;
-    int slot = a.C + (f % a.W) * a.nb + jj;
-    if (a.route_union && a.bid[static_cast<int64_t>(h) * a.slots + slot] != g) {
-      // not in the window: a persistent block (an id the cache does not hold becomes an
-      // empty entry, which contributes nothing)
-      int found = -1;
-      for (int ps = a.S; ps < a.C; ++ps)
-        if (pids[ps] == g) {
-          found = ps;
-          break;
-        }
-      if (found < 0) return slot_entry(0, 0);
-      slot = found;
-    }
-    return slot_entry(slot, a.blen[static_cast<int64_t>(h) * a.slots + slot]);
-  };
-  const int32_t* sa = a.sel + (static_cast<int64_t>(h) * a.nq + rA) * a.sel_stride;
-  const int32_t* sb = a.sel + (static_cast<int64_t>(h) * a.nq + rB) * a.sel_stride;
-  {
-    // Split A's and B's routed sets into A only, B only and both.  The ascending ids are
-    // staged in two K tiles (no gather has targeted them yet) and looked up by binary
-    // search; each part is compacted in id order with ballots, so the lists (and the
-    // summation order) do not depend on timing.
-    int32_t* rawA = reinterpret_cast<int32_t*>(&kb0[0][0]);
-    int32_t* rawB = reinterpret_cast<int32_t*>(&kb1[0][0]);
-    const int na = PERSIST ? a.sel_stride : a.nsel[static_cast<int64_t>(h) * a.nq + rA];
-    const int nbb = rB >= a.nq ? 0 : PERSIST ? a.sel_stride
-                                             : a.nsel[static_cast<int64_t>(h) * a.nq + rB];
-    for (int j = t; j < a.sel_stride; j += 256) {
-      rawA[j] = j < na ? sa[j] : -1;
-      rawB[j] = j < nbb ? sb[j] : -1;
-    }
-    __syncthreads();
-    int ca = 0, cb = 0;
-    for (int j = l; j < a.sel_stride; j += 64) {
-      ca += rawA[j] >= 0;
-      cb += rawB[j] >= 0;
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      ca += __shfl_xor(ca, o, 64);
-      cb += __shfl_xor(cb, o, 64);
-    }
-    const int nA = __builtin_amdgcn_readfirstlane(ca);
-    const int nB = __builtin_amdgcn_readfirstlane(cb);
-    auto contains = [](const int32_t* ids, int n_ids, int g) {
-      int lo = 0, hi = n_ids;
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (ids[mid] < g) lo = mid + 1;
-        else hi = mid;
-      }
-      return lo < n_ids && ids[lo] == g;
-    };
-    int oa = 0, ob = 0, oi = 0;
-    const unsigned long long below = (1ull << l) - 1ull;
-    for (int j0 = 0; j0 < a.sel_stride; j0 += 256) {
-      const int j = j0 + t;
-      const int ga = j < nA ? rawA[j] : -1;
-      const int gb = j < nB ? rawB[j] : -1;
-      const bool both = ga >= 0 && contains(rawB, nB, ga);
-      const bool a_only = ga >= 0 && !both;
-      const bool b_only = gb >= 0 && !contains(rawA, nA, gb);
-      const unsigned long long ma = __ballot(a_only), mb = __ballot(b_only), mi = __ballot(both);
-      if (l == 0) {
-        part_cnt[w][0] = __popcll(ma);
-        part_cnt[w][1] = __popcll(mb);
-        part_cnt[w][2] = __popcll(mi);
-      }
-      __syncthreads();
-      int pa = oa, pb = ob, pi = oi;
-      for (int u = 0; u < 4; ++u) {
-        if (u < w) {
-          pa += part_cnt[u][0];
-          pb += part_cnt[u][1];
-          pi += part_cnt[u][2];
-        }
-        oa += part_cnt[u][0];
-        ob += part_cnt[u][1];
-        oi += part_cnt[u][2];
-      }
-      if (a_only) listA[pa + __popcll(ma & below)] = entry(ga);
-      if (b_only) listB[pb + __popcll(mb & below)] = entry(gb);
-      if (both) listA[a.sel_stride - 1 - (pi + __popcll(mi & below))] = entry(ga);
-      __syncthreads();
-    }
-    cntA = __builtin_amdgcn_readfirstlane(oa);
-    cntB = __builtin_amdgcn_readfirstlane(ob);
-    nboth = __builtin_amdgcn_readfirstlane(oi);
-  }
-  const int nPq = nshared;  // P and chunk entries (persistent mode)
-  nshared += nboth;
-  __syncthreads();
   // a shared step takes both halves of one shared block; a private step takes one half
   // of A's next routed block (X) and the same half of B's (Y).  The shared phase is
   // padded to an even number of steps (an empty step) so that both phases alternate the
@@ -695,7 +526,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
   // they are decoded, so the LDS read's latency is never waited for.
   // (Indices into `lists` itself, not pointers chosen at run time: the compiler then still
   // sees that these reads cannot touch a tile being gathered and adds no wait for them.)
-  const int offA = static_cast<int>(listA - lists), offB = offA + a.sel_stride;
+  const int offA = fl.offA, offB = fl.offB;
   auto fetch = [&](int s, uint32_t& ex, uint32_t& ey) {
     ex = 0;
     ey = 0;

@@ -45,6 +45,11 @@ hipError_t launch_attn_fwd_fp8(const pbsa_dims& d, TokIn q, const pbsa_cache& c,
                                TokIn cv, const int32_t* sel, TokOut o, float* lse,
                                hipStream_t s);
 
+size_t attn_fwd_f8_workspace(const pbsa_dims& d);
+hipError_t launch_attn_fwd_f8(const pbsa_dims& d, TokIn q, const pbsa_cache& c, TokIn ck,
+                              TokIn cv, const int32_t* sel, TokOut o, float* lse,
+                              void* workspace, hipStream_t s);
+
 hipError_t launch_probe_mfma(int64_t iters, float* out, hipStream_t s);
 hipError_t launch_probe_fp8_decode(const uint8_t* codes, const float* scales, uint16_t* out,
                                    int n, hipStream_t s);

@@ -24,6 +24,7 @@ PBSA_OK = 0
 PBSA_OP_MEMORY_UPDATE = 1
 PBSA_OP_ATTN_BWD = 2
 PBSA_OP_ATTN_BWD_PERSISTENT = 3
+PBSA_OP_ATTN_FWD_FP8 = 4
 PBSA_ROUTE_WINDOW = 0
 PBSA_ROUTE_UNION = 1
 PBSA_KV_BF16 = 0
@@ -89,6 +90,8 @@ _SIGS = {
                    ctypes.c_int),
     "pbsa_attn_fwd": ([ctypes.POINTER(Dims), Tensor, ctypes.POINTER(CacheC), Tensor, Tensor, _P,
                        Tensor, _P, _P], ctypes.c_int),
+    "pbsa_attn_fwd_fp8": ([ctypes.POINTER(Dims), Tensor, ctypes.POINTER(CacheC), Tensor, Tensor,
+                           _P, Tensor, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "pbsa_memory_update": ([ctypes.POINTER(Dims), _P, ctypes.POINTER(CacheC), Tensor, Tensor, _P,
                             _P, ctypes.c_size_t, _P], ctypes.c_int),
     "pbsa_memory_select": ([ctypes.POINTER(Dims), _P, ctypes.POINTER(CacheC), _P, ctypes.c_size_t,
@@ -311,6 +314,22 @@ def pbsa_attn_fwd(shape: Shape, q, cache: Cache, chunk_k, chunk_v, sel, o, lse):
     _check("pbsa_attn_fwd", lib().pbsa_attn_fwd(ctypes.byref(shape.c()), qt,
                                                 ctypes.byref(cache.c()), kt, vt, _ptr(sel), ot,
                                                 _ptr(lse), _stream()))
+
+
+def pbsa_attn_fwd_fp8(shape: Shape, q, cache: Cache, chunk_k, chunk_v, sel, o, lse, workspace):
+    """pbsa_attn_fwd over an FP8 cache in FP8 arithmetic (pbsa.h); workspace: uint8 device
+    tensor of at least pbsa_workspace_bytes(shape, PBSA_OP_ATTN_FWD_FP8) bytes."""
+    H, d, T = shape.heads, shape.head_dim, shape.chunk_tokens
+    qt = _tok(q, "q", T, H, d)
+    kt = _tok(chunk_k, "chunk_k", T, H, d)
+    vt = _tok(chunk_v, "chunk_v", T, H, d)
+    ot = _tok(o, "o", T, H, d)
+    _contig(sel, "sel", torch.int32, (H, shape.nq, shape.topk))
+    _contig(lse, "lse", torch.float32, (H, T))
+    _dev(workspace, "workspace", torch.uint8)
+    _check("pbsa_attn_fwd_fp8", lib().pbsa_attn_fwd_fp8(
+        ctypes.byref(shape.c()), qt, ctypes.byref(cache.c()), kt, vt, _ptr(sel), ot, _ptr(lse),
+        _ptr(workspace), workspace.numel(), _stream()))
 
 
 def pbsa_probe_gather(shape: Shape, q, cache: Cache, chunk_k, chunk_v, sel):

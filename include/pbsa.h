@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define PBSA_ABI_VERSION 2
+#define PBSA_ABI_VERSION 3
 
 typedef enum pbsa_status {
   PBSA_OK = 0,
@@ -180,9 +180,14 @@ pbsa_status pbsa_check_selection(const pbsa_dims* dims, const int32_t* block_id,
 pbsa_status pbsa_check_selection_2lvl(const pbsa_dims* dims, int32_t chunks, const int32_t* sel,
                                       const int32_t* nsel, int32_t max_sel);
 
-enum { PBSA_OP_MEMORY_UPDATE = 1, PBSA_OP_ATTN_BWD = 2, PBSA_OP_ATTN_BWD_PERSISTENT = 3 };
-/* Workspace bytes a call needs.  MEMORY_UPDATE and ATTN_BWD_PERSISTENT: `arg`, `arg2`
- * unused.  ATTN_BWD: `arg` = clip chunks, `arg2` = max_sel. */
+enum {
+  PBSA_OP_MEMORY_UPDATE = 1,
+  PBSA_OP_ATTN_BWD = 2,
+  PBSA_OP_ATTN_BWD_PERSISTENT = 3,
+  PBSA_OP_ATTN_FWD_FP8 = 4
+};
+/* Workspace bytes a call needs.  MEMORY_UPDATE, ATTN_BWD_PERSISTENT and ATTN_FWD_FP8: `arg`,
+ * `arg2` unused.  ATTN_BWD: `arg` = clip chunks, `arg2` = max_sel. */
 size_t pbsa_workspace_bytes(const pbsa_dims* dims, int32_t op, int32_t arg, int32_t arg2);
 
 /* Empties the cache (block_id = -1, len = 0, chunk_index = 0).  K/V/rep are left as they
@@ -239,6 +244,31 @@ pbsa_status pbsa_route(const pbsa_dims* dims, pbsa_tensor q, const pbsa_cache* c
 pbsa_status pbsa_attn_fwd(const pbsa_dims* dims, pbsa_tensor q, const pbsa_cache* cache,
                           pbsa_tensor chunk_k, pbsa_tensor chunk_v, const int32_t* sel,
                           pbsa_tensor o, float* lse, void* stream);
+
+/* ---- step 3 in FP8 arithmetic (FP8 cache) --------------------------------------------
+ * Light Forcing, "Key findings" (the sparse attention deployed in FP8).  The attention of
+ * pbsa_attn_fwd over an FP8 cache (dims.kv_format = PBSA_KV_FP8: the cache's E4M3 codes and
+ * power-of-two block scales), computed on FP8 matrix cores instead of after an exact decode
+ * to bf16:
+ *   - each query row is quantized to E4M3 with its own power-of-two scale (the smallest 2^e
+ *     with max|q| <= 448 * 2^e), nearest even;
+ *   - the chunk's K/V blocks are quantized per block and tensor as pbsa_memory_update
+ *     quantizes a cache slot (codes and scales go to the workspace);
+ *   - scores are exact products of the decoded values summed in fp32; the probabilities
+ *     p = exp(scale * s - m) (a per-row offset m with every p <= 448) are rounded to E4M3
+ *     (nearest even) for the product with V, while the row sum adds the unrounded values.
+ * So o differs from the exact attention of the quantized q by at most 2^-4 * sum_j p_j |v_j|
+ * / sum_j p_j per channel (the rounding of p in E4M3's normal range) plus fp32 and bf16
+ * rounding and the subnormal range's absolute 2^-10 per p; lse is that of the quantized q.
+ * Arguments, layouts and errors as pbsa_attn_fwd, plus: kv_format must be PBSA_KV_FP8
+ * (PBSA_ERR_UNSUPPORTED otherwise); workspace: device, 16-byte aligned,
+ * >= pbsa_workspace_bytes(dims, PBSA_OP_ATTN_FWD_FP8, 0, 0) bytes (overwritten;
+ * PBSA_ERR_WORKSPACE if smaller).  Two kernels on `stream`: the chunk's quantization, then
+ * the attention. */
+pbsa_status pbsa_attn_fwd_fp8(const pbsa_dims* dims, pbsa_tensor q, const pbsa_cache* cache,
+                              pbsa_tensor chunk_k, pbsa_tensor chunk_v, const int32_t* sel,
+                              pbsa_tensor o, float* lse, void* workspace, size_t workspace_bytes,
+                              void* stream);
 
 /* ---- step 4: persistent-memory update and window append ------------------------------
  * Sparse Forcing 2.B/2.C (Top-C retention as the window slides, sinks always kept).  With

@@ -360,6 +360,53 @@ def e4m3_quantize_block(x):
     return e4m3_encode(np.asarray(x, dtype=np.float64) / sc), sc
 
 
+# --------------------------------------------------------------------------------------
+# FP8 arithmetic.  [LF] "Key findings": the sparse attention deployed in FP8.  Reading: the
+# queries are rounded to E4M3 row by row (each row with its own power-of-two scale, the
+# rule of a cache block), the chunk's own K/V block by block as the cache stores them, and
+# the attention of those values is exact; the probabilities are rounded to E4M3 before
+# their product with V, on a grid that an implementation's running offset decides, so the
+# reference bounds that rounding instead of reproducing it.
+# --------------------------------------------------------------------------------------
+
+
+def e4m3_rows(x):
+    """Each row of x [T, d] rounded to E4M3 with its own scale (e4m3_block_scale of the row),
+    as decoded values; a row whose scale would fall below 2^-127 (E8M0's smallest, i.e.
+    max|x| < 448 * 2^-128) takes 2^-127."""
+    x = np.asarray(x, dtype=np.float64)
+    out = np.empty_like(x)
+    for t in range(x.shape[0]):
+        sc = max(e4m3_block_scale(x[t]), 2.0 ** -127)
+        out[t] = e4m3_decode(e4m3_encode(x[t] / sc)) * sc
+    return out
+
+
+def fp8_attention(q, K, V, scale: float):
+    """FP8-arithmetic attention of query rows q over keys K, V (already the decoded E4M3
+    values): (O, LSE, bound).
+
+    O, LSE: the exact attention (masked_attention, every key allowed) of e4m3_rows(q).
+    bound[t, c]: how far rounding the probabilities to E4M3 can move O[t, c] when the
+    implementation keeps its row offset within 2^5 of the row max (the row max maps to
+    p >= 2^5 in its units, p <= 448): a p in E4M3's normal range moves by at most 2^-4 p;
+    one in the subnormal range (below 2^-6 in those units, so below 2^-11 pmax in the
+    normalised p) by at most min(p, 2^-10 in those units = 2^-15 pmax):
+        bound = 2^-4 sum_j p_j |V_jc| + sum_{p_j < 2^-11 pmax} min(p_j, 2^-15 pmax) |V_jc|
+    with p the exact normalised probabilities and pmax their row max.
+    """
+    q8 = e4m3_rows(q)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    o, lse = masked_attention(q8, K, V, np.ones((q8.shape[0], K.shape[0]), dtype=bool), scale)
+    p = np.exp(scale * (q8 @ K.T) - lse[:, None])
+    pmax = p.max(axis=1, keepdims=True)
+    aV = np.abs(V)
+    sub = np.where(p < 2.0 ** -11 * pmax, np.minimum(p, 2.0 ** -15 * pmax), 0.0)
+    bound = 2.0 ** -4 * (p @ aV) + sub @ aV
+    return o, lse, bound
+
+
 @dataclass
 class PersistentRollout:
     """Oracle state of one head's rollout: P_t plus the tokens of the blocks it can still use.
@@ -448,6 +495,40 @@ class PersistentRollout:
             oo, ll = masked_attention(np.asarray(q[idx], np.float64), K, V, mask, s.scale)
             o[idx], lse[idx] = oo, ll
         return o, lse
+
+    def attend_fp8(self, q_chunk, k_chunk, v_chunk, sel, rows=None):
+        """attend in FP8 arithmetic over an FP8 cache (kv_fp8): the stored blocks as their
+        decoded codes, the chunk's own blocks quantized per block and tensor like a cache
+        slot, the queries per row (fp8_attention).  Returns (O, LSE, bound) with rows not
+        asked for left as NaN."""
+        if not self.kv_fp8:
+            raise ValueError("FP8 arithmetic reads an FP8 cache")
+        s = self.sch
+        q = np.asarray(q_chunk)
+        base = self.chunk * s.F * s.nb
+        own_k, own_v = {}, {}
+        for b in range(s.F * s.nb):
+            a0, b0 = block_token_range(b, s.n, s.B)
+            kc, ks = e4m3_quantize_block(k_chunk[a0:b0])
+            vc, vs = e4m3_quantize_block(v_chunk[a0:b0])
+            own_k[base + b], own_v[base + b] = e4m3_decode(kc) * ks, e4m3_decode(vc) * vs
+        Tq = q.shape[0]
+        o = np.full((Tq, self.d), np.nan)
+        lse = np.full(Tq, np.nan)
+        bnd = np.full((Tq, self.d), np.nan)
+        want = None if rows is None else set(int(t) for t in rows)
+        for r, allowed in enumerate(self.attended_blocks(sel)):
+            a, b = block_token_range(r, s.n, s.B)
+            idx = [t for t in range(a, b) if want is None or t in want]
+            if not idx:
+                continue
+            K = np.concatenate([own_k[g] if g in own_k else np.asarray(self.tok_k[g], np.float64)
+                                for g in allowed])
+            V = np.concatenate([own_v[g] if g in own_v else np.asarray(self.tok_v[g], np.float64)
+                                for g in allowed])
+            o[idx], lse[idx], bnd[idx] = fp8_attention(np.asarray(q[idx], np.float64), K, V,
+                                                       s.scale)
+        return o, lse, bnd
 
     def attend_grad(self, q_chunk, k_chunk, v_chunk, sel, dout):
         """Gradient of attend's output O (dout = dL/dO) with the selection held constant

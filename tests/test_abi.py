@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     L = ops.lib()
-    assert L.pbsa_abi_version() == 2
+    assert L.pbsa_abi_version() == 3
     assert L.pbsa_status_str(0) == b"ok"
     assert L.pbsa_status_str(5) == b"workspace too small"
     assert L.pbsa_status_str(99) == b"unknown status"

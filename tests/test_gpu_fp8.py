@@ -6,7 +6,9 @@ and tensor.  Checked here: the attention's decode of every code against the form
 definition (bit for bit); rollouts whose persistent sets, routing, slot codes and scales
 match the oracle's after every update (codes and scales bit for bit); and the attention at
 the measured chunk against the oracle's attention over the decoded blocks (the stated
-tolerance; the chunk's own K/V stay bf16).
+tolerance; the chunk's own K/V stay bf16).  The FP8-arithmetic attention (pbsa_attn_fwd_fp8)
+is checked at the same chunk against the oracle's fp8_attention: element by element within
+its bound on the rounding of the probabilities (plus bf16 output rounding), LSE within 1e-3.
 """
 import dataclasses
 
@@ -44,7 +46,7 @@ def test_fp8_decode_matches_the_format():
 TINY128 = synth.Workload("tiny128", 1, 128, 64, 256, 1, 4, 2, 4, 1, 4)
 
 
-def fp8_rollout(wl, seed, heads, rows, union=False):
+def fp8_rollout(wl, seed, heads, rows, union=False, math8=False):
     shape = ops.Shape(wl.heads, wl.head_dim, wl.frame_tokens, wl.chunk_frames, wl.window_frames,
                       wl.capacity, wl.sinks, wl.topk, wl.scale,
                       route_mode=ops.PBSA_ROUTE_UNION if union else ops.PBSA_ROUTE_WINDOW,
@@ -80,6 +82,8 @@ def fp8_rollout(wl, seed, heads, rows, union=False):
                 o = layer.o[:, h].float().cpu().numpy()
                 assert_close_attn(o[idx], o_ref[idx], f"O head {h}")
                 assert np.abs(layer.lse[h].cpu().numpy()[idx] - l_ref[idx]).max() < 1e-3
+            if math8:
+                check_fp8_math(layer, ros, heads, rows, q, k, v, sel)
             return layer, ros
         layer.update(kd, vd)
         torch.cuda.synchronize()
@@ -108,6 +112,31 @@ def fp8_rollout(wl, seed, heads, rows, union=False):
     raise AssertionError("unreachable")
 
 
+def check_fp8_math(layer, ros, heads, rows, q, k, v, sel):
+    """pbsa_attn_fwd_fp8 at the rollout's current chunk against the oracle's FP8 arithmetic."""
+    shape = layer.shape
+    T = shape.chunk_tokens
+    ws = torch.empty(ops.pbsa_workspace_bytes(shape, ops.PBSA_OP_ATTN_FWD_FP8), dtype=torch.uint8,
+                     device="cuda")
+    o8 = torch.full_like(layer.o, float("nan"))
+    l8 = torch.full_like(layer.lse, float("nan"))
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    ops.pbsa_attn_fwd_fp8(shape, qd, layer.cache, kd, vd, layer.sel, o8, l8, ws)
+    torch.cuda.synchronize()
+    for h in heads:
+        gsel = [[int(g) for g in sel[h, r] if g >= 0] for r in range(shape.nq)]
+        idx = np.arange(T) if rows is None else rows(h, T)
+        o_ref, l_ref, bnd = ros[h].attend_fp8(q[:, h], k[:, h], v[:, h], gsel, rows=idx)
+        o = o8[:, h].float().cpu().numpy()[idx]
+        err = np.abs(o - o_ref[idx])
+        tol = bnd[idx] + 2.0 ** -8 * np.abs(o_ref[idx]) + 1e-4
+        say(f"  fp8 arithmetic head {h}: max-abs {err.max():.3e} mean-abs {err.mean():.3e}, "
+            f"max err/tol {(err / tol).max():.3f}, mean bound {bnd[idx].mean():.3e}")
+        assert np.isfinite(o).all()
+        assert np.all(err <= tol), f"head {h}: FP8 O outside its bound"
+        assert np.abs(l8[h].cpu().numpy()[idx] - l_ref[idx]).max() < 1e-3
+
+
 def _sampled(seed):
     def pick(h, T):
         rs = np.random.default_rng(seed + h)
@@ -122,6 +151,15 @@ def test_fp8_rollout_tiny128_all_rows():
 
 def test_fp8_rollout_wan_5s():
     fp8_rollout(synth.WORKLOADS["wan_5s"], synth.SEEDS["wan_5s"], (0, 5, 11), _sampled(8))
+
+
+def test_fp8_arithmetic_tiny128_all_rows():
+    fp8_rollout(TINY128, 43, (0,), None, math8=True)
+
+
+def test_fp8_arithmetic_wan_5s():
+    fp8_rollout(synth.WORKLOADS["wan_5s"], synth.SEEDS["wan_5s"], (1, 6), _sampled(10),
+                math8=True)
 
 
 def test_fp8_rollout_wan_5s_union_routing():

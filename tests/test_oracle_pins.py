@@ -670,3 +670,121 @@ def test_e4m3_dequantized_values_are_exact_in_bf16():
     # relative error of the nearest code: at most half a mantissa step (2^-4)
     big = np.abs(x) >= 2.0 ** -6 * sc
     assert np.all(np.abs(deq - x)[big] <= 2.0 ** -4 * np.abs(x)[big] + 1e-30)
+
+
+# ----------------------------------------------------------------------------- FP8 arithmetic
+def _nearest_grid(y, grid):
+    """Nearest value of a sorted grid to y, ties to the larger |mantissa| parity rule being
+    irrelevant here (the test data avoid exact ties)."""
+    i = np.searchsorted(grid, y)
+    lo = grid[max(i - 1, 0)]
+    hi = grid[min(i, len(grid) - 1)]
+    return lo if abs(y - lo) <= abs(hi - y) else hi
+
+
+def test_e4m3_rows_are_nearest_values_of_each_rows_own_grid():
+    # brute force: each row's values against every E4M3 value times that row's own scale,
+    # the scale being the smallest power of two that holds the row's max
+    vals = orc.e4m3_decode(np.arange(256, dtype=np.uint8))
+    grid = np.sort(np.unique(vals[~np.isnan(vals)]))
+    rs = np.random.default_rng(21)
+    x = rs.standard_normal((12, 40)) * (10.0 ** rs.uniform(-3, 3, (12, 1)))
+    got = orc.e4m3_rows(x)
+    for t in range(x.shape[0]):
+        amax = np.abs(x[t]).max()
+        e = 0
+        while amax > 448 * 2.0 ** e:
+            e += 1
+        while amax <= 448 * 2.0 ** (e - 1):
+            e -= 1
+        for c in range(x.shape[1]):
+            assert got[t, c] == _nearest_grid(x[t, c] / 2.0 ** e, grid) * 2.0 ** e
+
+
+def test_fp8_attention_reduces_to_the_attention_on_exact_grid_values():
+    # queries already on each row's E4M3 grid: the FP8 reference is the plain attention
+    rs = np.random.default_rng(22)
+    q = orc.e4m3_rows(rs.standard_normal((6, 16)))
+    K = orc.e4m3_decode(rs.integers(0, 0x7E, (30, 16)).astype(np.uint8)) * 2.0 ** -4
+    V = rs.standard_normal((30, 16))
+    o, lse, _ = orc.fp8_attention(q, K, V, 0.25)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None], torch.from_numpy(K)[None], torch.from_numpy(V)[None],
+        scale=0.25)[0].numpy()
+    assert np.abs(o - ref).max() < 1e-12
+    s = 0.25 * q @ K.T
+    assert np.abs(lse - np.log(np.exp(s).sum(axis=1))).max() < 1e-12
+
+
+def _simulate_fp8_pv(q8, K, V, scale, rs, head):
+    # an implementation's rounding of p: a row offset with the max mapping to 2^head
+    # (head in [5, 8.8]), p rounded to E4M3 by brute force over the value grid
+    vals = orc.e4m3_decode(np.arange(256, dtype=np.uint8))
+    grid = np.sort(np.unique(vals[~np.isnan(vals)]))
+    s = scale * (q8 @ K.T)
+    out = np.empty((q8.shape[0], V.shape[1]))
+    for t in range(q8.shape[0]):
+        pk = np.exp2((s[t] - s[t].max()) / math.log(2) + head)
+        assert pk.max() <= 448
+        p8 = np.array([_nearest_grid(x, grid) for x in pk])
+        out[t] = (p8 @ V) / pk.sum()
+    return out
+
+
+def test_fp8_attention_bound_covers_simulated_probability_rounding():
+    rs = np.random.default_rng(23)
+    for trial in range(6):
+        q = rs.standard_normal((4, 32)) * 1.5
+        K = rs.standard_normal((400, 32))
+        V = rs.standard_normal((400, 32)) + (0.5 if trial % 2 else 0.0)
+        o, _, bound = orc.fp8_attention(q, K, V, 0.3)
+        q8 = orc.e4m3_rows(q)
+        for head in (5.0, 6.5, 8.5):
+            sim = _simulate_fp8_pv(q8, K, V, 0.3, rs, head)
+            assert np.all(np.abs(sim - o) <= bound * (1 + 1e-9) + 1e-12)
+
+
+def test_fp8_attention_bound_needs_its_subnormal_term():
+    # one dominant key and many keys 16 exp2 units below it (p = 2^-11 against the max's
+    # 2^5), all with V = 1: every small p rounds to zero, so the error is one-signed and
+    # equals the subnormal term; the normal-range term alone does not cover it
+    q = np.zeros((1, 4))
+    q[0, 0] = 1.0
+    K = np.zeros((3001, 4))
+    K[0, 0] = 40.0                      # the dominant key
+    K[1:, 0] = 40.0 - 16.0 * math.log(2) - np.linspace(0, 0.05, 3000)
+    V = np.ones((3001, 4))
+    V[0] = 0.0
+    o, _, bound = orc.fp8_attention(q, K, V, 1.0)
+    q8 = orc.e4m3_rows(q)
+    sim = _simulate_fp8_pv(q8, K, V, 1.0, np.random.default_rng(0), 5.0)
+    err = np.abs(sim - o).max()
+    p = np.exp(q8 @ K.T - orc.fp8_attention(q, K, V, 1.0)[1][:, None])
+    normal_only = 2.0 ** -4 * (p @ np.abs(V)).max()
+    assert err > normal_only                     # the subnormal range matters here
+    assert err <= bound.max() * (1 + 1e-9)       # and the full bound covers it
+
+
+def test_rollout_attend_fp8_quantizes_queries_and_chunk_blocks():
+    # attend_fp8 = attend over the same stored blocks with the queries and the chunk's own
+    # blocks replaced by their quantized values
+    wl = synth.Workload("pin_fp8", 1, 16, 32, 64, 1, 4, 2, 4, 1, 2)
+    sch = orc.Schedule(wl.frame_tokens, wl.block, wl.chunk_frames, wl.window_frames,
+                       wl.capacity, wl.sinks, wl.topk, wl.scale, False)
+    ro = orc.PersistentRollout(sch, wl.head_dim, kv_fp8=True)
+    for c in range(4):
+        q, k, v = synth.chunk_qkv(wl, 5, c)
+        rt = ro.select(q[:, 0])
+        if c == 3:
+            o8, l8, b8 = ro.attend_fp8(q[:, 0], k[:, 0], v[:, 0], rt["sel"])
+            kq, vq = np.empty_like(k[:, 0], dtype=np.float64), np.empty_like(v[:, 0], dtype=np.float64)
+            for b in range(sch.F * sch.nb):
+                a0, b0 = orc.block_token_range(b, sch.n, sch.B)
+                kc, ks = orc.e4m3_quantize_block(k[a0:b0, 0])
+                vc, vs = orc.e4m3_quantize_block(v[a0:b0, 0])
+                kq[a0:b0], vq[a0:b0] = orc.e4m3_decode(kc) * ks, orc.e4m3_decode(vc) * vs
+            o, l = ro.attend(orc.e4m3_rows(q[:, 0]), kq, vq, rt["sel"])
+            assert np.abs(o8 - o).max() < 1e-12 and np.abs(l8 - l).max() < 1e-12
+            assert np.all(b8 > 0)
+            return
+        ro.update(rt, k[:, 0], v[:, 0])
