@@ -45,6 +45,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "PBSA ms/chunk + effective TFLOP/s & % MFMA/HBM roofline, 1 MI355X"
 PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP8_TFLOPS = 5000.0      # dense E4M3 MFMA, published
 PEAK_HBM_GBS = 8000.0
 PERSISTENT = ("tiny", "wan_5s", "wan_20s", "wan_1min")
 DESCR = {
@@ -79,6 +80,9 @@ def parse():
                          "--copy-probe run into the traffic file, then exit")
     ap.add_argument("--train-only", action="store_true",
                     help="only the trainable path's extra field (for profiling its kernels)")
+    ap.add_argument("--fp8-only", action="store_true",
+                    help="only the FP8-cache fields at --config: the bf16-arithmetic attention "
+                         "over the decoded cache and the FP8-arithmetic attention")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, copy a 512 MiB buffer 3 times (calibrates the "
                          "FETCH_SIZE / WRITE_SIZE counters against known bytes)")
@@ -198,13 +202,14 @@ def attn_bytes(wl, shape, slots_read):
 
 
 # ------------------------------------------------------------------------------ headline
-def persistent_line(cx, name, steps, warmup, oracle_heads=(), kv_format=0, route_mode=0):
+def persistent_line(cx, name, steps, warmup, oracle_heads=(), kv_format=0, route_mode=0,
+                    fp8_arithmetic=False):
     """Bootstrap `name`'s rollout to its measured chunk, then time `steps` successive
     chunks.  Returns (result dict, layer, device chunks, oracle rollouts, host measured chunk)."""
     ops, runtime, synth = cx.ops, cx.runtime, cx.synth
     wl, seed = synth.WORKLOADS[name], synth.SEEDS[name]
     shape = shape_of(ops, wl, kv_format, route_mode)
-    layer = runtime.PersistentLayer(shape)
+    layer = runtime.PersistentLayer(shape, fp8_arithmetic=fp8_arithmetic)
     layer.reset()
     m = wl.measured_chunk
     ros = {}
@@ -304,6 +309,22 @@ def persistent_line(cx, name, steps, warmup, oracle_heads=(), kv_format=0, route
     restore(layer.cache, snap)
     cx.sync()
     return res, layer, chunks, ros, measured_host, (sum(flop), sum(attn_ms), ms_step, abytes)
+
+
+def fp8_lines(cx, name, steps, warmup):
+    """The FP8 cache at `name`: the attention over the decoded codes (bf16 arithmetic) and
+    pbsa_attn_fwd_fp8 (FP8 arithmetic, also reported against the FP8 peak)."""
+    out = {}
+    for tag, f8 in (("fp8_cache", False), ("fp8_arithmetic", True)):
+        r, lay, ch, _, _, _ = persistent_line(cx, name, steps, warmup, kv_format=1,
+                                              fp8_arithmetic=f8)
+        r["workload"] += f"; {tag.replace('_', ' ')}"
+        if f8:
+            r["attn_fwd_frac_fp8_peak"] = round(r["attn_fwd_tflops"] / PEAK_FP8_TFLOPS, 4)
+        out[f"{name}_{tag}"] = r
+        del lay, ch
+        cx.torch.cuda.empty_cache()
+    return out
 
 
 def rollout_per_chunk(cx, name):
@@ -454,6 +475,9 @@ def main():
         return
     name = args.config
     wl = cx.synth.WORKLOADS[name]
+    if args.fp8_only:
+        print(json.dumps(fp8_lines(cx, name, args.steps, args.warmup)), flush=True)
+        return
     cpu_heads = ()
     if not args.no_cpu:
         n_h = args.cpu_heads or {"tiny": 1, "wan_5s": 12, "wan_20s": 8, "wan_1min": 8}[name]
@@ -511,14 +535,15 @@ def main():
             extras[other] = r
             del lay, ch
             cx.torch.cuda.empty_cache()
-        # FP8 cache (E4M3 codes, power-of-two scale per block) and routing over P and the
-        # window together, on the headline workload
-        for tag, kvf, rm in (("fp8_cache", 1, 0), ("union_routing", 0, 1)):
-            r, lay, ch, _, _, _ = persistent_line(cx, name, 10, 3, kv_format=kvf, route_mode=rm)
-            r["workload"] += f"; {tag.replace('_', ' ')}"
-            extras[f"{name}_{tag}"] = r
-            del lay, ch
-            cx.torch.cuda.empty_cache()
+        # FP8 cache (E4M3 codes, power-of-two scale per block; the attention in bf16 over
+        # the decoded codes, and in FP8 arithmetic) and routing over P and the window
+        # together, on the headline workload
+        extras.update(fp8_lines(cx, name, 10, 3))
+        r, lay, ch, _, _, _ = persistent_line(cx, name, 10, 3, route_mode=1)
+        r["workload"] += "; union routing"
+        extras[f"{name}_union_routing"] = r
+        del lay, ch
+        cx.torch.cuda.empty_cache()
         extras["wan_20s_rollout"] = rollout_per_chunk(cx, "wan_20s")
         cx.torch.cuda.empty_cache()
         extras[f"{name}_T{args.passes}"] = multi_pass(cx, name, args.passes, 6)

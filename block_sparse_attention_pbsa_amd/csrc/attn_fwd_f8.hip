@@ -15,8 +15,10 @@
 //     O^T += V^T P^T on the same MFMA, while the row sum adds the unrounded fp32 values.  The
 //     offset m is raised lazily, as in the bf16 kernel, but so that no p exceeds 448 (E4M3's
 //     largest value): a lane whose 32 exponentials of a block sum to more than 448 raises m to
-//     its row max minus 5 (the max then maps to p = 32) and redoes the block.  A block whose
-//     sum stays at or below 448 has every p <= 448.
+//     its row max minus 3 (the max then maps to p = 8) and redoes the block.  A block whose
+//     sum stays at or below 448 has every p <= 448; with the max at 8 the sum of a block's 32
+//     values stays below 448 until the row max grows (a larger head room, 2^5, re-raised on
+//     most blocks of keys that score alike and cost a quarter of the kernel's time).
 //
 // gfx950 design: the bf16 kernel's workgroup (two query blocks A, B of one head, four waves of
 // 32 query rows; shared blocks gathered once for both) and pipeline (K two steps ahead, V one
@@ -26,8 +28,8 @@
 // the MFMA work is half the bf16 kernel's (2 + 2 scaled FP8 MFMAs of 64 cycles per 32-key tile
 // pair against 8 + 8 bf16 MFMAs of 32), the LDS traffic too; the softmax's VALU work is the
 // same.  Tiles are row-major [64 keys][128 B] in LDS with the 16-byte chunk c of row r at
-// position c ^ swz8(r), swz8(r) = (r % 8) ^ 4 ((r / 8) % 2), filled straight from HBM/L2 by
-// buffer_load ... lds (the permutation is in each lane's source address):
+// position c ^ swz8(r) (below), filled straight from HBM/L2 by buffer_load ... lds (the
+// permutation is in each lane's source address):
 //   S^T: A = K (lane l: key l % 32, channels 64 m + 32 (l / 32) + [0, 32), two 16-byte reads),
 //        B = Q (registers, the same channels of the lane's query row);
 //   O^T: A = V^T (lane l: channel l % 32 of a 32-channel tile, 32 keys from four 8-bit
@@ -35,8 +37,6 @@
 //        B = P^T packed from the S^T accumulators: byte 16 t + i of lane l holds accumulator i
 //        of key tile t, i.e. key 32 t + 8 (i / 4) + 4 (l / 32) + i % 4; the V reads take the
 //        same keys in the same byte order, so the contraction pairs them.
-// Both chunk patterns are conflict-free: 8 consecutive rows of one logical chunk sit at 8
-// different positions, and the two 4-row groups of a transposing read at disjoint ones.
 #include "attn_lists.h"
 #include "fp8.h"
 
@@ -55,14 +55,23 @@ constexpr int kTile8 = kBlock * kD8;      // bytes of one block's codes
 constexpr int kPieces8 = kTile8 / 1024;   // gather instructions per block
 constexpr int kHP8 = kPieces8 / 2;        // ... per wave (two waves share a block)
 constexpr float kRaiseSum8 = 448.f;       // largest E4M3 value
-constexpr float kHead8 = 5.f;             // after a raise the row max maps to p = 2^5
+constexpr float kHead8 = 3.f;             // after a raise the row max maps to p = 2^3
 
 template <int N>
 struct B8 {
   static constexpr int value = N;
 };
 
-__device__ __forceinline__ int swz8(int row) { return (row & 7) ^ (4 * ((row >> 3) & 1)); }
+// Chunk position of a row's 16-byte chunks: c ^ swz8(r) with swz8(r) = the bits of
+// u = (r / 2) % 8 with bits 0 and 1 exchanged.  Of 16 consecutive rows, the 8 even ones and
+// the 8 odd ones each take 8 different positions (a K operand read, 16 rows of one chunk per
+// pass, is free of bank conflicts), and the rows a transposing V read takes in one pass
+// ({0, 1, 2, 3, 8, 9, 10, 11} + 4 g) have positions in different aligned pairs (its two
+// chunks' 8-byte halves then fill 32 different bank pairs).
+__device__ __forceinline__ int swz8(int row) {
+  const int u = (row >> 1) & 7;
+  return (u & 4) | ((u & 1) << 1) | ((u >> 1) & 1);
+}
 
 // E8M0 exponent field of a power-of-two float.
 __device__ __forceinline__ int e8m0_of(float pow2) {
@@ -186,7 +195,7 @@ struct RowState8 {
     so.pb[k] = wd;
   }
   // After the 8 stages: a lane whose sum exceeds 448 sends the wave down the rare branch
-  // (row max in-lane and from the other lane half, offset raised to max * c - 5, block
+  // (row max in-lane and from the other lane half, offset raised to max * c - 3, block
   // redone); the first block of every row takes it.
   __device__ __forceinline__ void finish(const f32x16 (&s)[2], Soft& so, float c) {
     asm volatile("" ::"v"(so.pb), "v"(so.ps));
@@ -430,10 +439,10 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f8_kernel(F8Args g) {
   // Gathers: each wave moves kHP8 = 4 of the 8 K pieces and 4 of the 8 V pieces of its block
   // (waves 0, 1: X; 2, 3: Y).  Piece P is rows 8 P .. 8 P + 7; lane l writes LDS byte 16 l of
   // it, i.e. row 8 P + l / 8, position l % 8, which holds logical chunk
-  // (l % 8) ^ (l / 8) ^ 4 (P % 2).
+  // (l % 8) ^ swz8(8 P + l / 8); swz8 depends on the row mod 16, so on P's parity.
   const int p0 = (w & 1) * kHP8;
-  const uint32_t d_even = (l >> 3) * 128u + 16u * static_cast<uint32_t>((l & 7) ^ (l >> 3));
-  const uint32_t d_odd = (l >> 3) * 128u + 16u * static_cast<uint32_t>((l & 7) ^ (l >> 3) ^ 4);
+  const uint32_t d_even = (l >> 3) * 128u + 16u * static_cast<uint32_t>((l & 7) ^ swz8(l >> 3));
+  const uint32_t d_odd = (l >> 3) * 128u + 16u * static_cast<uint32_t>((l & 7) ^ swz8(8 + (l >> 3)));
   const uint32_t vo_even = 1024u * p0 + d_even + 3072u, vo_odd = 1024u * p0 + d_odd + 3072u;
   auto gather = [&](uint8_t (*buf)[kTile8], const uint8_t* src, int i) {
     dma8(i, dma_base8(src), i & 1 ? vo_odd : vo_even, buf[tw] + 1024 * p0);

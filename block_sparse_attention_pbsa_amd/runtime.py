@@ -21,7 +21,7 @@ from . import ops
 
 class PersistentLayer:
     def __init__(self, shape: ops.Shape, device="cuda", passes: int = 1,
-                 device_counter: bool = False):
+                 device_counter: bool = False, fp8_arithmetic: bool = False):
         self.shape = shape
         H, d, nq, T = shape.heads, shape.head_dim, shape.nq, shape.chunk_tokens
         # device_counter: the cache keeps a device copy of its chunk index (needed by the
@@ -39,6 +39,14 @@ class PersistentLayer:
         nbytes = ops.pbsa_workspace_bytes(shape, ops.PBSA_OP_MEMORY_UPDATE)
         self.workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
         self.side = torch.cuda.Stream(device=device)  # default priority
+        # fp8_arithmetic (FP8 cache only): the attention runs pbsa_attn_fwd_fp8, whose
+        # workspace holds the chunk's quantized K/V
+        self.fp8_arithmetic = fp8_arithmetic
+        if fp8_arithmetic:
+            nb8 = ops.pbsa_workspace_bytes(shape, ops.PBSA_OP_ATTN_FWD_FP8)
+            if nb8 == 0:
+                raise ValueError("FP8 arithmetic needs an FP8 cache (kv_format PBSA_KV_FP8)")
+            self.workspace8 = torch.empty(nb8, dtype=torch.uint8, device=device)
 
     def reset(self):
         ops.pbsa_cache_reset(self.shape, self.cache)
@@ -47,6 +55,10 @@ class PersistentLayer:
         ops.pbsa_route(self.shape, q, self.cache, self.q_rep, self.scores, self.sel)
 
     def attend(self, q, k, v, p: int = 0):
+        if self.fp8_arithmetic:
+            ops.pbsa_attn_fwd_fp8(self.shape, q, self.cache, k, v, self.sel, self.os[p],
+                                  self.lses[p], self.workspace8)
+            return
         ops.pbsa_attn_fwd(self.shape, q, self.cache, k, v, self.sel, self.os[p], self.lses[p])
 
     def update(self, k, v):

@@ -257,9 +257,10 @@ pbsa_status pbsa_attn_fwd(const pbsa_dims* dims, pbsa_tensor q, const pbsa_cache
  *   - scores are exact products of the decoded values summed in fp32; the probabilities
  *     p = exp(scale * s - m) (a per-row offset m with every p <= 448) are rounded to E4M3
  *     (nearest even) for the product with V, while the row sum adds the unrounded values.
- * So o differs from the exact attention of the quantized q by at most 2^-4 * sum_j p_j |v_j|
- * / sum_j p_j per channel (the rounding of p in E4M3's normal range) plus fp32 and bf16
- * rounding and the subnormal range's absolute 2^-10 per p; lse is that of the quantized q.
+ * The offset keeps the row max at p >= 8, so o differs from the exact attention of the
+ * quantized q by at most 2^-4 * sum_j p_j |v_j| / sum_j p_j per channel (the rounding of p in
+ * E4M3's normal range) plus fp32 and bf16 rounding and the subnormal range's absolute 2^-10
+ * per p (p below 2^-9 of the row max); lse is that of the quantized q.
  * Arguments, layouts and errors as pbsa_attn_fwd, plus: kv_format must be PBSA_KV_FP8
  * (PBSA_ERR_UNSUPPORTED otherwise); workspace: device, 16-byte aligned,
  * >= pbsa_workspace_bytes(dims, PBSA_OP_ATTN_FWD_FP8, 0, 0) bytes (overwritten;

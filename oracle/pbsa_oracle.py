@@ -382,17 +382,18 @@ def e4m3_rows(x):
     return out
 
 
-def fp8_attention(q, K, V, scale: float):
+def fp8_attention(q, K, V, scale: float, head: int = 3):
     """FP8-arithmetic attention of query rows q over keys K, V (already the decoded E4M3
     values): (O, LSE, bound).
 
     O, LSE: the exact attention (masked_attention, every key allowed) of e4m3_rows(q).
     bound[t, c]: how far rounding the probabilities to E4M3 can move O[t, c] when the
-    implementation keeps its row offset within 2^5 of the row max (the row max maps to
-    p >= 2^5 in its units, p <= 448): a p in E4M3's normal range moves by at most 2^-4 p;
-    one in the subnormal range (below 2^-6 in those units, so below 2^-11 pmax in the
-    normalised p) by at most min(p, 2^-10 in those units = 2^-15 pmax):
-        bound = 2^-4 sum_j p_j |V_jc| + sum_{p_j < 2^-11 pmax} min(p_j, 2^-15 pmax) |V_jc|
+    implementation keeps its row offset so that the row max maps to p >= 2^head (and every
+    p <= 448) in its units: a p in E4M3's normal range moves by at most 2^-4 p; one in the
+    subnormal range (below 2^-6 in those units, so below 2^(-6-head) pmax in the normalised
+    p) by at most min(p, 2^-10 in those units, at most 2^(-10-head) pmax):
+        bound = 2^-4 sum_j p_j |V_jc|
+                + sum_{p_j < 2^(-6-head) pmax} min(p_j, 2^(-10-head) pmax) |V_jc|
     with p the exact normalised probabilities and pmax their row max.
     """
     q8 = e4m3_rows(q)
@@ -402,7 +403,7 @@ def fp8_attention(q, K, V, scale: float):
     p = np.exp(scale * (q8 @ K.T) - lse[:, None])
     pmax = p.max(axis=1, keepdims=True)
     aV = np.abs(V)
-    sub = np.where(p < 2.0 ** -11 * pmax, np.minimum(p, 2.0 ** -15 * pmax), 0.0)
+    sub = np.where(p < 2.0 ** (-6 - head) * pmax, np.minimum(p, 2.0 ** (-10 - head) * pmax), 0.0)
     bound = 2.0 ** -4 * (p @ aV) + sub @ aV
     return o, lse, bound
 

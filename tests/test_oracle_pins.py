@@ -739,27 +739,28 @@ def test_fp8_attention_bound_covers_simulated_probability_rounding():
         V = rs.standard_normal((400, 32)) + (0.5 if trial % 2 else 0.0)
         o, _, bound = orc.fp8_attention(q, K, V, 0.3)
         q8 = orc.e4m3_rows(q)
-        for head in (5.0, 6.5, 8.5):
+        for head in (3.0, 4.5, 6.5, 8.5):
             sim = _simulate_fp8_pv(q8, K, V, 0.3, rs, head)
             assert np.all(np.abs(sim - o) <= bound * (1 + 1e-9) + 1e-12)
 
 
-def test_fp8_attention_bound_needs_its_subnormal_term():
-    # one dominant key and many keys 16 exp2 units below it (p = 2^-11 against the max's
-    # 2^5), all with V = 1: every small p rounds to zero, so the error is one-signed and
-    # equals the subnormal term; the normal-range term alone does not cover it
+@pytest.mark.parametrize("head", [3, 5])
+def test_fp8_attention_bound_needs_its_subnormal_term(head):
+    # one dominant key and many keys head + 11 exp2 units below it (p = 2^-11 against the
+    # max's 2^head), all with V = 1: every small p rounds to zero, so the error is
+    # one-signed and equals the subnormal term; the normal-range term alone does not cover it
     q = np.zeros((1, 4))
     q[0, 0] = 1.0
     K = np.zeros((3001, 4))
     K[0, 0] = 40.0                      # the dominant key
-    K[1:, 0] = 40.0 - 16.0 * math.log(2) - np.linspace(0, 0.05, 3000)
+    K[1:, 0] = 40.0 - (head + 11) * math.log(2) - np.linspace(0, 0.05, 3000)
     V = np.ones((3001, 4))
     V[0] = 0.0
-    o, _, bound = orc.fp8_attention(q, K, V, 1.0)
+    o, lse, bound = orc.fp8_attention(q, K, V, 1.0, head=head)
     q8 = orc.e4m3_rows(q)
-    sim = _simulate_fp8_pv(q8, K, V, 1.0, np.random.default_rng(0), 5.0)
+    sim = _simulate_fp8_pv(q8, K, V, 1.0, np.random.default_rng(0), float(head))
     err = np.abs(sim - o).max()
-    p = np.exp(q8 @ K.T - orc.fp8_attention(q, K, V, 1.0)[1][:, None])
+    p = np.exp(q8 @ K.T - lse[:, None])
     normal_only = 2.0 ** -4 * (p @ np.abs(V)).max()
     assert err > normal_only                     # the subnormal range matters here
     assert err <= bound.max() * (1 + 1e-9)       # and the full bound covers it
