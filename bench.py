@@ -570,7 +570,7 @@ def main():
 
 
 TRAFFIC_KERNEL = "attn_fwd_kernel<128, true, false, false>"
-KERNEL_SOURCES = ("attn_fwd.hip", "attn_common.h", "common.h")
+KERNEL_SOURCES = ("attn_fwd.hip", "attn_lists.h", "attn_common.h", "common.h")
 
 
 def kernel_source_hash():

@@ -509,7 +509,11 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
       hr.stride = stride;
       if (FP8 && !tok) {
         hr.f8 = true;
-        const float* sc = a.kv_scale + (static_cast<int64_t>(h) * a.slots + id) * 2;
+        // (read through the constant address space: a wave-uniform load from it is a scalar
+        // load, which the gathers' vmcnt waits do not count; a vector load here made the
+        // compiler drain every gather in flight before using the scale)
+        typedef __attribute__((address_space(4))) const float cfloat;
+        const cfloat* sc = (const cfloat*)(a.kv_scale) + (static_cast<int64_t>(h) * a.slots + id) * 2;
         hr.ks = sc[0];
         hr.vs = sc[1];
       }
