@@ -4,14 +4,16 @@
 // Light Forcing (papernotes.org, "Key findings") deploys the sparse attention in FP8.  The
 // cache holds OCP E4M3 codes with one power-of-two scale per block and tensor (as the memory
 // update writes them); this path also computes in FP8:
-//   * Q is quantized per row: the smallest power of two 2^e with max|q| <= 448 * 2^e, then
-//     each value's nearest E4M3 code (ties to even);
+//   * Q is quantized per row as c q (c = scale * log2 e, so the scores come out in exp2
+//     units): the smallest power of two 2^e with max|c q| <= 448 * 2^e, then each value's
+//     nearest E4M3 code (ties to even);
 //   * the chunk's own K/V blocks (bf16) are quantized per block and tensor exactly as the
 //     memory update quantizes a cache slot, by chunk_e4m3_kernel, into the call's workspace;
 //   * S^T = K Q^T runs on gfx950's scaled FP8 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4): the
 //     power-of-two scales ride in the instruction as E8M0 exponents, so every product is the
 //     exact product of the decoded values and the sums are fp32;
-//   * P = exp2(c s - m) is rounded to E4M3 (nearest even, gfx950's v_cvt_pk_fp8_f32) for
+//   * each score tile's first MFMA starts from -m (the row offset) instead of zero, so
+//     P = exp2(accumulator) is rounded to E4M3 (nearest even, gfx950's v_cvt_pk_fp8_f32) for
 //     O^T += V^T P^T on the same MFMA, while the row sum adds the unrounded fp32 values.  The
 //     offset m is raised lazily, as in the bf16 kernel, but so that no p exceeds 448 (E4M3's
 //     largest value): a lane whose 32 exponentials of a block sum to more than 448 raises m to
@@ -165,42 +167,49 @@ __global__ void __launch_bounds__(256) chunk_e4m3_kernel(TokIn xk, TokIn xv, int
   }
 }
 
-// Online-softmax state of one wave (32 query rows; this lane's row = column l % 32).
+// Online-softmax state of one wave (32 query rows; this lane's row = column l % 32).  The
+// queries are quantized as c q (c = scale * log2 e), so the S MFMAs give scores in exp2 units;
+// each score tile's first MFMA starts from `neg` (-m in every entry), so the accumulators
+// already hold c s - m and a probability is one exp2.
 struct RowState8 {
-  i32x8 q[2];     // Q codes of MFMA m: channels 64 m + 32 h2 + [0, 32)
+  i32x8 q[2];     // codes of c q, MFMA m: channels 64 m + 32 h2 + [0, 32)
   int sq;         // E8M0 scale of this lane's query row
   f32x16 acc[4];  // O^T: channels 32 dt + acc_row(r, h2)
-  float m_off;    // exp2 offset; starts huge negative so the first block raises it
+  f32x16 neg;     // -m_off in every entry
+  float m_off;    // exp2 offset (starts at 0; the first block always sets it)
   float l_run;    // this lane's share of the row sum
-  static constexpr float kNoOffset = -3.0e38f;
+  bool first;     // (wave-uniform) no block processed yet
 
-  // Softmax of one block (two 32-key score tiles) in 8 stages (4 scores each), so that the
-  // stages can ride under MFMAs: exponentials against the current offset, their sum, and
-  // their E4M3 codes packed in the operand's byte order (byte 16 t + i = tile t, score i).
+  // Softmax of one block (two 32-key tiles of c s - m) in 8 stages (4 scores each), so that
+  // the stages can ride under MFMAs: the exponentials, their sum, and their E4M3 codes
+  // packed in the operand's byte order (byte 16 t + i = tile t, score i).
   struct Soft {
-    float ps, alpha;
+    float ps, alpha, delta;
     i32x8 pb;
     bool up;
   };
-  __device__ __forceinline__ void stage(int k, const f32x16 (&s)[2], Soft& so, float c) {
+  __device__ __forceinline__ static void stage(int k, const f32x16 (&s)[2], Soft& so) {
     const int t = k >> 2, i0 = 4 * (k & 3);
-    const float p0 = __builtin_amdgcn_exp2f(fmaf(s[t][i0], c, -m_off));
-    const float p1 = __builtin_amdgcn_exp2f(fmaf(s[t][i0 + 1], c, -m_off));
-    const float p2 = __builtin_amdgcn_exp2f(fmaf(s[t][i0 + 2], c, -m_off));
-    const float p3 = __builtin_amdgcn_exp2f(fmaf(s[t][i0 + 3], c, -m_off));
+    const float p0 = __builtin_amdgcn_exp2f(s[t][i0]);
+    const float p1 = __builtin_amdgcn_exp2f(s[t][i0 + 1]);
+    const float p2 = __builtin_amdgcn_exp2f(s[t][i0 + 2]);
+    const float p3 = __builtin_amdgcn_exp2f(s[t][i0 + 3]);
     const float s4 = (p0 + p1) + (p2 + p3);
     so.ps = k == 0 ? s4 : so.ps + s4;
     int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
     wd = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, wd, true);
     so.pb[k] = wd;
   }
-  // After the 8 stages: a lane whose sum exceeds 448 sends the wave down the rare branch
-  // (row max in-lane and from the other lane half, offset raised to max * c - 3, block
-  // redone); the first block of every row takes it.
-  __device__ __forceinline__ void finish(const f32x16 (&s)[2], Soft& so, float c) {
+  // After the 8 stages: a lane whose sum exceeds 448 (or the first block of the rows) sends
+  // the wave down the rare branch: the row max (in-lane and from the other lane half), the
+  // offset raised by d to the row max minus 3 (set outright on the first block), the scores
+  // shifted by -d and the block redone.  The caller shifts a tile computed before the raise
+  // (the second block of a shared step) by so.delta.
+  __device__ __forceinline__ void finish(f32x16 (&s)[2], Soft& so) {
     asm volatile("" ::"v"(so.pb), "v"(so.ps));
-    so.up = __any(so.ps > kRaiseSum8);
+    so.up = first || __any(so.ps > kRaiseSum8);
     so.alpha = 1.f;
+    so.delta = 0.f;
     if (so.up) {
       __builtin_amdgcn_sched_barrier(0);
       float mx = fmaxf(s[0][0], s[1][0]);
@@ -209,12 +218,22 @@ struct RowState8 {
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
                                                        false, false);
       mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-      const float m_new = fmaxf(m_off, mx * c - kHead8);
-      so.alpha = __builtin_amdgcn_exp2f(m_off - m_new);
-      m_off = m_new;
+      float d = first ? mx - kHead8 : fmaxf(0.f, mx - kHead8);
+      if (!(mx > -INFINITY)) d = 0.f;  // no valid key of the row in this block
+      // (before the first block nothing has been accumulated: the factor is 0, not 2^-d)
+      so.alpha = first ? 0.f : __builtin_amdgcn_exp2f(-d);
+      so.delta = d;
+      m_off += d;
       l_run *= so.alpha;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) stage(k, s, so, c);
+      for (int r = 0; r < 16; ++r) {
+        neg[r] -= d;
+        s[0][r] -= d;
+        s[1][r] -= d;
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) stage(k, s, so);
+      first = false;
     }
     l_run += so.ps;
   }
@@ -317,8 +336,8 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f8_kernel(F8Args g) {
   const int64_t t0 = r < a.nq ? block_token0(r, a.nb, a.n) : 0;
   const float c = a.scale * kLog2e;
 
-  // Q codes: this lane's 64 channels of its row, the row max over both lane halves, the
-  // power-of-two scale and the nearest codes (rows past the block: zero codes, scale 1)
+  // Q codes: this lane's 64 channels of its row times c (fp32), the row max over both lane
+  // halves, the power-of-two scale and the nearest codes (rows past the block: zero codes)
   RowState8 st;
   {
     const uint16_t* qp = a.q + h * a.qhs + (t0 + qrow) * a.qts;
@@ -331,8 +350,8 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f8_kernel(F8Args g) {
                            : u32x4{0, 0, 0, 0};
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(raw[i][e] << 16)),
-                                 fabsf(__uint_as_float(raw[i][e] & 0xffff0000u))));
+        amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(raw[i][e] << 16) * c),
+                                 fabsf(__uint_as_float(raw[i][e] & 0xffff0000u) * c)));
     }
     amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
     int eq = e4m3_scale_exp(amax);
@@ -343,20 +362,22 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f8_kernel(F8Args g) {
     for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int e = 0; e < 4; e += 2) {
-        int wd = __builtin_amdgcn_cvt_pk_fp8_f32(__uint_as_float(raw[i][e] << 16) * iq,
-                                                 __uint_as_float(raw[i][e] & 0xffff0000u) * iq,
-                                                 0, false);
-        wd = __builtin_amdgcn_cvt_pk_fp8_f32(__uint_as_float(raw[i][e + 1] << 16) * iq,
-                                             __uint_as_float(raw[i][e + 1] & 0xffff0000u) * iq,
-                                             wd, true);
+        int wd = __builtin_amdgcn_cvt_pk_fp8_f32(
+            (__uint_as_float(raw[i][e] << 16) * c) * iq,
+            (__uint_as_float(raw[i][e] & 0xffff0000u) * c) * iq, 0, false);
+        wd = __builtin_amdgcn_cvt_pk_fp8_f32(
+            (__uint_as_float(raw[i][e + 1] << 16) * c) * iq,
+            (__uint_as_float(raw[i][e + 1] & 0xffff0000u) * c) * iq, wd, true);
         st.q[i >> 2][2 * (i & 3) + (e >> 1)] = wd;
       }
     st.sq = 127 + eq;
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) st.acc[i] = f32x16{};
-  st.m_off = RowState8::kNoOffset;
+  st.neg = f32x16{};
+  st.m_off = 0.f;
   st.l_run = 0.f;
+  st.first = true;
 
   const FwdLists fl = build_lists<true, true>(
       a, h, rA, rB, lists, wave_cnt, part_cnt, n_list, reinterpret_cast<int32_t*>(&kb0[0][0]),
@@ -476,8 +497,8 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f8_kernel(F8Args g) {
     i32x8 kop[4];
     kop[0] = kread8(kt, koff, 0);
     kop[1] = kread8(kt, koff, 1);
-    s[0] = f32x16{};
-    s[1] = f32x16{};
+    s[0] = st.neg;
+    s[1] = st.neg;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       s[j >> 1] = mfma8<decltype(sel)::value>(kop[j], st.q[j & 1], s[j >> 1], sk, st.sq);
@@ -546,25 +567,33 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f8_kernel(F8Args g) {
       });
       RowState8::mask(sx, len_of(s0.ex), h2);
       s_mma(B8<1>{}, kc[1], s0.sc, sy, [&](int j) {
-        st.stage(2 * j, sx, so, c);
-        st.stage(2 * j + 1, sx, so, c);
+        st.stage(2 * j, sx, so);
+        st.stage(2 * j + 1, sx, so);
         if (j < 2) dma_v(2 + j);
       });
       __builtin_amdgcn_s_setprio(0);
-      st.finish(sx, so, c);
+      st.finish(sx, so);
       wait_keep_next();
       lds_barrier8();
-      // PV phase: PV of X carrying Y's softmax (and the K gathers), then PV of Y
-      if (so.up) st.rescale(so.alpha);
+      // PV phase: PV of X carrying Y's softmax (and the K gathers), then PV of Y.  Y's scores
+      // were computed against the offset before X's raise (if any): shift them by its d.
+      if (so.up) {
+        st.rescale(so.alpha);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          sy[0][r] -= so.delta;
+          sy[1][r] -= so.delta;
+        }
+      }
       RowState8::mask(sy, len_of(s0.ey), h2);
       __builtin_amdgcn_s_setprio(1);
       pv_mma(B8<2>{}, vc[0], s0.sc, so.pb, [&](int j) {
-        st.stage(2 * j, sy, sv2, c);
-        st.stage(2 * j + 1, sy, sv2, c);
+        st.stage(2 * j, sy, sv2);
+        st.stage(2 * j + 1, sy, sv2);
         dma_k(j);
       });
       __builtin_amdgcn_s_setprio(0);
-      st.finish(sy, sv2, c);
+      st.finish(sy, sv2);
       if (sv2.up) st.rescale(sv2.alpha);
       __builtin_amdgcn_s_setprio(1);
       pv_mma(B8<3>{}, vc[1], s0.sc, sv2.pb, [&](int) {});
@@ -578,8 +607,8 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f8_kernel(F8Args g) {
       __builtin_amdgcn_s_setprio(0);
       RowState8::mask(sx, len, h2);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) st.stage(k, sx, so, c);
-      st.finish(sx, so, c);
+      for (int k = 0; k < 8; ++k) st.stage(k, sx, so);
+      st.finish(sx, so);
       wait_keep_next();
       lds_barrier8();
       if (so.up) st.rescale(so.alpha);

@@ -250,13 +250,14 @@ pbsa_status pbsa_attn_fwd(const pbsa_dims* dims, pbsa_tensor q, const pbsa_cache
  * pbsa_attn_fwd over an FP8 cache (dims.kv_format = PBSA_KV_FP8: the cache's E4M3 codes and
  * power-of-two block scales), computed on FP8 matrix cores instead of after an exact decode
  * to bf16:
- *   - each query row is quantized to E4M3 with its own power-of-two scale (the smallest 2^e
- *     with max|q| <= 448 * 2^e), nearest even;
+ *   - each query row, times c = scale * log2(e) (fp32 product), is quantized to E4M3 with
+ *     its own power-of-two scale (the smallest 2^e with max|c q| <= 448 * 2^e), nearest even;
  *   - the chunk's K/V blocks are quantized per block and tensor as pbsa_memory_update
  *     quantizes a cache slot (codes and scales go to the workspace);
- *   - scores are exact products of the decoded values summed in fp32; the probabilities
- *     p = exp(scale * s - m) (a per-row offset m with every p <= 448) are rounded to E4M3
- *     (nearest even) for the product with V, while the row sum adds the unrounded values.
+ *   - scores are exact products of the decoded values summed in fp32 (in exp2 units); the
+ *     probabilities p = 2^(s - m) (a per-row offset m with every p <= 448) are rounded to
+ *     E4M3 (nearest even) for the product with V, while the row sum adds the unrounded
+ *     values.
  * The offset keeps the row max at p >= 8, so o differs from the exact attention of the
  * quantized q by at most 2^-4 * sum_j p_j |v_j| / sum_j p_j per channel (the rounding of p in
  * E4M3's normal range) plus fp32 and bf16 rounding and the subnormal range's absolute 2^-10

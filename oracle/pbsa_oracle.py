@@ -362,11 +362,12 @@ def e4m3_quantize_block(x):
 
 # --------------------------------------------------------------------------------------
 # FP8 arithmetic.  [LF] "Key findings": the sparse attention deployed in FP8.  Reading: the
-# queries are rounded to E4M3 row by row (each row with its own power-of-two scale, the
-# rule of a cache block), the chunk's own K/V block by block as the cache stores them, and
-# the attention of those values is exact; the probabilities are rounded to E4M3 before
-# their product with V, on a grid that an implementation's running offset decides, so the
-# reference bounds that rounding instead of reproducing it.
+# queries, times the softmax scale in exp2 units, are rounded to E4M3 row by row (each row
+# with its own power-of-two scale, the rule of a cache block), the chunk's own K/V block by
+# block as the cache stores them, and the attention of those values is exact; the
+# probabilities are rounded to E4M3 before their product with V, on a grid that an
+# implementation's running offset decides, so the reference bounds that rounding instead of
+# reproducing it.
 # --------------------------------------------------------------------------------------
 
 
@@ -386,7 +387,10 @@ def fp8_attention(q, K, V, scale: float, head: int = 3):
     """FP8-arithmetic attention of query rows q over keys K, V (already the decoded E4M3
     values): (O, LSE, bound).
 
-    O, LSE: the exact attention (masked_attention, every key allowed) of e4m3_rows(q).
+    The queries enter as x = c q with c = scale * log2(e), the product and c itself rounded
+    to float32 (the scores then come out in exp2 units), and x is rounded to E4M3 row by row
+    (e4m3_rows).  O, LSE: the exact attention of those values, softmax in base 2 over
+    t = x8 . k (LSE in natural log).
     bound[t, c]: how far rounding the probabilities to E4M3 can move O[t, c] when the
     implementation keeps its row offset so that the row max maps to p >= 2^head (and every
     p <= 448) in its units: a p in E4M3's normal range moves by at most 2^-4 p; one in the
@@ -396,11 +400,18 @@ def fp8_attention(q, K, V, scale: float, head: int = 3):
                 + sum_{p_j < 2^(-6-head) pmax} min(p_j, 2^(-10-head) pmax) |V_jc|
     with p the exact normalised probabilities and pmax their row max.
     """
-    q8 = e4m3_rows(q)
+    c = np.float32(np.float32(scale) * np.float32(1.4426950408889634))
+    x = (np.asarray(q, dtype=np.float32) * c).astype(np.float64)
+    x8 = e4m3_rows(x)
     K = np.asarray(K, dtype=np.float64)
     V = np.asarray(V, dtype=np.float64)
-    o, lse = masked_attention(q8, K, V, np.ones((q8.shape[0], K.shape[0]), dtype=bool), scale)
-    p = np.exp(scale * (q8 @ K.T) - lse[:, None])
+    t = x8 @ K.T
+    tm = t.max(axis=1, keepdims=True)
+    e = np.exp2(t - tm)
+    l = e.sum(axis=1, keepdims=True)
+    p = e / l
+    o = p @ V
+    lse = (np.log(2.0) * (tm + np.log2(l)))[:, 0]
     pmax = p.max(axis=1, keepdims=True)
     aV = np.abs(V)
     sub = np.where(p < 2.0 ** (-6 - head) * pmax, np.minimum(p, 2.0 ** (-10 - head) * pmax), 0.0)
@@ -500,8 +511,8 @@ class PersistentRollout:
     def attend_fp8(self, q_chunk, k_chunk, v_chunk, sel, rows=None):
         """attend in FP8 arithmetic over an FP8 cache (kv_fp8): the stored blocks as their
         decoded codes, the chunk's own blocks quantized per block and tensor like a cache
-        slot, the queries per row (fp8_attention).  Returns (O, LSE, bound) with rows not
-        asked for left as NaN."""
+        slot, the queries (times scale * log2 e) per row (fp8_attention).  Returns (O, LSE,
+        bound) with rows not asked for left as NaN."""
         if not self.kv_fp8:
             raise ValueError("FP8 arithmetic reads an FP8 cache")
         s = self.sch

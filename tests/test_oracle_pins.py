@@ -701,33 +701,41 @@ def test_e4m3_rows_are_nearest_values_of_each_rows_own_grid():
             assert got[t, c] == _nearest_grid(x[t, c] / 2.0 ** e, grid) * 2.0 ** e
 
 
-def test_fp8_attention_reduces_to_the_attention_on_exact_grid_values():
-    # queries already on each row's E4M3 grid: the FP8 reference is the plain attention
+def _c32(scale):
+    # scale * log2(e) as float32 (the product and both factors rounded to float32)
+    return np.float32(np.float32(scale) * np.float32(math.log2(math.e)))
+
+
+def test_fp8_attention_is_base2_attention_of_the_quantized_scaled_queries():
+    # x8 = E4M3 rows of float32(q) * c; torch's attention with scale ln 2 on x8 is the
+    # base-2 softmax of x8 . k
     rs = np.random.default_rng(22)
-    q = orc.e4m3_rows(rs.standard_normal((6, 16)))
+    q = rs.standard_normal((6, 16))
     K = orc.e4m3_decode(rs.integers(0, 0x7E, (30, 16)).astype(np.uint8)) * 2.0 ** -4
     V = rs.standard_normal((30, 16))
     o, lse, _ = orc.fp8_attention(q, K, V, 0.25)
+    x8 = orc.e4m3_rows((q.astype(np.float32) * _c32(0.25)).astype(np.float64))
     ref = torch.nn.functional.scaled_dot_product_attention(
-        torch.from_numpy(q)[None], torch.from_numpy(K)[None], torch.from_numpy(V)[None],
-        scale=0.25)[0].numpy()
+        torch.from_numpy(x8)[None], torch.from_numpy(K)[None], torch.from_numpy(V)[None],
+        scale=math.log(2))[0].numpy()
     assert np.abs(o - ref).max() < 1e-12
-    s = 0.25 * q @ K.T
-    assert np.abs(lse - np.log(np.exp(s).sum(axis=1))).max() < 1e-12
+    z = math.log(2) * (x8 @ K.T)
+    assert np.abs(lse - np.log(np.exp(z).sum(axis=1))).max() < 1e-12
 
 
-def _simulate_fp8_pv(q8, K, V, scale, rs, head):
-    # an implementation's rounding of p: a row offset with the max mapping to 2^head
-    # (head in [5, 8.8]), p rounded to E4M3 by brute force over the value grid
+def _simulate_fp8_pv(x8, K, V, head):
+    # an implementation's rounding of p: scores t = x8 . k in exp2 units, a row offset with
+    # the max mapping to 2^head (head in [3, 8.8]), p rounded to E4M3 by brute force over
+    # the value grid
     vals = orc.e4m3_decode(np.arange(256, dtype=np.uint8))
     grid = np.sort(np.unique(vals[~np.isnan(vals)]))
-    s = scale * (q8 @ K.T)
-    out = np.empty((q8.shape[0], V.shape[1]))
-    for t in range(q8.shape[0]):
-        pk = np.exp2((s[t] - s[t].max()) / math.log(2) + head)
+    t = x8 @ K.T
+    out = np.empty((x8.shape[0], V.shape[1]))
+    for r in range(x8.shape[0]):
+        pk = np.exp2(t[r] - t[r].max() + head)
         assert pk.max() <= 448
         p8 = np.array([_nearest_grid(x, grid) for x in pk])
-        out[t] = (p8 @ V) / pk.sum()
+        out[r] = (p8 @ V) / pk.sum()
     return out
 
 
@@ -738,9 +746,9 @@ def test_fp8_attention_bound_covers_simulated_probability_rounding():
         K = rs.standard_normal((400, 32))
         V = rs.standard_normal((400, 32)) + (0.5 if trial % 2 else 0.0)
         o, _, bound = orc.fp8_attention(q, K, V, 0.3)
-        q8 = orc.e4m3_rows(q)
+        x8 = orc.e4m3_rows((q.astype(np.float32) * _c32(0.3)).astype(np.float64))
         for head in (3.0, 4.5, 6.5, 8.5):
-            sim = _simulate_fp8_pv(q8, K, V, 0.3, rs, head)
+            sim = _simulate_fp8_pv(x8, K, V, head)
             assert np.all(np.abs(sim - o) <= bound * (1 + 1e-9) + 1e-12)
 
 
@@ -749,18 +757,23 @@ def test_fp8_attention_bound_needs_its_subnormal_term(head):
     # one dominant key and many keys head + 11 exp2 units below it (p = 2^-11 against the
     # max's 2^head), all with V = 1: every small p rounds to zero, so the error is
     # one-signed and equals the subnormal term; the normal-range term alone does not cover it
+    scale = 1.0
+    c = float(_c32(scale))
     q = np.zeros((1, 4))
     q[0, 0] = 1.0
     K = np.zeros((3001, 4))
+    x0 = float(orc.e4m3_rows(np.array([[c, 0.0, 0.0, 0.0]]))[0, 0])   # the quantized c q
     K[0, 0] = 40.0                      # the dominant key
-    K[1:, 0] = 40.0 - (head + 11) * math.log(2) - np.linspace(0, 0.05, 3000)
+    K[1:, 0] = 40.0 - (head + 11) / x0 - np.linspace(0, 0.05, 3000)
     V = np.ones((3001, 4))
     V[0] = 0.0
-    o, lse, bound = orc.fp8_attention(q, K, V, 1.0, head=head)
-    q8 = orc.e4m3_rows(q)
-    sim = _simulate_fp8_pv(q8, K, V, 1.0, np.random.default_rng(0), float(head))
+    o, lse, bound = orc.fp8_attention(q, K, V, scale, head=head)
+    x8 = orc.e4m3_rows((q.astype(np.float32) * _c32(scale)).astype(np.float64))
+    sim = _simulate_fp8_pv(x8, K, V, float(head))
     err = np.abs(sim - o).max()
-    p = np.exp(q8 @ K.T - lse[:, None])
+    t = x8 @ K.T
+    p = np.exp2(t - t.max())
+    p /= p.sum()
     normal_only = 2.0 ** -4 * (p @ np.abs(V)).max()
     assert err > normal_only                     # the subnormal range matters here
     assert err <= bound.max() * (1 + 1e-9)       # and the full bound covers it
@@ -768,7 +781,7 @@ def test_fp8_attention_bound_needs_its_subnormal_term(head):
 
 def test_rollout_attend_fp8_quantizes_queries_and_chunk_blocks():
     # attend_fp8 = attend over the same stored blocks with the queries and the chunk's own
-    # blocks replaced by their quantized values
+    # blocks replaced by their quantized values (the queries as scale * log2 e * q)
     wl = synth.Workload("pin_fp8", 1, 16, 32, 64, 1, 4, 2, 4, 1, 2)
     sch = orc.Schedule(wl.frame_tokens, wl.block, wl.chunk_frames, wl.window_frames,
                        wl.capacity, wl.sinks, wl.topk, wl.scale, False)
@@ -784,7 +797,10 @@ def test_rollout_attend_fp8_quantizes_queries_and_chunk_blocks():
                 kc, ks = orc.e4m3_quantize_block(k[a0:b0, 0])
                 vc, vs = orc.e4m3_quantize_block(v[a0:b0, 0])
                 kq[a0:b0], vq[a0:b0] = orc.e4m3_decode(kc) * ks, orc.e4m3_decode(vc) * vs
-            o, l = ro.attend(orc.e4m3_rows(q[:, 0]), kq, vq, rt["sel"])
+            # attend's softmax of scale * q' . k with q' = x8 ln 2 / scale is the base-2
+            # softmax of x8 . k
+            x8 = orc.e4m3_rows((q[:, 0].astype(np.float32) * _c32(wl.scale)).astype(np.float64))
+            o, l = ro.attend(x8 * math.log(2) / wl.scale, kq, vq, rt["sel"])
             assert np.abs(o8 - o).max() < 1e-12 and np.abs(l8 - l).max() < 1e-12
             assert np.all(b8 > 0)
             return
