@@ -481,6 +481,23 @@ pbsa_status check_chunk_args(const pbsa_dims* dims, const pbsa_chunk_args* a,
   if (!a->scores || !a->sel) return fail(PBSA_ERR_NULL, "scores and sel are required");
   if (reinterpret_cast<uintptr_t>(a->q_rep) % 16)
     return fail(PBSA_ERR_ALIGN, "q_rep must be 16-byte aligned");
+  if (a->fp8_arithmetic) {
+    if (dims->kv_format != PBSA_KV_FP8)
+      return fail(PBSA_ERR_UNSUPPORTED, "fp8_arithmetic needs an FP8 cache (kv_format PBSA_KV_FP8)");
+    for (int p = 0; p < a->passes; ++p) PBSA_TRY(check_span(a->q[p], "q", ctok, dims->head_dim));
+    const size_t need = pbsa::attn_fwd_f8_workspace(*dims);
+    if (!a->attn_workspace || a->attn_workspace_bytes < need)
+      return fail(PBSA_ERR_WORKSPACE, "chunk_step with fp8_arithmetic needs %zu attn_workspace "
+                  "bytes (got %zu)", need,
+                  a->attn_workspace ? a->attn_workspace_bytes : static_cast<size_t>(0));
+    if (reinterpret_cast<uintptr_t>(a->attn_workspace) % 16)
+      return fail(PBSA_ERR_ALIGN, "attn_workspace must be 16-byte aligned");
+    const uintptr_t w0 = reinterpret_cast<uintptr_t>(a->workspace),
+                    w1 = w0 + a->workspace_bytes;
+    const uintptr_t x0 = reinterpret_cast<uintptr_t>(a->attn_workspace), x1 = x0 + need;
+    if (x0 < w1 && w0 < x1)
+      return fail(PBSA_ERR_WORKSPACE, "attn_workspace overlaps workspace");
+  }
   return check_memory_ws(dims, cache, a->workspace, a->workspace_bytes, "chunk_step");
 }
 

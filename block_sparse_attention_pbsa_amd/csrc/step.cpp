@@ -34,7 +34,10 @@ hipError_t enqueue_chunk_step(const pbsa_dims& d, const pbsa_chunk_args& a, cons
         return e;
       if ((e = hipEventRecord(join, side)) != hipSuccess) return e;
     }
-    e = d.kv_format == PBSA_KV_FP8
+    e = a.fp8_arithmetic
+            ? launch_attn_fwd_f8(d, tok_in(a.q[p]), c, tok_in(a.k[p]), tok_in(a.v[p]), a.sel,
+                                 tok_out(a.o[p]), a.lse[p], a.attn_workspace, s)
+        : d.kv_format == PBSA_KV_FP8
             ? launch_attn_fwd_fp8(d, tok_in(a.q[p]), c, tok_in(a.k[p]), tok_in(a.v[p]), a.sel,
                                   tok_out(a.o[p]), a.lse[p], s)
             : launch_attn_fwd_persistent(d, tok_in(a.q[p]), c, tok_in(a.k[p]), tok_in(a.v[p]),

@@ -66,7 +66,9 @@ class ChunkArgs(ctypes.Structure):
                 ("k", Tensor * MAX_PASSES), ("v", Tensor * MAX_PASSES),
                 ("o", Tensor * MAX_PASSES), ("lse", ctypes.c_void_p * MAX_PASSES),
                 ("q_rep", ctypes.c_void_p), ("scores", ctypes.c_void_p), ("sel", ctypes.c_void_p),
-                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("fp8_arithmetic", ctypes.c_int32), ("attn_workspace", ctypes.c_void_p),
+                ("attn_workspace_bytes", ctypes.c_size_t)]
 
 
 _P = ctypes.c_void_p
@@ -458,9 +460,11 @@ def pbsa_attn_bwd(shape: Shape, chunks: int, q, k, v, o, lse, dout, sel, nsel, d
         workspace.numel(), _stream()))
 
 
-def chunk_args(shape: Shape, passes, q_rep, scores, sel, os_, lses, workspace) -> ChunkArgs:
+def chunk_args(shape: Shape, passes, q_rep, scores, sel, os_, lses, workspace,
+               attn_workspace=None) -> ChunkArgs:
     """pbsa_chunk_args for `passes` = [(q, k, v), ...] (the last pass's K/V enter the cache),
-    per-pass outputs os_[p], lses[p] and the shared routing / update buffers."""
+    per-pass outputs os_[p], lses[p] and the shared routing / update buffers; with
+    attn_workspace (uint8 device tensor) the attentions run in FP8 arithmetic."""
     H, d, T = shape.heads, shape.head_dim, shape.chunk_tokens
     n = len(passes)
     if not 1 <= n <= MAX_PASSES or len(os_) < n or len(lses) < n:
@@ -482,6 +486,11 @@ def chunk_args(shape: Shape, passes, q_rep, scores, sel, os_, lses, workspace) -
     a.q_rep = q_rep.data_ptr() if q_rep is not None else None
     a.scores, a.sel = scores.data_ptr(), sel.data_ptr()
     a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
+    if attn_workspace is not None:
+        _dev(attn_workspace, "attn_workspace", torch.uint8)
+        a.fp8_arithmetic = 1
+        a.attn_workspace = attn_workspace.data_ptr()
+        a.attn_workspace_bytes = attn_workspace.numel()
     return a
 
 

@@ -98,7 +98,8 @@ class PersistentLayer:
 
     def _args(self, passes):
         return ops.chunk_args(self.shape, passes, self.q_rep, self.scores, self.sel, self.os,
-                              self.lses, self.workspace)
+                              self.lses, self.workspace,
+                              self.workspace8 if self.fp8_arithmetic else None)
 
     def step_fused(self, passes):
         """step_passes as one library call (pbsa_chunk_step)."""

@@ -351,7 +351,11 @@ pbsa_status pbsa_attn_bwd_persistent(const pbsa_dims* dims, pbsa_tensor q,
  * then pbsa_memory_update with the last pass's scores and k/v (chunk_rep = NULL): the last
  * pass is the one whose K/V enter the cache.  Every buffer is as in those calls (q_rep may
  * be NULL); scores and sel are shared by the passes and end up holding the last pass's.
- * workspace: >= pbsa_workspace_bytes(dims, PBSA_OP_MEMORY_UPDATE, 0, 0) bytes. */
+ * workspace: >= pbsa_workspace_bytes(dims, PBSA_OP_MEMORY_UPDATE, 0, 0) bytes.
+ * fp8_arithmetic != 0 (FP8 cache only, else PBSA_ERR_UNSUPPORTED): the attentions are
+ * pbsa_attn_fwd_fp8, with attn_workspace (16-byte aligned, >= pbsa_workspace_bytes(dims,
+ * PBSA_OP_ATTN_FWD_FP8, 0, 0) bytes; it must not overlap `workspace`, which the captured
+ * update's selection uses at the same time); otherwise attn_workspace is not read. */
 #define PBSA_MAX_PASSES 8
 typedef struct pbsa_chunk_args {
   int32_t passes;
@@ -365,6 +369,9 @@ typedef struct pbsa_chunk_args {
   int32_t* sel;
   void* workspace;
   size_t workspace_bytes;
+  int32_t fp8_arithmetic;
+  void* attn_workspace;
+  size_t attn_workspace_bytes;
 } pbsa_chunk_args;
 
 /* The chunk step as one call: the launches above in order on `stream`; advances

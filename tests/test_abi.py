@@ -316,3 +316,40 @@ def test_fp8_cache_checks():
     assert L.pbsa_probe_gather(d, t, ctypes.byref(cache), t, t, ctypes.c_void_p(16), None) == 3
     assert L.pbsa_probe_fp8_decode(ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.c_void_p(16),
                                    17, None) == 2
+
+
+def test_fp8_arithmetic_checks():
+    L = ops.lib()
+    fp8 = dataclasses.replace(WAN, kv_format=ops.PBSA_KV_FP8)
+    need = ops.pbsa_workspace_bytes(fp8, ops.PBSA_OP_ATTN_FWD_FP8)
+    # the chunk's K and V codes (64 x 128 bytes per block) and two scales per block
+    assert need == 12 * 75 * (2 * 64 * 128 + 8)
+    assert ops.pbsa_workspace_bytes(WAN, ops.PBSA_OP_ATTN_FWD_FP8) == 0
+    t = _tensor(16)
+    cache = ops.CacheC(16, 16, 16, 16, 16, 0, None, 16)
+    d8, d16 = ctypes.byref(_dims(kv_format=1)), ctypes.byref(_dims())
+    sel, lse = ctypes.c_void_p(16), ctypes.c_void_p(16)
+    # a bf16 cache is refused; so is a missing, small or misaligned workspace
+    assert L.pbsa_attn_fwd_fp8(d16, t, ctypes.byref(ops.CacheC(16, 16, 16, 16, 16, 0)), t, t,
+                               sel, t, lse, ctypes.c_void_p(16), need, None) == 3
+    assert L.pbsa_attn_fwd_fp8(d8, t, ctypes.byref(cache), t, t, sel, t, lse, None, need,
+                               None) == 5
+    assert L.pbsa_attn_fwd_fp8(d8, t, ctypes.byref(cache), t, t, sel, t, lse,
+                               ctypes.c_void_p(16), need - 1, None) == 5
+    assert L.pbsa_attn_fwd_fp8(d8, t, ctypes.byref(cache), t, t, sel, t, lse,
+                               ctypes.c_void_p(24), need, None) == 4
+    # the chunk step: FP8 arithmetic needs the FP8 cache and its own, separate workspace
+    a = ops.ChunkArgs()
+    a.passes = 1
+    a.q[0] = a.k[0] = a.v[0] = a.o[0] = _tensor(16)
+    a.lse[0] = 16
+    a.scores, a.sel = 16, 16
+    a.workspace, a.workspace_bytes = 1 << 20, ops.pbsa_workspace_bytes(fp8, ops.PBSA_OP_MEMORY_UPDATE)
+    a.fp8_arithmetic = 1
+    assert L.pbsa_chunk_step(d16, ctypes.byref(a), ctypes.byref(ops.CacheC(16, 16, 16, 16, 16, 0)),
+                             None) == 3
+    assert L.pbsa_chunk_step(d8, ctypes.byref(a), ctypes.byref(cache), None) == 5
+    a.attn_workspace, a.attn_workspace_bytes = (1 << 20) + 64, need   # overlaps `workspace`
+    assert L.pbsa_chunk_step(d8, ctypes.byref(a), ctypes.byref(cache), None) == 5
+    a.attn_workspace = (1 << 20) + 8
+    assert L.pbsa_chunk_step(d8, ctypes.byref(a), ctypes.byref(cache), None) == 4

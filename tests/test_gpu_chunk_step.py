@@ -37,19 +37,21 @@ def caches_equal(a, b):
     return all(torch.equal(getattr(a, nm), getattr(b, nm)) for nm in names)
 
 
-@pytest.mark.parametrize("name,passes,heads,rows,fp8", [
-    ("tiny", 3, (0,), None, False),
-    ("wan_5s", 4, (0, 7), "sampled", False),
-    ("wan_5s", 2, (3,), "sampled", True),
+@pytest.mark.parametrize("name,passes,heads,rows,fp8,arith8", [
+    ("tiny", 3, (0,), None, False, False),
+    ("wan_5s", 4, (0, 7), "sampled", False, False),
+    ("wan_5s", 2, (3,), "sampled", True, False),
+    ("wan_5s", 2, (5,), "sampled", True, True),
 ])
-def test_chunk_step_fused_and_graph(name, passes, heads, rows, fp8):
+def test_chunk_step_fused_and_graph(name, passes, heads, rows, fp8, arith8):
     wl, seed = synth.WORKLOADS[name], synth.SEEDS[name]
     shape = shape_of(wl, fp8)
     sch = orc.Schedule(wl.frame_tokens, wl.block, wl.chunk_frames, wl.window_frames,
                        wl.capacity, wl.sinks, wl.topk, wl.scale)
-    seq = runtime.PersistentLayer(shape, passes=passes)
-    fus = runtime.PersistentLayer(shape, passes=passes)
-    gra = runtime.PersistentLayer(shape, passes=passes, device_counter=True)
+    # (arith8: the attentions in FP8 arithmetic, pbsa_attn_fwd_fp8)
+    seq = runtime.PersistentLayer(shape, passes=passes, fp8_arithmetic=arith8)
+    fus = runtime.PersistentLayer(shape, passes=passes, fp8_arithmetic=arith8)
+    gra = runtime.PersistentLayer(shape, passes=passes, device_counter=True, fp8_arithmetic=arith8)
     for lay in (seq, fus, gra):
         lay.reset()
     T = shape.chunk_tokens
@@ -59,7 +61,8 @@ def test_chunk_step_fused_and_graph(name, passes, heads, rows, fp8):
     last = wl.measured_chunk
     resync = 0
     for c in range(last + 1):
-        say(f"[chunk step {name}{' fp8' if fp8 else ''}, {passes} passes] chunk {c}")
+        say(f"[chunk step {name}{' fp8' if fp8 else ''}{' arith8' if arith8 else ''}, "
+            f"{passes} passes] chunk {c}")
         host = [synth.pass_qkv(wl, seed, c, p, passes) for p in range(passes)]
         ps = [tuple(dev(x) for x in qkv) for qkv in host]
         for buf, src in zip(staging, ps):
@@ -94,9 +97,18 @@ def test_chunk_step_fused_and_graph(name, passes, heads, rows, fp8):
                     idx = np.arange(T) if rows is None else np.unique(np.r_[
                         0:64, 1536:1560, T - 24:T,
                         np.random.default_rng(p + 10 * h).choice(T, 48, replace=False)])
-                    o_ref, l_ref = ros[h].attend(q[:, h], k[:, h], v[:, h], gsel, rows=idx)
                     o = seq.os[p][:, h].float().cpu().numpy()
-                    assert_close_attn(o[idx], o_ref[idx], f"pass {p} head {h}")
+                    if arith8:
+                        # within the oracle's bound on the rounding of the probabilities
+                        o_ref, l_ref, bnd = ros[h].attend_fp8(q[:, h], k[:, h], v[:, h], gsel,
+                                                              rows=idx)
+                        err = np.abs(o[idx] - o_ref[idx])
+                        tol = bnd[idx] + 2.0 ** -8 * np.abs(o_ref[idx]) + 1e-4
+                        say(f"  pass {p} head {h}: max err/tol {(err / tol).max():.3f}")
+                        assert np.all(err <= tol)
+                    else:
+                        o_ref, l_ref = ros[h].attend(q[:, h], k[:, h], v[:, h], gsel, rows=idx)
+                        assert_close_attn(o[idx], o_ref[idx], f"pass {p} head {h}")
                     assert np.abs(seq.lses[p][h].cpu().numpy()[idx] - l_ref[idx]).max() < 1e-3
         # the update against the oracle's (last pass)
         q, k, v = host[-1]
