@@ -311,6 +311,16 @@ def persistent_line(cx, name, steps, warmup, oracle_heads=(), kv_format=0, route
     return res, layer, chunks, ros, measured_host, (sum(flop), sum(attn_ms), ms_step, abytes)
 
 
+def copy_probe(cx):
+    """Three copies of a 512 MiB buffer: known bytes for calibrating FETCH_SIZE and
+    WRITE_SIZE in a profiled run."""
+    src = cx.torch.ones(256 * 1024 * 1024, dtype=cx.torch.bfloat16, device="cuda")
+    dst = cx.torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    cx.sync()
+
+
 def fp8_lines(cx, name, steps, warmup):
     """The FP8 cache at `name`: the attention over the decoded codes (bf16 arithmetic) and
     pbsa_attn_fwd_fp8 (FP8 arithmetic, also reported against the FP8 peak)."""
@@ -466,17 +476,16 @@ def main():
     if args.train_only:
         out = {"wan_train": bench_train(cx)}
         if args.copy_probe:
-            src = cx.torch.ones(256 * 1024 * 1024, dtype=cx.torch.bfloat16, device="cuda")
-            dst = cx.torch.empty_like(src)
-            for _ in range(3):
-                dst.copy_(src)
-            cx.sync()
+            copy_probe(cx)
         print(json.dumps(out), flush=True)
         return
     name = args.config
     wl = cx.synth.WORKLOADS[name]
     if args.fp8_only:
-        print(json.dumps(fp8_lines(cx, name, args.steps, args.warmup)), flush=True)
+        out = fp8_lines(cx, name, args.steps, args.warmup)
+        if args.copy_probe:
+            copy_probe(cx)
+        print(json.dumps(out), flush=True)
         return
     cpu_heads = ()
     if not args.no_cpu:
