@@ -46,7 +46,7 @@ def test_fp8_decode_matches_the_format():
 TINY128 = synth.Workload("tiny128", 1, 128, 64, 256, 1, 4, 2, 4, 1, 4)
 
 
-def fp8_rollout(wl, seed, heads, rows, union=False, math8=False):
+def fp8_rollout(wl, seed, heads, rows, union=False, math8=False, slot_check_every=1):
     shape = ops.Shape(wl.heads, wl.head_dim, wl.frame_tokens, wl.chunk_frames, wl.window_frames,
                       wl.capacity, wl.sinks, wl.topk, wl.scale,
                       route_mode=ops.PBSA_ROUTE_UNION if union else ops.PBSA_ROUTE_WINDOW,
@@ -99,6 +99,8 @@ def fp8_rollout(wl, seed, heads, rows, union=False, math8=False):
                                   wl.capacity - wl.sinks)
             ro.update(routed[h], k[:, h], v[:, h], P_override=None if exact else gp)
             assert gp == ro.P
+            if c % slot_check_every and c != last - 1:
+                continue
             for s_ in range(shape.slots):
                 g = int(bid[h, s_])
                 if g < 0:
@@ -160,6 +162,18 @@ def test_fp8_arithmetic_tiny128_all_rows():
 def test_fp8_arithmetic_wan_5s():
     fp8_rollout(synth.WORKLOADS["wan_5s"], synth.SEEDS["wan_5s"], (1, 6), _sampled(10),
                 math8=True)
+
+
+def test_fp8_arithmetic_wan_5s_union_routing():
+    # routed ids may name persistent blocks: the FP8 kernel's lookups of them
+    wl = dataclasses.replace(synth.WORKLOADS["wan_5s"], name="wan_5s_union")
+    fp8_rollout(wl, synth.SEEDS["wan_5s"], (4,), _sampled(11), union=True, math8=True)
+
+
+def test_fp8_arithmetic_wan_1min():
+    # the bench's workload: 240-frame history, capacity 256, top-64 routing
+    fp8_rollout(synth.WORKLOADS["wan_1min"], synth.SEEDS["wan_1min"], (2,), _sampled(12),
+                math8=True, slot_check_every=20)
 
 
 def test_fp8_rollout_wan_5s_union_routing():
