@@ -159,6 +159,13 @@ def test_fp8_arithmetic_tiny128_all_rows():
     fp8_rollout(TINY128, 43, (0,), None, math8=True)
 
 
+@pytest.mark.parametrize("history", [0, 1, 2])
+def test_fp8_arithmetic_first_chunks(history):
+    # an empty cache (only the chunk attends), then a cache holding only sinks and the window
+    wl = dataclasses.replace(TINY128, name=f"tiny128_h{history}", history_frames=history)
+    fp8_rollout(wl, 44 + history, (0,), None, math8=True)
+
+
 def test_fp8_arithmetic_wan_5s():
     fp8_rollout(synth.WORKLOADS["wan_5s"], synth.SEEDS["wan_5s"], (1, 6), _sampled(10),
                 math8=True)
