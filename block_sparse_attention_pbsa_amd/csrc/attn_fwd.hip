@@ -99,12 +99,12 @@ __device__ __forceinline__ void lds_barrier() {
 // so a run shares one LDS base (M0) and one scalar global base, and each piece costs one
 // vector add for its lane offsets.  src must already be lowered by 1024 i.
 __device__ __forceinline__ void lds_dma16_piece(int i, __amdgpu_buffer_rsrc_t rs, uint32_t voff,
-                                                char* lds) {
+                                                uint32_t soff, char* lds) {
   switch (i) {
-    case 0: __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds, 16, voff, 0, 0, 0); break;
-    case 1: __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds, 16, voff, 0, 1024, 0); break;
-    case 2: __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds, 16, voff, 0, 2048, 0); break;
-    default: __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds, 16, voff, 0, 3072, 0); break;
+    case 0: __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds, 16, voff, soff, 0, 0); break;
+    case 1: __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds, 16, voff, soff, 1024, 0); break;
+    case 2: __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds, 16, voff, soff, 2048, 0); break;
+    default: __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds, 16, voff, soff, 3072, 0); break;
   }
 }
 // Scalar base 3 KB below p: per-piece lane offsets (up to 3 KB lower for piece 3) then
@@ -117,8 +117,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t dma_base(const char* p) {
 
 // A half tile to gather: wave-uniform base (bytes), row stride (bytes) and valid rows.
 struct HalfRef {
-  const char* k;
-  const char* v;
+  uint32_t off;  // byte offset of the half tile from its tensor's head base
+  uint32_t tok;  // 1: a block of the chunk's K/V; 0: a cache slot
   uint32_t stride;
   int len;      // 0 = nothing to gather
   bool f8;      // E4M3 codes of an FP8 cache slot (loaded into registers and decoded)
@@ -442,7 +442,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char vb1[2][HT::BYTES];
   // Block lists: static (a dynamic LDS array defeats the compiler's alias analysis, which
   // then waits for every gather in flight before each list read).
-  __shared__ uint32_t lists[kAttnListCap];
+  __shared__ uint32_t lists[kAttnListCap + 1];
   __shared__ int wave_cnt[4];
   __shared__ int part_cnt[4][3];
   __shared__ int n_list;
@@ -499,13 +499,13 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
     const bool tok = (e >> 31) != 0;
     const uint32_t id = e & 0xffffffu;
     const uint32_t stride = tok ? xrow : (FP8 ? D : 2 * D);
-    const uint32_t o = (tok ? id * xrow : id * kCacheBlockBytes) + 32 * half * stride;
+    const uint32_t o = id * (tok ? xrow : kCacheBlockBytes) + 32 * half * stride;
     hr.len = half_len(e, half);
     hr.f8 = false;
     hr.ks = hr.vs = 1.f;
     if (hr.len > 0) {
-      hr.k = (tok ? xk_h : ck_h) + o;
-      hr.v = (tok ? xv_h : cv_h) + o;
+      hr.off = o;
+      hr.tok = tok;
       hr.stride = stride;
       if (FP8 && !tok) {
         hr.f8 = true;
@@ -521,8 +521,8 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
       // an empty half tile still gets its gathers (of the head's first token row, so
       // that every step issues the same number and the waits stay fixed); its rows are
       // masked or weighted by zero
-      hr.k = xk_h;
-      hr.v = xv_h;
+      hr.off = 0;
+      hr.tok = 1;
       hr.stride = 0;
     }
   };
@@ -532,17 +532,15 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
   // sees that these reads cannot touch a tile being gathered and adds no wait for them.)
   const int offA = fl.offA, offB = fl.offB;
   auto fetch = [&](int s, uint32_t& ex, uint32_t& ey) {
-    ex = 0;
-    ey = 0;
-    if (s >= nsteps) return;
-    if (s < nshared) {
-      ex = lists[s < nPq ? s : offB - 1 - (s - nPq)];
-      ey = ex;
-    } else if (s >= nsh2) {
-      const int blk = (s - nsh2) >> 1;
-      if (blk < cntA) ex = lists[offA + blk];
-      if (blk < cntB) ey = lists[offB + blk];
-    }
+    // two reads, always issued (no branch, and no copy of a value still in flight); an
+    // entry that does not exist reads the word past the lists, which holds 0
+    const int blk = (s - nsh2) >> 1;
+    const bool sh = s < nshared, pv = s >= nsh2 && s < nsteps;
+    const int is = s < nPq ? s : offB - 1 - (s - nPq);
+    const int ix = sh ? is : (pv && blk < cntA ? offA + blk : kAttnListCap);
+    const int iy = sh ? is : (pv && blk < cntB ? offB + blk : kAttnListCap);
+    ex = lists[ix];
+    ey = lists[iy];
   };
   // This wave's half tile of step s (see the gathers below) and the lengths of X and Y.
   // Only this wave's half tile is decoded into addresses; of the other, its length.
@@ -580,16 +578,20 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
   // scalar global base (dma_base, 3 KB low) and per-piece lane offsets raised by 3 KB and
   // lowered by the piece's 1 KB immediate offset.
   struct Offs {
-    __amdgpu_buffer_rsrc_t kb, vb;  // dma_base(hr.k), dma_base(hr.v)
+    __amdgpu_buffer_rsrc_t kb, vb;  // the head's K and V bases (chunk or cache)
+    uint32_t soff;                  // the half tile's byte offset from them
     uint32_t k, v0, v1;   // lane offsets of K, and of V rows (l >> 2) and 16 + (l >> 2)
     uint32_t fk, fv;      // (FP8 slot) lane offsets of this lane's 32 K and 32 V codes
     uint32_t flast;       // (FP8 slot) the last valid row
   };
+  const __amdgpu_buffer_rsrc_t rs_ck = dma_base(ck_h), rs_cv = dma_base(cv_h);
+  const __amdgpu_buffer_rsrc_t rs_xk = dma_base(xk_h), rs_xv = dma_base(xv_h);
   auto offsets = [&](const HalfRef& hr) {
     const uint32_t last = static_cast<uint32_t>(hr.len > 0 ? hr.len - 1 : 0);
     Offs o;
-    o.kb = dma_base(hr.k);
-    o.vb = dma_base(hr.v);
+    o.kb = hr.tok ? rs_xk : rs_ck;
+    o.vb = hr.tok ? rs_xv : rs_cv;
+    o.soff = hr.off;
     o.k = min(16u * (w & 1) + k_rowl, last) * hr.stride + k_colb + 3072u;
     // this wave's V pieces p0 + i lie in segments (p0 + i) / 2 = p0 / 2 + i / 2
     o.v0 = min(v_rowl, last) * hr.stride + v_colb + 32u * p0 + 3072u;
@@ -620,11 +622,11 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
       if (hr.f8) {
         // as many instructions as the bf16 pieces, so the waits below stay exact
         kpend[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                                                 o.kb, o.fk + 8u * i, 0, 0));
+                                                 o.kb, o.fk + 8u * i, o.soff, 0));
         return;
       }
     }
-    lds_dma16_piece(i, o.kb, o.k + 64u * i - 1024u * i, buf[tw] + 1024 * p0);
+    lds_dma16_piece(i, o.kb, o.k + 64u * i - 1024u * i, o.soff, buf[tw] + 1024 * p0);
   };
   auto gather_v = [&](char (*buf)[HT::BYTES], const HalfRef& hr, const Offs& o, int i) {
     if constexpr (FP8) {
@@ -635,11 +637,11 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
       if (hr.f8) {
         const uint32_t row = min(static_cast<uint32_t>(l >> 3) + 8u * i, o.flast);
         vpend[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                                                 o.vb, o.fv + row * hr.stride, 0, 0));
+                                                 o.vb, o.fv + row * hr.stride, o.soff, 0));
         return;
       }
     }
-    lds_dma16_piece(i, o.vb, (i % 2 ? o.v1 : o.v0) + 64u * (i / 2) - 1024u * i,
+    lds_dma16_piece(i, o.vb, (i % 2 ? o.v1 : o.v0) + 64u * (i / 2) - 1024u * i, o.soff,
                     buf[tw] + 1024 * p0);
   };
   // (FP8) decode the pending codes (exact in bf16: a power-of-two scale) and store them
@@ -698,7 +700,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
   }
   // r1, r2: this wave's half tile of steps s+1 and s+2; (lx0, ly0) .. (lx2, ly2): the
   // lengths of X and Y in steps s, s+1, s+2.
-  HalfRef r0{nullptr, nullptr, 0, 0}, r1{nullptr, nullptr, 0, 0}, r2{nullptr, nullptr, 0, 0};
+  HalfRef r0{0, 1, 0, 0}, r1{0, 1, 0, 0}, r2{0, 1, 0, 0};
   int lx0 = 0, ly0 = 0, lx1 = 0, ly1 = 0, lx2 = 0, ly2 = 0;
   uint32_t ex = 0, ey = 0;
   fetch(0, ex, ey);

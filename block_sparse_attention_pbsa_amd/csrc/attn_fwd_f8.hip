@@ -316,7 +316,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f8_kernel(F8Args g) {
   __shared__ __attribute__((aligned(1024))) uint8_t kb1[2][kTile8];
   __shared__ __attribute__((aligned(1024))) uint8_t vb0[2][kTile8];
   __shared__ __attribute__((aligned(1024))) uint8_t vb1[2][kTile8];
-  __shared__ uint32_t lists[kAttnListCap];
+  __shared__ uint32_t lists[kAttnListCap + 1];
   __shared__ int wave_cnt[4];
   __shared__ int part_cnt[4][3];
   __shared__ int n_list;
@@ -398,9 +398,9 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f8_kernel(F8Args g) {
   const uint8_t* wk_h = g.wk + hq * kTile8;
   const uint8_t* wv_h = g.wv + hq * kTile8;
   // Entries of step s for X and Y (0 = nothing), read one step before they are decoded.
-  // The two reads are unconditional (an entry that does not exist reads slot 0 and is
-  // dropped by a select): reads of `lists` under branches lose the compiler's knowledge that
-  // they cannot touch a tile being gathered, and it then waits for every gather first.
+  // The two reads are unconditional (an entry that does not exist reads the word past the
+  // lists, which holds 0): reads of `lists` under branches lose the compiler's knowledge
+  // that they cannot touch a tile being gathered, and it then waits for every gather first.
   auto fetch = [&](int s, uint32_t& ex, uint32_t& ey) {
     int ix, iy;
     bool vx, vy;
@@ -417,9 +417,8 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f8_kernel(F8Args g) {
       vx = k < cntA && s < nsteps;
       vy = k < cntB && s < nsteps;
     }
-    const uint32_t rx = lists[vx ? ix : 0], ry = lists[vy ? iy : 0];
-    ex = vx ? rx : 0u;
-    ey = vy ? ry : 0u;
+    ex = lists[vx ? ix : kAttnListCap];
+    ey = lists[vy ? iy : kAttnListCap];
   };
   // Step info: the raw entries of X and Y (0 = nothing) and their E8M0 scales packed in one
   // word (bytes: K of X, K of Y, V of X, V of Y; 1 for an empty entry), which the MFMAs take
@@ -506,6 +505,9 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f8_kernel(F8Args g) {
       extra(j);
       fence8();
     }
+    // (the scores are taken here: otherwise the compiler sinks these MFMAs past the next
+    // branch, away from the work they were meant to run beside)
+    asm volatile("" ::"v"(s[0]), "v"(s[1]));
   };
   // O^T += V^T P^T of one block; its MFMAs carry `extra`.
   auto pv_mma = [&](auto sel, const uint8_t* vt, int sv, const i32x8& pb, auto&& extra) {
@@ -519,6 +521,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_f8_kernel(F8Args g) {
       extra(dt);
       fence8();
     }
+    asm volatile("" ::"v"(st.acc[0]), "v"(st.acc[1]), "v"(st.acc[2]), "v"(st.acc[3]));
   };
 
   // prologue: K(0), V(0), K(1)

@@ -51,9 +51,10 @@ struct FwdLists {
   int offA, offB;  // first entries of A's and B's private lists in `lists`
 };
 
-// Builds the lists in LDS (`lists`, kAttnListCap entries) for the query blocks rA and
-// rB = rA + 1 of head h; rawA, rawB (sel_stride ints each) and pids (C ints) are LDS
-// staging areas that no gather targets yet.  Every thread of the workgroup calls it.
+// Builds the lists in LDS (`lists`: kAttnListCap entries, and one more word that is set to
+// 0) for the query blocks rA and rB = rA + 1 of head h; rawA, rawB (sel_stride ints each)
+// and pids (C ints) are LDS staging areas that no gather targets yet.  Every thread of the
+// workgroup calls it.
 template <bool PERSIST, bool CHUNK_IDS>
 __device__ __forceinline__ FwdLists build_lists(const FwdArgs& a, int h, int rA, int rB,
                                                 uint32_t* lists, int* wave_cnt,
@@ -194,6 +195,8 @@ __device__ __forceinline__ FwdLists build_lists(const FwdArgs& a, int h, int rA,
     cntB = __builtin_amdgcn_readfirstlane(ob);
     nboth = __builtin_amdgcn_readfirstlane(oi);
   }
+  // (the word past the lists holds 0: reads for steps without an entry point at it)
+  if (t == 0) lists[kAttnListCap] = 0u;
   __syncthreads();
   FwdLists r;
   r.cntA = cntA;
