@@ -284,15 +284,16 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
     // (l % 16) ^ swz(row) of the swizzled row-major layout.  Rows past the valid length
     // re-read the last valid row (finite data that a zero probability removes); an empty
     // half tile is not gathered, and no wave reads it.
-    auto gather = [&](int st, uint16_t* set) {
-      const int j = st >> 1, half = st & 1;
-      if (j >= (mine ? cntB : cntA)) return;
-      // (one list array indexed by mine, not a pointer chosen at run time: the compiler
-      // then still sees that this read cannot touch a gather in flight)
-      const uint32_t e = static_cast<uint32_t>(
-          __builtin_amdgcn_readfirstlane(static_cast<int>(lst[mine * kHalfCap + j])));
+    // This wave's list entries (its own query block's): the entry of a block is read from
+    // LDS a step before it is used (one list array indexed by mine, not a pointer chosen at
+    // run time: the compiler then still sees that the read cannot touch a gather in flight).
+    const int cnt = mine ? cntB : cntA;
+    auto entry_raw = [&](int j) { return lst[mine * kHalfCap + (j < cnt ? j : 0)]; };
+    auto half_len = [&](uint32_t e, int j, int half) {
       const int tl = entry_len(e) - 32 * half;
-      const int len = tl < 0 ? 0 : (tl < 32 ? tl : 32);
+      return j >= cnt ? 0 : (tl < 0 ? 0 : (tl < 32 ? tl : 32));
+    };
+    auto gather = [&](uint32_t e, int len, int half, uint16_t* set) {
       if (len == 0) return;
       uint32_t sb;
       const char* p;
@@ -321,26 +322,33 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
         dma_piece(i & 3, rs, voff, dst + 4096 * (i >> 2));
       }
     };
-    // step st: its tiles are in `cur`; the next step's go into `nxt`
-    auto run = [&](int st, const uint16_t* cur, uint16_t* nxt) {
-      // Every wave waits for its own gathers into `cur` (vmcnt(0)) before the barrier, so
-      // that after it every tile of step st has landed; the barrier's own release covers
-      // LDS instructions only, and the compiler, left to itself, may let the last gathers
-      // of a step still be in flight at the barrier.  After the barrier every wave is also
-      // done with the set step st - 1 read.
+    // Step st's tiles are in one set (tiles0 for even st, tiles1 for odd; lenC valid rows of
+    // this wave's half tile) while the next step's are gathered into the other.  Every wave
+    // waits for its own gathers (vmcnt(0)) before the barrier, so that after it every tile
+    // of step st has landed; the barrier's own release covers LDS instructions only, and the
+    // compiler, left to itself, may let the last gathers of a step still be in flight at
+    // the barrier.  After the barrier every wave is also done with the set step st - 1 read.
+    uint32_t eC = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(entry_raw(0))));
+    uint32_t eN = entry_raw(1);
+    int lenC = half_len(eC, 0, 0);
+    gather(eC, lenC, 0, tiles0);
+    // nsteps is even (two halves per block): step st = 2 j is half 0 of block j, st + 1 half 1
+    for (int st = 0; st < nsteps; st += 2) {
+      const int j = st >> 1;
       __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0); expcnt and lgkmcnt not waited
       __syncthreads();
-      if (st + 1 < nsteps) gather(st + 1, nxt);
-      Half kx, vx, ky, vy;
-      refs(st, kx, vx, ky, vy);
-      const int len = mine ? ky.len : kx.len;
-      if (qlen > 0 && len > 0) half_step(cur, 2 * mine * HT, len);
-    };
-    if (nsteps > 0) gather(0, tiles0);
-    // nsteps is even (two halves per block)
-    for (int st = 0; st < nsteps; st += 2) {
-      run(st, tiles0, tiles1);
-      run(st + 1, tiles1, tiles0);
+      int lenN = half_len(eC, j, 1);
+      gather(eC, lenN, 1, tiles1);
+      if (qlen > 0 && lenC > 0) half_step(tiles0, 2 * mine * HT, lenC);
+      lenC = lenN;
+      __builtin_amdgcn_s_waitcnt(0x0f70);
+      __syncthreads();
+      eC = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(eN)));
+      eN = entry_raw(j + 2);
+      lenN = half_len(eC, j + 1, 0);
+      gather(eC, lenN, 0, tiles0);
+      if (qlen > 0 && lenC > 0) half_step(tiles1, 2 * mine * HT, lenC);
+      lenC = lenN;
     }
   } else {
     Tile<D, 256, 32> tkx, tvx, tky, tvy;
