@@ -96,8 +96,9 @@ __device__ __forceinline__ void lds_barrier() {
 // 16 bytes per lane from global memory straight into LDS (lane l writes lds + 16 l; the LDS
 // address must be wave-uniform), as piece i (0..3) of a run of 1 KB LDS pieces: the
 // instruction's immediate offset 1024 i is added to both the global and the LDS address,
-// so a run shares one LDS base (M0) and one scalar global base, and each piece costs one
-// vector add for its lane offsets.  src must already be lowered by 1024 i.
+// so a run shares one LDS base (M0), one buffer resource and one scalar offset (soff, the
+// half tile's position), and each piece costs one vector add for its lane offsets, which
+// must already be lowered by 1024 i.
 __device__ __forceinline__ void lds_dma16_piece(int i, __amdgpu_buffer_rsrc_t rs, uint32_t voff,
                                                 uint32_t soff, char* lds) {
   switch (i) {
@@ -107,15 +108,15 @@ __device__ __forceinline__ void lds_dma16_piece(int i, __amdgpu_buffer_rsrc_t rs
     default: __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds, 16, voff, soff, 3072, 0); break;
   }
 }
-// Scalar base 3 KB below p: per-piece lane offsets (up to 3 KB lower for piece 3) then
-// stay non-negative.  The empty asm keeps the base in scalar registers as a value of its
-// own, so that the compiler cannot fold the bias back into each lane's address.
+// Buffer resource whose base is 3 KB below p: per-piece lane offsets (up to 3 KB lower for
+// piece 3) then stay non-negative.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t dma_base(const char* p) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p - 3072), (short)0, 0x7fffffff,
                                            0x00020000);
 }
 
-// A half tile to gather: wave-uniform base (bytes), row stride (bytes) and valid rows.
+// A half tile to gather: wave-uniform position (bytes from its tensor's head base), row
+// stride (bytes) and valid rows.
 struct HalfRef {
   uint32_t off;  // byte offset of the half tile from its tensor's head base
   uint32_t tok;  // 1: a block of the chunk's K/V; 0: a cache slot
@@ -574,9 +575,10 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
   // so this wave's K pieces all use rows 16 (w & 1) + (l & 15) (one lane offset per step)
   // and its V pieces rows (l >> 2) or 16 + (l >> 2) (two lane offsets per step); the
   // piece's chunk or segment is a scalar offset.
-  // The wave's HP pieces of a tile form one run (lds_dma16_piece): one LDS base, one
-  // scalar global base (dma_base, 3 KB low) and per-piece lane offsets raised by 3 KB and
-  // lowered by the piece's 1 KB immediate offset.
+  // The wave's HP pieces of a tile form one run (lds_dma16_piece): one LDS base, the
+  // head's buffer resource for the tensor (dma_base, 3 KB low; chosen per step between the
+  // chunk's and the cache's), the half tile's position as the scalar offset, and per-piece
+  // lane offsets raised by 3 KB and lowered by the piece's 1 KB immediate offset.
   struct Offs {
     __amdgpu_buffer_rsrc_t kb, vb;  // the head's K and V bases (chunk or cache)
     uint32_t soff;                  // the half tile's byte offset from them
