@@ -34,8 +34,11 @@ def sources():
 
 
 # Per-file flags.  The backward keeps large MFMA accumulators live across its loops; the
-# VGPR form of MFMA keeps them out of AGPR<->VGPR copies.
-FILE_FLAGS = {"attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# VGPR form of MFMA keeps them out of AGPR<->VGPR copies.  The FP8-arithmetic attention is
+# scheduled with the iterative ILP strategy, which halves its scalar-register spills (47 to
+# 23) and measured 2-3% faster than the default scheduler.
+FILE_FLAGS = {"attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+              "attn_fwd_f8.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
 
 
 def _compile(src: str) -> str:
