@@ -65,16 +65,17 @@ __device__ __forceinline__ void score_rows(const float (&qv)[QB][8], const float
   }
 }
 
-// grid (ceil(Nq / QB), H), QB waves scoring QB query blocks together: every representative
-// row is read once per QB query blocks, whole rows per load instruction, the waves taking
-// interleaved row groups.  Then wave q selects query block q's top K window candidates
-// and writes their ids in ascending order (each id's position = the number of selected ids
-// below it).  Dynamic LDS: [QB][slots] floats (a wave's row is reused for its selected ids).
-// POOL: wave q first pools query block q from the query tokens xq (the same arithmetic as
+// grid (ceil(Nq / QB), H), 2 QB waves scoring QB query blocks together: every
+// representative row is read once per QB query blocks, whole rows per load instruction, the
+// waves taking interleaved row groups (two waves per query block halve each wave's chain of
+// loads: 3.8 us less at 406 slots).  Then wave q < QB selects query block q's top K window
+// candidates and writes their ids in ascending order (each id's position = the number of
+// selected ids below it).  Dynamic LDS: [QB][slots] floats (a wave's row is reused for its
+// selected ids).  POOL: wave q < QB first pools query block q from the query tokens xq (the same arithmetic as
 // pool_blocks_kernel) and, if q_rep is not null, stores the mean there; otherwise q_rep is
 // read.
 template <int D, int E, int QB, bool POOL>
-__global__ void __launch_bounds__(64 * QB)
+__global__ void __launch_bounds__(128 * QB)
     score_topk_kernel(TokIn xq, int n, int nb, float* q_rep, const float* __restrict__ rep,
                       const int32_t* __restrict__ block_id, int slots, int C, int S, int K,
                       int nq, float scale, float* __restrict__ scores,
@@ -139,12 +140,12 @@ __global__ void __launch_bounds__(64 * QB)
   }
   const int32_t* bid = block_id + static_cast<int64_t>(h) * slots;
   const float* rp = rep + static_cast<int64_t>(h) * slots * D;
-  score_rows<D, QB, 8>(qv, rp, bid, slots, scale, sc_lds, slots, l, w * RPI, QB * RPI);
+  score_rows<D, QB, 8>(qv, rp, bid, slots, scale, sc_lds, slots, l, w * RPI, 2 * QB * RPI);
   __syncthreads();
   // scores out (coalesced rows)
   for (int q = 0; q < nrows; ++q) {
     float* srow = scores + (static_cast<int64_t>(h) * nq + r0 + q) * slots;
-    for (int s = t; s < slots; s += 64 * QB) srow[s] = sc_lds[q * slots + s];
+    for (int s = t; s < slots; s += 128 * QB) srow[s] = sc_lds[q * slots + s];
   }
   // candidates: occupied slots from cand0 on holding non-sink blocks (cand0 = C: the
   // window's ring slots; cand0 = 0: the persistent slots too)
@@ -212,7 +213,7 @@ static hipError_t launch_score_d(const pbsa_dims& d, TokIn xq, float* q_rep, con
   const size_t lds = static_cast<size_t>(QB) * slots * sizeof(float);
   dim3 grid(cdiv(nq, QB), d.heads);
 #define PBSA_SCORE_E(EE)                                                                     \
-  hipLaunchKernelGGL((score_topk_kernel<D, EE, QB, POOL>), grid, dim3(64 * QB), lds, s, xq,     \
+  hipLaunchKernelGGL((score_topk_kernel<D, EE, QB, POOL>), grid, dim3(128 * QB), lds, s, xq,    \
                      d.frame_tokens, nb, q_rep, c.rep, c.block_id, slots, d.capacity, d.sinks, \
                      d.topk, nq, d.scale, scores, sel, cand0)
   if (nwin <= 64) PBSA_SCORE_E(1);
