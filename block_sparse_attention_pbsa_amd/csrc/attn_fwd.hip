@@ -546,8 +546,8 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdArgs a) {
   // This wave's half tile of step s (see the gathers below) and the lengths of X and Y.
   // Only this wave's half tile is decoded into addresses; of the other, its length.
   auto decode = [&](int s, uint32_t ex_, uint32_t ey_, HalfRef& mineref, int& lenX, int& lenY) {
-    // list entries are wave-uniform: readfirstlane keeps them (and the gather base
-    // addresses) in scalar registers
+    // list entries are wave-uniform: readfirstlane keeps them (and the gathers' offsets)
+    // in scalar registers
     const uint32_t ex = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(ex_)));
     const uint32_t ey = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(ey_)));
     // a shared step takes halves 0 (X) and 1 (Y) of one block; a private step the same
