@@ -197,3 +197,75 @@ def test_attn_fwd_long_routed_lists(topk):
         ref_o.append(o_ref[0])
         assert abs(lg[0, t] - lse_ref[0]) < 1e-3
     assert_close_attn(np.array(got_o), np.array(ref_o), f"O of {len(rows)} rows, K={topk}")
+
+
+def test_attn_fwd_lists_at_capacity():
+    """The attention's per-workgroup lists filled to their capacity: C + chunk blocks + 2 K =
+    3072 entries (the most the boundary accepts, with C - sinks, the window and the chunk at
+    their own limits), each pair's routed sets disjoint, so that B's private list runs to the
+    last entry and every private step past it reads the empty entry kept after the lists.
+    Sampled rows of both query blocks of several pairs against the fp64 definition."""
+    H, D, n, nb = 1, 128, 2048, 32   # 32 full blocks per frame
+    F = W = 32                       # a 32-frame chunk (1024 blocks); 1024 window blocks
+    C, S, K = 1024, 1, 512           # two disjoint top-512 sets fill the window
+    nq = F * nb
+    assert C + nq + 2 * K == 3072
+    shape = ops.Shape(H, D, n, F, W, C, S, K)
+    rng = np.random.default_rng(3072)
+    cache = ops.Cache(shape)
+    chunk = 3                        # frames 96..127; the window holds frames 64..95
+    f_last = chunk * F - 1
+    bid = np.full((H, C + W * nb), -1, np.int32)
+    bid[0, :S] = np.arange(S)
+    bid[0, S:C] = np.sort(rng.choice(np.arange(S, (f_last - W + 1) * nb), C - S, replace=False))
+    for f in range(f_last - W + 1, f_last + 1):
+        for j in range(nb):
+            bid[0, C + (f % W) * nb + j] = f * nb + j
+    blen = np.where(bid >= 0, 64, 0).astype(np.int32)
+    kc = synth.round_bf16(rng.standard_normal((H, shape.slots, 64, D)).astype(np.float32))
+    vc = synth.round_bf16(rng.standard_normal((H, shape.slots, 64, D)).astype(np.float32))
+    cache.block_id.copy_(torch.from_numpy(bid))
+    cache.len.copy_(torch.from_numpy(blen))
+    cache.k.copy_(torch.from_numpy(kc).to(torch.bfloat16))
+    cache.v.copy_(torch.from_numpy(vc).to(torch.bfloat16))
+    cache.chunk_index = chunk
+    win = np.sort(bid[0, C:])
+    assert len(win) == 2 * K and win.min() >= 0
+    # even query blocks take the older half of the window, odd ones the newer half
+    sel_h = np.stack([win[:K] if r % 2 == 0 else win[K:] for r in range(nq)]).astype(np.int32)
+    T = F * n
+    q = synth.round_bf16(rng.standard_normal((T, H, D)).astype(np.float32))
+    k = synth.round_bf16(rng.standard_normal((T, H, D)).astype(np.float32))
+    v = synth.round_bf16(rng.standard_normal((T, H, D)).astype(np.float32))
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda().to(torch.bfloat16)
+    sel = torch.from_numpy(sel_h[None]).cuda()
+    o = torch.empty(T, H, D, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(H, T, dtype=torch.float32, device="cuda")
+    say(f"[attn lists at capacity] C={C} chunk blocks={nq} K={K}: {C + nq + 2 * K} list entries")
+    ops.pbsa_attn_fwd(shape, dev(q), cache, dev(k), dev(v), sel, o, lse)
+    torch.cuda.synchronize()
+    og = o.float().cpu().numpy()
+    lg = lse.cpu().numpy()
+    scale = shape.c().scale
+    slot_of = {int(g): s for s, g in enumerate(bid[0])}
+    P = [s for s in range(C) if bid[0, s] >= 0]
+    # the keys of an even and of an odd query block: P, its routed blocks, the whole chunk
+    keys = {}
+    for par in (0, 1):
+        picked = [slot_of[int(g)] for g in sel_h[par]]
+        keys[par] = tuple(np.concatenate([x[0, s] for s in P + picked] + [y[:, 0]])
+                          .astype(np.float64) for x, y in ((kc, k), (vc, v)))
+    # query blocks 0/1 (the first pair), 510/511 and the last pair; rows at both ends of
+    # each block and three inside
+    rows = []
+    for r in (0, 1, 510, 511, nq - 2, nq - 1):
+        rows += sorted({64 * r, 64 * r + 63} | set((64 * r + rng.choice(64, 3, replace=False)).tolist()))
+    got_o, ref_o = [], []
+    for t in rows:
+        K_, V_ = keys[(t // 64) % 2]
+        o_ref, lse_ref = orc.masked_attention(q[t:t + 1, 0].astype(np.float64), K_, V_,
+                                              np.ones((1, len(K_)), bool), scale)
+        got_o.append(og[t, 0])
+        ref_o.append(o_ref[0])
+        assert abs(lg[0, t] - lse_ref[0]) < 1e-3, f"row {t}: LSE {lg[0, t]} vs {lse_ref[0]}"
+    assert_close_attn(np.array(got_o), np.array(ref_o), f"O of {len(rows)} rows at the list capacity")
