@@ -145,20 +145,25 @@ __global__ void __launch_bounds__(NT) memory_select_kernel(MemArgs a) {
   {
     const float* sc = a.scores + static_cast<int64_t>(h) * a.nq * a.slots;
     const int full = a.nq & ~3;
+    // the head's first `full` score rows as a buffer: a load past them returns 0
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(sc), (short)0, full * a.slots * 4, 0x00020000);
     for (int c = t & 255; c < ncand; c += 256) {
       const int s = cslot[c];
       for (int g = t >> 8; g < 4; g += NT / 256) {
         float acc = 0.f;
-        int r = g;
-        // eight rows loaded before they are added (the order of the additions is kept)
-        for (; r + 28 < full; r += 32) {
-          float v[8];
+        // 24 rows loaded before they are added, rows past `full` as 0 (adding +0 leaves the
+        // sum as it is; the order of the additions is kept): up to 96 query blocks take a
+        // single round trip
+        for (int r = g; r < full; r += 96) {
+          float v[24];
 #pragma unroll
-          for (int u = 0; u < 8; ++u) v[u] = sc[static_cast<int64_t>(r + 4 * u) * a.slots + s];
+          for (int u = 0; u < 24; ++u)
+            v[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                 rs, 4u * static_cast<uint32_t>((r + 4 * u) * a.slots + s), 0, 0));
 #pragma unroll
-          for (int u = 0; u < 8; ++u) acc += v[u];
+          for (int u = 0; u < 24; ++u) acc += v[u];
         }
-        for (; r < full; r += 4) acc += sc[static_cast<int64_t>(r) * a.slots + s];
         if (g == 0)
           for (int r = full; r < a.nq; ++r) acc += sc[static_cast<int64_t>(r) * a.slots + s];
         part[g * ncand_max + c] = acc;
@@ -190,6 +195,12 @@ __global__ void __launch_bounds__(NT) memory_select_kernel(MemArgs a) {
         if (c < ncand && on[e]) cslot[c] = ~cslot[c];  // kept: negative
       }
     }
+    // kept flags per persistent slot, over the partial sums (read above by this wave only;
+    // one wave's LDS accesses complete in order)
+    int* keptf = reinterpret_cast<int*>(part);
+    for (int s = l; s < a.C; s += 64) keptf[s] = 0;
+    for (int c = l; c < nP; c += 64)
+      if (cslot[c] < 0) keptf[~cslot[c]] = 1;
   }
   __syncthreads();
   if (w == 0) {
@@ -199,18 +210,8 @@ __global__ void __launch_bounds__(NT) memory_select_kernel(MemArgs a) {
       const int s = s0 + l;
       bool fr = false;
       if (s < a.C) {
-        fr = sbid[s] < a.S;  // empty
-        if (!fr) {
-          // the candidate for slot s: binary search over the ascending P part of cslot
-          int lo = 0, hi = nP;
-          while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            const int cs = cslot[mid] < 0 ? ~cslot[mid] : cslot[mid];
-            if (cs < s) lo = mid + 1;
-            else hi = mid;
-          }
-          fr = cslot[lo] >= 0;  // not kept
-        }
+        const int* keptf = reinterpret_cast<const int*>(part);
+        fr = sbid[s] < a.S || keptf[s] == 0;  // empty, or its block is not kept
       }
       const unsigned long long m = __ballot(fr);
       if (fr) freel[nfree + __popcll(m & ((1ull << l) - 1ull))] = s;
