@@ -209,3 +209,85 @@ def test_fp8_cache_step_matches_bf16_routing_and_halves_bytes():
     say(f"  fp8 vs bf16 cache: O max-abs {err.max().item():.3e} mean-abs {err.mean().item():.3e}")
     assert b.cache.k.element_size() * 2 == a.cache.k.element_size()
     assert ops.pbsa_cache_bytes(b.shape) < 0.53 * ops.pbsa_cache_bytes(a.shape)
+
+
+def test_fp8_arithmetic_lists_at_capacity():
+    """pbsa_attn_fwd_fp8 with its lists at the FP8 path's limit (C + K + chunk blocks = 1536)
+    and each pair's routed sets disjoint, so that B's private list is as long as it can be;
+    the cache holds random finite E4M3 codes with power-of-two scales per block and tensor.
+    Sampled rows of three pairs against the oracle's fp8_attention within its bound."""
+    H, D, n, nb = 1, 128, 2048, 32   # 32 full blocks per frame
+    F, W = 8, 16                     # 256 chunk blocks; 512 window blocks
+    C, S, K = 1024, 1, 256
+    nq = F * nb
+    assert C + K + nq == 1536
+    shape = ops.Shape(H, D, n, F, W, C, S, K, kv_format=ops.PBSA_KV_FP8)
+    rng = np.random.default_rng(1536)
+    cache = ops.Cache(shape)
+    chunk = 6                        # frames 48..55; the window holds frames 32..47
+    f_last = chunk * F - 1
+    bid = np.full((H, C + W * nb), -1, np.int32)
+    bid[0, :S] = np.arange(S)
+    bid[0, S:C] = np.sort(rng.choice(np.arange(S, (f_last - W + 1) * nb), C - S, replace=False))
+    for f in range(f_last - W + 1, f_last + 1):
+        for j in range(nb):
+            bid[0, C + (f % W) * nb + j] = f * nb + j
+    # codes with exponent fields 3..8 (magnitudes 2^-4 .. 3.75) and a random sign
+    def codes(size):
+        e = rng.integers(3, 9, size)
+        m = rng.integers(0, 8, size)
+        return ((rng.integers(0, 2, size) << 7) | (e << 3) | m).astype(np.uint8)
+    kc, vc = codes((H, shape.slots, 64, D)), codes((H, shape.slots, 64, D))
+    scales = np.ldexp(1.0, rng.integers(-2, 2, (H, shape.slots, 2))).astype(np.float32)
+    cache.block_id.copy_(torch.from_numpy(bid))
+    cache.len.copy_(torch.from_numpy(np.where(bid >= 0, 64, 0).astype(np.int32)))
+    cache.k.copy_(torch.from_numpy(kc))
+    cache.v.copy_(torch.from_numpy(vc))
+    cache.kv_scale.copy_(torch.from_numpy(scales))
+    cache.chunk_index = chunk
+    win = np.sort(bid[0, C:])
+    assert len(win) == 2 * K and win.min() >= 0
+    sel_h = np.stack([win[:K] if r % 2 == 0 else win[K:] for r in range(nq)]).astype(np.int32)
+    T = F * n
+    q = synth.round_bf16(rng.standard_normal((T, H, D)).astype(np.float32))
+    k = synth.round_bf16(rng.standard_normal((T, H, D)).astype(np.float32))
+    v = synth.round_bf16(rng.standard_normal((T, H, D)).astype(np.float32))
+    ws = torch.empty(ops.pbsa_workspace_bytes(shape, ops.PBSA_OP_ATTN_FWD_FP8), dtype=torch.uint8,
+                     device="cuda")
+    o = torch.full((T, H, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((H, T), float("nan"), dtype=torch.float32, device="cuda")
+    say(f"[fp8 arithmetic lists at capacity] C={C} chunk blocks={nq} K={K}")
+    ops.pbsa_attn_fwd_fp8(shape, dev(q), cache, dev(k), dev(v), torch.from_numpy(sel_h[None]).cuda(),
+                          o, lse, ws)
+    torch.cuda.synchronize()
+    og = o[:, 0].float().cpu().numpy()
+    lg = lse[0].cpu().numpy()
+    # the oracle's values: cache blocks decoded; the chunk's blocks quantized per block
+    dec = lambda c, s_: orc.e4m3_decode(c) * float(s_)
+    slot_of = {int(g): s for s, g in enumerate(bid[0])}
+    own_k, own_v = [], []
+    for b in range(nq):
+        kq, ks = orc.e4m3_quantize_block(k[64 * b:64 * b + 64, 0])
+        vq, vs = orc.e4m3_quantize_block(v[64 * b:64 * b + 64, 0])
+        own_k.append(orc.e4m3_decode(kq) * ks)
+        own_v.append(orc.e4m3_decode(vq) * vs)
+    keys = {}
+    for par in (0, 1):
+        slots_ = list(range(C)) + [slot_of[int(g)] for g in sel_h[par]]
+        keys[par] = (np.concatenate([dec(kc[0, s], scales[0, s, 0]) for s in slots_] + own_k),
+                     np.concatenate([dec(vc[0, s], scales[0, s, 1]) for s in slots_] + own_v))
+    rows = []
+    for r in (0, 1, 128, 129, nq - 2, nq - 1):
+        rows += sorted({64 * r, 64 * r + 63} | set((64 * r + rng.choice(64, 3, replace=False)).tolist()))
+    worst = 0.0
+    for t in rows:
+        K_, V_ = keys[(t // 64) % 2]
+        o_ref, l_ref, bnd = orc.fp8_attention(q[t:t + 1, 0].astype(np.float64), K_, V_,
+                                              shape.c().scale)
+        err = np.abs(og[t] - o_ref[0])
+        tol = bnd[0] + 2.0 ** -8 * np.abs(o_ref[0]) + 1e-4
+        worst = max(worst, float((err / tol).max()))
+        assert np.isfinite(og[t]).all(), f"row {t}: non-finite output"
+        assert np.all(err <= tol), f"row {t}: FP8 O outside its bound (max err/tol {(err / tol).max():.3f})"
+        assert abs(lg[t] - l_ref[0]) < 1e-3, f"row {t}: LSE {lg[t]} vs {l_ref[0]}"
+    say(f"  {len(rows)} rows at the FP8 list limit: max err/tol {worst:.3f}")
