@@ -269,3 +269,77 @@ def test_attn_fwd_lists_at_capacity():
         ref_o.append(o_ref[0])
         assert abs(lg[0, t] - lse_ref[0]) < 1e-3, f"row {t}: LSE {lg[0, t]} vs {lse_ref[0]}"
     assert_close_attn(np.array(got_o), np.array(ref_o), f"O of {len(rows)} rows at the list capacity")
+
+
+def test_two_level_lists_at_capacity():
+    """Two-level attention and its backward with the largest selections the boundary accepts
+    (max_sel = 1536, so a query-block pair's lists fill the 3072-entry capacity, and the dQ
+    pass's per-block list is full): the last chunk's query blocks take 1536 earlier blocks
+    each, the two blocks of a pair disjoint sets; every other query block takes its own
+    block only.  Sampled rows of O, LSE and dQ, and dK/dV of one block with 17 users,
+    against the fp64 definition."""
+    H, D, n, nb, M = 1, 128, 2048, 32, 1536
+    chunks = 97                      # one frame per chunk; the last sees frames 0..96
+    shape = ops.Shape(H, D, n, 1, 1, 1, 1, 1)
+    nq, T = chunks * nb, chunks * n
+    last = range(nq - nb, nq)        # the last chunk's query blocks
+    sel_h = np.full((H, nq, M), -1, np.int32)
+    nsel_h = np.ones((H, nq), np.int32)
+    for r in range(nq):
+        if r in last:
+            sel_h[0, r] = np.arange(M) if r % 2 == 0 else np.arange(M, 2 * M)
+            nsel_h[0, r] = M
+        else:
+            sel_h[0, r, 0] = r
+    rng = np.random.default_rng(1536 * 2)
+    q, k, v, do = (synth.round_bf16(rng.standard_normal((T, H, D)).astype(np.float32))
+                   for _ in range(4))
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda().to(torch.bfloat16)
+    qd, kd, vd, dod = dev(q), dev(k), dev(v), dev(do)
+    sel, nsel = torch.from_numpy(sel_h).cuda(), torch.from_numpy(nsel_h).cuda()
+    o = torch.empty_like(qd)
+    lse = torch.empty(H, T, dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(qd), torch.empty_like(qd), torch.empty_like(qd)
+    ws = torch.empty(ops.pbsa_workspace_bytes(shape, ops.PBSA_OP_ATTN_BWD, chunks, M),
+                     dtype=torch.uint8, device="cuda")
+    say(f"[two-level lists at capacity] {chunks} chunks, max_sel {M}: forward and backward")
+    ops.pbsa_attn_fwd_2lvl(shape, chunks, qd, kd, vd, sel, nsel, o, lse)
+    ops.pbsa_attn_bwd(shape, chunks, qd, kd, vd, o, lse, dod, sel, nsel, dq, dk, dv, ws)
+    torch.cuda.synchronize()
+    og, lg = o[:, 0].float().cpu().numpy(), lse[0].cpu().numpy()
+    dqg, dkg, dvg = (x[:, 0].float().cpu().numpy() for x in (dq, dk, dv))
+    del ws
+    scale = shape.c().scale
+    tok = lambda blocks: np.concatenate([np.arange(64 * g, 64 * g + 64) for g in blocks])
+    keys_of = {0: tok(range(M)), 1: tok(range(M, 2 * M))}
+    q0, k0, v0, do0 = (x[:, 0].astype(np.float64) for x in (q, k, v, do))
+    # rows of both halves of two pairs of the last chunk, and of two own-block-only blocks
+    rows = []
+    for r in (nq - nb, nq - nb + 1, nq - 2, nq - 1, 5, 2000):
+        rows += sorted({64 * r, 64 * r + 63} | set((64 * r + rng.choice(64, 2, replace=False)).tolist()))
+    got, ref, gq, rq = [], [], [], []
+    for t in rows:
+        r = t // 64
+        kk = keys_of[r % 2] if r in last else tok([r])
+        mask = np.ones((1, len(kk)), bool)
+        o_ref, l_ref = orc.masked_attention(q0[t:t + 1], k0[kk], v0[kk], mask, scale)
+        dq_ref, _, _ = orc.masked_attention_grad(q0[t:t + 1], k0[kk], v0[kk], mask, scale,
+                                                 do0[t:t + 1])
+        got.append(og[t]); ref.append(o_ref[0]); gq.append(dqg[t]); rq.append(dq_ref[0])
+        assert abs(lg[t] - l_ref[0]) < 1e-3, f"row {t}: LSE {lg[t]} vs {l_ref[0]}"
+    assert_close_attn(np.array(got), np.array(ref), f"O of {len(rows)} rows, max_sel {M}")
+    assert_close_attn(np.array(gq), np.array(rq), f"dQ of {len(rows)} rows, max_sel {M}")
+    # dK, dV of block 5: the 16 even query blocks of the last chunk and block 5 itself
+    g = 5
+    users = tok([r for r in last if r % 2 == 0])
+    kk = keys_of[0]
+    _, rk_a, rv_a = orc.masked_attention_grad(q0[users], k0[kk], v0[kk],
+                                              np.ones((len(users), len(kk)), bool), scale,
+                                              do0[users])
+    own = tok([g])
+    _, rk_s, rv_s = orc.masked_attention_grad(q0[own], k0[own], v0[own],
+                                              np.ones((64, 64), bool), scale, do0[own])
+    rk = rk_a[64 * g:64 * g + 64] + rk_s
+    rv = rv_a[64 * g:64 * g + 64] + rv_s
+    assert_close_attn(dkg[own], rk, f"dK of block {g} (17 users)")
+    assert_close_attn(dvg[own], rv, f"dV of block {g} (17 users)")
