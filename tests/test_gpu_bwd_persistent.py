@@ -127,3 +127,76 @@ def test_persistent_backward_parity(name, heads, union):
     for nm, x, y in zip(("dq", "dk", "dv", "dk_cache", "dv_cache"), (dq, dk, dv, dkc, dvc), again):
         diff = (x.view(torch.int16) != y.view(torch.int16))
         assert not diff.any(), f"{nm}: {int(diff.sum())} values differ between two calls"
+
+
+def test_persistent_backward_lists_at_limit():
+    """The persistent-mode backward with its per-query-block list at the boundary's limit
+    (C + K + chunk blocks = 1536: the dQ pass's list full), each pair's routed sets
+    disjoint and 128 window blocks routed to no query block.  dQ of sampled rows of three
+    pairs against the fp64 definition; the unattended window slots' dK/dV exactly zero."""
+    H, D, n, nb = 1, 128, 2048, 32
+    F, W = 8, 20                     # 256 chunk blocks; 640 window blocks
+    C, S, K = 1024, 1, 256
+    nq = F * nb
+    assert C + K + nq == 1536
+    shape = ops.Shape(H, D, n, F, W, C, S, K)
+    rng = np.random.default_rng(1536 * 3)
+    cache = ops.Cache(shape)
+    chunk = 7                        # frames 56..63; the window holds frames 36..55
+    f_last = chunk * F - 1
+    bid = np.full((H, C + W * nb), -1, np.int32)
+    bid[0, :S] = np.arange(S)
+    bid[0, S:C] = np.sort(rng.choice(np.arange(S, (f_last - W + 1) * nb), C - S, replace=False))
+    for f in range(f_last - W + 1, f_last + 1):
+        for j in range(nb):
+            bid[0, C + (f % W) * nb + j] = f * nb + j
+    kc = synth.round_bf16(rng.standard_normal((H, shape.slots, 64, D)).astype(np.float32))
+    vc = synth.round_bf16(rng.standard_normal((H, shape.slots, 64, D)).astype(np.float32))
+    cache.block_id.copy_(torch.from_numpy(bid))
+    cache.len.copy_(torch.from_numpy(np.where(bid >= 0, 64, 0).astype(np.int32)))
+    cache.k.copy_(torch.from_numpy(kc).to(torch.bfloat16))
+    cache.v.copy_(torch.from_numpy(vc).to(torch.bfloat16))
+    cache.chunk_index = chunk
+    win = np.sort(bid[0, C:])
+    sel_h = np.stack([win[:K] if r % 2 == 0 else win[K:2 * K] for r in range(nq)]).astype(np.int32)
+    T = F * n
+    q, k, v, do = (synth.round_bf16(rng.standard_normal((T, H, D)).astype(np.float32))
+                   for _ in range(4))
+    sel = torch.from_numpy(sel_h[None]).cuda()
+    qd, kd, vd, dod = dev(q), dev(k), dev(v), dev(do)
+    o = torch.empty_like(qd)
+    lse = torch.empty(H, T, dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(qd), torch.empty_like(qd), torch.empty_like(qd)
+    dkc = torch.full_like(cache.k, float("nan"))
+    dvc = torch.full_like(cache.v, float("nan"))
+    ws = torch.empty(ops.pbsa_workspace_bytes(shape, ops.PBSA_OP_ATTN_BWD_PERSISTENT),
+                     dtype=torch.uint8, device="cuda")
+    say(f"[persistent backward at the list limit] C={C} K={K} chunk blocks={nq}")
+    ops.pbsa_attn_fwd(shape, qd, cache, kd, vd, sel, o, lse)
+    ops.pbsa_attn_bwd_persistent(shape, qd, cache, kd, vd, sel, o, lse, dod, dq, dk, dv, dkc,
+                                 dvc, ws)
+    torch.cuda.synchronize()
+    dqg = dq[:, 0].float().cpu().numpy()
+    slot_of = {int(g): s for s, g in enumerate(bid[0])}
+    q0, k0, v0, do0 = (x[:, 0].astype(np.float64) for x in (q, k, v, do))
+    keys = {}
+    for par in (0, 1):
+        slots_ = list(range(C)) + [slot_of[int(g)] for g in sel_h[par]]
+        keys[par] = (np.concatenate([kc[0, s] for s in slots_] + [k0]).astype(np.float64),
+                     np.concatenate([vc[0, s] for s in slots_] + [v0]).astype(np.float64))
+    rows = []
+    for r in (0, 1, 128, 129, nq - 2, nq - 1):
+        rows += sorted({64 * r, 64 * r + 63} | set((64 * r + rng.choice(64, 2, replace=False)).tolist()))
+    got, ref = [], []
+    for t in rows:
+        K_, V_ = keys[(t // 64) % 2]
+        dq_ref, _, _ = orc.masked_attention_grad(q0[t:t + 1], K_, V_, np.ones((1, len(K_)), bool),
+                                                 shape.c().scale, do0[t:t + 1])
+        got.append(dqg[t])
+        ref.append(dq_ref[0])
+    assert_close_attn(np.array(got), np.array(ref), f"dQ of {len(rows)} rows at the list limit")
+    unused = [slot_of[int(g)] for g in win[2 * K:]]
+    assert len(unused) == 128
+    dkz = dkc[0, unused].float().cpu().numpy()
+    dvz = dvc[0, unused].float().cpu().numpy()
+    assert not dkz.any() and not dvz.any(), "unattended window slots must have zero dK/dV"
