@@ -90,8 +90,8 @@ typedef struct pbsa_dims {
  *                 pbsa_attn_bwd_persistent and pbsa_probe_gather do not take this format. */
 enum { PBSA_KV_BF16 = 0, PBSA_KV_FP8 = 1 };
 
-/* What the persistent-mode top-K chooses from (Sparse Forcing 2.C; north_star's "score
- * against P and L, keep the top-k"):
+/* What the persistent-mode top-K chooses from (Sparse Forcing 2.C, where the query blocks are
+ * scored against the persistent memory P and the local window L and the top-k kept):
  *   PBSA_ROUTE_WINDOW: the window blocks; every persistent block is attended.
  *   PBSA_ROUTE_UNION:  the non-sink persistent blocks and the window blocks together; only
  *                      the sinks are attended whole.  Limit: capacity + window blocks
